@@ -1,0 +1,195 @@
+// tq_api.hip -- C-ABI entry points: argument validation on the host, then kernel
+// launches on the caller's stream.  Declarations and contracts: include/tq.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "tq.h"
+#include "tq_internal.h"
+
+namespace {
+
+constexpr int kDecodeChunk = 256;       // tokens per decode chunk (one thread each)
+constexpr int64_t kDecodeTargetWgs = 1024;  // aim for ~4 workgroups per CU
+constexpr int64_t kMaxSplits = 256;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+bool packed_ok(const tq_packed *p) {
+    return p && p->key_words && p->key_norms && p->val_words && p->val_scales && p->capacity >= 0 &&
+           aligned16(p->key_words) && aligned8(p->key_norms) && aligned16(p->val_words) && aligned8(p->val_scales);
+}
+
+bool tables_ok(const tq_tables *t) {
+    return t && t->centroids && t->boundaries && t->sign_bits && t->qjl_S && aligned16(t->qjl_S);
+}
+
+int64_t decode_splits(int64_t slices, int64_t n_packed) {
+    const int64_t by_tokens = std::max<int64_t>(1, (n_packed + kDecodeChunk - 1) / kDecodeChunk);
+    const int64_t want = std::max<int64_t>(1, (kDecodeTargetWgs + slices - 1) / slices);
+    return std::min({by_tokens, want, kMaxSplits});
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct DecodeLayout {
+    size_t prep, partial, tickets, total;
+};
+
+DecodeLayout decode_layout(int d, int64_t batch, int64_t hq, int64_t hkv, int64_t n_split) {
+    DecodeLayout L;
+    L.prep = 0;
+    L.partial = align256(sizeof(float) * (size_t)(batch * hq) * (3 * d + 4));
+    L.tickets = L.partial + align256(sizeof(float) * (size_t)(batch * hq) * n_split * (d + 2));
+    L.total = L.tickets + align256(sizeof(unsigned) * (size_t)(batch * hkv));
+    return L;
+}
+
+tq_status hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" tq_status tq_quantize_kv(const tq_config *cfg, const tq_tables *tables, const void *k, const void *v,
+                                    tq_dtype in_dtype, int32_t n_slices, int64_t n_tokens, const tq_packed *dst,
+                                    int64_t dst_offset, void *stream) {
+    if (!cfg) return TQ_ERR_INVALID_ARG;
+    tq_status st = tq::check_config(*cfg);
+    if (st != TQ_OK) return st;
+    if (n_slices < 0 || n_tokens < 0 || dst_offset < 0) return TQ_ERR_INVALID_ARG;
+    if (in_dtype != TQ_F32 && in_dtype != TQ_BF16 && in_dtype != TQ_F16) return TQ_ERR_INVALID_ARG;
+    if (n_slices == 0 || n_tokens == 0) return TQ_OK;
+    if (!tables_ok(tables) || !packed_ok(dst) || !k || !v || !aligned16(k) || !aligned16(v))
+        return TQ_ERR_INVALID_ARG;
+    if (dst_offset + n_tokens > dst->capacity) return TQ_ERR_INVALID_ARG;
+    tq::QuantArgs a{};
+    a.k = k;
+    a.v = v;
+    a.in_slice_stride = n_tokens * cfg->head_dim;
+    a.n_tokens = n_tokens;
+    a.n_rows = (int64_t)n_slices * n_tokens;
+    a.centroids = tables->centroids;
+    a.boundaries = tables->boundaries;
+    a.sign_bits = tables->sign_bits;
+    a.S = tables->qjl_S;
+    a.kw = dst->key_words;
+    a.kn = dst->key_norms;
+    a.vw = dst->val_words;
+    a.vs = dst->val_scales;
+    a.cap = dst->capacity;
+    a.dst_offset = dst_offset;
+    return hip_status(tq::launch_quantize(cfg->head_dim, cfg->value_bits, in_dtype, a, (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_append_ring(const tq_config *cfg, const tq_ring *ring, const void *k_new, const void *v_new,
+                                    tq_dtype in_dtype, int32_t n_slices, int32_t n_ring, void *stream) {
+    if (!cfg) return TQ_ERR_INVALID_ARG;
+    tq_status st = tq::check_config(*cfg);
+    if (st != TQ_OK) return st;
+    if (n_slices < 0 || n_ring < 0 || n_ring > cfg->buffer_size) return TQ_ERR_INVALID_ARG;
+    if (in_dtype != TQ_F32 && in_dtype != TQ_BF16 && in_dtype != TQ_F16) return TQ_ERR_INVALID_ARG;
+    if (n_ring == cfg->buffer_size) return TQ_ERR_RING_FULL;
+    if (n_slices == 0) return TQ_OK;
+    if (!ring || !ring->k || !ring->v || !aligned16(ring->k) || !aligned16(ring->v) || !k_new || !v_new ||
+        !aligned16(k_new) || !aligned16(v_new))
+        return TQ_ERR_INVALID_ARG;
+    return hip_status(tq::launch_ring_append(cfg->head_dim, in_dtype, k_new, v_new, ring->k, ring->v, n_slices,
+                                             cfg->buffer_size, n_ring, (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_flush(const tq_config *cfg, const tq_tables *tables, const tq_ring *ring, int32_t n_slices,
+                              int32_t n_ring, const tq_packed *dst, int64_t n_packed, void *stream) {
+    if (!cfg) return TQ_ERR_INVALID_ARG;
+    tq_status st = tq::check_config(*cfg);
+    if (st != TQ_OK) return st;
+    if (n_slices < 0 || n_ring < 0 || n_ring > cfg->buffer_size || n_packed < 0) return TQ_ERR_INVALID_ARG;
+    if (n_slices == 0 || n_ring == 0) return TQ_OK;
+    if (!ring || !ring->k || !ring->v || !aligned16(ring->k) || !aligned16(ring->v) || !tables_ok(tables) ||
+        !packed_ok(dst))
+        return TQ_ERR_INVALID_ARG;
+    if (n_packed + n_ring > dst->capacity) return TQ_ERR_INVALID_ARG;
+    tq::QuantArgs a{};
+    a.k = ring->k;
+    a.v = ring->v;
+    a.in_slice_stride = (int64_t)cfg->buffer_size * cfg->head_dim;
+    a.n_tokens = n_ring;
+    a.n_rows = (int64_t)n_slices * n_ring;
+    a.centroids = tables->centroids;
+    a.boundaries = tables->boundaries;
+    a.sign_bits = tables->sign_bits;
+    a.S = tables->qjl_S;
+    a.kw = dst->key_words;
+    a.kn = dst->key_norms;
+    a.vw = dst->val_words;
+    a.vs = dst->val_scales;
+    a.cap = dst->capacity;
+    a.dst_offset = n_packed;
+    return hip_status(tq::launch_quantize(cfg->head_dim, cfg->value_bits, TQ_F16, a, (hipStream_t)stream));
+}
+
+extern "C" size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch, int32_t n_q_heads,
+                                            int32_t n_kv_heads, int64_t max_context) {
+    if (!cfg || tq::check_config(*cfg) != TQ_OK || batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 ||
+        max_context < 0)
+        return 0;
+    const int64_t n_split = decode_splits((int64_t)batch * n_kv_heads, max_context);
+    return decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_split).total;
+}
+
+extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *tables, const void *q,
+                                         tq_dtype q_dtype, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                         const tq_packed *packed, int64_t n_packed, const tq_ring *ring,
+                                         int32_t n_ring, float softmax_scale, float *out, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+    if (!cfg) return TQ_ERR_INVALID_ARG;
+    tq_status st = tq::check_config(*cfg);
+    if (st != TQ_OK) return st;
+    if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0 || n_packed < 0 ||
+        n_ring < 0 || n_ring > cfg->buffer_size)
+        return TQ_ERR_INVALID_ARG;
+    if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_ERR_INVALID_ARG;
+    const int G = n_q_heads / n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return TQ_ERR_UNSUPPORTED;
+    if ((int64_t)batch * n_kv_heads > 65535) return TQ_ERR_UNSUPPORTED;
+    if (!tables_ok(tables) || !q || !out || !aligned16(q) || !aligned16(out) || !workspace || !aligned16(workspace))
+        return TQ_ERR_INVALID_ARG;
+    if (n_packed > 0 && (!packed_ok(packed) || n_packed > packed->capacity)) return TQ_ERR_INVALID_ARG;
+    if (n_ring > 0 && (!ring || !ring->k || !ring->v || !aligned16(ring->k) || !aligned16(ring->v)))
+        return TQ_ERR_INVALID_ARG;
+    const int64_t slices = (int64_t)batch * n_kv_heads;
+    const int64_t n_split = decode_splits(slices, n_packed);
+    const DecodeLayout L = decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_split);
+    if (workspace_bytes < L.total) return TQ_ERR_WORKSPACE;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    tq::DecodeArgs a{};
+    a.q = q;
+    a.centroids = tables->centroids;
+    a.sign_bits = tables->sign_bits;
+    a.S = tables->qjl_S;
+    if (n_packed > 0) {
+        a.kw = packed->key_words;
+        a.kn = packed->key_norms;
+        a.vw = packed->val_words;
+        a.vs = packed->val_scales;
+        a.cap = packed->capacity;
+    }
+    a.n_packed = n_packed;
+    if (n_ring > 0) {
+        a.rk = ring->k;
+        a.rv = ring->v;
+    }
+    a.buffer_size = cfg->buffer_size;
+    a.n_ring = n_ring;
+    a.batch = batch;
+    a.hq = n_q_heads;
+    a.hkv = n_kv_heads;
+    a.n_split = (int)n_split;
+    a.per_split = n_packed > 0 ? (n_packed + n_split - 1) / n_split : 0;
+    a.scale = softmax_scale;
+    a.out = out;
+    a.prep = reinterpret_cast<float *>(ws + L.prep);
+    a.partial = reinterpret_cast<float *>(ws + L.partial);
+    a.tickets = reinterpret_cast<unsigned *>(ws + L.tickets);
+    return hip_status(tq::launch_decode(cfg->head_dim, cfg->value_bits, G, q_dtype, a, (hipStream_t)stream));
+}

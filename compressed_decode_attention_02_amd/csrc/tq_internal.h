@@ -1,0 +1,69 @@
+// tq_internal.h -- declarations shared by the host and device translation units of the
+// library (not installed; the public interface is include/tq.h).
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+#include "tq.h"
+
+namespace tq {
+
+// byte offsets inside the device table blob (see tq_tables_bytes in tq.h)
+constexpr size_t kTableCentroidOffset = 0;
+constexpr size_t kTableBoundaryOffset = 64;
+constexpr size_t kTableSignOffset = 128;
+constexpr size_t kTableSOffset = 256;
+
+tq_status check_config(const tq_config &c);
+
+struct QuantArgs {
+    const void *k;
+    const void *v;
+    int64_t in_slice_stride;  // elements between consecutive slices of the input
+    int64_t n_tokens;         // tokens per slice
+    int64_t n_rows;           // n_slices * n_tokens
+    const float *centroids;
+    const float *boundaries;
+    const uint32_t *sign_bits;
+    const uint16_t *S;
+    uint32_t *kw;
+    float *kn;
+    uint32_t *vw;
+    uint16_t *vs;
+    int64_t cap;
+    int64_t dst_offset;
+};
+
+struct DecodeArgs {
+    const void *q;
+    const float *centroids;
+    const uint32_t *sign_bits;
+    const uint16_t *S;
+    const uint32_t *kw;
+    const float *kn;
+    const uint32_t *vw;
+    const uint16_t *vs;
+    int64_t cap;
+    int64_t n_packed;
+    const uint16_t *rk;
+    const uint16_t *rv;
+    int buffer_size;
+    int n_ring;
+    int batch, hq, hkv;
+    int n_split;
+    int64_t per_split;  // packed tokens per split
+    float scale;
+    float *out;
+    float *prep;         // [batch*hq][3*D + 4]: q', w, q, (sum w)
+    float *partial;      // [batch*hkv][n_split][G][D + 2]
+    unsigned *tickets;   // [batch*hkv]
+};
+
+hipError_t launch_quantize(int d, int vb, tq_dtype dt, const QuantArgs &a, hipStream_t st);
+hipError_t launch_decode(int d, int vb, int G, tq_dtype qdt, const DecodeArgs &a, hipStream_t st);
+hipError_t launch_ring_append(int d, tq_dtype dt, const void *kn, const void *vn, uint16_t *rk, uint16_t *rv,
+                              int n_slices, int buffer_size, int slot, hipStream_t st);
+
+}  // namespace tq

@@ -1,0 +1,288 @@
+// tq_quantize.hip -- compression of keys and values into the packed store (gfx950).
+//
+// Method: hotelren.com guide "企业官网建设流程全解析", section 二: (1) random orthogonal
+// rotation, (2) Lloyd-Max quantisation of the rotated unit key against the Beta-law
+// codebook, (3) one QJL sign bit per coordinate for the residual, (4) symmetric 2/4-bit
+// value quantisation in groups of 32 with a per-group scale, (5) bit packing.
+//
+// Kernel layout (one wave = 32 token-head rows):
+//   lane l works on row m = l % 32 and holds the d/2 coordinates 16 s + 8 h + e
+//   (h = l / 32, e = 0..7, s = 0..d/16-1) -- exactly the A-operand layout of
+//   v_mfma_f32_32x32x16_f16, so the QJL projection S r of all 32 rows is a [32 x d] x
+//   [d x d] MFMA product without any data movement.
+//   * rotation: sign flip, then the unnormalised Walsh-Hadamard butterflies: bits 0-2 and
+//     4.. of the coordinate index are in-lane, bit 3 is one lane swap (l ^ 32);
+//   * encode: the codebook is antisymmetric with b_3 = 0, so |u| is compared with the
+//     three positive boundaries and the sign picks the half;
+//   * QJL: r is scaled by 2^8 and split into fp16 hi + lo parts; S is stored as exact
+//     fp16, so two MFMAs per k-step give S r with fp32 accumulation; sign bits come from
+//     wave ballots of the accumulator signs;
+//   * values: the group max over 32 channels is an in-lane max plus one lane swap; the
+//     floor is exact (the estimate is corrected with exact integer multiples of s).
+#include <hip/hip_runtime.h>
+
+#include "tq.h"
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+
+template <typename Tag, int D, int VB>
+__global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
+    constexpr int NS = D / 16;  // 8-coordinate chunks per lane
+    constexpr int NJ = D / 32;  // 32-column output tiles of the projection
+    constexpr int NG = D / 32;  // value groups
+    constexpr int HALF = 1 << (VB - 1);
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int m = lane & 31;
+    const int h = lane >> 5;
+    const int64_t row = ((int64_t)blockIdx.x * 4 + wv) * 32 + m;
+    const bool valid = row < a.n_rows;
+    int64_t sl = 0, t = 0;
+    if (valid) {
+        sl = row / a.n_tokens;
+        t = row - sl * a.n_tokens;
+    }
+    const int64_t in_off = sl * a.in_slice_stride + t * D + 8 * h;
+    const int64_t rec = sl * a.cap + a.dst_offset + t;
+
+    // ------------------------------------------------------------ keys: load + norm
+    float x[NS][8];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        if (valid) {
+            load8(a.k, in_off + 16 * s, x[s], Tag{});
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[s][e] = 0.f;
+        }
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fma((double)x[s][e], (double)x[s][e], ss);
+    ss += __shfl_xor(ss, 32);
+
+    // ------------------------------------------------------------ rotation
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int c0 = 16 * s + 8 * h;
+        const uint32_t sb = (a.sign_bits[c0 >> 5] >> (c0 & 31)) & 0xffu;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[s][e] = flip_sign(x[s][e], (sb >> e) & 1u);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int len = 1; len < 8; len <<= 1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (!(e & len)) {
+                    float p = x[s][e], q = x[s][e + len];
+                    x[s][e] = p + q;
+                    x[s][e + len] = p - q;
+                }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float y = __shfl_xor(x[s][e], 32);
+            x[s][e] = h ? (y - x[s][e]) : (x[s][e] + y);
+        }
+#pragma unroll
+    for (int len = 1; len < NS; len <<= 1)
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            if (!(s & len))
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float p = x[s][e], q = x[s + len][e];
+                    x[s][e] = p + q;
+                    x[s + len][e] = p - q;
+                }
+
+    const float knorm = (float)sqrt(ss);
+    const float inv = ss > 0.0 ? (float)(1.0 / (sqrt((double)D) * sqrt(ss))) : 0.f;
+
+    // ------------------------------------------------------------ encode + residual
+    const float b4 = a.boundaries[4], b5 = a.boundaries[5], b6 = a.boundaries[6];
+    const float m0 = a.centroids[4], m1 = a.centroids[5], m2 = a.centroids[6], m3 = a.centroids[7];
+    uint32_t kword[NS];
+    half8_t ahi[NS], alo[NS];
+    double gg = 0.0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        uint32_t codes = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float u = x[s][e] * inv;
+            const float av = fabsf(u);
+            const int kk = (av > b4) + (av > b5) + (av > b6);
+            const float mag = av > b6 ? m3 : (av > b5 ? m2 : (av > b4 ? m1 : m0));
+            const bool pos = u > 0.f;
+            const uint32_t idx = pos ? 4u + kk : 3u - kk;
+            const float r = u - (pos ? mag : -mag);
+            gg = fma((double)r, (double)r, gg);
+            codes |= idx << (3 * e);
+            const float rs = r * 256.f;
+            const _Float16 hi = (_Float16)rs;
+            ahi[s][e] = hi;
+            alo[s][e] = (_Float16)(rs - (float)hi);
+        }
+        kword[s] = codes;
+    }
+    gg += __shfl_xor(gg, 32);
+
+    // ------------------------------------------------------------ QJL projection (MFMA)
+    uint32_t sgn[NJ];
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) {
+        f32x16_t acc = {};
+        const uint16_t *srow = a.S + (int64_t)(jt * 32 + m) * D + 8 * h;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const half8_t bf = *reinterpret_cast<const half8_t *>(srow + 16 * s);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[s], bf, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[s], bf, acc, 0, 0, 0);
+        }
+        // accumulator register r of lane l holds column l % 32 of row 8 (r/4) + 4 (l/32) + r%4
+        uint32_t w = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint64_t bal = __ballot(acc[r] >= 0.f);
+            const int tok = 8 * (r >> 2) + (r & 3);
+            if (m == tok) w = (uint32_t)bal;
+            if (m == tok + 4) w = (uint32_t)(bal >> 32);
+        }
+        sgn[jt] = w;
+    }
+
+    // ------------------------------------------------------------ key words + store
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const uint32_t byte_pos = (uint32_t)(2 * (s & 1) + h);  // word (2s+h) mod 4
+        kword[s] |= ((sgn[s >> 1] >> (8 * byte_pos)) & 0xffu) << 24;
+    }
+    uint32_t outw[NS];
+#pragma unroll
+    for (int i = 0; i < NS / 2; ++i) {
+        const uint32_t send = h ? kword[i] : kword[NS / 2 + i];
+        const uint32_t recv = __shfl_xor(send, 32);
+        outw[2 * i] = h ? recv : kword[i];
+        outw[2 * i + 1] = h ? kword[NS / 2 + i] : recv;
+    }
+    if (valid) {
+        uint4 *dstk = reinterpret_cast<uint4 *>(a.kw + rec * (D / 8) + h * NS);
+#pragma unroll
+        for (int i = 0; i < NS / 4; ++i)
+            dstk[i] = make_uint4(outw[4 * i], outw[4 * i + 1], outw[4 * i + 2], outw[4 * i + 3]);
+        if (h == 0) *reinterpret_cast<float2 *>(a.kn + rec * 2) = make_float2(knorm, (float)sqrt(gg));
+    }
+
+    // ------------------------------------------------------------ values
+    float vv[NS][8];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        if (valid) {
+            load8(a.v, in_off + 16 * s, vv[s], Tag{});
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vv[s][e] = 0.f;
+        }
+    }
+    uint32_t vcode[NS];  // VB=4: full word 2s+h; VB=2: 16-bit half of word s at bit 0
+    uint16_t scb[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        float am = 0.f;
+#pragma unroll
+        for (int s = 2 * g; s < 2 * g + 2; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(vv[s][e]));
+        am = fmaxf(am, __shfl_xor(am, 32));
+        const _Float16 sh = (_Float16)(am * (1.0f / HALF));
+        const float sc = (float)sh;
+        scb[g] = __builtin_bit_cast(uint16_t, sh);
+        const float rinv = sc > 0.f ? 1.0f / sc : 0.f;
+#pragma unroll
+        for (int s = 2 * g; s < 2 * g + 2; ++s) {
+            uint32_t cw = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float val = vv[s][e];
+                float q = floorf(val * rinv);
+                if ((q + 1.f) * sc <= val) q += 1.f;
+                else if (q * sc > val) q -= 1.f;
+                q = fminf(fmaxf(q, (float)-HALF), (float)(HALF - 1));
+                const uint32_t code = sc > 0.f ? (uint32_t)((int)q + HALF) : (uint32_t)HALF;
+                cw |= code << (VB * e);
+            }
+            vcode[s] = cw;
+        }
+    }
+    uint32_t vout[NS];
+    if constexpr (VB == 2) {
+#pragma unroll
+        for (int i = 0; i < NS / 2; ++i) {
+            const uint32_t send = h ? (vcode[i] << 16) : vcode[NS / 2 + i];
+            const uint32_t recv = __shfl_xor(send, 32);
+            vout[i] = h ? ((vcode[NS / 2 + i] << 16) | recv) : (vcode[i] | recv);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NS / 2; ++i) {
+            const uint32_t send = h ? vcode[i] : vcode[NS / 2 + i];
+            const uint32_t recv = __shfl_xor(send, 32);
+            vout[2 * i] = h ? recv : vcode[i];
+            vout[2 * i + 1] = h ? vcode[NS / 2 + i] : recv;
+        }
+    }
+    if (valid) {
+        constexpr int VW = VB * D / 32;  // value words per record
+        constexpr int PER = VW / 2;      // words stored by each lane of the pair
+        uint4 *dstv = reinterpret_cast<uint4 *>(a.vw + rec * VW + h * PER);
+#pragma unroll
+        for (int i = 0; i < PER / 4; ++i)
+            dstv[i] = make_uint4(vout[4 * i], vout[4 * i + 1], vout[4 * i + 2], vout[4 * i + 3]);
+        if (h == 0) {
+            if constexpr (NG == 4) {
+                *reinterpret_cast<uint2 *>(a.vs + rec * NG) =
+                    make_uint2(scb[0] | ((uint32_t)scb[1] << 16), scb[2] | ((uint32_t)scb[3] << 16));
+            } else {
+                *reinterpret_cast<uint4 *>(a.vs + rec * NG) =
+                    make_uint4(scb[0] | ((uint32_t)scb[1] << 16), scb[2] | ((uint32_t)scb[3] << 16),
+                               scb[4] | ((uint32_t)scb[5] << 16), scb[6] | ((uint32_t)scb[7] << 16));
+            }
+        }
+    }
+}
+
+template <typename Tag, int D, int VB>
+static hipError_t launch_quantize_t(const QuantArgs &a, hipStream_t st) {
+    const int64_t waves = (a.n_rows + 31) / 32;
+    const int64_t blocks = (waves + 3) / 4;
+    hipLaunchKernelGGL((k_quantize<Tag, D, VB>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename Tag>
+static hipError_t launch_quantize_d(int d, int vb, const QuantArgs &a, hipStream_t st) {
+    if (d == 128 && vb == 2) return launch_quantize_t<Tag, 128, 2>(a, st);
+    if (d == 128 && vb == 4) return launch_quantize_t<Tag, 128, 4>(a, st);
+    if (d == 256 && vb == 2) return launch_quantize_t<Tag, 256, 2>(a, st);
+    return launch_quantize_t<Tag, 256, 4>(a, st);
+}
+
+hipError_t launch_quantize(int d, int vb, tq_dtype dt, const QuantArgs &a, hipStream_t st) {
+    if (a.n_rows == 0) return hipSuccess;
+    switch (dt) {
+        case TQ_F32: return launch_quantize_d<f32_tag>(d, vb, a, st);
+        case TQ_BF16: return launch_quantize_d<bf16_tag>(d, vb, a, st);
+        default: return launch_quantize_d<f16_tag>(d, vb, a, st);
+    }
+}
+
+}  // namespace tq

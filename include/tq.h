@@ -1,0 +1,168 @@
+/*
+ * tq.h -- C ABI of the MI355X (gfx950) TurboQuant KV-cache library.
+ *
+ * The library compresses attention keys and values into a packed cache and runs
+ * decode attention directly on that cache plus an exact ring buffer of recent tokens.
+ * The method (rotation, Lloyd-Max codebook for a Beta law, one QJL residual sign bit per
+ * coordinate, 2/4-bit symmetric value groups of 32, bit packing, exact recent buffer,
+ * hybrid attention) is the one described in the hotelren.com guide
+ * "企业官网建设流程全解析", sections 二 (five-step pipeline) and 5.1 (KV-write and
+ * forward hooks: prefill batch capture, single-token ring buffer, hybrid attention).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named host_* are host memory; every other buffer pointer is device memory
+ *     owned by the caller.  The library never allocates device memory and keeps no state.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Device work is enqueued
+ *     asynchronously on it; the call returns once the work is enqueued.
+ *   - All argument checks run synchronously on the host before anything is enqueued; on
+ *     any error nothing is launched and a negative tq_status is returned.
+ *   - Device pointers must be 16-byte aligned, except tq_packed.key_norms and
+ *     tq_packed.val_scales, which need 8 bytes (TQ_ERR_INVALID_ARG otherwise).
+ *   - Supported now: head_dim in {128, 256}, key_bits = 3, value_bits in {2, 4},
+ *     group_size = 32, 1 <= buffer_size <= 1024.  Other values give TQ_ERR_UNSUPPORTED.
+ *   - Non-finite inputs give unspecified output (no device-side scan).
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TQ_OK = 0,
+    TQ_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, negative size, inconsistent shape */
+    TQ_ERR_UNSUPPORTED = -2,  /* head_dim / bit width / group size not implemented          */
+    TQ_ERR_RING_FULL = -3,    /* append to a ring that already holds buffer_size tokens     */
+    TQ_ERR_WORKSPACE = -4,    /* decode workspace smaller than tq_decode_workspace_bytes()  */
+    TQ_ERR_HIP = -5           /* a HIP launch or runtime call failed                        */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+/* Compression parameters, named after the pages' hook arguments (key_bits, value_bits,
+ * buffer_size; guide section 5.1) and the value grouping (32 per group; section 二).
+ * key_bits counts the codebook bits only; every key coordinate also stores one QJL sign
+ * bit (so key_bits = 3 costs 4 bits per coordinate). */
+typedef struct {
+    int32_t head_dim;     /* d: 128 or 256                                  */
+    int32_t key_bits;     /* codebook bits per key coordinate: 3            */
+    int32_t value_bits;   /* 2 or 4                                         */
+    int32_t group_size;   /* values per quantisation group: 32              */
+    int32_t buffer_size;  /* ring capacity in tokens (the pages use 128)    */
+} tq_config;
+
+/* ------------------------------------------------------------------ host-side tables */
+
+/* Lloyd-Max codebook for one coordinate of a uniform unit vector in R^head_dim, i.e. the
+ * law (t+1)/2 ~ Beta((d-1)/2, (d-1)/2) (guide section 二, step 2 and the pre-generated
+ * codebooks per dimension and bit width).  Writes 2^key_bits centroids (ascending,
+ * antisymmetric) and 2^key_bits - 1 decision boundaries (midpoints), in double precision.
+ * head_dim: power of two in [8, 4096]; key_bits in [1, 4].  Host buffers, caller-owned. */
+tq_status tq_build_codebook(int32_t head_dim, int32_t key_bits, double *host_centroids,
+                            double *host_boundaries);
+
+/* Seeded random tables of the method (guide section 二, steps 1 and 3): the sign vector
+ * sigma of the rotation Pi = H diag(sigma) / sqrt(d) (H: natural-order Sylvester Hadamard
+ * matrix) and the d x d QJL projection S with N(0,1) entries rounded to fp16, row-major.
+ * Drawn from the splitmix64 stream seed + (i+1) * 0x9E3779B97F4A7C15: sigma_j from the
+ * top bit of word j, S pairs by Box-Muller from words d + 2m, d + 2m + 1.
+ * host_signs: d int8 (+1/-1); host_qjl_S: d*d fp16 bit patterns. */
+tq_status tq_build_rotation(int32_t head_dim, uint64_t seed, int8_t *host_signs, uint16_t *host_qjl_S);
+
+/* The device-side table blob: fp32 centroids at byte 0, fp32 boundaries at byte 64,
+ * sign bits at byte 128 (bit j%32 of word j/32 set when sigma_j = -1), fp16 S at byte 256.
+ * tq_tables_bytes: blob size.  tq_build_tables: fills a host blob of that size (the caller
+ * copies it to device memory once).  tq_tables_view: fills `out` with pointers into a
+ * device copy of the blob. */
+size_t tq_tables_bytes(const tq_config *cfg);
+tq_status tq_build_tables(const tq_config *cfg, uint64_t seed, void *host_blob, size_t blob_bytes);
+
+typedef struct {
+    const float *centroids;     /* 2^key_bits fp32                    */
+    const float *boundaries;    /* 2^key_bits - 1 fp32                */
+    const uint32_t *sign_bits;  /* d/32 words                         */
+    const uint16_t *qjl_S;      /* d*d fp16, row-major                */
+} tq_tables;
+
+tq_status tq_tables_view(const tq_config *cfg, const void *device_blob, tq_tables *out);
+
+/* ------------------------------------------------------------------ packed store */
+
+/* One packed record per (slice, token), slice = flattened (layer, batch, kv head);
+ * every array is [n_slices][capacity][...] with the record of token t at t:
+ *   key_words  [d/8] u32 : word w covers coordinates 8w..8w+7; bits 3k..3k+2 hold the
+ *                          3-bit codebook index of coordinate 8w+k, bit 24+k its QJL sign
+ *                          (1 when the projected residual is >= 0);
+ *   key_norms  [2]   f32 : |k| and the residual norm |u - c[idx]| of the unit key u;
+ *   val_words  [vb*d/32] u32 : vb-bit codes, code j at bit vb*(j mod 32/vb) of word
+ *                          j*vb/32 (least significant first: four 2-bit codes per byte);
+ *   val_scales [d/32] fp16 : per-group scale s; value = (code - 2^(vb-1) + 1/2) * s.
+ * Bytes per record: 112 (d 128, vb 2), 144 (d 128, vb 4), 280 (d 256, vb 4). */
+typedef struct {
+    uint32_t *key_words;
+    float *key_norms;
+    uint32_t *val_words;
+    uint16_t *val_scales;
+    int64_t capacity;           /* tokens per slice */
+} tq_packed;
+
+/* Exact recent tokens: fp16 [n_slices][buffer_size][d] keys and values (guide 5.1). */
+typedef struct {
+    uint16_t *k;
+    uint16_t *v;
+} tq_ring;
+
+size_t tq_packed_bytes_per_token(const tq_config *cfg);
+
+/* ------------------------------------------------------------------ device entry points */
+
+/* Prefill batch capture (guide 5.1 item 1; pipeline of section 二): compress n_tokens
+ * tokens of each of n_slices slices.  k, v: [n_slices][n_tokens][d] in in_dtype.
+ * Writes records dst_offset .. dst_offset + n_tokens - 1 of every slice.
+ * Requires dst_offset + n_tokens <= dst->capacity.  n_tokens == 0 is a no-op. */
+tq_status tq_quantize_kv(const tq_config *cfg, const tq_tables *tables, const void *k, const void *v,
+                         tq_dtype in_dtype, int32_t n_slices, int64_t n_tokens,
+                         const tq_packed *dst, int64_t dst_offset, void *stream);
+
+/* Decode single-token capture into the ring (guide 5.1 item 1): k_new, v_new
+ * [n_slices][d] in in_dtype are rounded to fp16 into ring slot n_ring of each slice.
+ * n_ring is the caller's current fill count; n_ring == buffer_size -> TQ_ERR_RING_FULL. */
+tq_status tq_append_ring(const tq_config *cfg, const tq_ring *ring, const void *k_new, const void *v_new,
+                         tq_dtype in_dtype, int32_t n_slices, int32_t n_ring, void *stream);
+
+/* Periodic flush of the ring into the compressed store (zingnex.cn page, Bonsai section:
+ * the recent exact window is flushed into the main cache): compresses ring slots
+ * 0 .. n_ring-1 of every slice into records n_packed .. n_packed + n_ring - 1.  The caller
+ * then sets n_packed += n_ring and n_ring = 0. */
+tq_status tq_flush(const tq_config *cfg, const tq_tables *tables, const tq_ring *ring, int32_t n_slices,
+                   int32_t n_ring, const tq_packed *dst, int64_t n_packed, void *stream);
+
+/* Workspace (device bytes) needed by tq_decode_attention for up to max_context tokens
+ * (packed + ring).  The workspace must be zero-filled once after allocation; every
+ * decode call leaves it zero-filled again when its work completes.  Calls that share a
+ * workspace must be ordered (same stream), as they use it in turn. */
+size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch, int32_t n_q_heads,
+                                 int32_t n_kv_heads, int64_t max_context);
+
+/* Hybrid decode attention (guide 5.1 item 2): for each batch b and query head h (GQA:
+ * kv head h / (n_q_heads / n_kv_heads)), softmax(scale * s) over the n_packed compressed
+ * tokens (s = unbiased inner-product estimate from codes, signs and norms) and the n_ring
+ * exact ring tokens, applied to the dequantised / exact values.
+ * q: [batch][n_q_heads][d] in q_dtype; packed / ring slices are b * n_kv_heads + kv head;
+ * out: [batch][n_q_heads][d] fp32.  n_packed + n_ring == 0 writes zeros. */
+tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *tables, const void *q, tq_dtype q_dtype,
+                              int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                              const tq_packed *packed, int64_t n_packed, const tq_ring *ring, int32_t n_ring,
+                              float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+const char *tq_status_string(tq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H */

@@ -67,7 +67,7 @@ def lib():
     L.orc_rotate.argtypes = [_int, _i8, _dp, _dp]
     L.orc_quantize_keys.restype = None
     L.orc_quantize_keys.argtypes = [_int, _int, _dp, _dp, _i8, _u16, _dp, _i64,
-                                    _u8, _u8, _dp, _dp, _dp, _dp]
+                                    _u8, _u8, _dp, _dp, _dp, _dp, ctypes.c_void_p]
     L.orc_quantize_values.restype = None
     L.orc_quantize_values.argtypes = [_int, _int, _int, _dp, _i64, _u8, _u16, _dp]
     L.orc_pack_keys.restype = None
@@ -175,8 +175,9 @@ def rotate(sigma: np.ndarray, x: np.ndarray) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- quantize
 
-def quantize_keys(k: np.ndarray, c32, b32, sigma, S_bits, kb: int = 3):
-    """k: [rows, d] (values as stored).  Returns dict with idx, z, norm, rnorm, margins."""
+def quantize_keys(k: np.ndarray, c32, b32, sigma, S_bits, kb: int = 3, force_idx=None):
+    """k: [rows, d] (values as stored).  Returns dict with idx, z, norm, rnorm, margins.
+    force_idx: optional [rows, d] codebook indices to use instead of the nearest cell."""
     k = _c(k, np.float64)
     rows, d = k.shape
     idx = np.zeros((rows, d), np.uint8)
@@ -186,7 +187,9 @@ def quantize_keys(k: np.ndarray, c32, b32, sigma, S_bits, kb: int = 3):
     um = np.zeros((rows, d), np.float64)
     pm = np.zeros((rows, d), np.float64)
     lib().orc_quantize_keys(d, kb, _c(c32, np.float64), _c(b32, np.float64), _c(sigma, np.int8),
-                            _c(S_bits, np.uint16).ravel(), k, rows, idx, z, n, g, um, pm)
+                            _c(S_bits, np.uint16).ravel(), k, rows, idx, z, n, g, um, pm,
+                            None if force_idx is None else
+                            _c(force_idx, np.uint8).ctypes.data_as(ctypes.c_void_p))
     return {"idx": idx, "z": z, "norm": n, "rnorm": g, "u_margin": um, "p_margin": pm}
 
 

@@ -266,11 +266,14 @@ void orc_rotate(int d, const int8_t *sigma, const double *x, double *y)
 /* c32 / b32 hold the stored single-precision table values.  S is the stored fp16  */
 /* matrix, row-major.  Margins: distance of u_j to the nearest boundary and |p_j|, */
 /* the quantities whose size decides whether a rounding difference may flip a bit. */
+/* force_idx (may be NULL): use these codebook indices instead of the nearest cell   */
+/* (a code chosen inside the rounding window changes the residual, and with it      */
+/* every sign bit of the row; this re-derives the rest of the row from that choice). */
 /* ------------------------------------------------------------------------------ */
 void orc_quantize_keys(int d, int kb, const double *c32, const double *b32, const int8_t *sigma,
                        const uint16_t *S_bits, const double *k, int64_t n_rows,
                        uint8_t *idx, uint8_t *z, double *norm, double *rnorm,
-                       double *u_margin, double *p_margin)
+                       double *u_margin, double *p_margin, const uint8_t *force_idx)
 {
     int L = 1 << kb;
     double *S = (double *)malloc(sizeof(double) * d * d);
@@ -293,6 +296,7 @@ void orc_quantize_keys(int d, int kb, const double *c32, const double *b32, cons
                 double dist = fabs(u[j] - b32[i]);
                 if (dist < mg) mg = dist;
             }
+            if (force_idx) cnt = force_idx[row * d + j];
             idx[row * d + j] = (uint8_t)cnt;
             if (u_margin) u_margin[row * d + j] = mg;
             r[j] = u[j] - c32[cnt];

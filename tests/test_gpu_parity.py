@@ -1,0 +1,251 @@
+"""GPU parity of the HIP path against the oracle at sizes the oracle finishes in seconds
+(several tiles plus ragged tails), through the C ABI.  Rules: tests/gpu_common.py."""
+import math
+
+import numpy as np
+import pytest
+
+import tq_workloads as W
+import compressed_decode_attention_02_amd as tq
+
+pytestmark = pytest.mark.gpu
+
+from gpu_common import (Env, assert_decode_close, check_quantize, dev_to_stored, log, oracle_decode,  # noqa: E402
+                        packed_to_np, quantize_gpu, run_decode, to_dev)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need a GPU"
+    return t
+
+
+def _quantize_case(env, w: W.Workload, n_tokens, cap_extra=0, offset=0, label=""):
+    (k, v), _ = W.host_kv(w, 0, n_tokens)
+    n_slices = w.batch * w.hkv
+    k = k.reshape(n_slices, n_tokens, w.d)
+    v = v.reshape(n_slices, n_tokens, w.d)
+    kd, vd = to_dev(k, w.in_dtype), to_dev(v, w.in_dtype)
+    store = quantize_gpu(env, kd, vd, n_slices, n_tokens, capacity=n_tokens + cap_extra + offset, offset=offset)
+    P = packed_to_np(store)
+    sl = slice(offset, offset + n_tokens)
+    st = check_quantize(env, k.reshape(-1, w.d).astype(np.float64), v.reshape(-1, w.d).astype(np.float64),
+                        P["kw"][:, sl].reshape(-1, w.d // 8), P["kn"][:, sl].reshape(-1, 2),
+                        P["vw"][:, sl].reshape(-1, w.value_bits * w.d // 32),
+                        P["vs"][:, sl].reshape(-1, w.d // 32), label=label)
+    # records outside [offset, offset + n_tokens) are untouched (zero)
+    if offset:
+        assert not P["kw"][:, :offset].any() and not P["vw"][:, :offset].any()
+    if cap_extra:
+        assert not P["kw"][:, offset + n_tokens:].any()
+    log(f"{label}: {st}")
+    return store, (k, v)
+
+
+def test_quantize_tiny_fp32(torch):
+    w = W.WORKLOADS[1]
+    env = Env(w.d, w.value_bits)
+    _quantize_case(env, w, w.n_packed, label="tiny fp32")
+
+
+def test_quantize_llama_law_ragged_with_offset(torch):
+    w = W.custom(2, hkv=8)
+    env = Env(w.d, w.value_bits)
+    _quantize_case(env, w, 1000, cap_extra=5, offset=37, label="llama-law bf16 v2 ragged")
+
+
+def test_quantize_value_bits4(torch):
+    w = W.custom(3, batch=2, hkv=3)
+    env = Env(w.d, w.value_bits)
+    _quantize_case(env, w, 333, label="bf16 v4")
+
+
+def test_quantize_d256_student_t(torch):
+    w = W.custom(4, batch=1, hkv=4)
+    env = Env(w.d, w.value_bits)
+    _quantize_case(env, w, 301, label="d256 t3 v4")
+
+
+def test_quantize_d256_v2_fp16_input(torch):
+    w = W.custom(4, batch=1, hkv=2, value_bits=2, in_dtype="f32")
+    env = Env(w.d, 2)
+    (k, v), _ = W.host_kv(w, 0, 129)
+    k = k.reshape(2, 129, w.d).astype(np.float16).astype(np.float32)
+    v = v.reshape(2, 129, w.d).astype(np.float16).astype(np.float32)
+    store = quantize_gpu(env, to_dev(k, "f16"), to_dev(v, "f16"), 2, 129)
+    P = packed_to_np(store)
+    check_quantize(env, k.reshape(-1, w.d).astype(np.float64), v.reshape(-1, w.d).astype(np.float64),
+                   P["kw"].reshape(-1, w.d // 8), P["kn"].reshape(-1, 2), P["vw"].reshape(-1, 2 * w.d // 32),
+                   P["vs"].reshape(-1, w.d // 32), label="d256 f16 input")
+
+
+def test_quantize_edge_rows(torch):
+    """Zero key, zero value groups, a single huge coordinate, tiny values, a one-token call."""
+    env = Env(128, 2)
+    r = np.random.default_rng(5)
+    k = r.standard_normal((1, 40, 128)).astype(np.float32)
+    v = r.standard_normal((1, 40, 128)).astype(np.float32)
+    k[0, 0] = 0.0
+    v[0, 1, :64] = 0.0
+    k[0, 2] = 0.0
+    k[0, 2, 77] = 1e4
+    v[0, 3] = 1e-6
+    v[0, 4, 5] = 300.0
+    k[0, 5] = -k[0, 6]
+    store = quantize_gpu(env, to_dev(k, "f32"), to_dev(v, "f32"), 1, 40)
+    P = packed_to_np(store)
+    check_quantize(env, k.reshape(-1, 128).astype(np.float64), v.reshape(-1, 128).astype(np.float64),
+                   P["kw"].reshape(-1, 16), P["kn"].reshape(-1, 2), P["vw"].reshape(-1, 8),
+                   P["vs"].reshape(-1, 4), label="edge rows")
+    one = quantize_gpu(env, to_dev(k[:, :1], "f32"), to_dev(v[:, :1], "f32"), 1, 1)
+    np.testing.assert_array_equal(one.key_words.cpu().numpy()[0, 0], P["kw"][0, 0])
+
+
+def test_quantize_is_deterministic(torch):
+    w = W.custom(2, hkv=4)
+    env = Env(128, 2)
+    (k, v), _ = W.host_kv(w, 0, 500)
+    kd, vd = to_dev(k.reshape(4, 500, 128), "bf16"), to_dev(v.reshape(4, 500, 128), "bf16")
+    a = packed_to_np(quantize_gpu(env, kd, vd, 4, 500))
+    b = packed_to_np(quantize_gpu(env, kd, vd, 4, 500))
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_ring_append_is_exact_fp16(torch):
+    env = Env(128, 2, buffer_size=16)
+    ring = tq.Ring(env.cfg, 6)
+    r = np.random.default_rng(8)
+    ks, vs = [], []
+    for slot in range(16):
+        kn = r.standard_normal((6, 128)).astype(np.float32) * 3
+        vn = r.standard_normal((6, 128)).astype(np.float32)
+        kd, vd = to_dev(kn, "bf16"), to_dev(vn, "bf16")
+        tq.tq_append_ring(env.cfg, ring.struct(), kd, vd, 6, slot)
+        ks.append(dev_to_stored(kd))
+        vs.append(dev_to_stored(vd))
+    torch.cuda.synchronize()
+    with pytest.raises(tq.TqError):
+        tq.tq_append_ring(env.cfg, ring.struct(), kd, vd, 6, 16)
+    exp_k = np.stack(ks, 1).astype(np.float16)
+    exp_v = np.stack(vs, 1).astype(np.float16)
+    np.testing.assert_array_equal(ring.k.cpu().numpy().view(np.uint16), exp_k.view(np.uint16))
+    np.testing.assert_array_equal(ring.v.cpu().numpy().view(np.uint16), exp_v.view(np.uint16))
+
+
+def test_flush_writes_records_after_the_history(torch):
+    env = Env(128, 4, buffer_size=128)
+    n_sl, n_pk, n_ring = 5, 300, 97
+    w = W.custom(3, batch=1, hkv=n_sl)
+    (k, v), _ = W.host_kv(w, 0, n_pk + n_ring)
+    k = k.reshape(n_sl, -1, 128)
+    v = v.reshape(n_sl, -1, 128)
+    store = quantize_gpu(env, to_dev(np.ascontiguousarray(k[:, :n_pk]), "bf16"),
+                         to_dev(np.ascontiguousarray(v[:, :n_pk]), "bf16"), n_sl, n_pk, capacity=n_pk + 128)
+    ring = tq.Ring(env.cfg, n_sl)
+    for t in range(n_ring):
+        tq.tq_append_ring(env.cfg, ring.struct(), to_dev(np.ascontiguousarray(k[:, n_pk + t]), "bf16"),
+                          to_dev(np.ascontiguousarray(v[:, n_pk + t]), "bf16"), n_sl, t)
+    tq.tq_flush(env.cfg, env.tables, ring.struct(), n_sl, n_ring, store.struct(), n_pk)
+    torch.cuda.synchronize()
+    P = packed_to_np(store)
+    kr = k[:, n_pk:].astype(np.float16).astype(np.float64).reshape(-1, 128)
+    vr = v[:, n_pk:].astype(np.float16).astype(np.float64).reshape(-1, 128)
+    sl = slice(n_pk, n_pk + n_ring)
+    check_quantize(env, kr, vr, P["kw"][:, sl].reshape(-1, 16), P["kn"][:, sl].reshape(-1, 2),
+                   P["vw"][:, sl].reshape(-1, 16), P["vs"][:, sl].reshape(-1, 4), label="flush")
+    assert not P["kw"][:, n_pk + n_ring:].any()
+
+
+# ------------------------------------------------------------------------- decode
+
+def _decode_case(w: W.Workload, label, b_list=None, seed_layer=0):
+    env = Env(w.d, w.value_bits, buffer_size=w.buffer_size)
+    n_sl = w.batch * w.hkv
+    (k, v), _ = W.host_kv(w, seed_layer, w.n_packed + w.n_ring)
+    k = k.reshape(n_sl, -1, w.d)
+    v = v.reshape(n_sl, -1, w.d)
+    store = None
+    if w.n_packed:
+        store = quantize_gpu(env, to_dev(np.ascontiguousarray(k[:, :w.n_packed]), w.in_dtype),
+                             to_dev(np.ascontiguousarray(v[:, :w.n_packed]), w.in_dtype), n_sl, w.n_packed)
+    ring = None
+    if w.n_ring:
+        ring = tq.Ring(env.cfg, n_sl)
+        for t in range(w.n_ring):
+            tq.tq_append_ring(env.cfg, ring.struct(), to_dev(np.ascontiguousarray(k[:, w.n_packed + t]), w.in_dtype),
+                              to_dev(np.ascontiguousarray(v[:, w.n_packed + t]), w.in_dtype), n_sl, t)
+    q, _ = W.host_queries(w, seed_layer)
+    g, q_stored, ws = run_decode(env, q, w.in_dtype, w.batch, w.hq, w.hkv, store, w.n_packed, ring, w.n_ring)
+    b_list = list(range(w.batch)) if b_list is None else b_list
+    ref = oracle_decode(env, q_stored, w.hq, w.hkv, store, w.n_packed, ring, w.n_ring, b_list=b_list)
+    err = assert_decode_close(g[b_list], ref, label)
+    return env, store, ring, q, ws, g, err
+
+
+def test_decode_tiny(torch):
+    _decode_case(W.WORKLOADS[1], "tiny")
+
+
+def test_decode_llama_law_packed_and_ring(torch):
+    _decode_case(W.custom(2, n_packed=3000, n_ring=128), "llama-law b1")
+
+
+def test_decode_batched_v4(torch):
+    _decode_case(W.custom(3, batch=3, n_packed=700, n_ring=64), "b3 v4")
+
+
+def test_decode_d256(torch):
+    _decode_case(W.custom(4, batch=2, n_packed=1500, n_ring=128), "d256 v4")
+
+
+def test_decode_gqa_groups(torch):
+    for hq, hkv in ((8, 8), (16, 8), (64, 8)):
+        _decode_case(W.custom(2, hq=hq, hkv=hkv, n_packed=600, n_ring=5), f"G={hq // hkv}")
+
+
+def test_decode_ring_only_and_single_token(torch):
+    _decode_case(W.custom(2, n_packed=0, n_ring=77), "ring only")
+    _decode_case(W.custom(2, n_packed=1, n_ring=0), "one packed token")
+    _decode_case(W.custom(2, n_packed=257, n_ring=1), "257 + 1")
+
+
+def test_decode_empty_context_gives_zeros(torch):
+    env = Env(128, 2)
+    q = np.ones((1, 4, 128), np.float32)
+    g, _, _ = run_decode(env, q, "f32", 1, 4, 1, None, 0, None, 0)
+    assert not g.any()
+
+
+def test_decode_workspace_is_rearmed(torch):
+    """Two calls on the same workspace give identical results; tickets end at zero."""
+    w = W.custom(2, n_packed=2000, n_ring=3)
+    env, store, ring, q, ws, g1, _ = _decode_case(w, "rearm", b_list=[0])
+    qd = to_dev(q, w.in_dtype)
+    out = torch.zeros((w.batch, w.hq, w.d), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        tq.tq_decode_attention(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, store.struct(), w.n_packed,
+                               ring.struct(), w.n_ring, 1 / math.sqrt(w.d), out, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), g1.astype(np.float32))
+    tail = ws[-256:].cpu().numpy()
+    assert not tail.any()
+
+
+def test_append_flush_decode_sequence(torch):
+    """History + ring decode, then flush the ring and decode again over packed only."""
+    w = W.custom(3, batch=2, n_packed=500, n_ring=64)
+    env, store_unused, ring, q, ws, g, _ = _decode_case(w, "before flush")
+    n_sl = w.batch * w.hkv
+    (k, v), _ = W.host_kv(w, 0, w.n_packed + w.n_ring)
+    k = k.reshape(n_sl, -1, w.d)
+    v = v.reshape(n_sl, -1, w.d)
+    store = quantize_gpu(env, to_dev(np.ascontiguousarray(k[:, :w.n_packed]), "bf16"),
+                         to_dev(np.ascontiguousarray(v[:, :w.n_packed]), "bf16"), n_sl, w.n_packed,
+                         capacity=w.n_packed + w.buffer_size)
+    tq.tq_flush(env.cfg, env.tables, ring.struct(), n_sl, w.n_ring, store.struct(), w.n_packed)
+    n_packed = w.n_packed + w.n_ring
+    g2, q_stored, _ = run_decode(env, q, "bf16", w.batch, w.hq, w.hkv, store, n_packed, None, 0)
+    ref = oracle_decode(env, q_stored, w.hq, w.hkv, store, n_packed, None, 0, b_list=list(range(w.batch)))
+    assert_decode_close(g2, ref, "after flush")
