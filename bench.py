@@ -1,0 +1,218 @@
+"""Benchmark of the TurboQuant KV hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  1. tq_quantize_kv   -- compress the prefill history (Q1-Q6) of every (layer, batch, kv head)
+  2. tq_append_ring   -- one decode-time token per slice into the exact ring (R1)
+  3. tq_decode_attention -- hybrid attention over packed history + ring, every layer (D1-D5)
+  4. tq_flush         -- compress the ring contents into the packed store (R2)
+value = context KV-tokens (batch * layers * (packed + ring)) per second of step time.
+
+Per-kernel times come from HIP events on the stream the kernels run on; several copies of
+the inputs and stores are cycled so that the working set exceeds the 256 MB Infinity Cache.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "packed-KV decode attention KV-tokens/s + HBM GB/s; quantize tokens/s"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=2, help="workload id (1..5); 2 = Llama-3.1-8B b1 32K")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import tq_workloads as W
+    import compressed_decode_attention_02_amd as tq
+
+    w = W.WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    d, L, B, hq, hkv = w.d, w.layers, w.batch, w.hq, w.hkv
+    n_sl_layer = B * hkv
+    n_sl = L * n_sl_layer
+    Tp = w.n_packed
+    ring_fill = max(w.n_ring - 1, 0)  # the step's append brings the ring to n_ring tokens
+    cfg = tq.make_config(d, 3, w.value_bits, 32, w.buffer_size)
+    tables = tq.Tables(cfg, W.TABLE_SEED, device=dev)
+    rec = tq.tq_packed_bytes_per_token(cfg)
+    in_bytes = 2 if w.in_dtype == "bf16" else 4
+
+    # copies cycled through to defeat the MALL (only while a copy is small)
+    step_bytes = n_sl * Tp * (2 * d * in_bytes + rec)
+    n_copies = max(1, min(8, math.ceil(2 * 256e6 / max(step_bytes, 1)) + 1))
+    copies = []
+    for c in range(n_copies):
+        ks, vs = [], []
+        for layer in range(L):
+            k, v = W.device_kv(w, layer + 1000 * c, Tp, dev)
+            ks.append(k.reshape(n_sl_layer, Tp, d))
+            vs.append(v.reshape(n_sl_layer, Tp, d))
+        K = torch.cat(ks).contiguous() if L > 1 else ks[0]
+        V = torch.cat(vs).contiguous() if L > 1 else vs[0]
+        del ks, vs
+        store = tq.PackedStore(cfg, n_sl, Tp + w.buffer_size, device=dev)
+        ring = tq.Ring(cfg, n_sl, device=dev)
+        kn, vn = W.device_kv(w, 7777 + c, 1, dev, tensor_ids=(3, 4))
+        kn = kn.reshape(n_sl_layer, d).repeat(L, 1).contiguous()
+        vn = vn.reshape(n_sl_layer, d).repeat(L, 1).contiguous()
+        qs = [W.device_queries(w, layer + 1000 * c, dev) for layer in range(L)]
+        outs = [torch.zeros((B, hq, d), dtype=torch.float32, device=dev) for _ in range(L)]
+        ws = tq.new_workspace(cfg, B, hq, hkv, Tp + w.buffer_size, device=dev)
+        # pre-fill ring slots [0, ring_fill) so that the step's append brings it to n_ring tokens
+        for t in range(ring_fill):
+            tq.tq_append_ring(cfg, ring.struct(), kn, vn, n_sl, t)
+        copies.append(dict(K=K, V=V, store=store, ring=ring, kn=kn, vn=vn, qs=qs, outs=outs, ws=ws))
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(d)
+    stream = torch.cuda.current_stream()
+
+    def step(c, ev=None):
+        cp = copies[c]
+        st, rg = cp["store"], cp["ring"]
+        if ev: ev[0].record(stream)
+        tq.tq_quantize_kv(cfg, tables, cp["K"], cp["V"], n_sl, Tp, st.struct(), 0)
+        if ev: ev[1].record(stream)
+        if w.n_ring > 0:
+            tq.tq_append_ring(cfg, rg.struct(), cp["kn"], cp["vn"], n_sl, ring_fill)
+        if ev: ev[2].record(stream)
+        for layer in range(L):
+            off = layer * n_sl_layer
+            tq.tq_decode_attention(cfg, tables, cp["qs"][layer], B, hq, hkv, st.struct(off), Tp,
+                                   rg.struct(off), w.n_ring, scale, cp["outs"][layer], cp["ws"])
+        if ev: ev[3].record(stream)
+        if w.n_ring > 0:
+            tq.tq_flush(cfg, tables, rg.struct(), n_sl, w.n_ring, st.struct(), Tp)
+        if ev: ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i % n_copies)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % n_copies, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    a_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    d_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    f_ms = [e[3].elapsed_time(e[4]) for e in evs]
+    ms_step = wall * 1e3 / args.steps
+
+    ctx = Tp + w.n_ring
+    kv_tokens = B * L * ctx
+    q_bytes = n_sl * Tp * (2 * d * in_bytes + rec)
+    dec_bytes = L * (n_sl_layer * (Tp * rec + w.n_ring * 4 * d) + B * hq * d * (in_bytes + 4))
+    q_med, d_med = statistics.median(q_ms), statistics.median(d_ms)
+    q_gbps = q_bytes / (q_med * 1e-3) / 1e9
+    d_gbps = dec_bytes / (d_med * 1e-3) / 1e9
+    dominant = "quantize" if q_med >= d_med else "decode"
+    roof = {
+        "kernel": "k_quantize" if dominant == "quantize" else "k_decode_prep+k_decode_main",
+        "bound": "hbm",
+        "achieved": round(q_gbps if dominant == "quantize" else d_gbps, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round((q_gbps if dominant == "quantize" else d_gbps) / HBM_PEAK_GBPS, 4),
+        "traffic": None,
+        "algorithmic_bytes_per_launch": q_bytes if dominant == "quantize" else dec_bytes // L,
+    }
+
+    res = {
+        "metric": METRIC,
+        "value": round(kv_tokens / (ms_step * 1e-3), 1),
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.in_dtype,
+        "data": "synthetic (seeded device draws of the workload's laws)",
+        "config": {"workload": w.name, "layers": L, "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": d,
+                   "packed_tokens": Tp, "ring_tokens": w.n_ring, "key_bits": 3, "qjl_bits": 1,
+                   "value_bits": w.value_bits, "group": 32, "parallelism": "none (1 GPU)",
+                   "copies_cycled": n_copies},
+        "breakdown_ms_median": {"quantize": round(q_med, 4), "append": round(statistics.median(a_ms), 4),
+                                "decode_all_layers": round(d_med, 4), "flush": round(statistics.median(f_ms), 4)},
+        "quantize_tokens_per_s": round(B * L * Tp / (q_med * 1e-3), 1),
+        "quantize_GBps": round(q_gbps, 1),
+        "decode_kv_tokens_per_s": round(kv_tokens / (d_med * 1e-3), 1),
+        "decode_GBps": round(d_gbps, 1),
+        "decode_frac_of_hbm_peak": round(d_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": roof,
+        "roofline_decode": {"bound": "hbm", "achieved": round(d_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(d_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                            "algorithmic_bytes_per_launch": dec_bytes // L},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, sample_tokens: int):
+    """The oracle (plain C, fp64, one thread) timed on a bounded sample of the same step:
+    quantize `sample_tokens` tokens of every kv head of one layer and one batch element,
+    then decode all q heads of that batch element over those tokens."""
+    import numpy as np
+
+    import oracle as O
+    import tq_workloads as W
+
+    d = w.d
+    T = min(sample_tokens, w.n_packed)
+    ws = W.custom(w.cid, batch=1)
+    (k, v), _ = W.host_kv(ws, 0, T)
+    k = k.reshape(ws.hkv, T, d).astype(np.float64)
+    v = v.reshape(ws.hkv, T, d).astype(np.float64)
+    q, _ = W.host_queries(ws, 0)
+    c32, b32 = O.stored_codebook(d, 3)
+    sigma, S = O.tables(d, W.TABLE_SEED)
+    t0 = time.perf_counter()
+    kq = O.quantize_keys(k.reshape(-1, d), c32, b32, sigma, S)
+    vq = O.quantize_values(v.reshape(-1, d), w.value_bits)
+    kw = O.pack_keys(kq["idx"], kq["z"]).reshape(ws.hkv, T, -1)
+    kn = np.stack([kq["norm"], kq["rnorm"]], 1).astype(np.float32).reshape(ws.hkv, T, 2)
+    vw = O.pack_values(vq["code"], w.value_bits).reshape(ws.hkv, T, -1)
+    vs = vq["scale"].reshape(ws.hkv, T, -1)
+    t1 = time.perf_counter()
+    O.decode(d=d, kb=3, vb=w.value_bits, c32=c32, sigma=sigma, S_bits=S, B=1, Hq=ws.hq, Hkv=ws.hkv, kw=kw, kn=kn,
+             vw=vw, vs=vs, cap=T, n_packed=T, rk=None, rv=None, buf=0, n_ring=0, q=q.astype(np.float64),
+             scale=1 / math.sqrt(d))
+    t2 = time.perf_counter()
+    return {"value": round(T / (t2 - t0), 1), "unit": "KV-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"1 layer, batch 1, {ws.hkv} kv heads x {T} tokens quantized, then decode of {ws.hq} q heads "
+                      f"over them (quantize {t1 - t0:.2f} s, decode {t2 - t1:.2f} s, fp64 C, one thread)"}
+
+
+if __name__ == "__main__":
+    main()

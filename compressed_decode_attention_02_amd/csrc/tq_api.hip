@@ -10,9 +10,9 @@
 
 namespace {
 
-constexpr int kDecodeChunk = 256;       // tokens per decode chunk (one thread each)
-constexpr int64_t kDecodeTargetWgs = 1024;  // aim for ~4 workgroups per CU
-constexpr int64_t kMaxSplits = 256;
+constexpr int64_t kMinSplitTokens = 1024;  // at least four 256-token chunks per split
+constexpr int64_t kDecodeTargetWgs = 512;  // about two workgroups per CU
+constexpr int64_t kMaxSplits = 256;        // the merge keeps one weight per split in LDS
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
@@ -27,7 +27,7 @@ bool tables_ok(const tq_tables *t) {
 }
 
 int64_t decode_splits(int64_t slices, int64_t n_packed) {
-    const int64_t by_tokens = std::max<int64_t>(1, (n_packed + kDecodeChunk - 1) / kDecodeChunk);
+    const int64_t by_tokens = std::max<int64_t>(1, (n_packed + kMinSplitTokens - 1) / kMinSplitTokens);
     const int64_t want = std::max<int64_t>(1, (kDecodeTargetWgs + slices - 1) / slices);
     return std::min({by_tokens, want, kMaxSplits});
 }

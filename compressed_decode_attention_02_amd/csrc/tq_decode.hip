@@ -302,23 +302,37 @@ __global__ __launch_bounds__(kThreads) void k_decode_main(DecodeArgs a) {
     __syncthreads();
     if (s_ticket != (unsigned)(a.n_split - 1)) return;
     __threadfence();
-    // ---- last workgroup of this (batch, kv head): merge the n_split partials
+    // ---- last workgroup of this (batch, kv head): merge the n_split partials.
+    // Split weights f_s = exp(m_s - M) and the sum L per head are computed by one wave per
+    // head with all splits' loads in flight; then every thread sums o over the splits for
+    // its (head, coordinate) outputs, with the loads of many splits issued back to back.
     const float *base = a.partial + (int64_t)bk * a.n_split * G * (D + 2);
+    {
+        const int lane = tid & 63, wv = tid >> 6;
+        for (int g = wv; g < G; g += kThreads / 64) {
+            float mx = -INFINITY;
+            for (int sp = lane; sp < a.n_split; sp += 64) mx = fmaxf(mx, base[(sp * G + g) * (D + 2) + D]);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+            float ls = 0.f;
+            for (int sp = lane; sp < a.n_split; sp += 64) {
+                const float ms = base[(sp * G + g) * (D + 2) + D];
+                const float f = (ms == -INFINITY) ? 0.f : __expf(ms - mx);
+                s_p[g][sp] = f;
+                ls = fmaf(base[(sp * G + g) * (D + 2) + D + 1], f, ls);
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+            if (lane == 0) s_corr[g] = ls;
+        }
+    }
+    __syncthreads();
     for (int i = tid; i < G * D; i += kThreads) {
         const int g = i / D, j = i - g * D;
-        float M = -INFINITY;
-        for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, base[(sp * G + g) * (D + 2) + D]);
-        float L = 0.f, O = 0.f;
-        if (M != -INFINITY) {
-            for (int sp = 0; sp < a.n_split; ++sp) {
-                const float *ps = base + (sp * G + g) * (D + 2);
-                const float ms = ps[D];
-                if (ms == -INFINITY) continue;
-                const float f = __expf(ms - M);
-                L = fmaf(ps[D + 1], f, L);
-                O = fmaf(ps[j], f, O);
-            }
-        }
+        float O = 0.f;
+#pragma unroll 8
+        for (int sp = 0; sp < a.n_split; ++sp) O = fmaf(s_p[g][sp], base[(sp * G + g) * (D + 2) + j], O);
+        const float L = s_corr[g];
         a.out[((int64_t)b * a.hq + kvh * G + g) * D + j] = L > 0.f ? O / L : 0.f;
     }
     if (tid == 0) __hip_atomic_store(a.tickets + bk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

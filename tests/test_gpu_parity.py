@@ -99,7 +99,7 @@ def test_quantize_edge_rows(torch):
                    P["kw"].reshape(-1, 16), P["kn"].reshape(-1, 2), P["vw"].reshape(-1, 8),
                    P["vs"].reshape(-1, 4), label="edge rows")
     one = quantize_gpu(env, to_dev(k[:, :1], "f32"), to_dev(v[:, :1], "f32"), 1, 1)
-    np.testing.assert_array_equal(one.key_words.cpu().numpy()[0, 0], P["kw"][0, 0])
+    np.testing.assert_array_equal(one.key_words.cpu().numpy().view(np.uint32)[0, 0], P["kw"][0, 0])
 
 
 def test_quantize_is_deterministic(torch):
