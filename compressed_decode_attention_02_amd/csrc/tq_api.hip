@@ -12,7 +12,7 @@ namespace {
 
 constexpr int64_t kMinSplitTokens = 1024;  // at least four 256-token chunks per split
 constexpr int64_t kDecodeTargetWgs = 512;  // about two workgroups per CU
-constexpr int64_t kMaxSplits = 256;        // the merge keeps one weight per split in LDS
+constexpr int64_t kMaxSplits = 255;        // the merge keeps one weight per split (+ ring) in LDS
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
@@ -134,7 +134,7 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch,
         max_context < 0)
         return 0;
     const int64_t n_split = decode_splits((int64_t)batch * n_kv_heads, max_context);
-    return decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_split).total;
+    return decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_split + 1).total;
 }
 
 extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *tables, const void *q,
@@ -158,8 +158,11 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     if (n_ring > 0 && (!ring || !ring->k || !ring->v || !aligned16(ring->k) || !aligned16(ring->v)))
         return TQ_ERR_INVALID_ARG;
     const int64_t slices = (int64_t)batch * n_kv_heads;
-    const int64_t n_split = decode_splits(slices, n_packed);
-    const DecodeLayout L = decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_split);
+    // packed splits, plus one split for the ring; an empty context still runs one (empty)
+    // split so that the output is written
+    const int64_t n_split = n_packed > 0 ? decode_splits(slices, n_packed) : (n_ring > 0 ? 0 : 1);
+    const int64_t n_total = n_split + (n_ring > 0 ? 1 : 0);
+    const DecodeLayout L = decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_total);
     if (workspace_bytes < L.total) return TQ_ERR_WORKSPACE;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     tq::DecodeArgs a{};
@@ -185,6 +188,7 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     a.hq = n_q_heads;
     a.hkv = n_kv_heads;
     a.n_split = (int)n_split;
+    a.n_split_total = (int)n_total;
     a.per_split = n_packed > 0 ? (n_packed + n_split - 1) / n_split : 0;
     a.scale = softmax_scale;
     a.out = out;

@@ -145,8 +145,9 @@ extern "C" tq_status tq_build_tables(const tq_config *cfg, uint64_t seed, void *
     if (st != TQ_OK) return st;
     float *cf = reinterpret_cast<float *>(p + tq::kTableCentroidOffset);
     float *bf = reinterpret_cast<float *>(p + tq::kTableBoundaryOffset);
-    for (int i = 0; i < L; ++i) cf[i] = (float)c[i];
-    for (int i = 0; i + 1 < L; ++i) bf[i] = (float)b[i];
+    // stored table: centroids rounded to binary16, boundaries their exact midpoints
+    for (int i = 0; i < L; ++i) cf[i] = (float)(_Float16)c[i];
+    for (int i = 0; i + 1 < L; ++i) bf[i] = (float)(0.5 * ((double)cf[i] + (double)cf[i + 1]));
     std::vector<int8_t> sg(d);
     uint16_t *S = reinterpret_cast<uint16_t *>(p + tq::kTableSOffset);
     st = tq_build_rotation(d, seed, sg.data(), S);

@@ -52,12 +52,13 @@ struct DecodeArgs {
     int buffer_size;
     int n_ring;
     int batch, hq, hkv;
-    int n_split;
+    int n_split;        // splits over the packed tokens
+    int n_split_total;  // n_split, plus one split for the ring tokens when there are any
     int64_t per_split;  // packed tokens per split
     float scale;
     float *out;
     float *prep;         // [batch*hq][3*D + 4]: q', w, q, (sum w)
-    float *partial;      // [batch*hkv][n_split][G][D + 2]
+    float *partial;      // [batch*hkv][n_split_total][G][D + 2]
     unsigned *tickets;   // [batch*hkv]
 };
 

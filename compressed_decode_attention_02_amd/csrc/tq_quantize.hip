@@ -13,7 +13,8 @@
 //   * rotation: sign flip, then the unnormalised Walsh-Hadamard butterflies: bits 0-2 and
 //     4.. of the coordinate index are in-lane, bit 3 is one lane swap (l ^ 32);
 //   * encode: the codebook is antisymmetric with b_3 = 0, so |u| is compared with the
-//     three positive boundaries and the sign picks the half;
+//     three positive boundaries and the sign picks the half; each coordinate becomes a
+//     nibble (3-bit index, QJL sign bit on top), eight coordinates per 32-bit word;
 //   * QJL: r is scaled by 2^8 and split into fp16 hi + lo parts; S is stored as exact
 //     fp16, so two MFMAs per k-step give S r with fp32 accumulation; sign bits come from
 //     wave ballots of the accumulator signs;
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
             const uint32_t idx = pos ? 4u + kk : 3u - kk;
             const float r = u - (pos ? mag : -mag);
             gg = fma((double)r, (double)r, gg);
-            codes |= idx << (3 * e);
+            codes |= idx << (4 * e);
             const float rs = r * 256.f;
             const _Float16 hi = (_Float16)rs;
             ahi[s][e] = hi;
@@ -161,10 +162,16 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
     }
 
     // ------------------------------------------------------------ key words + store
+    // word 2s+h holds coordinates 16s+8h..+7 as nibbles (code | sign << 3); its 8 sign
+    // bits are byte (2s+h) mod 4 of the projection tile's sign word, spread to bit 4e+3
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        const uint32_t byte_pos = (uint32_t)(2 * (s & 1) + h);  // word (2s+h) mod 4
-        kword[s] |= ((sgn[s >> 1] >> (8 * byte_pos)) & 0xffu) << 24;
+        const uint32_t byte_pos = (uint32_t)(2 * (s & 1) + h);
+        uint32_t zb = (sgn[s >> 1] >> (8 * byte_pos)) & 0xffu;
+        zb = (zb | (zb << 12)) & 0x000f000fu;
+        zb = (zb | (zb << 6)) & 0x03030303u;
+        zb = (zb | (zb << 3)) & 0x11111111u;
+        kword[s] |= zb << 3;
     }
     uint32_t outw[NS];
 #pragma unroll

@@ -73,7 +73,9 @@ tq_status tq_build_codebook(int32_t head_dim, int32_t key_bits, double *host_cen
  * host_signs: d int8 (+1/-1); host_qjl_S: d*d fp16 bit patterns. */
 tq_status tq_build_rotation(int32_t head_dim, uint64_t seed, int8_t *host_signs, uint16_t *host_qjl_S);
 
-/* The device-side table blob: fp32 centroids at byte 0, fp32 boundaries at byte 64,
+/* The device-side table blob: centroids at byte 0 (fp32 holding the binary16 rounding of
+ * the Lloyd-Max values: the table precision of the fp16 KV path), decision boundaries at
+ * byte 64 (fp32, exact midpoints of adjacent stored centroids),
  * sign bits at byte 128 (bit j%32 of word j/32 set when sigma_j = -1), fp16 S at byte 256.
  * tq_tables_bytes: blob size.  tq_build_tables: fills a host blob of that size (the caller
  * copies it to device memory once).  tq_tables_view: fills `out` with pointers into a
@@ -94,9 +96,9 @@ tq_status tq_tables_view(const tq_config *cfg, const void *device_blob, tq_table
 
 /* One packed record per (slice, token), slice = flattened (layer, batch, kv head);
  * every array is [n_slices][capacity][...] with the record of token t at t:
- *   key_words  [d/8] u32 : word w covers coordinates 8w..8w+7; bits 3k..3k+2 hold the
- *                          3-bit codebook index of coordinate 8w+k, bit 24+k its QJL sign
- *                          (1 when the projected residual is >= 0);
+ *   key_words  [d/8] u32 : word w covers coordinates 8w..8w+7 as nibbles: bits 4k..4k+2
+ *                          hold the 3-bit codebook index of coordinate 8w+k, bit 4k+3 its
+ *                          QJL sign bit (1 when the projected residual is >= 0);
  *   key_norms  [2]   f32 : |k| and the residual norm |u - c[idx]| of the unit key u;
  *   val_words  [vb*d/32] u32 : vb-bit codes, code j at bit vb*(j mod 32/vb) of word
  *                          j*vb/32 (least significant first: four 2-bit codes per byte);

@@ -57,6 +57,8 @@ def lib():
     L.orc_tables.argtypes = [_int, ctypes.c_uint64, _i8, _u16]
     L.orc_codebook.restype = _int
     L.orc_codebook.argtypes = [_int, _int, _dp, _dp]
+    L.orc_stored_codebook.restype = _int
+    L.orc_stored_codebook.argtypes = [_int, _int, _dp, _dp]
     L.orc_coord_cdf.restype = ctypes.c_double
     L.orc_coord_cdf.argtypes = [_int, ctypes.c_double]
     L.orc_coord_moment.restype = ctypes.c_double
@@ -136,9 +138,13 @@ def codebook(d: int, kb: int):
 
 
 def stored_codebook(d: int, kb: int):
-    """The single-precision table values the method stores (round-to-nearest-even)."""
-    c, b, _ = codebook(d, kb)
-    return c.astype(np.float32).astype(np.float64), b.astype(np.float32).astype(np.float64)
+    """The table values the method stores and uses: centroids rounded to fp16, boundaries
+    the exact midpoints of adjacent stored centroids (both returned as doubles)."""
+    c = np.zeros(1 << kb, np.float64)
+    b = np.zeros((1 << kb) - 1, np.float64)
+    if lib().orc_stored_codebook(d, kb, c, b) < 0:
+        raise ValueError("bad codebook arguments")
+    return c, b
 
 
 def tables(d: int, seed: int):

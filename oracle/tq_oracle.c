@@ -25,7 +25,8 @@
  *   vector in R^d, whose law is (t+1)/2 ~ Beta((d-1)/2, (d-1)/2);
  *   QJL matrix S: d x d, N(0,1) entries rounded to fp16, drawn from a splitmix64
  *   counter stream through Box-Muller; estimator constant sqrt(pi/2)/d;
- *   value quantiser: bin-centre symmetric, scale fp16(max|v| / 2^(vb-1)).
+ *   value quantiser: bin-centre symmetric, scale fp16(max|v| / 2^(vb-1));
+ *   stored codebook: centroids rounded to fp16, boundaries their exact midpoints.
  *
  * Everything here runs in double precision on inputs already rounded to their stored
  * type.  No blocking, fusion or reordering: every quantity is computed from its
@@ -231,6 +232,22 @@ int orc_codebook(int d, int kb, double *c, double *b)
     return it;
 }
 
+/*
+ * The table values the method stores and uses: each centroid rounded to the nearest
+ * binary16 value (the precision of the fp16 KV path), and each decision boundary the
+ * exact midpoint of its two stored centroids (representable in binary32).
+ */
+int orc_stored_codebook(int d, int kb, double *c_store, double *b_store)
+{
+    int L = 1 << kb;
+    double c[256], b[255];
+    int it = orc_codebook(d, kb, c, b);
+    if (it < 0) return it;
+    for (int i = 0; i < L; ++i) c_store[i] = orc_f16_to_double(orc_double_to_f16(c[i]));
+    for (int i = 0; i + 1 < L; ++i) b_store[i] = 0.5 * (c_store[i] + c_store[i + 1]);
+    return it;
+}
+
 /* cell mass and conditional mean, exported so tests can probe the fixed point */
 double orc_coord_cdf(int d, double t) { return coord_cdf(0.5 * (d - 1), t); }
 double orc_coord_moment(int d, double a, double b) { return coord_first_moment(0.5 * (d - 1), a, b); }
@@ -361,8 +378,9 @@ void orc_quantize_values(int d, int vb, int group, const double *v, int64_t n_ro
 
 /* ------------------------------------------------------------------------------ */
 /* Packed record layout (one token-head):                                          */
-/*   key word w (0 <= w < d/8) covers coordinates 8w..8w+7: bits 3k..3k+2 hold the */
-/*   3-bit code of coordinate 8w+k, bit 24+k holds its QJL sign bit;               */
+/*   key word w (0 <= w < d/8) covers coordinates 8w..8w+7 as eight 4-bit nibbles: */
+/*   nibble k (bits 4k..4k+3) holds the 3-bit codebook index of coordinate 8w+k in */
+/*   its low three bits and that coordinate's QJL sign bit in its top bit;         */
 /*   value codes least-significant first: code j sits at bit vb*(j mod (32/vb)) of */
 /*   word floor(j*vb/32)  (four 2-bit codes per byte, as the pages state).         */
 /* ------------------------------------------------------------------------------ */
@@ -374,8 +392,8 @@ void orc_pack_keys(int d, const uint8_t *idx, const uint8_t *z, int64_t n_rows, 
             uint32_t x = 0;
             for (int k = 0; k < 8; ++k) {
                 int j = 8 * w + k;
-                x |= ((uint32_t)idx[row * d + j] & 7u) << (3 * k);
-                x |= ((uint32_t)z[row * d + j] & 1u) << (24 + k);
+                uint32_t nib = ((uint32_t)idx[row * d + j] & 7u) | (((uint32_t)z[row * d + j] & 1u) << 3);
+                x |= nib << (4 * k);
             }
             words[row * nw + w] = x;
         }
@@ -386,10 +404,9 @@ void orc_unpack_keys(int d, const uint32_t *words, int64_t n_rows, uint8_t *idx,
     int nw = d / 8;
     for (int64_t row = 0; row < n_rows; ++row)
         for (int j = 0; j < d; ++j) {
-            uint32_t x = words[row * nw + j / 8];
-            int k = j % 8;
-            idx[row * d + j] = (uint8_t)((x >> (3 * k)) & 7u);
-            z[row * d + j] = (uint8_t)((x >> (24 + k)) & 1u);
+            uint32_t nib = (words[row * nw + j / 8] >> (4 * (j % 8))) & 15u;
+            idx[row * d + j] = (uint8_t)(nib & 7u);
+            z[row * d + j] = (uint8_t)(nib >> 3);
         }
 }
 

@@ -88,6 +88,16 @@ def test_coordinate_law_cdf_against_monte_carlo_sphere():
         assert abs(emp - O.coord_cdf(d, q)) < 4 * math.sqrt(0.25 / len(t))
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_stored_codebook_is_fp16_rounding_with_midpoints(d):
+    c, _, _ = O.codebook(d, 3)
+    cs, bs = O.stored_codebook(d, 3)
+    np.testing.assert_array_equal(cs, c.astype(np.float16).astype(np.float64))
+    np.testing.assert_array_equal(bs, 0.5 * (cs[:-1] + cs[1:]))
+    assert bs[3] == 0.0 and np.array_equal(bs, -bs[::-1])
+    np.testing.assert_array_equal(bs, bs.astype(np.float32).astype(np.float64))   # exact in fp32
+
+
 # ------------------------------------------------------------------------- fp16 / tables
 
 def test_f16_decode_matches_numpy_for_every_pattern():
@@ -294,17 +304,18 @@ def test_value_quality_band_matches_page(vb, key):
 # ------------------------------------------------------------------------- packing
 
 def test_pack_single_bit_patterns():
+    """Key word w holds coordinates 8w..8w+7 as nibbles: code in bits 0-2, sign in bit 3."""
     d = 128
     for j in (0, 1, 7, 8, 63, 127):
         for code in range(8):
             idx = np.zeros((1, d), np.uint8); idx[0, j] = code
             z = np.zeros((1, d), np.uint8)
             w = O.pack_keys(idx, z)
-            expect = np.zeros(d // 8, np.uint32); expect[j // 8] = code << (3 * (j % 8))
+            expect = np.zeros(d // 8, np.uint32); expect[j // 8] = code << (4 * (j % 8))
             np.testing.assert_array_equal(w[0], expect)
         z = np.zeros((1, d), np.uint8); z[0, j] = 1
         w = O.pack_keys(np.zeros((1, d), np.uint8), z)
-        expect = np.zeros(d // 8, np.uint32); expect[j // 8] = 1 << (24 + j % 8)
+        expect = np.zeros(d // 8, np.uint32); expect[j // 8] = 8 << (4 * (j % 8))
         np.testing.assert_array_equal(w[0], expect)
     # values: four 2-bit codes per byte, least significant first
     code = np.zeros((1, d), np.uint8); code[0, 5] = 3
