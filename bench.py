@@ -36,7 +36,31 @@ def parse():
     p.add_argument("--config", type=int, default=2, help="workload id (1..5); 2 = Llama-3.1-8B b1 32K")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    p.add_argument("--probe-copy-mib", type=int, default=0,
+                   help="only time a plain device-to-device copy of this many MiB (achievable HBM "
+                        "bandwidth; also the known-size kernel that calibrates the traffic counters)")
     return p.parse_args()
+
+
+def probe_copy(mib: int, steps: int):
+    import torch
+    n = mib * 2**20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    moved = 2 * n * 4
+    print(json.dumps({"probe": "device copy", "bytes_read": n * 4, "bytes_written": n * 4,
+                      "ms": round(ms, 4), "GBps": round(moved / ms / 1e6, 1),
+                      "frac_of_8TBps": round(moved / ms / 1e6 / HBM_PEAK_GBPS, 4)}), flush=True)
 
 
 def main():
@@ -44,6 +68,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
         sys.exit(2)
+    if args.probe_copy_mib:
+        probe_copy(args.probe_copy_mib, args.steps)
+        return
     import numpy as np
     import torch
 
