@@ -63,6 +63,22 @@ def probe_copy(mib: int, steps: int):
                       "frac_of_8TBps": round(moved / ms / 1e6 / HBM_PEAK_GBPS, 4)}), flush=True)
 
 
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this workload,
+    or None when there is none or the kernel's sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic__{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get("kernels", {}).get(kernel)
+    if not rec:
+        return None
+    h = hashlib.sha1()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, "compressed_decode_attention_02_amd", "csrc", f), "rb").read())
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha1"] else None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -168,7 +184,7 @@ def main():
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round((q_gbps if dominant == "quantize" else d_gbps) / HBM_PEAK_GBPS, 4),
-        "traffic": None,
+        "traffic": measured_traffic(w.name, "k_quantize" if dominant == "quantize" else "k_decode_prep+k_decode_main"),
         "algorithmic_bytes_per_launch": q_bytes if dominant == "quantize" else dec_bytes // L,
     }
 
@@ -198,7 +214,8 @@ def main():
         "decode_frac_of_hbm_peak": round(d_gbps / HBM_PEAK_GBPS, 4),
         "roofline": roof,
         "roofline_decode": {"bound": "hbm", "achieved": round(d_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                            "frac": round(d_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                            "frac": round(d_gbps / HBM_PEAK_GBPS, 4),
+                            "traffic": measured_traffic(w.name, "k_decode_prep+k_decode_main"),
                             "algorithmic_bytes_per_launch": dec_bytes // L},
     }
     if not args.no_cpu_baseline:
