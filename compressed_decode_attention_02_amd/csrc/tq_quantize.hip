@@ -5,22 +5,29 @@
 // codebook, (3) one QJL sign bit per coordinate for the residual, (4) symmetric 2/4-bit
 // value quantisation in groups of 32 with a per-group scale, (5) bit packing.
 //
-// Kernel layout (one wave = 32 token-head rows):
-//   lane l works on row m = l % 32 and holds the d/2 coordinates 16 s + 8 h + e
-//   (h = l / 32, e = 0..7, s = 0..d/16-1) -- exactly the A-operand layout of
-//   v_mfma_f32_32x32x16_f16, so the QJL projection S r of all 32 rows is a [32 x d] x
-//   [d x d] MFMA product without any data movement.
-//   * rotation: sign flip, then the unnormalised Walsh-Hadamard butterflies: bits 0-2 and
-//     4.. of the coordinate index are in-lane, bit 3 is one lane swap (l ^ 32);
-//   * encode: the codebook is antisymmetric with b_3 = 0, so |u| is compared with the
-//     three positive boundaries and the sign picks the half; each coordinate becomes a
-//     nibble (3-bit index, QJL sign bit on top), eight coordinates per 32-bit word;
-//   * QJL: r is scaled by 2^8 and split into fp16 hi + lo parts; S is stored as exact
-//     fp16, so two MFMAs per k-step give S r with fp32 accumulation; sign bits come from
-//     wave ballots of the accumulator signs;
-//   * values: the group max over 32 channels is an in-lane max plus one lane swap; the
-//     floor is exact (the estimate is corrected with exact integer multiples of s).
+// Keys: k_quant_keys, one wave per tile of R tokens (R = 32 at d = 128 on
+// v_mfma_f32_32x32x16, R = 16 at d = 256 on v_mfma_f32_16x16x32); the KG = 64 / R lanes of
+// a token each hold 64 of its coordinates.
+//   * rotation: the Walsh-Hadamard product H (sigma o x) runs on the matrix cores with the
+//     raw 16-bit inputs as the B operand (exact: H has entries +-1, sigma is a sign flip
+//     applied by XOR on the raw words) and fp32 accumulation.  H factorises over the index
+//     bits, so the A operand of every (output tile, k-step) pair is one of two per-lane
+//     +-1 fragments, possibly negated;
+//   * the accumulator layout leaves lane group g of a token with the 64 coordinates
+//     slot_coord(f, g), f = 0..63; encode is elementwise on them: the codebook is
+//     antisymmetric with b_3 = 0, so |u| is compared with the three positive boundaries as
+//     integers (ties resolved as idx = #{i : u > b_i} on both sides);
+//   * QJL: the projection is computed transposed, D = S R^T with the residual (scaled by
+//     2^8, split into fp16 hi + lo) as the B operand, so the accumulator hands every lane
+//     the projections of exactly the coordinates it encoded; sign bits go straight into
+//     the nibbles;
+//   * nibble half-words of a key word live in the two lanes g, g ^ 1; one permlane swap
+//     and two byte permutes assemble the words.
+// Values: k_quant_values, one lane per (token, group of 32): in-lane group max, fp16 scale,
+// exact floor (see quant_group), codes accumulated in place.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "tq.h"
 #include "tq_device.h"
@@ -28,259 +35,509 @@
 
 namespace tq {
 
-template <typename Tag, int D, int VB>
-__global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
-    constexpr int NS = D / 16;  // 8-coordinate chunks per lane
-    constexpr int NJ = D / 32;  // 32-column output tiles of the projection
-    constexpr int NG = D / 32;  // value groups
-    constexpr int HALF = 1 << (VB - 1);
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct KeyShape {
+    static constexpr int R = D == 128 ? 32 : 16;  // tokens per wave (MFMA M = N)
+    static constexpr int KG = 64 / R;             // lanes per token
+    static constexpr int K = 8 * KG;              // MFMA k per instruction
+    static constexpr int NS = D / K;              // rotation k-steps
+    static constexpr int NJ = D / R;              // rotation / projection output tiles
+    static constexpr int RPT = R * R / 64;        // accumulator registers per tile and lane
+    static constexpr int NV = D / KG;             // coordinates per lane (64)
+    static constexpr int NQ = NV / 8;             // projection k-steps
+    static constexpr int KW = D / 8;              // key words per record
+    static constexpr int NP = NV / 8;             // u32 registers of nibble half-word pairs
+};
+
+template <int R>
+using acc_t = std::conditional_t<R == 32, f32x16_t, f32x4_t>;
+
+// coordinate held in accumulator slot f (tile f / RPT, register f % RPT) by lane group g:
+// the MFMA result layout (row 4 g + (r & 3) + 4 KG (r >> 2) of the tile)
+template <int D>
+__device__ __host__ constexpr int slot_coord(int f, int g) {
+    using S = KeyShape<D>;
+    return S::R * (f / S::RPT) + 4 * g + ((f % S::RPT) & 3) + 4 * S::KG * ((f % S::RPT) >> 2);
+}
+
+// rotation A operand of (output tile jt, k-step s): fragment variant and global sign, from
+// popcount((R jt + i) & (K s + k)) split over the index bits
+template <int D>
+__device__ __host__ constexpr int h_variant(int jt, int s) {
+    return KeyShape<D>::R == 32 ? (s & 1) : (jt & 1);
+}
+template <int D>
+__device__ __host__ constexpr int h_negated(int jt, int s) {
+    return __builtin_popcount(KeyShape<D>::R == 32 ? (jt & (s >> 1)) : ((jt >> 1) & s)) & 1;
+}
+
+template <int R, typename Tag>
+__device__ __forceinline__ acc_t<R> mfma_in(u32x4_t a, u32x4_t b, acc_t<R> c) {
+    if constexpr (R == 32) {
+        if constexpr (std::is_same_v<Tag, f16_tag>)
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
+                                                          __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                           __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    } else {
+        if constexpr (std::is_same_v<Tag, f16_tag>)
+            return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                          __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                           __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+}
+
+template <int R>
+__device__ __forceinline__ acc_t<R> mfma_f16(u32x4_t a, u32x4_t b, acc_t<R> c) {
+    if constexpr (R == 32)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b),
+                                                      c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b),
+                                                      c, 0, 0, 0);
+}
+
+// exact split of an fp32 value into three bf16 parts (x = hi + mid + lo)
+__device__ __forceinline__ void split3_bf16(float x, uint16_t &hi, uint16_t &mid, uint16_t &lo) {
+    const __bf16 h = (__bf16)x;
+    const float r1 = x - (float)h;
+    const __bf16 m = (__bf16)r1;
+    const __bf16 l = (__bf16)(r1 - (float)m);
+    hi = __builtin_bit_cast(uint16_t, h);
+    mid = __builtin_bit_cast(uint16_t, m);
+    lo = __builtin_bit_cast(uint16_t, l);
+}
+
+// ------------------------------------------------------------------------------ keys
+// Launch shape: persistent workgroups that loop over tiles of rows (the S copy in LDS is
+// made once per workgroup); latency is hidden by the other waves of the SIMD (a register
+// prefetch of the next tile does not fit the budget).  d = 128: 4-wave groups, 3 per CU; d = 256:
+// 12-wave groups, one per CU (sharing one 130 KB LDS copy of S).  Register budget: 3 waves
+// per SIMD (<= 168 VGPRs).
+template <int D>
+constexpr int kKeyGroupWaves = D == 128 ? 4 : 12;
+template <int D>
+constexpr int kKeyGroupsPerCU = D == 128 ? 3 : 1;
+// S rows in LDS are padded by 8 bytes: the 8-byte A-fragment reads of 32 consecutive rows
+// at one column then fall into distinct banks
+template <int D>
+constexpr int kSRow = D + 4;  // halfwords
+
+// row -> (slice, token) without a 64-bit integer division: the quotient from the fp64
+// product is off by at most one for rows < 2^52 and is corrected exactly
+__device__ __forceinline__ void split_row(int64_t r, int64_t n_tok, double inv, int64_t &sl, int64_t &t) {
+    int64_t q = (int64_t)((double)r * inv);
+    int64_t rem = r - q * n_tok;
+    if (rem < 0) {
+        q -= 1;
+        rem += n_tok;
+    } else if (rem >= n_tok) {
+        q += 1;
+        rem -= n_tok;
+    }
+    sl = q;
+    t = rem;
+}
+
+template <typename Tag, int D>
+__global__ __launch_bounds__(64 * kKeyGroupWaves<D>) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void k_quant_keys(QuantArgs a) {
+    using S = KeyShape<D>;
+    constexpr int R = S::R;
+    constexpr int NT = 64 * kKeyGroupWaves<D>;
+    constexpr bool kF32 = std::is_same_v<Tag, f32_tag>;
+    constexpr bool kF16 = std::is_same_v<Tag, f16_tag>;
+    constexpr int RAWW = kF32 ? 8 : 4;
+
+    // sigma as XOR masks on 16-bit pairs: word p has bit 15 = sigma_2p, bit 31 = sigma_2p+1
+    __shared__ __attribute__((aligned(16))) uint32_t smask[D / 2];
+    __shared__ __attribute__((aligned(16))) uint16_t sS[D * kSRow<D>];
+    if (threadIdx.x < D / 2) {
+        const int c = 2 * threadIdx.x;
+        const uint32_t w = a.sign_bits[c >> 5] >> (c & 31);
+        smask[threadIdx.x] = ((w & 1u) << 15) | ((w & 2u) << 30);
+    }
+    for (int i = threadIdx.x; i < D * D / 8; i += NT) {  // 16-byte chunks of S
+        const int j = i / (D / 8), c = (i % (D / 8)) * 8;
+        const uint4 x = *reinterpret_cast<const uint4 *>(a.S + (int64_t)j * D + c);
+        uint2 *dst = reinterpret_cast<uint2 *>(&sS[j * kSRow<D> + c]);
+        dst[0] = make_uint2(x.x, x.y);
+        dst[1] = make_uint2(x.z, x.w);
+    }
+    __syncthreads();
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
-    const int m = lane & 31;
-    const int h = lane >> 5;
-    const int64_t row = ((int64_t)blockIdx.x * 4 + wv) * 32 + m;
-    const bool valid = row < a.n_rows;
-    int64_t sl = 0, t = 0;
-    if (valid) {
-        sl = row / a.n_tokens;
-        t = row - sl * a.n_tokens;
-    }
-    const int64_t in_off = sl * a.in_slice_stride + t * D + 8 * h;
-    const int64_t rec = sl * a.cap + a.dst_offset + t;
+    const int n = lane % R, g = lane / R;
+    const int64_t my = (int64_t)(threadIdx.x >> 6) * R + n;  // row offset inside a group tile
+    const int64_t stride = (int64_t)gridDim.x * kKeyGroupWaves<D> * R;
+    const double inv_tok = 1.0 / (double)a.n_tokens;
 
-    // ------------------------------------------------------------ keys: load + norm
-    float x[NS][8];
+    // raw inputs of one row: k-step s holds coordinates K s + 8 g + 0..7 (rows past the end
+    // are clamped to the last row, so every lane reads real data)
+    uint32_t raw[S::NS][RAWW];
+    auto load_raw = [&](int64_t row) {
+        int64_t sl, t;
+        split_row(row < a.n_rows ? row : a.n_rows - 1, a.n_tokens, inv_tok, sl, t);
+        const int64_t in_off = sl * a.in_slice_stride + t * D + 8 * g;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        if (valid) {
-            load8(a.k, in_off + 16 * s, x[s], Tag{});
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[s][e] = 0.f;
-        }
-    }
-    double ss = 0.0;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fma((double)x[s][e], (double)x[s][e], ss);
-    ss += __shfl_xor(ss, 32);
-
-    // ------------------------------------------------------------ rotation
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const int c0 = 16 * s + 8 * h;
-        const uint32_t sb = (a.sign_bits[c0 >> 5] >> (c0 & 31)) & 0xffu;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[s][e] = flip_sign(x[s][e], (sb >> e) & 1u);
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int len = 1; len < 8; len <<= 1)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (!(e & len)) {
-                    float p = x[s][e], q = x[s][e + len];
-                    x[s][e] = p + q;
-                    x[s][e + len] = p - q;
-                }
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float y = __shfl_xor(x[s][e], 32);
-            x[s][e] = h ? (y - x[s][e]) : (x[s][e] + y);
-        }
-#pragma unroll
-    for (int len = 1; len < NS; len <<= 1)
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-            if (!(s & len))
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float p = x[s][e], q = x[s + len][e];
-                    x[s][e] = p + q;
-                    x[s + len][e] = p - q;
-                }
-
-    const float knorm = (float)sqrt(ss);
-    const float inv = ss > 0.0 ? (float)(1.0 / (sqrt((double)D) * sqrt(ss))) : 0.f;
-
-    // ------------------------------------------------------------ encode + residual
-    const float b4 = a.boundaries[4], b5 = a.boundaries[5], b6 = a.boundaries[6];
-    const float m0 = a.centroids[4], m1 = a.centroids[5], m2 = a.centroids[6], m3 = a.centroids[7];
-    uint32_t kword[NS];
-    half8_t ahi[NS], alo[NS];
-    double gg = 0.0;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        uint32_t codes = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float u = x[s][e] * inv;
-            const float av = fabsf(u);
-            const int kk = (av > b4) + (av > b5) + (av > b6);
-            const float mag = av > b6 ? m3 : (av > b5 ? m2 : (av > b4 ? m1 : m0));
-            const bool pos = u > 0.f;
-            const uint32_t idx = pos ? 4u + kk : 3u - kk;
-            const float r = u - (pos ? mag : -mag);
-            gg = fma((double)r, (double)r, gg);
-            codes |= idx << (4 * e);
-            const float rs = r * 256.f;
-            const _Float16 hi = (_Float16)rs;
-            ahi[s][e] = hi;
-            alo[s][e] = (_Float16)(rs - (float)hi);
-        }
-        kword[s] = codes;
-    }
-    gg += __shfl_xor(gg, 32);
-
-    // ------------------------------------------------------------ QJL projection (MFMA)
-    uint32_t sgn[NJ];
-#pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) {
-        f32x16_t acc = {};
-        const uint16_t *srow = a.S + (int64_t)(jt * 32 + m) * D + 8 * h;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const half8_t bf = *reinterpret_cast<const half8_t *>(srow + 16 * s);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[s], bf, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[s], bf, acc, 0, 0, 0);
-        }
-        // accumulator register r of lane l holds column l % 32 of row 8 (r/4) + 4 (l/32) + r%4
-        uint32_t w = 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const uint64_t bal = __ballot(acc[r] >= 0.f);
-            const int tok = 8 * (r >> 2) + (r & 3);
-            if (m == tok) w = (uint32_t)bal;
-            if (m == tok + 4) w = (uint32_t)(bal >> 32);
-        }
-        sgn[jt] = w;
-    }
-
-    // ------------------------------------------------------------ key words + store
-    // word 2s+h holds coordinates 16s+8h..+7 as nibbles (code | sign << 3); its 8 sign
-    // bits are byte (2s+h) mod 4 of the projection tile's sign word, spread to bit 4e+3
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const uint32_t byte_pos = (uint32_t)(2 * (s & 1) + h);
-        uint32_t zb = (sgn[s >> 1] >> (8 * byte_pos)) & 0xffu;
-        zb = (zb | (zb << 12)) & 0x000f000fu;
-        zb = (zb | (zb << 6)) & 0x03030303u;
-        zb = (zb | (zb << 3)) & 0x11111111u;
-        kword[s] |= zb << 3;
-    }
-    uint32_t outw[NS];
-#pragma unroll
-    for (int i = 0; i < NS / 2; ++i) {
-        const uint32_t send = h ? kword[i] : kword[NS / 2 + i];
-        const uint32_t recv = __shfl_xor(send, 32);
-        outw[2 * i] = h ? recv : kword[i];
-        outw[2 * i + 1] = h ? kword[NS / 2 + i] : recv;
-    }
-    if (valid) {
-        uint4 *dstk = reinterpret_cast<uint4 *>(a.kw + rec * (D / 8) + h * NS);
-#pragma unroll
-        for (int i = 0; i < NS / 4; ++i)
-            dstk[i] = make_uint4(outw[4 * i], outw[4 * i + 1], outw[4 * i + 2], outw[4 * i + 3]);
-        if (h == 0) *reinterpret_cast<float2 *>(a.kn + rec * 2) = make_float2(knorm, (float)sqrt(gg));
-    }
-
-    // ------------------------------------------------------------ values
-    float vv[NS][8];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        if (valid) {
-            load8(a.v, in_off + 16 * s, vv[s], Tag{});
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vv[s][e] = 0.f;
-        }
-    }
-    uint32_t vcode[NS];  // VB=4: full word 2s+h; VB=2: 16-bit half of word s at bit 0
-    uint16_t scb[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        float am = 0.f;
-#pragma unroll
-        for (int s = 2 * g; s < 2 * g + 2; ++s)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(vv[s][e]));
-        am = fmaxf(am, __shfl_xor(am, 32));
-        const _Float16 sh = (_Float16)(am * (1.0f / HALF));
-        const float sc = (float)sh;
-        scb[g] = __builtin_bit_cast(uint16_t, sh);
-        const float rinv = sc > 0.f ? 1.0f / sc : 0.f;
-#pragma unroll
-        for (int s = 2 * g; s < 2 * g + 2; ++s) {
-            uint32_t cw = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float val = vv[s][e];
-                float q = floorf(val * rinv);
-                if ((q + 1.f) * sc <= val) q += 1.f;
-                else if (q * sc > val) q -= 1.f;
-                q = fminf(fmaxf(q, (float)-HALF), (float)(HALF - 1));
-                const uint32_t code = sc > 0.f ? (uint32_t)((int)q + HALF) : (uint32_t)HALF;
-                cw |= code << (VB * e);
-            }
-            vcode[s] = cw;
-        }
-    }
-    uint32_t vout[NS];
-    if constexpr (VB == 2) {
-#pragma unroll
-        for (int i = 0; i < NS / 2; ++i) {
-            const uint32_t send = h ? (vcode[i] << 16) : vcode[NS / 2 + i];
-            const uint32_t recv = __shfl_xor(send, 32);
-            vout[i] = h ? ((vcode[NS / 2 + i] << 16) | recv) : (vcode[i] | recv);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < NS / 2; ++i) {
-            const uint32_t send = h ? vcode[i] : vcode[NS / 2 + i];
-            const uint32_t recv = __shfl_xor(send, 32);
-            vout[2 * i] = h ? recv : vcode[i];
-            vout[2 * i + 1] = h ? vcode[NS / 2 + i] : recv;
-        }
-    }
-    if (valid) {
-        constexpr int VW = VB * D / 32;  // value words per record
-        constexpr int PER = VW / 2;      // words stored by each lane of the pair
-        uint4 *dstv = reinterpret_cast<uint4 *>(a.vw + rec * VW + h * PER);
-#pragma unroll
-        for (int i = 0; i < PER / 4; ++i)
-            dstv[i] = make_uint4(vout[4 * i], vout[4 * i + 1], vout[4 * i + 2], vout[4 * i + 3]);
-        if (h == 0) {
-            if constexpr (NG == 4) {
-                *reinterpret_cast<uint2 *>(a.vs + rec * NG) =
-                    make_uint2(scb[0] | ((uint32_t)scb[1] << 16), scb[2] | ((uint32_t)scb[3] << 16));
+        for (int s = 0; s < S::NS; ++s) {
+            if constexpr (kF32) {
+                const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(a.k) + in_off + S::K * s);
+                const uint4 x0 = p[0], x1 = p[1];
+                raw[s][0] = x0.x; raw[s][1] = x0.y; raw[s][2] = x0.z; raw[s][3] = x0.w;
+                raw[s][4] = x1.x; raw[s][5] = x1.y; raw[s][6] = x1.z; raw[s][7] = x1.w;
             } else {
-                *reinterpret_cast<uint4 *>(a.vs + rec * NG) =
-                    make_uint4(scb[0] | ((uint32_t)scb[1] << 16), scb[2] | ((uint32_t)scb[3] << 16),
-                               scb[4] | ((uint32_t)scb[5] << 16), scb[6] | ((uint32_t)scb[7] << 16));
+                const uint4 x =
+                    *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + in_off + S::K * s);
+                raw[s][0] = x.x; raw[s][1] = x.y; raw[s][2] = x.z; raw[s][3] = x.w;
             }
+        }
+    };
+
+    // rotation A fragments: lane (row i = n, group g), element e <-> k = 8 g + e, the two
+    // variants v of (-1)^popcount(i & k) (R = 32: times (-1)^(i_4 v); R = 16: (-1)^(k_4 v))
+    u32x4_t hf[2];
+    {
+        const uint32_t one = kF16 ? 0x3C00u : 0x3F80u;
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t pair = 0;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int k = 8 * g + 2 * w + hh;
+                    const int par = __builtin_popcount(n & k & 15) +
+                                    (R == 32 ? ((n >> 4) & 1) * v : ((k >> 4) & 1) * v);
+                    pair |= (one | ((uint32_t)(par & 1) << 15)) << (16 * hh);
+                }
+                hf[v][w] = pair;
+            }
+    }
+    const uint32_t K4 = __float_as_uint(256.f * a.boundaries[4]);
+    const uint32_t K5 = __float_as_uint(256.f * a.boundaries[5]);
+    const uint32_t K6 = __float_as_uint(256.f * a.boundaries[6]);
+    float M0 = 256.f * a.centroids[4], M1 = 256.f * a.centroids[5];
+    float M2 = 256.f * a.centroids[6], M3 = 256.f * a.centroids[7];
+    // keep the scaled centroids as values (otherwise the scaling is re-done per element)
+    asm volatile("" : "+v"(M0), "+v"(M1), "+v"(M2), "+v"(M3));
+
+    int64_t base = (int64_t)blockIdx.x * kKeyGroupWaves<D> * R;
+    for (; base < a.n_rows; base += stride) {
+        const int64_t row = base + my;
+        load_raw(row);
+        int64_t rec = -1;  // destination record, -1 past the last row
+        if (row < a.n_rows) {
+            int64_t sl, t;
+            split_row(row, a.n_tokens, inv_tok, sl, t);
+            rec = sl * a.cap + a.dst_offset + t;
+        }
+
+        // ---- |k|^2 in fp32 (products of 16-bit inputs are exact; several partial sums)
+        float ssp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < S::NS; ++s)
+#pragma unroll
+            for (int w = 0; w < RAWW; ++w) {
+                if constexpr (kF32) {
+                    const float x = __uint_as_float(raw[s][w]);
+                    ssp[w & 3] = fmaf(x, x, ssp[w & 3]);
+                } else if constexpr (kF16) {
+                    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+                    const h2_t x = __builtin_bit_cast(h2_t, raw[s][w]);
+                    ssp[w] = __builtin_amdgcn_fdot2(x, x, ssp[w], false);
+                } else {
+                    typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+                    const b2_t x = __builtin_bit_cast(b2_t, raw[s][w]);
+                    ssp[w] = __builtin_amdgcn_fdot2_f32_bf16(x, x, ssp[w], false);
+                }
+            }
+        float ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);
+#pragma unroll
+        for (int o = R; o < 64; o <<= 1) ss += __shfl_xor(ss, o);
+
+        // ---- rotation on the matrix cores: y = H (sigma o x), fp32
+        acc_t<R> y[S::NJ];
+#pragma unroll
+        for (int jt = 0; jt < S::NJ; ++jt) y[jt] = acc_t<R>{};
+#pragma unroll
+        for (int s = 0; s < S::NS; ++s) {
+            const u32x4_t m4 = *reinterpret_cast<const u32x4_t *>(&smask[(S::K * s + 8 * g) / 2]);
+            if constexpr (kF32) {
+                u32x4_t bh, bm, bl;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    uint16_t h0, m0, l0, h1, m1, l1;
+                    split3_bf16(__uint_as_float(raw[s][2 * w] ^ (m4[w] << 16)), h0, m0, l0);
+                    split3_bf16(__uint_as_float(raw[s][2 * w + 1] ^ (m4[w] & 0x80000000u)), h1, m1, l1);
+                    bh[w] = h0 | ((uint32_t)h1 << 16);
+                    bm[w] = m0 | ((uint32_t)m1 << 16);
+                    bl[w] = l0 | ((uint32_t)l1 << 16);
+                }
+#pragma unroll
+                for (int jt = 0; jt < S::NJ; ++jt) {
+                    const u32x4_t A0 = hf[h_variant<D>(jt, s)];
+                    const u32x4_t A = h_negated<D>(jt, s) ? (A0 ^ 0x80008000u) : A0;
+                    y[jt] = mfma_in<R, bf16_tag>(A, bh, y[jt]);
+                    y[jt] = mfma_in<R, bf16_tag>(A, bm, y[jt]);
+                    y[jt] = mfma_in<R, bf16_tag>(A, bl, y[jt]);
+                }
+            } else {
+                u32x4_t b;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) b[w] = raw[s][w] ^ m4[w];
+#pragma unroll
+                for (int jt = 0; jt < S::NJ; ++jt) {
+                    const u32x4_t A0 = hf[h_variant<D>(jt, s)];
+                    const u32x4_t A = h_negated<D>(jt, s) ? (A0 ^ 0x80008000u) : A0;
+                    y[jt] = mfma_in<R, Tag>(A, b, y[jt]);
+                }
+            }
+        }
+
+        // ---- encode: u' = 2^8 u; key = |u'| as an integer, +1 when u' <= 0 so that
+        //      equality with a boundary falls in the lower cell on the negative side too
+        const float knorm = sqrtf(ss);
+        const float inv256 = ss > 0.f ? 256.f / sqrtf((float)D * ss) : 0.f;
+        uint32_t P[S::NP];  // nibble half-words: slot f at bit 4 (f & 7) of P[f >> 3]
+#pragma unroll
+        for (int p = 0; p < S::NP; ++p) P[p] = 0;
+        float ggp[4] = {0.f, 0.f, 0.f, 0.f};
+        // negated scaled residual -r' as fp16 hi + lo; projection k-step q = slots 8q .. 8q+7
+        u32x4_t rhi[S::NQ], rlo[S::NQ];
+        typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+        typedef float f2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int f2 = 0; f2 < S::NV; f2 += 2) {
+            float nr[2];
+#pragma unroll
+            for (int o = 0; o < 2; ++o) {
+                const int f = f2 + o;
+                const float yv = y[f / S::RPT][f % S::RPT];
+                const float u = yv * inv256;
+                const bool nonpos = !(u > 0.f);
+                const uint32_t key = (__float_as_uint(u) & 0x7fffffffu) + (nonpos ? 1u : 0u);
+                const bool c4 = key > K4, c5 = key > K5, c6 = key > K6;
+                const uint32_t tt = 4u + (uint32_t)c4 + (uint32_t)c5 + (uint32_t)c6;
+                const float mag = c6 ? M3 : (c5 ? M2 : (c4 ? M1 : M0));
+                // -r' = c - u': +mag - u' above zero, -mag - u' at or below
+                nr[o] = fmaf(-yv, inv256, nonpos ? -mag : mag);
+                uint32_t idx = tt ^ (nonpos ? 7u : 0u);
+                // materialise the index now: the compare masks die here instead of being
+                // kept (in scalar registers) until the nibble word is assembled
+                asm volatile("" : "+v"(idx));
+                P[f >> 3] |= idx << (4 * (f & 7));
+                ggp[f & 3] = fmaf(nr[o], nr[o], ggp[f & 3]);
+            }
+            const h2_t hi = __builtin_convertvector((f2_t){nr[0], nr[1]}, h2_t);
+            h2_t lo;
+            lo[0] = (_Float16)fmaf(-(float)hi[0], 1.0f, nr[0]);
+            lo[1] = (_Float16)fmaf(-(float)hi[1], 1.0f, nr[1]);
+            rhi[f2 >> 3][(f2 & 7) >> 1] = __builtin_bit_cast(uint32_t, hi);
+            rlo[f2 >> 3][(f2 & 7) >> 1] = __builtin_bit_cast(uint32_t, lo);
+            // one pair at a time: interleaving many elements only piles up compare masks
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        float gg = (ggp[0] + ggp[1]) + (ggp[2] + ggp[3]);
+#pragma unroll
+        for (int o = R; o < 64; o <<= 1) gg += __shfl_xor(gg, o);
+
+        // ---- the next tile's raw keys are loaded during the projection and the stores
+
+        // ---- QJL on the matrix cores: D[j][token] = -sum_c S[j][c] r'[c]; lane (n, g)
+        //      receives the projections j = slot_coord(f, g) of its own coordinates
+#pragma unroll
+        for (int jt2 = 0; jt2 < S::NJ; ++jt2) {
+            __builtin_amdgcn_sched_barrier(0);
+            acc_t<R> acc = acc_t<R>{};
+            const uint16_t *srow = sS + (R * jt2 + n) * kSRow<D>;
+#pragma unroll
+            for (int q = 0; q < S::NQ; ++q) {
+                const uint2 s0 = *reinterpret_cast<const uint2 *>(srow + slot_coord<D>(8 * q, g));
+                const uint2 s1 = *reinterpret_cast<const uint2 *>(srow + slot_coord<D>(8 * q + 4, g));
+                const u32x4_t A = {s0.x, s0.y, s1.x, s1.y};
+                acc = mfma_f16<R>(A, rhi[q], acc);
+                acc = mfma_f16<R>(A, rlo[q], acc);
+            }
+#pragma unroll
+            for (int r = 0; r < S::RPT; ++r) {
+                const int f = jt2 * S::RPT + r;
+                const int pos = 4 * (f & 7) + 3;
+                // the accumulator holds -(S r')_j: its sign bit is set exactly when the
+                // projection is positive (or a zero came out as -0)
+                P[f >> 3] |= (__float_as_uint(acc[r]) >> (31 - pos)) & (1u << pos);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- assemble key words: half-words of word w live in lanes g (even) and g ^ 1
+        uint32_t outw[S::NP];
+#pragma unroll
+        for (int p = 0; p < S::NP / 2; ++p) {
+            const uint32_t x = P[p], z = P[p + S::NP / 2];
+            uint32_t xs, zs;
+            if constexpr (R == 32) {
+                const auto pr = __builtin_amdgcn_permlane32_swap(x, z, false, false);
+                xs = pr[0];
+                zs = pr[1];
+            } else {
+                const auto pr = __builtin_amdgcn_permlane16_swap(x, z, false, false);
+                xs = pr[0];
+                zs = pr[1];
+            }
+            // even lanes now hold (own, partner) halves of P[p], odd lanes (partner, own) of
+            // P[p + NP/2]: low half-words from xs, high half-words from zs
+            outw[2 * p] = __builtin_amdgcn_perm(zs, xs, 0x05040100u);
+            outw[2 * p + 1] = __builtin_amdgcn_perm(zs, xs, 0x07060302u);
+        }
+        if (rec >= 0) {
+            uint32_t *dst = a.kw + rec * S::KW;
+            const int odd = g & 1;
+            if constexpr (R == 32) {
+                // slots of P[p] cover words 2p, 2p+1; even lanes store words 0..7, odd 8..15
+                uint4 *d4 = reinterpret_cast<uint4 *>(dst + 8 * odd);
+                d4[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+                d4[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
+            } else {
+#pragma unroll
+                for (int p = 0; p < S::NP / 2; ++p) {
+                    const int pp = p + odd * (S::NP / 2);
+                    dst[slot_coord<D>(8 * pp, g) >> 3] = outw[2 * p];
+                    dst[slot_coord<D>(8 * pp + 4, g) >> 3] = outw[2 * p + 1];
+                }
+            }
+            if (g == 0)
+                *reinterpret_cast<float2 *>(a.kn + rec * 2) = make_float2(knorm, sqrtf(gg) * (1.0f / 256.f));
         }
     }
 }
 
+// ------------------------------------------------------------------------------ values
+// Codes of one group: code = clamp(floor(v / s), -HALF, HALF - 1) + HALF, floor exact.
+// Fast form (16-bit inputs, normal fp16 s): v / s is then either an integer or at least
+// 2^-11 away from every integer (or inside (-1, 1)), so floor(p + |p| 2^-20), p = v * (1/s)
+// rounded, is exact: the nudge lifts exact integers that rounding pushed below, and is far
+// too small to cross a non-integer.  Otherwise the estimate is corrected with exact
+// products (q + 1) s and q s.
+template <int VB, bool Exact>
+__device__ __forceinline__ void quant_group(const float (&v)[32], float sc, uint32_t (&wd)[VB]) {
+    constexpr int HALF = 1 << (VB - 1);
+    constexpr int PER = 32 / VB;  // codes per word
+    const float rinv = 1.0f / sc;
+    const float nudge = rinv * 0x1p-20f;
+    // code offset HALF in every field
+    constexpr uint32_t kOff = VB == 2 ? 0xAAAAAAAAu : 0x88888888u;
+#pragma unroll
+    for (int w = 0; w < VB; ++w) {
+        uint32_t acc = kOff;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const float x = v[w * PER + e];
+            float q;
+            if constexpr (Exact) {
+                q = floorf(x * rinv);
+                if ((q + 1.f) * sc <= x) q += 1.f;
+                else if (q * sc > x) q -= 1.f;
+            } else {
+                q = floorf(fmaf(fabsf(x), nudge, x * rinv));
+            }
+            q = fminf(fmaxf(q, (float)-HALF), (float)(HALF - 1));
+            acc += (uint32_t)(int)q << (VB * e);
+        }
+        wd[w] = acc;
+    }
+}
+
 template <typename Tag, int D, int VB>
-static hipError_t launch_quantize_t(const QuantArgs &a, hipStream_t st) {
-    const int64_t waves = (a.n_rows + 31) / 32;
-    const int64_t blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((k_quantize<Tag, D, VB>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-    return hipGetLastError();
+__global__ __launch_bounds__(256) void k_quant_values(QuantArgs a) {
+    constexpr int NG = D / 32;
+    constexpr int HALF = 1 << (VB - 1);
+    constexpr int VW = VB * D / 32;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid / NG;
+    const int grp = (int)(gid - row * NG);
+    if (row >= a.n_rows) return;
+    int64_t sl, t;
+    split_row(row, a.n_tokens, 1.0 / (double)a.n_tokens, sl, t);
+    const int64_t in_off = sl * a.in_slice_stride + t * D + 32 * grp;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float tmp[8];
+        load8(a.v, in_off + 8 * i, tmp, Tag{});
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[8 * i + e] = tmp[e];
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) am = fmaxf(am, fabsf(v[e]));
+    const _Float16 sh = (_Float16)(am * (1.0f / HALF));
+    const float sc = (float)sh;
+    uint32_t wd[VB];
+    if (sc == 0.f) {
+#pragma unroll
+        for (int w = 0; w < VB; ++w) wd[w] = VB == 2 ? 0xAAAAAAAAu : 0x88888888u;
+    } else if (std::is_same_v<Tag, f32_tag> || sc < 0x1p-14f) {
+        quant_group<VB, true>(v, sc, wd);
+    } else {
+        quant_group<VB, false>(v, sc, wd);
+    }
+    const int64_t rec = sl * a.cap + a.dst_offset + t;
+    uint32_t *dst = a.vw + rec * VW + VB * grp;
+    if constexpr (VB == 2) *reinterpret_cast<uint2 *>(dst) = make_uint2(wd[0], wd[1]);
+    else *reinterpret_cast<uint4 *>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    a.vs[rec * NG + grp] = __builtin_bit_cast(uint16_t, sh);
+}
+
+// ------------------------------------------------------------------------------ launch
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+        cus[dev] = c;
+    }
+    return cus[dev];
+}
+
+template <typename Tag, int D>
+static void launch_keys_t(const QuantArgs &a, hipStream_t st) {
+    const int64_t rows_per_group = (int64_t)kKeyGroupWaves<D> * KeyShape<D>::R;
+    const int64_t groups = (a.n_rows + rows_per_group - 1) / rows_per_group;
+    const int64_t resident = (int64_t)device_cus() * kKeyGroupsPerCU<D>;
+    const int64_t grid = groups < resident ? groups : resident;
+    hipLaunchKernelGGL((k_quant_keys<Tag, D>), dim3((unsigned)grid), dim3(64 * kKeyGroupWaves<D>), 0, st, a);
+}
+
+template <typename Tag, int D, int VB>
+static void launch_values_t(const QuantArgs &a, hipStream_t st) {
+    const int64_t lanes = a.n_rows * (D / 32);
+    const int64_t blocks = (lanes + 255) / 256;
+    hipLaunchKernelGGL((k_quant_values<Tag, D, VB>), dim3((unsigned)blocks), dim3(256), 0, st, a);
 }
 
 template <typename Tag>
 static hipError_t launch_quantize_d(int d, int vb, const QuantArgs &a, hipStream_t st) {
-    if (d == 128 && vb == 2) return launch_quantize_t<Tag, 128, 2>(a, st);
-    if (d == 128 && vb == 4) return launch_quantize_t<Tag, 128, 4>(a, st);
-    if (d == 256 && vb == 2) return launch_quantize_t<Tag, 256, 2>(a, st);
-    return launch_quantize_t<Tag, 256, 4>(a, st);
+    if (d == 128) {
+        launch_keys_t<Tag, 128>(a, st);
+        if (vb == 2) launch_values_t<Tag, 128, 2>(a, st);
+        else launch_values_t<Tag, 128, 4>(a, st);
+    } else {
+        launch_keys_t<Tag, 256>(a, st);
+        if (vb == 2) launch_values_t<Tag, 256, 2>(a, st);
+        else launch_values_t<Tag, 256, 4>(a, st);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize(int d, int vb, tq_dtype dt, const QuantArgs &a, hipStream_t st) {
