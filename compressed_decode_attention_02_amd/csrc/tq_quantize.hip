@@ -118,16 +118,19 @@ __device__ __forceinline__ void split3_bf16(float x, uint16_t &hi, uint16_t &mid
 
 // ------------------------------------------------------------------------------ keys
 // Launch shape: persistent workgroups that loop over tiles of rows (the S copy in LDS is
-// made once per workgroup); latency is hidden by the other waves of the SIMD (a register
-// prefetch of the next tile does not fit the budget).  d = 128: 4-wave groups, 3 per CU; d = 256:
-// 12-wave groups, one per CU (sharing one 130 KB LDS copy of S).  Register budget: 3 waves
-// per SIMD (<= 168 VGPRs).
+// made once per workgroup); latency is hidden by the other waves of the SIMD (3 per SIMD,
+// <= 168 VGPRs).  d = 128: 4-wave groups, 3 per CU (33 KB of LDS each); d = 256: 12-wave
+// groups, one per CU (sharing one 130 KB LDS copy of S).  Measured alternative: 16-token
+// waves at d = 128 (5 per SIMD) are slower -- each S fragment read from LDS then serves
+// half as many tokens.
 template <int D>
 constexpr int kKeyGroupWaves = D == 128 ? 4 : 12;
 template <int D>
 constexpr int kKeyGroupsPerCU = D == 128 ? 3 : 1;
-// S rows in LDS are padded by 8 bytes: the 8-byte A-fragment reads of 32 consecutive rows
-// at one column then fall into distinct banks
+template <int D>
+constexpr int kKeyWavesPerSimd = 3;
+// S rows in LDS are padded by 8 bytes (2 banks): the 8-byte A-fragment reads of 32
+// consecutive rows at one column then fall into distinct banks
 template <int D>
 constexpr int kSRow = D + 4;  // halfwords
 
@@ -148,7 +151,8 @@ __device__ __forceinline__ void split_row(int64_t r, int64_t n_tok, double inv, 
 }
 
 template <typename Tag, int D>
-__global__ __launch_bounds__(64 * kKeyGroupWaves<D>) __attribute__((amdgpu_waves_per_eu(3, 3)))
+__global__ __launch_bounds__(64 * kKeyGroupWaves<D>)
+__attribute__((amdgpu_waves_per_eu(kKeyWavesPerSimd<D>, kKeyWavesPerSimd<D>)))
 void k_quant_keys(QuantArgs a) {
     using S = KeyShape<D>;
     constexpr int R = S::R;
@@ -225,9 +229,12 @@ void k_quant_keys(QuantArgs a) {
     const uint32_t K4 = __float_as_uint(256.f * a.boundaries[4]);
     const uint32_t K5 = __float_as_uint(256.f * a.boundaries[5]);
     const uint32_t K6 = __float_as_uint(256.f * a.boundaries[6]);
-    float M0 = 256.f * a.centroids[4], M1 = 256.f * a.centroids[5];
-    float M2 = 256.f * a.centroids[6], M3 = 256.f * a.centroids[7];
-    // keep the scaled centroids as values (otherwise the scaling is re-done per element)
+    // scaled positive centroids 2^8 c[4+k], tagged with their index 4 + k in the three low
+    // mantissa bits (the stored centroids are binary16 values, so those bits are zero)
+    float M0 = __uint_as_float((__float_as_uint(256.f * a.centroids[4]) & ~7u) | 4u);
+    float M1 = __uint_as_float((__float_as_uint(256.f * a.centroids[5]) & ~7u) | 5u);
+    float M2 = __uint_as_float((__float_as_uint(256.f * a.centroids[6]) & ~7u) | 6u);
+    float M3 = __uint_as_float((__float_as_uint(256.f * a.centroids[7]) & ~7u) | 7u);
     asm volatile("" : "+v"(M0), "+v"(M1), "+v"(M2), "+v"(M3));
 
     int64_t base = (int64_t)blockIdx.x * kKeyGroupWaves<D> * R;
@@ -316,35 +323,44 @@ void k_quant_keys(QuantArgs a) {
         typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
         typedef float f2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-        for (int f2 = 0; f2 < S::NV; f2 += 2) {
-            float nr[2];
+        for (int f4 = 0; f4 < S::NV; f4 += 4) {
+            float nr[4];
+            uint32_t idx[4];
 #pragma unroll
-            for (int o = 0; o < 2; ++o) {
-                const int f = f2 + o;
+            for (int o = 0; o < 4; ++o) {
+                const int f = f4 + o;
                 const float yv = y[f / S::RPT][f % S::RPT];
                 const float u = yv * inv256;
                 const bool nonpos = !(u > 0.f);
                 const uint32_t key = (__float_as_uint(u) & 0x7fffffffu) + (nonpos ? 1u : 0u);
                 const bool c4 = key > K4, c5 = key > K5, c6 = key > K6;
-                const uint32_t tt = 4u + (uint32_t)c4 + (uint32_t)c5 + (uint32_t)c6;
-                const float mag = c6 ? M3 : (c5 ? M2 : (c4 ? M1 : M0));
-                // -r' = c - u': +mag - u' above zero, -mag - u' at or below
-                nr[o] = fmaf(-yv, inv256, nonpos ? -mag : mag);
-                uint32_t idx = tt ^ (nonpos ? 7u : 0u);
-                // materialise the index now: the compare masks die here instead of being
-                // kept (in scalar registers) until the nibble word is assembled
-                asm volatile("" : "+v"(idx));
-                P[f >> 3] |= idx << (4 * (f & 7));
-                ggp[f & 3] = fmaf(nr[o], nr[o], ggp[f & 3]);
+                // signed tagged centroid: sign = (u <= 0), low bits = 4 + #{boundaries passed}
+                const float mt = c6 ? M3 : (c5 ? M2 : (c4 ? M1 : M0));
+                const uint32_t sb = __float_as_uint(nonpos ? -mt : mt);
+                // index: 4 + k above zero, 3 - k = (4 + k) ^ 7 at or below
+                idx[o] = (sb ^ (uint32_t)((int32_t)sb >> 31)) & 7u;
+                // -r' = c[idx] - u'
+                nr[o] = fmaf(-yv, inv256, __uint_as_float(sb & ~7u));
+                ggp[o] = fmaf(nr[o], nr[o], ggp[o]);
             }
-            const h2_t hi = __builtin_convertvector((f2_t){nr[0], nr[1]}, h2_t);
-            h2_t lo;
-            lo[0] = (_Float16)fmaf(-(float)hi[0], 1.0f, nr[0]);
-            lo[1] = (_Float16)fmaf(-(float)hi[1], 1.0f, nr[1]);
-            rhi[f2 >> 3][(f2 & 7) >> 1] = __builtin_bit_cast(uint32_t, hi);
-            rlo[f2 >> 3][(f2 & 7) >> 1] = __builtin_bit_cast(uint32_t, lo);
-            // one pair at a time: interleaving many elements only piles up compare masks
-            __builtin_amdgcn_sched_barrier(0);
+            // materialise the four indices here: the compare masks die now instead of being
+            // kept (in scalar registers) until the nibble word is assembled
+            asm volatile("" : "+v"(idx[0]), "+v"(idx[1]), "+v"(idx[2]), "+v"(idx[3]));
+#pragma unroll
+            for (int o = 0; o < 4; ++o) P[(f4 + o) >> 3] |= idx[o] << (4 * ((f4 + o) & 7));
+#pragma unroll
+            for (int o = 0; o < 4; o += 2) {
+                const int f2 = f4 + o;
+                const h2_t hi = __builtin_convertvector((f2_t){nr[o], nr[o + 1]}, h2_t);
+                const uint32_t hb = __builtin_bit_cast(uint32_t, hi);
+                // lo = fp16(-r' - hi), one rounding of an exact difference, per half
+                uint32_t lb;
+                asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=&v"(lb) : "v"(hb), "v"(nr[o]));
+                asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+                    : "+v"(lb) : "v"(hb), "v"(nr[o + 1]));
+                rhi[f2 >> 3][(f2 & 7) >> 1] = hb;
+                rlo[f2 >> 3][(f2 & 7) >> 1] = lb;
+            }
         }
         float gg = (ggp[0] + ggp[1]) + (ggp[2] + ggp[3]);
 #pragma unroll
