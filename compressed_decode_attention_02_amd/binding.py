@@ -227,9 +227,9 @@ def tq_decode_attention(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv
 
 
 def new_workspace(cfg, batch: int, n_q_heads: int, n_kv_heads: int, max_context: int, device="cuda"):
-    """Zero-filled decode workspace of the size tq_decode_workspace_bytes reports."""
+    """Decode workspace (scratch) of the size tq_decode_workspace_bytes reports."""
     import torch
     n = tq_decode_workspace_bytes(cfg, batch, n_q_heads, n_kv_heads, max_context)
     if n == 0:
         raise TqError("tq_decode_workspace_bytes", TQ_ERR_INVALID_ARG)
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)

@@ -10,8 +10,9 @@
 
 namespace {
 
-constexpr int64_t kMinSplitTokens = 1024;  // at least four 256-token chunks per split
-constexpr int64_t kDecodeTargetWgs = 512;  // about two workgroups per CU
+constexpr int64_t kSplitQuantum = 128;     // tokens per pass of a split's four waves (4 x 32)
+constexpr int64_t kMinSplitTokens = 256;   // at least two blocks per wave
+constexpr int64_t kDecodeTargetWgs = 512;  // about two workgroups per CU (more splits cost more in the merge)
 constexpr int64_t kMaxSplits = 255;        // the merge keeps one weight per split (+ ring) in LDS
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -32,18 +33,26 @@ int64_t decode_splits(int64_t slices, int64_t n_packed) {
     return std::min({by_tokens, want, kMaxSplits});
 }
 
+// tokens per split: a whole number of four-wave passes; then as few splits as cover n_packed
+void split_shape(int64_t slices, int64_t n_packed, int64_t &n_split, int64_t &per_split) {
+    const int64_t s0 = decode_splits(slices, n_packed);
+    per_split = (n_packed + s0 - 1) / s0;
+    per_split = (per_split + kSplitQuantum - 1) / kSplitQuantum * kSplitQuantum;
+    n_split = (n_packed + per_split - 1) / per_split;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct DecodeLayout {
-    size_t prep, partial, tickets, total;
+    size_t prep, partial, partial_ml, total;
 };
 
 DecodeLayout decode_layout(int d, int64_t batch, int64_t hq, int64_t hkv, int64_t n_split) {
     DecodeLayout L;
     L.prep = 0;
     L.partial = align256(sizeof(float) * (size_t)(batch * hq) * (3 * d + 4));
-    L.tickets = L.partial + align256(sizeof(float) * (size_t)(batch * hq) * n_split * (d + 2));
-    L.total = L.tickets + align256(sizeof(unsigned) * (size_t)(batch * hkv));
+    L.partial_ml = L.partial + align256(sizeof(float) * (size_t)(batch * hq) * n_split * d);
+    L.total = L.partial_ml + align256(sizeof(float) * (size_t)(batch * hq) * n_split * 2);
     return L;
 }
 
@@ -160,7 +169,8 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     const int64_t slices = (int64_t)batch * n_kv_heads;
     // packed splits, plus one split for the ring; an empty context still runs one (empty)
     // split so that the output is written
-    const int64_t n_split = n_packed > 0 ? decode_splits(slices, n_packed) : (n_ring > 0 ? 0 : 1);
+    int64_t n_split = n_ring > 0 ? 0 : 1, per_split = 0;
+    if (n_packed > 0) split_shape(slices, n_packed, n_split, per_split);
     const int64_t n_total = n_split + (n_ring > 0 ? 1 : 0);
     const DecodeLayout L = decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_total);
     if (workspace_bytes < L.total) return TQ_ERR_WORKSPACE;
@@ -189,11 +199,11 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     a.hkv = n_kv_heads;
     a.n_split = (int)n_split;
     a.n_split_total = (int)n_total;
-    a.per_split = n_packed > 0 ? (n_packed + n_split - 1) / n_split : 0;
+    a.per_split = per_split;
     a.scale = softmax_scale;
     a.out = out;
     a.prep = reinterpret_cast<float *>(ws + L.prep);
     a.partial = reinterpret_cast<float *>(ws + L.partial);
-    a.tickets = reinterpret_cast<unsigned *>(ws + L.tickets);
+    a.partial_ml = reinterpret_cast<float *>(ws + L.partial_ml);
     return hip_status(tq::launch_decode(cfg->head_dim, cfg->value_bits, G, q_dtype, a, (hipStream_t)stream));
 }

@@ -34,7 +34,6 @@ namespace tq {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBlock = 32;       // tokens per wave iteration
-constexpr int kLutCopies = 32;   // copies of the byte -> centroid-pair table (one per LDS bank)
 constexpr int kRingChunk = 256;  // ring tokens per pass of the ring split
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -113,9 +112,8 @@ __global__ __launch_bounds__(D) void k_decode_prep(DecodeArgs a) {
 template <int D, int VB, int G>
 struct DecodeShape {
     static constexpr int KW = D / 8;          // key words per token
-    static constexpr int NKS = D / 32;        // score k-steps per part (one key word per lane group)
+    static constexpr int NKS = D / 32;        // score k-steps per tile (one key word per lane group)
     static constexpr int VW = VB * D / 32;    // value words per token
-    static constexpr int VWP = VW + 2;        // padded LDS row (row groups of 8 hit distinct banks)
     static constexpr int NG = D / 32;         // value groups
     static constexpr int NT = D / 16;         // value tiles; row m owns coordinates m*NT .. m*NT+NT-1
     static constexpr int H = VB * NT / 16;    // halfwords of codes per row and token (1, 2 or 4)
@@ -123,24 +121,39 @@ struct DecodeShape {
     static constexpr int NPASS = (NCOL + 15) / 16;
     static constexpr int HALF = 1 << (VB - 1);
     static constexpr int PARTS = kThreads / D;  // ring split: token partitions per coordinate
+    // per-wave staging buffer of one 32-token block (bytes): key words, norms, value words
+    // (records in slot order 4 (t % 8) + t / 8, so that the code reads of four lane groups
+    // hit different banks), scales
+    static constexpr int KW_B = kBlock * KW * 4;
+    static constexpr int KN_B = kBlock * 8;
+    static constexpr int VW_B = kBlock * VW * 4;
+    static constexpr int VS_B = kBlock * NG * 2;
+    static constexpr int OFF_KN = KW_B;
+    static constexpr int OFF_VW = OFF_KN + KN_B;
+    static constexpr int OFF_VS = OFF_VW + VW_B;
+    static constexpr int BUF_B = OFF_VS + VS_B;
+    // global -> LDS copies per block: 16-byte (key and value words) and 4-byte (norms, scales)
+    static constexpr int N_KW = KW_B / 1024;
+    static constexpr int N_VW = VW_B / 1024;
+    static constexpr int N_VS = VS_B / 256;
+    static constexpr int N_DMA = N_KW + 1 + N_VW + N_VS;
 };
 
 template <int D, int VB, int G>
 struct alignas(16) DecodeSmem {
     using S = DecodeShape<D, VB, G>;
-    uint32_t lut[256 * kLutCopies];
-    uint32_t val[kWaves][kBlock][S::VWP];
-    float scl[kWaves][S::NG][kBlock + 4];
+    union {
+        unsigned char stage[kWaves][2][S::BUF_B];  // packed splits: per-wave double buffer
+        struct {                                    // wave combine, ring split
+            float wo[kWaves][G][D];
+            float ring_q[G][D];
+            float ring_p[G][kRingChunk];
+        } x;
+    };
     float pb[kWaves][G][kBlock + 4];
     float corr[kWaves][G];
     float wm[kWaves][G], wl[kWaves][G];
-    float wo[kWaves][G][D];
-    float ring_q[G][D];
-    float ring_p[G][kRingChunk];
     float ring_red[kWaves * G];
-    float ml[G];
-    float merge_f[G][256];
-    unsigned ticket;
 };
 
 // block-wide reduction of G values (max or sum); every thread gets the result
@@ -168,6 +181,33 @@ __device__ __forceinline__ void block_reduce(float (&v)[G], float *scratch /* [k
     __syncthreads();
 }
 
+// ---- global -> LDS copies issued by hand, waited for with explicit counts.  M0 holds the
+//      LDS destination of the wave's 64 x 16 (or 64 x 4) bytes; every LDS read of a buffer
+//      is complete (lgkmcnt(0)) before the buffer is refilled.
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void *gptr, uint32_t lds) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// lane n16 < G receives the value of lane n16 + G of its 16-lane row (DPP row shift)
+template <int G>
+__device__ __forceinline__ float from_lane_plus_g(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 + G, 0xf,
+                                                                  0xf, true));
+}
+
 // ------------------------------------------------------------------ packed split (one wave)
 template <int D, int VB, int G>
 __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk, int b, int kvh,
@@ -177,14 +217,33 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n16 = lane & 15, q = lane >> 4;
 
-    // score B fragments, column g < G for head g: q'_g (fp16 hi + lo) for the centroid part,
-    // w_g (fp16) for the sign part.  k-step ks of lane group q covers key word
-    // w = q*NKS + ks; centroid element e is coordinate 8w+e, sign element e = 2r+h' is
-    // coordinate 8w + r + 4h' (nibbles r and r+4 of the word).
-    half8_t bm_hi[S::NKS], bm_lo[S::NKS], bq[S::NKS];
+    // centroid byte tables: v_perm with selector byte idx picks byte idx of (t*1 : t*0), so
+    // tl/th hold the low/high bytes of the eight fp16 centroids
+    uint32_t tl0 = 0, tl1 = 0, th0 = 0, th1 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t h = f32_to_f16_bits(a.centroids[i]);
+        const int sh = 8 * (i & 3);
+        if (i < 4) {
+            tl0 |= (h & 0xffu) << sh;
+            th0 |= (h >> 8) << sh;
+        } else {
+            tl1 |= (h & 0xffu) << sh;
+            th1 |= (h >> 8) << sh;
+        }
+    }
+
+    // score B fragments.  k-step ks of lane group q covers key word w = q*NKS + ks.  Centroid
+    // part: element e is coordinate 8w + {0,2,4,6,1,3,5,7}[e] (even nibbles, then odd),
+    // columns g < G hold q'_g (fp16 hi), columns G + g its lo part.  Sign part: element e is
+    // coordinate 8w + {0,4,1,5,2,6,3,7}[e], columns hold -w_g hi / lo.
+    u32x4_t bc[S::NKS], bs[S::NKS];
     {
-        const bool col = n16 < G;
-        const float *pq = a.prep + ((int64_t)b * a.hq + kvh * G + (col ? n16 : 0)) * (3 * D + 4);
+        const bool hic = n16 < G, loc = n16 >= G && n16 < 2 * G;
+        const int g = hic ? n16 : (loc ? n16 - G : 0);
+        const float *pq = a.prep + ((int64_t)b * a.hq + kvh * G + g) * (3 * D + 4);
+        constexpr int ce[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+        constexpr int se[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 #pragma unroll
         for (int ks = 0; ks < S::NKS; ++ks) {
             const int w = q * S::NKS + ks;
@@ -193,14 +252,20 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
             const float4 s0 = *reinterpret_cast<const float4 *>(pq + D + 8 * w);
             const float4 s1 = *reinterpret_cast<const float4 *>(pq + D + 8 * w + 4);
             const float vm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-            const float vq[8] = {s0.x, s1.x, s0.y, s1.y, s0.z, s1.z, s0.w, s1.w};
+            const float vs[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            uint16_t hc[8], hs[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 _Float16 h, l;
-                split_hl(col ? vm[e] : 0.f, h, l);
-                bm_hi[ks][e] = h;
-                bm_lo[ks][e] = l;
-                bq[ks][e] = (_Float16)(col ? vq[e] : 0.f);
+                split_hl(vm[ce[e]], h, l);
+                hc[e] = hic ? __builtin_bit_cast(uint16_t, h) : (loc ? __builtin_bit_cast(uint16_t, l) : 0);
+                split_hl(-vs[se[e]], h, l);
+                hs[e] = hic ? __builtin_bit_cast(uint16_t, h) : (loc ? __builtin_bit_cast(uint16_t, l) : 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bc[ks][i] = hc[2 * i] | ((uint32_t)hc[2 * i + 1] << 16);
+                bs[ks][i] = hs[2 * i] | ((uint32_t)hs[2 * i + 1] << 16);
             }
         }
     }
@@ -216,136 +281,95 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
 #pragma unroll
         for (int t = 0; t < S::NT; ++t) acc_v[p][t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     }
-    const uint32_t *lut = sm.lut + (lane & (kLutCopies - 1));
-    const int64_t rec0 = (int64_t)bk * a.cap;
 
-    // one block's global data, held in registers so that the next block's loads are in
-    // flight while the current block is computed
-    struct Blk {
-        uint32_t kw[2][S::NKS];   // key words of A row token t0 + 16 tt + n16, words q*NKS ..
-        float2 an[2];             // (norm, residual norm) of that token
-        float dn[2][4];           // norm of accumulator row token t0 + 16 tt + 4 q + i
-        uint4 vw[S::VW / 8];      // half hv of the value record of token t0 + (lane & 31)
-        uint32_t sc[S::NG / 2];   // fp16 scale pairs of token t0 + (lane & 31)
+    // ---- staging: block at token t0 into buffer bi (token indices clamped to the last
+    //      packed token, so every copy reads records of this slice)
+    const int64_t rec0 = (int64_t)bk * a.cap;
+    const uint32_t *kw_s = a.kw + rec0 * S::KW;
+    const float *kn_s = a.kn + rec0 * 2;
+    const uint32_t *vw_s = a.vw + rec0 * S::VW;
+    const uint16_t *vs_s = a.vs + rec0 * S::NG;
+    const int64_t last = a.n_packed - 1;
+    const uint32_t lds_wave = (uint32_t)(uintptr_t)&sm.stage[wave][0][0];
+    auto issue = [&](int64_t t0, int bi) {
+        const uint32_t base = lds_wave + (uint32_t)(bi * S::BUF_B);
+#pragma unroll
+        for (int i = 0; i < S::N_KW; ++i) {
+            const int c = lane + 64 * i;  // 16-byte chunk of the block's key words
+            const int64_t tok = min(t0 + c / (S::KW / 4), last);
+            dma16(kw_s + tok * S::KW + (c % (S::KW / 4)) * 4, base + 1024 * i);
+        }
+        {
+            const int64_t tok = min(t0 + (lane >> 1), last);
+            dma4(kn_s + tok * 2 + (lane & 1), base + S::OFF_KN);
+        }
+#pragma unroll
+        for (int i = 0; i < S::N_VW; ++i) {
+            const int c = lane + 64 * i;
+            const int slot = c / (S::VW / 4);
+            const int64_t tok = min(t0 + 8 * (slot & 3) + (slot >> 2), last);
+            dma16(vw_s + tok * S::VW + (c % (S::VW / 4)) * 4, base + S::OFF_VW + 1024 * i);
+        }
+#pragma unroll
+        for (int i = 0; i < S::N_VS; ++i) {
+            const int c = lane + 64 * i;  // 4-byte piece of the block's scales
+            const int64_t tok = min(t0 + c / (S::NG / 2), last);
+            dma4(vs_s + tok * S::NG + 2 * (c % (S::NG / 2)), base + S::OFF_VS + 256 * i);
+        }
     };
-    const int tl = lane & 31, hv = lane >> 5;
-    // buffer descriptors over this slice's records: 32-bit offsets, and loads past the
-    // last packed token return zeros (those rows are masked out of the softmax)
-    const int np = (int)a.n_packed;
-    const __amdgpu_buffer_rsrc_t rs_kw = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.kw + rec0 * S::KW), (short)0, np * S::KW * 4, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rs_kn = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.kn + rec0 * 2), (short)0, np * 8, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rs_vw = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.vw + rec0 * S::VW), (short)0, np * S::VW * 4, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rs_vs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.vs + rec0 * S::NG), (short)0, np * S::NG * 2, kBufferFlags);
-    auto load_blk = [&](int t0, Blk &r) {
+
+    auto process = [&](const unsigned char *buf, int64_t t0) {
+        // ---- scores: centroid and sign parts on MFMA (hi and lo parts in separate columns)
+        f32x4_t accc[2], accs[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const int tok = t0 + 16 * tt + n16;
+            accc[tt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            accs[tt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            const uint32_t *kwp = reinterpret_cast<const uint32_t *>(buf) + (16 * tt + n16) * S::KW + q * S::NKS;
+            uint32_t wds[S::NKS];
 #pragma unroll
             for (int i = 0; i < S::NKS / 4; ++i) {
-                const u32x4_t u = __builtin_amdgcn_raw_buffer_load_b128(
-                    rs_kw, (uint32_t)((tok * S::KW + q * S::NKS + 4 * i) * 4), 0, 0);
-                r.kw[tt][4 * i + 0] = u[0]; r.kw[tt][4 * i + 1] = u[1];
-                r.kw[tt][4 * i + 2] = u[2]; r.kw[tt][4 * i + 3] = u[3];
+                const u32x4_t u = *reinterpret_cast<const u32x4_t *>(kwp + 4 * i);
+                wds[4 * i] = u[0]; wds[4 * i + 1] = u[1]; wds[4 * i + 2] = u[2]; wds[4 * i + 3] = u[3];
             }
-            const u32x2_t an = __builtin_amdgcn_raw_buffer_load_b64(rs_kn, (uint32_t)(tok * 8), 0, 0);
-            r.an[tt] = make_float2(__uint_as_float(an[0]), __uint_as_float(an[1]));
-            const int tr = t0 + 16 * tt + 4 * q;  // four consecutive row tokens: 32 bytes
-            const u32x4_t d01 = __builtin_amdgcn_raw_buffer_load_b128(rs_kn, (uint32_t)(tr * 8), 0, 0);
-            const u32x4_t d23 = __builtin_amdgcn_raw_buffer_load_b128(rs_kn, (uint32_t)(tr * 8 + 16), 0, 0);
-            r.dn[tt][0] = __uint_as_float(d01[0]);
-            r.dn[tt][1] = __uint_as_float(d01[2]);
-            r.dn[tt][2] = __uint_as_float(d23[0]);
-            r.dn[tt][3] = __uint_as_float(d23[2]);
-        }
-        const int tok = t0 + tl;
 #pragma unroll
-        for (int i = 0; i < S::VW / 8; ++i) {
-            const u32x4_t u = __builtin_amdgcn_raw_buffer_load_b128(
-                rs_vw, (uint32_t)((tok * S::VW + hv * (S::VW / 2) + 4 * i) * 4), 0, 0);
-            r.vw[i] = make_uint4(u[0], u[1], u[2], u[3]);
-        }
-        if constexpr (S::NG == 4) {
-            const u32x2_t u = __builtin_amdgcn_raw_buffer_load_b64(rs_vs, (uint32_t)(tok * 8), 0, 0);
-            r.sc[0] = u[0];
-            r.sc[1] = u[1];
-        } else {
-            const u32x4_t u = __builtin_amdgcn_raw_buffer_load_b128(rs_vs, (uint32_t)(tok * S::NG * 2), 0, 0);
+            for (int ks = 0; ks < S::NKS; ++ks) {
+                const uint32_t word = wds[ks];
+                const uint32_t sel_e = word & 0x07070707u, sel_o = (word >> 4) & 0x07070707u;
+                const uint32_t le = __builtin_amdgcn_perm(tl1, tl0, sel_e);
+                const uint32_t he = __builtin_amdgcn_perm(th1, th0, sel_e);
+                const uint32_t lo = __builtin_amdgcn_perm(tl1, tl0, sel_o);
+                const uint32_t ho = __builtin_amdgcn_perm(th1, th0, sel_o);
+                const u32x4_t Ac = {__builtin_amdgcn_perm(he, le, 0x05010400u), __builtin_amdgcn_perm(he, le, 0x07030602u),
+                                    __builtin_amdgcn_perm(ho, lo, 0x05010400u), __builtin_amdgcn_perm(ho, lo, 0x07030602u)};
+                u32x4_t As;
 #pragma unroll
-            for (int i = 0; i < S::NG / 2; ++i) r.sc[i] = u[i];
-        }
-    };
-
-    // ping-pong register buffers: the loads of the block after next are issued right
-    // after a buffer is consumed, and every load is issued unconditionally (clamped to the
-    // last token) so that each wait covers exactly the buffer about to be used
-    auto process = [&](const Blk &cur, int t0) {
-        // ---- stage this block's value records and scales in the wave's LDS slots
-#pragma unroll
-        for (int i = 0; i < S::VW / 8; ++i) {
-            uint32_t *dst = &sm.val[wave][tl][hv * (S::VW / 2) + 4 * i];
-            dst[0] = cur.vw[i].x; dst[1] = cur.vw[i].y; dst[2] = cur.vw[i].z; dst[3] = cur.vw[i].w;
-        }
-        if (hv == 0) {
-#pragma unroll
-            for (int i = 0; i < S::NG / 2; ++i) {
-                sm.scl[wave][2 * i][tl] = f16_lo(cur.sc[i]);
-                sm.scl[wave][2 * i + 1][tl] = f16_hi(cur.sc[i]);
+                for (int r = 0; r < 4; ++r) As[r] = ((word << (12 - 4 * r)) & 0x80008000u) | 0x3C003C00u;
+                accc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, Ac),
+                                                                  __builtin_bit_cast(half8_t, bc[ks]), accc[tt], 0, 0, 0);
+                accs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, As),
+                                                                  __builtin_bit_cast(half8_t, bs[ks]), accs[tt], 0, 0, 0);
             }
         }
-
-        // ---- scores: centroid part and sign part in separate accumulators (4 independent
-        //      MFMA chains); the sign part's A carries (2z - 1) g_t sqrt(pi/2)/d, hi + lo
-        f32x4_t acc_m[2], acc_q[2];
-        uint32_t kg_hi[2], kg_lo[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            acc_m[tt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-            acc_q[tt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-            _Float16 h, l;
-            split_hl(-cur.an[tt].y * kQjl, h, l);  // negative: the sign bit is cleared where z = 1
-            const uint32_t hb = __builtin_bit_cast(uint16_t, h), lb = __builtin_bit_cast(uint16_t, l);
-            kg_hi[tt] = hb | (hb << 16);
-            kg_lo[tt] = lb | (lb << 16);
-        }
-#pragma unroll
-        for (int ks = 0; ks < S::NKS; ++ks) {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const uint32_t word = cur.kw[tt][ks];
-                half8_t am, aqh, aql;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t mr = lut[((word >> (8 * r)) & 0xffu) * kLutCopies];
-                    const uint32_t zs = (word << (12 - 4 * r)) & 0x80008000u;
-                    const half2_t hm = __builtin_bit_cast(half2_t, mr);
-                    const half2_t hh = __builtin_bit_cast(half2_t, kg_hi[tt] ^ zs);
-                    const half2_t hl = __builtin_bit_cast(half2_t, kg_lo[tt] ^ zs);
-                    am[2 * r] = hm[0]; am[2 * r + 1] = hm[1];
-                    aqh[2 * r] = hh[0]; aqh[2 * r + 1] = hh[1];
-                    aql[2 * r] = hl[0]; aql[2 * r + 1] = hl[1];
-                }
-                acc_m[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bm_hi[ks], acc_m[tt], 0, 0, 0);
-                acc_q[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aqh, bq[ks], acc_q[tt], 0, 0, 0);
-                acc_m[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bm_lo[ks], acc_m[tt], 0, 0, 0);
-                acc_q[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aql, bq[ks], acc_q[tt], 0, 0, 0);
-            }
-        }
-        // lane (n16, q) holds head n16 (if < G) for rows 4q..4q+3 of each tile
+        // lane (n16, q) holds rows 4q..4q+3 of each tile: (|k|, gamma) of those tokens
         float lg[2][4];
         float lmax = -INFINITY;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt) {
+            const float4 n01 = *reinterpret_cast<const float4 *>(buf + S::OFF_KN + (16 * tt + 4 * q) * 8);
+            const float4 n23 = *reinterpret_cast<const float4 *>(buf + S::OFF_KN + (16 * tt + 4 * q) * 8 + 16);
+            const float dn[4] = {n01.x, n01.z, n23.x, n23.z};
+            const float gm[4] = {n01.y, n01.w, n23.y, n23.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                const float c = accc[tt][i] + from_lane_plus_g<G>(accc[tt][i]);
+                const float sv = accs[tt][i] + from_lane_plus_g<G>(accs[tt][i]);
                 const int64_t tok = t0 + 16 * tt + 4 * q + i;
                 const bool ok = (n16 < G) && (tok < t_end);
-                lg[tt][i] = ok ? cur.dn[tt][i] * (acc_m[tt][i] + acc_q[tt][i]) * a.scale : -INFINITY;
+                lg[tt][i] = ok ? a.scale * dn[i] * fmaf(kQjl * gm[i], sv, c) : -INFINITY;
                 lmax = fmaxf(lmax, lg[tt][i]);
             }
+        }
 
         // ---- online softmax with a reference max that only moves when a logit exceeds it
         //      (rare after the first block); p <= 1 always
@@ -389,11 +413,11 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
             const int gg = col ? n / S::NG : 0, grp = col ? n % S::NG : 0;
             const f32x4_t p0 = *reinterpret_cast<const f32x4_t *>(&sm.pb[wave][gg][8 * q]);
             const f32x4_t p1 = *reinterpret_cast<const f32x4_t *>(&sm.pb[wave][gg][8 * q + 4]);
-            const f32x4_t s0 = *reinterpret_cast<const f32x4_t *>(&sm.scl[wave][grp][8 * q]);
-            const f32x4_t s1 = *reinterpret_cast<const f32x4_t *>(&sm.scl[wave][grp][8 * q + 4]);
+            const uint16_t *scl = reinterpret_cast<const uint16_t *>(buf + S::OFF_VS) + 8 * q * S::NG + grp;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float bvv = col ? (e < 4 ? p0[e] * s0[e] : p1[e - 4] * s1[e - 4]) : 0.f;
+                const float sc = (float)__builtin_bit_cast(_Float16, scl[e * S::NG]);
+                const float bvv = col ? (e < 4 ? p0[e] : p1[e - 4]) * sc : 0.f;
                 sumb[p] += bvv;
                 _Float16 h, l;
                 split_hl(bvv, h, l);
@@ -401,19 +425,32 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
                 bv_lo[p][e] = l;
             }
         }
-        // row n16's code run of each of the lane's 8 tokens (8q .. 8q+7), as halfword pairs
-        // z[k][r] = (halfword k of token 8q+2r) | (halfword k of token 8q+2r+1) << 16
+        // row n16's code run of each of the lane's 8 tokens (8q .. 8q+7, LDS slot 4e + q), as
+        // halfword pairs z[k][r] = (halfword k of token 8q+2r) | (halfword k of token 8q+2r+1) << 16
         uint32_t z[S::H][4];
-#pragma unroll
-        for (int k = 0; k < S::H; ++k) {
-            const int hw = n16 * S::H + k;       // halfword index inside the record
-            const int wi = hw >> 1;
-            const uint32_t sel = (hw & 1) ? 0x07060302u : 0x05040100u;
+        {
+            const unsigned char *vb = buf + S::OFF_VW + q * S::VW * 4 + n16 * S::H * 2;
+            constexpr int SLOT = S::VW * 4 * 4;  // bytes between tokens e and e + 1 (slots 4 apart)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const uint32_t wa = sm.val[wave][8 * q + 2 * r][wi];
-                const uint32_t wb = sm.val[wave][8 * q + 2 * r + 1][wi];
-                z[k][r] = __builtin_amdgcn_perm(wb, wa, sel);
+                if constexpr (S::H == 1) {
+                    const uint32_t ha = *reinterpret_cast<const uint16_t *>(vb + (2 * r) * SLOT);
+                    const uint32_t hb = *reinterpret_cast<const uint16_t *>(vb + (2 * r + 1) * SLOT);
+                    z[0][r] = ha | (hb << 16);
+                } else if constexpr (S::H == 2) {
+                    const uint32_t wa = *reinterpret_cast<const uint32_t *>(vb + (2 * r) * SLOT);
+                    const uint32_t wb = *reinterpret_cast<const uint32_t *>(vb + (2 * r + 1) * SLOT);
+                    z[0][r] = __builtin_amdgcn_perm(wb, wa, 0x05040100u);
+                    z[1][r] = __builtin_amdgcn_perm(wb, wa, 0x07060302u);
+                } else {
+                    const u32x2_t wa = *reinterpret_cast<const u32x2_t *>(vb + (2 * r) * SLOT);
+                    const u32x2_t wb = *reinterpret_cast<const u32x2_t *>(vb + (2 * r + 1) * SLOT);
+#pragma unroll
+                    for (int hw = 0; hw < 2; ++hw) {
+                        z[2 * hw][r] = __builtin_amdgcn_perm(wb[hw], wa[hw], 0x05040100u);
+                        z[2 * hw + 1][r] = __builtin_amdgcn_perm(wb[hw], wa[hw], 0x07060302u);
+                    }
+                }
             }
         }
         constexpr uint32_t kMask = ((1u << VB) - 1u) * 0x00010001u;
@@ -435,26 +472,30 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
                 acc_v[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv_lo[p], acc_v[p][t], 0, 0, 0);
             }
         }
-        wave_sync();  // this wave's LDS slots are rewritten by its next block
+        wave_sync();  // this wave's p slots are rewritten by its next block
     };
+
+    // ---- the wave's blocks: t_begin + wave*32 + k*128 < t_end, two staging buffers, the
+    //      next block's copies in flight while the current one is computed
     const int stride = kWaves * kBlock;
-    const int t_stop = (int)t_end;
-    int t0 = (int)t_begin + wave * kBlock;
-    if (t0 < t_stop) {
-        Blk bufa, bufb;
-        load_blk(t0, bufa);
-        load_blk(t0 + stride, bufb);
-        while (true) {
-            process(bufa, t0);
-            load_blk(t0 + 2 * stride, bufa);
-            t0 += stride;
-            if (t0 >= t_stop) break;
-            process(bufb, t0);
-            load_blk(t0 + 2 * stride, bufb);
-            t0 += stride;
-            if (t0 >= t_stop) break;
+    const int64_t tw = t_begin + wave * kBlock;
+    const int64_t nblk = tw < t_end ? (t_end - tw + stride - 1) / stride : 0;
+    if (nblk > 0) {
+        issue(tw, 0);
+        issue(tw + stride, 1);
+        for (int64_t k = 0;; k += 2) {
+            wait_vm<S::N_DMA>();
+            process(&sm.stage[wave][0][0], tw + k * stride);
+            if (k + 1 >= nblk) break;
+            issue(tw + (k + 2) * stride, 0);
+            wait_vm<S::N_DMA>();
+            process(&sm.stage[wave][1][0], tw + (k + 1) * stride);
+            if (k + 2 >= nblk) break;
+            issue(tw + (k + 3) * stride, 1);
         }
+        wait_vm<0>();  // the trailing prefetch lands before the buffers are reused
     }
+    __syncthreads();  // every wave is done with its staging buffers (aliased by wo below)
 
     // ---- wave results: m, l per head; o[g][c] = acc - (HALF - 1/2) * column sum of B
     l_part += __shfl_xor(l_part, 16);
@@ -478,7 +519,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int c = (4 * q + i) * S::NT + t;
-                if (c / 32 == grp) sm.wo[wave][gg][c] = acc_v[p][t][i] - (float)(S::HALF - 0.5f) * sumb[p];
+                if (c / 32 == grp) sm.x.wo[wave][gg][c] = acc_v[p][t][i] - (float)(S::HALF - 0.5f) * sumb[p];
             }
     }
 }
@@ -491,7 +532,7 @@ __device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk
     const int tid = threadIdx.x;
     for (int i = tid; i < G * D; i += kThreads) {
         const int g = i / D, j = i - g * D;
-        sm.ring_q[g][j] = a.prep[((int64_t)b * a.hq + kvh * G + g) * (3 * D + 4) + 2 * D + j];
+        sm.x.ring_q[g][j] = a.prep[((int64_t)b * a.hq + kvh * G + g) * (3 * D + 4) + 2 * D + j];
     }
     __syncthreads();
     float m_run[G], l_run[G], o[G];
@@ -511,7 +552,7 @@ __device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
 #pragma unroll
-                    for (int g = 0; g < G; ++g) acc[g] = fmaf(sm.ring_q[g][i + e], kv8[e], acc[g]);
+                    for (int g = 0; g < G; ++g) acc[g] = fmaf(sm.x.ring_q[g][i + e], kv8[e], acc[g]);
             }
 #pragma unroll
             for (int g = 0; g < G; ++g) lg[g] = acc[g] * a.scale;
@@ -529,7 +570,7 @@ __device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk
             const float mnew = fmaxf(m_run[g], mx[g]);
             corr[g] = (m_run[g] == -INFINITY) ? 0.f : __expf(m_run[g] - mnew);
             pe[g] = (tid < cnt) ? __expf(lg[g] - mnew) : 0.f;
-            sm.ring_p[g][tid] = pe[g];
+            sm.x.ring_p[g][tid] = pe[g];
             m_run[g] = mnew;
         }
         block_reduce<G, false>(pe, sm.ring_red);
@@ -542,7 +583,7 @@ __device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk
             const float vh = (float)__builtin_bit_cast(
                 _Float16, a.rv[((int64_t)bk * a.buffer_size + c0 + tt) * D + jv]);
 #pragma unroll
-            for (int g = 0; g < G; ++g) o[g] = fmaf(sm.ring_p[g][tt], vh, o[g]);
+            for (int g = 0; g < G; ++g) o[g] = fmaf(sm.x.ring_p[g][tt], vh, o[g]);
         }
         __syncthreads();
     }
@@ -551,8 +592,15 @@ __device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk
 }
 
 // ------------------------------------------------------------------ main kernel
+// register budget: 3 waves per SIMD (<= 168 VGPRs) at d = 128 with up to 4 query heads per
+// kv head, 2 otherwise (more accumulators)
+template <int D, int G>
+constexpr int kDecodeWavesPerSimd = (D == 128 && G <= 4) ? 3 : 2;
+
 template <int D, int VB, int G>
-__global__ __launch_bounds__(kThreads) void k_decode_main(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd<D, G>, kDecodeWavesPerSimd<D, G>)))
+void k_decode_main(DecodeArgs a) {
     using S = DecodeShape<D, VB, G>;
     __shared__ DecodeSmem<D, VB, G> sm;
     const int tid = threadIdx.x;
@@ -560,18 +608,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_main(DecodeArgs a) {
     const int bk = blockIdx.y;  // b * hkv + kv head == slice
     const int b = bk / a.hkv, kvh = bk - b * a.hkv;
     const int n_total = a.n_split_total;
-    float *pp = a.partial + ((int64_t)bk * n_total + split) * G * (D + 2);
+    float *pp = a.partial + ((int64_t)bk * n_total + split) * G * D;
+    float *pml = a.partial_ml + ((int64_t)bk * n_total + split) * G * 2;
 
     if (split < a.n_split) {
-        // byte -> (c[low nibble & 7], c[high nibble & 7]) as an fp16 pair, one copy per bank
-        {
-            const float c_lo = a.centroids[tid & 7];
-            const float c_hi = a.centroids[(tid >> 4) & 7];
-            const uint32_t e = pack_half2(c_lo, c_hi);
-#pragma unroll
-            for (int cp = 0; cp < kLutCopies; ++cp) sm.lut[tid * kLutCopies + cp] = e;
-        }
-        __syncthreads();
         const int64_t t_begin = (int64_t)split * a.per_split;
         const int64_t t_end = min(a.n_packed, t_begin + a.per_split);
         packed_wave<D, VB, G>(a, sm, bk, b, kvh, t_begin, t_end);
@@ -589,13 +629,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_main(DecodeArgs a) {
                     if (sm.wm[w][g] == -INFINITY) continue;
                     const float f = __expf(sm.wm[w][g] - M);
                     L = fmaf(sm.wl[w][g], f, L);
-                    O = fmaf(sm.wo[w][g][j], f, O);
+                    O = fmaf(sm.x.wo[w][g][j], f, O);
                 }
             }
-            pp[g * (D + 2) + j] = O;
+            pp[g * D + j] = O;
             if (j == 0) {
-                pp[g * (D + 2) + D] = M;
-                pp[g * (D + 2) + D + 1] = L;
+                pml[g * 2] = M;
+                pml[g * 2 + 1] = L;
             }
         }
     } else {
@@ -605,64 +645,96 @@ __global__ __launch_bounds__(kThreads) void k_decode_main(DecodeArgs a) {
         if constexpr (S::PARTS > 1) {
             if (part > 0)
 #pragma unroll
-                for (int g = 0; g < G; ++g) sm.wo[part - 1][g][jv] = o_r[g];
+                for (int g = 0; g < G; ++g) sm.x.wo[part - 1][g][jv] = o_r[g];
             __syncthreads();
             if (part == 0)
 #pragma unroll
                 for (int pt = 0; pt < S::PARTS - 1; ++pt)
 #pragma unroll
-                    for (int g = 0; g < G; ++g) o_r[g] += sm.wo[pt][g][jv];
+                    for (int g = 0; g < G; ++g) o_r[g] += sm.x.wo[pt][g][jv];
         }
         if (part == 0) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) pp[g * (D + 2) + jv] = o_r[g];
+            for (int g = 0; g < G; ++g) pp[g * D + jv] = o_r[g];
             if (jv == 0)
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    pp[g * (D + 2) + D] = m_r[g];
-                    pp[g * (D + 2) + D + 1] = l_r[g];
+                    pml[g * 2] = m_r[g];
+                    pml[g * 2 + 1] = l_r[g];
                 }
         }
     }
 
-    // ---- ticket: the last split of this (batch, kv head) merges all partials
-    __threadfence();
-    __syncthreads();
-    if (tid == 0)
-        sm.ticket = __hip_atomic_fetch_add(a.tickets + bk, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (sm.ticket != (unsigned)(n_total - 1)) return;
-    __threadfence();
-    const float *base = a.partial + (int64_t)bk * n_total * G * (D + 2);
-    {
-        const int lane = tid & 63, wv = tid >> 6;
-        for (int g = wv; g < G; g += kWaves) {
-            float mx = -INFINITY;
-            for (int sp = lane; sp < n_total; sp += 64) mx = fmaxf(mx, base[(sp * G + g) * (D + 2) + D]);
+}
+
+// ------------------------------------------------------------------ split merge
+// One workgroup per (batch * kv head, query head of the group): combines the (m, l, o)
+// partials of every split (a separate launch, so the partials of all workgroups are
+// visible without device-wide fences).
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void k_decode_merge(DecodeArgs a) {
+    constexpr int NJ4 = D / 4;             // float4 columns of one head
+    constexpr int NSG = kThreads / NJ4;    // split groups summed in parallel
+    __shared__ float f[256];
+    __shared__ float red[kWaves];
+    __shared__ float4 acc_s[NSG][NJ4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int bk = blockIdx.x / G, g = blockIdx.x % G;
+    const int b = bk / a.hkv, kvh = bk - b * a.hkv;
+    const int n_total = a.n_split_total;
+    const float *ml = a.partial_ml + (int64_t)bk * n_total * G * 2;
+    const float *po = a.partial + (int64_t)bk * n_total * G * D;
+
+    float m = -INFINITY;
+    for (int sp = tid; sp < n_total; sp += kThreads) m = fmaxf(m, ml[(sp * G + g) * 2]);
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-            float ls = 0.f;
-            for (int sp = lane; sp < n_total; sp += 64) {
-                const float ms = base[(sp * G + g) * (D + 2) + D];
-                const float f = (ms == -INFINITY) ? 0.f : __expf(ms - mx);
-                sm.merge_f[g][sp] = f;
-                ls = fmaf(base[(sp * G + g) * (D + 2) + D + 1], f, ls);
-            }
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) red[wv] = m;
+    __syncthreads();
+    float M = red[0];
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
-            if (lane == 0) sm.ml[g] = ls;
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red[w]);
+    __syncthreads();
+    float l = 0.f;
+    for (int sp = tid; sp < n_total; sp += kThreads) {
+        const float ms = ml[(sp * G + g) * 2];
+        const float fw = (ms == -INFINITY) ? 0.f : __expf(ms - M);
+        f[sp] = fw;
+        l = fmaf(fw, ml[(sp * G + g) * 2 + 1], l);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+    if (lane == 0) red[wv] = l;
+    __syncthreads();
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) L += red[w];
+
+    const int j4 = tid % NJ4, sg = tid / NJ4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = sg; sp < n_total; sp += NSG) {
+        const float4 v = *reinterpret_cast<const float4 *>(po + (int64_t)(sp * G + g) * D + 4 * j4);
+        const float fw = f[sp];
+        acc.x = fmaf(fw, v.x, acc.x);
+        acc.y = fmaf(fw, v.y, acc.y);
+        acc.z = fmaf(fw, v.z, acc.z);
+        acc.w = fmaf(fw, v.w, acc.w);
+    }
+    acc_s[sg][j4] = acc;
+    __syncthreads();
+    if (sg == 0) {
+#pragma unroll
+        for (int k = 1; k < NSG; ++k) {
+            const float4 v = acc_s[k][j4];
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
         }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        *reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.hq + kvh * G + g) * D + 4 * j4) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
-    __syncthreads();
-    for (int i = tid; i < G * D; i += kThreads) {
-        const int g = i / D, j = i - g * D;
-        float O = 0.f;
-#pragma unroll 8
-        for (int sp = 0; sp < n_total; ++sp) O = fmaf(sm.merge_f[g][sp], base[(sp * G + g) * (D + 2) + j], O);
-        const float L = sm.ml[g];
-        a.out[((int64_t)b * a.hq + kvh * G + g) * D + j] = L > 0.f ? O / L : 0.f;
-    }
-    if (tid == 0) __hip_atomic_store(a.tickets + bk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ ring append
@@ -702,11 +774,24 @@ static hipError_t launch_prep_t(int d, const DecodeArgs &a, hipStream_t st) {
 template <int D, int VB>
 static hipError_t launch_main_dv(int G, const DecodeArgs &a, hipStream_t st) {
     dim3 grid((unsigned)a.n_split_total, (unsigned)(a.batch * a.hkv));
+    const unsigned mgrid = (unsigned)(a.batch * a.hkv * G);
     switch (G) {
-        case 1: hipLaunchKernelGGL((k_decode_main<D, VB, 1>), grid, dim3(kThreads), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((k_decode_main<D, VB, 2>), grid, dim3(kThreads), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((k_decode_main<D, VB, 4>), grid, dim3(kThreads), 0, st, a); break;
-        default: hipLaunchKernelGGL((k_decode_main<D, VB, 8>), grid, dim3(kThreads), 0, st, a); break;
+        case 1:
+            hipLaunchKernelGGL((k_decode_main<D, VB, 1>), grid, dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((k_decode_merge<D, 1>), dim3(mgrid), dim3(kThreads), 0, st, a);
+            break;
+        case 2:
+            hipLaunchKernelGGL((k_decode_main<D, VB, 2>), grid, dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((k_decode_merge<D, 2>), dim3(mgrid), dim3(kThreads), 0, st, a);
+            break;
+        case 4:
+            hipLaunchKernelGGL((k_decode_main<D, VB, 4>), grid, dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((k_decode_merge<D, 4>), dim3(mgrid), dim3(kThreads), 0, st, a);
+            break;
+        default:
+            hipLaunchKernelGGL((k_decode_main<D, VB, 8>), grid, dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((k_decode_merge<D, 8>), dim3(mgrid), dim3(kThreads), 0, st, a);
+            break;
     }
     return hipGetLastError();
 }

@@ -58,8 +58,8 @@ struct DecodeArgs {
     float scale;
     float *out;
     float *prep;         // [batch*hq][3*D + 4]: q', w, q, (sum w)
-    float *partial;      // [batch*hkv][n_split_total][G][D + 2]
-    unsigned *tickets;   // [batch*hkv]
+    float *partial;      // [batch*hkv][n_split_total][G][D]: o of each split
+    float *partial_ml;   // [batch*hkv][n_split_total][G][2]: (m, l) of each split
 };
 
 hipError_t launch_quantize(int d, int vb, tq_dtype dt, const QuantArgs &a, hipStream_t st);

@@ -218,19 +218,19 @@ def test_decode_empty_context_gives_zeros(torch):
     assert not g.any()
 
 
-def test_decode_workspace_is_rearmed(torch):
-    """Two calls on the same workspace give identical results; tickets end at zero."""
+def test_decode_workspace_reuse_needs_no_reset(torch):
+    """Repeated calls on one workspace, first filled with garbage, give identical results
+    (the workspace is scratch: every value read is written by the same call first)."""
     w = W.custom(2, n_packed=2000, n_ring=3)
-    env, store, ring, q, ws, g1, _ = _decode_case(w, "rearm", b_list=[0])
+    env, store, ring, q, ws, g1, _ = _decode_case(w, "reuse", b_list=[0])
     qd = to_dev(q, w.in_dtype)
     out = torch.zeros((w.batch, w.hq, w.d), dtype=torch.float32, device="cuda")
+    ws.fill_(0x7F)  # large finite floats everywhere
     for _ in range(3):
         tq.tq_decode_attention(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, store.struct(), w.n_packed,
                                ring.struct(), w.n_ring, 1 / math.sqrt(w.d), out, ws)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy(), g1.astype(np.float32))
-    tail = ws[-256:].cpu().numpy()
-    assert not tail.any()
 
 
 def test_append_flush_decode_sequence(torch):
