@@ -182,18 +182,19 @@ __device__ __forceinline__ void block_reduce(float (&v)[G], float *scratch /* [k
 }
 
 // ---- global -> LDS copies issued by hand, waited for with explicit counts.  M0 holds the
-//      LDS destination of the wave's 64 x 16 (or 64 x 4) bytes; every LDS read of a buffer
-//      is complete (lgkmcnt(0)) before the buffer is refilled.
-__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds) {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+//      LDS destination of the wave's 64 x 16 (or 64 x 4) bytes, the global address is a
+//      uniform base plus a 32-bit per-lane byte offset; every LDS read of a buffer is
+//      complete (lgkmcnt(0)) before the buffer is refilled.
+__device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void *gptr, uint32_t lds) {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+__device__ __forceinline__ void dma4(const void *base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                  :
-                 : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory", "m0");
 }
 template <int N>
@@ -210,8 +211,8 @@ __device__ __forceinline__ float from_lane_plus_g(float x) {
 
 // ------------------------------------------------------------------ packed split (one wave)
 template <int D, int VB, int G>
-__device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk, int b, int kvh,
-                            int64_t t_begin, int64_t t_end) {
+__device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk, int b, int kvh, int t_begin,
+                            int t_end) {
     using S = DecodeShape<D, VB, G>;
     constexpr float kQjl = 1.2533141373155003f / D;  // sqrt(pi/2) / d
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -289,36 +290,42 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
     const float *kn_s = a.kn + rec0 * 2;
     const uint32_t *vw_s = a.vw + rec0 * S::VW;
     const uint16_t *vs_s = a.vs + rec0 * S::NG;
-    const int64_t last = a.n_packed - 1;
+    const int last = (int)a.n_packed - 1;
     const uint32_t lds_wave = (uint32_t)(uintptr_t)&sm.stage[wave][0][0];
-    auto issue = [&](int64_t t0, int bi) {
+    auto issue = [&](int t0, int bi) {
         const uint32_t base = lds_wave + (uint32_t)(bi * S::BUF_B);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int i = 0; i < S::N_KW; ++i) {
             const int c = lane + 64 * i;  // 16-byte chunk of the block's key words
-            const int64_t tok = min(t0 + c / (S::KW / 4), last);
-            dma16(kw_s + tok * S::KW + (c % (S::KW / 4)) * 4, base + 1024 * i);
+            const uint32_t tok = (uint32_t)min(t0 + c / (S::KW / 4), last);
+            dma16(kw_s, tok * (S::KW * 4) + (c % (S::KW / 4)) * 16, base + 1024 * i);
         }
         {
-            const int64_t tok = min(t0 + (lane >> 1), last);
-            dma4(kn_s + tok * 2 + (lane & 1), base + S::OFF_KN);
+            const uint32_t tok = (uint32_t)min(t0 + (lane >> 1), last);
+            dma4(kn_s, tok * 8 + (lane & 1) * 4, base + S::OFF_KN);
         }
 #pragma unroll
         for (int i = 0; i < S::N_VW; ++i) {
             const int c = lane + 64 * i;
             const int slot = c / (S::VW / 4);
-            const int64_t tok = min(t0 + 8 * (slot & 3) + (slot >> 2), last);
-            dma16(vw_s + tok * S::VW + (c % (S::VW / 4)) * 4, base + S::OFF_VW + 1024 * i);
+            const uint32_t tok = (uint32_t)min(t0 + 8 * (slot & 3) + (slot >> 2), last);
+            dma16(vw_s, tok * (S::VW * 4) + (c % (S::VW / 4)) * 16, base + S::OFF_VW + 1024 * i);
         }
 #pragma unroll
         for (int i = 0; i < S::N_VS; ++i) {
             const int c = lane + 64 * i;  // 4-byte piece of the block's scales
-            const int64_t tok = min(t0 + c / (S::NG / 2), last);
-            dma4(vs_s + tok * S::NG + 2 * (c % (S::NG / 2)), base + S::OFF_VS + 256 * i);
+            const uint32_t tok = (uint32_t)min(t0 + c / (S::NG / 2), last);
+            dma4(vs_s, tok * (S::NG * 2) + (c % (S::NG / 2)) * 4, base + S::OFF_VS + 256 * i);
         }
     };
 
-    auto process = [&](const unsigned char *buf, int64_t t0) {
+    // constants kept in registers so that and-or forms take them as operands
+    uint32_t kSel = 0x07070707u, kSgn = 0x80008000u, kOne = 0x3C003C00u;
+    uint32_t kCode = (((1u << VB) - 1u) << (10 - VB)) * 0x00010001u;
+    asm volatile("" : "+v"(kSel), "+v"(kSgn), "+v"(kOne), "+v"(kCode));
+
+    auto process = [&](const unsigned char *buf, int t0) {
         // ---- scores: centroid and sign parts on MFMA (hi and lo parts in separate columns)
         f32x4_t accc[2], accs[2];
 #pragma unroll
@@ -335,7 +342,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
 #pragma unroll
             for (int ks = 0; ks < S::NKS; ++ks) {
                 const uint32_t word = wds[ks];
-                const uint32_t sel_e = word & 0x07070707u, sel_o = (word >> 4) & 0x07070707u;
+                const uint32_t sel_e = word & kSel, sel_o = (word >> 4) & kSel;
                 const uint32_t le = __builtin_amdgcn_perm(tl1, tl0, sel_e);
                 const uint32_t he = __builtin_amdgcn_perm(th1, th0, sel_e);
                 const uint32_t lo = __builtin_amdgcn_perm(tl1, tl0, sel_o);
@@ -344,7 +351,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
                                     __builtin_amdgcn_perm(ho, lo, 0x05010400u), __builtin_amdgcn_perm(ho, lo, 0x07030602u)};
                 u32x4_t As;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) As[r] = ((word << (12 - 4 * r)) & 0x80008000u) | 0x3C003C00u;
+                for (int r = 0; r < 4; ++r) As[r] = ((word << (12 - 4 * r)) & kSgn) | kOne;
                 accc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, Ac),
                                                                   __builtin_bit_cast(half8_t, bc[ks]), accc[tt], 0, 0, 0);
                 accs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, As),
@@ -364,9 +371,9 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
             for (int i = 0; i < 4; ++i) {
                 const float c = accc[tt][i] + from_lane_plus_g<G>(accc[tt][i]);
                 const float sv = accs[tt][i] + from_lane_plus_g<G>(accs[tt][i]);
-                const int64_t tok = t0 + 16 * tt + 4 * q + i;
-                const bool ok = (n16 < G) && (tok < t_end);
-                lg[tt][i] = ok ? a.scale * dn[i] * fmaf(kQjl * gm[i], sv, c) : -INFINITY;
+                const int tok = t0 + 16 * tt + 4 * q + i;
+                const float v = a.scale * dn[i] * fmaf(kQjl * gm[i], sv, c);
+                lg[tt][i] = (n16 < G && tok < t_end) ? v : -INFINITY;
                 lmax = fmaxf(lmax, lg[tt][i]);
             }
         }
@@ -453,19 +460,17 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
                 }
             }
         }
-        constexpr uint32_t kMask = ((1u << VB) - 1u) * 0x00010001u;
-        const half2_t k1024 = {(_Float16)1024.f, (_Float16)1024.f};
+        // A = 1 + code / 2^VB (exact fp16: the code in the top VB mantissa bits of each half)
 #pragma unroll
         for (int t = 0; t < S::NT; ++t) {
             const int k = (VB * t) / 16, sh = (VB * t) % 16;
-            half8_t av;
+            u32x4_t avu;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const uint32_t x = ((z[k][r] >> sh) & kMask) | 0x64006400u;
-                const half2_t hv2 = __builtin_bit_cast(half2_t, x) - k1024;
-                av[2 * r] = hv2[0];
-                av[2 * r + 1] = hv2[1];
+                const uint32_t zz = sh >= 10 - VB ? (z[k][r] >> (sh - (10 - VB))) : (z[k][r] << ((10 - VB) - sh));
+                avu[r] = (zz & kCode) | kOne;
             }
+            const half8_t av = __builtin_bit_cast(half8_t, avu);
 #pragma unroll
             for (int p = 0; p < S::NPASS; ++p) {
                 acc_v[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv_hi[p], acc_v[p][t], 0, 0, 0);
@@ -478,12 +483,12 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
     // ---- the wave's blocks: t_begin + wave*32 + k*128 < t_end, two staging buffers, the
     //      next block's copies in flight while the current one is computed
     const int stride = kWaves * kBlock;
-    const int64_t tw = t_begin + wave * kBlock;
-    const int64_t nblk = tw < t_end ? (t_end - tw + stride - 1) / stride : 0;
+    const int tw = t_begin + wave * kBlock;
+    const int nblk = tw < t_end ? (t_end - tw + stride - 1) / stride : 0;
     if (nblk > 0) {
         issue(tw, 0);
         issue(tw + stride, 1);
-        for (int64_t k = 0;; k += 2) {
+        for (int k = 0;; k += 2) {
             wait_vm<S::N_DMA>();
             process(&sm.stage[wave][0][0], tw + k * stride);
             if (k + 1 >= nblk) break;
@@ -497,7 +502,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
     }
     __syncthreads();  // every wave is done with its staging buffers (aliased by wo below)
 
-    // ---- wave results: m, l per head; o[g][c] = acc - (HALF - 1/2) * column sum of B
+    // ---- wave results: m, l per head; o[g][c] from the accumulators and the column sums of B
     l_part += __shfl_xor(l_part, 16);
     l_part += __shfl_xor(l_part, 32);
 #pragma unroll
@@ -519,7 +524,9 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int c = (4 * q + i) * S::NT + t;
-                if (c / 32 == grp) sm.x.wo[wave][gg][c] = acc_v[p][t][i] - (float)(S::HALF - 0.5f) * sumb[p];
+                // acc = sum B (1 + code / 2^VB): o = 2^VB acc - (2^VB + HALF - 1/2) sum B
+                if (c / 32 == grp)
+                    sm.x.wo[wave][gg][c] = (float)(1 << VB) * acc_v[p][t][i] - (float)((1 << VB) + S::HALF - 0.5f) * sumb[p];
             }
     }
 }
@@ -612,8 +619,8 @@ void k_decode_main(DecodeArgs a) {
     float *pml = a.partial_ml + ((int64_t)bk * n_total + split) * G * 2;
 
     if (split < a.n_split) {
-        const int64_t t_begin = (int64_t)split * a.per_split;
-        const int64_t t_end = min(a.n_packed, t_begin + a.per_split);
+        const int t_begin = split * (int)a.per_split;
+        const int t_end = (int)min(a.n_packed, (int64_t)t_begin + a.per_split);
         packed_wave<D, VB, G>(a, sm, bk, b, kvh, t_begin, t_end);
         __syncthreads();
         // combine the four waves
