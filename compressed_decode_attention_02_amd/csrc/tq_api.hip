@@ -11,8 +11,7 @@
 namespace {
 
 constexpr int64_t kSplitQuantum = 128;     // tokens per pass of a split's four waves (4 x 32)
-constexpr int64_t kMinSplitTokens = 256;   // at least two blocks per wave
-constexpr int64_t kDecodeTargetWgs = 512;  // about two workgroups per CU (more splits cost more in the merge)
+constexpr int64_t kMinSplitTokens = 512;   // at least four blocks per wave
 constexpr int64_t kMaxSplits = 255;        // the merge keeps one weight per split (+ ring) in LDS
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -27,15 +26,21 @@ bool tables_ok(const tq_tables *t) {
     return t && t->centroids && t->boundaries && t->sign_bits && t->qjl_S && aligned16(t->qjl_S);
 }
 
-int64_t decode_splits(int64_t slices, int64_t n_packed) {
+// decode workgroups resident per CU (LDS at d = 256, registers with 8 query heads per kv
+// head): the split count fills one such wave of workgroups on the current device
+int64_t decode_target_wgs(int d, int64_t G) {
+    return (int64_t)tq::device_cus() * ((d == 128 && G <= 4) ? 3 : 2);
+}
+
+int64_t decode_splits(int d, int64_t G, int64_t slices, int64_t n_packed) {
     const int64_t by_tokens = std::max<int64_t>(1, (n_packed + kMinSplitTokens - 1) / kMinSplitTokens);
-    const int64_t want = std::max<int64_t>(1, (kDecodeTargetWgs + slices - 1) / slices);
+    const int64_t want = std::max<int64_t>(1, (decode_target_wgs(d, G) + slices - 1) / slices);
     return std::min({by_tokens, want, kMaxSplits});
 }
 
 // tokens per split: a whole number of four-wave passes; then as few splits as cover n_packed
-void split_shape(int64_t slices, int64_t n_packed, int64_t &n_split, int64_t &per_split) {
-    const int64_t s0 = decode_splits(slices, n_packed);
+void split_shape(int d, int64_t G, int64_t slices, int64_t n_packed, int64_t &n_split, int64_t &per_split) {
+    const int64_t s0 = decode_splits(d, G, slices, n_packed);
     per_split = (n_packed + s0 - 1) / s0;
     per_split = (per_split + kSplitQuantum - 1) / kSplitQuantum * kSplitQuantum;
     n_split = (n_packed + per_split - 1) / per_split;
@@ -142,7 +147,9 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch,
     if (!cfg || tq::check_config(*cfg) != TQ_OK || batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 ||
         max_context < 0)
         return 0;
-    const int64_t n_split = decode_splits((int64_t)batch * n_kv_heads, max_context);
+    if (n_q_heads % n_kv_heads != 0) return 0;
+    const int64_t n_split = decode_splits(cfg->head_dim, n_q_heads / n_kv_heads, (int64_t)batch * n_kv_heads,
+                                          max_context);
     return decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_split + 1).total;
 }
 
@@ -170,7 +177,7 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     // packed splits, plus one split for the ring; an empty context still runs one (empty)
     // split so that the output is written
     int64_t n_split = n_ring > 0 ? 0 : 1, per_split = 0;
-    if (n_packed > 0) split_shape(slices, n_packed, n_split, per_split);
+    if (n_packed > 0) split_shape(cfg->head_dim, G, slices, n_packed, n_split, per_split);
     const int64_t n_total = n_split + (n_ring > 0 ? 1 : 0);
     const DecodeLayout L = decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_total);
     if (workspace_bytes < L.total) return TQ_ERR_WORKSPACE;

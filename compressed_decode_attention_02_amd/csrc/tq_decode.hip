@@ -35,6 +35,8 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBlock = 32;       // tokens per wave iteration
 constexpr int kRingChunk = 256;  // ring tokens per pass of the ring split
+// logits and running maxima are kept in log2 units (softmax weights by exp2)
+constexpr float kLog2e = 1.4426950408889634f;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -137,6 +139,10 @@ struct DecodeShape {
     static constexpr int N_VW = VW_B / 1024;
     static constexpr int N_VS = VS_B / 256;
     static constexpr int N_DMA = N_KW + 1 + N_VW + N_VS;
+    // d = 128: the score B fragments live in LDS (one copy per workgroup: all four waves
+    // serve the same query heads), which frees 32 VGPRs per lane; d = 256 keeps them in
+    // registers (its LDS is taken by the staging buffers)
+    static constexpr bool BLDS = D == 128;
 };
 
 template <int D, int VB, int G>
@@ -150,6 +156,7 @@ struct alignas(16) DecodeSmem {
             float ring_p[G][kRingChunk];
         } x;
     };
+    u32x4_t bfrag[S::BLDS ? 2 * S::NKS : 1][64];  // [centroid k-steps, sign k-steps][lane]
     float pb[kWaves][G][kBlock + 4];
     float corr[kWaves][G];
     float wm[kWaves][G], wl[kWaves][G];
@@ -188,13 +195,13 @@ __device__ __forceinline__ void block_reduce(float (&v)[G], float *scratch /* [k
 __device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "v"(off), "s"(base), "s"(lds)
                  : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void *base, uint32_t off, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                  :
-                 : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "v"(off), "s"(base), "s"(lds)
                  : "memory", "m0");
 }
 template <int N>
@@ -215,7 +222,10 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
                             int t_end) {
     using S = DecodeShape<D, VB, G>;
     constexpr float kQjl = 1.2533141373155003f / D;  // sqrt(pi/2) / d
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    // wave index made visibly uniform: block positions, record bases and LDS addresses are
+    // then scalar values
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n16 = lane & 15, q = lane >> 4;
 
     // centroid byte tables: v_perm with selector byte idx picks byte idx of (t*1 : t*0), so
@@ -238,15 +248,17 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
     // part: element e is coordinate 8w + {0,2,4,6,1,3,5,7}[e] (even nibbles, then odd),
     // columns g < G hold q'_g (fp16 hi), columns G + g its lo part.  Sign part: element e is
     // coordinate 8w + {0,4,1,5,2,6,3,7}[e], columns hold -w_g hi / lo.
-    u32x4_t bc[S::NKS], bs[S::NKS];
+    // Both parts are pre-scaled by scale * log2(e) (the sign part also by sqrt(pi/2)/d), so
+    // that the logit in log2 units is |k| (centroid part + gamma * sign part).
+    u32x4_t bc[S::BLDS ? 1 : S::NKS], bs[S::BLDS ? 1 : S::NKS];
     {
+        const float cs = a.scale * kLog2e, ss = cs * kQjl;
         const bool hic = n16 < G, loc = n16 >= G && n16 < 2 * G;
         const int g = hic ? n16 : (loc ? n16 - G : 0);
         const float *pq = a.prep + ((int64_t)b * a.hq + kvh * G + g) * (3 * D + 4);
         constexpr int ce[8] = {0, 2, 4, 6, 1, 3, 5, 7};
         constexpr int se[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-#pragma unroll
-        for (int ks = 0; ks < S::NKS; ++ks) {
+        auto frag = [&](int ks, u32x4_t &fc, u32x4_t &fs) {
             const int w = q * S::NKS + ks;
             const float4 m0 = *reinterpret_cast<const float4 *>(pq + 8 * w);
             const float4 m1 = *reinterpret_cast<const float4 *>(pq + 8 * w + 4);
@@ -258,16 +270,28 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 _Float16 h, l;
-                split_hl(vm[ce[e]], h, l);
+                split_hl(cs * vm[ce[e]], h, l);
                 hc[e] = hic ? __builtin_bit_cast(uint16_t, h) : (loc ? __builtin_bit_cast(uint16_t, l) : 0);
-                split_hl(-vs[se[e]], h, l);
+                split_hl(-ss * vs[se[e]], h, l);
                 hs[e] = hic ? __builtin_bit_cast(uint16_t, h) : (loc ? __builtin_bit_cast(uint16_t, l) : 0);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                bc[ks][i] = hc[2 * i] | ((uint32_t)hc[2 * i + 1] << 16);
-                bs[ks][i] = hs[2 * i] | ((uint32_t)hs[2 * i + 1] << 16);
+                fc[i] = hc[2 * i] | ((uint32_t)hc[2 * i + 1] << 16);
+                fs[i] = hs[2 * i] | ((uint32_t)hs[2 * i + 1] << 16);
             }
+        };
+        if constexpr (S::BLDS) {
+            // wave w builds k-step w (NKS == kWaves at d = 128)
+            static_assert(!S::BLDS || S::NKS == kWaves, "one k-step per wave");
+            u32x4_t fc, fs;
+            frag(wave, fc, fs);
+            sm.bfrag[wave][lane] = fc;
+            sm.bfrag[S::NKS + wave][lane] = fs;
+            __syncthreads();
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < S::NKS; ++ks) frag(ks, bc[ks], bs[ks]);
         }
     }
 
@@ -292,31 +316,66 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
     const uint16_t *vs_s = a.vs + rec0 * S::NG;
     const int last = (int)a.n_packed - 1;
     const uint32_t lds_wave = (uint32_t)(uintptr_t)&sm.stage[wave][0][0];
+    // per-lane parts of the copies of a block (offsets from the block's first record);
+    // value records go to LDS slot 4 (t % 8) + t / 8
+    uint32_t o_kw[S::N_KW], o_vw[S::N_VW], o_vs[S::N_VS], r_kw[S::N_KW], r_vw[S::N_VW], r_vs[S::N_VS];
+#pragma unroll
+    for (int i = 0; i < S::N_KW; ++i) {
+        const int c = lane + 64 * i;  // 16-byte chunk of the block's key words
+        r_kw[i] = c / (S::KW / 4);
+        o_kw[i] = r_kw[i] * (S::KW * 4) + (c % (S::KW / 4)) * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < S::N_VW; ++i) {
+        const int c = lane + 64 * i;
+        const int slot = c / (S::VW / 4);
+        r_vw[i] = 8 * (slot & 3) + (slot >> 2);
+        o_vw[i] = r_vw[i] * (S::VW * 4) + (c % (S::VW / 4)) * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < S::N_VS; ++i) {
+        const int c = lane + 64 * i;  // 4-byte piece of the block's scales
+        r_vs[i] = c / (S::NG / 2);
+        o_vs[i] = r_vs[i] * (S::NG * 2) + (c % (S::NG / 2)) * 4;
+    }
+    const uint32_t r_kn = lane >> 1, o_kn = r_kn * 8 + (lane & 1) * 4;
     auto issue = [&](int t0, int bi) {
         const uint32_t base = lds_wave + (uint32_t)(bi * S::BUF_B);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (t0 + kBlock - 1 <= last) {
+            // whole block in range: uniform record base, loop-invariant lane offsets
+            const uint32_t *kw_b = kw_s + (int64_t)t0 * S::KW;
+            const float *kn_b = kn_s + (int64_t)t0 * 2;
+            const uint32_t *vw_b = vw_s + (int64_t)t0 * S::VW;
+            const uint16_t *vs_b = vs_s + (int64_t)t0 * S::NG;
 #pragma unroll
-        for (int i = 0; i < S::N_KW; ++i) {
-            const int c = lane + 64 * i;  // 16-byte chunk of the block's key words
-            const uint32_t tok = (uint32_t)min(t0 + c / (S::KW / 4), last);
-            dma16(kw_s, tok * (S::KW * 4) + (c % (S::KW / 4)) * 16, base + 1024 * i);
-        }
-        {
-            const uint32_t tok = (uint32_t)min(t0 + (lane >> 1), last);
-            dma4(kn_s, tok * 8 + (lane & 1) * 4, base + S::OFF_KN);
-        }
+            for (int i = 0; i < S::N_KW; ++i) dma16(kw_b, o_kw[i], base + 1024 * i);
+            dma4(kn_b, o_kn, base + S::OFF_KN);
 #pragma unroll
-        for (int i = 0; i < S::N_VW; ++i) {
-            const int c = lane + 64 * i;
-            const int slot = c / (S::VW / 4);
-            const uint32_t tok = (uint32_t)min(t0 + 8 * (slot & 3) + (slot >> 2), last);
-            dma16(vw_s, tok * (S::VW * 4) + (c % (S::VW / 4)) * 16, base + S::OFF_VW + 1024 * i);
-        }
+            for (int i = 0; i < S::N_VW; ++i) dma16(vw_b, o_vw[i], base + S::OFF_VW + 1024 * i);
 #pragma unroll
-        for (int i = 0; i < S::N_VS; ++i) {
-            const int c = lane + 64 * i;  // 4-byte piece of the block's scales
-            const uint32_t tok = (uint32_t)min(t0 + c / (S::NG / 2), last);
-            dma4(vs_s, tok * (S::NG * 2) + (c % (S::NG / 2)) * 4, base + S::OFF_VS + 256 * i);
+            for (int i = 0; i < S::N_VS; ++i) dma4(vs_b, o_vs[i], base + S::OFF_VS + 256 * i);
+        } else {
+            // the last block(s): token indices clamped to the last packed token
+#pragma unroll
+            for (int i = 0; i < S::N_KW; ++i) {
+                const uint32_t tok = (uint32_t)min(t0 + (int)r_kw[i], last);
+                dma16(kw_s, tok * (S::KW * 4) + (o_kw[i] - r_kw[i] * (S::KW * 4)), base + 1024 * i);
+            }
+            {
+                const uint32_t tok = (uint32_t)min(t0 + (int)r_kn, last);
+                dma4(kn_s, tok * 8 + (o_kn - r_kn * 8), base + S::OFF_KN);
+            }
+#pragma unroll
+            for (int i = 0; i < S::N_VW; ++i) {
+                const uint32_t tok = (uint32_t)min(t0 + (int)r_vw[i], last);
+                dma16(vw_s, tok * (S::VW * 4) + (o_vw[i] - r_vw[i] * (S::VW * 4)), base + S::OFF_VW + 1024 * i);
+            }
+#pragma unroll
+            for (int i = 0; i < S::N_VS; ++i) {
+                const uint32_t tok = (uint32_t)min(t0 + (int)r_vs[i], last);
+                dma4(vs_s, tok * (S::NG * 2) + (o_vs[i] - r_vs[i] * (S::NG * 2)), base + S::OFF_VS + 256 * i);
+            }
         }
     };
 
@@ -328,20 +387,31 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
     auto process = [&](const unsigned char *buf, int t0) {
         // ---- scores: centroid and sign parts on MFMA (hi and lo parts in separate columns)
         f32x4_t accc[2], accs[2];
+        uint32_t wds[2][S::NKS];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             accc[tt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
             accs[tt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
             const uint32_t *kwp = reinterpret_cast<const uint32_t *>(buf) + (16 * tt + n16) * S::KW + q * S::NKS;
-            uint32_t wds[S::NKS];
 #pragma unroll
             for (int i = 0; i < S::NKS / 4; ++i) {
                 const u32x4_t u = *reinterpret_cast<const u32x4_t *>(kwp + 4 * i);
-                wds[4 * i] = u[0]; wds[4 * i + 1] = u[1]; wds[4 * i + 2] = u[2]; wds[4 * i + 3] = u[3];
+                wds[tt][4 * i] = u[0]; wds[tt][4 * i + 1] = u[1]; wds[tt][4 * i + 2] = u[2]; wds[tt][4 * i + 3] = u[3];
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < S::NKS; ++ks) {
+            u32x4_t bck, bsk;
+            if constexpr (S::BLDS) {
+                bck = sm.bfrag[ks][lane];
+                bsk = sm.bfrag[S::NKS + ks][lane];
+            } else {
+                bck = bc[ks];
+                bsk = bs[ks];
             }
 #pragma unroll
-            for (int ks = 0; ks < S::NKS; ++ks) {
-                const uint32_t word = wds[ks];
+            for (int tt = 0; tt < 2; ++tt) {
+                const uint32_t word = wds[tt][ks];
                 const uint32_t sel_e = word & kSel, sel_o = (word >> 4) & kSel;
                 const uint32_t le = __builtin_amdgcn_perm(tl1, tl0, sel_e);
                 const uint32_t he = __builtin_amdgcn_perm(th1, th0, sel_e);
@@ -353,9 +423,9 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
 #pragma unroll
                 for (int r = 0; r < 4; ++r) As[r] = ((word << (12 - 4 * r)) & kSgn) | kOne;
                 accc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, Ac),
-                                                                  __builtin_bit_cast(half8_t, bc[ks]), accc[tt], 0, 0, 0);
+                                                                  __builtin_bit_cast(half8_t, bck), accc[tt], 0, 0, 0);
                 accs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, As),
-                                                                  __builtin_bit_cast(half8_t, bs[ks]), accs[tt], 0, 0, 0);
+                                                                  __builtin_bit_cast(half8_t, bsk), accs[tt], 0, 0, 0);
             }
         }
         // lane (n16, q) holds rows 4q..4q+3 of each tile: (|k|, gamma) of those tokens
@@ -372,7 +442,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
                 const float c = accc[tt][i] + from_lane_plus_g<G>(accc[tt][i]);
                 const float sv = accs[tt][i] + from_lane_plus_g<G>(accs[tt][i]);
                 const int tok = t0 + 16 * tt + 4 * q + i;
-                const float v = a.scale * dn[i] * fmaf(kQjl * gm[i], sv, c);
+                const float v = dn[i] * fmaf(gm[i], sv, c);
                 lg[tt][i] = (n16 < G && tok < t_end) ? v : -INFINITY;
                 lmax = fmaxf(lmax, lg[tt][i]);
             }
@@ -385,7 +455,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
             mb = fmaxf(mb, __shfl_xor(mb, 16));
             mb = fmaxf(mb, __shfl_xor(mb, 32));
             const float m_new = fmaxf(m_ref, mb);
-            const float corr = (m_ref == -INFINITY) ? 0.f : __expf(m_ref - m_new);
+            const float corr = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
             if (n16 < G && q == 0) sm.corr[wave][n16] = corr;
             l_part *= corr;
             m_ref = m_new;
@@ -404,7 +474,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
             f32x4_t pv;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pv[i] = (n16 < G) ? __expf(lg[tt][i] - m_ref) : 0.f;
+                pv[i] = (n16 < G) ? exp2f(lg[tt][i] - m_ref) : 0.f;
                 l_part += pv[i];
             }
             if (n16 < G) *reinterpret_cast<f32x4_t *>(&sm.pb[wave][n16][16 * tt + 4 * q]) = pv;
@@ -562,7 +632,7 @@ __device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk
                     for (int g = 0; g < G; ++g) acc[g] = fmaf(sm.x.ring_q[g][i + e], kv8[e], acc[g]);
             }
 #pragma unroll
-            for (int g = 0; g < G; ++g) lg[g] = acc[g] * a.scale;
+            for (int g = 0; g < G; ++g) lg[g] = acc[g] * (a.scale * kLog2e);
         } else {
 #pragma unroll
             for (int g = 0; g < G; ++g) lg[g] = -INFINITY;
@@ -575,8 +645,8 @@ __device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const float mnew = fmaxf(m_run[g], mx[g]);
-            corr[g] = (m_run[g] == -INFINITY) ? 0.f : __expf(m_run[g] - mnew);
-            pe[g] = (tid < cnt) ? __expf(lg[g] - mnew) : 0.f;
+            corr[g] = (m_run[g] == -INFINITY) ? 0.f : exp2f(m_run[g] - mnew);
+            pe[g] = (tid < cnt) ? exp2f(lg[g] - mnew) : 0.f;
             sm.x.ring_p[g][tid] = pe[g];
             m_run[g] = mnew;
         }
@@ -599,10 +669,10 @@ __device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk
 }
 
 // ------------------------------------------------------------------ main kernel
-// register budget: 3 waves per SIMD (<= 168 VGPRs) at d = 128 with up to 4 query heads per
+// register budget: 4 waves per SIMD (<= 128 VGPRs) at d = 128 with up to 4 query heads per
 // kv head, 2 otherwise (more accumulators)
 template <int D, int G>
-constexpr int kDecodeWavesPerSimd = (D == 128 && G <= 4) ? 3 : 2;
+constexpr int kDecodeWavesPerSimd = (D == 128 && G <= 4) ? 4 : 2;
 
 template <int D, int VB, int G>
 __global__ __launch_bounds__(kThreads)
@@ -634,7 +704,7 @@ void k_decode_main(DecodeArgs a) {
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w) {
                     if (sm.wm[w][g] == -INFINITY) continue;
-                    const float f = __expf(sm.wm[w][g] - M);
+                    const float f = exp2f(sm.wm[w][g] - M);
                     L = fmaf(sm.wl[w][g], f, L);
                     O = fmaf(sm.x.wo[w][g][j], f, O);
                 }
@@ -705,7 +775,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_merge(DecodeArgs a) {
     float l = 0.f;
     for (int sp = tid; sp < n_total; sp += kThreads) {
         const float ms = ml[(sp * G + g) * 2];
-        const float fw = (ms == -INFINITY) ? 0.f : __expf(ms - M);
+        const float fw = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
         f[sp] = fw;
         l = fmaf(fw, ml[(sp * G + g) * 2 + 1], l);
     }

@@ -12,6 +12,8 @@
 #include <cstring>
 #include <vector>
 
+#include <hip/hip_runtime.h>
+
 #include "tq.h"
 #include "tq_internal.h"
 
@@ -190,6 +192,18 @@ extern "C" const char *tq_status_string(tq_status s) {
 }
 
 namespace tq {
+
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+        cus[dev] = c;
+    }
+    return cus[dev];
+}
 
 tq_status check_config(const tq_config &c) {
     if (c.head_dim <= 0 || c.key_bits <= 0 || c.value_bits <= 0 || c.group_size <= 0 || c.buffer_size <= 0)

@@ -18,6 +18,9 @@ constexpr size_t kTableSOffset = 256;
 
 tq_status check_config(const tq_config &c);
 
+// compute units of the current device (cached per device; 256 if the query fails)
+int device_cus();
+
 struct QuantArgs {
     const void *k;
     const void *v;

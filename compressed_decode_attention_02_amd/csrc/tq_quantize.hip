@@ -514,18 +514,6 @@ __global__ __launch_bounds__(256) void k_quant_values(QuantArgs a) {
 }
 
 // ------------------------------------------------------------------------------ launch
-static int device_cus() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int c = 0;
-        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
-        cus[dev] = c;
-    }
-    return cus[dev];
-}
-
 template <typename Tag, int D>
 static void launch_keys_t(const QuantArgs &a, hipStream_t st) {
     const int64_t rows_per_group = (int64_t)kKeyGroupWaves<D> * KeyShape<D>::R;
