@@ -26,21 +26,22 @@ bool tables_ok(const tq_tables *t) {
     return t && t->centroids && t->boundaries && t->sign_bits && t->qjl_S && aligned16(t->qjl_S);
 }
 
-// decode workgroups resident per CU (LDS at d = 256, registers with 8 query heads per kv
-// head): the split count fills one such wave of workgroups on the current device
-int64_t decode_target_wgs(int d, int64_t G) {
-    return (int64_t)tq::device_cus() * ((d == 128 && G <= 4) ? 3 : 2);
+// decode workgroups resident per CU (LDS and registers; see the decode kernel's budget): the
+// split count fills one such wave of workgroups on the current device
+int64_t decode_target_wgs(int d, int vb, int64_t G) {
+    return (int64_t)tq::device_cus() * ((d == 128 && G <= 4) ? (vb == 2 ? 4 : 3) : 2);
 }
 
-int64_t decode_splits(int d, int64_t G, int64_t slices, int64_t n_packed) {
+int64_t decode_splits(int d, int vb, int64_t G, int64_t slices, int64_t n_packed) {
     const int64_t by_tokens = std::max<int64_t>(1, (n_packed + kMinSplitTokens - 1) / kMinSplitTokens);
-    const int64_t want = std::max<int64_t>(1, (decode_target_wgs(d, G) + slices - 1) / slices);
+    const int64_t want = std::max<int64_t>(1, (decode_target_wgs(d, vb, G) + slices - 1) / slices);
     return std::min({by_tokens, want, kMaxSplits});
 }
 
 // tokens per split: a whole number of four-wave passes; then as few splits as cover n_packed
-void split_shape(int d, int64_t G, int64_t slices, int64_t n_packed, int64_t &n_split, int64_t &per_split) {
-    const int64_t s0 = decode_splits(d, G, slices, n_packed);
+void split_shape(int d, int vb, int64_t G, int64_t slices, int64_t n_packed, int64_t &n_split,
+                 int64_t &per_split) {
+    const int64_t s0 = decode_splits(d, vb, G, slices, n_packed);
     per_split = (n_packed + s0 - 1) / s0;
     per_split = (per_split + kSplitQuantum - 1) / kSplitQuantum * kSplitQuantum;
     n_split = (n_packed + per_split - 1) / per_split;
@@ -55,7 +56,7 @@ struct DecodeLayout {
 DecodeLayout decode_layout(int d, int64_t batch, int64_t hq, int64_t hkv, int64_t n_split) {
     DecodeLayout L;
     L.prep = 0;
-    L.partial = align256(sizeof(float) * (size_t)(batch * hq) * (3 * d + 4));
+    L.partial = align256(sizeof(float) * (size_t)(batch * hq) * (2 * d));
     L.partial_ml = L.partial + align256(sizeof(float) * (size_t)(batch * hq) * n_split * d);
     L.total = L.partial_ml + align256(sizeof(float) * (size_t)(batch * hq) * n_split * 2);
     return L;
@@ -148,8 +149,8 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch,
         max_context < 0)
         return 0;
     if (n_q_heads % n_kv_heads != 0) return 0;
-    const int64_t n_split = decode_splits(cfg->head_dim, n_q_heads / n_kv_heads, (int64_t)batch * n_kv_heads,
-                                          max_context);
+    const int64_t n_split = decode_splits(cfg->head_dim, cfg->value_bits, n_q_heads / n_kv_heads,
+                                          (int64_t)batch * n_kv_heads, max_context);
     return decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_split + 1).total;
 }
 
@@ -177,13 +178,14 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     // packed splits, plus one split for the ring; an empty context still runs one (empty)
     // split so that the output is written
     int64_t n_split = n_ring > 0 ? 0 : 1, per_split = 0;
-    if (n_packed > 0) split_shape(cfg->head_dim, G, slices, n_packed, n_split, per_split);
+    if (n_packed > 0) split_shape(cfg->head_dim, cfg->value_bits, G, slices, n_packed, n_split, per_split);
     const int64_t n_total = n_split + (n_ring > 0 ? 1 : 0);
     const DecodeLayout L = decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_total);
     if (workspace_bytes < L.total) return TQ_ERR_WORKSPACE;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     tq::DecodeArgs a{};
     a.q = q;
+    a.q_dtype = (int)q_dtype;
     a.centroids = tables->centroids;
     a.sign_bits = tables->sign_bits;
     a.S = tables->qjl_S;
@@ -209,8 +211,8 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     a.per_split = per_split;
     a.scale = softmax_scale;
     a.out = out;
-    a.prep = reinterpret_cast<float *>(ws + L.prep);
     a.partial = reinterpret_cast<float *>(ws + L.partial);
     a.partial_ml = reinterpret_cast<float *>(ws + L.partial_ml);
-    return hip_status(tq::launch_decode(cfg->head_dim, cfg->value_bits, G, q_dtype, a, (hipStream_t)stream));
+    a.prep = reinterpret_cast<float *>(ws + L.prep);
+    return hip_status(tq::launch_decode(cfg->head_dim, cfg->value_bits, G, a, (hipStream_t)stream));
 }

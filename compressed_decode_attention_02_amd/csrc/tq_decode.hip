@@ -62,52 +62,75 @@ __device__ __forceinline__ void split_hl(float x, _Float16 &hi, _Float16 &lo) {
     lo = (_Float16)(x - (float)hi);
 }
 
+// ------------------------------------------------------------------ query loads
+// element `off` of q in its storage dtype, as fp32
+__device__ __forceinline__ float load_q(const DecodeArgs &a, int64_t off) {
+    if (a.q_dtype == TQ_F32) return load1(a.q, off, f32_tag{});
+    if (a.q_dtype == TQ_BF16) return load1(a.q, off, bf16_tag{});
+    return load1(a.q, off, f16_tag{});
+}
+
 // ------------------------------------------------------------------ query preparation
-template <typename Tag, int D>
-__global__ __launch_bounds__(D) void k_decode_prep(DecodeArgs a) {
+// One 256-thread workgroup per (batch, query head): q' = H (sigma o q) (unnormalised; the
+// 1/sqrt(d) of the rotation is folded into the decode's operand scale) and w = S q', with
+// kThreads / d threads per row of S.  prep[b * hq + h] = (q' [d], w [d]).  The S and q loads
+// are issued first so that their latencies overlap.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_decode_prep(DecodeArgs a) {
+    constexpr int PER = kThreads / D;  // threads per S row
+    constexpr int SW = D / PER / 8;    // 16-byte pieces of S per thread
     __shared__ float y[D];
-    __shared__ float red[D / 64];
-    const int j = threadIdx.x;
-    const int64_t bh = blockIdx.x;  // b * hq + h
-    const float qv = load1(a.q, bh * D + j, Tag{});
-    y[j] = flip_sign(qv, (a.sign_bits[j >> 5] >> (j & 31)) & 1u);
-    __syncthreads();
-    for (int len = 1; len < D; len <<= 1) {
-        float p = y[j], o = y[j ^ len];
+    __shared__ float part_acc[PER][D];
+    const int t = threadIdx.x, lane = t & 63;
+    const int j = t % D, part = t / D;
+    const int64_t h = blockIdx.x;
+    uint4 spk[SW];
+    const uint16_t *srow = a.S + (int64_t)j * D + part * (D / PER);
+#pragma unroll
+    for (int i = 0; i < SW; ++i) spk[i] = *reinterpret_cast<const uint4 *>(srow + 8 * i);
+    float v = 0.f;
+    if (t < D) v = flip_sign(load_q(a, h * D + t), (a.sign_bits[t >> 5] >> (t & 31)) & 1u);
+    // Walsh-Hadamard butterflies: strides below 64 inside the wave, the others through LDS
+#pragma unroll
+    for (int len = 1; len < 64; len <<= 1) {
+        const float o = __shfl_xor(v, len);
+        v = (lane & len) ? (o - v) : (v + o);
+    }
+    for (int len = 64; len < D; len <<= 1) {
+        if (t < D) y[t] = v;
         __syncthreads();
-        y[j] = (j & len) ? (o - p) : (p + o);
+        if (t < D) {
+            const float o = y[t ^ len];
+            v = (t & len) ? (o - v) : (v + o);
+        }
         __syncthreads();
     }
-    const float qr = y[j] * (1.0f / sqrtf((float)D));
+    if (t < D) y[t] = v;
     __syncthreads();
-    y[j] = qr;
-    __syncthreads();
-    // w_j = sum_i S[j][i] q'_i
-    const uint16_t *srow = a.S + (int64_t)j * D;
     float acc = 0.f;
-    for (int i = 0; i < D; i += 8) {
-        uint4 pk = *reinterpret_cast<const uint4 *>(srow + i);
-        acc = fmaf(f16_lo(pk.x), y[i + 0], acc);
-        acc = fmaf(f16_hi(pk.x), y[i + 1], acc);
-        acc = fmaf(f16_lo(pk.y), y[i + 2], acc);
-        acc = fmaf(f16_hi(pk.y), y[i + 3], acc);
-        acc = fmaf(f16_lo(pk.z), y[i + 4], acc);
-        acc = fmaf(f16_hi(pk.z), y[i + 5], acc);
-        acc = fmaf(f16_lo(pk.w), y[i + 6], acc);
-        acc = fmaf(f16_hi(pk.w), y[i + 7], acc);
+#pragma unroll
+    for (int i = 0; i < SW; ++i) {
+        const uint4 pk = spk[i];
+        const float4 q0 = *reinterpret_cast<const float4 *>(&y[part * (D / PER) + 8 * i]);
+        const float4 q1 = *reinterpret_cast<const float4 *>(&y[part * (D / PER) + 8 * i + 4]);
+        acc = fmaf(f16_lo(pk.x), q0.x, acc);
+        acc = fmaf(f16_hi(pk.x), q0.y, acc);
+        acc = fmaf(f16_lo(pk.y), q0.z, acc);
+        acc = fmaf(f16_hi(pk.y), q0.w, acc);
+        acc = fmaf(f16_lo(pk.z), q1.x, acc);
+        acc = fmaf(f16_hi(pk.z), q1.y, acc);
+        acc = fmaf(f16_lo(pk.w), q1.z, acc);
+        acc = fmaf(f16_hi(pk.w), q1.w, acc);
     }
-    float *p = a.prep + bh * (3 * D + 4);
-    p[j] = qr;
-    p[D + j] = acc;
-    p[2 * D + j] = qv;
-    float sw = acc;
-    for (int o = 32; o > 0; o >>= 1) sw += __shfl_xor(sw, o);
-    if ((j & 63) == 0) red[j >> 6] = sw;
+    part_acc[part][j] = acc;
     __syncthreads();
-    if (j == 0) {
-        float tot = 0.f;
-        for (int i = 0; i < D / 64; ++i) tot += red[i];
-        p[3 * D] = tot;
+    if (t < D) {
+        float w = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < PER; ++pt) w += part_acc[pt][t];
+        float *pp = a.prep + h * (2 * D);
+        pp[t] = y[t];
+        pp[D + t] = w;
     }
 }
 
@@ -148,15 +171,18 @@ struct DecodeShape {
 template <int D, int VB, int G>
 struct alignas(16) DecodeSmem {
     using S = DecodeShape<D, VB, G>;
+    // score B fragments in LDS (d = 128): only lanes n16 < 2G carry data; the other lanes
+    // read one zero fragment at index FZ
+    static constexpr int FZ = 4 * 2 * G;
     union {
         unsigned char stage[kWaves][2][S::BUF_B];  // packed splits: per-wave double buffer
-        struct {                                    // wave combine, ring split
+        struct {                                    // wave combine, ring split (after the loop)
             float wo[kWaves][G][D];
             float ring_q[G][D];
             float ring_p[G][kRingChunk];
         } x;
     };
-    u32x4_t bfrag[S::BLDS ? 2 * S::NKS : 1][64];  // [centroid k-steps, sign k-steps][lane]
+    u32x4_t bfrag[S::BLDS ? 2 * S::NKS : 1][FZ + 1];  // [centroid, sign k-steps][lane slot]
     float pb[kWaves][G][kBlock + 4];
     float corr[kWaves][G];
     float wm[kWaves][G], wl[kWaves][G];
@@ -248,67 +274,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
     // part: element e is coordinate 8w + {0,2,4,6,1,3,5,7}[e] (even nibbles, then odd),
     // columns g < G hold q'_g (fp16 hi), columns G + g its lo part.  Sign part: element e is
     // coordinate 8w + {0,4,1,5,2,6,3,7}[e], columns hold -w_g hi / lo.
-    // Both parts are pre-scaled by scale * log2(e) (the sign part also by sqrt(pi/2)/d), so
-    // that the logit in log2 units is |k| (centroid part + gamma * sign part).
-    u32x4_t bc[S::BLDS ? 1 : S::NKS], bs[S::BLDS ? 1 : S::NKS];
-    {
-        const float cs = a.scale * kLog2e, ss = cs * kQjl;
-        const bool hic = n16 < G, loc = n16 >= G && n16 < 2 * G;
-        const int g = hic ? n16 : (loc ? n16 - G : 0);
-        const float *pq = a.prep + ((int64_t)b * a.hq + kvh * G + g) * (3 * D + 4);
-        constexpr int ce[8] = {0, 2, 4, 6, 1, 3, 5, 7};
-        constexpr int se[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-        auto frag = [&](int ks, u32x4_t &fc, u32x4_t &fs) {
-            const int w = q * S::NKS + ks;
-            const float4 m0 = *reinterpret_cast<const float4 *>(pq + 8 * w);
-            const float4 m1 = *reinterpret_cast<const float4 *>(pq + 8 * w + 4);
-            const float4 s0 = *reinterpret_cast<const float4 *>(pq + D + 8 * w);
-            const float4 s1 = *reinterpret_cast<const float4 *>(pq + D + 8 * w + 4);
-            const float vm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-            const float vs[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-            uint16_t hc[8], hs[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                _Float16 h, l;
-                split_hl(cs * vm[ce[e]], h, l);
-                hc[e] = hic ? __builtin_bit_cast(uint16_t, h) : (loc ? __builtin_bit_cast(uint16_t, l) : 0);
-                split_hl(-ss * vs[se[e]], h, l);
-                hs[e] = hic ? __builtin_bit_cast(uint16_t, h) : (loc ? __builtin_bit_cast(uint16_t, l) : 0);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                fc[i] = hc[2 * i] | ((uint32_t)hc[2 * i + 1] << 16);
-                fs[i] = hs[2 * i] | ((uint32_t)hs[2 * i + 1] << 16);
-            }
-        };
-        if constexpr (S::BLDS) {
-            // wave w builds k-step w (NKS == kWaves at d = 128)
-            static_assert(!S::BLDS || S::NKS == kWaves, "one k-step per wave");
-            u32x4_t fc, fs;
-            frag(wave, fc, fs);
-            sm.bfrag[wave][lane] = fc;
-            sm.bfrag[S::NKS + wave][lane] = fs;
-            __syncthreads();
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < S::NKS; ++ks) frag(ks, bc[ks], bs[ks]);
-        }
-    }
-
-    // running reference max per head (lanes n16 == g), per-lane partial sums of p (the
-    // lane's rows), value accumulators and column sums of B
-    float m_ref = -INFINITY, l_part = 0.f;
-    f32x4_t acc_v[S::NPASS][S::NT];
-    float sumb[S::NPASS];
-#pragma unroll
-    for (int p = 0; p < S::NPASS; ++p) {
-        sumb[p] = 0.f;
-#pragma unroll
-        for (int t = 0; t < S::NT; ++t) acc_v[p][t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    }
-
-    // ---- staging: block at token t0 into buffer bi (token indices clamped to the last
-    //      packed token, so every copy reads records of this slice)
+    // ---- staging setup
     const int64_t rec0 = (int64_t)bk * a.cap;
     const uint32_t *kw_s = a.kw + rec0 * S::KW;
     const float *kn_s = a.kn + rec0 * 2;
@@ -316,6 +282,8 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
     const uint16_t *vs_s = a.vs + rec0 * S::NG;
     const int last = (int)a.n_packed - 1;
     const uint32_t lds_wave = (uint32_t)(uintptr_t)&sm.stage[wave][0][0];
+    // ---- staging: block at token t0 into buffer bi (token indices clamped to the last
+    //      packed token, so every copy reads records of this slice)
     // per-lane parts of the copies of a block (offsets from the block's first record);
     // value records go to LDS slot 4 (t % 8) + t / 8
     uint32_t o_kw[S::N_KW], o_vw[S::N_VW], o_vs[S::N_VS], r_kw[S::N_KW], r_vw[S::N_VW], r_vs[S::N_VS];
@@ -379,6 +347,83 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
         }
     };
 
+    const int stride = kWaves * kBlock;
+    const int tw = t_begin + wave * kBlock;
+    const int nblk = tw < t_end ? (t_end - tw + stride - 1) / stride : 0;
+
+    // Both parts are pre-scaled by scale * log2(e) / sqrt(d) (the sign part also by
+    // sqrt(pi/2)/d), so that the logit in log2 units is |k| (centroid part + gamma * sign part).
+    u32x4_t bc[S::BLDS ? 1 : S::NKS], bs[S::BLDS ? 1 : S::NKS];
+    {
+        const float cs = a.scale * kLog2e * (1.0f / sqrtf((float)D)), ss = cs * kQjl;
+        const bool hic = n16 < G, loc = n16 >= G && n16 < 2 * G;
+        const int g = hic ? n16 : (loc ? n16 - G : 0);
+        const float *pq = a.prep + ((int64_t)b * a.hq + kvh * G + g) * (2 * D);
+        const float *pw = pq + D;
+        constexpr int ce[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+        constexpr int se[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+        auto frag = [&](int ks, u32x4_t &fc, u32x4_t &fs) {
+            const int w = q * S::NKS + ks;
+            const float4 m0 = *reinterpret_cast<const float4 *>(pq + 8 * w);
+            const float4 m1 = *reinterpret_cast<const float4 *>(pq + 8 * w + 4);
+            const float4 s0 = *reinterpret_cast<const float4 *>(pw + 8 * w);
+            const float4 s1 = *reinterpret_cast<const float4 *>(pw + 8 * w + 4);
+            const float vm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+            const float vs[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            uint16_t hc[8], hs[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                _Float16 h, l;
+                split_hl(cs * vm[ce[e]], h, l);
+                hc[e] = hic ? __builtin_bit_cast(uint16_t, h) : (loc ? __builtin_bit_cast(uint16_t, l) : 0);
+                split_hl(-ss * vs[se[e]], h, l);
+                hs[e] = hic ? __builtin_bit_cast(uint16_t, h) : (loc ? __builtin_bit_cast(uint16_t, l) : 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                fc[i] = hc[2 * i] | ((uint32_t)hc[2 * i + 1] << 16);
+                fs[i] = hs[2 * i] | ((uint32_t)hs[2 * i + 1] << 16);
+            }
+        };
+        if constexpr (S::BLDS) {
+            // wave w builds k-step w (NKS == kWaves at d = 128)
+            static_assert(!S::BLDS || S::NKS == kWaves, "one k-step per wave");
+            u32x4_t fc, fs;
+            frag(wave, fc, fs);
+            if (n16 < 2 * G) {
+                sm.bfrag[wave][q * 2 * G + n16] = fc;
+                sm.bfrag[S::NKS + wave][q * 2 * G + n16] = fs;
+            }
+            if (lane == 0) {
+                sm.bfrag[wave][DecodeSmem<D, VB, G>::FZ] = (u32x4_t){0u, 0u, 0u, 0u};
+                sm.bfrag[S::NKS + wave][DecodeSmem<D, VB, G>::FZ] = (u32x4_t){0u, 0u, 0u, 0u};
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < S::NKS; ++ks) frag(ks, bc[ks], bs[ks]);
+        }
+        __syncthreads();  // fragments visible (d = 128)
+    }
+    const int fslot = n16 < 2 * G ? q * 2 * G + n16 : DecodeSmem<D, VB, G>::FZ;
+    // the first two blocks' copies (after the fragment loads, which the compiler waits for
+    // with its own counts)
+    if (nblk > 0) {
+        issue(tw, 0);
+        issue(tw + stride, 1);
+    }
+
+    // running reference max per head (lanes n16 == g), per-lane partial sums of p (the
+    // lane's rows), value accumulators and column sums of B
+    float m_ref = -INFINITY, l_part = 0.f;
+    f32x4_t acc_v[S::NPASS][S::NT];
+    float sumb[S::NPASS];
+#pragma unroll
+    for (int p = 0; p < S::NPASS; ++p) {
+        sumb[p] = 0.f;
+#pragma unroll
+        for (int t = 0; t < S::NT; ++t) acc_v[p][t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    }
+
     // constants kept in registers so that and-or forms take them as operands
     uint32_t kSel = 0x07070707u, kSgn = 0x80008000u, kOne = 0x3C003C00u;
     uint32_t kCode = (((1u << VB) - 1u) << (10 - VB)) * 0x00010001u;
@@ -403,8 +448,8 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
         for (int ks = 0; ks < S::NKS; ++ks) {
             u32x4_t bck, bsk;
             if constexpr (S::BLDS) {
-                bck = sm.bfrag[ks][lane];
-                bsk = sm.bfrag[S::NKS + ks][lane];
+                bck = sm.bfrag[ks][fslot];
+                bsk = sm.bfrag[S::NKS + ks][fslot];
             } else {
                 bck = bc[ks];
                 bsk = bs[ks];
@@ -552,12 +597,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
 
     // ---- the wave's blocks: t_begin + wave*32 + k*128 < t_end, two staging buffers, the
     //      next block's copies in flight while the current one is computed
-    const int stride = kWaves * kBlock;
-    const int tw = t_begin + wave * kBlock;
-    const int nblk = tw < t_end ? (t_end - tw + stride - 1) / stride : 0;
     if (nblk > 0) {
-        issue(tw, 0);
-        issue(tw + stride, 1);
         for (int k = 0;; k += 2) {
             wait_vm<S::N_DMA>();
             process(&sm.stage[wave][0][0], tw + k * stride);
@@ -609,7 +649,7 @@ __device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk
     const int tid = threadIdx.x;
     for (int i = tid; i < G * D; i += kThreads) {
         const int g = i / D, j = i - g * D;
-        sm.x.ring_q[g][j] = a.prep[((int64_t)b * a.hq + kvh * G + g) * (3 * D + 4) + 2 * D + j];
+        sm.x.ring_q[g][j] = load_q(a, ((int64_t)b * a.hq + kvh * G + g) * D + j);
     }
     __syncthreads();
     float m_run[G], l_run[G], o[G];
@@ -669,14 +709,15 @@ __device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk
 }
 
 // ------------------------------------------------------------------ main kernel
-// register budget: 4 waves per SIMD (<= 128 VGPRs) at d = 128 with up to 4 query heads per
-// kv head, 2 otherwise (more accumulators)
-template <int D, int G>
-constexpr int kDecodeWavesPerSimd = (D == 128 && G <= 4) ? 4 : 2;
+// register budget (waves per SIMD): 4 (<= 128 VGPRs) for d = 128 / 2-bit values with up to 4
+// query heads per kv head (LDS allows four workgroups per CU), 3 for 4-bit values (LDS allows
+// three), 2 otherwise
+template <int D, int VB, int G>
+constexpr int kDecodeWavesPerSimd = (D == 128 && G <= 4) ? (VB == 2 ? 4 : 3) : 2;
 
 template <int D, int VB, int G>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd<D, G>, kDecodeWavesPerSimd<D, G>)))
+__attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd<D, VB, G>, kDecodeWavesPerSimd<D, VB, G>)))
 void k_decode_main(DecodeArgs a) {
     using S = DecodeShape<D, VB, G>;
     __shared__ DecodeSmem<D, VB, G> sm;
@@ -838,34 +879,29 @@ __global__ __launch_bounds__(256) void k_ring_append(const void *kn, const void 
 }
 
 // ------------------------------------------------------------------ launchers
-template <typename Tag>
-static hipError_t launch_prep_t(int d, const DecodeArgs &a, hipStream_t st) {
-    const unsigned grid = (unsigned)(a.batch * a.hq);
-    if (d == 128)
-        hipLaunchKernelGGL((k_decode_prep<Tag, 128>), dim3(grid), dim3(128), 0, st, a);
-    else
-        hipLaunchKernelGGL((k_decode_prep<Tag, 256>), dim3(grid), dim3(256), 0, st, a);
-    return hipGetLastError();
-}
-
 template <int D, int VB>
 static hipError_t launch_main_dv(int G, const DecodeArgs &a, hipStream_t st) {
     dim3 grid((unsigned)a.n_split_total, (unsigned)(a.batch * a.hkv));
+    const unsigned pgrid = (unsigned)(a.batch * a.hq);
     const unsigned mgrid = (unsigned)(a.batch * a.hkv * G);
     switch (G) {
         case 1:
+            hipLaunchKernelGGL((k_decode_prep<D>), dim3(pgrid), dim3(kThreads), 0, st, a);
             hipLaunchKernelGGL((k_decode_main<D, VB, 1>), grid, dim3(kThreads), 0, st, a);
             hipLaunchKernelGGL((k_decode_merge<D, 1>), dim3(mgrid), dim3(kThreads), 0, st, a);
             break;
         case 2:
+            hipLaunchKernelGGL((k_decode_prep<D>), dim3(pgrid), dim3(kThreads), 0, st, a);
             hipLaunchKernelGGL((k_decode_main<D, VB, 2>), grid, dim3(kThreads), 0, st, a);
             hipLaunchKernelGGL((k_decode_merge<D, 2>), dim3(mgrid), dim3(kThreads), 0, st, a);
             break;
         case 4:
+            hipLaunchKernelGGL((k_decode_prep<D>), dim3(pgrid), dim3(kThreads), 0, st, a);
             hipLaunchKernelGGL((k_decode_main<D, VB, 4>), grid, dim3(kThreads), 0, st, a);
             hipLaunchKernelGGL((k_decode_merge<D, 4>), dim3(mgrid), dim3(kThreads), 0, st, a);
             break;
         default:
+            hipLaunchKernelGGL((k_decode_prep<D>), dim3(pgrid), dim3(kThreads), 0, st, a);
             hipLaunchKernelGGL((k_decode_main<D, VB, 8>), grid, dim3(kThreads), 0, st, a);
             hipLaunchKernelGGL((k_decode_merge<D, 8>), dim3(mgrid), dim3(kThreads), 0, st, a);
             break;
@@ -873,14 +909,7 @@ static hipError_t launch_main_dv(int G, const DecodeArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_decode(int d, int vb, int G, tq_dtype qdt, const DecodeArgs &a, hipStream_t st) {
-    hipError_t e;
-    switch (qdt) {
-        case TQ_F32: e = launch_prep_t<f32_tag>(d, a, st); break;
-        case TQ_BF16: e = launch_prep_t<bf16_tag>(d, a, st); break;
-        default: e = launch_prep_t<f16_tag>(d, a, st); break;
-    }
-    if (e != hipSuccess) return e;
+hipError_t launch_decode(int d, int vb, int G, const DecodeArgs &a, hipStream_t st) {
     if (d == 128 && vb == 2) return launch_main_dv<128, 2>(G, a, st);
     if (d == 128 && vb == 4) return launch_main_dv<128, 4>(G, a, st);
     if (d == 256 && vb == 2) return launch_main_dv<256, 2>(G, a, st);

@@ -41,6 +41,7 @@ struct QuantArgs {
 
 struct DecodeArgs {
     const void *q;
+    int q_dtype;  // tq_dtype of q
     const float *centroids;
     const uint32_t *sign_bits;
     const uint16_t *S;
@@ -60,13 +61,13 @@ struct DecodeArgs {
     int64_t per_split;  // packed tokens per split
     float scale;
     float *out;
-    float *prep;         // [batch*hq][3*D + 4]: q', w, q, (sum w)
+    float *prep;         // [batch*hq][2*D]: q' = H sigma q, w = S q' 
     float *partial;      // [batch*hkv][n_split_total][G][D]: o of each split
     float *partial_ml;   // [batch*hkv][n_split_total][G][2]: (m, l) of each split
 };
 
 hipError_t launch_quantize(int d, int vb, tq_dtype dt, const QuantArgs &a, hipStream_t st);
-hipError_t launch_decode(int d, int vb, int G, tq_dtype qdt, const DecodeArgs &a, hipStream_t st);
+hipError_t launch_decode(int d, int vb, int G, const DecodeArgs &a, hipStream_t st);
 hipError_t launch_ring_append(int d, tq_dtype dt, const void *kn, const void *vn, uint16_t *rk, uint16_t *rv,
                               int n_slices, int buffer_size, int slot, hipStream_t st);
 
