@@ -642,40 +642,69 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
 }
 
 // ------------------------------------------------------------------ ring split (VALU)
+// The exact fp16 ring tokens of one (batch, kv head): scores by one thread per token (its key
+// row loaded whole, then G dot products against q in LDS), block-wide softmax statistics, and
+// values by threads that own a pair of coordinates and a residue class of tokens (one 4-byte
+// load per token, many in flight), reduced through LDS.  Writes the split's (m, l, o).
 template <int D, int VB, int G>
-__device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk, int b, int kvh,
-                           float (&m_out)[G], float (&l_out)[G], float (&o_out)[G], int jv, int part) {
-    using S = DecodeShape<D, VB, G>;
+__device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk, int b, int kvh, float *pp,
+                           float *pml) {
+    constexpr int NCP = D / 2;             // coordinate pairs
+    constexpr int NTG = kThreads / NCP;    // token residue classes of the value pass
     const int tid = threadIdx.x;
     for (int i = tid; i < G * D; i += kThreads) {
         const int g = i / D, j = i - g * D;
         sm.x.ring_q[g][j] = load_q(a, ((int64_t)b * a.hq + kvh * G + g) * D + j);
     }
     __syncthreads();
-    float m_run[G], l_run[G], o[G];
+    const int cp = tid % NCP, tg = tid / NCP;
+    float m_run[G], l_run[G], o0[G], o1[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) { m_run[g] = -INFINITY; l_run[g] = 0.f; o[g] = 0.f; }
+    for (int g = 0; g < G; ++g) {
+        m_run[g] = -INFINITY;
+        l_run[g] = 0.f;
+        o0[g] = 0.f;
+        o1[g] = 0.f;
+    }
+    const uint16_t *rk = a.rk + (int64_t)bk * a.buffer_size * D;
+    const uint32_t *rv2 = reinterpret_cast<const uint32_t *>(a.rv + (int64_t)bk * a.buffer_size * D);
     for (int c0 = 0; c0 < a.n_ring; c0 += kRingChunk) {
         const int cnt = min(kRingChunk, a.n_ring - c0);
         float lg[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) lg[g] = -INFINITY;
         if (tid < cnt) {
-            const uint16_t *kr = a.rk + ((int64_t)bk * a.buffer_size + c0 + tid) * D;
+            const uint4 *kr = reinterpret_cast<const uint4 *>(rk + (int64_t)(c0 + tid) * D);
             float acc[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) acc[g] = 0.f;
-            for (int i = 0; i < D; i += 8) {
-                float kv8[8];
-                load8(kr, i, kv8, f16_tag{});
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+            for (int h = 0; h < 2; ++h) {
+                uint4 k4[D / 16];
 #pragma unroll
-                    for (int g = 0; g < G; ++g) acc[g] = fmaf(sm.x.ring_q[g][i + e], kv8[e], acc[g]);
+                for (int i = 0; i < D / 16; ++i) k4[i] = kr[h * (D / 16) + i];
+#pragma unroll
+                for (int i = 0; i < D / 16; ++i) {
+                    const int c = 8 * (h * (D / 16) + i);
+                    const float kv[8] = {f16_lo(k4[i].x), f16_hi(k4[i].x), f16_lo(k4[i].y), f16_hi(k4[i].y),
+                                         f16_lo(k4[i].z), f16_hi(k4[i].z), f16_lo(k4[i].w), f16_hi(k4[i].w)};
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const float4 q0 = *reinterpret_cast<const float4 *>(&sm.x.ring_q[g][c]);
+                        const float4 q1 = *reinterpret_cast<const float4 *>(&sm.x.ring_q[g][c + 4]);
+                        acc[g] = fmaf(q0.x, kv[0], acc[g]);
+                        acc[g] = fmaf(q0.y, kv[1], acc[g]);
+                        acc[g] = fmaf(q0.z, kv[2], acc[g]);
+                        acc[g] = fmaf(q0.w, kv[3], acc[g]);
+                        acc[g] = fmaf(q1.x, kv[4], acc[g]);
+                        acc[g] = fmaf(q1.y, kv[5], acc[g]);
+                        acc[g] = fmaf(q1.z, kv[6], acc[g]);
+                        acc[g] = fmaf(q1.w, kv[7], acc[g]);
+                    }
+                }
             }
 #pragma unroll
             for (int g = 0; g < G; ++g) lg[g] = acc[g] * (a.scale * kLog2e);
-        } else {
-#pragma unroll
-            for (int g = 0; g < G; ++g) lg[g] = -INFINITY;
         }
         float mx[G];
 #pragma unroll
@@ -690,22 +719,52 @@ __device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk
             sm.x.ring_p[g][tid] = pe[g];
             m_run[g] = mnew;
         }
-        block_reduce<G, false>(pe, sm.ring_red);
+        block_reduce<G, false>(pe, sm.ring_red);  // its barriers also publish ring_p
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             l_run[g] = l_run[g] * corr[g] + pe[g];
-            o[g] *= corr[g];
+            o0[g] *= corr[g];
+            o1[g] *= corr[g];
         }
-        for (int tt = part; tt < cnt; tt += S::PARTS) {
-            const float vh = (float)__builtin_bit_cast(
-                _Float16, a.rv[((int64_t)bk * a.buffer_size + c0 + tt) * D + jv]);
+        // values: coordinates 2cp, 2cp + 1 over tokens tg, tg + NTG, ...
+#pragma unroll 8
+        for (int tt = tg; tt < cnt; tt += NTG) {
+            const uint32_t v2 = rv2[(int64_t)(c0 + tt) * NCP + cp];
+            const float va = f16_lo(v2), vb = f16_hi(v2);
 #pragma unroll
-            for (int g = 0; g < G; ++g) o[g] = fmaf(sm.x.ring_p[g][tt], vh, o[g]);
+            for (int g = 0; g < G; ++g) {
+                const float pg = sm.x.ring_p[g][tt];
+                o0[g] = fmaf(pg, va, o0[g]);
+                o1[g] = fmaf(pg, vb, o1[g]);
+            }
         }
-        __syncthreads();
+        __syncthreads();  // ring_p is rewritten by the next chunk
     }
+    // reduce the token classes through LDS (wo is free in the ring split)
+    if (tg > 0)
 #pragma unroll
-    for (int g = 0; g < G; ++g) { m_out[g] = m_run[g]; l_out[g] = l_run[g]; o_out[g] = o[g]; }
+        for (int g = 0; g < G; ++g) {
+            sm.x.wo[tg - 1][g][2 * cp] = o0[g];
+            sm.x.wo[tg - 1][g][2 * cp + 1] = o1[g];
+        }
+    __syncthreads();
+    if (tg == 0) {
+#pragma unroll
+        for (int t2 = 0; t2 < NTG - 1; ++t2)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                o0[g] += sm.x.wo[t2][g][2 * cp];
+                o1[g] += sm.x.wo[t2][g][2 * cp + 1];
+            }
+#pragma unroll
+        for (int g = 0; g < G; ++g) *reinterpret_cast<float2 *>(&pp[g * D + 2 * cp]) = make_float2(o0[g], o1[g]);
+        if (cp == 0)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                pml[g * 2] = m_run[g];
+                pml[g * 2 + 1] = l_run[g];
+            }
+    }
 }
 
 // ------------------------------------------------------------------ main kernel
@@ -757,32 +816,8 @@ void k_decode_main(DecodeArgs a) {
             }
         }
     } else {
-        float m_r[G], l_r[G], o_r[G];
-        const int jv = tid % D, part = tid / D;
-        ring_split<D, VB, G>(a, sm, bk, b, kvh, m_r, l_r, o_r, jv, part);
-        if constexpr (S::PARTS > 1) {
-            if (part > 0)
-#pragma unroll
-                for (int g = 0; g < G; ++g) sm.x.wo[part - 1][g][jv] = o_r[g];
-            __syncthreads();
-            if (part == 0)
-#pragma unroll
-                for (int pt = 0; pt < S::PARTS - 1; ++pt)
-#pragma unroll
-                    for (int g = 0; g < G; ++g) o_r[g] += sm.x.wo[pt][g][jv];
-        }
-        if (part == 0) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) pp[g * D + jv] = o_r[g];
-            if (jv == 0)
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    pml[g * 2] = m_r[g];
-                    pml[g * 2 + 1] = l_r[g];
-                }
-        }
+        ring_split<D, VB, G>(a, sm, bk, b, kvh, pp, pml);
     }
-
 }
 
 // ------------------------------------------------------------------ split merge

@@ -116,7 +116,43 @@ __device__ __forceinline__ void split3_bf16(float x, uint16_t &hi, uint16_t &mid
     lo = __builtin_bit_cast(uint16_t, l);
 }
 
-// ------------------------------------------------------------------------------ keys
+// ------------------------------------------------------------------------------ values of one group
+// Codes of one group: code = clamp(floor(v / s), -HALF, HALF - 1) + HALF, floor exact.
+// Fast form (16-bit inputs, normal fp16 s): v / s is then either an integer or at least
+// 2^-11 away from every integer (or inside (-1, 1)), so floor(p + |p| 2^-20), p = v * (1/s)
+// rounded, is exact: the nudge lifts exact integers that rounding pushed below, and is far
+// too small to cross a non-integer.  Otherwise the estimate is corrected with exact
+// products (q + 1) s and q s.
+template <int VB, bool Exact>
+__device__ __forceinline__ void quant_group(const float (&v)[32], float sc, uint32_t (&wd)[VB]) {
+    constexpr int HALF = 1 << (VB - 1);
+    constexpr int PER = 32 / VB;  // codes per word
+    const float rinv = 1.0f / sc;
+    const float nudge = rinv * 0x1p-20f;
+    // code offset HALF in every field
+    constexpr uint32_t kOff = VB == 2 ? 0xAAAAAAAAu : 0x88888888u;
+#pragma unroll
+    for (int w = 0; w < VB; ++w) {
+        uint32_t acc = kOff;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const float x = v[w * PER + e];
+            float q;
+            if constexpr (Exact) {
+                q = floorf(x * rinv);
+                if ((q + 1.f) * sc <= x) q += 1.f;
+                else if (q * sc > x) q -= 1.f;
+            } else {
+                q = floorf(fmaf(fabsf(x), nudge, x * rinv));
+            }
+            q = fminf(fmaxf(q, (float)-HALF), (float)(HALF - 1));
+            acc += (uint32_t)(int)q << (VB * e);
+        }
+        wd[w] = acc;
+    }
+}
+
+// ------------------------------------------------------------------------------ keys (and values)
 // Launch shape: persistent workgroups that loop over tiles of rows (the S copy in LDS is
 // made once per workgroup); latency is hidden by the other waves of the SIMD (3 per SIMD,
 // <= 168 VGPRs).  d = 128: 4-wave groups, 3 per CU (33 KB of LDS each); d = 256: 12-wave
@@ -150,10 +186,10 @@ __device__ __forceinline__ void split_row(int64_t r, int64_t n_tok, double inv, 
     t = rem;
 }
 
-template <typename Tag, int D>
+template <typename Tag, int D, int VB>
 __global__ __launch_bounds__(64 * kKeyGroupWaves<D>)
 __attribute__((amdgpu_waves_per_eu(kKeyWavesPerSimd<D>, kKeyWavesPerSimd<D>)))
-void k_quant_keys(QuantArgs a) {
+void k_quant_kv(QuantArgs a) {
     using S = KeyShape<D>;
     constexpr int R = S::R;
     constexpr int NT = 64 * kKeyGroupWaves<D>;
@@ -246,6 +282,75 @@ void k_quant_keys(QuantArgs a) {
             int64_t sl, t;
             split_row(row, a.n_tokens, inv_tok, sl, t);
             rec = sl * a.cap + a.dst_offset + t;
+        }
+
+        // ---- the tile's values: this lane's 64 coordinates g*64 .. g*64+63 of its token (two
+        //      groups of 32), loaded with the keys and quantised first (their registers are free again before the
+        //      key encode needs its peak)
+        constexpr int VCH = kF32 ? 16 : 8;  // 16-byte chunks of 64 values
+        uint4 vr[VCH];
+        {
+            int64_t sl, t;
+            split_row(row < a.n_rows ? row : a.n_rows - 1, a.n_tokens, inv_tok, sl, t);
+            const uint4 *vp = reinterpret_cast<const uint4 *>(static_cast<const unsigned char *>(a.v) +
+                                                              ((sl * a.in_slice_stride + t * D + 64 * g) * (kF32 ? 4 : 2)));
+#pragma unroll
+            for (int i = 0; i < VCH; ++i) vr[i] = vp[i];
+        }
+
+        // ---- values: groups 2g and 2g + 1 of the token, all in this lane
+        {
+            constexpr int NG = D / 32;
+            constexpr int VW = VB * D / 32;
+            uint32_t wd[2][VB];
+            uint16_t scb[2];
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) {
+                float vv[32];
+#pragma unroll
+                for (int c = 0; c < VCH / 2; ++c) {
+                    const uint4 x = vr[gi * (VCH / 2) + c];
+                    if constexpr (kF32) {
+                        vv[4 * c + 0] = __uint_as_float(x.x); vv[4 * c + 1] = __uint_as_float(x.y);
+                        vv[4 * c + 2] = __uint_as_float(x.z); vv[4 * c + 3] = __uint_as_float(x.w);
+                    } else if constexpr (kF16) {
+                        vv[8 * c + 0] = f16_lo(x.x); vv[8 * c + 1] = f16_hi(x.x);
+                        vv[8 * c + 2] = f16_lo(x.y); vv[8 * c + 3] = f16_hi(x.y);
+                        vv[8 * c + 4] = f16_lo(x.z); vv[8 * c + 5] = f16_hi(x.z);
+                        vv[8 * c + 6] = f16_lo(x.w); vv[8 * c + 7] = f16_hi(x.w);
+                    } else {
+                        vv[8 * c + 0] = bf16_lo(x.x); vv[8 * c + 1] = bf16_hi(x.x);
+                        vv[8 * c + 2] = bf16_lo(x.y); vv[8 * c + 3] = bf16_hi(x.y);
+                        vv[8 * c + 4] = bf16_lo(x.z); vv[8 * c + 5] = bf16_hi(x.z);
+                        vv[8 * c + 6] = bf16_lo(x.w); vv[8 * c + 7] = bf16_hi(x.w);
+                    }
+                }
+                float am = 0.f;
+#pragma unroll
+                for (int e = 0; e < 32; ++e) am = fmaxf(am, fabsf(vv[e]));
+                const _Float16 sh = (_Float16)(am * (1.0f / (1 << (VB - 1))));
+                const float sc = (float)sh;
+                scb[gi] = __builtin_bit_cast(uint16_t, sh);
+                if (sc == 0.f) {
+#pragma unroll
+                    for (int w = 0; w < VB; ++w) wd[gi][w] = VB == 2 ? 0xAAAAAAAAu : 0x88888888u;
+                } else if (kF32 || sc < 0x1p-14f) {
+                    quant_group<VB, true>(vv, sc, wd[gi]);
+                } else {
+                    quant_group<VB, false>(vv, sc, wd[gi]);
+                }
+            }
+            if (rec >= 0) {
+                uint32_t *dstv = a.vw + rec * VW + 2 * g * VB;
+                if constexpr (VB == 2) {
+                    *reinterpret_cast<uint4 *>(dstv) = make_uint4(wd[0][0], wd[0][1], wd[1][0], wd[1][1]);
+                } else {
+                    uint4 *d4 = reinterpret_cast<uint4 *>(dstv);
+                    d4[0] = make_uint4(wd[0][0], wd[0][1], wd[0][2], wd[0][3]);
+                    d4[1] = make_uint4(wd[1][0], wd[1][1], wd[1][2], wd[1][3]);
+                }
+                *reinterpret_cast<uint32_t *>(a.vs + rec * NG + 2 * g) = scb[0] | ((uint32_t)scb[1] << 16);
+            }
         }
 
         // ---- |k|^2 in fp32 (products of 16-bit inputs are exact; several partial sums)
@@ -433,113 +538,29 @@ void k_quant_keys(QuantArgs a) {
             if (g == 0)
                 *reinterpret_cast<float2 *>(a.kn + rec * 2) = make_float2(knorm, sqrtf(gg) * (1.0f / 256.f));
         }
+
     }
 }
 
 // ------------------------------------------------------------------------------ values
-// Codes of one group: code = clamp(floor(v / s), -HALF, HALF - 1) + HALF, floor exact.
-// Fast form (16-bit inputs, normal fp16 s): v / s is then either an integer or at least
-// 2^-11 away from every integer (or inside (-1, 1)), so floor(p + |p| 2^-20), p = v * (1/s)
-// rounded, is exact: the nudge lifts exact integers that rounding pushed below, and is far
-// too small to cross a non-integer.  Otherwise the estimate is corrected with exact
-// products (q + 1) s and q s.
-template <int VB, bool Exact>
-__device__ __forceinline__ void quant_group(const float (&v)[32], float sc, uint32_t (&wd)[VB]) {
-    constexpr int HALF = 1 << (VB - 1);
-    constexpr int PER = 32 / VB;  // codes per word
-    const float rinv = 1.0f / sc;
-    const float nudge = rinv * 0x1p-20f;
-    // code offset HALF in every field
-    constexpr uint32_t kOff = VB == 2 ? 0xAAAAAAAAu : 0x88888888u;
-#pragma unroll
-    for (int w = 0; w < VB; ++w) {
-        uint32_t acc = kOff;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const float x = v[w * PER + e];
-            float q;
-            if constexpr (Exact) {
-                q = floorf(x * rinv);
-                if ((q + 1.f) * sc <= x) q += 1.f;
-                else if (q * sc > x) q -= 1.f;
-            } else {
-                q = floorf(fmaf(fabsf(x), nudge, x * rinv));
-            }
-            q = fminf(fmaxf(q, (float)-HALF), (float)(HALF - 1));
-            acc += (uint32_t)(int)q << (VB * e);
-        }
-        wd[w] = acc;
-    }
-}
-
-template <typename Tag, int D, int VB>
-__global__ __launch_bounds__(256) void k_quant_values(QuantArgs a) {
-    constexpr int NG = D / 32;
-    constexpr int HALF = 1 << (VB - 1);
-    constexpr int VW = VB * D / 32;
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = gid / NG;
-    const int grp = (int)(gid - row * NG);
-    if (row >= a.n_rows) return;
-    int64_t sl, t;
-    split_row(row, a.n_tokens, 1.0 / (double)a.n_tokens, sl, t);
-    const int64_t in_off = sl * a.in_slice_stride + t * D + 32 * grp;
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float tmp[8];
-        load8(a.v, in_off + 8 * i, tmp, Tag{});
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[8 * i + e] = tmp[e];
-    }
-    float am = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) am = fmaxf(am, fabsf(v[e]));
-    const _Float16 sh = (_Float16)(am * (1.0f / HALF));
-    const float sc = (float)sh;
-    uint32_t wd[VB];
-    if (sc == 0.f) {
-#pragma unroll
-        for (int w = 0; w < VB; ++w) wd[w] = VB == 2 ? 0xAAAAAAAAu : 0x88888888u;
-    } else if (std::is_same_v<Tag, f32_tag> || sc < 0x1p-14f) {
-        quant_group<VB, true>(v, sc, wd);
-    } else {
-        quant_group<VB, false>(v, sc, wd);
-    }
-    const int64_t rec = sl * a.cap + a.dst_offset + t;
-    uint32_t *dst = a.vw + rec * VW + VB * grp;
-    if constexpr (VB == 2) *reinterpret_cast<uint2 *>(dst) = make_uint2(wd[0], wd[1]);
-    else *reinterpret_cast<uint4 *>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-    a.vs[rec * NG + grp] = __builtin_bit_cast(uint16_t, sh);
-}
-
 // ------------------------------------------------------------------------------ launch
-template <typename Tag, int D>
-static void launch_keys_t(const QuantArgs &a, hipStream_t st) {
+template <typename Tag, int D, int VB>
+static void launch_kv_t(const QuantArgs &a, hipStream_t st) {
     const int64_t rows_per_group = (int64_t)kKeyGroupWaves<D> * KeyShape<D>::R;
     const int64_t groups = (a.n_rows + rows_per_group - 1) / rows_per_group;
     const int64_t resident = (int64_t)device_cus() * kKeyGroupsPerCU<D>;
     const int64_t grid = groups < resident ? groups : resident;
-    hipLaunchKernelGGL((k_quant_keys<Tag, D>), dim3((unsigned)grid), dim3(64 * kKeyGroupWaves<D>), 0, st, a);
-}
-
-template <typename Tag, int D, int VB>
-static void launch_values_t(const QuantArgs &a, hipStream_t st) {
-    const int64_t lanes = a.n_rows * (D / 32);
-    const int64_t blocks = (lanes + 255) / 256;
-    hipLaunchKernelGGL((k_quant_values<Tag, D, VB>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_quant_kv<Tag, D, VB>), dim3((unsigned)grid), dim3(64 * kKeyGroupWaves<D>), 0, st, a);
 }
 
 template <typename Tag>
 static hipError_t launch_quantize_d(int d, int vb, const QuantArgs &a, hipStream_t st) {
     if (d == 128) {
-        launch_keys_t<Tag, 128>(a, st);
-        if (vb == 2) launch_values_t<Tag, 128, 2>(a, st);
-        else launch_values_t<Tag, 128, 4>(a, st);
+        if (vb == 2) launch_kv_t<Tag, 128, 2>(a, st);
+        else launch_kv_t<Tag, 128, 4>(a, st);
     } else {
-        launch_keys_t<Tag, 256>(a, st);
-        if (vb == 2) launch_values_t<Tag, 256, 2>(a, st);
-        else launch_values_t<Tag, 256, 4>(a, st);
+        if (vb == 2) launch_kv_t<Tag, 256, 2>(a, st);
+        else launch_kv_t<Tag, 256, 4>(a, st);
     }
     return hipGetLastError();
 }
