@@ -209,6 +209,8 @@ def main():
         "breakdown_ms_median": {"quantize": round(q_med, 4), "append": round(statistics.median(a_ms), 4),
                                 "decode_all_layers": round(d_med, 4), "flush": round(statistics.median(f_ms), 4)},
         "quantize_tokens_per_s": round(B * L * Tp / (q_med * 1e-3), 1),
+        "quantize_algorithmic_bytes": q_bytes,
+        "decode_algorithmic_bytes_per_layer": dec_bytes // L,
         "quantize_GBps": round(q_gbps, 1),
         "decode_kv_tokens_per_s": round(kv_tokens / (d_med * 1e-3), 1),
         "decode_GBps": round(d_gbps, 1),
