@@ -12,7 +12,8 @@ namespace {
 
 constexpr int64_t kSplitQuantum = 128;     // tokens per pass of a split's four waves (4 x 32)
 constexpr int64_t kMinSplitTokens = 512;   // at least four blocks per wave
-constexpr int64_t kMaxSplits = 255;        // the merge keeps one weight per split (+ ring) in LDS
+constexpr int64_t kMaxRingSplits = 8;      // ring splits per slice (64 tokens or more each)
+constexpr int64_t kMaxSplits = 255 - kMaxRingSplits;  // the merge keeps one weight per split in LDS
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
@@ -39,6 +40,19 @@ int64_t decode_splits(int d, int vb, int64_t G, int64_t slices, int64_t n_packed
 }
 
 // tokens per split: a whole number of four-wave passes; then as few splits as cover n_packed
+// ring splits of n_ring tokens (each a multiple of 64 tokens, at most kMaxRingSplits)
+int64_t ring_per_split(int64_t n_ring) {
+    const int64_t per = (n_ring + kMaxRingSplits - 1) / kMaxRingSplits;
+    return std::max<int64_t>(64, (per + 63) / 64 * 64);
+}
+int64_t ring_splits(int64_t n_ring) {
+    return n_ring > 0 ? (n_ring + ring_per_split(n_ring) - 1) / ring_per_split(n_ring) : 0;
+}
+// an upper bound of ring_splits(n) over n <= buffer_size
+int64_t ring_splits_max(int64_t buffer_size) {
+    return std::min<int64_t>(kMaxRingSplits, (buffer_size + 63) / 64);
+}
+
 void split_shape(int d, int vb, int64_t G, int64_t slices, int64_t n_packed, int64_t &n_split,
                  int64_t &per_split) {
     const int64_t s0 = decode_splits(d, vb, G, slices, n_packed);
@@ -151,7 +165,8 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch,
     if (n_q_heads % n_kv_heads != 0) return 0;
     const int64_t n_split = decode_splits(cfg->head_dim, cfg->value_bits, n_q_heads / n_kv_heads,
                                           (int64_t)batch * n_kv_heads, max_context);
-    return decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_split + 1).total;
+    return decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads,
+                         n_split + ring_splits_max(cfg->buffer_size)).total;
 }
 
 extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *tables, const void *q,
@@ -175,12 +190,14 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     if (n_ring > 0 && (!ring || !ring->k || !ring->v || !aligned16(ring->k) || !aligned16(ring->v)))
         return TQ_ERR_INVALID_ARG;
     const int64_t slices = (int64_t)batch * n_kv_heads;
-    // packed splits, plus one split for the ring; an empty context still runs one (empty)
-    // split so that the output is written
+    // packed splits, plus the ring splits; an empty context still runs one (empty) split so
+    // that the output is written
     int64_t n_split = n_ring > 0 ? 0 : 1, per_split = 0;
     if (n_packed > 0) split_shape(cfg->head_dim, cfg->value_bits, G, slices, n_packed, n_split, per_split);
-    const int64_t n_total = n_split + (n_ring > 0 ? 1 : 0);
-    const DecodeLayout L = decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_total);
+    const int64_t n_total = n_split + ring_splits(n_ring);
+    // (sized for the most ring splits any fill of this ring can need, like the workspace query)
+    const DecodeLayout L =
+        decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_split + ring_splits_max(cfg->buffer_size));
     if (workspace_bytes < L.total) return TQ_ERR_WORKSPACE;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     tq::DecodeArgs a{};
@@ -208,6 +225,7 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     a.hkv = n_kv_heads;
     a.n_split = (int)n_split;
     a.n_split_total = (int)n_total;
+    a.ring_per_split = (int)ring_per_split(n_ring);
     a.per_split = per_split;
     a.scale = softmax_scale;
     a.out = out;

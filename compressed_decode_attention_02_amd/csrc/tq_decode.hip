@@ -34,7 +34,8 @@ namespace tq {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBlock = 32;       // tokens per wave iteration
-constexpr int kRingChunk = 256;  // ring tokens per pass of the ring split
+constexpr int kRingChunk = 64;   // ring tokens per pass of a ring split (four threads per token)
+constexpr int kMaxRingSplits = 8;  // ring splits per slice
 // logits and running maxima are kept in log2 units (softmax weights by exp2)
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -62,6 +63,15 @@ __device__ __forceinline__ void split_hl(float x, _Float16 &hi, _Float16 &lo) {
     lo = (_Float16)(x - (float)hi);
 }
 
+// The products x0 = p0 s0, x1 = p1 s1 (p fp32, s fp16) as fp16 pairs: hi = fp16(x) and
+// lo = fp16(x - hi), each one rounding of an exact value (mixed fma)
+__device__ __forceinline__ void mix_hl2(float p0, _Float16 s0, float p1, _Float16 s1, uint32_t &hi, uint32_t &lo) {
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=&v"(hi) : "v"(p0), "v"(s0));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "+v"(hi) : "v"(p1), "v"(s1));
+    asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,1,1]" : "=&v"(lo) : "v"(p0), "v"(s0), "v"(hi));
+    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,1,1]" : "+v"(lo) : "v"(p1), "v"(s1), "v"(hi));
+}
+
 // ------------------------------------------------------------------ query loads
 // element `off` of q in its storage dtype, as fp32
 __device__ __forceinline__ float load_q(const DecodeArgs &a, int64_t off) {
@@ -76,14 +86,13 @@ __device__ __forceinline__ float load_q(const DecodeArgs &a, int64_t off) {
 // kThreads / d threads per row of S.  prep[b * hq + h] = (q' [d], w [d]).  The S and q loads
 // are issued first so that their latencies overlap.
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_decode_prep(DecodeArgs a) {
+__device__ void prep_head(const DecodeArgs &a, int64_t h) {
     constexpr int PER = kThreads / D;  // threads per S row
     constexpr int SW = D / PER / 8;    // 16-byte pieces of S per thread
     __shared__ float y[D];
     __shared__ float part_acc[PER][D];
     const int t = threadIdx.x, lane = t & 63;
     const int j = t % D, part = t / D;
-    const int64_t h = blockIdx.x;
     uint4 spk[SW];
     const uint16_t *srow = a.S + (int64_t)j * D + part * (D / PER);
 #pragma unroll
@@ -171,22 +180,33 @@ struct DecodeShape {
 template <int D, int VB, int G>
 struct alignas(16) DecodeSmem {
     using S = DecodeShape<D, VB, G>;
-    // score B fragments in LDS (d = 128): only lanes n16 < 2G carry data; the other lanes
-    // read one zero fragment at index FZ
-    static constexpr int FZ = 4 * 2 * G;
+    // score query operands in LDS (d = 128): NSL nonzero rows per operand and lane group
+    // are stored; lanes of zero rows read one zero fragment at index FZ
+    static constexpr int NSL = G == 8 ? 16 : (G == 4 ? 8 : 4);
+    static constexpr int FZ = 4 * NSL;
     union {
         unsigned char stage[kWaves][2][S::BUF_B];  // packed splits: per-wave double buffer
-        struct {                                    // wave combine, ring split (after the loop)
+        struct {                                    // wave combine (after the loop)
             float wo[kWaves][G][D];
-            float ring_q[G][D];
-            float ring_p[G][kRingChunk];
         } x;
     };
-    u32x4_t bfrag[S::BLDS ? 2 * S::NKS : 1][FZ + 1];  // [centroid, sign k-steps][lane slot]
+    u32x4_t bfrag[S::BLDS ? 2 * S::NKS : 1][FZ + 1];  // [centroid, sign k-steps][row slot]
     float pb[kWaves][G][kBlock + 4];
     float corr[kWaves][G];
+    float mref[kWaves][G];  // running reference max per wave and head (packed splits)
     float wm[kWaves][G], wl[kWaves][G];
-    float ring_red[kWaves * G];
+};
+
+// ring split: the query (rows split in four padded quarters, so that the four threads of a
+// token read different banks), logits then p of a chunk, the token classes' partial o, and
+// the block reductions
+template <int D, int G>
+struct alignas(16) RingSmem {
+    static constexpr int QW = D / 4 + 4;
+    float q[G][4][QW];
+    float p[kRingChunk][G];
+    float wo[kWaves][G][D];
+    float red[kWaves * G];
 };
 
 // block-wide reduction of G values (max or sum); every thread gets the result
@@ -216,18 +236,23 @@ __device__ __forceinline__ void block_reduce(float (&v)[G], float *scratch /* [k
 
 // ---- global -> LDS copies issued by hand, waited for with explicit counts.  M0 holds the
 //      LDS destination of the wave's 64 x 16 (or 64 x 4) bytes, the global address is a
-//      uniform base plus a 32-bit per-lane byte offset; every LDS read of a buffer is
+//      uniform base plus a 32-bit per-lane byte offset; the instruction's immediate offset
+//      IMM is added to both the global and the LDS address.  Every LDS read of a buffer is
 //      complete (lgkmcnt(0)) before the buffer is refilled.
+template <int IMM = 0>
 __device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+    static_assert(IMM >= 0 && IMM < 4096, "global instruction offset range");
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
                  :
-                 : "v"(off), "s"(base), "s"(lds)
+                 : "v"(off), "s"(base), "s"(lds), "n"(IMM)
                  : "memory", "m0");
 }
+template <int IMM = 0>
 __device__ __forceinline__ void dma4(const void *base, uint32_t off, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+    static_assert(IMM >= 0 && IMM < 4096, "global instruction offset range");
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1 offset:%3"
                  :
-                 : "v"(off), "s"(base), "s"(lds)
+                 : "v"(off), "s"(base), "s"(lds), "n"(IMM)
                  : "memory", "m0");
 }
 template <int N>
@@ -270,10 +295,16 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
         }
     }
 
-    // score B fragments.  k-step ks of lane group q covers key word w = q*NKS + ks.  Centroid
-    // part: element e is coordinate 8w + {0,2,4,6,1,3,5,7}[e] (even nibbles, then odd),
-    // columns g < G hold q'_g (fp16 hi), columns G + g its lo part.  Sign part: element e is
-    // coordinate 8w + {0,4,1,5,2,6,3,7}[e], columns hold -w_g hi / lo.
+    // score products.  The query is the A operand (16 rows of query parts), the key block
+    // the B operand (16 token columns per tile), so a tile's result holds every part of
+    // every head for each of its tokens.  k-step ks of lane group q covers key word
+    // w = q*NKS + ks.  Centroid part: element e is coordinate 8w + {0,2,4,6,1,3,5,7}[e] (even
+    // nibbles, then odd), rows hold q'_g as fp16 hi and lo.  Sign part: element e is
+    // coordinate 8w + {0,4,1,5,2,6,3,7}[e], rows hold -w_g hi and lo.  Row roles: G <= 4
+    // places centroid hi, centroid lo, sign hi and sign lo of every head in disjoint rows of
+    // one accumulator (G = 1: rows 0..3 and a copy in rows 8..11; G = 2: rows 0..7; G = 4:
+    // all 16); G = 8 has one accumulator for the centroid rows (hi 0..7, lo 8..15) and one
+    // for the sign rows.
     // ---- staging setup
     const int64_t rec0 = (int64_t)bk * a.cap;
     const uint32_t *kw_s = a.kw + rec0 * S::KW;
@@ -286,27 +317,35 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
     //      packed token, so every copy reads records of this slice)
     // per-lane parts of the copies of a block (offsets from the block's first record);
     // value records go to LDS slot 4 (t % 8) + t / 8
-    uint32_t o_kw[S::N_KW], o_vw[S::N_VW], o_vs[S::N_VS], r_kw[S::N_KW], r_vw[S::N_VW], r_vs[S::N_VS];
-#pragma unroll
-    for (int i = 0; i < S::N_KW; ++i) {
-        const int c = lane + 64 * i;  // 16-byte chunk of the block's key words
-        r_kw[i] = c / (S::KW / 4);
-        o_kw[i] = r_kw[i] * (S::KW * 4) + (c % (S::KW / 4)) * 16;
-    }
+    // (copy i of a kind: record r of the block, byte column inside the record; the clamped
+    // path recomputes them, the offsets of the whole-block path stay in registers)
+    auto kw_rc = [&](int ln, int i, uint32_t &r, uint32_t &col) {
+        const int c = ln + 64 * i;  // 16-byte chunk of the block's key words
+        r = c / (S::KW / 4);
+        col = (c % (S::KW / 4)) * 16;
+    };
+    auto vw_rc = [&](int ln, int i, uint32_t &r, uint32_t &col) {
+        const int c = ln + 64 * i;
+        const int slot = c / (S::VW / 4);
+        r = 8 * (slot & 3) + (slot >> 2);
+        col = (c % (S::VW / 4)) * 16;
+    };
+    auto vs_rc = [&](int ln, int i, uint32_t &r, uint32_t &col) {
+        const int c = ln + 64 * i;  // 4-byte piece of the block's scales
+        r = c / (S::NG / 2);
+        col = (c % (S::NG / 2)) * 4;
+    };
+    // whole-block path: key words, norms and scales of a block are contiguous bytes (copy i
+    // of a lane at 16 (lane + 64 i) or 4 (lane + 64 i), the 64 i part as an immediate); the
+    // value records are permuted into LDS slot order
+    const uint32_t o16 = 16u * lane, o4 = 4u * lane;
+    uint32_t o_vw[S::N_VW];
 #pragma unroll
     for (int i = 0; i < S::N_VW; ++i) {
-        const int c = lane + 64 * i;
-        const int slot = c / (S::VW / 4);
-        r_vw[i] = 8 * (slot & 3) + (slot >> 2);
-        o_vw[i] = r_vw[i] * (S::VW * 4) + (c % (S::VW / 4)) * 16;
+        uint32_t r, col;
+        vw_rc(lane, i, r, col);
+        o_vw[i] = r * (S::VW * 4) + col;
     }
-#pragma unroll
-    for (int i = 0; i < S::N_VS; ++i) {
-        const int c = lane + 64 * i;  // 4-byte piece of the block's scales
-        r_vs[i] = c / (S::NG / 2);
-        o_vs[i] = r_vs[i] * (S::NG * 2) + (c % (S::NG / 2)) * 4;
-    }
-    const uint32_t r_kn = lane >> 1, o_kn = r_kn * 8 + (lane & 1) * 4;
     auto issue = [&](int t0, int bi) {
         const uint32_t base = lds_wave + (uint32_t)(bi * S::BUF_B);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -316,33 +355,47 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
             const float *kn_b = kn_s + (int64_t)t0 * 2;
             const uint32_t *vw_b = vw_s + (int64_t)t0 * S::VW;
             const uint16_t *vs_b = vs_s + (int64_t)t0 * S::NG;
-#pragma unroll
-            for (int i = 0; i < S::N_KW; ++i) dma16(kw_b, o_kw[i], base + 1024 * i);
-            dma4(kn_b, o_kn, base + S::OFF_KN);
+            static_assert(S::N_KW <= 4 && S::N_VS <= 16, "immediate offsets");
+            // (the immediate offsets move the LDS destination too: one M0 per section)
+            dma16<0>(kw_b, o16, base);
+            if constexpr (S::N_KW > 1) dma16<1024>(kw_b, o16, base);
+            if constexpr (S::N_KW > 2) dma16<2048>(kw_b, o16, base);
+            if constexpr (S::N_KW > 3) dma16<3072>(kw_b, o16, base);
+            dma4<0>(kn_b, o4, base + S::OFF_KN);
 #pragma unroll
             for (int i = 0; i < S::N_VW; ++i) dma16(vw_b, o_vw[i], base + S::OFF_VW + 1024 * i);
-#pragma unroll
-            for (int i = 0; i < S::N_VS; ++i) dma4(vs_b, o_vs[i], base + S::OFF_VS + 256 * i);
+            dma4<0>(vs_b, o4, base + S::OFF_VS);
+            if constexpr (S::N_VS > 1) dma4<256>(vs_b, o4, base + S::OFF_VS);
+            static_assert(S::N_VS <= 2, "scale copies");
         } else {
-            // the last block(s): token indices clamped to the last packed token
+            // the last block(s): token indices clamped to the last packed token (the lane's
+            // rows and columns are recomputed here rather than held across the loop)
+            int lane_c = lane;
+            asm volatile("" : "+v"(lane_c));
 #pragma unroll
             for (int i = 0; i < S::N_KW; ++i) {
-                const uint32_t tok = (uint32_t)min(t0 + (int)r_kw[i], last);
-                dma16(kw_s, tok * (S::KW * 4) + (o_kw[i] - r_kw[i] * (S::KW * 4)), base + 1024 * i);
+                uint32_t r, col;
+                kw_rc(lane_c, i, r, col);
+                const uint32_t tok = (uint32_t)min(t0 + (int)r, last);
+                dma16(kw_s, tok * (S::KW * 4) + col, base + 1024 * i);
             }
             {
-                const uint32_t tok = (uint32_t)min(t0 + (int)r_kn, last);
-                dma4(kn_s, tok * 8 + (o_kn - r_kn * 8), base + S::OFF_KN);
+                const uint32_t tok = (uint32_t)min(t0 + (lane_c >> 1), last);
+                dma4(kn_s, tok * 8 + (lane_c & 1) * 4, base + S::OFF_KN);
             }
 #pragma unroll
             for (int i = 0; i < S::N_VW; ++i) {
-                const uint32_t tok = (uint32_t)min(t0 + (int)r_vw[i], last);
-                dma16(vw_s, tok * (S::VW * 4) + (o_vw[i] - r_vw[i] * (S::VW * 4)), base + S::OFF_VW + 1024 * i);
+                uint32_t r, col;
+                vw_rc(lane_c, i, r, col);
+                const uint32_t tok = (uint32_t)min(t0 + (int)r, last);
+                dma16(vw_s, tok * (S::VW * 4) + col, base + S::OFF_VW + 1024 * i);
             }
 #pragma unroll
             for (int i = 0; i < S::N_VS; ++i) {
-                const uint32_t tok = (uint32_t)min(t0 + (int)r_vs[i], last);
-                dma4(vs_s, tok * (S::NG * 2) + (o_vs[i] - r_vs[i] * (S::NG * 2)), base + S::OFF_VS + 256 * i);
+                uint32_t r, col;
+                vs_rc(lane_c, i, r, col);
+                const uint32_t tok = (uint32_t)min(t0 + (int)r, last);
+                dma4(vs_s, tok * (S::NG * 2) + col, base + S::OFF_VS + 256 * i);
             }
         }
     };
@@ -350,15 +403,43 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
     const int stride = kWaves * kBlock;
     const int tw = t_begin + wave * kBlock;
     const int nblk = tw < t_end ? (t_end - tw + stride - 1) / stride : 0;
+    // the first two blocks' copies go out before the query loads below: the compiler's own
+    // waits for those then also cover these older copies, and both latencies overlap
+    if (nblk > 0) issue(tw, 0);
+    if (nblk > 1) issue(tw + stride, 1);
 
     // Both parts are pre-scaled by scale * log2(e) / sqrt(d) (the sign part also by
     // sqrt(pi/2)/d), so that the logit in log2 units is |k| (centroid part + gamma * sign part).
+    // This lane's row n16: role in the centroid and in the sign operand (0: zero row, 1: hi,
+    // 2: lo), its head, and its slot among the nonzero rows (compact LDS copy).
+    using SM = DecodeSmem<D, VB, G>;
+    int rc, rs, rg, ri;
+    if constexpr (G == 8) {
+        rg = n16 & 7;
+        rc = rs = 1 + (n16 >> 3);
+        ri = n16;
+    } else {
+        int part;  // 0: centroid hi, 1: centroid lo, 2: sign hi, 3: sign lo, -1: none
+        if constexpr (G == 1) {
+            part = (n16 & 4) ? -1 : (n16 & 3);
+            rg = 0;
+            ri = (n16 & 1) + 2 * (n16 >> 3);
+        } else if constexpr (G == 2) {
+            part = n16 < 8 ? (n16 >> 1) : -1;
+            rg = n16 & 1;
+            ri = n16 & 3;
+        } else {
+            part = n16 >> 2;
+            rg = n16 & 3;
+            ri = n16 & 7;
+        }
+        rc = part == 0 ? 1 : (part == 1 ? 2 : 0);
+        rs = part == 2 ? 1 : (part == 3 ? 2 : 0);
+    }
     u32x4_t bc[S::BLDS ? 1 : S::NKS], bs[S::BLDS ? 1 : S::NKS];
     {
         const float cs = a.scale * kLog2e * (1.0f / sqrtf((float)D)), ss = cs * kQjl;
-        const bool hic = n16 < G, loc = n16 >= G && n16 < 2 * G;
-        const int g = hic ? n16 : (loc ? n16 - G : 0);
-        const float *pq = a.prep + ((int64_t)b * a.hq + kvh * G + g) * (2 * D);
+        const float *pq = a.prep + ((int64_t)b * a.hq + kvh * G + rg) * (2 * D);
         const float *pw = pq + D;
         constexpr int ce[8] = {0, 2, 4, 6, 1, 3, 5, 7};
         constexpr int se[8] = {0, 4, 1, 5, 2, 6, 3, 7};
@@ -375,9 +456,9 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
             for (int e = 0; e < 8; ++e) {
                 _Float16 h, l;
                 split_hl(cs * vm[ce[e]], h, l);
-                hc[e] = hic ? __builtin_bit_cast(uint16_t, h) : (loc ? __builtin_bit_cast(uint16_t, l) : 0);
+                hc[e] = rc == 1 ? __builtin_bit_cast(uint16_t, h) : (rc == 2 ? __builtin_bit_cast(uint16_t, l) : 0);
                 split_hl(-ss * vs[se[e]], h, l);
-                hs[e] = hic ? __builtin_bit_cast(uint16_t, h) : (loc ? __builtin_bit_cast(uint16_t, l) : 0);
+                hs[e] = rs == 1 ? __builtin_bit_cast(uint16_t, h) : (rs == 2 ? __builtin_bit_cast(uint16_t, l) : 0);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -390,13 +471,11 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
             static_assert(!S::BLDS || S::NKS == kWaves, "one k-step per wave");
             u32x4_t fc, fs;
             frag(wave, fc, fs);
-            if (n16 < 2 * G) {
-                sm.bfrag[wave][q * 2 * G + n16] = fc;
-                sm.bfrag[S::NKS + wave][q * 2 * G + n16] = fs;
-            }
+            if (rc) sm.bfrag[wave][q * SM::NSL + ri] = fc;
+            if (rs) sm.bfrag[S::NKS + wave][q * SM::NSL + ri] = fs;
             if (lane == 0) {
-                sm.bfrag[wave][DecodeSmem<D, VB, G>::FZ] = (u32x4_t){0u, 0u, 0u, 0u};
-                sm.bfrag[S::NKS + wave][DecodeSmem<D, VB, G>::FZ] = (u32x4_t){0u, 0u, 0u, 0u};
+                sm.bfrag[wave][SM::FZ] = (u32x4_t){0u, 0u, 0u, 0u};
+                sm.bfrag[S::NKS + wave][SM::FZ] = (u32x4_t){0u, 0u, 0u, 0u};
             }
         } else {
 #pragma unroll
@@ -404,22 +483,22 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
         }
         __syncthreads();  // fragments visible (d = 128)
     }
-    const int fslot = n16 < 2 * G ? q * 2 * G + n16 : DecodeSmem<D, VB, G>::FZ;
-    // the first two blocks' copies (after the fragment loads, which the compiler waits for
-    // with its own counts)
-    if (nblk > 0) {
-        issue(tw, 0);
-        issue(tw + stride, 1);
-    }
-
-    // running reference max per head (lanes n16 == g), per-lane partial sums of p (the
-    // lane's rows), value accumulators and column sums of B
-    float m_ref = -INFINITY, l_part = 0.f;
+    const int cslot = rc ? q * SM::NSL + ri : SM::FZ, sslot = rs ? q * SM::NSL + ri : SM::FZ;
+    // The lane's logits after the score products: token row trow of the block, heads
+    // hbase .. hbase + NLR - 1.  The running reference max per head is kept in LDS (read
+    // once per block); value accumulators; per value column (head, group): sums of B and of
+    // p over the lane's tokens.
+    constexpr int NLR = G < 4 ? G : 4;
+    const int trow = (G == 2 || G == 8) ? 16 * (q >> 1) + n16 : 16 * (q & 1) + n16;
+    const int hbase = G == 8 ? 4 * (q & 1) : 0;
+    if (lane < G) sm.mref[wave][lane] = -INFINITY;
+    wave_sync();
     f32x4_t acc_v[S::NPASS][S::NT];
-    float sumb[S::NPASS];
+    float sumb[S::NPASS], lsum[S::NPASS];
 #pragma unroll
     for (int p = 0; p < S::NPASS; ++p) {
         sumb[p] = 0.f;
+        lsum[p] = 0.f;
 #pragma unroll
         for (int t = 0; t < S::NT; ++t) acc_v[p][t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     }
@@ -430,13 +509,10 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
     asm volatile("" : "+v"(kSel), "+v"(kSgn), "+v"(kOne), "+v"(kCode));
 
     auto process = [&](const unsigned char *buf, int t0) {
-        // ---- scores: centroid and sign parts on MFMA (hi and lo parts in separate columns)
-        f32x4_t accc[2], accs[2];
+        // ---- scores: query rows x token columns, centroid and sign parts on MFMA
         uint32_t wds[2][S::NKS];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            accc[tt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-            accs[tt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
             const uint32_t *kwp = reinterpret_cast<const uint32_t *>(buf) + (16 * tt + n16) * S::KW + q * S::NKS;
 #pragma unroll
             for (int i = 0; i < S::NKS / 4; ++i) {
@@ -444,15 +520,21 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
                 wds[tt][4 * i] = u[0]; wds[tt][4 * i + 1] = u[1]; wds[tt][4 * i + 2] = u[2]; wds[tt][4 * i + 3] = u[3];
             }
         }
+        constexpr int NACC = G == 8 ? 2 : 1;  // [centroid, sign] for G = 8, one stacked otherwise
+        f32x4_t acc[NACC][2];
+#pragma unroll
+        for (int j = 0; j < NACC; ++j)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) acc[j][tt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < S::NKS; ++ks) {
-            u32x4_t bck, bsk;
+            u32x4_t qc, qs;
             if constexpr (S::BLDS) {
-                bck = sm.bfrag[ks][fslot];
-                bsk = sm.bfrag[S::NKS + ks][fslot];
+                qc = sm.bfrag[ks][cslot];
+                qs = sm.bfrag[S::NKS + ks][sslot];
             } else {
-                bck = bc[ks];
-                bsk = bs[ks];
+                qc = bc[ks];
+                qs = bs[ks];
             }
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
@@ -462,72 +544,123 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
                 const uint32_t he = __builtin_amdgcn_perm(th1, th0, sel_e);
                 const uint32_t lo = __builtin_amdgcn_perm(tl1, tl0, sel_o);
                 const uint32_t ho = __builtin_amdgcn_perm(th1, th0, sel_o);
-                const u32x4_t Ac = {__builtin_amdgcn_perm(he, le, 0x05010400u), __builtin_amdgcn_perm(he, le, 0x07030602u),
+                const u32x4_t Kc = {__builtin_amdgcn_perm(he, le, 0x05010400u), __builtin_amdgcn_perm(he, le, 0x07030602u),
                                     __builtin_amdgcn_perm(ho, lo, 0x05010400u), __builtin_amdgcn_perm(ho, lo, 0x07030602u)};
-                u32x4_t As;
+                u32x4_t Ks;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) As[r] = ((word << (12 - 4 * r)) & kSgn) | kOne;
-                accc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, Ac),
-                                                                  __builtin_bit_cast(half8_t, bck), accc[tt], 0, 0, 0);
-                accs[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, As),
-                                                                  __builtin_bit_cast(half8_t, bsk), accs[tt], 0, 0, 0);
+                for (int r = 0; r < 4; ++r) Ks[r] = ((word << (12 - 4 * r)) & kSgn) | kOne;
+                acc[0][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, qc),
+                                                                    __builtin_bit_cast(half8_t, Kc), acc[0][tt], 0, 0, 0);
+                acc[NACC - 1][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    __builtin_bit_cast(half8_t, qs), __builtin_bit_cast(half8_t, Ks), acc[NACC - 1][tt], 0, 0, 0);
             }
         }
-        // lane (n16, q) holds rows 4q..4q+3 of each tile: (|k|, gamma) of those tokens
-        float lg[2][4];
-        float lmax = -INFINITY;
+        // ---- logits: hi + lo of each part and centroid + gamma * sign, gathered by row swaps
+        //      (lane rows q: 16-lane swaps exchange rows 1 <-> 0 and 3 <-> 2 of two registers,
+        //      32-lane swaps the halves)
+        float lg[NLR];
+        {
+            const float2 kn = *reinterpret_cast<const float2 *>(buf + S::OFF_KN + trow * 8);
+            const float dn = kn.x, gm = kn.y;
+            auto f2u = [](float x) { return __builtin_bit_cast(uint32_t, x); };
+            auto u2f = [](uint32_t x) { return __builtin_bit_cast(float, x); };
+            if constexpr (G == 4) {
+                // rows (tile 0, 1): [c hi | c lo | s hi | s lo] -> [c0 c1 s0 s1] -> c and s
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const float4 n01 = *reinterpret_cast<const float4 *>(buf + S::OFF_KN + (16 * tt + 4 * q) * 8);
-            const float4 n23 = *reinterpret_cast<const float4 *>(buf + S::OFF_KN + (16 * tt + 4 * q) * 8 + 16);
-            const float dn[4] = {n01.x, n01.z, n23.x, n23.z};
-            const float gm[4] = {n01.y, n01.w, n23.y, n23.w};
+                for (int i = 0; i < 4; ++i) {
+                    const auto x = __builtin_amdgcn_permlane16_swap(f2u(acc[0][0][i]), f2u(acc[0][1][i]), false, false);
+                    const float y = u2f(x[0]) + u2f(x[1]);
+                    const auto z = __builtin_amdgcn_permlane32_swap(f2u(y), f2u(y), false, false);
+                    lg[i] = dn * fmaf(gm, u2f(z[1]), u2f(z[0]));
+                }
+            } else if constexpr (G == 2) {
+                // row 0: [c hi g0 g1, c lo g0 g1], row 1: the sign part; tile 1 into rows 2, 3
+                float f[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float c = accc[tt][i] + from_lane_plus_g<G>(accc[tt][i]);
-                const float sv = accs[tt][i] + from_lane_plus_g<G>(accs[tt][i]);
-                const int tok = t0 + 16 * tt + 4 * q + i;
-                const float v = dn[i] * fmaf(gm[i], sv, c);
-                lg[tt][i] = (n16 < G && tok < t_end) ? v : -INFINITY;
-                lmax = fmaxf(lmax, lg[tt][i]);
+                for (int i = 0; i < 4; ++i)
+                    f[i] = u2f(__builtin_amdgcn_permlane32_swap(f2u(acc[0][0][i]), f2u(acc[0][1][i]), false, false)[0]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float u = f[h] + f[h + 2];  // rows [c t0, s t0, c t1, s t1]
+                    const auto z = __builtin_amdgcn_permlane16_swap(f2u(u), f2u(u), false, false);
+                    lg[h] = dn * fmaf(gm, u2f(z[1]), u2f(z[0]));
+                }
+            } else if constexpr (G == 1) {
+                // rows 0 and 2: [c hi, c lo, s hi, s lo]; tile 1 into rows 1 and 3
+                float f[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    f[i] = u2f(__builtin_amdgcn_permlane16_swap(f2u(acc[0][0][i]), f2u(acc[0][1][i]), false, false)[0]);
+                lg[0] = dn * fmaf(gm, f[2] + f[3], f[0] + f[1]);
+            } else {
+                // rows: hi g0..3, hi g4..7, lo g0..3, lo g4..7 -> tile 0 in rows 0, 1, tile 1 in 2, 3
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const auto c = __builtin_amdgcn_permlane32_swap(f2u(acc[0][0][i]), f2u(acc[0][1][i]), false, false);
+                    const auto sg = __builtin_amdgcn_permlane32_swap(f2u(acc[1][0][i]), f2u(acc[1][1][i]), false, false);
+                    lg[i] = dn * fmaf(gm, u2f(sg[0]) + u2f(sg[1]), u2f(c[0]) + u2f(c[1]));
+                }
             }
+            if (t0 + kBlock > t_end && t0 + trow >= t_end)
+#pragma unroll
+                for (int i = 0; i < NLR; ++i) lg[i] = -INFINITY;
         }
 
         // ---- online softmax with a reference max that only moves when a logit exceeds it
         //      (rare after the first block); p <= 1 always
-        if (__ballot(lmax > m_ref)) {
-            float mb = lmax;
-            mb = fmaxf(mb, __shfl_xor(mb, 16));
-            mb = fmaxf(mb, __shfl_xor(mb, 32));
-            const float m_new = fmaxf(m_ref, mb);
-            const float corr = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
-            if (n16 < G && q == 0) sm.corr[wave][n16] = corr;
-            l_part *= corr;
-            m_ref = m_new;
+        float m_ref[NLR];
+#pragma unroll
+        for (int i = 0; i < NLR; ++i) m_ref[i] = sm.mref[wave][hbase + i];
+        uint64_t gt = 0;
+#pragma unroll
+        for (int i = 0; i < NLR; ++i) gt |= __ballot(lg[i] > m_ref[i]);
+        if (gt) {
+#pragma unroll
+            for (int i = 0; i < NLR; ++i) {
+                float mb = lg[i];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o));
+                if constexpr (G != 8) mb = fmaxf(mb, __shfl_xor(mb, 16));
+                mb = fmaxf(mb, __shfl_xor(mb, 32));
+                float m_new = fmaxf(m_ref[i], mb);
+                // G <= 4: every lane holds the same heads, so the max is wave-uniform (scalar)
+                if constexpr (G != 8)
+                    m_new = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, m_new)));
+                // 2^(m_old - m_new) <= 1 (flushes to 0 far below); nothing to rescale at the start
+                const float corr = (m_ref[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref[i] - m_new);
+                m_ref[i] = m_new;
+                if (n16 == 0) {
+                    sm.corr[wave][hbase + i] = corr;
+                    sm.mref[wave][hbase + i] = m_new;
+                }
+            }
             wave_sync();
 #pragma unroll
             for (int p = 0; p < S::NPASS; ++p) {
                 const int n = n16 + 16 * p;
                 const float c = (n < S::NCOL) ? sm.corr[wave][n / S::NG] : 0.f;
                 sumb[p] *= c;
+                lsum[p] *= c;
 #pragma unroll
-                for (int t = 0; t < S::NT; ++t) acc_v[p][t] *= c;
+                for (int t = 0; t < S::NT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        // in place, so the accumulators keep their registers across the branch
+                        float e = acc_v[p][t][i];
+                        asm volatile("v_mul_f32 %0, %0, %1" : "+v"(e) : "v"(c));
+                        acc_v[p][t][i] = e;
+                    }
             }
         }
+        // p = 2^(logit - m): the argument is <= 0 (or -inf for masked tokens, giving 0)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            f32x4_t pv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pv[i] = (n16 < G) ? exp2f(lg[tt][i] - m_ref) : 0.f;
-                l_part += pv[i];
-            }
-            if (n16 < G) *reinterpret_cast<f32x4_t *>(&sm.pb[wave][n16][16 * tt + 4 * q]) = pv;
+        for (int i = 0; i < NLR; ++i) {
+            sm.pb[wave][hbase + i][trow] = __builtin_amdgcn_exp2f(lg[i] - m_ref[i]);
         }
         wave_sync();
 
         // ---- values: B = p * scale in columns (head, group), hi + lo; A = codes of row n16
-        half8_t bv_hi[S::NPASS], bv_lo[S::NPASS];
+        u32x4_t bv_hi[S::NPASS], bv_lo[S::NPASS];
 #pragma unroll
         for (int p = 0; p < S::NPASS; ++p) {
             const int n = n16 + 16 * p;
@@ -535,16 +668,23 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
             const int gg = col ? n / S::NG : 0, grp = col ? n % S::NG : 0;
             const f32x4_t p0 = *reinterpret_cast<const f32x4_t *>(&sm.pb[wave][gg][8 * q]);
             const f32x4_t p1 = *reinterpret_cast<const f32x4_t *>(&sm.pb[wave][gg][8 * q + 4]);
-            const uint16_t *scl = reinterpret_cast<const uint16_t *>(buf + S::OFF_VS) + 8 * q * S::NG + grp;
+            float pe[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            lsum[p] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+            if constexpr (S::NCOL % 16 != 0)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float sc = (float)__builtin_bit_cast(_Float16, scl[e * S::NG]);
-                const float bvv = col ? (e < 4 ? p0[e] : p1[e - 4]) * sc : 0.f;
-                sumb[p] += bvv;
-                _Float16 h, l;
-                split_hl(bvv, h, l);
-                bv_hi[p][e] = h;
-                bv_lo[p][e] = l;
+                for (int e = 0; e < 8; ++e) pe[e] = col ? pe[e] : 0.f;
+            const _Float16 *scl = reinterpret_cast<const _Float16 *>(buf + S::OFF_VS) + 8 * q * S::NG + grp;
+            typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+            const h2_t ones = __builtin_bit_cast(h2_t, kOne);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t h, l;
+                mix_hl2(pe[2 * i], scl[2 * i * S::NG], pe[2 * i + 1], scl[(2 * i + 1) * S::NG], h, l);
+                bv_hi[p][i] = h;
+                bv_lo[p][i] = l;
+                // column sums of B as the products see them (hi + lo)
+                sumb[p] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, h), ones, sumb[p], false);
+                sumb[p] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, l), ones, sumb[p], false);
             }
         }
         // row n16's code run of each of the lane's 8 tokens (8q .. 8q+7, LDS slot 4e + q), as
@@ -588,41 +728,34 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
             const half8_t av = __builtin_bit_cast(half8_t, avu);
 #pragma unroll
             for (int p = 0; p < S::NPASS; ++p) {
-                acc_v[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv_hi[p], acc_v[p][t], 0, 0, 0);
-                acc_v[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv_lo[p], acc_v[p][t], 0, 0, 0);
+                acc_v[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, bv_hi[p]), acc_v[p][t], 0, 0, 0);
+                acc_v[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, bv_lo[p]), acc_v[p][t], 0, 0, 0);
             }
         }
         wave_sync();  // this wave's p slots are rewritten by its next block
     };
 
     // ---- the wave's blocks: t_begin + wave*32 + k*128 < t_end, two staging buffers, the
-    //      next block's copies in flight while the current one is computed
-    if (nblk > 0) {
-        for (int k = 0;; k += 2) {
-            wait_vm<S::N_DMA>();
-            process(&sm.stage[wave][0][0], tw + k * stride);
-            if (k + 1 >= nblk) break;
-            issue(tw + (k + 2) * stride, 0);
-            wait_vm<S::N_DMA>();
-            process(&sm.stage[wave][1][0], tw + (k + 1) * stride);
-            if (k + 2 >= nblk) break;
-            issue(tw + (k + 3) * stride, 1);
-        }
-        wait_vm<0>();  // the trailing prefetch lands before the buffers are reused
+    //      next block's copies in flight while the current one is computed.  Only blocks of
+    //      the split are copied: before the last one every copy is waited for.
+    for (int k = 0; k < nblk; ++k) {
+        if (k + 1 < nblk) wait_vm<S::N_DMA>(); else wait_vm<0>();
+        process(&sm.stage[wave][k & 1][0], tw + k * stride);
+        if (k + 2 < nblk) issue(tw + (k + 2) * stride, k & 1);
     }
     __syncthreads();  // every wave is done with its staging buffers (aliased by wo below)
 
     // ---- wave results: m, l per head; o[g][c] from the accumulators and the column sums of B
-    l_part += __shfl_xor(l_part, 16);
-    l_part += __shfl_xor(l_part, 32);
+    if (lane < G) sm.wm[wave][lane] = sm.mref[wave][lane];
 #pragma unroll
     for (int p = 0; p < S::NPASS; ++p) {
         sumb[p] += __shfl_xor(sumb[p], 16);
         sumb[p] += __shfl_xor(sumb[p], 32);
-    }
-    if (n16 < G && q == 0) {
-        sm.wm[wave][n16] = m_ref;
-        sm.wl[wave][n16] = l_part;
+        lsum[p] += __shfl_xor(lsum[p], 16);
+        lsum[p] += __shfl_xor(lsum[p], 32);
+        // column (head, group 0) holds the head's sum of p
+        const int n = n16 + 16 * p;
+        if (q == 0 && n < S::NCOL && n % S::NG == 0) sm.wl[wave][n / S::NG] = lsum[p];
     }
 #pragma unroll
     for (int p = 0; p < S::NPASS; ++p) {
@@ -642,22 +775,42 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
 }
 
 // ------------------------------------------------------------------ ring split (VALU)
-// The exact fp16 ring tokens of one (batch, kv head): scores by one thread per token (its key
-// row loaded whole, then G dot products against q in LDS), block-wide softmax statistics, and
-// values by threads that own a pair of coordinates and a residue class of tokens (one 4-byte
-// load per token, many in flight), reduced through LDS.  Writes the split's (m, l, o).
-template <int D, int VB, int G>
-__device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk, int b, int kvh, float *pp,
-                           float *pml) {
-    constexpr int NCP = D / 2;             // coordinate pairs
-    constexpr int NTG = kThreads / NCP;    // token residue classes of the value pass
+// Ring tokens [r0, r1) of one (batch, kv head), exact fp16: scores by four threads per token
+// (a quarter of the key row each, G dot products against q in LDS, summed across the four
+// lanes), block-wide softmax statistics, and values by threads that own a pair of
+// coordinates and a residue class of tokens (one 4-byte load per token, all of a chunk in
+// flight), reduced through LDS.  The first chunk's loads are issued before the query is
+// staged.  Writes the split's (m, l, o).
+template <int D, int G>
+__device__ void ring_split(const DecodeArgs &a, RingSmem<D, G> &sm, int bk, int b, int kvh, int r0, int r1,
+                           float *pp, float *pml) {
+    constexpr int NCP = D / 2;                 // coordinate pairs
+    constexpr int NTG = kThreads / NCP;        // token residue classes of the value pass
+    constexpr int QD = D / 4;                  // coordinates per scoring thread
+    constexpr int TPL = kRingChunk / NTG;      // value tokens per lane and chunk
+    static_assert(kThreads / 4 == kRingChunk, "one scoring pass per chunk");
     const int tid = threadIdx.x;
+    const int cp = tid % NCP, tg = tid / NCP, part = tid & 3, tk = tid >> 2;
+    const uint16_t *rk = a.rk + (int64_t)bk * a.buffer_size * D;
+    const uint32_t *rv2 = reinterpret_cast<const uint32_t *>(a.rv + (int64_t)bk * a.buffer_size * D);
+    uint4 k4[QD / 8];
+    uint32_t v2[TPL];
+    auto load_chunk = [&](int c0, int cnt) {
+        const uint4 *kr = reinterpret_cast<const uint4 *>(rk + (int64_t)(c0 + min(tk, cnt - 1)) * D + part * QD);
+#pragma unroll
+        for (int i = 0; i < QD / 8; ++i) k4[i] = kr[i];
+#pragma unroll
+        for (int u = 0; u < TPL; ++u) {
+            const int tt = tg + u * NTG;
+            v2[u] = tt < cnt ? rv2[(int64_t)(c0 + tt) * NCP + cp] : 0u;
+        }
+    };
+    load_chunk(r0, min(kRingChunk, r1 - r0));
     for (int i = tid; i < G * D; i += kThreads) {
         const int g = i / D, j = i - g * D;
-        sm.x.ring_q[g][j] = load_q(a, ((int64_t)b * a.hq + kvh * G + g) * D + j);
+        sm.q[g][j / QD][j % QD] = load_q(a, ((int64_t)b * a.hq + kvh * G + g) * D + j);
     }
     __syncthreads();
-    const int cp = tid % NCP, tg = tid / NCP;
     float m_run[G], l_run[G], o0[G], o1[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -666,86 +819,96 @@ __device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk
         o0[g] = 0.f;
         o1[g] = 0.f;
     }
-    const uint16_t *rk = a.rk + (int64_t)bk * a.buffer_size * D;
-    const uint32_t *rv2 = reinterpret_cast<const uint32_t *>(a.rv + (int64_t)bk * a.buffer_size * D);
-    for (int c0 = 0; c0 < a.n_ring; c0 += kRingChunk) {
-        const int cnt = min(kRingChunk, a.n_ring - c0);
-        float lg[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) lg[g] = -INFINITY;
-        if (tid < cnt) {
-            const uint4 *kr = reinterpret_cast<const uint4 *>(rk + (int64_t)(c0 + tid) * D);
+    const float lscale = a.scale * kLog2e;
+    for (int c0 = r0; c0 < r1; c0 += kRingChunk) {
+        const int cnt = min(kRingChunk, r1 - c0);
+        if (c0 != r0) load_chunk(c0, cnt);
+        // logits (log2 units) of the chunk into sm.p
+        {
             float acc[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) acc[g] = 0.f;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint4 k4[D / 16];
+            for (int i = 0; i < QD / 8; ++i) {
+                const float kv[8] = {f16_lo(k4[i].x), f16_hi(k4[i].x), f16_lo(k4[i].y), f16_hi(k4[i].y),
+                                     f16_lo(k4[i].z), f16_hi(k4[i].z), f16_lo(k4[i].w), f16_hi(k4[i].w)};
 #pragma unroll
-                for (int i = 0; i < D / 16; ++i) k4[i] = kr[h * (D / 16) + i];
-#pragma unroll
-                for (int i = 0; i < D / 16; ++i) {
-                    const int c = 8 * (h * (D / 16) + i);
-                    const float kv[8] = {f16_lo(k4[i].x), f16_hi(k4[i].x), f16_lo(k4[i].y), f16_hi(k4[i].y),
-                                         f16_lo(k4[i].z), f16_hi(k4[i].z), f16_lo(k4[i].w), f16_hi(k4[i].w)};
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const float4 q0 = *reinterpret_cast<const float4 *>(&sm.x.ring_q[g][c]);
-                        const float4 q1 = *reinterpret_cast<const float4 *>(&sm.x.ring_q[g][c + 4]);
-                        acc[g] = fmaf(q0.x, kv[0], acc[g]);
-                        acc[g] = fmaf(q0.y, kv[1], acc[g]);
-                        acc[g] = fmaf(q0.z, kv[2], acc[g]);
-                        acc[g] = fmaf(q0.w, kv[3], acc[g]);
-                        acc[g] = fmaf(q1.x, kv[4], acc[g]);
-                        acc[g] = fmaf(q1.y, kv[5], acc[g]);
-                        acc[g] = fmaf(q1.z, kv[6], acc[g]);
-                        acc[g] = fmaf(q1.w, kv[7], acc[g]);
-                    }
+                for (int g = 0; g < G; ++g) {
+                    const float4 q0 = *reinterpret_cast<const float4 *>(&sm.q[g][part][8 * i]);
+                    const float4 q1 = *reinterpret_cast<const float4 *>(&sm.q[g][part][8 * i + 4]);
+                    acc[g] = fmaf(q0.x, kv[0], acc[g]);
+                    acc[g] = fmaf(q0.y, kv[1], acc[g]);
+                    acc[g] = fmaf(q0.z, kv[2], acc[g]);
+                    acc[g] = fmaf(q0.w, kv[3], acc[g]);
+                    acc[g] = fmaf(q1.x, kv[4], acc[g]);
+                    acc[g] = fmaf(q1.y, kv[5], acc[g]);
+                    acc[g] = fmaf(q1.z, kv[6], acc[g]);
+                    acc[g] = fmaf(q1.w, kv[7], acc[g]);
                 }
             }
 #pragma unroll
-            for (int g = 0; g < G; ++g) lg[g] = acc[g] * (a.scale * kLog2e);
+            for (int g = 0; g < G; ++g) {
+                acc[g] += __shfl_xor(acc[g], 1);
+                acc[g] += __shfl_xor(acc[g], 2);
+            }
+            if (part == 0)
+#pragma unroll
+                for (int g = 0; g < G; ++g) sm.p[tk][g] = tk < cnt ? acc[g] * lscale : -INFINITY;
         }
+        __syncthreads();
+        float lg[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) lg[g] = tid < kRingChunk ? sm.p[tid][g] : -INFINITY;
         float mx[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) mx[g] = lg[g];
-        block_reduce<G, true>(mx, sm.ring_red);
+        block_reduce<G, true>(mx, sm.red);  // its first barrier also ends every read of the logits
         float pe[G], corr[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const float mnew = fmaxf(m_run[g], mx[g]);
             corr[g] = (m_run[g] == -INFINITY) ? 0.f : exp2f(m_run[g] - mnew);
             pe[g] = (tid < cnt) ? exp2f(lg[g] - mnew) : 0.f;
-            sm.x.ring_p[g][tid] = pe[g];
+            if (tid < kRingChunk) sm.p[tid][g] = pe[g];
             m_run[g] = mnew;
         }
-        block_reduce<G, false>(pe, sm.ring_red);  // its barriers also publish ring_p
+        block_reduce<G, false>(pe, sm.red);  // its barriers also publish p
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             l_run[g] = l_run[g] * corr[g] + pe[g];
             o0[g] *= corr[g];
             o1[g] *= corr[g];
         }
-        // values: coordinates 2cp, 2cp + 1 over tokens tg, tg + NTG, ...
-#pragma unroll 8
-        for (int tt = tg; tt < cnt; tt += NTG) {
-            const uint32_t v2 = rv2[(int64_t)(c0 + tt) * NCP + cp];
-            const float va = f16_lo(v2), vb = f16_hi(v2);
+        // values: coordinates 2cp, 2cp + 1 over tokens tg, tg + NTG, ... (p past cnt is 0)
+#pragma unroll
+        for (int u = 0; u < TPL; ++u) {
+            const int tt = tg + u * NTG;
+            const float va = f16_lo(v2[u]), vb = f16_hi(v2[u]);
+            float pg[G];
+            if constexpr (G >= 4) {
+#pragma unroll
+                for (int g4 = 0; g4 < G; g4 += 4) {
+                    const float4 p4 = *reinterpret_cast<const float4 *>(&sm.p[tt][g4]);
+                    pg[g4] = p4.x; pg[g4 + 1] = p4.y; pg[g4 + 2] = p4.z; pg[g4 + 3] = p4.w;
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < G; ++g) pg[g] = sm.p[tt][g];
+            }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const float pg = sm.x.ring_p[g][tt];
-                o0[g] = fmaf(pg, va, o0[g]);
-                o1[g] = fmaf(pg, vb, o1[g]);
+                o0[g] = fmaf(pg[g], va, o0[g]);
+                o1[g] = fmaf(pg[g], vb, o1[g]);
             }
         }
-        __syncthreads();  // ring_p is rewritten by the next chunk
+        __syncthreads();  // p is rewritten by the next chunk
     }
-    // reduce the token classes through LDS (wo is free in the ring split)
+    // reduce the token classes through LDS
     if (tg > 0)
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            sm.x.wo[tg - 1][g][2 * cp] = o0[g];
-            sm.x.wo[tg - 1][g][2 * cp + 1] = o1[g];
+            sm.wo[tg - 1][g][2 * cp] = o0[g];
+            sm.wo[tg - 1][g][2 * cp + 1] = o1[g];
         }
     __syncthreads();
     if (tg == 0) {
@@ -753,8 +916,8 @@ __device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk
         for (int t2 = 0; t2 < NTG - 1; ++t2)
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                o0[g] += sm.x.wo[t2][g][2 * cp];
-                o1[g] += sm.x.wo[t2][g][2 * cp + 1];
+                o0[g] += sm.wo[t2][g][2 * cp];
+                o1[g] += sm.wo[t2][g][2 * cp + 1];
             }
 #pragma unroll
         for (int g = 0; g < G; ++g) *reinterpret_cast<float2 *>(&pp[g * D + 2 * cp]) = make_float2(o0[g], o1[g]);
@@ -765,6 +928,30 @@ __device__ void ring_split(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk
                 pml[g * 2 + 1] = l_run[g];
             }
     }
+}
+
+// ------------------------------------------------------------------ prep and ring launch
+// With ring tokens, workgroups 0 .. batch*hkv*R - 1 compute ring split r of one slice each
+// (R = n_split_total - n_split splits of ring_per_split tokens; first, as they are the longer
+// ones); the next batch*hq prepare one query head each.  Both only read the query and the
+// ring, so they share one launch ahead of the packed splits.
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? (G == 8 ? 3 : 4) : (G == 8 ? 2 : 3), 8)))
+void k_decode_prep(DecodeArgs a) {
+    const int R = a.n_split_total - a.n_split;
+    const int64_t nr = a.n_ring > 0 ? (int64_t)a.batch * a.hkv * R : 0;
+    if ((int64_t)blockIdx.x >= nr) {
+        prep_head<D>(a, (int64_t)blockIdx.x - nr);
+        return;
+    }
+    __shared__ RingSmem<D, G> rsm;
+    const int bk = (int)blockIdx.x / R, r = (int)blockIdx.x % R;
+    const int b = bk / a.hkv, kvh = bk - b * a.hkv;
+    const int n_total = a.n_split_total, split = a.n_split + r;
+    float *pp = a.partial + ((int64_t)bk * n_total + split) * G * D;
+    float *pml = a.partial_ml + ((int64_t)bk * n_total + split) * G * 2;
+    const int r0 = r * a.ring_per_split, r1 = min(a.n_ring, r0 + a.ring_per_split);
+    ring_split<D, G>(a, rsm, bk, b, kvh, r0, r1, pp, pml);
 }
 
 // ------------------------------------------------------------------ main kernel
@@ -781,14 +968,14 @@ void k_decode_main(DecodeArgs a) {
     using S = DecodeShape<D, VB, G>;
     __shared__ DecodeSmem<D, VB, G> sm;
     const int tid = threadIdx.x;
-    const int split = blockIdx.x;
-    const int bk = blockIdx.y;  // b * hkv + kv head == slice
+    const int split = blockIdx.x;  // packed splits only (the ring split runs with the prep)
+    const int bk = blockIdx.y;     // b * hkv + kv head == slice
     const int b = bk / a.hkv, kvh = bk - b * a.hkv;
     const int n_total = a.n_split_total;
     float *pp = a.partial + ((int64_t)bk * n_total + split) * G * D;
     float *pml = a.partial_ml + ((int64_t)bk * n_total + split) * G * 2;
 
-    if (split < a.n_split) {
+    {
         const int t_begin = split * (int)a.per_split;
         const int t_end = (int)min(a.n_packed, (int64_t)t_begin + a.per_split);
         packed_wave<D, VB, G>(a, sm, bk, b, kvh, t_begin, t_end);
@@ -815,8 +1002,6 @@ void k_decode_main(DecodeArgs a) {
                 pml[g * 2 + 1] = L;
             }
         }
-    } else {
-        ring_split<D, VB, G>(a, sm, bk, b, kvh, pp, pml);
     }
 }
 
@@ -914,32 +1099,24 @@ __global__ __launch_bounds__(256) void k_ring_append(const void *kn, const void 
 }
 
 // ------------------------------------------------------------------ launchers
+template <int D, int VB, int G>
+static void launch_g(const DecodeArgs &a, hipStream_t st) {
+    const unsigned pgrid =
+        (unsigned)(a.batch * a.hq + (a.n_ring > 0 ? a.batch * a.hkv * (a.n_split_total - a.n_split) : 0));
+    hipLaunchKernelGGL((k_decode_prep<D, G>), dim3(pgrid), dim3(kThreads), 0, st, a);
+    if (a.n_split > 0)
+        hipLaunchKernelGGL((k_decode_main<D, VB, G>), dim3((unsigned)a.n_split, (unsigned)(a.batch * a.hkv)),
+                           dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((k_decode_merge<D, G>), dim3((unsigned)(a.batch * a.hkv * G)), dim3(kThreads), 0, st, a);
+}
+
 template <int D, int VB>
 static hipError_t launch_main_dv(int G, const DecodeArgs &a, hipStream_t st) {
-    dim3 grid((unsigned)a.n_split_total, (unsigned)(a.batch * a.hkv));
-    const unsigned pgrid = (unsigned)(a.batch * a.hq);
-    const unsigned mgrid = (unsigned)(a.batch * a.hkv * G);
     switch (G) {
-        case 1:
-            hipLaunchKernelGGL((k_decode_prep<D>), dim3(pgrid), dim3(kThreads), 0, st, a);
-            hipLaunchKernelGGL((k_decode_main<D, VB, 1>), grid, dim3(kThreads), 0, st, a);
-            hipLaunchKernelGGL((k_decode_merge<D, 1>), dim3(mgrid), dim3(kThreads), 0, st, a);
-            break;
-        case 2:
-            hipLaunchKernelGGL((k_decode_prep<D>), dim3(pgrid), dim3(kThreads), 0, st, a);
-            hipLaunchKernelGGL((k_decode_main<D, VB, 2>), grid, dim3(kThreads), 0, st, a);
-            hipLaunchKernelGGL((k_decode_merge<D, 2>), dim3(mgrid), dim3(kThreads), 0, st, a);
-            break;
-        case 4:
-            hipLaunchKernelGGL((k_decode_prep<D>), dim3(pgrid), dim3(kThreads), 0, st, a);
-            hipLaunchKernelGGL((k_decode_main<D, VB, 4>), grid, dim3(kThreads), 0, st, a);
-            hipLaunchKernelGGL((k_decode_merge<D, 4>), dim3(mgrid), dim3(kThreads), 0, st, a);
-            break;
-        default:
-            hipLaunchKernelGGL((k_decode_prep<D>), dim3(pgrid), dim3(kThreads), 0, st, a);
-            hipLaunchKernelGGL((k_decode_main<D, VB, 8>), grid, dim3(kThreads), 0, st, a);
-            hipLaunchKernelGGL((k_decode_merge<D, 8>), dim3(mgrid), dim3(kThreads), 0, st, a);
-            break;
+        case 1: launch_g<D, VB, 1>(a, st); break;
+        case 2: launch_g<D, VB, 2>(a, st); break;
+        case 4: launch_g<D, VB, 4>(a, st); break;
+        default: launch_g<D, VB, 8>(a, st); break;
     }
     return hipGetLastError();
 }

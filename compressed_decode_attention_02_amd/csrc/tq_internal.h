@@ -57,7 +57,8 @@ struct DecodeArgs {
     int n_ring;
     int batch, hq, hkv;
     int n_split;        // splits over the packed tokens
-    int n_split_total;  // n_split, plus one split for the ring tokens when there are any
+    int n_split_total;  // n_split, plus the ring splits when there are ring tokens
+    int ring_per_split; // ring tokens per ring split
     int64_t per_split;  // packed tokens per split
     float scale;
     float *out;
