@@ -153,16 +153,23 @@ __device__ __forceinline__ void quant_group(const float (&v)[32], float sc, uint
 }
 
 // ------------------------------------------------------------------------------ keys (and values)
-// Launch shape: persistent workgroups that loop over tiles of rows (the S copy in LDS is
-// made once per workgroup); latency is hidden by the other waves of the SIMD (3 per SIMD,
-// <= 168 VGPRs).  d = 128: 4-wave groups, 3 per CU (33 KB of LDS each); d = 256: 12-wave
-// groups, one per CU (sharing one 130 KB LDS copy of S).  Measured alternative: 16-token
-// waves at d = 128 (5 per SIMD) are slower -- each S fragment read from LDS then serves
-// half as many tokens.
+// Launch shape: one persistent 12-wave workgroup per CU (one LDS copy of S: 33 KB at d = 128,
+// 130 KB at d = 256), 3 waves per SIMD (<= 168 VGPRs).  Workgroup g owns the wave tiles (R
+// rows each) g, g + G, g + 2G, ... and its waves take the next one from an LDS counter, so
+// the waves of a CU finish together.  (With several workgroups per CU on a static split, the
+// first-dispatched one was measured to finish at about half the time of the last.)
+// Measured alternative: 16-token waves at d = 128 (5 per SIMD) are slower -- each S fragment
+// read from LDS then serves half as many tokens.
 template <int D>
-constexpr int kKeyGroupWaves = D == 128 ? 4 : 12;
-template <int D>
-constexpr int kKeyGroupsPerCU = D == 128 ? 3 : 1;
+constexpr int kKeyGroupWaves = 12;
+
+// waves per workgroup (at least 4, which the S copy relies on): 12 (one workgroup per CU)
+// once the waves have a tile each on average, else 4, so that short inputs spread over more
+// CUs (d = 256: its LDS copy of S allows one workgroup per CU, so always 12)
+static int quant_waves_per_group(int d, int64_t tiles, int64_t cus) {
+    if (d != 128) return 12;
+    return tiles >= cus * 12 ? 12 : 4;
+}
 template <int D>
 constexpr int kKeyWavesPerSimd = 3;
 // S rows in LDS are padded by 8 bytes (2 banks): the 8-byte A-fragment reads of 32
@@ -192,7 +199,6 @@ __attribute__((amdgpu_waves_per_eu(kKeyWavesPerSimd<D>, kKeyWavesPerSimd<D>)))
 void k_quant_kv(QuantArgs a) {
     using S = KeyShape<D>;
     constexpr int R = S::R;
-    constexpr int NT = 64 * kKeyGroupWaves<D>;
     constexpr bool kF32 = std::is_same_v<Tag, f32_tag>;
     constexpr bool kF16 = std::is_same_v<Tag, f16_tag>;
     constexpr int RAWW = kF32 ? 8 : 4;
@@ -205,19 +211,35 @@ void k_quant_kv(QuantArgs a) {
         const uint32_t w = a.sign_bits[c >> 5] >> (c & 31);
         smask[threadIdx.x] = ((w & 1u) << 15) | ((w & 2u) << 30);
     }
-    for (int i = threadIdx.x; i < D * D / 8; i += NT) {  // 16-byte chunks of S
-        const int j = i / (D / 8), c = (i % (D / 8)) * 8;
-        const uint4 x = *reinterpret_cast<const uint4 *>(a.S + (int64_t)j * D + c);
-        uint2 *dst = reinterpret_cast<uint2 *>(&sS[j * kSRow<D> + c]);
-        dst[0] = make_uint2(x.x, x.y);
-        dst[1] = make_uint2(x.z, x.w);
+    {
+        // 16-byte chunks of S: every load of the thread issued before the LDS stores (the
+        // block has at least 256 threads at d = 128 and 768 at d = 256)
+        constexpr int NCH = D * D / 8, KMAX = D == 128 ? NCH / 256 : (NCH + 767) / 768;
+        uint4 x[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int i = threadIdx.x + k * blockDim.x;
+            if (i < NCH) x[k] = *reinterpret_cast<const uint4 *>(a.S + (int64_t)(i / (D / 8)) * D + (i % (D / 8)) * 8);
+        }
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int i = threadIdx.x + k * blockDim.x;
+            if (i < NCH) {
+                uint2 *dst = reinterpret_cast<uint2 *>(&sS[(i / (D / 8)) * kSRow<D> + (i % (D / 8)) * 8]);
+                dst[0] = make_uint2(x[k].x, x[k].y);
+                dst[1] = make_uint2(x[k].z, x[k].w);
+            }
+        }
     }
+    // this workgroup's wave tiles blockIdx.x + c * gridDim.x (c = 0, 1, ...: all workgroups
+    // move through the rows together), handed out one at a time
+    const int64_t n_tiles = (a.n_rows + R - 1) / R;
+    __shared__ unsigned long long next_tile;
+    if (threadIdx.x == 0) next_tile = 0ull;
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
     const int n = lane % R, g = lane / R;
-    const int64_t my = (int64_t)(threadIdx.x >> 6) * R + n;  // row offset inside a group tile
-    const int64_t stride = (int64_t)gridDim.x * kKeyGroupWaves<D> * R;
     const double inv_tok = 1.0 / (double)a.n_tokens;
 
     // raw inputs of one row: k-step s holds coordinates K s + 8 g + 0..7 (rows past the end
@@ -262,6 +284,7 @@ void k_quant_kv(QuantArgs a) {
                 hf[v][w] = pair;
             }
     }
+    // the positive decision boundaries b_4 < b_5 < b_6 (the codebook is symmetric), scaled by 2^8
     const uint32_t K4 = __float_as_uint(256.f * a.boundaries[4]);
     const uint32_t K5 = __float_as_uint(256.f * a.boundaries[5]);
     const uint32_t K6 = __float_as_uint(256.f * a.boundaries[6]);
@@ -273,9 +296,13 @@ void k_quant_kv(QuantArgs a) {
     float M3 = __uint_as_float((__float_as_uint(256.f * a.centroids[7]) & ~7u) | 7u);
     asm volatile("" : "+v"(M0), "+v"(M1), "+v"(M2), "+v"(M3));
 
-    int64_t base = (int64_t)blockIdx.x * kKeyGroupWaves<D> * R;
-    for (; base < a.n_rows; base += stride) {
-        const int64_t row = base + my;
+    for (;;) {
+        int64_t tile = 0;
+        if (lane == 0) tile = (int64_t)atomicAdd(&next_tile, 1ull) * gridDim.x + blockIdx.x;
+        tile = (int64_t)__builtin_amdgcn_readfirstlane((int)tile) |
+               ((int64_t)__builtin_amdgcn_readfirstlane((int)(tile >> 32)) << 32);
+        if (tile >= n_tiles) break;
+        const int64_t row = tile * R + n;
         load_raw(row);
         int64_t rec = -1;  // destination record, -1 past the last row
         if (row < a.n_rows) {
@@ -415,8 +442,10 @@ void k_quant_kv(QuantArgs a) {
             }
         }
 
-        // ---- encode: u' = 2^8 u; key = |u'| as an integer, +1 when u' <= 0 so that
-        //      equality with a boundary falls in the lower cell on the negative side too
+        // ---- encode.  u' = 2^8 u = 2^8 y / sqrt(d |k|^2); the cell of u follows from |u'|
+        //      against the scaled positive boundaries and the side u > 0 or u <= 0 (a zero
+        //      row gives u = 0, cell 3, as the count of boundaries strictly below 0).  A tie
+        //      with a boundary may land in either neighbouring cell.
         const float knorm = sqrtf(ss);
         const float inv256 = ss > 0.f ? 256.f / sqrtf((float)D * ss) : 0.f;
         uint32_t P[S::NP];  // nibble half-words: slot f at bit 4 (f & 7) of P[f >> 3]
@@ -437,7 +466,7 @@ void k_quant_kv(QuantArgs a) {
                 const float yv = y[f / S::RPT][f % S::RPT];
                 const float u = yv * inv256;
                 const bool nonpos = !(u > 0.f);
-                const uint32_t key = (__float_as_uint(u) & 0x7fffffffu) + (nonpos ? 1u : 0u);
+                const uint32_t key = __float_as_uint(u) & 0x7fffffffu;  // |u'| as an ordered integer
                 const bool c4 = key > K4, c5 = key > K5, c6 = key > K6;
                 // signed tagged centroid: sign = (u <= 0), low bits = 4 + #{boundaries passed}
                 const float mt = c6 ? M3 : (c5 ? M2 : (c4 ? M1 : M0));
@@ -546,11 +575,13 @@ void k_quant_kv(QuantArgs a) {
 // ------------------------------------------------------------------------------ launch
 template <typename Tag, int D, int VB>
 static void launch_kv_t(const QuantArgs &a, hipStream_t st) {
-    const int64_t rows_per_group = (int64_t)kKeyGroupWaves<D> * KeyShape<D>::R;
-    const int64_t groups = (a.n_rows + rows_per_group - 1) / rows_per_group;
-    const int64_t resident = (int64_t)device_cus() * kKeyGroupsPerCU<D>;
-    const int64_t grid = groups < resident ? groups : resident;
-    hipLaunchKernelGGL((k_quant_kv<Tag, D, VB>), dim3((unsigned)grid), dim3(64 * kKeyGroupWaves<D>), 0, st, a);
+    const int64_t tiles = (a.n_rows + KeyShape<D>::R - 1) / KeyShape<D>::R;
+    const int64_t cus = (int64_t)device_cus();
+    const int nw = quant_waves_per_group(D, tiles, cus);
+    const int64_t per_cu = kKeyGroupWaves<D> / nw;  // workgroups of nw waves resident per CU
+    int64_t grid = (tiles + nw - 1) / nw;
+    if (grid > cus * per_cu) grid = cus * per_cu;
+    hipLaunchKernelGGL((k_quant_kv<Tag, D, VB>), dim3((unsigned)grid), dim3(64 * nw), 0, st, a);
 }
 
 template <typename Tag>
