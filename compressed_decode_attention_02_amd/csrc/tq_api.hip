@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int64_t kSplitQuantum = 128;     // tokens per pass of a split's four waves (4 x 32)
+constexpr int64_t kSplitQuantum = 128;     // split sizes are multiples of four 32-token blocks
 constexpr int64_t kMinSplitTokens = 512;   // at least four blocks per wave
 constexpr int64_t kMaxRingSplits = 8;      // ring splits per slice (64 tokens or more each)
 constexpr int64_t kMaxSplits = 255 - kMaxRingSplits;  // the merge keeps one weight per split in LDS
@@ -27,19 +27,29 @@ bool tables_ok(const tq_tables *t) {
     return t && t->centroids && t->boundaries && t->sign_bits && t->qjl_S && aligned16(t->qjl_S);
 }
 
-// decode workgroups resident per CU (LDS and registers; see the decode kernel's budget): the
-// split count fills one such wave of workgroups on the current device
-int64_t decode_target_wgs(int d, int vb, int64_t G) {
-    return (int64_t)tq::device_cus() * ((d == 128 && G <= 4) ? (vb == 2 ? 4 : 3) : 2);
+// waves per decode workgroup: 12 (one workgroup per CU; d = 128 with up to 4 query heads per
+// kv head) when every wave then has at least 6 blocks of 32 tokens, else 4
+int decode_waves(int d, int64_t G, int64_t slices, int64_t n_packed) {
+    if (d != 128 || G > 4) return 4;
+    const int64_t blocks_per_wave = slices * n_packed / ((int64_t)tq::device_cus() * 12 * 32);
+    return blocks_per_wave >= 6 ? 12 : 4;
 }
 
-int64_t decode_splits(int d, int vb, int64_t G, int64_t slices, int64_t n_packed) {
+// decode workgroups resident per CU (LDS and registers; see the decode kernel's budget): the
+// split count fills one such wave of workgroups on the current device
+int64_t decode_target_wgs(int d, int vb, int64_t G, int waves) {
+    const int64_t cus = tq::device_cus();
+    if (waves == 12) return cus;
+    return cus * ((d == 128 && G <= 4) ? (vb == 2 ? 4 : 3) : 2);
+}
+
+// (4-wave workgroups give the most splits: the workspace is sized with them)
+int64_t decode_splits(int d, int vb, int64_t G, int64_t slices, int64_t n_packed, int waves) {
     const int64_t by_tokens = std::max<int64_t>(1, (n_packed + kMinSplitTokens - 1) / kMinSplitTokens);
-    const int64_t want = std::max<int64_t>(1, (decode_target_wgs(d, vb, G) + slices - 1) / slices);
+    const int64_t want = std::max<int64_t>(1, (decode_target_wgs(d, vb, G, waves) + slices - 1) / slices);
     return std::min({by_tokens, want, kMaxSplits});
 }
 
-// tokens per split: a whole number of four-wave passes; then as few splits as cover n_packed
 // ring splits of n_ring tokens (each a multiple of 64 tokens, at most kMaxRingSplits)
 int64_t ring_per_split(int64_t n_ring) {
     const int64_t per = (n_ring + kMaxRingSplits - 1) / kMaxRingSplits;
@@ -53,9 +63,10 @@ int64_t ring_splits_max(int64_t buffer_size) {
     return std::min<int64_t>(kMaxRingSplits, (buffer_size + 63) / 64);
 }
 
-void split_shape(int d, int vb, int64_t G, int64_t slices, int64_t n_packed, int64_t &n_split,
+// tokens per split: a whole number of 128-token passes; then as few splits as cover n_packed
+void split_shape(int d, int vb, int64_t G, int64_t slices, int64_t n_packed, int waves, int64_t &n_split,
                  int64_t &per_split) {
-    const int64_t s0 = decode_splits(d, vb, G, slices, n_packed);
+    const int64_t s0 = decode_splits(d, vb, G, slices, n_packed, waves);
     per_split = (n_packed + s0 - 1) / s0;
     per_split = (per_split + kSplitQuantum - 1) / kSplitQuantum * kSplitQuantum;
     n_split = (n_packed + per_split - 1) / per_split;
@@ -164,7 +175,7 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch,
         return 0;
     if (n_q_heads % n_kv_heads != 0) return 0;
     const int64_t n_split = decode_splits(cfg->head_dim, cfg->value_bits, n_q_heads / n_kv_heads,
-                                          (int64_t)batch * n_kv_heads, max_context);
+                                          (int64_t)batch * n_kv_heads, max_context, 4);
     return decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads,
                          n_split + ring_splits_max(cfg->buffer_size)).total;
 }
@@ -193,7 +204,8 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     // packed splits, plus the ring splits; an empty context still runs one (empty) split so
     // that the output is written
     int64_t n_split = n_ring > 0 ? 0 : 1, per_split = 0;
-    if (n_packed > 0) split_shape(cfg->head_dim, cfg->value_bits, G, slices, n_packed, n_split, per_split);
+    const int waves = n_packed > 0 ? decode_waves(cfg->head_dim, G, slices, n_packed) : 4;
+    if (n_packed > 0) split_shape(cfg->head_dim, cfg->value_bits, G, slices, n_packed, waves, n_split, per_split);
     const int64_t n_total = n_split + ring_splits(n_ring);
     // (sized for the most ring splits any fill of this ring can need, like the workspace query)
     const DecodeLayout L =
@@ -226,6 +238,7 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     a.n_split = (int)n_split;
     a.n_split_total = (int)n_total;
     a.ring_per_split = (int)ring_per_split(n_ring);
+    a.waves = waves;
     a.per_split = per_split;
     a.scale = softmax_scale;
     a.out = out;

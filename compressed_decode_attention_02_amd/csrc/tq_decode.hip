@@ -177,7 +177,7 @@ struct DecodeShape {
     static constexpr bool BLDS = D == 128;
 };
 
-template <int D, int VB, int G>
+template <int D, int VB, int G, int NW>
 struct alignas(16) DecodeSmem {
     using S = DecodeShape<D, VB, G>;
     // score query operands in LDS (d = 128): NSL nonzero rows per operand and lane group
@@ -185,16 +185,17 @@ struct alignas(16) DecodeSmem {
     static constexpr int NSL = G == 8 ? 16 : (G == 4 ? 8 : 4);
     static constexpr int FZ = 4 * NSL;
     union {
-        unsigned char stage[kWaves][2][S::BUF_B];  // packed splits: per-wave double buffer
-        struct {                                    // wave combine (after the loop)
-            float wo[kWaves][G][D];
+        unsigned char stage[NW][2][S::BUF_B];  // packed splits: per-wave double buffer
+        struct {                                // wave combine (after the loop)
+            float wo[NW][G][D];
         } x;
     };
     u32x4_t bfrag[S::BLDS ? 2 * S::NKS : 1][FZ + 1];  // [centroid, sign k-steps][row slot]
-    float pb[kWaves][G][kBlock + 4];
-    float corr[kWaves][G];
-    float mref[kWaves][G];  // running reference max per wave and head (packed splits)
-    float wm[kWaves][G], wl[kWaves][G];
+    float pb[NW][G][kBlock + 4];
+    float corr[NW][G];
+    float mref[NW][G];  // running reference max per wave and head (packed splits)
+    float wm[NW][G], wl[NW][G];
+    int next_blk;       // the split's next block not yet handed to a wave
 };
 
 // ring split: the query (rows split in four padded quarters, so that the four threads of a
@@ -268,8 +269,8 @@ __device__ __forceinline__ float from_lane_plus_g(float x) {
 }
 
 // ------------------------------------------------------------------ packed split (one wave)
-template <int D, int VB, int G>
-__device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int bk, int b, int kvh, int t_begin,
+template <int D, int VB, int G, int NW>
+__device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, int bk, int b, int kvh, int t_begin,
                             int t_end) {
     using S = DecodeShape<D, VB, G>;
     constexpr float kQjl = 1.2533141373155003f / D;  // sqrt(pi/2) / d
@@ -319,11 +320,11 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
     // value records go to LDS slot 4 (t % 8) + t / 8
     // (copy i of a kind: record r of the block, byte column inside the record; the clamped
     // path recomputes them, the offsets of the whole-block path stay in registers)
-    auto kw_rc = [&](int ln, int i, uint32_t &r, uint32_t &col) {
-        const int c = ln + 64 * i;  // 16-byte chunk of the block's key words
-        r = c / (S::KW / 4);
-        col = (c % (S::KW / 4)) * 16;
-    };
+    // key words: LDS chunk (copy i = tile tt * NC + j, lane L) holds the 16 bytes that lane L
+    // reads for tile tt, part j: token 16 tt + L % 16, words (L / 16) NKS + 4 j .. + 3, so the
+    // reads of a tile are one contiguous kilobyte (no bank conflicts)
+    constexpr int NC = S::NKS / 4;
+    static_assert(S::N_KW == 2 * NC, "two tiles of key chunks per block");
     auto vw_rc = [&](int ln, int i, uint32_t &r, uint32_t &col) {
         const int c = ln + 64 * i;
         const int slot = c / (S::VW / 4);
@@ -335,10 +336,10 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
         r = c / (S::NG / 2);
         col = (c % (S::NG / 2)) * 4;
     };
-    // whole-block path: key words, norms and scales of a block are contiguous bytes (copy i
-    // of a lane at 16 (lane + 64 i) or 4 (lane + 64 i), the 64 i part as an immediate); the
-    // value records are permuted into LDS slot order
-    const uint32_t o16 = 16u * lane, o4 = 4u * lane;
+    // whole-block path: norms and scales of a block are contiguous bytes (copy i of a lane at
+    // 4 (lane + 64 i), the 64 i part as an immediate); key chunks at the lane's offset plus a
+    // uniform part per copy; the value records are permuted into LDS slot order
+    const uint32_t ok0 = (uint32_t)n16 * (S::KW * 4) + (uint32_t)q * (S::NKS * 4), o4 = 4u * lane;
     uint32_t o_vw[S::N_VW];
 #pragma unroll
     for (int i = 0; i < S::N_VW; ++i) {
@@ -356,11 +357,17 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
             const uint32_t *vw_b = vw_s + (int64_t)t0 * S::VW;
             const uint16_t *vs_b = vs_s + (int64_t)t0 * S::NG;
             static_assert(S::N_KW <= 4 && S::N_VS <= 16, "immediate offsets");
-            // (the immediate offsets move the LDS destination too: one M0 per section)
-            dma16<0>(kw_b, o16, base);
-            if constexpr (S::N_KW > 1) dma16<1024>(kw_b, o16, base);
-            if constexpr (S::N_KW > 2) dma16<2048>(kw_b, o16, base);
-            if constexpr (S::N_KW > 3) dma16<3072>(kw_b, o16, base);
+            // (the immediate offset IMM moves the LDS destination too: copy i of the keys reads
+            // the block at ok0 + IMM, IMM = 16 tt KW 4 + 16 j, and lands at base + 1024 i)
+            dma16<0>(kw_b, ok0, base);
+            if constexpr (NC == 1) {
+                dma16<1024>(kw_b, ok0, base);  // tile 1: 16 records of 64 bytes further
+            } else {
+                static_assert(NC == 1 || (NC == 2 && S::KW * 4 * 16 == 2048), "key chunk layout");
+                dma16<16>(kw_b, ok0, base + 1024 - 16);
+                dma16<2048>(kw_b, ok0, base + 2048 - 2048);
+                dma16<2064>(kw_b, ok0, base + 3072 - 2064);
+            }
             dma4<0>(kn_b, o4, base + S::OFF_KN);
 #pragma unroll
             for (int i = 0; i < S::N_VW; ++i) dma16(vw_b, o_vw[i], base + S::OFF_VW + 1024 * i);
@@ -374,10 +381,9 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
             asm volatile("" : "+v"(lane_c));
 #pragma unroll
             for (int i = 0; i < S::N_KW; ++i) {
-                uint32_t r, col;
-                kw_rc(lane_c, i, r, col);
-                const uint32_t tok = (uint32_t)min(t0 + (int)r, last);
-                dma16(kw_s, tok * (S::KW * 4) + col, base + 1024 * i);
+                const int tt = i / NC, j = i % NC;
+                const uint32_t tok = (uint32_t)min(t0 + 16 * tt + (lane_c & 15), last);
+                dma16(kw_s, tok * (S::KW * 4) + (uint32_t)(lane_c >> 4) * (S::NKS * 4) + 16 * j, base + 1024 * i);
             }
             {
                 const uint32_t tok = (uint32_t)min(t0 + (lane_c >> 1), last);
@@ -400,19 +406,23 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
         }
     };
 
-    const int stride = kWaves * kBlock;
-    const int tw = t_begin + wave * kBlock;
-    const int nblk = tw < t_end ? (t_end - tw + stride - 1) / stride : 0;
-    // the first two blocks' copies go out before the query loads below: the compiler's own
-    // waits for those then also cover these older copies, and both latencies overlap
-    if (nblk > 0) issue(tw, 0);
-    if (nblk > 1) issue(tw + stride, 1);
+    // The split's blocks (32 tokens from t_begin): wave w starts with blocks w and w + NW.
+    // 4-wave groups: then every NW-th block (a fixed order, so results repeat bit for bit).
+    // 12-wave groups: each further block from an LDS counter, so the waves of the CU finish
+    // together (which wave sums which block then varies between calls).  The first two
+    // blocks' copies go out before the query loads below: the compiler's own waits for those
+    // then also cover these older copies.
+    const int nb = (t_end - t_begin + kBlock - 1) / kBlock;
+    int b0 = wave, b1 = wave + NW;
+    if (threadIdx.x == 0) sm.next_blk = 2 * NW;  // read after the barrier below
+    if (b0 < nb) issue(t_begin + kBlock * b0, 0);
+    if (b1 < nb) issue(t_begin + kBlock * b1, 1);
 
     // Both parts are pre-scaled by scale * log2(e) / sqrt(d) (the sign part also by
     // sqrt(pi/2)/d), so that the logit in log2 units is |k| (centroid part + gamma * sign part).
     // This lane's row n16: role in the centroid and in the sign operand (0: zero row, 1: hi,
     // 2: lo), its head, and its slot among the nonzero rows (compact LDS copy).
-    using SM = DecodeSmem<D, VB, G>;
+    using SM = DecodeSmem<D, VB, G, NW>;
     int rc, rs, rg, ri;
     if constexpr (G == 8) {
         rg = n16 & 7;
@@ -467,15 +477,17 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
             }
         };
         if constexpr (S::BLDS) {
-            // wave w builds k-step w (NKS == kWaves at d = 128)
-            static_assert(!S::BLDS || S::NKS == kWaves, "one k-step per wave");
-            u32x4_t fc, fs;
-            frag(wave, fc, fs);
-            if (rc) sm.bfrag[wave][q * SM::NSL + ri] = fc;
-            if (rs) sm.bfrag[S::NKS + wave][q * SM::NSL + ri] = fs;
-            if (lane == 0) {
-                sm.bfrag[wave][SM::FZ] = (u32x4_t){0u, 0u, 0u, 0u};
-                sm.bfrag[S::NKS + wave][SM::FZ] = (u32x4_t){0u, 0u, 0u, 0u};
+            // wave w < NKS builds k-step w (NKS == 4 at d = 128)
+            static_assert(!S::BLDS || (S::NKS == 4 && NW >= 4), "one k-step per wave");
+            if (wave < S::NKS) {
+                u32x4_t fc, fs;
+                frag(wave, fc, fs);
+                if (rc) sm.bfrag[wave][q * SM::NSL + ri] = fc;
+                if (rs) sm.bfrag[S::NKS + wave][q * SM::NSL + ri] = fs;
+                if (lane == 0) {
+                    sm.bfrag[wave][SM::FZ] = (u32x4_t){0u, 0u, 0u, 0u};
+                    sm.bfrag[S::NKS + wave][SM::FZ] = (u32x4_t){0u, 0u, 0u, 0u};
+                }
             }
         } else {
 #pragma unroll
@@ -513,10 +525,9 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
         uint32_t wds[2][S::NKS];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const uint32_t *kwp = reinterpret_cast<const uint32_t *>(buf) + (16 * tt + n16) * S::KW + q * S::NKS;
 #pragma unroll
             for (int i = 0; i < S::NKS / 4; ++i) {
-                const u32x4_t u = *reinterpret_cast<const u32x4_t *>(kwp + 4 * i);
+                const u32x4_t u = *reinterpret_cast<const u32x4_t *>(buf + (tt * (S::NKS / 4) + i) * 1024 + 16 * lane);
                 wds[tt][4 * i] = u[0]; wds[tt][4 * i + 1] = u[1]; wds[tt][4 * i + 2] = u[2]; wds[tt][4 * i + 3] = u[3];
             }
         }
@@ -735,13 +746,23 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G> &sm, int b
         wave_sync();  // this wave's p slots are rewritten by its next block
     };
 
-    // ---- the wave's blocks: t_begin + wave*32 + k*128 < t_end, two staging buffers, the
-    //      next block's copies in flight while the current one is computed.  Only blocks of
-    //      the split are copied: before the last one every copy is waited for.
-    for (int k = 0; k < nblk; ++k) {
-        if (k + 1 < nblk) wait_vm<S::N_DMA>(); else wait_vm<0>();
-        process(&sm.stage[wave][k & 1][0], tw + k * stride);
-        if (k + 2 < nblk) issue(tw + (k + 2) * stride, k & 1);
+    // ---- the wave's blocks b0 (being computed) and b1 (copies in flight), two staging
+    //      buffers.  Only blocks of the split are copied: before the last one every copy is
+    //      waited for.
+    for (int k = 0; b0 < nb; ++k) {
+        if (b1 < nb) wait_vm<S::N_DMA>(); else wait_vm<0>();
+        process(&sm.stage[wave][k & 1][0], t_begin + kBlock * b0);
+        b0 = b1;
+        if (b1 < nb) {
+            if constexpr (NW == 12) {
+                int nx = 0;
+                if (lane == 0) nx = atomicAdd(&sm.next_blk, 1);
+                b1 = __builtin_amdgcn_readfirstlane(nx);
+            } else {
+                b1 += NW;
+            }
+            if (b1 < nb) issue(t_begin + kBlock * b1, k & 1);
+        }
     }
     __syncthreads();  // every wave is done with its staging buffers (aliased by wo below)
 
@@ -955,18 +976,21 @@ void k_decode_prep(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ main kernel
-// register budget (waves per SIMD): 4 (<= 128 VGPRs) for d = 128 / 2-bit values with up to 4
-// query heads per kv head (LDS allows four workgroups per CU), 3 for 4-bit values (LDS allows
-// three), 2 otherwise
-template <int D, int VB, int G>
-constexpr int kDecodeWavesPerSimd = (D == 128 && G <= 4) ? (VB == 2 ? 4 : 3) : 2;
+// Workgroups of NW waves: 4 (several workgroups per CU) or 12 (one per CU, d = 128 with up
+// to 4 query heads per kv head, for long splits: its waves share the split's blocks, so a
+// CU's waves finish together).  Register budget (waves per SIMD): 12-wave groups 3; 4-wave
+// groups 4 (<= 128 VGPRs) for d = 128 / 2-bit values with up to 4 query heads per kv head
+// (LDS allows four workgroups per CU), 3 for 4-bit values (LDS allows three), 2 otherwise.
+template <int D, int VB, int G, int NW>
+constexpr int kDecodeWavesPerSimd = NW == 12 ? 3 : ((D == 128 && G <= 4) ? (VB == 2 ? 4 : 3) : 2);
 
-template <int D, int VB, int G>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd<D, VB, G>, kDecodeWavesPerSimd<D, VB, G>)))
+template <int D, int VB, int G, int NW>
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd<D, VB, G, NW>, kDecodeWavesPerSimd<D, VB, G, NW>)))
 void k_decode_main(DecodeArgs a) {
     using S = DecodeShape<D, VB, G>;
-    __shared__ DecodeSmem<D, VB, G> sm;
+    static_assert(sizeof(DecodeSmem<D, VB, G, NW>) <= 160 * 1024, "LDS of one workgroup");
+    __shared__ DecodeSmem<D, VB, G, NW> sm;
     const int tid = threadIdx.x;
     const int split = blockIdx.x;  // packed splits only (the ring split runs with the prep)
     const int bk = blockIdx.y;     // b * hkv + kv head == slice
@@ -978,18 +1002,18 @@ void k_decode_main(DecodeArgs a) {
     {
         const int t_begin = split * (int)a.per_split;
         const int t_end = (int)min(a.n_packed, (int64_t)t_begin + a.per_split);
-        packed_wave<D, VB, G>(a, sm, bk, b, kvh, t_begin, t_end);
+        packed_wave<D, VB, G, NW>(a, sm, bk, b, kvh, t_begin, t_end);
         __syncthreads();
-        // combine the four waves
-        for (int i = tid; i < G * D; i += kThreads) {
+        // combine the waves
+        for (int i = tid; i < G * D; i += 64 * NW) {
             const int g = i / D, j = i - g * D;
             float M = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.wm[w][g]);
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.wm[w][g]);
             float L = 0.f, O = 0.f;
             if (M != -INFINITY) {
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) {
+                for (int w = 0; w < NW; ++w) {
                     if (sm.wm[w][g] == -INFINITY) continue;
                     const float f = exp2f(sm.wm[w][g] - M);
                     L = fmaf(sm.wl[w][g], f, L);
@@ -1104,9 +1128,15 @@ static void launch_g(const DecodeArgs &a, hipStream_t st) {
     const unsigned pgrid =
         (unsigned)(a.batch * a.hq + (a.n_ring > 0 ? a.batch * a.hkv * (a.n_split_total - a.n_split) : 0));
     hipLaunchKernelGGL((k_decode_prep<D, G>), dim3(pgrid), dim3(kThreads), 0, st, a);
-    if (a.n_split > 0)
-        hipLaunchKernelGGL((k_decode_main<D, VB, G>), dim3((unsigned)a.n_split, (unsigned)(a.batch * a.hkv)),
-                           dim3(kThreads), 0, st, a);
+    if (a.n_split > 0) {
+        const dim3 grid((unsigned)a.n_split, (unsigned)(a.batch * a.hkv));
+        if constexpr (D == 128 && G <= 4) {
+            if (a.waves == 12) hipLaunchKernelGGL((k_decode_main<D, VB, G, 12>), grid, dim3(64 * 12), 0, st, a);
+            else hipLaunchKernelGGL((k_decode_main<D, VB, G, 4>), grid, dim3(64 * 4), 0, st, a);
+        } else {
+            hipLaunchKernelGGL((k_decode_main<D, VB, G, 4>), grid, dim3(64 * 4), 0, st, a);
+        }
+    }
     hipLaunchKernelGGL((k_decode_merge<D, G>), dim3((unsigned)(a.batch * a.hkv * G)), dim3(kThreads), 0, st, a);
 }
 

@@ -59,6 +59,7 @@ struct DecodeArgs {
     int n_split;        // splits over the packed tokens
     int n_split_total;  // n_split, plus the ring splits when there are ring tokens
     int ring_per_split; // ring tokens per ring split
+    int waves;          // waves per workgroup of the packed splits (4 or 12)
     int64_t per_split;  // packed tokens per split
     float scale;
     float *out;
