@@ -1032,23 +1032,35 @@ void k_decode_main(DecodeArgs a) {
 // ------------------------------------------------------------------ split merge
 // One workgroup per (batch * kv head, query head of the group): combines the (m, l, o)
 // partials of every split (a separate launch, so the partials of all workgroups are
-// visible without device-wide fences).
+// visible without device-wide fences).  The thread's first PF partial columns and its
+// (m, l) pair are loaded together up front, so the merge waits on memory once.
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void k_decode_merge(DecodeArgs a) {
     constexpr int NJ4 = D / 4;             // float4 columns of one head
     constexpr int NSG = kThreads / NJ4;    // split groups summed in parallel
+    constexpr int PF = 96 / NSG;           // partials per thread loaded up front
     __shared__ float f[256];
     __shared__ float red[kWaves];
     __shared__ float4 acc_s[NSG][NJ4];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int bk = blockIdx.x / G, g = blockIdx.x % G;
     const int b = bk / a.hkv, kvh = bk - b * a.hkv;
-    const int n_total = a.n_split_total;
+    const int n_total = a.n_split_total;  // <= 256
     const float *ml = a.partial_ml + (int64_t)bk * n_total * G * 2;
     const float *po = a.partial + (int64_t)bk * n_total * G * D;
+    const int j4 = tid % NJ4, sg = tid / NJ4;
 
-    float m = -INFINITY;
-    for (int sp = tid; sp < n_total; sp += kThreads) m = fmaxf(m, ml[(sp * G + g) * 2]);
+    float4 pre[PF];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+        const int sp = sg + k * NSG;
+        pre[k] = sp < n_total ? *reinterpret_cast<const float4 *>(po + (int64_t)(sp * G + g) * D + 4 * j4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float2 mlv = make_float2(-INFINITY, 0.f);
+    if (tid < n_total) mlv = *reinterpret_cast<const float2 *>(ml + (tid * G + g) * 2);
+
+    float m = mlv.x;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     if (lane == 0) red[wv] = m;
@@ -1057,13 +1069,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_merge(DecodeArgs a) {
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red[w]);
     __syncthreads();
-    float l = 0.f;
-    for (int sp = tid; sp < n_total; sp += kThreads) {
-        const float ms = ml[(sp * G + g) * 2];
-        const float fw = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-        f[sp] = fw;
-        l = fmaf(fw, ml[(sp * G + g) * 2 + 1], l);
-    }
+    const float fw = (mlv.x == -INFINITY) ? 0.f : exp2f(mlv.x - M);
+    if (tid < n_total) f[tid] = fw;
+    float l = fw * mlv.y;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
     if (lane == 0) red[wv] = l;
@@ -1072,15 +1080,23 @@ __global__ __launch_bounds__(kThreads) void k_decode_merge(DecodeArgs a) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) L += red[w];
 
-    const int j4 = tid % NJ4, sg = tid / NJ4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp = sg; sp < n_total; sp += NSG) {
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+        const int sp = sg + k * NSG;
+        const float w = sp < n_total ? f[sp] : 0.f;
+        acc.x = fmaf(w, pre[k].x, acc.x);
+        acc.y = fmaf(w, pre[k].y, acc.y);
+        acc.z = fmaf(w, pre[k].z, acc.z);
+        acc.w = fmaf(w, pre[k].w, acc.w);
+    }
+    for (int sp = sg + PF * NSG; sp < n_total; sp += NSG) {
         const float4 v = *reinterpret_cast<const float4 *>(po + (int64_t)(sp * G + g) * D + 4 * j4);
-        const float fw = f[sp];
-        acc.x = fmaf(fw, v.x, acc.x);
-        acc.y = fmaf(fw, v.y, acc.y);
-        acc.z = fmaf(fw, v.z, acc.z);
-        acc.w = fmaf(fw, v.w, acc.w);
+        const float w = f[sp];
+        acc.x = fmaf(w, v.x, acc.x);
+        acc.y = fmaf(w, v.y, acc.y);
+        acc.z = fmaf(w, v.z, acc.z);
+        acc.w = fmaf(w, v.w, acc.w);
     }
     acc_s[sg][j4] = acc;
     __syncthreads();
