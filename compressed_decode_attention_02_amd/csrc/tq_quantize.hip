@@ -119,15 +119,21 @@ __device__ __forceinline__ void split3_bf16(float x, uint16_t &hi, uint16_t &mid
 // ------------------------------------------------------------------------------ values of one group
 // Codes of one group: code = clamp(floor(v / s), -HALF, HALF - 1) + HALF, floor exact.
 // Fast form (16-bit inputs, normal fp16 s): v / s is then either an integer or at least
-// 2^-11 away from every integer (or inside (-1, 1)), so floor(p + |p| 2^-20), p = v * (1/s)
-// rounded, is exact: the nudge lifts exact integers that rounding pushed below, and is far
-// too small to cross a non-integer.  Otherwise the estimate is corrected with exact
-// products (q + 1) s and q s.
+// 2^-11 away from every integer (or inside (-1, 1)), so floor(p + |v| 2^-20 / s), p = v * r
+// rounded with r = 1/s from v_rcp_f32 (within 1 ulp), is exact: the nudge (|v / s| 2^-20,
+// eight times the rounding error of p) lifts exact integers that rounding pushed below, and
+// is far too small to cross a non-integer.  Otherwise the estimate (off by at most one) is
+// corrected with exact products (q + 1) s and q s.
+__device__ __forceinline__ int floor_to_int(float x) {
+    int q;
+    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(q) : "v"(x));
+    return q;
+}
 template <int VB, bool Exact>
 __device__ __forceinline__ void quant_group(const float (&v)[32], float sc, uint32_t (&wd)[VB]) {
     constexpr int HALF = 1 << (VB - 1);
     constexpr int PER = 32 / VB;  // codes per word
-    const float rinv = 1.0f / sc;
+    const float rinv = __builtin_amdgcn_rcpf(sc);
     const float nudge = rinv * 0x1p-20f;
     // code offset HALF in every field
     constexpr uint32_t kOff = VB == 2 ? 0xAAAAAAAAu : 0x88888888u;
@@ -137,16 +143,17 @@ __device__ __forceinline__ void quant_group(const float (&v)[32], float sc, uint
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
             const float x = v[w * PER + e];
-            float q;
+            int q;
             if constexpr (Exact) {
-                q = floorf(x * rinv);
-                if ((q + 1.f) * sc <= x) q += 1.f;
-                else if (q * sc > x) q -= 1.f;
+                float qf = floorf(x * rinv);
+                if ((qf + 1.f) * sc <= x) qf += 1.f;
+                else if (qf * sc > x) qf -= 1.f;
+                q = (int)fminf(fmaxf(qf, (float)-HALF), (float)(HALF - 1));
             } else {
-                q = floorf(fmaf(fabsf(x), nudge, x * rinv));
+                q = floor_to_int(fmaf(fabsf(x), nudge, x * rinv));
+                q = min(max(q, -HALF), HALF - 1);
             }
-            q = fminf(fmaxf(q, (float)-HALF), (float)(HALF - 1));
-            acc += (uint32_t)(int)q << (VB * e);
+            acc += (uint32_t)q << (VB * e);
         }
         wd[w] = acc;
     }
@@ -284,10 +291,8 @@ void k_quant_kv(QuantArgs a) {
                 hf[v][w] = pair;
             }
     }
-    // the positive decision boundaries b_4 < b_5 < b_6 (the codebook is symmetric), scaled by 2^8
-    const uint32_t K4 = __float_as_uint(256.f * a.boundaries[4]);
-    const uint32_t K5 = __float_as_uint(256.f * a.boundaries[5]);
-    const uint32_t K6 = __float_as_uint(256.f * a.boundaries[6]);
+    // the positive decision boundaries b_4 < b_5 < b_6 (the codebook is symmetric)
+    const float B4 = a.boundaries[4], B5 = a.boundaries[5], B6 = a.boundaries[6];
     // scaled positive centroids 2^8 c[4+k], tagged with their index 4 + k in the three low
     // mantissa bits (the stored centroids are binary16 values, so those bits are zero)
     float M0 = __uint_as_float((__float_as_uint(256.f * a.centroids[4]) & ~7u) | 4u);
@@ -442,46 +447,51 @@ void k_quant_kv(QuantArgs a) {
             }
         }
 
-        // ---- encode.  u' = 2^8 u = 2^8 y / sqrt(d |k|^2); the cell of u follows from |u'|
-        //      against the scaled positive boundaries and the side u > 0 or u <= 0 (a zero
-        //      row gives u = 0, cell 3, as the count of boundaries strictly below 0).  A tie
-        //      with a boundary may land in either neighbouring cell.
+        // ---- encode.  u' = 2^8 u = y inv256 with inv256 = 2^8 / sqrt(d |k|^2).  The cell of u
+        //      follows from |y| against the row's thresholds b_i sqrt(d |k|^2) (i = 4, 5, 6, the
+        //      positive boundaries; fp32 products, within a few ulp of the exact ones) and the
+        //      side y > 0 or y <= 0 (a zero row gives u = 0, cell 3, as the count of boundaries
+        //      strictly below 0).  A tie with a boundary may land in either neighbouring cell.
         const float knorm = sqrtf(ss);
-        const float inv256 = ss > 0.f ? 256.f / sqrtf((float)D * ss) : 0.f;
+        const float rsd = sqrtf((float)D * ss);
+        const float inv256 = ss > 0.f ? 256.f / rsd : 0.f;
+        const float T4 = B4 * rsd, T5 = B5 * rsd, T6 = B6 * rsd;
         uint32_t P[S::NP];  // nibble half-words: slot f at bit 4 (f & 7) of P[f >> 3]
-#pragma unroll
-        for (int p = 0; p < S::NP; ++p) P[p] = 0;
         float ggp[4] = {0.f, 0.f, 0.f, 0.f};
         // negated scaled residual -r' as fp16 hi + lo; projection k-step q = slots 8q .. 8q+7
         u32x4_t rhi[S::NQ], rlo[S::NQ];
         typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
         typedef float f2_t __attribute__((ext_vector_type(2)));
+        // indices of slots (x, z) from one byte permute: bytes 0, 1 = the tags of x and z,
+        // bytes 2, 3 = their sign bits replicated (selectors 11 and 9); index = tag, or
+        // tag ^ 7 = 3 - k on the non-positive side
+        auto pair_idx = [](uint32_t x, uint32_t z) {
+            const uint32_t w = __builtin_amdgcn_perm(x, z, 0x090B0004u);
+            return (w ^ (w >> 16)) & 0x0707u;
+        };
 #pragma unroll
         for (int f4 = 0; f4 < S::NV; f4 += 4) {
+            uint32_t sb[4];
             float nr[4];
-            uint32_t idx[4];
 #pragma unroll
             for (int o = 0; o < 4; ++o) {
-                const int f = f4 + o;
-                const float yv = y[f / S::RPT][f % S::RPT];
-                const float u = yv * inv256;
-                const bool nonpos = !(u > 0.f);
-                const uint32_t key = __float_as_uint(u) & 0x7fffffffu;  // |u'| as an ordered integer
-                const bool c4 = key > K4, c5 = key > K5, c6 = key > K6;
-                // signed tagged centroid: sign = (u <= 0), low bits = 4 + #{boundaries passed}
-                const float mt = c6 ? M3 : (c5 ? M2 : (c4 ? M1 : M0));
-                const uint32_t sb = __float_as_uint(nonpos ? -mt : mt);
-                // index: 4 + k above zero, 3 - k = (4 + k) ^ 7 at or below
-                idx[o] = (sb ^ (uint32_t)((int32_t)sb >> 31)) & 7u;
+                const float yv = y[(f4 + o) / S::RPT][(f4 + o) % S::RPT];
+                const float ay = fabsf(yv);
+                // signed tagged centroid: sign = (y <= 0), low bits = 4 + #{boundaries passed}
+                float mt = ay > T4 ? M1 : M0;
+                mt = ay > T5 ? M2 : mt;
+                mt = ay > T6 ? M3 : mt;
+                sb[o] = __float_as_uint(yv > 0.f ? mt : -mt);
                 // -r' = c[idx] - u'
-                nr[o] = fmaf(-yv, inv256, __uint_as_float(sb & ~7u));
+                nr[o] = fmaf(-yv, inv256, __uint_as_float(sb[o] & ~7u));
                 ggp[o] = fmaf(nr[o], nr[o], ggp[o]);
             }
-            // materialise the four indices here: the compare masks die now instead of being
-            // kept (in scalar registers) until the nibble word is assembled
-            asm volatile("" : "+v"(idx[0]), "+v"(idx[1]), "+v"(idx[2]), "+v"(idx[3]));
-#pragma unroll
-            for (int o = 0; o < 4; ++o) P[(f4 + o) >> 3] |= idx[o] << (4 * ((f4 + o) & 7));
+            // slots (0, 2) and (1, 3) of the four at nibble offsets 0 and 4 (plus 16 for the
+            // upper four of a word); materialised here so that the centroids die now
+            uint32_t q4 = pair_idx(sb[0], sb[2]) | (pair_idx(sb[1], sb[3]) << 4);
+            asm volatile("" : "+v"(q4));
+            if (f4 & 4) P[f4 >> 3] |= q4 << 16;
+            else P[f4 >> 3] = q4;
 #pragma unroll
             for (int o = 0; o < 4; o += 2) {
                 const int f2 = f4 + o;
@@ -504,6 +514,7 @@ void k_quant_kv(QuantArgs a) {
 
         // ---- QJL on the matrix cores: D[j][token] = -sum_c S[j][c] r'[c]; lane (n, g)
         //      receives the projections j = slot_coord(f, g) of its own coordinates
+        uint32_t se = 0, so = 0;  // sign bytes of the first half of the current word
 #pragma unroll
         for (int jt2 = 0; jt2 < S::NJ; ++jt2) {
             __builtin_amdgcn_sched_barrier(0);
@@ -517,13 +528,23 @@ void k_quant_kv(QuantArgs a) {
                 acc = mfma_f16<R>(A, rhi[q], acc);
                 acc = mfma_f16<R>(A, rlo[q], acc);
             }
+            // the accumulator holds -(S r')_j: its sign bit is set exactly when the projection
+            // is positive (or a zero came out as -0); it goes to bit 4 (f & 7) + 3 of
+            // P[f >> 3].  Byte permutes replicate the sign bits of slots (f, f + 2) into bytes
+            // (0, 1) of a word for f & 7 < 4, else bytes (2, 3), and of slots (f + 1, f + 3)
+            // likewise into a second word shifted by 4 at the end.
 #pragma unroll
-            for (int r = 0; r < S::RPT; ++r) {
-                const int f = jt2 * S::RPT + r;
-                const int pos = 4 * (f & 7) + 3;
-                // the accumulator holds -(S r')_j: its sign bit is set exactly when the
-                // projection is positive (or a zero came out as -0)
-                P[f >> 3] |= (__float_as_uint(acc[r]) >> (31 - pos)) & (1u << pos);
+            for (int r4 = 0; r4 < S::RPT; r4 += 4) {
+                const int f = jt2 * S::RPT + r4;
+                const uint32_t sel = (f & 4) ? 0x090B0C0Cu : 0x0C0C090Bu;
+                const uint32_t e = __builtin_amdgcn_perm(__float_as_uint(acc[r4]), __float_as_uint(acc[r4 + 2]), sel);
+                const uint32_t o = __builtin_amdgcn_perm(__float_as_uint(acc[r4 + 1]), __float_as_uint(acc[r4 + 3]), sel);
+                if (f & 4) {
+                    P[f >> 3] |= ((se | e) & 0x08080808u) | (((so | o) & 0x08080808u) << 4);
+                } else {
+                    se = e;
+                    so = o;
+                }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
