@@ -40,18 +40,22 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <int D>
+// tile shape: RR tokens per wave, 32 (v_mfma_f32_32x32x16, d = 128 only) or 16
+// (v_mfma_f32_16x16x32)
+template <int D, int RR>
 struct KeyShape {
-    static constexpr int R = D == 128 ? 32 : 16;  // tokens per wave (MFMA M = N)
+    static constexpr int R = RR;                  // tokens per wave (MFMA M = N)
     static constexpr int KG = 64 / R;             // lanes per token
     static constexpr int K = 8 * KG;              // MFMA k per instruction
     static constexpr int NS = D / K;              // rotation k-steps
     static constexpr int NJ = D / R;              // rotation / projection output tiles
     static constexpr int RPT = R * R / 64;        // accumulator registers per tile and lane
-    static constexpr int NV = D / KG;             // coordinates per lane (64)
+    static constexpr int NV = D / KG;             // coordinates per lane (64, or 32 at d = 128, R = 16)
     static constexpr int NQ = NV / 8;             // projection k-steps
     static constexpr int KW = D / 8;              // key words per record
     static constexpr int NP = NV / 8;             // u32 registers of nibble half-word pairs
+    static constexpr int NVG = NV / 32;           // value groups per lane
+    static_assert(R == 16 || (R == 32 && D == 128), "tile shapes");
 };
 
 template <int R>
@@ -59,21 +63,21 @@ using acc_t = std::conditional_t<R == 32, f32x16_t, f32x4_t>;
 
 // coordinate held in accumulator slot f (tile f / RPT, register f % RPT) by lane group g:
 // the MFMA result layout (row 4 g + (r & 3) + 4 KG (r >> 2) of the tile)
-template <int D>
+template <int D, int RR>
 __device__ __host__ constexpr int slot_coord(int f, int g) {
-    using S = KeyShape<D>;
+    using S = KeyShape<D, RR>;
     return S::R * (f / S::RPT) + 4 * g + ((f % S::RPT) & 3) + 4 * S::KG * ((f % S::RPT) >> 2);
 }
 
 // rotation A operand of (output tile jt, k-step s): fragment variant and global sign, from
 // popcount((R jt + i) & (K s + k)) split over the index bits
-template <int D>
+template <int RR>
 __device__ __host__ constexpr int h_variant(int jt, int s) {
-    return KeyShape<D>::R == 32 ? (s & 1) : (jt & 1);
+    return RR == 32 ? (s & 1) : (jt & 1);
 }
-template <int D>
+template <int RR>
 __device__ __host__ constexpr int h_negated(int jt, int s) {
-    return __builtin_popcount(KeyShape<D>::R == 32 ? (jt & (s >> 1)) : ((jt >> 1) & s)) & 1;
+    return __builtin_popcount(RR == 32 ? (jt & (s >> 1)) : ((jt >> 1) & s)) & 1;
 }
 
 template <int R, typename Tag>
@@ -200,11 +204,11 @@ __device__ __forceinline__ void split_row(int64_t r, int64_t n_tok, double inv, 
     t = rem;
 }
 
-template <typename Tag, int D, int VB>
+template <typename Tag, int D, int VB, int RR>
 __global__ __launch_bounds__(64 * kKeyGroupWaves<D>)
 __attribute__((amdgpu_waves_per_eu(kKeyWavesPerSimd<D>, kKeyWavesPerSimd<D>)))
 void k_quant_kv(QuantArgs a) {
-    using S = KeyShape<D>;
+    using S = KeyShape<D, RR>;
     constexpr int R = S::R;
     constexpr bool kF32 = std::is_same_v<Tag, f32_tag>;
     constexpr bool kF16 = std::is_same_v<Tag, f16_tag>;
@@ -316,32 +320,33 @@ void k_quant_kv(QuantArgs a) {
             rec = sl * a.cap + a.dst_offset + t;
         }
 
-        // ---- the tile's values: this lane's 64 coordinates g*64 .. g*64+63 of its token (two
-        //      groups of 32), loaded with the keys and quantised first (their registers are free again before the
-        //      key encode needs its peak)
-        constexpr int VCH = kF32 ? 16 : 8;  // 16-byte chunks of 64 values
+        // ---- the tile's values: this lane's NV coordinates g NV .. g NV + NV - 1 of its token
+        //      (NVG groups of 32), loaded with the keys and quantised first (their registers are
+        //      free again before the key encode needs its peak)
+        constexpr int NVG = S::NVG;
+        constexpr int VCH = NVG * (kF32 ? 8 : 4);  // 16-byte chunks of the lane's values
         uint4 vr[VCH];
         {
             int64_t sl, t;
             split_row(row < a.n_rows ? row : a.n_rows - 1, a.n_tokens, inv_tok, sl, t);
             const uint4 *vp = reinterpret_cast<const uint4 *>(static_cast<const unsigned char *>(a.v) +
-                                                              ((sl * a.in_slice_stride + t * D + 64 * g) * (kF32 ? 4 : 2)));
+                                                              ((sl * a.in_slice_stride + t * D + S::NV * g) * (kF32 ? 4 : 2)));
 #pragma unroll
             for (int i = 0; i < VCH; ++i) vr[i] = vp[i];
         }
 
-        // ---- values: groups 2g and 2g + 1 of the token, all in this lane
+        // ---- values: groups NVG g .. NVG g + NVG - 1 of the token, all in this lane
         {
             constexpr int NG = D / 32;
             constexpr int VW = VB * D / 32;
-            uint32_t wd[2][VB];
-            uint16_t scb[2];
+            uint32_t wd[NVG][VB];
+            uint16_t scb[NVG];
 #pragma unroll
-            for (int gi = 0; gi < 2; ++gi) {
+            for (int gi = 0; gi < NVG; ++gi) {
                 float vv[32];
 #pragma unroll
-                for (int c = 0; c < VCH / 2; ++c) {
-                    const uint4 x = vr[gi * (VCH / 2) + c];
+                for (int c = 0; c < VCH / NVG; ++c) {
+                    const uint4 x = vr[gi * (VCH / NVG) + c];
                     if constexpr (kF32) {
                         vv[4 * c + 0] = __uint_as_float(x.x); vv[4 * c + 1] = __uint_as_float(x.y);
                         vv[4 * c + 2] = __uint_as_float(x.z); vv[4 * c + 3] = __uint_as_float(x.w);
@@ -373,15 +378,20 @@ void k_quant_kv(QuantArgs a) {
                 }
             }
             if (rec >= 0) {
-                uint32_t *dstv = a.vw + rec * VW + 2 * g * VB;
-                if constexpr (VB == 2) {
+                uint32_t *dstv = a.vw + rec * VW + NVG * g * VB;
+                if constexpr (NVG == 1) {
+                    if constexpr (VB == 2) *reinterpret_cast<uint2 *>(dstv) = make_uint2(wd[0][0], wd[0][1]);
+                    else *reinterpret_cast<uint4 *>(dstv) = make_uint4(wd[0][0], wd[0][1], wd[0][2], wd[0][3]);
+                    a.vs[rec * NG + g] = scb[0];
+                } else if constexpr (VB == 2) {
                     *reinterpret_cast<uint4 *>(dstv) = make_uint4(wd[0][0], wd[0][1], wd[1][0], wd[1][1]);
                 } else {
                     uint4 *d4 = reinterpret_cast<uint4 *>(dstv);
                     d4[0] = make_uint4(wd[0][0], wd[0][1], wd[0][2], wd[0][3]);
                     d4[1] = make_uint4(wd[1][0], wd[1][1], wd[1][2], wd[1][3]);
                 }
-                *reinterpret_cast<uint32_t *>(a.vs + rec * NG + 2 * g) = scb[0] | ((uint32_t)scb[1] << 16);
+                if constexpr (NVG == 2)
+                    *reinterpret_cast<uint32_t *>(a.vs + rec * NG + 2 * g) = scb[0] | ((uint32_t)scb[1] << 16);
             }
         }
 
@@ -428,8 +438,8 @@ void k_quant_kv(QuantArgs a) {
                 }
 #pragma unroll
                 for (int jt = 0; jt < S::NJ; ++jt) {
-                    const u32x4_t A0 = hf[h_variant<D>(jt, s)];
-                    const u32x4_t A = h_negated<D>(jt, s) ? (A0 ^ 0x80008000u) : A0;
+                    const u32x4_t A0 = hf[h_variant<R>(jt, s)];
+                    const u32x4_t A = h_negated<R>(jt, s) ? (A0 ^ 0x80008000u) : A0;
                     y[jt] = mfma_in<R, bf16_tag>(A, bh, y[jt]);
                     y[jt] = mfma_in<R, bf16_tag>(A, bm, y[jt]);
                     y[jt] = mfma_in<R, bf16_tag>(A, bl, y[jt]);
@@ -440,8 +450,8 @@ void k_quant_kv(QuantArgs a) {
                 for (int w = 0; w < 4; ++w) b[w] = raw[s][w] ^ m4[w];
 #pragma unroll
                 for (int jt = 0; jt < S::NJ; ++jt) {
-                    const u32x4_t A0 = hf[h_variant<D>(jt, s)];
-                    const u32x4_t A = h_negated<D>(jt, s) ? (A0 ^ 0x80008000u) : A0;
+                    const u32x4_t A0 = hf[h_variant<R>(jt, s)];
+                    const u32x4_t A = h_negated<R>(jt, s) ? (A0 ^ 0x80008000u) : A0;
                     y[jt] = mfma_in<R, Tag>(A, b, y[jt]);
                 }
             }
@@ -522,8 +532,8 @@ void k_quant_kv(QuantArgs a) {
             const uint16_t *srow = sS + (R * jt2 + n) * kSRow<D>;
 #pragma unroll
             for (int q = 0; q < S::NQ; ++q) {
-                const uint2 s0 = *reinterpret_cast<const uint2 *>(srow + slot_coord<D>(8 * q, g));
-                const uint2 s1 = *reinterpret_cast<const uint2 *>(srow + slot_coord<D>(8 * q + 4, g));
+                const uint2 s0 = *reinterpret_cast<const uint2 *>(srow + slot_coord<D, R>(8 * q, g));
+                const uint2 s1 = *reinterpret_cast<const uint2 *>(srow + slot_coord<D, R>(8 * q + 4, g));
                 const u32x4_t A = {s0.x, s0.y, s1.x, s1.y};
                 acc = mfma_f16<R>(A, rhi[q], acc);
                 acc = mfma_f16<R>(A, rlo[q], acc);
@@ -581,8 +591,8 @@ void k_quant_kv(QuantArgs a) {
 #pragma unroll
                 for (int p = 0; p < S::NP / 2; ++p) {
                     const int pp = p + odd * (S::NP / 2);
-                    dst[slot_coord<D>(8 * pp, g) >> 3] = outw[2 * p];
-                    dst[slot_coord<D>(8 * pp + 4, g) >> 3] = outw[2 * p + 1];
+                    dst[slot_coord<D, R>(8 * pp, g) >> 3] = outw[2 * p];
+                    dst[slot_coord<D, R>(8 * pp + 4, g) >> 3] = outw[2 * p + 1];
                 }
             }
             if (g == 0)
@@ -594,15 +604,24 @@ void k_quant_kv(QuantArgs a) {
 
 // ------------------------------------------------------------------------------ values
 // ------------------------------------------------------------------------------ launch
-template <typename Tag, int D, int VB>
-static void launch_kv_t(const QuantArgs &a, hipStream_t st) {
-    const int64_t tiles = (a.n_rows + KeyShape<D>::R - 1) / KeyShape<D>::R;
-    const int64_t cus = (int64_t)device_cus();
+template <typename Tag, int D, int VB, int RR>
+static void launch_kv_r(const QuantArgs &a, int64_t cus, hipStream_t st) {
+    const int64_t tiles = (a.n_rows + RR - 1) / RR;
     const int nw = quant_waves_per_group(D, tiles, cus);
     const int64_t per_cu = kKeyGroupWaves<D> / nw;  // workgroups of nw waves resident per CU
     int64_t grid = (tiles + nw - 1) / nw;
     if (grid > cus * per_cu) grid = cus * per_cu;
-    hipLaunchKernelGGL((k_quant_kv<Tag, D, VB>), dim3((unsigned)grid), dim3(64 * nw), 0, st, a);
+    hipLaunchKernelGGL((k_quant_kv<Tag, D, VB, RR>), dim3((unsigned)grid), dim3(64 * nw), 0, st, a);
+}
+
+// d = 128: 32-token tiles, or 16-token tiles (half the arithmetic per wave, twice the waves)
+// while the 32-token ones would not give every CU one: a short input such as a ring flush is
+// bound by the latency of one tile
+template <typename Tag, int D, int VB>
+static void launch_kv_t(const QuantArgs &a, hipStream_t st) {
+    const int64_t cus = (int64_t)device_cus();
+    if (D == 128 && (a.n_rows + 31) / 32 >= cus) launch_kv_r<Tag, D, VB, D == 128 ? 32 : 16>(a, cus, st);
+    else launch_kv_r<Tag, D, VB, 16>(a, cus, st);
 }
 
 template <typename Tag>

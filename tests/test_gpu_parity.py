@@ -55,6 +55,14 @@ def test_quantize_llama_law_ragged_with_offset(torch):
     _quantize_case(env, w, 1000, cap_extra=5, offset=37, label="llama-law bf16 v2 ragged")
 
 
+def test_quantize_d128_32_token_tiles(torch):
+    # 12008 rows: enough 32-token tiles for one per CU (smaller inputs at d = 128 run
+    # 16-token tiles), with a ragged last tile and slices that end inside tiles
+    w = W.custom(2, hkv=8)
+    env = Env(w.d, w.value_bits)
+    _quantize_case(env, w, 1501, label="llama-law bf16 v2, 32-token tiles")
+
+
 def test_quantize_value_bits4(torch):
     w = W.custom(3, batch=2, hkv=3)
     env = Env(w.d, w.value_bits)
