@@ -5,26 +5,27 @@
 // codebook, (3) one QJL sign bit per coordinate for the residual, (4) symmetric 2/4-bit
 // value quantisation in groups of 32 with a per-group scale, (5) bit packing.
 //
-// Keys: k_quant_keys, one wave per tile of R tokens (R = 32 at d = 128 on
-// v_mfma_f32_32x32x16, R = 16 at d = 256 on v_mfma_f32_16x16x32); the KG = 64 / R lanes of
-// a token each hold 64 of its coordinates.
+// k_quant_kv: one wave per tile of R tokens (R = 32 at d = 128 on v_mfma_f32_32x32x16,
+// R = 16 at d = 256, and at d = 128 for short inputs, on v_mfma_f32_16x16x32); the
+// KG = 64 / R lanes of a token each hold D / KG of its coordinates and values.
+//   * values first: the lane's values are whole groups of 32, so group max, fp16 scale and
+//     exact floor (see quant_group) are in-lane;
 //   * rotation: the Walsh-Hadamard product H (sigma o x) runs on the matrix cores with the
 //     raw 16-bit inputs as the B operand (exact: H has entries +-1, sigma is a sign flip
 //     applied by XOR on the raw words) and fp32 accumulation.  H factorises over the index
 //     bits, so the A operand of every (output tile, k-step) pair is one of two per-lane
 //     +-1 fragments, possibly negated;
-//   * the accumulator layout leaves lane group g of a token with the 64 coordinates
-//     slot_coord(f, g), f = 0..63; encode is elementwise on them: the codebook is
-//     antisymmetric with b_3 = 0, so |u| is compared with the three positive boundaries as
-//     integers (ties resolved as idx = #{i : u > b_i} on both sides);
+//   * the accumulator layout leaves lane group g of a token with the coordinates
+//     slot_coord(f, g); encode is elementwise on them: the codebook is antisymmetric with
+//     b_3 = 0, so |y| is compared with the row's thresholds for the three positive
+//     boundaries, and the side decides the sign (the oracle resolves ties as
+//     idx = #{i : u > b_i}; here a tie within a few ulp may take either neighbouring cell);
 //   * QJL: the projection is computed transposed, D = S R^T with the residual (scaled by
 //     2^8, split into fp16 hi + lo) as the B operand, so the accumulator hands every lane
-//     the projections of exactly the coordinates it encoded; sign bits go straight into
-//     the nibbles;
+//     the projections of exactly the coordinates it encoded; byte permutes gather their
+//     sign bits into the nibbles;
 //   * nibble half-words of a key word live in the two lanes g, g ^ 1; one permlane swap
 //     and two byte permutes assemble the words.
-// Values: k_quant_values, one lane per (token, group of 32): in-lane group max, fp16 scale,
-// exact floor (see quant_group), codes accumulated in place.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -157,7 +158,8 @@ __device__ __forceinline__ void quant_group(const float (&v)[32], float sc, uint
                 q = floor_to_int(fmaf(fabsf(x), nudge, x * rinv));
                 q = min(max(q, -HALF), HALF - 1);
             }
-            acc += (uint32_t)q << (VB * e);
+            // acc += q << (VB e): one shift-add per code
+            asm("v_lshl_add_u32 %0, %1, %2, %0" : "+v"(acc) : "v"(q), "i"(VB * e));
         }
         wd[w] = acc;
     }
