@@ -12,8 +12,7 @@ namespace {
 
 constexpr int64_t kSplitQuantum = 128;     // split sizes are multiples of four 32-token blocks
 constexpr int64_t kMinSplitTokens = 512;   // at least four blocks per wave
-constexpr int64_t kMaxRingSplits = 8;      // ring splits per slice (64 tokens or more each)
-constexpr int64_t kMaxSplits = 255 - kMaxRingSplits;  // the merge keeps one weight per split in LDS
+constexpr int64_t kMaxSplits = 256;        // the merge keeps one weight per split in LDS
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
@@ -28,11 +27,11 @@ bool tables_ok(const tq_tables *t) {
 }
 
 // waves per decode workgroup: 12 (one workgroup per CU; d = 128 with up to 4 query heads per
-// kv head) when every wave then has at least 6 blocks of 32 tokens, else 4
+// kv head) when every wave then has at least 2 blocks of 32 tokens, else 4
 int decode_waves(int d, int64_t G, int64_t slices, int64_t n_packed) {
     if (d != 128 || G > 4) return 4;
     const int64_t blocks_per_wave = slices * n_packed / ((int64_t)tq::device_cus() * 12 * 32);
-    return blocks_per_wave >= 6 ? 12 : 4;
+    return blocks_per_wave >= 2 ? 12 : 4;
 }
 
 // decode workgroups resident per CU (LDS and registers; see the decode kernel's budget): the
@@ -50,19 +49,6 @@ int64_t decode_splits(int d, int vb, int64_t G, int64_t slices, int64_t n_packed
     return std::min({by_tokens, want, kMaxSplits});
 }
 
-// ring splits of n_ring tokens (each a multiple of 64 tokens, at most kMaxRingSplits)
-int64_t ring_per_split(int64_t n_ring) {
-    const int64_t per = (n_ring + kMaxRingSplits - 1) / kMaxRingSplits;
-    return std::max<int64_t>(64, (per + 63) / 64 * 64);
-}
-int64_t ring_splits(int64_t n_ring) {
-    return n_ring > 0 ? (n_ring + ring_per_split(n_ring) - 1) / ring_per_split(n_ring) : 0;
-}
-// an upper bound of ring_splits(n) over n <= buffer_size
-int64_t ring_splits_max(int64_t buffer_size) {
-    return std::min<int64_t>(kMaxRingSplits, (buffer_size + 63) / 64);
-}
-
 // tokens per split: a whole number of 128-token passes; then as few splits as cover n_packed
 void split_shape(int d, int vb, int64_t G, int64_t slices, int64_t n_packed, int waves, int64_t &n_split,
                  int64_t &per_split) {
@@ -74,16 +60,19 @@ void split_shape(int d, int vb, int64_t G, int64_t slices, int64_t n_packed, int
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// decode workspace: at d = 256 the prepared queries (q', w) [slices][2][G][d]; the packed
+// splits' partials o [slices][n_split][G][d] and (m, l) pairs [slices][n_split][G][2]
+// (slices * G = batch * hq)
 struct DecodeLayout {
     size_t prep, partial, partial_ml, total;
 };
 
-DecodeLayout decode_layout(int d, int64_t batch, int64_t hq, int64_t hkv, int64_t n_split) {
+DecodeLayout decode_layout(int d, int64_t batch, int64_t hq, int64_t n_split) {
     DecodeLayout L;
     L.prep = 0;
-    L.partial = align256(sizeof(float) * (size_t)(batch * hq) * (2 * d));
+    L.partial = d == 256 ? align256(sizeof(float) * (size_t)(batch * hq) * 2 * d) : 0;
     L.partial_ml = L.partial + align256(sizeof(float) * (size_t)(batch * hq) * n_split * d);
-    L.total = L.partial_ml + align256(sizeof(float) * (size_t)(batch * hq) * n_split * 2);
+    L.total = std::max<size_t>(256, L.partial_ml + align256(sizeof(float) * (size_t)(batch * hq) * n_split * 2));
     return L;
 }
 
@@ -176,8 +165,7 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch,
     if (n_q_heads % n_kv_heads != 0) return 0;
     const int64_t n_split = decode_splits(cfg->head_dim, cfg->value_bits, n_q_heads / n_kv_heads,
                                           (int64_t)batch * n_kv_heads, max_context, 4);
-    return decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads,
-                         n_split + ring_splits_max(cfg->buffer_size)).total;
+    return decode_layout(cfg->head_dim, batch, n_q_heads, n_split).total;
 }
 
 extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *tables, const void *q,
@@ -201,15 +189,12 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     if (n_ring > 0 && (!ring || !ring->k || !ring->v || !aligned16(ring->k) || !aligned16(ring->v)))
         return TQ_ERR_INVALID_ARG;
     const int64_t slices = (int64_t)batch * n_kv_heads;
-    // packed splits, plus the ring splits; an empty context still runs one (empty) split so
-    // that the output is written
-    int64_t n_split = n_ring > 0 ? 0 : 1, per_split = 0;
+    // packed splits (none for an empty packed store: the merge launch then attends to the ring
+    // alone, or writes zeros for an empty context)
+    int64_t n_split = 0, per_split = 0;
     const int waves = n_packed > 0 ? decode_waves(cfg->head_dim, G, slices, n_packed) : 4;
     if (n_packed > 0) split_shape(cfg->head_dim, cfg->value_bits, G, slices, n_packed, waves, n_split, per_split);
-    const int64_t n_total = n_split + ring_splits(n_ring);
-    // (sized for the most ring splits any fill of this ring can need, like the workspace query)
-    const DecodeLayout L =
-        decode_layout(cfg->head_dim, batch, n_q_heads, n_kv_heads, n_split + ring_splits_max(cfg->buffer_size));
+    const DecodeLayout L = decode_layout(cfg->head_dim, batch, n_q_heads, n_split);
     if (workspace_bytes < L.total) return TQ_ERR_WORKSPACE;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     tq::DecodeArgs a{};
@@ -236,14 +221,12 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     a.hq = n_q_heads;
     a.hkv = n_kv_heads;
     a.n_split = (int)n_split;
-    a.n_split_total = (int)n_total;
-    a.ring_per_split = (int)ring_per_split(n_ring);
     a.waves = waves;
     a.per_split = per_split;
     a.scale = softmax_scale;
     a.out = out;
+    a.prep = reinterpret_cast<float *>(ws + L.prep);
     a.partial = reinterpret_cast<float *>(ws + L.partial);
     a.partial_ml = reinterpret_cast<float *>(ws + L.partial_ml);
-    a.prep = reinterpret_cast<float *>(ws + L.prep);
     return hip_status(tq::launch_decode(cfg->head_dim, cfg->value_bits, G, a, (hipStream_t)stream));
 }

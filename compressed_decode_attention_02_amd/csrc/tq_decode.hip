@@ -4,25 +4,21 @@
 // (section 5.1 item 1: a decode-time token goes into the ring buffer).
 //
 // Score of a packed token t for query head g is the unbiased inner-product estimate of
-// section 二 evaluated in the rotated domain (q' = Pi q, w = S q', computed once per query
-// by k_decode_prep):
+// section 二 evaluated in the rotated domain (q' = Pi q, w = S q'):
 //   s_tg = |k_t| ( sum_j q'_gj c[idx_tj] + g_t sqrt(pi/2)/d sum_j w_gj (2 z_tj - 1) ).
 //
-// k_decode_main, grid (splits, batch * kv heads), 4 waves per workgroup.  Splits 0..P-1
-// cover the packed tokens in contiguous ranges; split P (present when the ring holds
-// tokens) covers the ring.  Each wave of a packed split streams blocks of 32 tokens:
-//   * scores on MFMA (v_mfma_f32_16x16x32_f16, 16 tokens x 16 columns): A holds, per
-//     token, the fp16 centroid values of 8 coordinates (a 256-entry LDS table maps one
-//     byte = two nibbles to a packed fp16 pair) and the +-1 sign of each QJL bit; B holds
-//     q'_g in columns g and -w_g in columns 8+g as fp16 hi + lo pairs (kept in registers);
-//   * per-wave online softmax on the accumulator layout;
-//   * values on MFMA: A = raw value codes as fp16 (lane row m owns the codes of
-//     coordinates m*NT .. m*NT+NT-1, read from LDS-staged records), B = p_t * scale_t,grp
-//     (hi + lo) in columns (head, group); the constant code offset is removed with the
-//     column sums of B at the end.
-// The four waves' (m, l, o) are combined in LDS, every split writes (m, l, o) partials,
-// and the last split to finish a (batch, kv head) -- atomic ticket -- merges them and
-// re-arms the ticket to zero.
+// Launches per call:
+//   * d = 256 only: k_decode_prep, q' and w of every query head into the workspace (bands of
+//     S rows per workgroup);
+//   * k_decode_main, grid (packed splits, batch * kv heads): each workgroup prepares its
+//     slice's queries in LDS (d = 128) or copies them from the workspace (d = 256), then its
+//     waves stream blocks of 32 packed tokens through LDS (hand-issued global -> LDS copies):
+//     scores on MFMA (query rows x token columns; centroid values from byte tables by
+//     v_perm_b32, QJL signs as +-1), a lazily rescaled online softmax, values on MFMA with
+//     A = 1 + code / 2^vb and B = p * scale; the waves' (m, l, o) are combined in LDS and
+//     written as the split's partials;
+//   * k_decode_merge, one workgroup per query head: attention over the ring's exact fp16
+//     tokens against the unrotated query, combined with the packed splits' partials.
 #include <hip/hip_runtime.h>
 
 #include "tq.h"
@@ -34,8 +30,6 @@ namespace tq {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBlock = 32;       // tokens per wave iteration
-constexpr int kRingChunk = 64;   // ring tokens per pass of a ring split (four threads per token)
-constexpr int kMaxRingSplits = 8;  // ring splits per slice
 // logits and running maxima are kept in log2 units (softmax weights by exp2)
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -43,8 +37,6 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-// raw buffer descriptor word 3 for gfx9-family raw (untyped) buffer loads
-constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -81,66 +73,91 @@ __device__ __forceinline__ float load_q(const DecodeArgs &a, int64_t off) {
 }
 
 // ------------------------------------------------------------------ query preparation
-// One 256-thread workgroup per (batch, query head): q' = H (sigma o q) (unnormalised; the
-// 1/sqrt(d) of the rotation is folded into the decode's operand scale) and w = S q', with
-// kThreads / d threads per row of S.  prep[b * hq + h] = (q' [d], w [d]).  The S and q loads
-// are issued first so that their latencies overlap.
-template <int D>
-__device__ void prep_head(const DecodeArgs &a, int64_t h) {
-    constexpr int PER = kThreads / D;  // threads per S row
-    constexpr int SW = D / PER / 8;    // 16-byte pieces of S per thread
-    __shared__ float y[D];
-    __shared__ float part_acc[PER][D];
-    const int t = threadIdx.x, lane = t & 63;
-    const int j = t % D, part = t / D;
-    uint4 spk[SW];
-    const uint16_t *srow = a.S + (int64_t)j * D + part * (D / PER);
+// Every workgroup of the packed splits prepares the G query heads of its (batch, kv head)
+// in LDS: q'_g = H (sigma o q_g) (unnormalised; the rotation's 1/sqrt(d) is folded into the
+// score operands' scale) and w_g = S q'_g as PARTS partial sums over column ranges of S,
+// added by the reader.  qw layout (fp32): q' [G][D], then the partial sums [PARTS][G][D].
+// Thread (row, part) holds D / PARTS entries of one row of S, loaded first (S is a few
+// tens of kilobytes, shared by every workgroup, so after the first ones these are L2 hits).
+template <int D, int NW>
+struct PrepShape {
+    static constexpr int NT = 64 * NW;
+    static constexpr int PARTS = NT / D >= 4 ? 4 : (NT / D >= 2 ? 2 : 1);
+    static constexpr int SEG = D / PARTS;  // columns of S per thread
+    template <int G>
+    static constexpr int floats() { return (1 + PARTS) * G * D; }
+};
+
+template <int D, int G, int NW>
+__device__ void prep_query(const DecodeArgs &a, float *qw, int b, int kvh) {
+    using P = PrepShape<D, NW>;
+    constexpr int E = D / 64;  // coordinates per lane in the transform, j = lane + 64 e
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = tid % D, part = tid / D;
+    const bool mine = part < P::PARTS;
+    uint4 spk[P::SEG / 8];
+    if (mine) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.S + (int64_t)row * D + part * P::SEG);
 #pragma unroll
-    for (int i = 0; i < SW; ++i) spk[i] = *reinterpret_cast<const uint4 *>(srow + 8 * i);
-    float v = 0.f;
-    if (t < D) v = flip_sign(load_q(a, h * D + t), (a.sign_bits[t >> 5] >> (t & 31)) & 1u);
-    // Walsh-Hadamard butterflies: strides below 64 inside the wave, the others through LDS
-#pragma unroll
-    for (int len = 1; len < 64; len <<= 1) {
-        const float o = __shfl_xor(v, len);
-        v = (lane & len) ? (o - v) : (v + o);
+        for (int i = 0; i < P::SEG / 8; ++i) spk[i] = src[i];
     }
-    for (int len = 64; len < D; len <<= 1) {
-        if (t < D) y[t] = v;
-        __syncthreads();
-        if (t < D) {
-            const float o = y[t ^ len];
-            v = (t & len) ? (o - v) : (v + o);
+    // Walsh-Hadamard transform of head g by wave g (mod NW): strides below 64 across lanes,
+    // the others between a lane's own coordinates
+    for (int g = wave; g < G; g += NW) {
+        const int64_t qoff = ((int64_t)b * a.hq + kvh * G + g) * D;
+        float v[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = lane + 64 * e;
+            v[e] = flip_sign(load_q(a, qoff + j), (a.sign_bits[j >> 5] >> (j & 31)) & 1u);
         }
-        __syncthreads();
-    }
-    if (t < D) y[t] = v;
-    __syncthreads();
-    float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < SW; ++i) {
-        const uint4 pk = spk[i];
-        const float4 q0 = *reinterpret_cast<const float4 *>(&y[part * (D / PER) + 8 * i]);
-        const float4 q1 = *reinterpret_cast<const float4 *>(&y[part * (D / PER) + 8 * i + 4]);
-        acc = fmaf(f16_lo(pk.x), q0.x, acc);
-        acc = fmaf(f16_hi(pk.x), q0.y, acc);
-        acc = fmaf(f16_lo(pk.y), q0.z, acc);
-        acc = fmaf(f16_hi(pk.y), q0.w, acc);
-        acc = fmaf(f16_lo(pk.z), q1.x, acc);
-        acc = fmaf(f16_hi(pk.z), q1.y, acc);
-        acc = fmaf(f16_lo(pk.w), q1.z, acc);
-        acc = fmaf(f16_hi(pk.w), q1.w, acc);
-    }
-    part_acc[part][j] = acc;
-    __syncthreads();
-    if (t < D) {
-        float w = 0.f;
+        for (int len = 1; len < 64; len <<= 1)
 #pragma unroll
-        for (int pt = 0; pt < PER; ++pt) w += part_acc[pt][t];
-        float *pp = a.prep + h * (2 * D);
-        pp[t] = y[t];
-        pp[D + t] = w;
+            for (int e = 0; e < E; ++e) {
+                const float o = __shfl_xor(v[e], len);
+                v[e] = (lane & len) ? (o - v[e]) : (v[e] + o);
+            }
+#pragma unroll
+        for (int m = 1; m < E; m <<= 1) {
+            float u[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) u[e] = (e & m) ? (v[e ^ m] - v[e]) : (v[e] + v[e ^ m]);
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = u[e];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) qw[g * D + lane + 64 * e] = v[e];
     }
+    __syncthreads();
+    if (mine) {
+        float acc[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g] = 0.f;
+#pragma unroll
+        for (int i = 0; i < P::SEG / 8; ++i) {
+            const uint4 pk = spk[i];
+            const float s[8] = {f16_lo(pk.x), f16_hi(pk.x), f16_lo(pk.y), f16_hi(pk.y),
+                                f16_lo(pk.z), f16_hi(pk.z), f16_lo(pk.w), f16_hi(pk.w)};
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float *qg = qw + g * D + part * P::SEG + 8 * i;
+                const float4 q0 = *reinterpret_cast<const float4 *>(qg);
+                const float4 q1 = *reinterpret_cast<const float4 *>(qg + 4);
+                acc[g] = fmaf(s[0], q0.x, acc[g]);
+                acc[g] = fmaf(s[1], q0.y, acc[g]);
+                acc[g] = fmaf(s[2], q0.z, acc[g]);
+                acc[g] = fmaf(s[3], q0.w, acc[g]);
+                acc[g] = fmaf(s[4], q1.x, acc[g]);
+                acc[g] = fmaf(s[5], q1.y, acc[g]);
+                acc[g] = fmaf(s[6], q1.z, acc[g]);
+                acc[g] = fmaf(s[7], q1.w, acc[g]);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) qw[(G + part * G + g) * D + row] = acc[g];
+    }
+    __syncthreads();
 }
 
 template <int D, int VB, int G>
@@ -154,7 +171,6 @@ struct DecodeShape {
     static constexpr int NCOL = G * NG;       // value columns (head, group)
     static constexpr int NPASS = (NCOL + 15) / 16;
     static constexpr int HALF = 1 << (VB - 1);
-    static constexpr int PARTS = kThreads / D;  // ring split: token partitions per coordinate
     // per-wave staging buffer of one 32-token block (bytes): key words, norms, value words
     // (records in slot order 4 (t % 8) + t / 8, so that the code reads of four lane groups
     // hit different banks), scales
@@ -185,8 +201,10 @@ struct alignas(16) DecodeSmem {
     static constexpr int NSL = G == 8 ? 16 : (G == 4 ? 8 : 4);
     static constexpr int FZ = 4 * NSL;
     union {
-        unsigned char stage[NW][2][S::BUF_B];  // packed splits: per-wave double buffer
-        struct {                                // wave combine (after the loop)
+        // per-wave double buffer, buffer-major: stage[1] (NW * BUF_B contiguous bytes) also
+        // holds the query preparation before the first copy into it
+        unsigned char stage[2][NW][S::BUF_B];
+        struct {  // wave combine (after the loop)
             float wo[NW][G][D];
         } x;
     };
@@ -197,43 +215,6 @@ struct alignas(16) DecodeSmem {
     float wm[NW][G], wl[NW][G];
     int next_blk;       // the split's next block not yet handed to a wave
 };
-
-// ring split: the query (rows split in four padded quarters, so that the four threads of a
-// token read different banks), logits then p of a chunk, the token classes' partial o, and
-// the block reductions
-template <int D, int G>
-struct alignas(16) RingSmem {
-    static constexpr int QW = D / 4 + 4;
-    float q[G][4][QW];
-    float p[kRingChunk][G];
-    float wo[kWaves][G][D];
-    float red[kWaves * G];
-};
-
-// block-wide reduction of G values (max or sum); every thread gets the result
-template <int G, bool IsMax>
-__device__ __forceinline__ void block_reduce(float (&v)[G], float *scratch /* [kWaves][G] */) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float x = v[g];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            float y = __shfl_xor(x, o);
-            x = IsMax ? fmaxf(x, y) : x + y;
-        }
-        if (lane == 0) scratch[wv * G + g] = x;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float x = scratch[g];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) x = IsMax ? fmaxf(x, scratch[w * G + g]) : x + scratch[w * G + g];
-        v[g] = x;
-    }
-    __syncthreads();
-}
 
 // ---- global -> LDS copies issued by hand, waited for with explicit counts.  M0 holds the
 //      LDS destination of the wave's 64 x 16 (or 64 x 4) bytes, the global address is a
@@ -313,7 +294,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     const uint32_t *vw_s = a.vw + rec0 * S::VW;
     const uint16_t *vs_s = a.vs + rec0 * S::NG;
     const int last = (int)a.n_packed - 1;
-    const uint32_t lds_wave = (uint32_t)(uintptr_t)&sm.stage[wave][0][0];
+    const uint32_t lds_wave = (uint32_t)(uintptr_t)&sm.stage[0][wave][0];
     // ---- staging: block at token t0 into buffer bi (token indices clamped to the last
     //      packed token, so every copy reads records of this slice)
     // per-lane parts of the copies of a block (offsets from the block's first record);
@@ -348,7 +329,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
         o_vw[i] = r * (S::VW * 4) + col;
     }
     auto issue = [&](int t0, int bi) {
-        const uint32_t base = lds_wave + (uint32_t)(bi * S::BUF_B);
+        const uint32_t base = lds_wave + (uint32_t)(bi * NW * S::BUF_B);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (t0 + kBlock - 1 <= last) {
             // whole block in range: uniform record base, loop-invariant lane offsets
@@ -409,14 +390,26 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     // The split's blocks (32 tokens from t_begin): wave w starts with blocks w and w + NW.
     // 4-wave groups: then every NW-th block (a fixed order, so results repeat bit for bit).
     // 12-wave groups: each further block from an LDS counter, so the waves of the CU finish
-    // together (which wave sums which block then varies between calls).  The first two
-    // blocks' copies go out before the query loads below: the compiler's own waits for those
-    // then also cover these older copies.
+    // together (which wave sums which block then varies between calls).  The first block's
+    // copies go out before the query preparation (which uses the second staging buffers),
+    // the second block's after it.  The compiler's own waits for the preparation's loads
+    // then also cover the older copies.
     const int nb = (t_end - t_begin + kBlock - 1) / kBlock;
     int b0 = wave, b1 = wave + NW;
-    if (threadIdx.x == 0) sm.next_blk = 2 * NW;  // read after the barrier below
+    if (threadIdx.x == 0) sm.next_blk = 2 * NW;  // read after the barriers below
     if (b0 < nb) issue(t_begin + kBlock * b0, 0);
-    if (b1 < nb) issue(t_begin + kBlock * b1, 1);
+    float *qw = reinterpret_cast<float *>(&sm.stage[1][0][0]);
+    static_assert(PrepShape<D, NW>::template floats<G>() * 4 <= NW * S::BUF_B, "query preparation in LDS");
+    if constexpr (D == 256) {
+        // prepared once per slice by k_decode_prep (at d = 256, reading the 128 KB S matrix
+        // in every workgroup costs more than a launch): copied into LDS
+        static_assert(D != 256 || PrepShape<D, NW>::PARTS == 1, "prepared-query layout");
+        const float4 *src = reinterpret_cast<const float4 *>(a.prep + (int64_t)bk * 2 * G * D);
+        for (int i = threadIdx.x; i < 2 * G * D / 4; i += 64 * NW) reinterpret_cast<float4 *>(qw)[i] = src[i];
+        __syncthreads();
+    } else {
+        prep_query<D, G, NW>(a, qw, b, kvh);
+    }
 
     // Both parts are pre-scaled by scale * log2(e) / sqrt(d) (the sign part also by
     // sqrt(pi/2)/d), so that the logit in log2 units is |k| (centroid part + gamma * sign part).
@@ -449,16 +442,25 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     u32x4_t bc[S::BLDS ? 1 : S::NKS], bs[S::BLDS ? 1 : S::NKS];
     {
         const float cs = a.scale * kLog2e * (1.0f / sqrtf((float)D)), ss = cs * kQjl;
-        const float *pq = a.prep + ((int64_t)b * a.hq + kvh * G + rg) * (2 * D);
-        const float *pw = pq + D;
+        // q' of head rg, and the partial sums of w = S q' (summed here)
+        constexpr int PARTS = PrepShape<D, NW>::PARTS;
+        const float *pq = qw + rg * D;
+        const float *pw = qw + (G + rg) * D;
         constexpr int ce[8] = {0, 2, 4, 6, 1, 3, 5, 7};
         constexpr int se[8] = {0, 4, 1, 5, 2, 6, 3, 7};
         auto frag = [&](int ks, u32x4_t &fc, u32x4_t &fs) {
             const int w = q * S::NKS + ks;
             const float4 m0 = *reinterpret_cast<const float4 *>(pq + 8 * w);
             const float4 m1 = *reinterpret_cast<const float4 *>(pq + 8 * w + 4);
-            const float4 s0 = *reinterpret_cast<const float4 *>(pw + 8 * w);
-            const float4 s1 = *reinterpret_cast<const float4 *>(pw + 8 * w + 4);
+            float4 s0 = *reinterpret_cast<const float4 *>(pw + 8 * w);
+            float4 s1 = *reinterpret_cast<const float4 *>(pw + 8 * w + 4);
+#pragma unroll
+            for (int pt = 1; pt < PARTS; ++pt) {
+                const float4 u0 = *reinterpret_cast<const float4 *>(pw + pt * G * D + 8 * w);
+                const float4 u1 = *reinterpret_cast<const float4 *>(pw + pt * G * D + 8 * w + 4);
+                s0.x += u0.x; s0.y += u0.y; s0.z += u0.z; s0.w += u0.w;
+                s1.x += u1.x; s1.y += u1.y; s1.z += u1.z; s1.w += u1.w;
+            }
             const float vm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
             const float vs[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
             uint16_t hc[8], hs[8];
@@ -493,8 +495,9 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
 #pragma unroll
             for (int ks = 0; ks < S::NKS; ++ks) frag(ks, bc[ks], bs[ks]);
         }
-        __syncthreads();  // fragments visible (d = 128)
+        __syncthreads();  // fragments visible (d = 128); the second staging buffers are free
     }
+    if (b1 < nb) issue(t_begin + kBlock * b1, 1);
     const int cslot = rc ? q * SM::NSL + ri : SM::FZ, sslot = rs ? q * SM::NSL + ri : SM::FZ;
     // The lane's logits after the score products: token row trow of the block, heads
     // hbase .. hbase + NLR - 1.  The running reference max per head is kept in LDS (read
@@ -751,7 +754,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     //      waited for.
     for (int k = 0; b0 < nb; ++k) {
         if (b1 < nb) wait_vm<S::N_DMA>(); else wait_vm<0>();
-        process(&sm.stage[wave][k & 1][0], t_begin + kBlock * b0);
+        process(&sm.stage[k & 1][wave][0], t_begin + kBlock * b0);
         b0 = b1;
         if (b1 < nb) {
             if constexpr (NW == 12) {
@@ -795,184 +798,104 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     }
 }
 
-// ------------------------------------------------------------------ ring split (VALU)
-// Ring tokens [r0, r1) of one (batch, kv head), exact fp16: scores by four threads per token
-// (a quarter of the key row each, G dot products against q in LDS, summed across the four
-// lanes), block-wide softmax statistics, and values by threads that own a pair of
-// coordinates and a residue class of tokens (one 4-byte load per token, all of a chunk in
-// flight), reduced through LDS.  The first chunk's loads are issued before the query is
-// staged.  Writes the split's (m, l, o).
-template <int D, int G>
-__device__ void ring_split(const DecodeArgs &a, RingSmem<D, G> &sm, int bk, int b, int kvh, int r0, int r1,
-                           float *pp, float *pml) {
-    constexpr int NCP = D / 2;                 // coordinate pairs
-    constexpr int NTG = kThreads / NCP;        // token residue classes of the value pass
-    constexpr int QD = D / 4;                  // coordinates per scoring thread
-    constexpr int TPL = kRingChunk / NTG;      // value tokens per lane and chunk
-    static_assert(kThreads / 4 == kRingChunk, "one scoring pass per chunk");
-    const int tid = threadIdx.x;
-    const int cp = tid % NCP, tg = tid / NCP, part = tid & 3, tk = tid >> 2;
-    const uint16_t *rk = a.rk + (int64_t)bk * a.buffer_size * D;
-    const uint32_t *rv2 = reinterpret_cast<const uint32_t *>(a.rv + (int64_t)bk * a.buffer_size * D);
-    uint4 k4[QD / 8];
-    uint32_t v2[TPL];
-    auto load_chunk = [&](int c0, int cnt) {
-        const uint4 *kr = reinterpret_cast<const uint4 *>(rk + (int64_t)(c0 + min(tk, cnt - 1)) * D + part * QD);
-#pragma unroll
-        for (int i = 0; i < QD / 8; ++i) k4[i] = kr[i];
-#pragma unroll
-        for (int u = 0; u < TPL; ++u) {
-            const int tt = tg + u * NTG;
-            v2[u] = tt < cnt ? rv2[(int64_t)(c0 + tt) * NCP + cp] : 0u;
-        }
-    };
-    load_chunk(r0, min(kRingChunk, r1 - r0));
-    for (int i = tid; i < G * D; i += kThreads) {
-        const int g = i / D, j = i - g * D;
-        sm.q[g][j / QD][j % QD] = load_q(a, ((int64_t)b * a.hq + kvh * G + g) * D + j);
-    }
-    __syncthreads();
-    float m_run[G], l_run[G], o0[G], o1[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m_run[g] = -INFINITY;
-        l_run[g] = 0.f;
-        o0[g] = 0.f;
-        o1[g] = 0.f;
-    }
-    const float lscale = a.scale * kLog2e;
-    for (int c0 = r0; c0 < r1; c0 += kRingChunk) {
-        const int cnt = min(kRingChunk, r1 - c0);
-        if (c0 != r0) load_chunk(c0, cnt);
-        // logits (log2 units) of the chunk into sm.p
-        {
-            float acc[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) acc[g] = 0.f;
-#pragma unroll
-            for (int i = 0; i < QD / 8; ++i) {
-                const float kv[8] = {f16_lo(k4[i].x), f16_hi(k4[i].x), f16_lo(k4[i].y), f16_hi(k4[i].y),
-                                     f16_lo(k4[i].z), f16_hi(k4[i].z), f16_lo(k4[i].w), f16_hi(k4[i].w)};
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const float4 q0 = *reinterpret_cast<const float4 *>(&sm.q[g][part][8 * i]);
-                    const float4 q1 = *reinterpret_cast<const float4 *>(&sm.q[g][part][8 * i + 4]);
-                    acc[g] = fmaf(q0.x, kv[0], acc[g]);
-                    acc[g] = fmaf(q0.y, kv[1], acc[g]);
-                    acc[g] = fmaf(q0.z, kv[2], acc[g]);
-                    acc[g] = fmaf(q0.w, kv[3], acc[g]);
-                    acc[g] = fmaf(q1.x, kv[4], acc[g]);
-                    acc[g] = fmaf(q1.y, kv[5], acc[g]);
-                    acc[g] = fmaf(q1.z, kv[6], acc[g]);
-                    acc[g] = fmaf(q1.w, kv[7], acc[g]);
-                }
-            }
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                acc[g] += __shfl_xor(acc[g], 1);
-                acc[g] += __shfl_xor(acc[g], 2);
-            }
-            if (part == 0)
-#pragma unroll
-                for (int g = 0; g < G; ++g) sm.p[tk][g] = tk < cnt ? acc[g] * lscale : -INFINITY;
-        }
-        __syncthreads();
-        float lg[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) lg[g] = tid < kRingChunk ? sm.p[tid][g] : -INFINITY;
-        float mx[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) mx[g] = lg[g];
-        block_reduce<G, true>(mx, sm.red);  // its first barrier also ends every read of the logits
-        float pe[G], corr[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float mnew = fmaxf(m_run[g], mx[g]);
-            corr[g] = (m_run[g] == -INFINITY) ? 0.f : exp2f(m_run[g] - mnew);
-            pe[g] = (tid < cnt) ? exp2f(lg[g] - mnew) : 0.f;
-            if (tid < kRingChunk) sm.p[tid][g] = pe[g];
-            m_run[g] = mnew;
-        }
-        block_reduce<G, false>(pe, sm.red);  // its barriers also publish p
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            l_run[g] = l_run[g] * corr[g] + pe[g];
-            o0[g] *= corr[g];
-            o1[g] *= corr[g];
-        }
-        // values: coordinates 2cp, 2cp + 1 over tokens tg, tg + NTG, ... (p past cnt is 0)
-#pragma unroll
-        for (int u = 0; u < TPL; ++u) {
-            const int tt = tg + u * NTG;
-            const float va = f16_lo(v2[u]), vb = f16_hi(v2[u]);
-            float pg[G];
-            if constexpr (G >= 4) {
-#pragma unroll
-                for (int g4 = 0; g4 < G; g4 += 4) {
-                    const float4 p4 = *reinterpret_cast<const float4 *>(&sm.p[tt][g4]);
-                    pg[g4] = p4.x; pg[g4 + 1] = p4.y; pg[g4 + 2] = p4.z; pg[g4 + 3] = p4.w;
-                }
-            } else {
-#pragma unroll
-                for (int g = 0; g < G; ++g) pg[g] = sm.p[tt][g];
-            }
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                o0[g] = fmaf(pg[g], va, o0[g]);
-                o1[g] = fmaf(pg[g], vb, o1[g]);
-            }
-        }
-        __syncthreads();  // p is rewritten by the next chunk
-    }
-    // reduce the token classes through LDS
-    if (tg > 0)
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            sm.wo[tg - 1][g][2 * cp] = o0[g];
-            sm.wo[tg - 1][g][2 * cp + 1] = o1[g];
-        }
-    __syncthreads();
-    if (tg == 0) {
-#pragma unroll
-        for (int t2 = 0; t2 < NTG - 1; ++t2)
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                o0[g] += sm.wo[t2][g][2 * cp];
-                o1[g] += sm.wo[t2][g][2 * cp + 1];
-            }
-#pragma unroll
-        for (int g = 0; g < G; ++g) *reinterpret_cast<float2 *>(&pp[g * D + 2 * cp]) = make_float2(o0[g], o1[g]);
-        if (cp == 0)
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                pml[g * 2] = m_run[g];
-                pml[g * 2 + 1] = l_run[g];
-            }
-    }
-}
+// ------------------------------------------------------------------ prep kernel (d = 256)
+// Workgroup (slice, band): rows band*RB .. band*RB + RB - 1 of w = S q' for the G query heads
+// of one (batch, kv head); band 0 also stores q'.  prep[slice] = (q' [G][D], w [G][D]).
+// The band of S is copied into LDS with coalesced loads (consecutive 16-byte chunks per
+// wave), rows padded by 16 bytes; TPR threads per row (adjacent lanes) split its columns and
+// are summed by lane shuffles.  Every workgroup transforms the G queries itself.
+template <int D>
+struct PrepBand {
+    static constexpr int RB = 64;                   // rows of S per workgroup
+    static constexpr int NB = D / RB;               // bands per slice
+    static constexpr int RS = D + 8;                // padded LDS row stride (halfwords)
+    static constexpr int TPR = kThreads / RB;       // threads per row
+    static constexpr int CPT = D / TPR;             // columns per thread
+    static constexpr int NCH = RB * D / 8 / kThreads;  // 16-byte chunks of the band per thread
+};
 
-// ------------------------------------------------------------------ prep and ring launch
-// With ring tokens, workgroups 0 .. batch*hkv*R - 1 compute ring split r of one slice each
-// (R = n_split_total - n_split splits of ring_per_split tokens; first, as they are the longer
-// ones); the next batch*hq prepare one query head each.  Both only read the query and the
-// ring, so they share one launch ahead of the packed splits.
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? (G == 8 ? 3 : 4) : (G == 8 ? 2 : 3), 8)))
-void k_decode_prep(DecodeArgs a) {
-    const int R = a.n_split_total - a.n_split;
-    const int64_t nr = a.n_ring > 0 ? (int64_t)a.batch * a.hkv * R : 0;
-    if ((int64_t)blockIdx.x >= nr) {
-        prep_head<D>(a, (int64_t)blockIdx.x - nr);
-        return;
-    }
-    __shared__ RingSmem<D, G> rsm;
-    const int bk = (int)blockIdx.x / R, r = (int)blockIdx.x % R;
+__global__ __launch_bounds__(kThreads) void k_decode_prep(DecodeArgs a) {
+    using P = PrepBand<D>;
+    static_assert(P::CPT % 8 == 0 && (P::TPR & (P::TPR - 1)) == 0 && P::NCH * kThreads * 8 == P::RB * D, "band shape");
+    __shared__ __align__(16) uint16_t s_lds[P::RB * P::RS];
+    __shared__ __align__(16) float qs[G * D];  // q' [G][D]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int bk = blockIdx.x / P::NB, band = blockIdx.x % P::NB;
     const int b = bk / a.hkv, kvh = bk - b * a.hkv;
-    const int n_total = a.n_split_total, split = a.n_split + r;
-    float *pp = a.partial + ((int64_t)bk * n_total + split) * G * D;
-    float *pml = a.partial_ml + ((int64_t)bk * n_total + split) * G * 2;
-    const int r0 = r * a.ring_per_split, r1 = min(a.n_ring, r0 + a.ring_per_split);
-    ring_split<D, G>(a, rsm, bk, b, kvh, r0, r1, pp, pml);
+    uint4 ch[P::NCH];
+    const uint4 *src = reinterpret_cast<const uint4 *>(a.S + (int64_t)band * P::RB * D);
+#pragma unroll
+    for (int k = 0; k < P::NCH; ++k) ch[k] = src[k * kThreads + tid];
+    // q' of head g by wave g (mod 4), as in prep_query
+    constexpr int E = D / 64;
+    float *dst = a.prep + (int64_t)bk * 2 * G * D;
+    for (int g = wave; g < G; g += kWaves) {
+        const int64_t qoff = ((int64_t)b * a.hq + kvh * G + g) * D;
+        float v[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = lane + 64 * e;
+            v[e] = flip_sign(load_q(a, qoff + j), (a.sign_bits[j >> 5] >> (j & 31)) & 1u);
+        }
+#pragma unroll
+        for (int len = 1; len < 64; len <<= 1)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float o = __shfl_xor(v[e], len);
+                v[e] = (lane & len) ? (o - v[e]) : (v[e] + o);
+            }
+#pragma unroll
+        for (int m = 1; m < E; m <<= 1) {
+            float u[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) u[e] = (e & m) ? (v[e ^ m] - v[e]) : (v[e] + v[e ^ m]);
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = u[e];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            qs[g * D + lane + 64 * e] = v[e];
+            if (band == 0) dst[g * D + lane + 64 * e] = v[e];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < P::NCH; ++k) {
+        const int f = k * kThreads + tid;  // chunk f: band row f / (D / 8), columns 8 (f % (D / 8)) ..
+        *reinterpret_cast<uint4 *>(s_lds + (f / (D / 8)) * P::RS + 8 * (f % (D / 8))) = ch[k];
+    }
+    __syncthreads();
+    const int row = tid / P::TPR, part = tid % P::TPR;
+    float acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = 0.f;
+    const uint16_t *srow = s_lds + row * P::RS + part * P::CPT;
+#pragma unroll
+    for (int i = 0; i < P::CPT / 8; ++i) {
+        const uint4 pk = *reinterpret_cast<const uint4 *>(srow + 8 * i);
+        const float s[8] = {f16_lo(pk.x), f16_hi(pk.x), f16_lo(pk.y), f16_hi(pk.y),
+                            f16_lo(pk.z), f16_hi(pk.z), f16_lo(pk.w), f16_hi(pk.w)};
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float4 q0 = *reinterpret_cast<const float4 *>(qs + g * D + part * P::CPT + 8 * i);
+            const float4 q1 = *reinterpret_cast<const float4 *>(qs + g * D + part * P::CPT + 8 * i + 4);
+            acc[g] = fmaf(s[0], q0.x, acc[g]);
+            acc[g] = fmaf(s[1], q0.y, acc[g]);
+            acc[g] = fmaf(s[2], q0.z, acc[g]);
+            acc[g] = fmaf(s[3], q0.w, acc[g]);
+            acc[g] = fmaf(s[4], q1.x, acc[g]);
+            acc[g] = fmaf(s[5], q1.y, acc[g]);
+            acc[g] = fmaf(s[6], q1.z, acc[g]);
+            acc[g] = fmaf(s[7], q1.w, acc[g]);
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int o = 1; o < P::TPR; o <<= 1) acc[g] += __shfl_xor(acc[g], o);
+    if (part == 0)
+#pragma unroll
+        for (int g = 0; g < G; ++g) dst[(G + g) * D + band * P::RB + row] = acc[g];
 }
 
 // ------------------------------------------------------------------ main kernel
@@ -988,14 +911,13 @@ template <int D, int VB, int G, int NW>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd<D, VB, G, NW>, kDecodeWavesPerSimd<D, VB, G, NW>)))
 void k_decode_main(DecodeArgs a) {
-    using S = DecodeShape<D, VB, G>;
     static_assert(sizeof(DecodeSmem<D, VB, G, NW>) <= 160 * 1024, "LDS of one workgroup");
     __shared__ DecodeSmem<D, VB, G, NW> sm;
     const int tid = threadIdx.x;
-    const int split = blockIdx.x;  // packed splits only (the ring split runs with the prep)
+    const int split = blockIdx.x;  // packed splits (the merge launch attends to the ring)
     const int bk = blockIdx.y;     // b * hkv + kv head == slice
     const int b = bk / a.hkv, kvh = bk - b * a.hkv;
-    const int n_total = a.n_split_total;
+    const int n_total = a.n_split;
     float *pp = a.partial + ((int64_t)bk * n_total + split) * G * D;
     float *pml = a.partial_ml + ((int64_t)bk * n_total + split) * G * 2;
 
@@ -1029,48 +951,155 @@ void k_decode_main(DecodeArgs a) {
     }
 }
 
-// ------------------------------------------------------------------ split merge
-// One workgroup per (batch * kv head, query head of the group): combines the (m, l, o)
-// partials of every split (a separate launch, so the partials of all workgroups are
-// visible without device-wide fences).  The thread's first PF partial columns and its
-// (m, l) pair are loaded together up front, so the merge waits on memory once.
+// ------------------------------------------------------------------ merge and ring
+// One workgroup per query head (batch, kv head, head of the group), after the packed splits
+// (a separate launch, so their partials are visible without device-wide fences).  It adds
+// the head's attention over the ring's exact fp16 tokens (scored against the unrotated
+// query) to the (m, l, o) partials of the packed splits:
+//   * the partials' columns and (m, l) pairs, the query and the first ring chunk's key and
+//     value words are all loaded up front, so the workgroup waits on memory once (a ring
+//     longer than one chunk loads its further chunks in turn);
+//   * ring logits by TPT threads per token (a coordinate range each, against q in LDS),
+//     p = 2^(logit - m_r) with a running ring maximum m_r, values by threads that own a
+//     coordinate pair and a residue class of the chunk's tokens;
+//   * M = max(m_c, m_r); o = (sum_c 2^(m_c - M) o_c + 2^(m_r - M) o_r) /
+//     (sum_c 2^(m_c - M) l_c + 2^(m_r - M) l_r), zero for an empty context.
+template <int D>
+struct MergeShape {
+    static constexpr int NJ4 = D / 4;                // float4 columns of one head
+    static constexpr int NSG = kThreads / NJ4;       // split groups summed in parallel
+    static constexpr int PF = 4;                     // partials per thread loaded up front
+    static constexpr int RC = 128;                   // ring tokens per chunk
+    static constexpr int TPT = kThreads / RC;        // scoring threads per ring token
+    static constexpr int SEGK = D / TPT;             // key coordinates per scoring thread
+    static constexpr int NCP = D / 2;                // value coordinate pairs
+    static constexpr int NTG = kThreads / NCP;       // value token classes
+    static constexpr int TPV = RC / NTG;             // value tokens per thread and chunk
+};
+
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void k_decode_merge(DecodeArgs a) {
-    constexpr int NJ4 = D / 4;             // float4 columns of one head
-    constexpr int NSG = kThreads / NJ4;    // split groups summed in parallel
-    constexpr int PF = 96 / NSG;           // partials per thread loaded up front
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 2, 8))) void k_decode_merge(DecodeArgs a) {
+    using M = MergeShape<D>;
+    static_assert(M::RC <= 128 && M::SEGK % 8 == 0 && (M::TPT & (M::TPT - 1)) == 0, "ring chunk shape");
     __shared__ float f[256];
     __shared__ float red[kWaves];
-    __shared__ float4 acc_s[NSG][NJ4];
+    __shared__ float4 acc_s[M::NSG][M::NJ4];
+    __shared__ float qs[D];
+    __shared__ float sp[M::RC];           // ring logits of a chunk, then p
+    __shared__ float ro[M::NTG][D];       // ring o per token class
+    __shared__ float rl[M::NTG];          // ring sum of p per token class
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int bk = blockIdx.x / G, g = blockIdx.x % G;
+    // workgroup x -> (slice, head of the group).  Workgroups are dispatched round-robin over
+    // the 8 XCDs, so the G heads of a slice get indices 8 apart: they run on one XCD and read
+    // the slice's ring through one L2.
+    const int xcd = blockIdx.x & 7, r8 = blockIdx.x >> 3;
+    const int g = r8 % G, bk = (r8 / G) * 8 + xcd;
+    if (bk >= a.batch * a.hkv) return;
     const int b = bk / a.hkv, kvh = bk - b * a.hkv;
-    const int n_total = a.n_split_total;  // <= 256
-    const float *ml = a.partial_ml + (int64_t)bk * n_total * G * 2;
-    const float *po = a.partial + (int64_t)bk * n_total * G * D;
-    const int j4 = tid % NJ4, sg = tid / NJ4;
+    const int64_t head = (int64_t)b * a.hq + kvh * G + g;
+    const int n_split = a.n_split;  // <= 256
+    const int n_ring = a.n_ring;
+    const float *ml = a.partial_ml + (int64_t)bk * n_split * G * 2;
+    const float *po = a.partial + (int64_t)bk * n_split * G * D;
+    const int j4 = tid % M::NJ4, sg = tid / M::NJ4;
 
-    float4 pre[PF];
+    // ---- loads up front
+    float4 pre[M::PF];
 #pragma unroll
-    for (int k = 0; k < PF; ++k) {
-        const int sp = sg + k * NSG;
-        pre[k] = sp < n_total ? *reinterpret_cast<const float4 *>(po + (int64_t)(sp * G + g) * D + 4 * j4)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < M::PF; ++k) {
+        const int sp_ = sg + k * M::NSG;
+        pre[k] = sp_ < n_split ? *reinterpret_cast<const float4 *>(po + (int64_t)(sp_ * G + g) * D + 4 * j4)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float2 mlv = make_float2(-INFINITY, 0.f);
-    if (tid < n_total) mlv = *reinterpret_cast<const float2 *>(ml + (tid * G + g) * 2);
+    if (tid < n_split) mlv = *reinterpret_cast<const float2 *>(ml + (tid * G + g) * 2);
 
+    const int tk = tid / M::TPT, kp = tid % M::TPT;  // ring scoring: token, coordinate range
+    const int cp = tid % M::NCP, tg = tid / M::NCP;  // ring values: coordinate pair, token class
+    const uint16_t *rk = a.rk + (int64_t)bk * a.buffer_size * D;
+    const uint32_t *rv2 = reinterpret_cast<const uint32_t *>(a.rv + (int64_t)bk * a.buffer_size * D);
+    uint4 k4[M::SEGK / 8];
+    uint32_t v2[M::TPV];
+    // chunk [c0, c0 + cnt): key rows clamped to the chunk's last token, values past it zero
+    auto load_chunk = [&](int c0, int cnt) {
+        const uint4 *kr = reinterpret_cast<const uint4 *>(rk + (int64_t)(c0 + min(tk, cnt - 1)) * D + kp * M::SEGK);
+#pragma unroll
+        for (int i = 0; i < M::SEGK / 8; ++i) k4[i] = kr[i];
+#pragma unroll
+        for (int u = 0; u < M::TPV; ++u) {
+            const int tt = tg + u * M::NTG;
+            v2[u] = tt < cnt ? rv2[(int64_t)(c0 + tt) * M::NCP + cp] : 0u;
+        }
+    };
+    float mr = -INFINITY, lr = 0.f, o0 = 0.f, o1 = 0.f;
+    if (n_ring > 0) {
+        load_chunk(0, min(M::RC, n_ring));
+        for (int j = tid; j < D; j += kThreads) qs[j] = load_q(a, head * D + j);
+        __syncthreads();  // q visible
+        const float lscale = a.scale * kLog2e;
+        for (int c0 = 0; c0 < n_ring; c0 += M::RC) {
+            const int cnt = min(M::RC, n_ring - c0);
+            if (c0 != 0) load_chunk(c0, cnt);
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < M::SEGK / 8; ++i) {
+                const float kv[8] = {f16_lo(k4[i].x), f16_hi(k4[i].x), f16_lo(k4[i].y), f16_hi(k4[i].y),
+                                     f16_lo(k4[i].z), f16_hi(k4[i].z), f16_lo(k4[i].w), f16_hi(k4[i].w)};
+                const float4 q0 = *reinterpret_cast<const float4 *>(&qs[kp * M::SEGK + 8 * i]);
+                const float4 q1 = *reinterpret_cast<const float4 *>(&qs[kp * M::SEGK + 8 * i + 4]);
+                acc = fmaf(q0.x, kv[0], acc);
+                acc = fmaf(q0.y, kv[1], acc);
+                acc = fmaf(q0.z, kv[2], acc);
+                acc = fmaf(q0.w, kv[3], acc);
+                acc = fmaf(q1.x, kv[4], acc);
+                acc = fmaf(q1.y, kv[5], acc);
+                acc = fmaf(q1.z, kv[6], acc);
+                acc = fmaf(q1.w, kv[7], acc);
+            }
+#pragma unroll
+            for (int o = 1; o < M::TPT; o <<= 1) acc += __shfl_xor(acc, o);
+            if (kp == 0) sp[tk] = tk < cnt ? acc * lscale : -INFINITY;
+            __syncthreads();
+            // the chunk's maximum, by every wave on its own
+            float cm = sp[lane];
+            if constexpr (M::RC > 64) cm = fmaxf(cm, sp[lane + 64]);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o));
+            const float mnew = fmaxf(mr, cm);  // finite: the chunk holds a token
+            const float corr = mr == -INFINITY ? 0.f : exp2f(mr - mnew);
+            __syncthreads();  // every wave has read the logits
+            if (tid < M::RC) sp[tid] = exp2f(sp[tid] - mnew);  // masked tokens: 0
+            __syncthreads();
+            mr = mnew;
+            lr *= corr;
+            o0 *= corr;
+            o1 *= corr;
+#pragma unroll
+            for (int u = 0; u < M::TPV; ++u) {
+                const float pt = sp[tg + u * M::NTG];
+                lr += pt;
+                o0 = fmaf(pt, f16_lo(v2[u]), o0);
+                o1 = fmaf(pt, f16_hi(v2[u]), o1);
+            }
+            __syncthreads();  // sp is rewritten by the next chunk
+        }
+        *reinterpret_cast<float2 *>(&ro[tg][2 * cp]) = make_float2(o0, o1);
+        if (cp == 0) rl[tg] = lr;
+    }
+
+    // ---- maximum over the splits and the ring
     float m = mlv.x;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     if (lane == 0) red[wv] = m;
-    __syncthreads();
-    float M = red[0];
+    __syncthreads();  // also publishes ro and rl
+    float Mx = mr;
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red[w]);
+    for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, red[w]);
     __syncthreads();
-    const float fw = (mlv.x == -INFINITY) ? 0.f : exp2f(mlv.x - M);
-    if (tid < n_total) f[tid] = fw;
+    const float fw = (mlv.x == -INFINITY) ? 0.f : exp2f(mlv.x - Mx);
+    const float fr = (mr == -INFINITY) ? 0.f : exp2f(mr - Mx);
+    if (tid < n_split) f[tid] = fw;
     float l = fw * mlv.y;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
@@ -1079,20 +1108,26 @@ __global__ __launch_bounds__(kThreads) void k_decode_merge(DecodeArgs a) {
     float L = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) L += red[w];
+    if (n_ring > 0) {
+        float lrt = 0.f;
+#pragma unroll
+        for (int c = 0; c < M::NTG; ++c) lrt += rl[c];
+        L = fmaf(fr, lrt, L);
+    }
 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int k = 0; k < PF; ++k) {
-        const int sp = sg + k * NSG;
-        const float w = sp < n_total ? f[sp] : 0.f;
+    for (int k = 0; k < M::PF; ++k) {
+        const int sp_ = sg + k * M::NSG;
+        const float w = sp_ < n_split ? f[sp_] : 0.f;
         acc.x = fmaf(w, pre[k].x, acc.x);
         acc.y = fmaf(w, pre[k].y, acc.y);
         acc.z = fmaf(w, pre[k].z, acc.z);
         acc.w = fmaf(w, pre[k].w, acc.w);
     }
-    for (int sp = sg + PF * NSG; sp < n_total; sp += NSG) {
-        const float4 v = *reinterpret_cast<const float4 *>(po + (int64_t)(sp * G + g) * D + 4 * j4);
-        const float w = f[sp];
+    for (int sp_ = sg + M::PF * M::NSG; sp_ < n_split; sp_ += M::NSG) {
+        const float4 v = *reinterpret_cast<const float4 *>(po + (int64_t)(sp_ * G + g) * D + 4 * j4);
+        const float w = f[sp_];
         acc.x = fmaf(w, v.x, acc.x);
         acc.y = fmaf(w, v.y, acc.y);
         acc.z = fmaf(w, v.z, acc.z);
@@ -1102,15 +1137,25 @@ __global__ __launch_bounds__(kThreads) void k_decode_merge(DecodeArgs a) {
     __syncthreads();
     if (sg == 0) {
 #pragma unroll
-        for (int k = 1; k < NSG; ++k) {
+        for (int k = 1; k < M::NSG; ++k) {
             const float4 v = acc_s[k][j4];
             acc.x += v.x;
             acc.y += v.y;
             acc.z += v.z;
             acc.w += v.w;
         }
+        if (n_ring > 0) {
+#pragma unroll
+            for (int c = 0; c < M::NTG; ++c) {
+                const float4 v = *reinterpret_cast<const float4 *>(&ro[c][4 * j4]);
+                acc.x = fmaf(fr, v.x, acc.x);
+                acc.y = fmaf(fr, v.y, acc.y);
+                acc.z = fmaf(fr, v.z, acc.z);
+                acc.w = fmaf(fr, v.w, acc.w);
+            }
+        }
         const float inv = L > 0.f ? 1.f / L : 0.f;
-        *reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.hq + kvh * G + g) * D + 4 * j4) =
+        *reinterpret_cast<float4 *>(a.out + head * D + 4 * j4) =
             make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
 }
@@ -1141,10 +1186,10 @@ __global__ __launch_bounds__(256) void k_ring_append(const void *kn, const void 
 // ------------------------------------------------------------------ launchers
 template <int D, int VB, int G>
 static void launch_g(const DecodeArgs &a, hipStream_t st) {
-    const unsigned pgrid =
-        (unsigned)(a.batch * a.hq + (a.n_ring > 0 ? a.batch * a.hkv * (a.n_split_total - a.n_split) : 0));
-    hipLaunchKernelGGL((k_decode_prep<D, G>), dim3(pgrid), dim3(kThreads), 0, st, a);
     if (a.n_split > 0) {
+        if constexpr (D == 256)
+            hipLaunchKernelGGL((k_decode_prep<D, G>), dim3((unsigned)(a.batch * a.hkv * PrepBand<D>::NB)),
+                               dim3(kThreads), 0, st, a);
         const dim3 grid((unsigned)a.n_split, (unsigned)(a.batch * a.hkv));
         if constexpr (D == 128 && G <= 4) {
             if (a.waves == 12) hipLaunchKernelGGL((k_decode_main<D, VB, G, 12>), grid, dim3(64 * 12), 0, st, a);
@@ -1153,7 +1198,8 @@ static void launch_g(const DecodeArgs &a, hipStream_t st) {
             hipLaunchKernelGGL((k_decode_main<D, VB, G, 4>), grid, dim3(64 * 4), 0, st, a);
         }
     }
-    hipLaunchKernelGGL((k_decode_merge<D, G>), dim3((unsigned)(a.batch * a.hkv * G)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((k_decode_merge<D, G>), dim3((unsigned)((a.batch * a.hkv + 7) / 8 * 8 * G)), dim3(kThreads), 0,
+                       st, a);
 }
 
 template <int D, int VB>

@@ -56,16 +56,14 @@ struct DecodeArgs {
     int buffer_size;
     int n_ring;
     int batch, hq, hkv;
-    int n_split;        // splits over the packed tokens
-    int n_split_total;  // n_split, plus the ring splits when there are ring tokens
-    int ring_per_split; // ring tokens per ring split
+    int n_split;        // splits over the packed tokens (0 when there are none), <= 256
     int waves;          // waves per workgroup of the packed splits (4 or 12)
     int64_t per_split;  // packed tokens per split
     float scale;
     float *out;
-    float *prep;         // [batch*hq][2*D]: q' = H sigma q, w = S q' 
-    float *partial;      // [batch*hkv][n_split_total][G][D]: o of each split
-    float *partial_ml;   // [batch*hkv][n_split_total][G][2]: (m, l) of each split
+    float *prep;         // d = 256: [batch*hkv][2][G][D], q' then w of the slice's query heads
+    float *partial;      // [batch*hkv][n_split][G][D]: o of each split
+    float *partial_ml;   // [batch*hkv][n_split][G][2]: (m, l) of each split
 };
 
 hipError_t launch_quantize(int d, int vb, tq_dtype dt, const QuantArgs &a, hipStream_t st);

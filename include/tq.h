@@ -144,8 +144,8 @@ tq_status tq_flush(const tq_config *cfg, const tq_tables *tables, const tq_ring 
                    int32_t n_ring, const tq_packed *dst, int64_t n_packed, void *stream);
 
 /* Workspace (device bytes) needed by tq_decode_attention for up to max_context tokens
- * (packed + ring): prepared queries and per-split partial results, scratch only (no
- * initialisation needed).  Calls that share a workspace must be ordered (same stream), as
+ * (packed + ring): per-split partial results of the packed tokens, and at head_dim 256 the
+ * prepared queries; scratch only (no initialisation needed).  Calls that share a workspace must be ordered (same stream), as
  * they use it in turn. */
 size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch, int32_t n_q_heads,
                                  int32_t n_kv_heads, int64_t max_context);
