@@ -219,6 +219,21 @@ def test_decode_ring_only_and_single_token(torch):
     _decode_case(W.custom(2, n_packed=257, n_ring=1), "257 + 1")
 
 
+def test_decode_ring_longer_than_one_chunk(torch):
+    # the ring is scored in chunks of 128 tokens with a running maximum: several chunks and a
+    # ragged last one, with and without packed history, at both head sizes
+    _decode_case(W.custom(2, n_packed=400, n_ring=300, buffer_size=512), "d128 ring 300")
+    _decode_case(W.custom(2, n_packed=0, n_ring=257, buffer_size=512), "d128 ring only 257")
+    _decode_case(W.custom(4, batch=1, n_packed=300, n_ring=200, buffer_size=256), "d256 ring 200")
+
+
+def test_decode_slices_not_a_multiple_of_eight(torch):
+    # the merge groups a slice's query heads on one XCD by workgroup index; 6 and 3 slices
+    # leave part of the last group of 8 empty
+    _decode_case(W.custom(2, batch=3, hq=8, hkv=2, n_packed=900, n_ring=17), "6 slices G=4")
+    _decode_case(W.custom(4, batch=3, hq=2, hkv=1, n_packed=700, n_ring=128), "3 slices d256 G=2")
+
+
 def test_decode_empty_context_gives_zeros(torch):
     env = Env(128, 2)
     q = np.ones((1, 4, 128), np.float32)
