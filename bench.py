@@ -177,7 +177,10 @@ def main():
     q_gbps = q_bytes / (q_med * 1e-3) / 1e9
     d_gbps = dec_bytes / (d_med * 1e-3) / 1e9
     dominant = "quantize" if q_med >= d_med else "decode"
-    q_kernels, d_kernels = "k_quant_kv", "k_decode_prep+k_decode_main+k_decode_merge"
+    # decode kernel set: a prep launch only at head_dim 256 (at 128 the main kernel prepares
+    # the queries itself)
+    q_kernels = "k_quant_kv"
+    d_kernels = ("k_decode_prep+" if d == 256 else "") + "k_decode_main+k_decode_merge"
     roof = {
         "kernel": q_kernels if dominant == "quantize" else d_kernels,
         "bound": "hbm",
