@@ -13,6 +13,8 @@ namespace {
 constexpr int64_t kSplitQuantum = 128;     // split sizes are multiples of four 32-token blocks
 constexpr int64_t kMinSplitTokens = 512;   // at least four blocks per wave
 constexpr int64_t kMaxSplits = 256;        // the merge keeps one weight per split in LDS
+// ring tokens attended to per split, at most (the main kernel's register budget)
+int64_t ring_per_split_max(int d) { return d == 128 ? 64 : 32; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
@@ -163,8 +165,10 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch,
         max_context < 0)
         return 0;
     if (n_q_heads % n_kv_heads != 0) return 0;
-    const int64_t n_split = decode_splits(cfg->head_dim, cfg->value_bits, n_q_heads / n_kv_heads,
-                                          (int64_t)batch * n_kv_heads, max_context, 4);
+    const int64_t n_split =
+        std::max(decode_splits(cfg->head_dim, cfg->value_bits, n_q_heads / n_kv_heads, (int64_t)batch * n_kv_heads,
+                               max_context, 4),
+                 ((int64_t)cfg->buffer_size + ring_per_split_max(cfg->head_dim) - 1) / ring_per_split_max(cfg->head_dim));
     return decode_layout(cfg->head_dim, batch, n_q_heads, n_split).total;
 }
 
@@ -189,11 +193,21 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     if (n_ring > 0 && (!ring || !ring->k || !ring->v || !aligned16(ring->k) || !aligned16(ring->v)))
         return TQ_ERR_INVALID_ARG;
     const int64_t slices = (int64_t)batch * n_kv_heads;
-    // packed splits (none for an empty packed store: the merge launch then attends to the ring
-    // alone, or writes zeros for an empty context)
-    int64_t n_split = 0, per_split = 0;
+    // splits of the packed tokens, at least one (an empty context still writes its zeros), and
+    // enough for the ring tokens at ring_per_split_max per split; the ring is spread evenly
+    int64_t n_split = 1, per_split = 0;
     const int waves = n_packed > 0 ? decode_waves(cfg->head_dim, G, slices, n_packed) : 4;
     if (n_packed > 0) split_shape(cfg->head_dim, cfg->value_bits, G, slices, n_packed, waves, n_split, per_split);
+    const int64_t ring_splits = (n_ring + ring_per_split_max(cfg->head_dim) - 1) / ring_per_split_max(cfg->head_dim);
+    if (ring_splits > n_split) {
+        // more splits for the ring than for the packed tokens: spread the packed tokens too
+        n_split = ring_splits;
+        if (n_packed > 0) {
+            per_split = (n_packed + n_split - 1) / n_split;
+            per_split = (per_split + kSplitQuantum - 1) / kSplitQuantum * kSplitQuantum;
+        }
+    }
+    const int64_t ring_per_split = (n_ring + n_split - 1) / n_split;
     const DecodeLayout L = decode_layout(cfg->head_dim, batch, n_q_heads, n_split);
     if (workspace_bytes < L.total) return TQ_ERR_WORKSPACE;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
@@ -221,6 +235,7 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     a.hq = n_q_heads;
     a.hkv = n_kv_heads;
     a.n_split = (int)n_split;
+    a.ring_per_split = (int)ring_per_split;
     a.waves = waves;
     a.per_split = per_split;
     a.scale = softmax_scale;

@@ -88,29 +88,55 @@ struct PrepShape {
     static constexpr int floats() { return (1 + PARTS) * G * D; }
 };
 
+// The loads of the preparation (this thread's part of S, the query coordinates it
+// transforms), issued ahead of other work; prep_query then computes from them.
 template <int D, int G, int NW>
-__device__ void prep_query(const DecodeArgs &a, float *qw, int b, int kvh) {
+struct PrepRegs {
+    static constexpr int E = D / 64;                // coordinates per lane in the transform
+    static constexpr int HPW = (G + NW - 1) / NW;   // heads per wave
+    uint4 spk[PrepShape<D, NW>::SEG / 8];
+    float v[HPW][E];
+};
+
+template <int D, int G, int NW>
+__device__ __forceinline__ void prep_load(const DecodeArgs &a, PrepRegs<D, G, NW> &pr, int b, int kvh) {
     using P = PrepShape<D, NW>;
-    constexpr int E = D / 64;  // coordinates per lane in the transform, j = lane + 64 e
+    using Q = PrepRegs<D, G, NW>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = tid % D, part = tid / D;
-    const bool mine = part < P::PARTS;
-    uint4 spk[P::SEG / 8];
-    if (mine) {
+    if (part < P::PARTS) {
         const uint4 *src = reinterpret_cast<const uint4 *>(a.S + (int64_t)row * D + part * P::SEG);
 #pragma unroll
-        for (int i = 0; i < P::SEG / 8; ++i) spk[i] = src[i];
+        for (int i = 0; i < P::SEG / 8; ++i) pr.spk[i] = src[i];
     }
+#pragma unroll
+    for (int h = 0; h < Q::HPW; ++h) {
+        const int g = wave + h * NW;
+        if (g < G) {
+            const int64_t qoff = ((int64_t)b * a.hq + kvh * G + g) * D;
+#pragma unroll
+            for (int e = 0; e < Q::E; ++e) {
+                const int j = lane + 64 * e;
+                pr.v[h][e] = flip_sign(load_q(a, qoff + j), (a.sign_bits[j >> 5] >> (j & 31)) & 1u);
+            }
+        }
+    }
+}
+
+template <int D, int G, int NW>
+__device__ void prep_query(PrepRegs<D, G, NW> &pr, float *qw) {
+    using P = PrepShape<D, NW>;
+    using Q = PrepRegs<D, G, NW>;
+    constexpr int E = Q::E;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = tid % D, part = tid / D;
     // Walsh-Hadamard transform of head g by wave g (mod NW): strides below 64 across lanes,
     // the others between a lane's own coordinates
-    for (int g = wave; g < G; g += NW) {
-        const int64_t qoff = ((int64_t)b * a.hq + kvh * G + g) * D;
-        float v[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int j = lane + 64 * e;
-            v[e] = flip_sign(load_q(a, qoff + j), (a.sign_bits[j >> 5] >> (j & 31)) & 1u);
-        }
+    for (int h = 0; h < Q::HPW; ++h) {
+        const int g = wave + h * NW;
+        if (g >= G) break;
+        float *v = pr.v[h];
 #pragma unroll
         for (int len = 1; len < 64; len <<= 1)
 #pragma unroll
@@ -130,13 +156,13 @@ __device__ void prep_query(const DecodeArgs &a, float *qw, int b, int kvh) {
         for (int e = 0; e < E; ++e) qw[g * D + lane + 64 * e] = v[e];
     }
     __syncthreads();
-    if (mine) {
+    if (part < P::PARTS) {
         float acc[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) acc[g] = 0.f;
 #pragma unroll
         for (int i = 0; i < P::SEG / 8; ++i) {
-            const uint4 pk = spk[i];
+            const uint4 pk = pr.spk[i];
             const float s[8] = {f16_lo(pk.x), f16_hi(pk.x), f16_lo(pk.y), f16_hi(pk.y),
                                 f16_lo(pk.z), f16_hi(pk.z), f16_lo(pk.w), f16_hi(pk.w)};
 #pragma unroll
@@ -213,6 +239,7 @@ struct alignas(16) DecodeSmem {
     float corr[NW][G];
     float mref[NW][G];  // running reference max per wave and head (packed splits)
     float wm[NW][G], wl[NW][G];
+    float rm[G], rl[G];  // the split's ring tokens: maximum and sum of p per head
     int next_blk;       // the split's next block not yet handed to a wave
 };
 
@@ -249,10 +276,178 @@ __device__ __forceinline__ float from_lane_plus_g(float x) {
                                                                   0xf, true));
 }
 
+// ------------------------------------------------------------------ ring tokens of a split
+// The ring's exact fp16 tokens are spread over the packed splits of their slice (at most
+// kRingPerSplit<D> per split: 64 at d = 128, 32 at d = 256, a register budget).  Each
+// main-kernel workgroup attends to its share against the unrotated queries while its first
+// packed block's copy is in flight and folds the result into the split's (m, l, o) partial.
+// The ring words are loaded right after the first block's copies, with the query
+// preparation's inputs (one wait for both); scores, softmax statistics and values use the
+// second staging buffers as scratch before the query preparation and the second block's
+// copies take them.
+template <int D>
+constexpr int kRingPerSplit = D == 128 ? 64 : 32;
+
+template <int D, int G, int NW>
+struct RingShape {
+    static constexpr int NT = 64 * NW;
+    static constexpr int TPT = 8;                     // scoring threads per token
+    static constexpr int SEG = D / TPT;               // key coordinates per scoring thread
+    static constexpr int TCH = NT / TPT;              // tokens per scoring pass
+    static constexpr int NP = (kRingPerSplit<D> + TCH - 1) / TCH;  // scoring passes
+    static constexpr int NCP = D / 2;                 // value coordinate pairs
+    static constexpr int NTG = NT / NCP;              // value token classes
+    static constexpr int TPV = (kRingPerSplit<D> + NTG - 1) / NTG;  // value tokens per thread
+    static constexpr int NE = (G * D + NT - 1) / NT;  // combined output elements per thread
+    // LDS scratch (floats): q [G][D], logits then p [G][kRingPerSplit<D>], per-class value sums
+    // [NTG][GB][D] for a group of GB heads at a time
+    static constexpr int fixed() { return G * D + G * kRingPerSplit<D>; }
+    static constexpr int gb(int bytes) {
+        return (fixed() + NTG * 4 * D) * 4 <= bytes ? (G < 4 ? G : 4) : ((fixed() + NTG * 2 * D) * 4 <= bytes ? (G < 2 ? G : 2) : 1);
+    }
+};
+
+template <int D, int G, int NW>
+struct RingRegs {
+    using R = RingShape<D, G, NW>;
+    uint4 k4[R::NP][R::SEG / 8];
+    uint32_t v2[R::TPV];
+};
+
+// loads of the split's ring tokens [r0, r0 + n) (addresses clamped into the ring, unused
+// words ignored)
+template <int D, int G, int NW>
+__device__ __forceinline__ void ring_load(const DecodeArgs &a, RingRegs<D, G, NW> &rr, int bk, int r0, int n) {
+    using R = RingShape<D, G, NW>;
+    const int tid = threadIdx.x;
+    const int part = tid % R::TPT, cp = tid % R::NCP, tg = tid / R::NCP;
+    const uint16_t *rk = a.rk + (int64_t)bk * a.buffer_size * D;
+    const uint32_t *rv2 = reinterpret_cast<const uint32_t *>(a.rv + (int64_t)bk * a.buffer_size * D);
+#pragma unroll
+    for (int ps = 0; ps < R::NP; ++ps) {
+        const int tt = min(ps * R::TCH + tid / R::TPT, n - 1);
+        const uint4 *kr = reinterpret_cast<const uint4 *>(rk + (int64_t)(r0 + tt) * D + part * R::SEG);
+#pragma unroll
+        for (int i = 0; i < R::SEG / 8; ++i) rr.k4[ps][i] = ps * R::TCH < n ? kr[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < R::TPV; ++u) {
+        const int tt = tg + u * R::NTG;
+        rr.v2[u] = tt < n ? rv2[(int64_t)(r0 + tt) * R::NCP + cp] : 0u;
+    }
+}
+
+// attention of the G query heads over the split's n ring tokens: per head the maximum m_r
+// (log2 units) and sum l_r into rm / rl (LDS), and the unnormalised o_r of this thread's
+// output elements e = tid + k NT ([G][D] order) into orr.  scr: LDS scratch of SCR bytes.
+template <int D, int G, int NW, int SCR>
+__device__ void ring_attend(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, float *scr, float *rm, float *rl,
+                            int b, int kvh, int n, float (&orr)[RingShape<D, G, NW>::NE]) {
+    using R = RingShape<D, G, NW>;
+    constexpr int RP = kRingPerSplit<D>;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int part = tid % R::TPT, cp = tid % R::NCP, tg = tid / R::NCP;
+    float *qr = scr, *pr = scr + G * D, *os = pr + G * RP;
+    for (int i = tid; i < G * D; i += R::NT) qr[i] = load_q(a, ((int64_t)b * a.hq + kvh * G) * D + i);
+    __syncthreads();
+    const float lscale = a.scale * kLog2e;
+#pragma unroll
+    for (int ps = 0; ps < R::NP; ++ps) {
+        if (ps * R::TCH >= n) break;
+        const int tt = ps * R::TCH + tid / R::TPT;
+        float acc[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g] = 0.f;
+#pragma unroll
+        for (int i = 0; i < R::SEG / 8; ++i) {
+            const uint4 k = rr.k4[ps][i];
+            const float kv[8] = {f16_lo(k.x), f16_hi(k.x), f16_lo(k.y), f16_hi(k.y),
+                                 f16_lo(k.z), f16_hi(k.z), f16_lo(k.w), f16_hi(k.w)};
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float4 q0 = *reinterpret_cast<const float4 *>(qr + g * D + part * R::SEG + 8 * i);
+                const float4 q1 = *reinterpret_cast<const float4 *>(qr + g * D + part * R::SEG + 8 * i + 4);
+                acc[g] = fmaf(q0.x, kv[0], acc[g]);
+                acc[g] = fmaf(q0.y, kv[1], acc[g]);
+                acc[g] = fmaf(q0.z, kv[2], acc[g]);
+                acc[g] = fmaf(q0.w, kv[3], acc[g]);
+                acc[g] = fmaf(q1.x, kv[4], acc[g]);
+                acc[g] = fmaf(q1.y, kv[5], acc[g]);
+                acc[g] = fmaf(q1.z, kv[6], acc[g]);
+                acc[g] = fmaf(q1.w, kv[7], acc[g]);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int o = 1; o < R::TPT; o <<= 1) acc[g] += __shfl_xor(acc[g], o);
+            if (part == 0 && tt < n) pr[g * RP + tt] = acc[g] * lscale;
+        }
+    }
+    __syncthreads();
+    // per head (wave g, g + NW, ...): maximum, then p = 2^(logit - m) in place and its sum
+    for (int g = wave; g < G; g += NW) {
+        float m = -INFINITY;
+        for (int tt = lane; tt < n; tt += 64) m = fmaxf(m, pr[g * RP + tt]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        float l = 0.f;
+        for (int tt = lane; tt < n; tt += 64) {
+            const float pv = exp2f(pr[g * RP + tt] - m);
+            pr[g * RP + tt] = pv;
+            l += pv;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+        if (lane == 0) {
+            rm[g] = m;
+            rl[g] = l;
+        }
+    }
+    __syncthreads();
+    // values by (coordinate pair, token class) for GB heads at a time, summed over the classes
+    // by the threads that own the output elements
+    constexpr int GB = R::gb(SCR);
+    static_assert((R::fixed() + R::NTG * GB * D) * 4 <= SCR, "ring scratch in LDS");
+#pragma unroll
+    for (int k = 0; k < R::NE; ++k) orr[k] = 0.f;
+#pragma unroll
+    for (int g0 = 0; g0 < G; g0 += GB) {
+        float o0[GB], o1[GB];
+#pragma unroll
+        for (int h = 0; h < GB; ++h) o0[h] = o1[h] = 0.f;
+#pragma unroll
+        for (int u = 0; u < R::TPV; ++u) {
+            const int tt = tg + u * R::NTG;
+            const float va = f16_lo(rr.v2[u]), vb = f16_hi(rr.v2[u]);
+#pragma unroll
+            for (int h = 0; h < GB; ++h) {
+                const float pv = tt < n ? pr[(g0 + h) * RP + tt] : 0.f;
+                o0[h] = fmaf(pv, va, o0[h]);
+                o1[h] = fmaf(pv, vb, o1[h]);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < GB; ++h) *reinterpret_cast<float2 *>(os + (tg * GB + h) * D + 2 * cp) = make_float2(o0[h], o1[h]);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < R::NE; ++k) {
+            const int e = tid + k * R::NT, g = e / D, j = e - g * D;
+            if (e < G * D && g >= g0 && g < g0 + GB) {
+                float s = 0.f;
+#pragma unroll
+                for (int c = 0; c < R::NTG; ++c) s += os[(c * GB + g - g0) * D + j];
+                orr[k] = s;
+            }
+        }
+        __syncthreads();  // os is rewritten by the next group, the region by the staging copies
+    }
+}
+
 // ------------------------------------------------------------------ packed split (one wave)
 template <int D, int VB, int G, int NW>
 __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, int bk, int b, int kvh, int t_begin,
-                            int t_end) {
+                            int t_end, int r0, int nr, float (&orr)[RingShape<D, G, NW>::NE]) {
     using S = DecodeShape<D, VB, G>;
     constexpr float kQjl = 1.2533141373155003f / D;  // sqrt(pi/2) / d
     const int lane = threadIdx.x & 63;
@@ -398,17 +593,36 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     int b0 = wave, b1 = wave + NW;
     if (threadIdx.x == 0) sm.next_blk = 2 * NW;  // read after the barriers below
     if (b0 < nb) issue(t_begin + kBlock * b0, 0);
+    // all loads of the start at once: the ring tokens' words, then the query preparation's
+    // inputs (at d = 256 the prepared queries from the workspace)
+    RingRegs<D, G, NW> rr;
+    if (nr > 0) ring_load<D, G, NW>(a, rr, bk, r0, nr);
     float *qw = reinterpret_cast<float *>(&sm.stage[1][0][0]);
     static_assert(PrepShape<D, NW>::template floats<G>() * 4 <= NW * S::BUF_B, "query preparation in LDS");
+    constexpr int NQ4 = 2 * G * D / 4;                        // float4 of the prepared queries (d = 256)
+    constexpr int NPW = (NQ4 + 64 * NW - 1) / (64 * NW);      // per thread
+    float4 pw4[D == 256 ? NPW : 1];
+    PrepRegs<D, G, NW> prg;
     if constexpr (D == 256) {
         // prepared once per slice by k_decode_prep (at d = 256, reading the 128 KB S matrix
-        // in every workgroup costs more than a launch): copied into LDS
+        // in every workgroup costs more than a launch)
         static_assert(D != 256 || PrepShape<D, NW>::PARTS == 1, "prepared-query layout");
         const float4 *src = reinterpret_cast<const float4 *>(a.prep + (int64_t)bk * 2 * G * D);
-        for (int i = threadIdx.x; i < 2 * G * D / 4; i += 64 * NW) reinterpret_cast<float4 *>(qw)[i] = src[i];
+#pragma unroll
+        for (int i = 0; i < NPW; ++i)
+            if (threadIdx.x + i * 64 * NW < NQ4) pw4[i] = src[threadIdx.x + i * 64 * NW];
+    } else {
+        prep_load<D, G, NW>(a, prg, b, kvh);
+    }
+    // the split's ring tokens (the second staging buffers as scratch)
+    if (nr > 0) ring_attend<D, G, NW, NW * S::BUF_B>(a, rr, qw, sm.rm, sm.rl, b, kvh, nr, orr);
+    if constexpr (D == 256) {
+#pragma unroll
+        for (int i = 0; i < NPW; ++i)
+            if (threadIdx.x + i * 64 * NW < NQ4) reinterpret_cast<float4 *>(qw)[threadIdx.x + i * 64 * NW] = pw4[i];
         __syncthreads();
     } else {
-        prep_query<D, G, NW>(a, qw, b, kvh);
+        prep_query<D, G, NW>(prg, qw);
     }
 
     // Both parts are pre-scaled by scale * log2(e) / sqrt(d) (the sign part also by
@@ -914,7 +1128,7 @@ void k_decode_main(DecodeArgs a) {
     static_assert(sizeof(DecodeSmem<D, VB, G, NW>) <= 160 * 1024, "LDS of one workgroup");
     __shared__ DecodeSmem<D, VB, G, NW> sm;
     const int tid = threadIdx.x;
-    const int split = blockIdx.x;  // packed splits (the merge launch attends to the ring)
+    const int split = blockIdx.x;  // split: a range of packed tokens and of ring tokens
     const int bk = blockIdx.y;     // b * hkv + kv head == slice
     const int b = bk / a.hkv, kvh = bk - b * a.hkv;
     const int n_total = a.n_split;
@@ -922,14 +1136,21 @@ void k_decode_main(DecodeArgs a) {
     float *pml = a.partial_ml + ((int64_t)bk * n_total + split) * G * 2;
 
     {
+        using R = RingShape<D, G, NW>;
         const int t_begin = split * (int)a.per_split;
-        const int t_end = (int)min(a.n_packed, (int64_t)t_begin + a.per_split);
-        packed_wave<D, VB, G, NW>(a, sm, bk, b, kvh, t_begin, t_end);
+        const int t_end = max(t_begin, (int)min(a.n_packed, (int64_t)t_begin + a.per_split));
+        const int r0 = split * a.ring_per_split, nr = max(0, min(a.n_ring - r0, a.ring_per_split));
+        float orr[R::NE];
+        packed_wave<D, VB, G, NW>(a, sm, bk, b, kvh, t_begin, t_end, r0, nr, orr);
         __syncthreads();
-        // combine the waves
-        for (int i = tid; i < G * D; i += 64 * NW) {
+        // combine the waves and the split's ring tokens
+#pragma unroll
+        for (int k = 0; k < R::NE; ++k) {
+            const int i = tid + k * 64 * NW;
+            if (i >= G * D) break;
             const int g = i / D, j = i - g * D;
-            float M = -INFINITY;
+            const float mr = nr > 0 ? sm.rm[g] : -INFINITY;
+            float M = mr;
 #pragma unroll
             for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.wm[w][g]);
             float L = 0.f, O = 0.f;
@@ -941,6 +1162,11 @@ void k_decode_main(DecodeArgs a) {
                     L = fmaf(sm.wl[w][g], f, L);
                     O = fmaf(sm.x.wo[w][g][j], f, O);
                 }
+                if (mr != -INFINITY) {
+                    const float f = exp2f(mr - M);
+                    L = fmaf(sm.rl[g], f, L);
+                    O = fmaf(orr[k], f, O);
+                }
             }
             pp[g * D + j] = O;
             if (j == 0) {
@@ -951,155 +1177,48 @@ void k_decode_main(DecodeArgs a) {
     }
 }
 
-// ------------------------------------------------------------------ merge and ring
-// One workgroup per query head (batch, kv head, head of the group), after the packed splits
-// (a separate launch, so their partials are visible without device-wide fences).  It adds
-// the head's attention over the ring's exact fp16 tokens (scored against the unrotated
-// query) to the (m, l, o) partials of the packed splits:
-//   * the partials' columns and (m, l) pairs, the query and the first ring chunk's key and
-//     value words are all loaded up front, so the workgroup waits on memory once (a ring
-//     longer than one chunk loads its further chunks in turn);
-//   * ring logits by TPT threads per token (a coordinate range each, against q in LDS),
-//     p = 2^(logit - m_r) with a running ring maximum m_r, values by threads that own a
-//     coordinate pair and a residue class of the chunk's tokens;
-//   * M = max(m_c, m_r); o = (sum_c 2^(m_c - M) o_c + 2^(m_r - M) o_r) /
-//     (sum_c 2^(m_c - M) l_c + 2^(m_r - M) l_r), zero for an empty context.
-template <int D>
-struct MergeShape {
-    static constexpr int NJ4 = D / 4;                // float4 columns of one head
-    static constexpr int NSG = kThreads / NJ4;       // split groups summed in parallel
-    static constexpr int PF = 4;                     // partials per thread loaded up front
-    static constexpr int RC = 128;                   // ring tokens per chunk
-    static constexpr int TPT = kThreads / RC;        // scoring threads per ring token
-    static constexpr int SEGK = D / TPT;             // key coordinates per scoring thread
-    static constexpr int NCP = D / 2;                // value coordinate pairs
-    static constexpr int NTG = kThreads / NCP;       // value token classes
-    static constexpr int TPV = RC / NTG;             // value tokens per thread and chunk
-};
-
+// ------------------------------------------------------------------ split merge
+// One workgroup per (batch * kv head, query head of the group): combines the (m, l, o)
+// partials of every split, the ring included (a separate launch, so the partials of all
+// workgroups are visible without device-wide fences).  The thread's first PF partial columns and its
+// (m, l) pair are loaded together up front, so the merge waits on memory once.
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 2, 8))) void k_decode_merge(DecodeArgs a) {
-    using M = MergeShape<D>;
-    static_assert(M::RC <= 128 && M::SEGK % 8 == 0 && (M::TPT & (M::TPT - 1)) == 0, "ring chunk shape");
+__global__ __launch_bounds__(kThreads) void k_decode_merge(DecodeArgs a) {
+    constexpr int NJ4 = D / 4;             // float4 columns of one head
+    constexpr int NSG = kThreads / NJ4;    // split groups summed in parallel
+    constexpr int PF = 96 / NSG;           // partials per thread loaded up front
     __shared__ float f[256];
     __shared__ float red[kWaves];
-    __shared__ float4 acc_s[M::NSG][M::NJ4];
-    __shared__ float qs[D];
-    __shared__ float sp[M::RC];           // ring logits of a chunk, then p
-    __shared__ float ro[M::NTG][D];       // ring o per token class
-    __shared__ float rl[M::NTG];          // ring sum of p per token class
+    __shared__ float4 acc_s[NSG][NJ4];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    // workgroup x -> (slice, head of the group).  Workgroups are dispatched round-robin over
-    // the 8 XCDs, so the G heads of a slice get indices 8 apart: they run on one XCD and read
-    // the slice's ring through one L2.
-    const int xcd = blockIdx.x & 7, r8 = blockIdx.x >> 3;
-    const int g = r8 % G, bk = (r8 / G) * 8 + xcd;
-    if (bk >= a.batch * a.hkv) return;
+    const int bk = blockIdx.x / G, g = blockIdx.x % G;
     const int b = bk / a.hkv, kvh = bk - b * a.hkv;
-    const int64_t head = (int64_t)b * a.hq + kvh * G + g;
-    const int n_split = a.n_split;  // <= 256
-    const int n_ring = a.n_ring;
-    const float *ml = a.partial_ml + (int64_t)bk * n_split * G * 2;
-    const float *po = a.partial + (int64_t)bk * n_split * G * D;
-    const int j4 = tid % M::NJ4, sg = tid / M::NJ4;
+    const int n_total = a.n_split;  // <= 256
+    const float *ml = a.partial_ml + (int64_t)bk * n_total * G * 2;
+    const float *po = a.partial + (int64_t)bk * n_total * G * D;
+    const int j4 = tid % NJ4, sg = tid / NJ4;
 
-    // ---- loads up front
-    float4 pre[M::PF];
+    float4 pre[PF];
 #pragma unroll
-    for (int k = 0; k < M::PF; ++k) {
-        const int sp_ = sg + k * M::NSG;
-        pre[k] = sp_ < n_split ? *reinterpret_cast<const float4 *>(po + (int64_t)(sp_ * G + g) * D + 4 * j4)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < PF; ++k) {
+        const int sp = sg + k * NSG;
+        pre[k] = sp < n_total ? *reinterpret_cast<const float4 *>(po + (int64_t)(sp * G + g) * D + 4 * j4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float2 mlv = make_float2(-INFINITY, 0.f);
-    if (tid < n_split) mlv = *reinterpret_cast<const float2 *>(ml + (tid * G + g) * 2);
+    if (tid < n_total) mlv = *reinterpret_cast<const float2 *>(ml + (tid * G + g) * 2);
 
-    const int tk = tid / M::TPT, kp = tid % M::TPT;  // ring scoring: token, coordinate range
-    const int cp = tid % M::NCP, tg = tid / M::NCP;  // ring values: coordinate pair, token class
-    const uint16_t *rk = a.rk + (int64_t)bk * a.buffer_size * D;
-    const uint32_t *rv2 = reinterpret_cast<const uint32_t *>(a.rv + (int64_t)bk * a.buffer_size * D);
-    uint4 k4[M::SEGK / 8];
-    uint32_t v2[M::TPV];
-    // chunk [c0, c0 + cnt): key rows clamped to the chunk's last token, values past it zero
-    auto load_chunk = [&](int c0, int cnt) {
-        const uint4 *kr = reinterpret_cast<const uint4 *>(rk + (int64_t)(c0 + min(tk, cnt - 1)) * D + kp * M::SEGK);
-#pragma unroll
-        for (int i = 0; i < M::SEGK / 8; ++i) k4[i] = kr[i];
-#pragma unroll
-        for (int u = 0; u < M::TPV; ++u) {
-            const int tt = tg + u * M::NTG;
-            v2[u] = tt < cnt ? rv2[(int64_t)(c0 + tt) * M::NCP + cp] : 0u;
-        }
-    };
-    float mr = -INFINITY, lr = 0.f, o0 = 0.f, o1 = 0.f;
-    if (n_ring > 0) {
-        load_chunk(0, min(M::RC, n_ring));
-        for (int j = tid; j < D; j += kThreads) qs[j] = load_q(a, head * D + j);
-        __syncthreads();  // q visible
-        const float lscale = a.scale * kLog2e;
-        for (int c0 = 0; c0 < n_ring; c0 += M::RC) {
-            const int cnt = min(M::RC, n_ring - c0);
-            if (c0 != 0) load_chunk(c0, cnt);
-            float acc = 0.f;
-#pragma unroll
-            for (int i = 0; i < M::SEGK / 8; ++i) {
-                const float kv[8] = {f16_lo(k4[i].x), f16_hi(k4[i].x), f16_lo(k4[i].y), f16_hi(k4[i].y),
-                                     f16_lo(k4[i].z), f16_hi(k4[i].z), f16_lo(k4[i].w), f16_hi(k4[i].w)};
-                const float4 q0 = *reinterpret_cast<const float4 *>(&qs[kp * M::SEGK + 8 * i]);
-                const float4 q1 = *reinterpret_cast<const float4 *>(&qs[kp * M::SEGK + 8 * i + 4]);
-                acc = fmaf(q0.x, kv[0], acc);
-                acc = fmaf(q0.y, kv[1], acc);
-                acc = fmaf(q0.z, kv[2], acc);
-                acc = fmaf(q0.w, kv[3], acc);
-                acc = fmaf(q1.x, kv[4], acc);
-                acc = fmaf(q1.y, kv[5], acc);
-                acc = fmaf(q1.z, kv[6], acc);
-                acc = fmaf(q1.w, kv[7], acc);
-            }
-#pragma unroll
-            for (int o = 1; o < M::TPT; o <<= 1) acc += __shfl_xor(acc, o);
-            if (kp == 0) sp[tk] = tk < cnt ? acc * lscale : -INFINITY;
-            __syncthreads();
-            // the chunk's maximum, by every wave on its own
-            float cm = sp[lane];
-            if constexpr (M::RC > 64) cm = fmaxf(cm, sp[lane + 64]);
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o));
-            const float mnew = fmaxf(mr, cm);  // finite: the chunk holds a token
-            const float corr = mr == -INFINITY ? 0.f : exp2f(mr - mnew);
-            __syncthreads();  // every wave has read the logits
-            if (tid < M::RC) sp[tid] = exp2f(sp[tid] - mnew);  // masked tokens: 0
-            __syncthreads();
-            mr = mnew;
-            lr *= corr;
-            o0 *= corr;
-            o1 *= corr;
-#pragma unroll
-            for (int u = 0; u < M::TPV; ++u) {
-                const float pt = sp[tg + u * M::NTG];
-                lr += pt;
-                o0 = fmaf(pt, f16_lo(v2[u]), o0);
-                o1 = fmaf(pt, f16_hi(v2[u]), o1);
-            }
-            __syncthreads();  // sp is rewritten by the next chunk
-        }
-        *reinterpret_cast<float2 *>(&ro[tg][2 * cp]) = make_float2(o0, o1);
-        if (cp == 0) rl[tg] = lr;
-    }
-
-    // ---- maximum over the splits and the ring
     float m = mlv.x;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     if (lane == 0) red[wv] = m;
-    __syncthreads();  // also publishes ro and rl
-    float Mx = mr;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, red[w]);
     __syncthreads();
-    const float fw = (mlv.x == -INFINITY) ? 0.f : exp2f(mlv.x - Mx);
-    const float fr = (mr == -INFINITY) ? 0.f : exp2f(mr - Mx);
-    if (tid < n_split) f[tid] = fw;
+    float M = red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red[w]);
+    __syncthreads();
+    const float fw = (mlv.x == -INFINITY) ? 0.f : exp2f(mlv.x - M);
+    if (tid < n_total) f[tid] = fw;
     float l = fw * mlv.y;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
@@ -1108,26 +1227,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     float L = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) L += red[w];
-    if (n_ring > 0) {
-        float lrt = 0.f;
-#pragma unroll
-        for (int c = 0; c < M::NTG; ++c) lrt += rl[c];
-        L = fmaf(fr, lrt, L);
-    }
 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int k = 0; k < M::PF; ++k) {
-        const int sp_ = sg + k * M::NSG;
-        const float w = sp_ < n_split ? f[sp_] : 0.f;
+    for (int k = 0; k < PF; ++k) {
+        const int sp = sg + k * NSG;
+        const float w = sp < n_total ? f[sp] : 0.f;
         acc.x = fmaf(w, pre[k].x, acc.x);
         acc.y = fmaf(w, pre[k].y, acc.y);
         acc.z = fmaf(w, pre[k].z, acc.z);
         acc.w = fmaf(w, pre[k].w, acc.w);
     }
-    for (int sp_ = sg + M::PF * M::NSG; sp_ < n_split; sp_ += M::NSG) {
-        const float4 v = *reinterpret_cast<const float4 *>(po + (int64_t)(sp_ * G + g) * D + 4 * j4);
-        const float w = f[sp_];
+    for (int sp = sg + PF * NSG; sp < n_total; sp += NSG) {
+        const float4 v = *reinterpret_cast<const float4 *>(po + (int64_t)(sp * G + g) * D + 4 * j4);
+        const float w = f[sp];
         acc.x = fmaf(w, v.x, acc.x);
         acc.y = fmaf(w, v.y, acc.y);
         acc.z = fmaf(w, v.z, acc.z);
@@ -1137,28 +1250,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     __syncthreads();
     if (sg == 0) {
 #pragma unroll
-        for (int k = 1; k < M::NSG; ++k) {
+        for (int k = 1; k < NSG; ++k) {
             const float4 v = acc_s[k][j4];
             acc.x += v.x;
             acc.y += v.y;
             acc.z += v.z;
             acc.w += v.w;
         }
-        if (n_ring > 0) {
-#pragma unroll
-            for (int c = 0; c < M::NTG; ++c) {
-                const float4 v = *reinterpret_cast<const float4 *>(&ro[c][4 * j4]);
-                acc.x = fmaf(fr, v.x, acc.x);
-                acc.y = fmaf(fr, v.y, acc.y);
-                acc.z = fmaf(fr, v.z, acc.z);
-                acc.w = fmaf(fr, v.w, acc.w);
-            }
-        }
         const float inv = L > 0.f ? 1.f / L : 0.f;
-        *reinterpret_cast<float4 *>(a.out + head * D + 4 * j4) =
+        *reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.hq + kvh * G + g) * D + 4 * j4) =
             make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
 }
+
 
 // ------------------------------------------------------------------ ring append
 template <typename Tag, int D>
@@ -1186,7 +1290,7 @@ __global__ __launch_bounds__(256) void k_ring_append(const void *kn, const void 
 // ------------------------------------------------------------------ launchers
 template <int D, int VB, int G>
 static void launch_g(const DecodeArgs &a, hipStream_t st) {
-    if (a.n_split > 0) {
+    {
         if constexpr (D == 256)
             hipLaunchKernelGGL((k_decode_prep<D, G>), dim3((unsigned)(a.batch * a.hkv * PrepBand<D>::NB)),
                                dim3(kThreads), 0, st, a);
@@ -1198,8 +1302,7 @@ static void launch_g(const DecodeArgs &a, hipStream_t st) {
             hipLaunchKernelGGL((k_decode_main<D, VB, G, 4>), grid, dim3(64 * 4), 0, st, a);
         }
     }
-    hipLaunchKernelGGL((k_decode_merge<D, G>), dim3((unsigned)((a.batch * a.hkv + 7) / 8 * 8 * G)), dim3(kThreads), 0,
-                       st, a);
+    hipLaunchKernelGGL((k_decode_merge<D, G>), dim3((unsigned)(a.batch * a.hkv * G)), dim3(kThreads), 0, st, a);
 }
 
 template <int D, int VB>

@@ -56,7 +56,8 @@ struct DecodeArgs {
     int buffer_size;
     int n_ring;
     int batch, hq, hkv;
-    int n_split;        // splits over the packed tokens (0 when there are none), <= 256
+    int n_split;        // splits of the packed and the ring tokens (>= 1), <= 256
+    int ring_per_split; // ring tokens per split (<= 64 at d = 128, <= 32 at d = 256)
     int waves;          // waves per workgroup of the packed splits (4 or 12)
     int64_t per_split;  // packed tokens per split
     float scale;
