@@ -7,9 +7,11 @@ One step = one pass of the whole path over one batch of synthetic input:
   4. tq_flush         -- compress the ring contents into the packed store (R2)
 value = context KV-tokens (batch * layers * (packed + ring)) per second of step time.
 
-Per-kernel times come from HIP events on the stream the kernels run on; several copies of
-the inputs and stores are cycled so that the working set exceeds the 256 MB Infinity Cache.
-Prints one JSON line.
+The K timed steps run back to back with no events inside (wall clock between device
+synchronisations); the per-phase times come from a second pass of K steps with HIP events
+between the phases, on the stream the kernels run on.  Several copies of the inputs and
+stores are cycled so that the working set exceeds the 256 MB Infinity Cache.  Prints one JSON
+line.
 """
 from __future__ import annotations
 
@@ -156,13 +158,21 @@ def main():
         step(i % n_copies)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # timed steps: no events inside (an event between kernels leaves the GPU idle for a few
+    # microseconds), bracketed by device synchronisation
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i % n_copies, evs[i])
+        step(i % n_copies)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # per-phase breakdown from a second pass of the same steps, HIP events between the phases
+    # on the stream the kernels run on
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i % n_copies, evs[i])
+    torch.cuda.synchronize()
     q_ms = [e[0].elapsed_time(e[1]) for e in evs]
     a_ms = [e[1].elapsed_time(e[2]) for e in evs]
     d_ms = [e[2].elapsed_time(e[3]) for e in evs]
