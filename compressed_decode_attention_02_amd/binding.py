@@ -17,7 +17,7 @@ TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 EXPORTS = [
     "tq_build_codebook", "tq_build_rotation", "tq_tables_bytes", "tq_build_tables", "tq_tables_view",
     "tq_packed_bytes_per_token", "tq_quantize_kv", "tq_append_ring", "tq_flush",
-    "tq_decode_workspace_bytes", "tq_decode_attention", "tq_status_string",
+    "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_step", "tq_status_string",
 ]
 
 
@@ -73,6 +73,8 @@ def _lib():
         "tq_flush": (ctypes.c_int, [C, T, R, I32, I32, K, I64, P]),
         "tq_decode_workspace_bytes": (SZ, [C, I32, I32, I32, I64]),
         "tq_decode_attention": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, K, I64, R, I32, F, P, P, SZ, P]),
+        "tq_decode_step": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, K, ctypes.POINTER(I64), R,
+                                          ctypes.POINTER(I32), P, P, ctypes.c_int, F, P, P, SZ, P]),
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -224,6 +226,24 @@ def tq_decode_attention(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv
         ctypes.byref(ring) if ring is not None else None, n_ring, ctypes.c_float(softmax_scale), _ptr(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("tq_decode_attention", st)
+
+
+def tq_decode_step(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv_heads: int,
+                   packed: tq_packed | None, n_packed: int, ring: tq_ring, n_ring: int, k_new, v_new,
+                   softmax_scale: float, out, workspace, stream=None):
+    """Append k_new / v_new to the ring (flushing a full ring first) and decode, in one call.
+    Returns the new (n_packed, n_ring)."""
+    if k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must share a dtype")
+    np_ = ctypes.c_int64(n_packed)
+    nr_ = ctypes.c_int32(n_ring)
+    st = _lib().tq_decode_step(
+        ctypes.byref(cfg), ctypes.byref(tables.view), _ptr(q), _dtype_code(q), batch, n_q_heads, n_kv_heads,
+        ctypes.byref(packed) if packed is not None else None, ctypes.byref(np_), ctypes.byref(ring),
+        ctypes.byref(nr_), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), ctypes.c_float(softmax_scale), _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("tq_decode_step", st)
+    return np_.value, nr_.value
 
 
 def new_workspace(cfg, batch: int, n_q_heads: int, n_kv_heads: int, max_context: int, device="cuda"):

@@ -172,11 +172,14 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch,
     return decode_layout(cfg->head_dim, batch, n_q_heads, n_split).total;
 }
 
-extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *tables, const void *q,
-                                         tq_dtype q_dtype, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
-                                         const tq_packed *packed, int64_t n_packed, const tq_ring *ring,
-                                         int32_t n_ring, float softmax_scale, float *out, void *workspace,
-                                         size_t workspace_bytes, void *stream) {
+namespace {
+// decode over n_packed records and n_ring ring tokens; with k_new / v_new, ring slot
+// n_ring - 1 is the new token, taken from them (and written into the ring) by the kernel
+tq_status decode_impl(const tq_config *cfg, const tq_tables *tables, const void *q, tq_dtype q_dtype, int32_t batch,
+                      int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *packed, int64_t n_packed,
+                      const tq_ring *ring, int32_t n_ring, float softmax_scale, float *out, void *workspace,
+                      size_t workspace_bytes, void *stream, const void *k_new, const void *v_new, tq_dtype kv_dtype,
+                      bool check_only = false) {
     if (!cfg) return TQ_ERR_INVALID_ARG;
     tq_status st = tq::check_config(*cfg);
     if (st != TQ_OK) return st;
@@ -211,6 +214,7 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     const DecodeLayout L = decode_layout(cfg->head_dim, batch, n_q_heads, n_split);
     if (workspace_bytes < L.total) return TQ_ERR_WORKSPACE;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
+    if (check_only) return TQ_OK;
     tq::DecodeArgs a{};
     a.q = q;
     a.q_dtype = (int)q_dtype;
@@ -241,7 +245,59 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
     a.scale = softmax_scale;
     a.out = out;
     a.prep = reinterpret_cast<float *>(ws + L.prep);
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.kv_dtype = (int)kv_dtype;
+    a.new_slot = k_new ? n_ring - 1 : -1;
     a.partial = reinterpret_cast<float *>(ws + L.partial);
     a.partial_ml = reinterpret_cast<float *>(ws + L.partial_ml);
     return hip_status(tq::launch_decode(cfg->head_dim, cfg->value_bits, G, a, (hipStream_t)stream));
+}
+}  // namespace
+
+extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *tables, const void *q,
+                                         tq_dtype q_dtype, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                         const tq_packed *packed, int64_t n_packed, const tq_ring *ring,
+                                         int32_t n_ring, float softmax_scale, float *out, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+    return decode_impl(cfg, tables, q, q_dtype, batch, n_q_heads, n_kv_heads, packed, n_packed, ring, n_ring,
+                       softmax_scale, out, workspace, workspace_bytes, stream, nullptr, nullptr, TQ_F32);
+}
+
+extern "C" tq_status tq_decode_step(const tq_config *cfg, const tq_tables *tables, const void *q, tq_dtype q_dtype,
+                                    int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *packed,
+                                    int64_t *n_packed, const tq_ring *ring, int32_t *n_ring, const void *k_new,
+                                    const void *v_new, tq_dtype kv_dtype, float softmax_scale, float *out,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+    if (!cfg || !n_packed || !n_ring) return TQ_ERR_INVALID_ARG;
+    tq_status st = tq::check_config(*cfg);
+    if (st != TQ_OK) return st;
+    if (kv_dtype != TQ_F32 && kv_dtype != TQ_BF16 && kv_dtype != TQ_F16) return TQ_ERR_INVALID_ARG;
+    if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new) || !ring || !ring->k || !ring->v)
+        return TQ_ERR_INVALID_ARG;
+    if (batch <= 0 || n_kv_heads <= 0) return TQ_ERR_INVALID_ARG;
+    int64_t np = *n_packed;
+    int32_t nr = *n_ring;
+    if (np < 0 || nr < 0 || nr > cfg->buffer_size) return TQ_ERR_INVALID_ARG;
+    const int32_t slices = batch * n_kv_heads;
+    const bool flush = nr == cfg->buffer_size;
+    // every argument is checked before anything is launched
+    st = decode_impl(cfg, tables, q, q_dtype, batch, n_q_heads, n_kv_heads, packed, flush ? np + nr : np, ring,
+                     flush ? 1 : nr + 1, softmax_scale, out, workspace, workspace_bytes, stream, k_new, v_new,
+                     kv_dtype, true);
+    if (st != TQ_OK) return st;
+    if (flush) {
+        // a full ring is flushed into the packed store first (tq_flush checks its arguments
+        // before it launches)
+        st = tq_flush(cfg, tables, ring, slices, nr, packed, np, stream);
+        if (st != TQ_OK) return st;
+        np += nr;
+        nr = 0;
+    }
+    st = decode_impl(cfg, tables, q, q_dtype, batch, n_q_heads, n_kv_heads, packed, np, ring, nr + 1, softmax_scale,
+                     out, workspace, workspace_bytes, stream, k_new, v_new, kv_dtype);
+    if (st != TQ_OK) return st;
+    *n_packed = np;
+    *n_ring = nr + 1;
+    return TQ_OK;
 }

@@ -314,6 +314,19 @@ struct RingRegs {
     uint32_t v2[R::TPV];
 };
 
+// 8 elements of the new token (fused append) from element `off` of its input, rounded to
+// fp16 as the ring append rounds them, packed in pairs
+__device__ __forceinline__ uint4 new_token8(const void *src, int dtype, int64_t off) {
+    float f[8];
+    if (dtype == TQ_F32) load8(src, off, f, f32_tag{});
+    else if (dtype == TQ_BF16) load8(src, off, f, bf16_tag{});
+    else load8(src, off, f, f16_tag{});
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = f32_to_f16_bits(f[2 * e]) | ((uint32_t)f32_to_f16_bits(f[2 * e + 1]) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // loads of the split's ring tokens [r0, r0 + n) (addresses clamped into the ring, unused
 // words ignored)
 template <int D, int G, int NW>
@@ -334,6 +347,31 @@ __device__ __forceinline__ void ring_load(const DecodeArgs &a, RingRegs<D, G, NW
     for (int u = 0; u < R::TPV; ++u) {
         const int tt = tg + u * R::NTG;
         rr.v2[u] = tt < n ? rv2[(int64_t)(r0 + tt) * R::NCP + cp] : 0u;
+    }
+    // fused append: the new token replaces what the ring slot held, read from the input and
+    // rounded as the append rounds it, and this workgroup writes it into the ring
+    const int ns = a.new_slot - r0;
+    if (a.new_slot >= 0 && ns >= 0 && ns < n) {
+        const int64_t in0 = (int64_t)bk * D;
+#pragma unroll
+        for (int ps = 0; ps < R::NP; ++ps)
+            if (ps * R::TCH + tid / R::TPT == ns)
+#pragma unroll
+                for (int i = 0; i < R::SEG / 8; ++i) rr.k4[ps][i] = new_token8(a.k_new, a.kv_dtype, in0 + part * R::SEG + 8 * i);
+#pragma unroll
+        for (int u = 0; u < R::TPV; ++u)
+            if (tg + u * R::NTG == ns) {
+                const uint4 w = new_token8(a.v_new, a.kv_dtype, in0 + (2 * cp & ~7));
+                const uint32_t sel = (cp & 3);
+                rr.v2[u] = sel == 0 ? w.x : (sel == 1 ? w.y : (sel == 2 ? w.z : w.w));
+            }
+        uint16_t *rkw = const_cast<uint16_t *>(a.rk) + ((int64_t)bk * a.buffer_size + a.new_slot) * D;
+        uint16_t *rvw = const_cast<uint16_t *>(a.rv) + ((int64_t)bk * a.buffer_size + a.new_slot) * D;
+        for (int c = tid; c < 2 * (D / 8); c += R::NT) {
+            const bool key = c < D / 8;
+            const int c8 = 8 * (key ? c : c - D / 8);
+            *reinterpret_cast<uint4 *>((key ? rkw : rvw) + c8) = new_token8(key ? a.k_new : a.v_new, a.kv_dtype, in0 + c8);
+        }
     }
 }
 

@@ -63,6 +63,12 @@ struct DecodeArgs {
     float scale;
     float *out;
     float *prep;         // d = 256: [batch*hkv][2][G][D], q' then w of the slice's query heads
+    // fused append (tq_decode_step): the new token of every slice, [batch*hkv][D] in kv_dtype,
+    // goes to ring slot new_slot (< n_ring) by the split that attends to that slot; -1: none
+    const void *k_new;
+    const void *v_new;
+    int kv_dtype;
+    int new_slot;
     float *partial;      // [batch*hkv][n_split][G][D]: o of each split
     float *partial_ml;   // [batch*hkv][n_split][G][2]: (m, l) of each split
 };

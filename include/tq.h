@@ -162,6 +162,22 @@ tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *tables, con
                               float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
                               void *stream);
 
+/* One decode step (guide 5.1 items 1 and 2 in one call, with the forum's flush of a full
+ * recent window): the new token k_new / v_new ([batch * n_kv_heads][d] in kv_dtype) of every
+ * slice enters the ring and the hybrid attention runs over packed + ring, as
+ * tq_append_ring followed by tq_decode_attention would, without the append's launch: the
+ * decode kernel takes the new token from k_new / v_new (rounded to fp16 as the append rounds
+ * it) and writes it into ring slot *n_ring.  When the ring is full (*n_ring == buffer_size)
+ * it is first flushed into records *n_packed .. *n_packed + buffer_size - 1, as tq_flush.
+ * *n_packed and *n_ring (host memory) are updated in place only on success; every argument
+ * is checked before anything is launched.  Other arguments as tq_decode_attention; the
+ * workspace must cover *n_packed + *n_ring + 1 tokens. */
+tq_status tq_decode_step(const tq_config *cfg, const tq_tables *tables, const void *q, tq_dtype q_dtype,
+                         int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *packed,
+                         int64_t *n_packed, const tq_ring *ring, int32_t *n_ring, const void *k_new,
+                         const void *v_new, tq_dtype kv_dtype, float softmax_scale, float *out, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 const char *tq_status_string(tq_status s);
 
 #ifdef __cplusplus

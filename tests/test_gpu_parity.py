@@ -11,7 +11,7 @@ import compressed_decode_attention_02_amd as tq
 pytestmark = pytest.mark.gpu
 
 from gpu_common import (Env, assert_decode_close, check_quantize, dev_to_stored, log, oracle_decode,  # noqa: E402
-                        packed_to_np, quantize_gpu, run_decode, to_dev)
+                        packed_to_np, quantize_gpu, run_decode, to_dev, torch_mod)
 
 
 @pytest.fixture(scope="module")
@@ -232,6 +232,85 @@ def test_decode_slices_not_a_multiple_of_eight(torch):
     # leave part of the last group of 8 empty
     _decode_case(W.custom(2, batch=3, hq=8, hkv=2, n_packed=900, n_ring=17), "6 slices G=4")
     _decode_case(W.custom(4, batch=3, hq=2, hkv=1, n_packed=700, n_ring=128), "3 slices d256 G=2")
+
+
+def _step_case(w: W.Workload, fill: int, label: str):
+    """Two identical stores and rings, `fill` ring tokens; returns the fused step's and the
+    two-call path's outputs, rings and stores."""
+    env = Env(w.d, w.value_bits, buffer_size=w.buffer_size)
+    n_sl = w.batch * w.hkv
+    (k, v), _ = W.host_kv(w, 0, w.n_packed + fill + 1)
+    k = k.reshape(n_sl, -1, w.d)
+    v = v.reshape(n_sl, -1, w.d)
+    cap = w.n_packed + w.buffer_size
+    stores, rings = [], []
+    for _ in range(2):
+        st = tq.PackedStore(env.cfg, n_sl, cap)
+        if w.n_packed:
+            quantize_gpu(env, to_dev(np.ascontiguousarray(k[:, :w.n_packed]), w.in_dtype),
+                         to_dev(np.ascontiguousarray(v[:, :w.n_packed]), w.in_dtype), n_sl, w.n_packed, store=st)
+        rg = tq.Ring(env.cfg, n_sl)
+        for t_ in range(fill):
+            tq.tq_append_ring(env.cfg, rg.struct(), to_dev(np.ascontiguousarray(k[:, w.n_packed + t_]), w.in_dtype),
+                              to_dev(np.ascontiguousarray(v[:, w.n_packed + t_]), w.in_dtype), n_sl, t_)
+        stores.append(st)
+        rings.append(rg)
+    kn = to_dev(np.ascontiguousarray(k[:, w.n_packed + fill]), w.in_dtype)
+    vn = to_dev(np.ascontiguousarray(v[:, w.n_packed + fill]), w.in_dtype)
+    q, _ = W.host_queries(w, 0)
+    qd = to_dev(q, w.in_dtype)
+    scale = 1.0 / math.sqrt(w.d)
+    outs = [torch_mod().zeros((w.batch, w.hq, w.d), dtype=torch_mod().float32, device="cuda") for _ in range(2)]
+    ws = tq.new_workspace(env.cfg, w.batch, w.hq, w.hkv, cap + 1)
+    # two calls: (flush a full ring,) append, decode
+    n_packed, n_ring = w.n_packed, fill
+    if n_ring == w.buffer_size:
+        tq.tq_flush(env.cfg, env.tables, rings[0].struct(), n_sl, n_ring, stores[0].struct(), n_packed)
+        n_packed, n_ring = n_packed + n_ring, 0
+    tq.tq_append_ring(env.cfg, rings[0].struct(), kn, vn, n_sl, n_ring)
+    tq.tq_decode_attention(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, stores[0].struct(), n_packed,
+                           rings[0].struct(), n_ring + 1, scale, outs[0], ws)
+    # the fused step
+    got = tq.tq_decode_step(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, stores[1].struct(), w.n_packed,
+                            rings[1].struct(), fill, kn, vn, scale, outs[1], ws)
+    torch_mod().cuda.synchronize()
+    assert got == (n_packed, n_ring + 1), (label, got)
+    return env, q, qd, stores, rings, [o.cpu().numpy() for o in outs], got
+
+
+def test_decode_step_matches_append_then_decode(torch):
+    """The new token taken from the input inside the decode kernel gives the results of
+    tq_append_ring + tq_decode_attention bit for bit, and the same ring."""
+    for w, fill, label in ((W.custom(2, n_packed=1000, n_ring=40), 40, "d128 v2"),
+                           (W.custom(3, batch=2, n_packed=500, n_ring=63), 63, "d128 v4 split edge"),
+                           (W.custom(4, batch=1, n_packed=700, n_ring=20), 20, "d256"),
+                           (W.custom(2, n_packed=0, n_ring=5), 5, "ring only"),
+                           (W.custom(1, n_packed=512, n_ring=0), 0, "tiny fp32 empty ring")):
+        env, q, qd, stores, rings, outs, (n_packed, n_ring) = _step_case(w, fill, label)
+        np.testing.assert_array_equal(outs[1], outs[0], err_msg=label)
+        for a_, b_ in ((rings[0].k, rings[1].k), (rings[0].v, rings[1].v)):
+            np.testing.assert_array_equal(b_.cpu().numpy().view(np.uint16), a_.cpu().numpy().view(np.uint16),
+                                          err_msg=label)
+        ref = oracle_decode(env, dev_to_stored(qd).astype(np.float64), w.hq, w.hkv, stores[1], n_packed, rings[1],
+                            n_ring, b_list=list(range(w.batch)))
+        assert_decode_close(outs[1].astype(np.float64), ref, f"step {label}")
+
+
+def test_decode_step_flushes_a_full_ring(torch):
+    """A full ring is flushed into the packed store first: the same records, ring and
+    output as tq_flush + tq_append_ring + tq_decode_attention."""
+    w = W.custom(3, batch=2, n_packed=300, n_ring=64, buffer_size=64)
+    env, q, qd, stores, rings, outs, (n_packed, n_ring) = _step_case(w, 64, "full ring")
+    assert (n_packed, n_ring) == (364, 1)
+    np.testing.assert_array_equal(outs[1], outs[0])
+    P0, P1 = packed_to_np(stores[0]), packed_to_np(stores[1])
+    for key in P0:
+        np.testing.assert_array_equal(P1[key], P0[key], err_msg=key)
+    np.testing.assert_array_equal(rings[1].k[:, :1].cpu().numpy().view(np.uint16),
+                                  rings[0].k[:, :1].cpu().numpy().view(np.uint16))
+    ref = oracle_decode(env, dev_to_stored(qd).astype(np.float64), w.hq, w.hkv, stores[1], n_packed, rings[1],
+                        n_ring, b_list=[0, 1])
+    assert_decode_close(outs[1].astype(np.float64), ref, "step after flush")
 
 
 def test_decode_empty_context_gives_zeros(torch):

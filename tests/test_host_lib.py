@@ -155,3 +155,31 @@ def test_decode_errors():
     # a shorter context needs no more workspace than the maximum it was sized for
     for ctx in (0, 1, 255, 256, 1000, 4095):
         assert L.tq_decode_workspace_bytes(ctypes.byref(cfg), 2, 8, 2, ctx) <= need
+
+
+def test_decode_step_errors_leave_the_counts():
+    """tq_decode_step checks everything before it launches: each error returns with the
+    caller's fill counts untouched (no GPU needed: every case here fails a check, so nothing
+    is launched)."""
+    cfg = tq.make_config(buffer_size=128)
+    L = tq.lib()
+    T, P, R = _fake_tables(), _fake_packed(cap=4096), B.tq_ring(FAKE, FAKE)
+    need = L.tq_decode_workspace_bytes(ctypes.byref(cfg), 2, 8, 2, 4096)
+
+    def step(n_packed, n_ring, ws=need, kv_dtype=B.TQ_BF16, k_new=FAKE, counts=True):
+        np_, nr_ = ctypes.c_int64(n_packed), ctypes.c_int32(n_ring)
+        st = L.tq_decode_step(ctypes.byref(cfg), ctypes.byref(T), FAKE, B.TQ_BF16, 2, 8, 2, ctypes.byref(P),
+                              ctypes.byref(np_) if counts else None, ctypes.byref(R),
+                              ctypes.byref(nr_) if counts else None, k_new, FAKE, kv_dtype, ctypes.c_float(0.1),
+                              FAKE, FAKE, ws, None)
+        return st, np_.value, nr_.value
+    assert step(100, 5, counts=False)[0] == B.TQ_ERR_INVALID_ARG
+    assert step(100, 5, ws=16) == (B.TQ_ERR_WORKSPACE, 100, 5)
+    assert step(100, 129) == (B.TQ_ERR_INVALID_ARG, 100, 129)
+    assert step(100, 5, kv_dtype=7) == (B.TQ_ERR_INVALID_ARG, 100, 5)
+    assert step(100, 5, k_new=FAKE + 2) == (B.TQ_ERR_INVALID_ARG, 100, 5)
+    assert step(4097, 5) == (B.TQ_ERR_INVALID_ARG, 4097, 5)     # more records than the store holds
+    # a full ring would be flushed to records 4000..4127 of a 4096-record store: refused
+    # before the flush is launched
+    assert step(4000, 128) == (B.TQ_ERR_INVALID_ARG, 4000, 128)
+
