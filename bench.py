@@ -2,9 +2,10 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
   1. tq_quantize_kv   -- compress the prefill history (Q1-Q6) of every (layer, batch, kv head)
-  2. tq_append_ring   -- one decode-time token per slice into the exact ring (R1)
-  3. tq_decode_attention -- hybrid attention over packed history + ring, every layer (D1-D5)
-  4. tq_flush         -- compress the ring contents into the packed store (R2)
+  2. tq_decode_step   -- per layer: one decode-time token per slice into the exact ring (R1,
+                         inside the decode kernel) and hybrid attention over packed history +
+                         ring (D1-D5)
+  3. tq_flush         -- compress the ring contents into the packed store (R2)
 value = context KV-tokens (batch * layers * (packed + ring)) per second of step time.
 
 The K timed steps run back to back with no events inside (wall clock between device
@@ -142,17 +143,21 @@ def main():
         if ev: ev[0].record(stream)
         tq.tq_quantize_kv(cfg, tables, cp["K"], cp["V"], n_sl, Tp, st.struct(), 0)
         if ev: ev[1].record(stream)
-        if w.n_ring > 0:
-            tq.tq_append_ring(cfg, rg.struct(), cp["kn"], cp["vn"], n_sl, ring_fill)
-        if ev: ev[2].record(stream)
         for layer in range(L):
             off = layer * n_sl_layer
-            tq.tq_decode_attention(cfg, tables, cp["qs"][layer], B, hq, hkv, st.struct(off), Tp,
-                                   rg.struct(off), w.n_ring, scale, cp["outs"][layer], cp["ws"])
-        if ev: ev[3].record(stream)
+            if w.n_ring > 0:
+                # the decode step: the layer's new token into ring slot ring_fill (inside the
+                # decode kernel), then attention over packed + ring
+                lo, hi = off, off + n_sl_layer
+                tq.tq_decode_step(cfg, tables, cp["qs"][layer], B, hq, hkv, st.struct(off), Tp, rg.struct(off),
+                                  ring_fill, cp["kn"][lo:hi], cp["vn"][lo:hi], scale, cp["outs"][layer], cp["ws"])
+            else:
+                tq.tq_decode_attention(cfg, tables, cp["qs"][layer], B, hq, hkv, st.struct(off), Tp,
+                                       None, 0, scale, cp["outs"][layer], cp["ws"])
+        if ev: ev[2].record(stream)
         if w.n_ring > 0:
             tq.tq_flush(cfg, tables, rg.struct(), n_sl, w.n_ring, st.struct(), Tp)
-        if ev: ev[4].record(stream)
+        if ev: ev[3].record(stream)
 
     for i in range(args.warmup):
         step(i % n_copies)
@@ -168,21 +173,23 @@ def main():
     wall = time.perf_counter() - t0
     # per-phase breakdown from a second pass of the same steps, HIP events between the phases
     # on the stream the kernels run on
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i % n_copies, evs[i])
     torch.cuda.synchronize()
     q_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    a_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    d_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    f_ms = [e[3].elapsed_time(e[4]) for e in evs]
+    d_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    f_ms = [e[2].elapsed_time(e[3]) for e in evs]
     ms_step = wall * 1e3 / args.steps
 
     ctx = Tp + w.n_ring
     kv_tokens = B * L * ctx
     q_bytes = n_sl * Tp * (2 * d * in_bytes + rec)
-    dec_bytes = L * (n_sl_layer * (Tp * rec + w.n_ring * 4 * d) + B * hq * d * (in_bytes + 4))
+    # per layer: packed records, ring tokens (fp16 K and V; the step's new token is read from its
+    # input instead and written to the ring once), queries in, outputs out
+    dec_bytes = L * (n_sl_layer * (Tp * rec + w.n_ring * 4 * d + (2 * d * in_bytes if w.n_ring else 0))
+                     + B * hq * d * (in_bytes + 4))
     q_med, d_med = statistics.median(q_ms), statistics.median(d_ms)
     q_gbps = q_bytes / (q_med * 1e-3) / 1e9
     d_gbps = dec_bytes / (d_med * 1e-3) / 1e9
@@ -219,8 +226,8 @@ def main():
                    "packed_tokens": Tp, "ring_tokens": w.n_ring, "key_bits": 3, "qjl_bits": 1,
                    "value_bits": w.value_bits, "group": 32, "parallelism": "none (1 GPU)",
                    "copies_cycled": n_copies},
-        "breakdown_ms_median": {"quantize": round(q_med, 4), "append": round(statistics.median(a_ms), 4),
-                                "decode_all_layers": round(d_med, 4), "flush": round(statistics.median(f_ms), 4)},
+        "breakdown_ms_median": {"quantize": round(q_med, 4), "append_and_decode_all_layers": round(d_med, 4),
+                                "flush": round(statistics.median(f_ms), 4)},
         "quantize_tokens_per_s": round(B * L * Tp / (q_med * 1e-3), 1),
         "quantize_algorithmic_bytes": q_bytes,
         "decode_algorithmic_bytes_per_layer": dec_bytes // L,
