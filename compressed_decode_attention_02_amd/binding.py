@@ -17,7 +17,8 @@ TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 EXPORTS = [
     "tq_build_codebook", "tq_build_rotation", "tq_tables_bytes", "tq_build_tables", "tq_tables_view",
     "tq_packed_bytes_per_token", "tq_quantize_kv", "tq_append_ring", "tq_flush",
-    "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_step", "tq_status_string",
+    "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_attention_ragged", "tq_decode_step",
+    "tq_status_string",
 ]
 
 
@@ -73,6 +74,8 @@ def _lib():
         "tq_flush": (ctypes.c_int, [C, T, R, I32, I32, K, I64, P]),
         "tq_decode_workspace_bytes": (SZ, [C, I32, I32, I32, I64]),
         "tq_decode_attention": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, K, I64, R, I32, F, P, P, SZ, P]),
+        "tq_decode_attention_ragged": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, K, P, I64, R, P, I32, F,
+                                                      P, P, SZ, P]),
         "tq_decode_step": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, K, ctypes.POINTER(I64), R,
                                           ctypes.POINTER(I32), P, P, ctypes.c_int, F, P, P, SZ, P]),
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -226,6 +229,22 @@ def tq_decode_attention(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv
         ctypes.byref(ring) if ring is not None else None, n_ring, ctypes.c_float(softmax_scale), _ptr(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("tq_decode_attention", st)
+
+
+def tq_decode_attention_ragged(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv_heads: int,
+                               packed: tq_packed | None, seq_packed, n_packed_max: int, ring: tq_ring | None,
+                               seq_ring, n_ring_max: int, softmax_scale: float, out, workspace, stream=None):
+    """Decode with per-sequence lengths: seq_packed (int64) and seq_ring (int32) are device
+    tensors of `batch` entries."""
+    import torch
+    if seq_packed.dtype != torch.int64 or seq_ring.dtype != torch.int32:
+        raise ValueError("seq_packed must be int64 and seq_ring int32")
+    st = _lib().tq_decode_attention_ragged(
+        ctypes.byref(cfg), ctypes.byref(tables.view), _ptr(q), _dtype_code(q), batch, n_q_heads, n_kv_heads,
+        ctypes.byref(packed) if packed is not None else None, _ptr(seq_packed), n_packed_max,
+        ctypes.byref(ring) if ring is not None else None, _ptr(seq_ring), n_ring_max, ctypes.c_float(softmax_scale),
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("tq_decode_attention_ragged", st)
 
 
 def tq_decode_step(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv_heads: int,

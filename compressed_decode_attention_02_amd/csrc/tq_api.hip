@@ -179,7 +179,8 @@ tq_status decode_impl(const tq_config *cfg, const tq_tables *tables, const void 
                       int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *packed, int64_t n_packed,
                       const tq_ring *ring, int32_t n_ring, float softmax_scale, float *out, void *workspace,
                       size_t workspace_bytes, void *stream, const void *k_new, const void *v_new, tq_dtype kv_dtype,
-                      bool check_only = false) {
+                      bool check_only = false, const int64_t *seq_packed = nullptr,
+                      const int32_t *seq_ring = nullptr) {
     if (!cfg) return TQ_ERR_INVALID_ARG;
     tq_status st = tq::check_config(*cfg);
     if (st != TQ_OK) return st;
@@ -245,6 +246,8 @@ tq_status decode_impl(const tq_config *cfg, const tq_tables *tables, const void 
     a.scale = softmax_scale;
     a.out = out;
     a.prep = reinterpret_cast<float *>(ws + L.prep);
+    a.seq_packed = seq_packed;
+    a.seq_ring = seq_ring;
     a.k_new = k_new;
     a.v_new = v_new;
     a.kv_dtype = (int)kv_dtype;
@@ -262,6 +265,19 @@ extern "C" tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *
                                          size_t workspace_bytes, void *stream) {
     return decode_impl(cfg, tables, q, q_dtype, batch, n_q_heads, n_kv_heads, packed, n_packed, ring, n_ring,
                        softmax_scale, out, workspace, workspace_bytes, stream, nullptr, nullptr, TQ_F32);
+}
+
+extern "C" tq_status tq_decode_attention_ragged(const tq_config *cfg, const tq_tables *tables, const void *q,
+                                                tq_dtype q_dtype, int32_t batch, int32_t n_q_heads,
+                                                int32_t n_kv_heads, const tq_packed *packed,
+                                                const int64_t *seq_packed, int64_t n_packed_max, const tq_ring *ring,
+                                                const int32_t *seq_ring, int32_t n_ring_max, float softmax_scale,
+                                                float *out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!seq_packed || !seq_ring || !aligned8(seq_packed) || (reinterpret_cast<uintptr_t>(seq_ring) & 3u))
+        return TQ_ERR_INVALID_ARG;
+    return decode_impl(cfg, tables, q, q_dtype, batch, n_q_heads, n_kv_heads, packed, n_packed_max, ring, n_ring_max,
+                       softmax_scale, out, workspace, workspace_bytes, stream, nullptr, nullptr, TQ_F32, false,
+                       seq_packed, seq_ring);
 }
 
 extern "C" tq_status tq_decode_step(const tq_config *cfg, const tq_tables *tables, const void *q, tq_dtype q_dtype,

@@ -484,8 +484,8 @@ __device__ void ring_attend(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, f
 
 // ------------------------------------------------------------------ packed split (one wave)
 template <int D, int VB, int G, int NW>
-__device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, int bk, int b, int kvh, int t_begin,
-                            int t_end, int r0, int nr, float (&orr)[RingShape<D, G, NW>::NE]) {
+__device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, int bk, int b, int kvh, int n_packed,
+                            int t_begin, int t_end, int r0, int nr, float (&orr)[RingShape<D, G, NW>::NE]) {
     using S = DecodeShape<D, VB, G>;
     constexpr float kQjl = 1.2533141373155003f / D;  // sqrt(pi/2) / d
     const int lane = threadIdx.x & 63;
@@ -526,7 +526,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     const float *kn_s = a.kn + rec0 * 2;
     const uint32_t *vw_s = a.vw + rec0 * S::VW;
     const uint16_t *vs_s = a.vs + rec0 * S::NG;
-    const int last = (int)a.n_packed - 1;
+    const int last = n_packed - 1;
     const uint32_t lds_wave = (uint32_t)(uintptr_t)&sm.stage[0][wave][0];
     // ---- staging: block at token t0 into buffer bi (token indices clamped to the last
     //      packed token, so every copy reads records of this slice)
@@ -1175,11 +1175,15 @@ void k_decode_main(DecodeArgs a) {
 
     {
         using R = RingShape<D, G, NW>;
+        // this sequence's lengths: the call's, or (ragged batches) its own, clamped to them
+        int n_packed = (int)a.n_packed, n_ring = a.n_ring;
+        if (a.seq_packed) n_packed = (int)min(max(a.seq_packed[b], (int64_t)0), a.n_packed);
+        if (a.seq_ring) n_ring = min(max(a.seq_ring[b], 0), a.n_ring);
         const int t_begin = split * (int)a.per_split;
-        const int t_end = max(t_begin, (int)min(a.n_packed, (int64_t)t_begin + a.per_split));
-        const int r0 = split * a.ring_per_split, nr = max(0, min(a.n_ring - r0, a.ring_per_split));
+        const int t_end = max(t_begin, min(n_packed, t_begin + (int)a.per_split));
+        const int r0 = split * a.ring_per_split, nr = max(0, min(n_ring - r0, a.ring_per_split));
         float orr[R::NE];
-        packed_wave<D, VB, G, NW>(a, sm, bk, b, kvh, t_begin, t_end, r0, nr, orr);
+        packed_wave<D, VB, G, NW>(a, sm, bk, b, kvh, n_packed, t_begin, t_end, r0, nr, orr);
         __syncthreads();
         // combine the waves and the split's ring tokens
 #pragma unroll

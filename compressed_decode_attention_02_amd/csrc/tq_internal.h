@@ -63,6 +63,10 @@ struct DecodeArgs {
     float scale;
     float *out;
     float *prep;         // d = 256: [batch*hkv][2][G][D], q' then w of the slice's query heads
+    // ragged batches: per-sequence lengths [batch] on the device (n_packed / n_ring are then
+    // their maxima, each length clamped to [0, maximum]); null: every sequence n_packed / n_ring
+    const int64_t *seq_packed;
+    const int32_t *seq_ring;
     // fused append (tq_decode_step): the new token of every slice, [batch*hkv][D] in kv_dtype,
     // goes to ring slot new_slot (< n_ring) by the split that attends to that slot; -1: none
     const void *k_new;

@@ -162,6 +162,19 @@ tq_status tq_decode_attention(const tq_config *cfg, const tq_tables *tables, con
                               float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
                               void *stream);
 
+/* Hybrid decode attention over a ragged batch (sequences of unequal length; a serving batch
+ * holds requests at different positions): as tq_decode_attention, but batch element b
+ * attends to its own seq_packed[b] records and seq_ring[b] ring tokens.  seq_packed (int64,
+ * 8-byte aligned) and seq_ring (int32, 4-byte aligned) are device arrays of `batch` entries,
+ * read by the kernel; n_packed_max / n_ring_max bound them (each length is clamped to
+ * [0, its maximum] on the device) and size the work split; the workspace must cover
+ * n_packed_max + n_ring_max tokens.  A sequence with no tokens gets zeros. */
+tq_status tq_decode_attention_ragged(const tq_config *cfg, const tq_tables *tables, const void *q, tq_dtype q_dtype,
+                                     int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *packed,
+                                     const int64_t *seq_packed, int64_t n_packed_max, const tq_ring *ring,
+                                     const int32_t *seq_ring, int32_t n_ring_max, float softmax_scale, float *out,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
 /* One decode step (guide 5.1 items 1 and 2 in one call, with the forum's flush of a full
  * recent window): the new token k_new / v_new ([batch * n_kv_heads][d] in kv_dtype) of every
  * slice enters the ring and the hybrid attention runs over packed + ring, as

@@ -313,6 +313,51 @@ def test_decode_step_flushes_a_full_ring(torch):
     assert_decode_close(outs[1].astype(np.float64), ref, "step after flush")
 
 
+def test_decode_ragged_batch(torch):
+    """Per-sequence lengths: every batch element against the oracle at its own lengths
+    (including an empty sequence, a ring-only one and one longer than a split); lengths past
+    the maxima are clamped."""
+    for w, lens in ((W.custom(3, batch=6, n_packed=3000, n_ring=64),
+                     [(0, 0), (1, 5), (700, 64), (3000, 17), (1500, 0), (0, 33)]),
+                    (W.custom(4, batch=3, n_packed=900, n_ring=128), [(900, 128), (37, 2), (450, 90)])):
+        env = Env(w.d, w.value_bits, buffer_size=w.buffer_size)
+        n_sl = w.batch * w.hkv
+        (k, v), _ = W.host_kv(w, 0, w.n_packed + w.n_ring)
+        k = k.reshape(n_sl, -1, w.d)
+        v = v.reshape(n_sl, -1, w.d)
+        store = quantize_gpu(env, to_dev(np.ascontiguousarray(k[:, :w.n_packed]), w.in_dtype),
+                             to_dev(np.ascontiguousarray(v[:, :w.n_packed]), w.in_dtype), n_sl, w.n_packed)
+        ring = tq.Ring(env.cfg, n_sl)
+        for t_ in range(w.n_ring):
+            tq.tq_append_ring(env.cfg, ring.struct(), to_dev(np.ascontiguousarray(k[:, w.n_packed + t_]), w.in_dtype),
+                              to_dev(np.ascontiguousarray(v[:, w.n_packed + t_]), w.in_dtype), n_sl, t_)
+        q, _ = W.host_queries(w, 0)
+        qd = to_dev(q, w.in_dtype)
+        sp = torch.tensor([a for a, _ in lens], dtype=torch.int64, device="cuda")
+        sr = torch.tensor([r for _, r in lens], dtype=torch.int32, device="cuda")
+        out = torch.zeros((w.batch, w.hq, w.d), dtype=torch.float32, device="cuda")
+        ws = tq.new_workspace(env.cfg, w.batch, w.hq, w.hkv, w.n_packed + w.n_ring)
+        tq.tq_decode_attention_ragged(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, store.struct(), sp, w.n_packed,
+                                      ring.struct(), sr, w.n_ring, 1.0 / math.sqrt(w.d), out, ws)
+        torch.cuda.synchronize()
+        g = out.cpu().numpy().astype(np.float64)
+        q_stored = dev_to_stored(qd).astype(np.float64)
+        for b, (n_p, n_r) in enumerate(lens):
+            if n_p + n_r == 0:
+                assert not g[b].any(), f"sequence {b} has no tokens"
+                continue
+            ref = oracle_decode(env, q_stored[b:b + 1], w.hq, w.hkv, store, n_p, ring, n_r, slice_offset=b * w.hkv,
+                                b_list=[0])
+            assert_decode_close(g[b:b + 1], ref, f"ragged d{w.d} b{b} ({n_p} + {n_r})")
+        # every sequence at the maxima (and lengths beyond them, clamped) = the uniform decode
+        sp.fill_(w.n_packed + 1000)
+        sr.fill_(w.n_ring)
+        tq.tq_decode_attention_ragged(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, store.struct(), sp, w.n_packed,
+                                      ring.struct(), sr, w.n_ring, 1.0 / math.sqrt(w.d), out, ws)
+        g2, _, _ = run_decode(env, q, w.in_dtype, w.batch, w.hq, w.hkv, store, w.n_packed, ring, w.n_ring, qd=qd)
+        np.testing.assert_array_equal(out.cpu().numpy(), g2.astype(np.float32))
+
+
 def test_decode_empty_context_gives_zeros(torch):
     env = Env(128, 2)
     q = np.ones((1, 4, 128), np.float32)

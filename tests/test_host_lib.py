@@ -183,3 +183,22 @@ def test_decode_step_errors_leave_the_counts():
     # before the flush is launched
     assert step(4000, 128) == (B.TQ_ERR_INVALID_ARG, 4000, 128)
 
+
+def test_decode_ragged_errors():
+    cfg = tq.make_config()
+    L = tq.lib()
+    T, P, R = _fake_tables(), _fake_packed(cap=4096), B.tq_ring(FAKE, FAKE)
+    need = L.tq_decode_workspace_bytes(ctypes.byref(cfg), 2, 8, 2, 4096)
+
+    def rag(sp=FAKE, sr=FAKE, n_packed_max=4096, n_ring_max=5, ws=need):
+        return L.tq_decode_attention_ragged(ctypes.byref(cfg), ctypes.byref(T), FAKE, B.TQ_BF16, 2, 8, 2,
+                                            ctypes.byref(P), sp, n_packed_max, ctypes.byref(R), sr, n_ring_max,
+                                            ctypes.c_float(0.1), FAKE, FAKE, ws, None)
+    assert rag(sp=None) == B.TQ_ERR_INVALID_ARG
+    assert rag(sr=None) == B.TQ_ERR_INVALID_ARG
+    assert rag(sp=FAKE + 4) == B.TQ_ERR_INVALID_ARG       # int64 lengths: 8-byte aligned
+    assert rag(sr=FAKE + 2) == B.TQ_ERR_INVALID_ARG       # int32 lengths: 4-byte aligned
+    assert rag(n_packed_max=4097) == B.TQ_ERR_INVALID_ARG
+    assert rag(n_ring_max=129) == B.TQ_ERR_INVALID_ARG
+    assert rag(ws=16) == B.TQ_ERR_WORKSPACE
+
