@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=2, help="workload id (1..5); 2 = Llama-3.1-8B b1 32K")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--ragged", action="store_true",
+                   help="time only the decode, over a ragged batch: sequence b attends to its own seeded "
+                        "lengths (packed uniform in [1, packed tokens], ring uniform in [0, ring tokens])")
     p.add_argument("--cpu-sample-tokens", type=int, default=32768)
     p.add_argument("--probe-copy-mib", type=int, default=0,
                    help="only time a plain device-to-device copy of this many MiB (achievable HBM "
@@ -163,6 +166,10 @@ def main():
         step(i % n_copies)
     torch.cuda.synchronize()
 
+    if args.ragged:
+        ragged(args, w, cfg, tables, copies, n_copies, scale, rec, in_bytes)
+        return
+
     # timed steps: no events inside (an event between kernels leaves the GPU idle for a few
     # microseconds), bracketed by device synchronisation
     torch.cuda.synchronize()
@@ -244,6 +251,66 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
     print(json.dumps(res), flush=True)
+
+
+def ragged(args, w, cfg, tables, copies, n_copies, scale, rec, in_bytes):
+    """Decode-only timing over a ragged batch (per-sequence lengths on the device), against the
+    uniform decode of the same stores at the maxima, HIP events around K back-to-back calls."""
+    import numpy as np
+    import torch
+    import compressed_decode_attention_02_amd as tq
+    d, L, B, hq, hkv, Tp = w.d, w.layers, w.batch, w.hq, w.hkv, w.n_packed
+    r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.cid, 0, 9])))
+    lp = r.integers(1, Tp + 1, size=B)
+    lr = r.integers(0, w.n_ring + 1, size=B)
+    sp = torch.tensor(lp, dtype=torch.int64, device="cuda")
+    sr = torch.tensor(lr, dtype=torch.int32, device="cuda")
+    n_sl_layer = B * hkv
+
+    def run(rag: bool):
+        for i in range(args.warmup):
+            call(i % n_copies, rag)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            call(i % n_copies, rag)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    def call(c, rag):
+        cp = copies[c]
+        for layer in range(L):
+            off = layer * n_sl_layer
+            if rag:
+                tq.tq_decode_attention_ragged(cfg, tables, cp["qs"][layer], B, hq, hkv, cp["store"].struct(off), sp,
+                                              Tp, cp["ring"].struct(off), sr, w.n_ring, scale, cp["outs"][layer],
+                                              cp["ws"])
+            else:
+                tq.tq_decode_attention(cfg, tables, cp["qs"][layer], B, hq, hkv, cp["store"].struct(off), Tp,
+                                       cp["ring"].struct(off), w.n_ring, scale, cp["outs"][layer], cp["ws"])
+
+    ms_r = run(True)
+    ms_u = run(False)
+    kv_r = int(L * (lp.sum() + lr.sum()))
+    bytes_r = L * (hkv * int((lp * rec + lr * 4 * d).sum()) + B * hq * d * (in_bytes + 4))
+    print(json.dumps({
+        "metric": "ragged-batch decode attention KV-tokens/s + HBM GB/s",
+        "value": round(kv_r / (ms_r * 1e-3), 1), "unit": "KV-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_r, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.in_dtype, "data": "synthetic (seeded device draws of the workload's laws)",
+        "config": {"workload": w.name + "_ragged", "layers": L, "batch": B, "q_heads": hq, "kv_heads": hkv,
+                   "head_dim": d, "packed_tokens_max": Tp, "ring_tokens_max": w.n_ring,
+                   "packed_lengths": "uniform [1, %d], seeded" % Tp, "ring_lengths": "uniform [0, %d], seeded" % w.n_ring,
+                   "mean_packed": round(float(lp.mean()), 1), "mean_ring": round(float(lr.mean()), 1)},
+        "decode_GBps": round(bytes_r / (ms_r * 1e-3) / 1e9, 1),
+        "roofline_decode": {"kernel": ("k_decode_prep+" if d == 256 else "") + "k_decode_main+k_decode_merge",
+                            "bound": "hbm", "achieved": round(bytes_r / (ms_r * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": round(bytes_r / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                            "traffic": None, "algorithmic_bytes_per_launch": bytes_r // L},
+        "uniform_at_maxima_ms": round(ms_u, 4),
+    }), flush=True)
 
 
 def cpu_baseline(w, sample_tokens: int):

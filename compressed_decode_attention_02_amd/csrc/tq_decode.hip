@@ -1179,9 +1179,14 @@ void k_decode_main(DecodeArgs a) {
         int n_packed = (int)a.n_packed, n_ring = a.n_ring;
         if (a.seq_packed) n_packed = (int)min(max(a.seq_packed[b], (int64_t)0), a.n_packed);
         if (a.seq_ring) n_ring = min(max(a.seq_ring[b], 0), a.n_ring);
-        const int t_begin = split * (int)a.per_split;
-        const int t_end = max(t_begin, min(n_packed, t_begin + (int)a.per_split));
-        const int r0 = split * a.ring_per_split, nr = max(0, min(n_ring - r0, a.ring_per_split));
+        // ragged batches: this sequence's own lengths divided evenly over the splits (whole
+        // 32-token blocks; at most the call's split sizes, since the lengths are clamped)
+        int per_split = (int)a.per_split, ring_per_split = a.ring_per_split;
+        if (a.seq_packed) per_split = ((n_packed + a.n_split - 1) / a.n_split + kBlock - 1) / kBlock * kBlock;
+        if (a.seq_ring) ring_per_split = (n_ring + a.n_split - 1) / a.n_split;
+        const int t_begin = split * per_split;
+        const int t_end = max(t_begin, min(n_packed, t_begin + per_split));
+        const int r0 = split * ring_per_split, nr = max(0, min(n_ring - r0, ring_per_split));
         float orr[R::NE];
         packed_wave<D, VB, G, NW>(a, sm, bk, b, kvh, n_packed, t_begin, t_end, r0, nr, orr);
         __syncthreads();
