@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=2, help="workload id (1..5); 2 = Llama-3.1-8B b1 32K")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--paged", type=int, default=0, metavar="PAGE_TOKENS",
+                   help="keep the packed cache in pages of this many tokens (a multiple of 32), in a "
+                        "seeded random page order per slice")
     p.add_argument("--ragged", action="store_true",
                    help="time only the decode, over a ragged batch: sequence b attends to its own seeded "
                         "lengths (packed uniform in [1, packed tokens], ring uniform in [0, ring tokens])")
@@ -124,7 +127,11 @@ def main():
         K = torch.cat(ks).contiguous() if L > 1 else ks[0]
         V = torch.cat(vs).contiguous() if L > 1 else vs[0]
         del ks, vs
-        store = tq.PackedStore(cfg, n_sl, Tp + w.buffer_size, device=dev)
+        if args.paged:
+            pps = -(-(Tp + w.buffer_size) // args.paged)
+            store = tq.PagedStore(cfg, n_sl, args.paged, pps, n_sl * pps, seed=c, device=dev)
+        else:
+            store = tq.PackedStore(cfg, n_sl, Tp + w.buffer_size, device=dev)
         ring = tq.Ring(cfg, n_sl, device=dev)
         kn, vn = W.device_kv(w, 7777 + c, 1, dev, tensor_ids=(3, 4))
         kn = kn.reshape(n_sl_layer, d).repeat(L, 1).contiguous()
@@ -232,7 +239,7 @@ def main():
         "config": {"workload": w.name, "layers": L, "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": d,
                    "packed_tokens": Tp, "ring_tokens": w.n_ring, "key_bits": 3, "qjl_bits": 1,
                    "value_bits": w.value_bits, "group": 32, "parallelism": "none (1 GPU)",
-                   "copies_cycled": n_copies},
+                   "copies_cycled": n_copies, "paged": args.paged or None},
         "breakdown_ms_median": {"quantize": round(q_med, 4), "append_and_decode_all_layers": round(d_med, 4),
                                 "flush": round(statistics.median(f_ms), 4)},
         "quantize_tokens_per_s": round(B * L * Tp / (q_med * 1e-3), 1),

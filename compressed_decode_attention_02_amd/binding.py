@@ -40,7 +40,8 @@ class tq_tables(ctypes.Structure):
 
 class tq_packed(ctypes.Structure):
     _fields_ = [("key_words", ctypes.c_void_p), ("key_norms", ctypes.c_void_p), ("val_words", ctypes.c_void_p),
-                ("val_scales", ctypes.c_void_p), ("capacity", ctypes.c_int64)]
+                ("val_scales", ctypes.c_void_p), ("capacity", ctypes.c_int64), ("block_table", ctypes.c_void_p),
+                ("page_tokens", ctypes.c_int32), ("pages_per_slice", ctypes.c_int32), ("n_pages", ctypes.c_int64)]
 
 
 class tq_ring(ctypes.Structure):
@@ -178,7 +179,44 @@ class PackedStore:
         """tq_packed view starting at slice `slice_offset` (e.g. one layer of a larger store)."""
         return tq_packed(self.key_words[slice_offset:].data_ptr(), self.key_norms[slice_offset:].data_ptr(),
                          self.val_words[slice_offset:].data_ptr(), self.val_scales[slice_offset:].data_ptr(),
-                         self.capacity)
+                         self.capacity, None, 0, 0, 0)
+
+
+class PagedStore:
+    """A paged packed cache: a pool of n_pages pages of page_tokens records ([n_pages][page_tokens]
+    [...] per array) and a block table [n_slices][pages_per_slice] of page indices (layout in tq.h).
+    Without a table, slices take pages in a seeded random order (pages need not be contiguous)."""
+
+    def __init__(self, cfg: tq_config, n_slices: int, page_tokens: int, pages_per_slice: int, n_pages: int,
+                 table=None, seed: int = 0, device="cuda"):
+        import torch
+        d, vb = cfg.head_dim, cfg.value_bits
+        self.cfg, self.n_slices, self.page_tokens = cfg, n_slices, page_tokens
+        self.pages_per_slice, self.n_pages = pages_per_slice, n_pages
+        self.capacity = pages_per_slice * page_tokens
+        self.key_words = torch.zeros((n_pages, page_tokens, d // 8), dtype=torch.int32, device=device)
+        self.key_norms = torch.zeros((n_pages, page_tokens, 2), dtype=torch.float32, device=device)
+        self.val_words = torch.zeros((n_pages, page_tokens, vb * d // 32), dtype=torch.int32, device=device)
+        self.val_scales = torch.zeros((n_pages, page_tokens, d // 32), dtype=torch.int16, device=device)
+        if table is None:
+            perm = np.random.Generator(np.random.PCG64(seed)).permutation(n_pages)[:n_slices * pages_per_slice]
+            table = perm.reshape(n_slices, pages_per_slice)
+        self.table_np = np.asarray(table, np.int32).reshape(n_slices, pages_per_slice)
+        self.block_table = torch.from_numpy(self.table_np.copy()).to(device)
+
+    def struct(self, slice_offset: int = 0) -> tq_packed:
+        """tq_packed view of slices slice_offset.. (their block-table rows; the pool is shared)."""
+        return tq_packed(self.key_words.data_ptr(), self.key_norms.data_ptr(), self.val_words.data_ptr(),
+                         self.val_scales.data_ptr(), self.capacity, self.block_table[slice_offset:].data_ptr(),
+                         self.page_tokens, self.pages_per_slice, self.n_pages)
+
+    def gather(self):
+        """The store as contiguous [n_slices][capacity][...] arrays (host copies through the table)."""
+        out = {}
+        for name in ("key_words", "key_norms", "val_words", "val_scales"):
+            pool = getattr(self, name).cpu().numpy()
+            out[name] = pool[self.table_np].reshape(self.n_slices, self.capacity, *pool.shape[2:])
+        return out
 
 
 class Ring:

@@ -20,8 +20,22 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 bool packed_ok(const tq_packed *p) {
-    return p && p->key_words && p->key_norms && p->val_words && p->val_scales && p->capacity >= 0 &&
-           aligned16(p->key_words) && aligned8(p->key_norms) && aligned16(p->val_words) && aligned8(p->val_scales);
+    if (!(p && p->key_words && p->key_norms && p->val_words && p->val_scales && p->capacity >= 0 &&
+          aligned16(p->key_words) && aligned8(p->key_norms) && aligned16(p->val_words) && aligned8(p->val_scales)))
+        return false;
+    if (!p->block_table) return true;
+    // paged: whole 32-token blocks per page, the capacity the table covers, a non-empty pool
+    return (reinterpret_cast<uintptr_t>(p->block_table) & 3u) == 0 && p->page_tokens > 0 &&
+           p->page_tokens % 32 == 0 && p->pages_per_slice > 0 && p->n_pages > 0 &&
+           p->capacity == (int64_t)p->pages_per_slice * p->page_tokens;
+}
+
+template <typename Args>
+void set_pages(Args &a, const tq_packed *p) {
+    a.bt = p->block_table;
+    a.pt = p->block_table ? p->page_tokens : 1;
+    a.pps = p->block_table ? p->pages_per_slice : 0;
+    a.n_pages = p->block_table ? p->n_pages : 0;
 }
 
 bool tables_ok(const tq_tables *t) {
@@ -110,6 +124,7 @@ extern "C" tq_status tq_quantize_kv(const tq_config *cfg, const tq_tables *table
     a.vs = dst->val_scales;
     a.cap = dst->capacity;
     a.dst_offset = dst_offset;
+    set_pages(a, dst);
     return hip_status(tq::launch_quantize(cfg->head_dim, cfg->value_bits, in_dtype, a, (hipStream_t)stream));
 }
 
@@ -156,6 +171,7 @@ extern "C" tq_status tq_flush(const tq_config *cfg, const tq_tables *tables, con
     a.vs = dst->val_scales;
     a.cap = dst->capacity;
     a.dst_offset = n_packed;
+    set_pages(a, dst);
     return hip_status(tq::launch_quantize(cfg->head_dim, cfg->value_bits, TQ_F16, a, (hipStream_t)stream));
 }
 
@@ -228,6 +244,7 @@ tq_status decode_impl(const tq_config *cfg, const tq_tables *tables, const void 
         a.vw = packed->val_words;
         a.vs = packed->val_scales;
         a.cap = packed->capacity;
+        set_pages(a, packed);
     }
     a.n_packed = n_packed;
     if (n_ring > 0) {

@@ -248,12 +248,20 @@ struct alignas(16) DecodeSmem {
 //      uniform base plus a 32-bit per-lane byte offset; the instruction's immediate offset
 //      IMM is added to both the global and the LDS address.  Every LDS read of a buffer is
 //      complete (lgkmcnt(0)) before the buffer is refilled.
+// (the base is uniform by construction; readfirstlane makes that visible to the compiler
+// wherever it would otherwise keep the pointer in vector registers, and folds away elsewhere)
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return reinterpret_cast<const void *>(lo | (hi << 32));
+}
 template <int IMM = 0>
 __device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t lds) {
     static_assert(IMM >= 0 && IMM < 4096, "global instruction offset range");
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
                  :
-                 : "v"(off), "s"(base), "s"(lds), "n"(IMM)
+                 : "v"(off), "s"(uniform_ptr(base)), "s"(lds), "n"(IMM)
                  : "memory", "m0");
 }
 template <int IMM = 0>
@@ -261,7 +269,7 @@ __device__ __forceinline__ void dma4(const void *base, uint32_t off, uint32_t ld
     static_assert(IMM >= 0 && IMM < 4096, "global instruction offset range");
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1 offset:%3"
                  :
-                 : "v"(off), "s"(base), "s"(lds), "n"(IMM)
+                 : "v"(off), "s"(uniform_ptr(base)), "s"(lds), "n"(IMM)
                  : "memory", "m0");
 }
 template <int N>
@@ -521,11 +529,14 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     // all 16); G = 8 has one accumulator for the centroid rows (hi 0..7, lo 8..15) and one
     // for the sign rows.
     // ---- staging setup
-    const int64_t rec0 = (int64_t)bk * a.cap;
-    const uint32_t *kw_s = a.kw + rec0 * S::KW;
-    const float *kn_s = a.kn + rec0 * 2;
-    const uint32_t *vw_s = a.vw + rec0 * S::VW;
-    const uint16_t *vs_s = a.vs + rec0 * S::NG;
+    // record of token t0 of this slice (a block of 32 tokens from t0, a multiple of 32, lies in
+    // one page of a paged store, since pages hold a multiple of 32 tokens)
+    // (the same for every lane: made visibly uniform, so the copy bases are scalar values)
+    auto block_rec = [&](int t0) -> int64_t {
+        const int64_t r = record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, bk, t0);
+        return (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)r) |
+               ((int64_t)__builtin_amdgcn_readfirstlane((int)(r >> 32)) << 32);
+    };
     const int last = n_packed - 1;
     const uint32_t lds_wave = (uint32_t)(uintptr_t)&sm.stage[0][wave][0];
     // ---- staging: block at token t0 into buffer bi (token indices clamped to the last
@@ -564,12 +575,13 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     auto issue = [&](int t0, int bi) {
         const uint32_t base = lds_wave + (uint32_t)(bi * NW * S::BUF_B);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int64_t rb = block_rec(t0);
+        const uint32_t *kw_b = a.kw + rb * S::KW;
+        const float *kn_b = a.kn + rb * 2;
+        const uint32_t *vw_b = a.vw + rb * S::VW;
+        const uint16_t *vs_b = a.vs + rb * S::NG;
         if (t0 + kBlock - 1 <= last) {
             // whole block in range: uniform record base, loop-invariant lane offsets
-            const uint32_t *kw_b = kw_s + (int64_t)t0 * S::KW;
-            const float *kn_b = kn_s + (int64_t)t0 * 2;
-            const uint32_t *vw_b = vw_s + (int64_t)t0 * S::VW;
-            const uint16_t *vs_b = vs_s + (int64_t)t0 * S::NG;
             static_assert(S::N_KW <= 4 && S::N_VS <= 16, "immediate offsets");
             // (the immediate offset IMM moves the LDS destination too: copy i of the keys reads
             // the block at ok0 + IMM, IMM = 16 tt KW 4 + 16 j, and lands at base + 1024 i)
@@ -589,33 +601,34 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
             if constexpr (S::N_VS > 1) dma4<256>(vs_b, o4, base + S::OFF_VS);
             static_assert(S::N_VS <= 2, "scale copies");
         } else {
-            // the last block(s): token indices clamped to the last packed token (the lane's
-            // rows and columns are recomputed here rather than held across the loop)
+            // the last block(s): token indices clamped to the last packed token, as offsets
+            // from the block's first record (the lane's rows and columns are recomputed here
+            // rather than held across the loop)
             int lane_c = lane;
             asm volatile("" : "+v"(lane_c));
 #pragma unroll
             for (int i = 0; i < S::N_KW; ++i) {
                 const int tt = i / NC, j = i % NC;
-                const uint32_t tok = (uint32_t)min(t0 + 16 * tt + (lane_c & 15), last);
-                dma16(kw_s, tok * (S::KW * 4) + (uint32_t)(lane_c >> 4) * (S::NKS * 4) + 16 * j, base + 1024 * i);
+                const uint32_t tok = (uint32_t)(min(t0 + 16 * tt + (lane_c & 15), last) - t0);
+                dma16(kw_b, tok * (S::KW * 4) + (uint32_t)(lane_c >> 4) * (S::NKS * 4) + 16 * j, base + 1024 * i);
             }
             {
-                const uint32_t tok = (uint32_t)min(t0 + (lane_c >> 1), last);
-                dma4(kn_s, tok * 8 + (lane_c & 1) * 4, base + S::OFF_KN);
+                const uint32_t tok = (uint32_t)(min(t0 + (lane_c >> 1), last) - t0);
+                dma4(kn_b, tok * 8 + (lane_c & 1) * 4, base + S::OFF_KN);
             }
 #pragma unroll
             for (int i = 0; i < S::N_VW; ++i) {
                 uint32_t r, col;
                 vw_rc(lane_c, i, r, col);
-                const uint32_t tok = (uint32_t)min(t0 + (int)r, last);
-                dma16(vw_s, tok * (S::VW * 4) + col, base + S::OFF_VW + 1024 * i);
+                const uint32_t tok = (uint32_t)(min(t0 + (int)r, last) - t0);
+                dma16(vw_b, tok * (S::VW * 4) + col, base + S::OFF_VW + 1024 * i);
             }
 #pragma unroll
             for (int i = 0; i < S::N_VS; ++i) {
                 uint32_t r, col;
                 vs_rc(lane_c, i, r, col);
-                const uint32_t tok = (uint32_t)min(t0 + (int)r, last);
-                dma4(vs_s, tok * (S::NG * 2) + col, base + S::OFF_VS + 256 * i);
+                const uint32_t tok = (uint32_t)(min(t0 + (int)r, last) - t0);
+                dma4(vs_b, tok * (S::NG * 2) + col, base + S::OFF_VS + 256 * i);
             }
         }
     };

@@ -37,6 +37,10 @@ struct QuantArgs {
     uint16_t *vs;
     int64_t cap;
     int64_t dst_offset;
+    // paged store (bt != nullptr): record of token t of slice s = pt * bt[s * pps + t / pt] + t % pt
+    const int32_t *bt;
+    int pt, pps;
+    int64_t n_pages;
 };
 
 struct DecodeArgs {
@@ -50,6 +54,9 @@ struct DecodeArgs {
     const uint32_t *vw;
     const uint16_t *vs;
     int64_t cap;
+    const int32_t *bt;  // paged store, as in QuantArgs
+    int pt, pps;
+    int64_t n_pages;
     int64_t n_packed;
     const uint16_t *rk;
     const uint16_t *rv;
@@ -76,6 +83,15 @@ struct DecodeArgs {
     float *partial;      // [batch*hkv][n_split][G][D]: o of each split
     float *partial_ml;   // [batch*hkv][n_split][G][2]: (m, l) of each split
 };
+
+// record index of token t of slice s (paged or contiguous store; page entries clamped to the pool)
+__host__ __device__ inline int64_t record_index(const int32_t *bt, int pt, int pps, int64_t n_pages, int64_t cap,
+                                                int64_t s, int64_t t) {
+    if (!bt) return s * cap + t;
+    int64_t p = bt[s * pps + t / pt];
+    p = p < 0 ? 0 : (p >= n_pages ? n_pages - 1 : p);
+    return p * pt + t % pt;
+}
 
 hipError_t launch_quantize(int d, int vb, tq_dtype dt, const QuantArgs &a, hipStream_t st);
 hipError_t launch_decode(int d, int vb, int G, const DecodeArgs &a, hipStream_t st);

@@ -110,6 +110,18 @@ typedef struct {
     uint32_t *val_words;
     uint16_t *val_scales;
     int64_t capacity;           /* tokens per slice */
+    /* Paged store (block_table != NULL; NULL/0 fields give the contiguous layout above): the
+     * four arrays are a pool of n_pages pages of page_tokens records ([n_pages][page_tokens]
+     * [...]), and token t of slice s is record page_tokens * p + t % page_tokens of page
+     * p = block_table[s * pages_per_slice + t / page_tokens] (device int32 table, 4-byte
+     * aligned).  page_tokens must be a multiple of 32 and capacity == pages_per_slice *
+     * page_tokens.  Table entries outside [0, n_pages) are clamped on the device, so no entry
+     * addresses outside the pool; pages shared by two slices receive both writes (the
+     * caller's table decides which tokens land where). */
+    const int32_t *block_table;
+    int32_t page_tokens;
+    int32_t pages_per_slice;
+    int64_t n_pages;
 } tq_packed;
 
 /* Exact recent tokens: fp16 [n_slices][buffer_size][d] keys and values (guide 5.1). */

@@ -358,6 +358,77 @@ def test_decode_ragged_batch(torch):
         np.testing.assert_array_equal(out.cpu().numpy(), g2.astype(np.float32))
 
 
+def test_paged_store_matches_contiguous(torch):
+    """A paged store (pages in a seeded random order, spare pages in the pool) holds exactly the
+    contiguous store's records, and every decode entry point reads it to the same results bit
+    for bit: history quantise, full-ring flush inside the fused step, uniform, ragged and
+    layer-offset (slice_offset) decodes; one case also against the oracle."""
+    w = W.custom(3, batch=2, n_packed=600, n_ring=64, buffer_size=64)
+    env = Env(w.d, w.value_bits, buffer_size=w.buffer_size)
+    n_sl = w.batch * w.hkv
+    pt, pps = 64, 12                       # capacity 768 >= 600 + 64 + 1
+    (k, v), _ = W.host_kv(w, 0, w.n_packed + w.n_ring + 1)
+    k = k.reshape(n_sl, -1, w.d)
+    v = v.reshape(n_sl, -1, w.d)
+    cont = tq.PackedStore(env.cfg, n_sl, pt * pps)
+    paged = tq.PagedStore(env.cfg, n_sl, pt, pps, n_sl * pps + 7, seed=5)
+    for st in (cont, paged):
+        quantize_gpu(env, to_dev(np.ascontiguousarray(k[:, :w.n_packed]), w.in_dtype),
+                     to_dev(np.ascontiguousarray(v[:, :w.n_packed]), w.in_dtype), n_sl, w.n_packed, store=st)
+    G = paged.gather()
+    C = {n: getattr(cont, n).cpu().numpy() for n in G}
+    for n in G:
+        np.testing.assert_array_equal(G[n].view(np.uint8), C[n].view(np.uint8), err_msg=n)
+    rings = []
+    for _ in range(2):
+        rg = tq.Ring(env.cfg, n_sl)
+        for t_ in range(w.n_ring):
+            tq.tq_append_ring(env.cfg, rg.struct(), to_dev(np.ascontiguousarray(k[:, w.n_packed + t_]), w.in_dtype),
+                              to_dev(np.ascontiguousarray(v[:, w.n_packed + t_]), w.in_dtype), n_sl, t_)
+        rings.append(rg)
+    q, _ = W.host_queries(w, 0)
+    qd = to_dev(q, w.in_dtype)
+    scale = 1.0 / math.sqrt(w.d)
+    ws = tq.new_workspace(env.cfg, w.batch, w.hq, w.hkv, pt * pps)
+    outs = [torch.zeros((w.batch, w.hq, w.d), dtype=torch.float32, device="cuda") for _ in range(2)]
+    # uniform decode over history + full ring
+    for o, st, rg in zip(outs, (cont, paged), rings):
+        tq.tq_decode_attention(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, st.struct(), w.n_packed, rg.struct(),
+                               w.n_ring, scale, o, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(outs[1].cpu().numpy(), outs[0].cpu().numpy())
+    # layer-offset views: the second batch element alone through slice_offset
+    half = [torch.zeros((1, w.hq, w.d), dtype=torch.float32, device="cuda") for _ in range(2)]
+    for o, st, rg in zip(half, (cont, paged), rings):
+        tq.tq_decode_attention(env.cfg, env.tables, qd[1:], 1, w.hq, w.hkv, st.struct(w.hkv), w.n_packed,
+                               rg.struct(w.hkv), w.n_ring, scale, o, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(half[1].cpu().numpy(), half[0].cpu().numpy())
+    # ragged
+    sp = torch.tensor([599, 37], dtype=torch.int64, device="cuda")
+    sr = torch.tensor([3, 64], dtype=torch.int32, device="cuda")
+    for o, st, rg in zip(outs, (cont, paged), rings):
+        tq.tq_decode_attention_ragged(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, st.struct(), sp, w.n_packed,
+                                      rg.struct(), sr, w.n_ring, scale, o, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(outs[1].cpu().numpy(), outs[0].cpu().numpy())
+    # fused step on the full ring: flush into records 600..663, then append and decode
+    kn = to_dev(np.ascontiguousarray(k[:, w.n_packed + w.n_ring]), w.in_dtype)
+    vn = to_dev(np.ascontiguousarray(v[:, w.n_packed + w.n_ring]), w.in_dtype)
+    for o, st, rg in zip(outs, (cont, paged), rings):
+        got = tq.tq_decode_step(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, st.struct(), w.n_packed, rg.struct(),
+                                w.n_ring, kn, vn, scale, o, ws)
+        assert got == (w.n_packed + w.n_ring, 1)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(outs[1].cpu().numpy(), outs[0].cpu().numpy())
+    G = paged.gather()
+    for n in G:
+        np.testing.assert_array_equal(G[n].view(np.uint8), getattr(cont, n).cpu().numpy().view(np.uint8), err_msg=n)
+    ref = oracle_decode(env, dev_to_stored(qd).astype(np.float64), w.hq, w.hkv, cont, w.n_packed + w.n_ring,
+                        rings[1], 1, b_list=[0, 1])
+    assert_decode_close(outs[1].cpu().numpy().astype(np.float64), ref, "paged step")
+
+
 def test_decode_empty_context_gives_zeros(torch):
     env = Env(128, 2)
     q = np.ones((1, 4, 128), np.float32)

@@ -202,3 +202,21 @@ def test_decode_ragged_errors():
     assert rag(n_ring_max=129) == B.TQ_ERR_INVALID_ARG
     assert rag(ws=16) == B.TQ_ERR_WORKSPACE
 
+
+def test_paged_store_errors():
+    """A paged store must hold whole 32-token blocks per page, cover its capacity with its table
+    and have an aligned table; each violation is refused before any launch."""
+    cfg = tq.make_config()
+    L = tq.lib()
+    T = _fake_tables()
+
+    def q(page_tokens=64, pps=4, n_pages=40, cap=256, table=FAKE):
+        P = B.tq_packed(FAKE, FAKE, FAKE, FAKE, cap, table, page_tokens, pps, n_pages)
+        return L.tq_quantize_kv(ctypes.byref(cfg), ctypes.byref(T), FAKE, FAKE, B.TQ_BF16, 8, 100,
+                                ctypes.byref(P), 300, None)   # offset 300 > capacity in every case
+    assert q() == B.TQ_ERR_INVALID_ARG                       # (the offset check: a valid paged store)
+    assert q(page_tokens=48, cap=192) == B.TQ_ERR_INVALID_ARG  # not whole 32-token blocks
+    assert q(cap=512) == B.TQ_ERR_INVALID_ARG                 # capacity != pages * page tokens
+    assert q(n_pages=0) == B.TQ_ERR_INVALID_ARG
+    assert q(table=FAKE + 2) == B.TQ_ERR_INVALID_ARG          # int32 table: 4-byte aligned
+
