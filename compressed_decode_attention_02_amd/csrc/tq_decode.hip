@@ -357,7 +357,8 @@ __device__ __forceinline__ void ring_load(const DecodeArgs &a, RingRegs<D, G, NW
         rr.v2[u] = tt < n ? rv2[(int64_t)(r0 + tt) * R::NCP + cp] : 0u;
     }
     // fused append: the new token replaces what the ring slot held, read from the input and
-    // rounded as the append rounds it, and this workgroup writes it into the ring
+    // rounded as the append rounds it (ring_attend writes it into the ring from these
+    // registers, once every load has landed)
     const int ns = a.new_slot - r0;
     if (a.new_slot >= 0 && ns >= 0 && ns < n) {
         const int64_t in0 = (int64_t)bk * D;
@@ -373,13 +374,6 @@ __device__ __forceinline__ void ring_load(const DecodeArgs &a, RingRegs<D, G, NW
                 const uint32_t sel = (cp & 3);
                 rr.v2[u] = sel == 0 ? w.x : (sel == 1 ? w.y : (sel == 2 ? w.z : w.w));
             }
-        uint16_t *rkw = const_cast<uint16_t *>(a.rk) + ((int64_t)bk * a.buffer_size + a.new_slot) * D;
-        uint16_t *rvw = const_cast<uint16_t *>(a.rv) + ((int64_t)bk * a.buffer_size + a.new_slot) * D;
-        for (int c = tid; c < 2 * (D / 8); c += R::NT) {
-            const bool key = c < D / 8;
-            const int c8 = 8 * (key ? c : c - D / 8);
-            *reinterpret_cast<uint4 *>((key ? rkw : rvw) + c8) = new_token8(key ? a.k_new : a.v_new, a.kv_dtype, in0 + c8);
-        }
     }
 }
 
@@ -388,7 +382,7 @@ __device__ __forceinline__ void ring_load(const DecodeArgs &a, RingRegs<D, G, NW
 // output elements e = tid + k NT ([G][D] order) into orr.  scr: LDS scratch of SCR bytes.
 template <int D, int G, int NW, int SCR>
 __device__ void ring_attend(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, float *scr, float *rm, float *rl,
-                            int b, int kvh, int n, float (&orr)[RingShape<D, G, NW>::NE]) {
+                            int bk, int b, int kvh, int r0, int n, float (&orr)[RingShape<D, G, NW>::NE]) {
     using R = RingShape<D, G, NW>;
     constexpr int RP = kRingPerSplit<D>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -396,6 +390,21 @@ __device__ void ring_attend(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, f
     float *qr = scr, *pr = scr + G * D, *os = pr + G * RP;
     for (int i = tid; i < G * D; i += R::NT) qr[i] = load_q(a, ((int64_t)b * a.hq + kvh * G) * D + i);
     __syncthreads();
+    // fused append: the threads holding the new token's words write them into its ring slot
+    const int ns = a.new_slot - r0;
+    if (a.new_slot >= 0 && ns >= 0 && ns < n) {
+        uint16_t *rkw = const_cast<uint16_t *>(a.rk) + ((int64_t)bk * a.buffer_size + a.new_slot) * D;
+        uint32_t *rvw = reinterpret_cast<uint32_t *>(const_cast<uint16_t *>(a.rv) +
+                                                     ((int64_t)bk * a.buffer_size + a.new_slot) * D);
+#pragma unroll
+        for (int ps = 0; ps < R::NP; ++ps)
+            if (ps * R::TCH + tid / R::TPT == ns)
+#pragma unroll
+                for (int i = 0; i < R::SEG / 8; ++i) *reinterpret_cast<uint4 *>(rkw + part * R::SEG + 8 * i) = rr.k4[ps][i];
+#pragma unroll
+        for (int u = 0; u < R::TPV; ++u)
+            if (tg + u * R::NTG == ns) rvw[cp] = rr.v2[u];
+    }
     const float lscale = a.scale * kLog2e;
 #pragma unroll
     for (int ps = 0; ps < R::NP; ++ps) {
@@ -666,7 +675,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
         prep_load<D, G, NW>(a, prg, b, kvh);
     }
     // the split's ring tokens (the second staging buffers as scratch)
-    if (nr > 0) ring_attend<D, G, NW, NW * S::BUF_B>(a, rr, qw, sm.rm, sm.rl, b, kvh, nr, orr);
+    if (nr > 0) ring_attend<D, G, NW, NW * S::BUF_B>(a, rr, qw, sm.rm, sm.rl, bk, b, kvh, r0, nr, orr);
     if constexpr (D == 256) {
 #pragma unroll
         for (int i = 0; i < NPW; ++i)
