@@ -10,15 +10,17 @@
 // Launches per call:
 //   * d = 256 only: k_decode_prep, q' and w of every query head into the workspace (bands of
 //     S rows per workgroup);
-//   * k_decode_main, grid (packed splits, batch * kv heads): each workgroup prepares its
-//     slice's queries in LDS (d = 128) or copies them from the workspace (d = 256), then its
-//     waves stream blocks of 32 packed tokens through LDS (hand-issued global -> LDS copies):
+//   * k_decode_main, grid (splits, batch * kv heads): each workgroup attends to its split's
+//     share of the ring's exact fp16 tokens against the unrotated queries (the new token of a
+//     fused step taken from the input), prepares its slice's queries in LDS (d = 128) or copies
+//     them from the workspace (d = 256), then its waves stream blocks of 32 packed tokens
+//     through LDS (hand-issued global -> LDS copies):
 //     scores on MFMA (query rows x token columns; centroid values from byte tables by
 //     v_perm_b32, QJL signs as +-1), a lazily rescaled online softmax, values on MFMA with
-//     A = 1 + code / 2^vb and B = p * scale; the waves' (m, l, o) are combined in LDS and
-//     written as the split's partials;
-//   * k_decode_merge, one workgroup per query head: attention over the ring's exact fp16
-//     tokens against the unrotated query, combined with the packed splits' partials.
+//     A = 1 + code / 2^vb and B = p * scale; the waves' and the ring's (m, l, o) are combined
+//     in LDS and written as the split's partials;
+//   * k_decode_merge, one workgroup per query head: the splits' partials combined (skipped
+//     with a single split, whose workgroup writes the output itself).
 #include <hip/hip_runtime.h>
 
 #include "tq.h"
@@ -1237,10 +1239,15 @@ void k_decode_main(DecodeArgs a) {
                     O = fmaf(orr[k], f, O);
                 }
             }
-            pp[g * D + j] = O;
-            if (j == 0) {
-                pml[g * 2] = M;
-                pml[g * 2 + 1] = L;
+            if (a.n_split == 1) {
+                // the only split: its result is the output (no merge launch)
+                a.out[((int64_t)b * a.hq + kvh * G + g) * D + j] = L > 0.f ? O / L : 0.f;
+            } else {
+                pp[g * D + j] = O;
+                if (j == 0) {
+                    pml[g * 2] = M;
+                    pml[g * 2 + 1] = L;
+                }
             }
         }
     }
@@ -1371,7 +1378,8 @@ static void launch_g(const DecodeArgs &a, hipStream_t st) {
             hipLaunchKernelGGL((k_decode_main<D, VB, G, 4>), grid, dim3(64 * 4), 0, st, a);
         }
     }
-    hipLaunchKernelGGL((k_decode_merge<D, G>), dim3((unsigned)(a.batch * a.hkv * G)), dim3(kThreads), 0, st, a);
+    if (a.n_split > 1)
+        hipLaunchKernelGGL((k_decode_merge<D, G>), dim3((unsigned)(a.batch * a.hkv * G)), dim3(kThreads), 0, st, a);
 }
 
 template <int D, int VB>
