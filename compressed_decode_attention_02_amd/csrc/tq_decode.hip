@@ -395,9 +395,8 @@ __device__ void ring_attend(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, f
     // fused append: the threads holding the new token's words write them into its ring slot
     const int ns = a.new_slot - r0;
     if (a.new_slot >= 0 && ns >= 0 && ns < n) {
-        uint16_t *rkw = const_cast<uint16_t *>(a.rk) + ((int64_t)bk * a.buffer_size + a.new_slot) * D;
-        uint32_t *rvw = reinterpret_cast<uint32_t *>(const_cast<uint16_t *>(a.rv) +
-                                                     ((int64_t)bk * a.buffer_size + a.new_slot) * D);
+        uint16_t *rkw = a.rk + ((int64_t)bk * a.buffer_size + a.new_slot) * D;
+        uint32_t *rvw = reinterpret_cast<uint32_t *>(a.rv + ((int64_t)bk * a.buffer_size + a.new_slot) * D);
 #pragma unroll
         for (int ps = 0; ps < R::NP; ++ps)
             if (ps * R::TCH + tid / R::TPT == ns)

@@ -58,8 +58,8 @@ struct DecodeArgs {
     int pt, pps;
     int64_t n_pages;
     int64_t n_packed;
-    const uint16_t *rk;
-    const uint16_t *rv;
+    uint16_t *rk;  // ring (written only by a fused step's append)
+    uint16_t *rv;
     int buffer_size;
     int n_ring;
     int batch, hq, hkv;
