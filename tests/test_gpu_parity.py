@@ -358,15 +358,20 @@ def test_decode_ragged_batch(torch):
         np.testing.assert_array_equal(out.cpu().numpy(), g2.astype(np.float32))
 
 
-def test_paged_store_matches_contiguous(torch):
+@pytest.mark.parametrize("case", ["d128_v4", "d256_v4"])
+def test_paged_store_matches_contiguous(torch, case):
     """A paged store (pages in a seeded random order, spare pages in the pool) holds exactly the
     contiguous store's records, and every decode entry point reads it to the same results bit
     for bit: history quantise, full-ring flush inside the fused step, uniform, ragged and
     layer-offset (slice_offset) decodes; one case also against the oracle."""
-    w = W.custom(3, batch=2, n_packed=600, n_ring=64, buffer_size=64)
+    if case == "d128_v4":
+        w = W.custom(3, batch=2, n_packed=600, n_ring=64, buffer_size=64)
+        pt, pps = 64, 12                   # capacity 768 >= 600 + 64 + 1
+    else:
+        w = W.custom(4, batch=2, n_packed=500, n_ring=32, buffer_size=32)
+        pt, pps = 32, 18                   # capacity 576 >= 500 + 32 + 1
     env = Env(w.d, w.value_bits, buffer_size=w.buffer_size)
     n_sl = w.batch * w.hkv
-    pt, pps = 64, 12                       # capacity 768 >= 600 + 64 + 1
     (k, v), _ = W.host_kv(w, 0, w.n_packed + w.n_ring + 1)
     k = k.reshape(n_sl, -1, w.d)
     v = v.reshape(n_sl, -1, w.d)
@@ -405,14 +410,14 @@ def test_paged_store_matches_contiguous(torch):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(half[1].cpu().numpy(), half[0].cpu().numpy())
     # ragged
-    sp = torch.tensor([599, 37], dtype=torch.int64, device="cuda")
-    sr = torch.tensor([3, 64], dtype=torch.int32, device="cuda")
+    sp = torch.tensor([w.n_packed - 1, 37], dtype=torch.int64, device="cuda")
+    sr = torch.tensor([3, w.n_ring], dtype=torch.int32, device="cuda")
     for o, st, rg in zip(outs, (cont, paged), rings):
         tq.tq_decode_attention_ragged(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, st.struct(), sp, w.n_packed,
                                       rg.struct(), sr, w.n_ring, scale, o, ws)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(outs[1].cpu().numpy(), outs[0].cpu().numpy())
-    # fused step on the full ring: flush into records 600..663, then append and decode
+    # fused step on the full ring: flush it after the history, then append and decode
     kn = to_dev(np.ascontiguousarray(k[:, w.n_packed + w.n_ring]), w.in_dtype)
     vn = to_dev(np.ascontiguousarray(v[:, w.n_packed + w.n_ring]), w.in_dtype)
     for o, st, rg in zip(outs, (cont, paged), rings):
