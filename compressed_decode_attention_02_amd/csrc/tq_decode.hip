@@ -126,12 +126,10 @@ __device__ __forceinline__ void prep_load(const DecodeArgs &a, PrepRegs<D, G, NW
 }
 
 template <int D, int G, int NW>
-__device__ void prep_query(PrepRegs<D, G, NW> &pr, float *qw) {
-    using P = PrepShape<D, NW>;
+__device__ __forceinline__ void prep_transform(PrepRegs<D, G, NW> &pr, float *qw) {
     using Q = PrepRegs<D, G, NW>;
     constexpr int E = Q::E;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int row = tid % D, part = tid / D;
     // Walsh-Hadamard transform of head g by wave g (mod NW): strides below 64 across lanes,
     // the others between a lane's own coordinates
 #pragma unroll
@@ -157,7 +155,14 @@ __device__ void prep_query(PrepRegs<D, G, NW> &pr, float *qw) {
 #pragma unroll
         for (int e = 0; e < E; ++e) qw[g * D + lane + 64 * e] = v[e];
     }
-    __syncthreads();
+}
+
+// the partial sums of w = S q' (after a barrier that makes q' visible)
+template <int D, int G, int NW>
+__device__ __forceinline__ void prep_product(PrepRegs<D, G, NW> &pr, float *qw) {
+    using P = PrepShape<D, NW>;
+    const int tid = threadIdx.x;
+    const int row = tid % D, part = tid / D;
     if (part < P::PARTS) {
         float acc[G];
 #pragma unroll
@@ -185,6 +190,14 @@ __device__ void prep_query(PrepRegs<D, G, NW> &pr, float *qw) {
 #pragma unroll
         for (int g = 0; g < G; ++g) qw[(G + part * G + g) * D + row] = acc[g];
     }
+}
+
+// the preparation in turn: transform, barrier, product, barrier
+template <int D, int G, int NW>
+__device__ void prep_query(PrepRegs<D, G, NW> &pr, float *qw) {
+    prep_transform<D, G, NW>(pr, qw);
+    __syncthreads();
+    prep_product<D, G, NW>(pr, qw);
     __syncthreads();
 }
 
@@ -379,20 +392,20 @@ __device__ __forceinline__ void ring_load(const DecodeArgs &a, RingRegs<D, G, NW
     }
 }
 
-// attention of the G query heads over the split's n ring tokens: per head the maximum m_r
-// (log2 units) and sum l_r into rm / rl (LDS), and the unnormalised o_r of this thread's
-// output elements e = tid + k NT ([G][D] order) into orr.  scr: LDS scratch of SCR bytes.
-template <int D, int G, int NW, int SCR>
-__device__ void ring_attend(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, float *scr, float *rm, float *rl,
-                            int bk, int b, int kvh, int r0, int n, float (&orr)[RingShape<D, G, NW>::NE]) {
+// Attention of the G query heads over the split's n ring tokens, in phases separated by
+// workgroup barriers (so that another start-up task can share them): per head the maximum m_r
+// (log2 units) and sum l_r into rm / rl (LDS), and the unnormalised o_r of this thread's output
+// elements e = tid + k NT ([G][D] order) into orr.  Scratch: qr [G][D], pr [G][RP], os
+// [NTG][GB][D] (floats).
+// phase 1: the unrotated queries into LDS; a fused step's new token into its ring slot (by
+// the threads holding its words)
+template <int D, int G, int NW>
+__device__ __forceinline__ void ring_p1(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, float *qr, int bk, int b,
+                                        int kvh, int r0, int n) {
     using R = RingShape<D, G, NW>;
-    constexpr int RP = kRingPerSplit<D>;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     const int part = tid % R::TPT, cp = tid % R::NCP, tg = tid / R::NCP;
-    float *qr = scr, *pr = scr + G * D, *os = pr + G * RP;
     for (int i = tid; i < G * D; i += R::NT) qr[i] = load_q(a, ((int64_t)b * a.hq + kvh * G) * D + i);
-    __syncthreads();
-    // fused append: the threads holding the new token's words write them into its ring slot
     const int ns = a.new_slot - r0;
     if (a.new_slot >= 0 && ns >= 0 && ns < n) {
         uint16_t *rkw = a.rk + ((int64_t)bk * a.buffer_size + a.new_slot) * D;
@@ -406,6 +419,15 @@ __device__ void ring_attend(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, f
         for (int u = 0; u < R::TPV; ++u)
             if (tg + u * R::NTG == ns) rvw[cp] = rr.v2[u];
     }
+}
+
+// phase 2: logits (log2 units) of the token-head pairs into pr
+template <int D, int G, int NW>
+__device__ __forceinline__ void ring_p2(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, const float *qr, float *pr,
+                                        int n) {
+    using R = RingShape<D, G, NW>;
+    constexpr int RP = kRingPerSplit<D>;
+    const int tid = threadIdx.x, part = tid % R::TPT;
     const float lscale = a.scale * kLog2e;
 #pragma unroll
     for (int ps = 0; ps < R::NP; ++ps) {
@@ -440,8 +462,14 @@ __device__ void ring_attend(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, f
             if (part == 0 && tt < n) pr[g * RP + tt] = acc[g] * lscale;
         }
     }
-    __syncthreads();
-    // per head (wave g, g + NW, ...): maximum, then p = 2^(logit - m) in place and its sum
+}
+
+// phase 3: per head (wave g, g + NW, ...) the maximum, then p = 2^(logit - m) in place and
+// its sum
+template <int D, int G, int NW>
+__device__ __forceinline__ void ring_p3(float *pr, float *rm, float *rl, int n) {
+    constexpr int RP = kRingPerSplit<D>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int g = wave; g < G; g += NW) {
         float m = -INFINITY;
         for (int tt = lane; tt < n; tt += 64) m = fmaxf(m, pr[g * RP + tt]);
@@ -460,42 +488,71 @@ __device__ void ring_attend(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, f
             rl[g] = l;
         }
     }
-    __syncthreads();
-    // values by (coordinate pair, token class) for GB heads at a time, summed over the classes
-    // by the threads that own the output elements
+}
+
+// phase 4: values of heads g0 .. g0 + GB - 1 by (coordinate pair, token class) into os
+template <int D, int G, int NW, int GB>
+__device__ __forceinline__ void ring_p4(const RingRegs<D, G, NW> &rr, const float *pr, float *os, int g0, int n) {
+    using R = RingShape<D, G, NW>;
+    constexpr int RP = kRingPerSplit<D>;
+    const int tid = threadIdx.x, cp = tid % R::NCP, tg = tid / R::NCP;
+    float o0[GB], o1[GB];
+#pragma unroll
+    for (int h = 0; h < GB; ++h) o0[h] = o1[h] = 0.f;
+#pragma unroll
+    for (int u = 0; u < R::TPV; ++u) {
+        const int tt = tg + u * R::NTG;
+        const float va = f16_lo(rr.v2[u]), vb = f16_hi(rr.v2[u]);
+#pragma unroll
+        for (int h = 0; h < GB; ++h) {
+            const float pv = tt < n ? pr[(g0 + h) * RP + tt] : 0.f;
+            o0[h] = fmaf(pv, va, o0[h]);
+            o1[h] = fmaf(pv, vb, o1[h]);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < GB; ++h) *reinterpret_cast<float2 *>(os + (tg * GB + h) * D + 2 * cp) = make_float2(o0[h], o1[h]);
+}
+
+// phase 5: this thread's output elements of heads g0 .. g0 + GB - 1, summed over the classes
+template <int D, int G, int NW, int GB>
+__device__ __forceinline__ void ring_p5(const float *os, int g0, float (&orr)[RingShape<D, G, NW>::NE]) {
+    using R = RingShape<D, G, NW>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < R::NE; ++k) {
+        const int e = tid + k * R::NT, g = e / D, j = e - g * D;
+        if (e < G * D && g >= g0 && g < g0 + GB) {
+            float s = 0.f;
+#pragma unroll
+            for (int c = 0; c < R::NTG; ++c) s += os[(c * GB + g - g0) * D + j];
+            orr[k] = s;
+        }
+    }
+}
+
+// the phases in turn, on SCR bytes of scratch
+template <int D, int G, int NW, int SCR>
+__device__ void ring_attend(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, float *scr, float *rm, float *rl,
+                            int bk, int b, int kvh, int r0, int n, float (&orr)[RingShape<D, G, NW>::NE]) {
+    using R = RingShape<D, G, NW>;
+    constexpr int RP = kRingPerSplit<D>;
     constexpr int GB = R::gb(SCR);
     static_assert((R::fixed() + R::NTG * GB * D) * 4 <= SCR, "ring scratch in LDS");
+    float *qr = scr, *pr = scr + G * D, *os = pr + G * RP;
+    ring_p1<D, G, NW>(a, rr, qr, bk, b, kvh, r0, n);
+    __syncthreads();
+    ring_p2<D, G, NW>(a, rr, qr, pr, n);
+    __syncthreads();
+    ring_p3<D, G, NW>(pr, rm, rl, n);
+    __syncthreads();
 #pragma unroll
     for (int k = 0; k < R::NE; ++k) orr[k] = 0.f;
 #pragma unroll
     for (int g0 = 0; g0 < G; g0 += GB) {
-        float o0[GB], o1[GB];
-#pragma unroll
-        for (int h = 0; h < GB; ++h) o0[h] = o1[h] = 0.f;
-#pragma unroll
-        for (int u = 0; u < R::TPV; ++u) {
-            const int tt = tg + u * R::NTG;
-            const float va = f16_lo(rr.v2[u]), vb = f16_hi(rr.v2[u]);
-#pragma unroll
-            for (int h = 0; h < GB; ++h) {
-                const float pv = tt < n ? pr[(g0 + h) * RP + tt] : 0.f;
-                o0[h] = fmaf(pv, va, o0[h]);
-                o1[h] = fmaf(pv, vb, o1[h]);
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < GB; ++h) *reinterpret_cast<float2 *>(os + (tg * GB + h) * D + 2 * cp) = make_float2(o0[h], o1[h]);
+        ring_p4<D, G, NW, GB>(rr, pr, os, g0, n);
         __syncthreads();
-#pragma unroll
-        for (int k = 0; k < R::NE; ++k) {
-            const int e = tid + k * R::NT, g = e / D, j = e - g * D;
-            if (e < G * D && g >= g0 && g < g0 + GB) {
-                float s = 0.f;
-#pragma unroll
-                for (int c = 0; c < R::NTG; ++c) s += os[(c * GB + g - g0) * D + j];
-                orr[k] = s;
-            }
-        }
+        ring_p5<D, G, NW, GB>(os, g0, orr);
         __syncthreads();  // os is rewritten by the next group, the region by the staging copies
     }
 }
@@ -675,16 +732,34 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     } else {
         prep_load<D, G, NW>(a, prg, b, kvh);
     }
-    // the split's ring tokens (the second staging buffers as scratch)
-    if (nr > 0) ring_attend<D, G, NW, NW * S::BUF_B>(a, rr, qw, sm.rm, sm.rl, bk, b, kvh, r0, nr, orr);
+    // The split's ring tokens use the second staging buffers as scratch too.  Where the ring
+    // scratch fits after the query preparation's (with the same head grouping as on its own),
+    // the phases of the two share their barriers (MERGED); otherwise the ring goes first.
+    using RS = RingShape<D, G, NW>;
+    constexpr int QWB = PrepShape<D, NW>::template floats<G>() * 4;
+    constexpr int RSB = NW * S::BUF_B - QWB;
+    constexpr int GBM = RS::gb(NW * S::BUF_B);
+    constexpr bool MERGED = (RS::fixed() + RS::NTG * GBM * D) * 4 <= RSB;
+    float *rqr = qw + QWB / 4, *rpr = rqr + G * D, *ros = rpr + G * kRingPerSplit<D>;
+    if constexpr (!MERGED) {
+        if (nr > 0) ring_attend<D, G, NW, NW * S::BUF_B>(a, rr, qw, sm.rm, sm.rl, bk, b, kvh, r0, nr, orr);
+    }
     if constexpr (D == 256) {
 #pragma unroll
         for (int i = 0; i < NPW; ++i)
             if (threadIdx.x + i * 64 * NW < NQ4) reinterpret_cast<float4 *>(qw)[threadIdx.x + i * 64 * NW] = pw4[i];
-        __syncthreads();
     } else {
-        prep_query<D, G, NW>(prg, qw);
+        prep_transform<D, G, NW>(prg, qw);
     }
+    if constexpr (MERGED) {
+        if (nr > 0) ring_p1<D, G, NW>(a, rr, rqr, bk, b, kvh, r0, nr);
+    }
+    __syncthreads();
+    if constexpr (D != 256) prep_product<D, G, NW>(prg, qw);
+    if constexpr (MERGED) {
+        if (nr > 0) ring_p2<D, G, NW>(a, rr, rqr, rpr, nr);
+    }
+    __syncthreads();
 
     // Both parts are pre-scaled by scale * log2(e) / sqrt(d) (the sign part also by
     // sqrt(pi/2)/d), so that the logit in log2 units is |k| (centroid part + gamma * sign part).
@@ -770,8 +845,25 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
 #pragma unroll
             for (int ks = 0; ks < S::NKS; ++ks) frag(ks, bc[ks], bs[ks]);
         }
-        __syncthreads();  // fragments visible (d = 128); the second staging buffers are free
+        if constexpr (MERGED) {
+            if (nr > 0) ring_p3<D, G, NW>(rpr, sm.rm, sm.rl, nr);
+        }
+        __syncthreads();  // fragments visible (d = 128)
     }
+    if constexpr (MERGED) {
+        if (nr > 0) {
+#pragma unroll
+            for (int k = 0; k < RS::NE; ++k) orr[k] = 0.f;
+#pragma unroll
+            for (int g0 = 0; g0 < G; g0 += GBM) {
+                ring_p4<D, G, NW, GBM>(rr, rpr, ros, g0, nr);
+                __syncthreads();
+                ring_p5<D, G, NW, GBM>(ros, g0, orr);
+                __syncthreads();  // os is rewritten by the next group, the region by the staging copies
+            }
+        }
+    }
+    // (the second staging buffers are free)
     if (b1 < nb) issue(t_begin + kBlock * b1, 1);
     const int cslot = rc ? q * SM::NSL + ri : SM::FZ, sslot = rs ? q * SM::NSL + ri : SM::FZ;
     // The lane's logits after the score products: token row trow of the block, heads
