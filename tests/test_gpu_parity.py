@@ -228,8 +228,7 @@ def test_decode_ring_longer_than_one_chunk(torch):
 
 
 def test_decode_slices_not_a_multiple_of_eight(torch):
-    # the merge groups a slice's query heads on one XCD by workgroup index; 6 and 3 slices
-    # leave part of the last group of 8 empty
+    # slice counts that do not fill the eight XCDs evenly (6 and 3 slices)
     _decode_case(W.custom(2, batch=3, hq=8, hkv=2, n_packed=900, n_ring=17), "6 slices G=4")
     _decode_case(W.custom(4, batch=3, hq=2, hkv=1, n_packed=700, n_ring=128), "3 slices d256 G=2")
 
@@ -443,10 +442,12 @@ def test_decode_empty_context_gives_zeros(torch):
 
 def test_decode_workspace_reuse_needs_no_reset(torch):
     """Repeated calls on one workspace, first filled with garbage, give identical results
-    (the workspace is scratch: every value read is written by the same call first)."""
+    (the workspace is scratch: every value read is written by the same call first), also
+    when the calls alternate between split counts (2000 packed tokens: 4 splits, 700: 2)."""
     w = W.custom(2, n_packed=2000, n_ring=3)
     env, store, ring, q, ws, g1, _ = _decode_case(w, "reuse", b_list=[0])
     qd = to_dev(q, w.in_dtype)
+    q_stored = dev_to_stored(qd).astype(np.float64)
     out = torch.zeros((w.batch, w.hq, w.d), dtype=torch.float32, device="cuda")
     ws.fill_(0x7F)  # large finite floats everywhere
     for _ in range(3):
@@ -454,6 +455,23 @@ def test_decode_workspace_reuse_needs_no_reset(torch):
                                ring.struct(), w.n_ring, 1 / math.sqrt(w.d), out, ws)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy(), g1.astype(np.float32))
+    for n_packed in (700, w.n_packed):
+        tq.tq_decode_attention(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, store.struct(), n_packed,
+                               ring.struct(), w.n_ring, 1 / math.sqrt(w.d), out, ws)
+        torch.cuda.synchronize()
+        if n_packed == w.n_packed:
+            np.testing.assert_array_equal(out.cpu().numpy(), g1.astype(np.float32))
+        else:
+            ref = oracle_decode(env, q_stored, w.hq, w.hkv, store, n_packed, ring, w.n_ring, b_list=[0])
+            assert_decode_close(out.cpu().numpy().astype(np.float64)[:1], ref, f"reuse n_packed={n_packed}")
+
+
+def test_decode_many_splits_per_slice(torch):
+    # the merge of a slice's splits past the partials it loads up front (96: one slice, 137
+    # splits at d = 128), and one slice at d = 256 with two and with eight query heads
+    _decode_case(W.custom(2, batch=1, hq=4, hkv=1, n_packed=70000, n_ring=128), "1 slice d128 70000")
+    _decode_case(W.custom(4, batch=1, hq=2, hkv=1, n_packed=40000, n_ring=128), "1 slice d256 40000")
+    _decode_case(W.custom(4, batch=1, hq=8, hkv=1, n_packed=9000, n_ring=10), "1 slice d256 G=8")
 
 
 def test_append_flush_decode_sequence(torch):
