@@ -211,6 +211,8 @@ def test_decode_d256(torch):
 def test_decode_gqa_groups(torch):
     for hq, hkv in ((8, 8), (16, 8), (64, 8)):
         _decode_case(W.custom(2, hq=hq, hkv=hkv, n_packed=600, n_ring=5), f"G={hq // hkv}")
+    for hq, hkv in ((8, 8), (32, 8)):
+        _decode_case(W.custom(4, batch=1, hq=hq, hkv=hkv, n_packed=600, n_ring=5), f"d256 G={hq // hkv}")
 
 
 def test_decode_ring_only_and_single_token(torch):
