@@ -5,6 +5,7 @@ import math
 import numpy as np
 import pytest
 
+import oracle as O
 import tq_workloads as W
 import compressed_decode_attention_02_amd as tq
 
@@ -474,6 +475,41 @@ def test_decode_many_splits_per_slice(torch):
     _decode_case(W.custom(2, batch=1, hq=4, hkv=1, n_packed=70000, n_ring=128), "1 slice d128 70000")
     _decode_case(W.custom(4, batch=1, hq=2, hkv=1, n_packed=40000, n_ring=128), "1 slice d256 40000")
     _decode_case(W.custom(4, batch=1, hq=8, hkv=1, n_packed=9000, n_ring=10), "1 slice d256 G=8")
+
+
+class _OracleRecords:
+    """The oracle's own packed records of a history, with a PackedStore's tensor shapes (host
+    tensors, read by oracle_decode like a store's)."""
+
+    def __init__(self, torch, env: Env, k, v, n_slices, n_tokens):
+        d, vb = env.d, env.vb
+        kq = O.quantize_keys(k, env.c32, env.b32, env.sigma, env.S)
+        vq = O.quantize_values(v, vb)
+        self.capacity = n_tokens
+        self.key_words = torch.from_numpy(O.pack_keys(kq["idx"], kq["z"]).view(np.int32).reshape(n_slices, n_tokens, d // 8))
+        self.key_norms = torch.from_numpy(np.stack([kq["norm"], kq["rnorm"]], -1).astype(np.float32)
+                                          .reshape(n_slices, n_tokens, 2))
+        self.val_words = torch.from_numpy(O.pack_values(vq["code"], vb).view(np.int32).reshape(n_slices, n_tokens, -1))
+        self.val_scales = torch.from_numpy(vq["scale"].view(np.int16).reshape(n_slices, n_tokens, d // 32))
+
+
+def test_decode_end_to_end_against_oracle_compression(torch):
+    """End to end, each side on its own records: the oracle compresses the history and
+    attends over its own packed bytes, the GPU path compresses and attends over its own (the
+    same ring of exact fp16 tokens).  Codes may differ only within 1e-6 of a decision
+    boundary, so the two outputs meet the decode bar; the error is logged."""
+    cases = ((W.WORKLOADS[1], "tiny"), (W.custom(2, batch=2, n_packed=1500, n_ring=40), "llama-law b2"),
+             (W.custom(4, batch=1, n_packed=600, n_ring=20), "d256 v4"))
+    for w, label in cases:
+        env, store, ring, q, ws, g, _ = _decode_case(w, label + " (GPU records)")
+        n_sl = w.batch * w.hkv
+        (k, v), _ = W.host_kv(w, 0, w.n_packed + w.n_ring)
+        k = k.reshape(n_sl, -1, w.d)[:, :w.n_packed].reshape(-1, w.d).astype(np.float64)
+        v = v.reshape(n_sl, -1, w.d)[:, :w.n_packed].reshape(-1, w.d).astype(np.float64)
+        recs = _OracleRecords(torch, env, k, v, n_sl, w.n_packed)
+        q_stored = dev_to_stored(to_dev(q, w.in_dtype)).astype(np.float64)
+        ref = oracle_decode(env, q_stored, w.hq, w.hkv, recs, w.n_packed, ring, w.n_ring, b_list=range(w.batch))
+        assert_decode_close(g, ref, label + " end to end (oracle records)")
 
 
 def test_append_flush_decode_sequence(torch):
