@@ -18,7 +18,7 @@ EXPORTS = [
     "tq_build_codebook", "tq_build_rotation", "tq_tables_bytes", "tq_build_tables", "tq_tables_view",
     "tq_packed_bytes_per_token", "tq_quantize_kv", "tq_append_ring", "tq_flush",
     "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_attention_ragged", "tq_decode_step",
-    "tq_status_string",
+    "tq_status_string", "tq_rotate", "tq_decode_scores",
 ]
 
 
@@ -80,6 +80,8 @@ def _lib():
         "tq_decode_step": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, K, ctypes.POINTER(I64), R,
                                           ctypes.POINTER(I32), P, P, ctypes.c_int, F, P, P, SZ, P]),
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "tq_rotate": (ctypes.c_int, [C, T, P, ctypes.c_int, I64, P, P]),
+        "tq_decode_scores": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, K, I64, R, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -267,6 +269,23 @@ def tq_decode_attention(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv
         ctypes.byref(ring) if ring is not None else None, n_ring, ctypes.c_float(softmax_scale), _ptr(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("tq_decode_attention", st)
+
+
+def tq_rotate(cfg, tables: Tables, x, n_rows: int, out, stream=None):
+    """Test hook: out = Pi x for n_rows rows (out: fp32 device tensor [n_rows][d])."""
+    st = _lib().tq_rotate(ctypes.byref(cfg), ctypes.byref(tables.view), _ptr(x), _dtype_code(x), n_rows, _ptr(out),
+                          _stream(stream))
+    _check("tq_rotate", st)
+
+
+def tq_decode_scores(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv_heads: int, packed: tq_packed | None,
+                     n_packed: int, ring: tq_ring | None, n_ring: int, scores, stream=None):
+    """Test hook: raw pre-softmax scores [batch][n_q_heads][n_packed + n_ring] (fp32 device tensor)."""
+    st = _lib().tq_decode_scores(
+        ctypes.byref(cfg), ctypes.byref(tables.view), _ptr(q), _dtype_code(q), batch, n_q_heads, n_kv_heads,
+        ctypes.byref(packed) if packed is not None else None, n_packed,
+        ctypes.byref(ring) if ring is not None else None, n_ring, _ptr(scores), _stream(stream))
+    _check("tq_decode_scores", st)
 
 
 def tq_decode_attention_ragged(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv_heads: int,

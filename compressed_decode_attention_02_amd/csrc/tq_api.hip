@@ -7,6 +7,7 @@
 
 #include "tq.h"
 #include "tq_internal.h"
+#include "tq_hooks.h"
 
 namespace {
 
@@ -333,4 +334,60 @@ extern "C" tq_status tq_decode_step(const tq_config *cfg, const tq_tables *table
     *n_packed = np;
     *n_ring = nr + 1;
     return TQ_OK;
+}
+
+// ------------------------------------------------------------------ test hooks
+extern "C" tq_status tq_rotate(const tq_config *cfg, const tq_tables *tables, const void *x, tq_dtype in_dtype,
+                               int64_t n_rows, float *out, void *stream) {
+    if (!cfg) return TQ_ERR_INVALID_ARG;
+    tq_status st = tq::check_config(*cfg);
+    if (st != TQ_OK) return st;
+    if (!tables_ok(tables) || n_rows < 0 || (in_dtype != TQ_F32 && in_dtype != TQ_BF16 && in_dtype != TQ_F16))
+        return TQ_ERR_INVALID_ARG;
+    if (n_rows > 0 && (!x || !out || !aligned16(x) || !aligned16(out))) return TQ_ERR_INVALID_ARG;
+    if ((n_rows + 3) / 4 > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
+    return hip_status(tq::launch_rotate(cfg->head_dim, tables->sign_bits, x, (int)in_dtype, n_rows, out,
+                                        (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_decode_scores(const tq_config *cfg, const tq_tables *tables, const void *q, tq_dtype q_dtype,
+                                      int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *packed,
+                                      int64_t n_packed, const tq_ring *ring, int32_t n_ring, float *scores,
+                                      void *stream) {
+    if (!cfg) return TQ_ERR_INVALID_ARG;
+    tq_status st = tq::check_config(*cfg);
+    if (st != TQ_OK) return st;
+    if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0 || n_packed < 0 ||
+        n_ring < 0 || n_ring > cfg->buffer_size)
+        return TQ_ERR_INVALID_ARG;
+    if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_ERR_INVALID_ARG;
+    if ((int64_t)batch * n_q_heads > 65535) return TQ_ERR_UNSUPPORTED;
+    if (!tables_ok(tables) || !q || !scores || !aligned16(q) || !aligned16(scores)) return TQ_ERR_INVALID_ARG;
+    if (n_packed > 0 && (!packed_ok(packed) || n_packed > packed->capacity)) return TQ_ERR_INVALID_ARG;
+    if (n_ring > 0 && (!ring || !ring->k || !aligned16(ring->k))) return TQ_ERR_INVALID_ARG;
+    if ((n_packed + n_ring + 255) / 256 > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
+    tq::ScoreArgs a{};
+    a.q = q;
+    a.q_dtype = (int)q_dtype;
+    a.batch = batch;
+    a.hq = n_q_heads;
+    a.hkv = n_kv_heads;
+    if (n_packed > 0) {
+        a.kw = packed->key_words;
+        a.kn = packed->key_norms;
+        a.cap = packed->capacity;
+        a.bt = packed->block_table;
+        a.pt = packed->block_table ? packed->page_tokens : 1;
+        a.pps = packed->block_table ? packed->pages_per_slice : 0;
+        a.n_pages = packed->block_table ? packed->n_pages : 0;
+    }
+    a.n_packed = n_packed;
+    a.rk = n_ring > 0 ? ring->k : nullptr;
+    a.buffer_size = cfg->buffer_size;
+    a.n_ring = n_ring;
+    a.centroids = tables->centroids;
+    a.sign_bits = tables->sign_bits;
+    a.S = tables->qjl_S;
+    a.scores = scores;
+    return hip_status(tq::launch_scores(cfg->head_dim, a, (hipStream_t)stream));
 }

@@ -205,6 +205,24 @@ tq_status tq_decode_step(const tq_config *cfg, const tq_tables *tables, const vo
 
 const char *tq_status_string(tq_status s);
 
+/* ------------------------------------------------------------------ test hooks
+ * Unstable entry points for checking the method's steps one at a time; plain kernels, off
+ * the decode path.  Device pointers, 16-byte aligned; same errors as the calls above. */
+
+/* out = Pi x for n_rows rows of head_dim values (guide section 二 step 1: Pi = H diag(sigma)
+ * / sqrt(d)); x [n_rows][d] in in_dtype, out [n_rows][d] fp32. */
+tq_status tq_rotate(const tq_config *cfg, const tq_tables *tables, const void *x, tq_dtype in_dtype,
+                    int64_t n_rows, float *out, void *stream);
+
+/* The raw scores of a decode call before the softmax and its scale, scores [batch]
+ * [n_q_heads][n_packed + n_ring] fp32: packed tokens first, by the estimate of guide section
+ * 二 (|k| (q'.c[idx] + gamma sqrt(pi/2)/d w.(2z - 1)), q' = Pi q, w = S q'), then the ring's
+ * tokens by q.k over the exact fp16 keys (guide 5.1 item 2).  Arguments as
+ * tq_decode_attention; no workspace. */
+tq_status tq_decode_scores(const tq_config *cfg, const tq_tables *tables, const void *q, tq_dtype q_dtype,
+                           int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *packed,
+                           int64_t n_packed, const tq_ring *ring, int32_t n_ring, float *scores, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -512,6 +512,62 @@ def test_decode_end_to_end_against_oracle_compression(torch):
         assert_decode_close(g, ref, label + " end to end (oracle records)")
 
 
+def test_rotate_hook(torch):
+    """Pi x on the device against the oracle's rotation (dense Sylvester matrix), at both
+    head sizes, for fp32 and bf16 rows: relative error <= 1e-6 per row, and |Pi x| = |x|."""
+    for d in (128, 256):
+        env = Env(d, 4)
+        x = np.random.default_rng(11).standard_normal((37, d)).astype(np.float32)
+        x[3] = 0.0
+        for dt in ("f32", "bf16"):
+            xd = to_dev(x, dt)
+            xs = dev_to_stored(xd).astype(np.float64)
+            out = torch.zeros((37, d), dtype=torch.float32, device="cuda")
+            tq.tq_rotate(env.cfg, env.tables, xd, 37, out)
+            torch.cuda.synchronize()
+            g = out.cpu().numpy().astype(np.float64)
+            ref = O.rotate(env.sigma, xs)
+            err = np.abs(g - ref).max(axis=1) / np.maximum(np.abs(ref).max(axis=1), 1e-30)
+            log(f"rotate d={d} {dt}: max rel err {err.max():.3e}")
+            assert err.max() <= 1e-6 and not g[3].any()
+            nrm = np.linalg.norm(xs, axis=1)
+            assert np.allclose(np.linalg.norm(g, axis=1), nrm, rtol=1e-6, atol=0)
+
+
+def test_decode_scores_hook(torch):
+    """Raw pre-softmax scores on the device against the oracle's, on the same packed bytes and
+    ring: packed tokens (the estimator) and ring tokens (exact products), both head sizes,
+    GQA, a paged store.  Per (batch, head): max |s - s*| / max |s*| <= 1e-5."""
+    cases = ((W.custom(2, batch=2, n_packed=700, n_ring=40), "d128 b2"),
+             (W.custom(4, batch=1, hq=8, hkv=2, n_packed=300, n_ring=20), "d256 G=4"))
+    for w, label in cases:
+        env, store, ring, q, ws, g, _ = _decode_case(w, label)
+        qd = to_dev(q, w.in_dtype)
+        q_stored = dev_to_stored(qd).astype(np.float64)
+        T = w.n_packed + w.n_ring
+        sc = torch.zeros((w.batch, w.hq, T), dtype=torch.float32, device="cuda")
+        tq.tq_decode_scores(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, store.struct(), w.n_packed,
+                            ring.struct(), w.n_ring, sc)
+        torch.cuda.synchronize()
+        got = sc.cpu().numpy().astype(np.float64)
+        P = packed_to_np(store)
+        ref_all = []
+        for b in range(w.batch):
+            sl = slice(b * w.hkv, (b + 1) * w.hkv)
+            _, ref = O.decode(d=w.d, kb=3, vb=w.value_bits, c32=env.c32, sigma=env.sigma, S_bits=env.S, B=1, Hq=w.hq,
+                              Hkv=w.hkv, kw=P["kw"][sl], kn=P["kn"][sl], vw=P["vw"][sl], vs=P["vs"][sl],
+                              cap=store.capacity, n_packed=w.n_packed,
+                              rk=ring.k[sl].cpu().numpy().view(np.uint16), rv=ring.v[sl].cpu().numpy().view(np.uint16),
+                              buf=ring.k.shape[1], n_ring=w.n_ring, q=q_stored[b:b + 1], scale=1.0 / math.sqrt(w.d),
+                              want_scores=True)
+            ref_all.append(ref[0])
+        ref = np.stack(ref_all)
+        err = np.abs(got - ref).max(axis=-1) / np.maximum(np.abs(ref).max(axis=-1), 1e-30)
+        log(f"{label}: scores max rel err {err.max():.3e} (packed {np.abs(got - ref)[..., :w.n_packed].max():.3e}, "
+            f"ring {np.abs(got - ref)[..., w.n_packed:].max():.3e} abs)")
+        assert err.max() <= 1e-5, f"{label}: score rel err {err.max()}"
+
+
 def test_append_flush_decode_sequence(torch):
     """History + ring decode, then flush the ring and decode again over packed only."""
     w = W.custom(3, batch=2, n_packed=500, n_ring=64)

@@ -220,3 +220,32 @@ def test_paged_store_errors():
     assert q(n_pages=0) == B.TQ_ERR_INVALID_ARG
     assert q(table=FAKE + 2) == B.TQ_ERR_INVALID_ARG          # int32 table: 4-byte aligned
 
+
+
+def test_test_hook_errors():
+    # every case fails validation, so nothing is launched
+    cfg = tq.make_config()
+    L = tq.lib()
+    T, P, R = _fake_tables(), _fake_packed(cap=4096), B.tq_ring(FAKE, FAKE)
+    assert L.tq_rotate(None, ctypes.byref(T), FAKE, B.TQ_F32, 4, FAKE, None) == B.TQ_ERR_INVALID_ARG
+    assert L.tq_rotate(ctypes.byref(cfg), None, FAKE, B.TQ_F32, 4, FAKE, None) == B.TQ_ERR_INVALID_ARG
+    assert L.tq_rotate(ctypes.byref(cfg), ctypes.byref(T), FAKE, 7, 4, FAKE, None) == B.TQ_ERR_INVALID_ARG
+    assert L.tq_rotate(ctypes.byref(cfg), ctypes.byref(T), FAKE, B.TQ_F32, -1, FAKE, None) == B.TQ_ERR_INVALID_ARG
+    assert L.tq_rotate(ctypes.byref(cfg), ctypes.byref(T), FAKE + 4, B.TQ_F32, 4, FAKE, None) == B.TQ_ERR_INVALID_ARG
+    assert L.tq_rotate(ctypes.byref(cfg), ctypes.byref(T), FAKE, B.TQ_F32, 4, None, None) == B.TQ_ERR_INVALID_ARG
+    bad = tq.make_config(576)
+    assert L.tq_rotate(ctypes.byref(bad), ctypes.byref(T), FAKE, B.TQ_F32, 4, FAKE, None) == B.TQ_ERR_UNSUPPORTED
+
+    def scores(hq=8, hkv=2, n_packed=100, n_ring=5, out=FAKE, packed=P, q=FAKE):
+        return L.tq_decode_scores(ctypes.byref(cfg), ctypes.byref(T), q, B.TQ_BF16, 2, hq, hkv,
+                                  ctypes.byref(packed) if packed is not None else None, n_packed,
+                                  ctypes.byref(R), n_ring, out, None)
+    assert scores(hq=8, hkv=3) == B.TQ_ERR_INVALID_ARG
+    assert scores(n_ring=129) == B.TQ_ERR_INVALID_ARG
+    assert scores(n_packed=-1) == B.TQ_ERR_INVALID_ARG
+    assert scores(n_packed=4097) == B.TQ_ERR_INVALID_ARG    # beyond the store's capacity
+    assert scores(packed=None) == B.TQ_ERR_INVALID_ARG
+    assert scores(out=None) == B.TQ_ERR_INVALID_ARG
+    assert scores(out=FAKE + 4) == B.TQ_ERR_INVALID_ARG
+    assert scores(q=None) == B.TQ_ERR_INVALID_ARG
+    assert scores(hq=40000, hkv=1) == B.TQ_ERR_UNSUPPORTED  # batch * heads above the grid's y limit
