@@ -138,8 +138,9 @@ def codebook(d: int, kb: int):
 
 
 def stored_codebook(d: int, kb: int):
-    """The table values the method stores and uses: centroids rounded to fp16, boundaries
-    the exact midpoints of adjacent stored centroids (both returned as doubles)."""
+    """The table values the library stores and uses (a storage format choice, not a reading
+    of the pages): centroids rounded to fp16, boundaries the exact midpoints of adjacent
+    stored centroids (both returned as doubles)."""
     c = np.zeros(1 << kb, np.float64)
     b = np.zeros((1 << kb) - 1, np.float64)
     if lib().orc_stored_codebook(d, kb, c, b) < 0:

@@ -25,8 +25,13 @@
  *   vector in R^d, whose law is (t+1)/2 ~ Beta((d-1)/2, (d-1)/2);
  *   QJL matrix S: d x d, N(0,1) entries rounded to fp16, drawn from a splitmix64
  *   counter stream through Box-Muller; estimator constant sqrt(pi/2)/d;
- *   value quantiser: bin-centre symmetric, scale fp16(max|v| / 2^(vb-1));
- *   stored codebook: centroids rounded to fp16, boundaries their exact midpoints.
+ *   value quantiser: bin-centre symmetric, scale fp16(max|v| / 2^(vb-1)).
+ *
+ * Format choice of the library (not a reading of the pages, which fix no table
+ * precision): the stored codebook holds each Lloyd-Max centroid rounded to binary16 and
+ * each decision boundary at the exact midpoint of its two stored centroids.  Its cost is
+ * pinned by the tests: d times the mean squared error of the stored table stays within
+ * 1e-5 (relative) of the fp64 optimum's at d = 64, 128 and 256 for 1 to 4 bits.
  *
  * Everything here runs in double precision on inputs already rounded to their stored
  * type.  No blocking, fusion or reordering: every quantity is computed from its
@@ -35,7 +40,6 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
-#include <string.h>
 
 /* ------------------------------------------------------------------------------ */
 /* IEEE binary16 <-> double, written from the format's definition (1 sign bit,     */
@@ -81,15 +85,6 @@ uint16_t orc_double_to_f16(double x)
     int e_field = ex2 - 1 + 15;
     int frac = (int)ldexp(m2 * 2.0 - 1.0, 10);
     return sign | (uint16_t)(e_field << 10) | (uint16_t)frac;
-}
-
-/* bfloat16 -> double: the upper 16 bits of an IEEE binary32 */
-double orc_bf16_to_double(uint16_t h)
-{
-    uint32_t u = (uint32_t)h << 16;
-    float f;
-    memcpy(&f, &u, 4);
-    return (double)f;
 }
 
 /* ------------------------------------------------------------------------------ */
@@ -233,8 +228,8 @@ int orc_codebook(int d, int kb, double *c, double *b)
 }
 
 /*
- * The table values the method stores and uses: each centroid rounded to the nearest
- * binary16 value (the precision of the fp16 KV path), and each decision boundary the
+ * The table values the library stores and uses (its storage format, see the header):
+ * each centroid rounded to the nearest binary16 value, and each decision boundary the
  * exact midpoint of its two stored centroids (representable in binary32).
  */
 int orc_stored_codebook(int d, int kb, double *c_store, double *b_store)

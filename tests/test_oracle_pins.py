@@ -98,6 +98,34 @@ def test_stored_codebook_is_fp16_rounding_with_midpoints(d):
     np.testing.assert_array_equal(bs, bs.astype(np.float32).astype(np.float64))   # exact in fp32
 
 
+def _cell_distortion(d, c, b):
+    """d * sum_i int_{cell i} (t - c_i)^2 f(t) dt for the coordinate law of a uniform unit
+    vector in R^d, cells bounded by b, by scipy quadrature (independent of the oracle)."""
+    p = (d - 1) / 2
+    lognorm = (2 * p - 1) * math.log(2) + scipy.special.betaln(p, p)
+    edges = [-1.0] + list(b) + [1.0]
+    tot = 0.0
+    for i in range(len(c)):
+        f = lambda t, ci=c[i]: (t - ci) ** 2 * math.exp((p - 1) * math.log1p(-t * t) - lognorm)
+        v, _ = scipy.integrate.quad(f, edges[i], edges[i + 1], epsabs=1e-20, epsrel=1e-13, limit=400)
+        tot += v
+    return d * tot
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("kb", [1, 2, 3, 4])
+def test_stored_table_distortion_cost(d, kb):
+    """The stored table (binary16 centroids, boundaries at their midpoints) is the library's
+    storage format, not a reading of the pages.  Its cost: d * MSE of the stored table is at
+    least the fp64 Lloyd-Max optimum's (which minimises it) and within 1e-5 of it (relative;
+    measured at most 3.3e-6)."""
+    c, b, _ = O.codebook(d, kb)
+    cs, bs = O.stored_codebook(d, kb)
+    opt, st = _cell_distortion(d, c, b), _cell_distortion(d, cs, bs)
+    assert st >= opt * (1 - 1e-9)
+    assert st <= opt * (1 + 1e-5), (d, kb, opt, st)
+
+
 # ------------------------------------------------------------------------- fp16 / tables
 
 def test_f16_decode_matches_numpy_for_every_pattern():
@@ -187,6 +215,91 @@ def test_key_encode_invariants(d):
     Sd = O.f16_bits_fast(S)
     p = (u - chat) @ Sd.T
     np.testing.assert_array_equal(r["z"], (p >= 0).astype(np.uint8))
+
+
+def _rotate_numpy(sigma, k):
+    """Pi k with Pi = H diag(sigma) / sqrt(d), H from scipy (not the oracle's rotation)."""
+    d = sigma.shape[0]
+    H = scipy.linalg.hadamard(d).astype(np.float64)
+    return (np.asarray(k, np.float64) * sigma.astype(np.float64)) @ H.T / math.sqrt(d)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_key_margins_against_numpy(d):
+    """u_margin (distance of the unit rotated key to the nearest stored boundary) and p_margin
+    (|S r|) decide which GPU/oracle differences the parity window forgives; both recomputed
+    with scipy's Hadamard matrix and numpy's fp16 decode of S."""
+    c32, b32 = O.stored_codebook(d, 3)
+    sigma, S = O.tables(d, W.TABLE_SEED)
+    k = _keys(d, 48, seed=21)
+    r = O.quantize_keys(k, c32, b32, sigma, S)
+    u = _rotate_numpy(sigma, k) / np.linalg.norm(k, axis=1)[:, None]
+    um = np.abs(u[:, :, None] - b32[None, None, :]).min(-1)
+    np.testing.assert_allclose(r["u_margin"], um, rtol=0, atol=1e-15)
+    idx = np.searchsorted(b32, u, side="left")          # #{i : b_i < u}
+    np.testing.assert_array_equal(r["idx"], idx)
+    Sd = S.view(np.float16).astype(np.float64)
+    p = (u - c32[idx]) @ Sd.T
+    np.testing.assert_allclose(r["p_margin"], np.abs(p), rtol=1e-11, atol=1e-15)
+    np.testing.assert_array_equal(r["z"], (p >= 0).astype(np.uint8))
+
+
+def test_key_margins_hand_built_rows():
+    """Unit keys with coordinates placed at chosen distances from the stored boundaries (the
+    key is Pi^T u, so the rotation returns u): the margins are those distances."""
+    d = 128
+    c32, b32 = O.stored_codebook(d, 3)
+    sigma, S = O.tables(d, W.TABLE_SEED)
+    rng = np.random.default_rng(7)
+    u = c32[rng.integers(0, 8, d)]                      # centroids: far from every boundary
+    placed = {0: (b32[4], 3e-7), 1: (b32[5], -2e-6), 2: (b32[1], 5e-5), 3: (b32[6], -1e-6)}
+    for j, (bb, delta) in placed.items():
+        u[j] = 0.0
+    rest = np.ones(d, bool)
+    rest[list(placed)] = False
+    target = 1.0 - sum((bb + delta) ** 2 for bb, delta in placed.values())
+    u[rest] *= math.sqrt(target / (u[rest] ** 2).sum())
+    for j, (bb, delta) in placed.items():
+        u[j] = bb + delta
+    assert abs(np.linalg.norm(u) - 1) < 1e-15
+    far = np.abs(u[rest][:, None] - b32[None, :]).min(-1)
+    assert far.min() > 1e-4
+    H = scipy.linalg.hadamard(d).astype(np.float64)
+    k = (sigma * (H @ u) / math.sqrt(d)) * 3.7            # Pi^T u = diag(sigma) H u / sqrt(d)
+    r = O.quantize_keys(k[None], c32, b32, sigma, S)
+    for j, (bb, delta) in placed.items():
+        assert abs(r["u_margin"][0, j] - abs(delta)) < 1e-14, (j, r["u_margin"][0, j], delta)
+    np.testing.assert_allclose(r["u_margin"][0, rest], far, rtol=0, atol=1e-14)
+    assert r["idx"][0, 0] == 5 and r["idx"][0, 1] == 5 and r["idx"][0, 2] == 2 and r["idx"][0, 3] == 6
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_force_idx_rederives_the_row(d):
+    """A code chosen inside the rounding window changes the residual and with it every sign
+    bit of the row: with force_idx the oracle keeps the given codes and recomputes gamma, the
+    signs and |S r| from them (checked against numpy); the unforced rows are unchanged."""
+    c32, b32 = O.stored_codebook(d, 3)
+    sigma, S = O.tables(d, W.TABLE_SEED)
+    k = _keys(d, 6, seed=33)
+    base = O.quantize_keys(k, c32, b32, sigma, S)
+    forced = base["idx"].copy()
+    forced[1, 5] = min(7, forced[1, 5] + 1)
+    forced[1, 40] = max(0, forced[1, 40] - 1)
+    forced[4, 17] = 7 - forced[4, 17]
+    assert (forced != base["idx"]).sum() == 3
+    r = O.quantize_keys(k, c32, b32, sigma, S, force_idx=forced)
+    np.testing.assert_array_equal(r["idx"], forced)
+    u = _rotate_numpy(sigma, k) / np.linalg.norm(k, axis=1)[:, None]
+    res = u - c32[forced]
+    np.testing.assert_allclose(r["rnorm"], np.linalg.norm(res, axis=1), rtol=1e-12)
+    p = res @ S.view(np.float16).astype(np.float64).T
+    np.testing.assert_array_equal(r["z"], (p >= 0).astype(np.uint8))
+    np.testing.assert_allclose(r["p_margin"], np.abs(p), rtol=1e-11, atol=1e-15)
+    np.testing.assert_array_equal(r["u_margin"], base["u_margin"])
+    for row in (0, 2, 3, 5):
+        for key in ("z", "rnorm", "p_margin"):
+            np.testing.assert_array_equal(r[key][row], base[key][row])
+    assert (r["z"][1] != base["z"][1]).any() and (r["z"][4] != base["z"][4]).any()
 
 
 @pytest.mark.parametrize("d", [128, 256])
