@@ -1,18 +1,28 @@
 """Benchmark of the TurboQuant KV hot path on one MI355X.
 
+Workload (default): the 32-layer Llama-3.1-8B-shaped stack, batch 4, 32 q / 8 kv heads,
+head_dim 128, 32768-token context quantised from bf16 (3-bit keys + QJL, 2-bit values), then
+one decode step over all 32 layers.
+
 One step = one pass of the whole path over one batch of synthetic input:
   1. tq_quantize_kv   -- compress the prefill history (Q1-Q6) of every (layer, batch, kv head)
   2. tq_decode_step   -- per layer: one decode-time token per slice into the exact ring (R1,
                          inside the decode kernel) and hybrid attention over packed history +
                          ring (D1-D5)
   3. tq_flush         -- compress the ring contents into the packed store (R2)
-value = context KV-tokens (batch * layers * (packed + ring)) per second of step time.
 
-The K timed steps run back to back with no events inside (wall clock between device
-synchronisations); the per-phase times come from a second pass of K steps with HIP events
-between the phases, on the stream the kernels run on.  Several copies of the inputs and
-stores are cycled so that the working set exceeds the 256 MB Infinity Cache.  Prints one JSON
-line.
+Reported:
+  * value = decode KV-tokens/s: batch * layers * (packed + ring) context tokens per second of
+    decode time (all layers' decode calls), timed back to back over stores that were not
+    written or read within the last 512 MB of traffic (the Infinity Cache holds 256 MB);
+  * quantize tokens/s (the history's batch * layers * tokens per second of tq_quantize_kv),
+    over inputs cycled the same way;
+  * ms_per_step: the whole step (quantize + decode + flush) back to back;
+  * roofline objects for the dominant kernel of the step and for the decode kernel set,
+    achieved = algorithmic bytes per launch / average launch time (HIP events on the stream the
+    kernels run on), with measured HBM traffic from the committed rocprofv3 counter summary;
+  * cpu_baseline: the oracle on a bounded sample, on the host's cores (threads over slices).
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -36,7 +46,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", type=int, default=2, help="workload id (1..5); 2 = Llama-3.1-8B b1 32K")
+    p.add_argument("--config", type=int, default=5,
+                   help="workload id (1..5); 5 = 32 layers x batch 4 x 32K context (the default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--paged", type=int, default=0, metavar="PAGE_TOKENS",
                    help="keep the packed cache in pages of this many tokens (a multiple of 32), in a "
@@ -114,11 +125,17 @@ def main():
     rec = tq.tq_packed_bytes_per_token(cfg)
     in_bytes = 2 if w.in_dtype == "bf16" else 4
 
-    # copies cycled through to defeat the MALL (only while a copy is small)
-    step_bytes = n_sl * Tp * (2 * d * in_bytes + rec)
-    n_copies = max(1, min(8, math.ceil(2 * 256e6 / max(step_bytes, 1)) + 1))
-    copies = []
-    for c in range(n_copies):
+    # Working sets: the quantize leg cycles n_in copies of the history K/V and the decode leg
+    # n_dec copies of the packed store (with its ring, queries and outputs), enough that each
+    # leg streams at least 512 MB (twice the 256 MB Infinity Cache) before it touches the same
+    # bytes again.  The large workloads need a single copy.
+    mall2 = 2 * 256 * 10**6
+    in_bytes_all = n_sl * Tp * 2 * d * in_bytes
+    dec_bytes_all = n_sl * ((Tp + w.n_ring) * rec)
+    n_in = max(1, math.ceil(mall2 / in_bytes_all))
+    n_dec = max(1, math.ceil(mall2 / max(dec_bytes_all, 1)))
+    inputs = []
+    for c in range(n_in):
         ks, vs = [], []
         for layer in range(L):
             k, v = W.device_kv(w, layer + 1000 * c, Tp, dev)
@@ -127,32 +144,39 @@ def main():
         K = torch.cat(ks).contiguous() if L > 1 else ks[0]
         V = torch.cat(vs).contiguous() if L > 1 else vs[0]
         del ks, vs
+        inputs.append((K, V))
+    kn, vn = W.device_kv(w, 7777, 1, dev, tensor_ids=(3, 4))
+    kn = kn.reshape(n_sl_layer, d).repeat(L, 1).contiguous()
+    vn = vn.reshape(n_sl_layer, d).repeat(L, 1).contiguous()
+    copies = []
+    for c in range(n_dec):
         if args.paged:
             pps = -(-(Tp + w.buffer_size) // args.paged)
             store = tq.PagedStore(cfg, n_sl, args.paged, pps, n_sl * pps, seed=c, device=dev)
         else:
             store = tq.PackedStore(cfg, n_sl, Tp + w.buffer_size, device=dev)
         ring = tq.Ring(cfg, n_sl, device=dev)
-        kn, vn = W.device_kv(w, 7777 + c, 1, dev, tensor_ids=(3, 4))
-        kn = kn.reshape(n_sl_layer, d).repeat(L, 1).contiguous()
-        vn = vn.reshape(n_sl_layer, d).repeat(L, 1).contiguous()
         qs = [W.device_queries(w, layer + 1000 * c, dev) for layer in range(L)]
         outs = [torch.zeros((B, hq, d), dtype=torch.float32, device=dev) for _ in range(L)]
         ws = tq.new_workspace(cfg, B, hq, hkv, Tp + w.buffer_size, device=dev)
         # pre-fill ring slots [0, ring_fill) so that the step's append brings it to n_ring tokens
         for t in range(ring_fill):
             tq.tq_append_ring(cfg, ring.struct(), kn, vn, n_sl, t)
-        copies.append(dict(K=K, V=V, store=store, ring=ring, kn=kn, vn=vn, qs=qs, outs=outs, ws=ws))
+        # the history of every store copy, compressed once (the decode leg reads it)
+        K, V = inputs[c % n_in]
+        tq.tq_quantize_kv(cfg, tables, K, V, n_sl, Tp, store.struct(), 0)
+        copies.append(dict(store=store, ring=ring, qs=qs, outs=outs, ws=ws))
     torch.cuda.synchronize()
     scale = 1.0 / math.sqrt(d)
     stream = torch.cuda.current_stream()
 
-    def step(c, ev=None):
-        cp = copies[c]
+    def quantize(i):
+        K, V = inputs[i % n_in]
+        tq.tq_quantize_kv(cfg, tables, K, V, n_sl, Tp, copies[i % n_dec]["store"].struct(), 0)
+
+    def decode_all_layers(i):
+        cp = copies[i % n_dec]
         st, rg = cp["store"], cp["ring"]
-        if ev: ev[0].record(stream)
-        tq.tq_quantize_kv(cfg, tables, cp["K"], cp["V"], n_sl, Tp, st.struct(), 0)
-        if ev: ev[1].record(stream)
         for layer in range(L):
             off = layer * n_sl_layer
             if w.n_ring > 0:
@@ -160,42 +184,61 @@ def main():
                 # decode kernel), then attention over packed + ring
                 lo, hi = off, off + n_sl_layer
                 tq.tq_decode_step(cfg, tables, cp["qs"][layer], B, hq, hkv, st.struct(off), Tp, rg.struct(off),
-                                  ring_fill, cp["kn"][lo:hi], cp["vn"][lo:hi], scale, cp["outs"][layer], cp["ws"])
+                                  ring_fill, kn[lo:hi], vn[lo:hi], scale, cp["outs"][layer], cp["ws"])
             else:
                 tq.tq_decode_attention(cfg, tables, cp["qs"][layer], B, hq, hkv, st.struct(off), Tp,
                                        None, 0, scale, cp["outs"][layer], cp["ws"])
-        if ev: ev[2].record(stream)
+
+    def flush(i):
         if w.n_ring > 0:
-            tq.tq_flush(cfg, tables, rg.struct(), n_sl, w.n_ring, st.struct(), Tp)
-        if ev: ev[3].record(stream)
+            cp = copies[i % n_dec]
+            tq.tq_flush(cfg, tables, cp["ring"].struct(), n_sl, w.n_ring, cp["store"].struct(), Tp)
+
+    def step(i):
+        quantize(i)
+        decode_all_layers(i)
+        flush(i)
+
+    def back_to_back(fn, k):
+        """Mean ms of fn(i), k calls back to back with no events between them."""
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(k):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / k
+
+    def per_call(fn, k):
+        """Per-call ms from HIP events recorded around each call on the kernels' stream (an
+        event between two launches adds a few microseconds of idle time)."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+        torch.cuda.synchronize()
+        for i in range(k):
+            evs[i][0].record(stream)
+            fn(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
 
     for i in range(args.warmup):
-        step(i % n_copies)
+        step(i)
     torch.cuda.synchronize()
 
     if args.ragged:
-        ragged(args, w, cfg, tables, copies, n_copies, scale, rec, in_bytes)
+        ragged(args, w, cfg, tables, copies, n_dec, scale, rec, in_bytes, kn, vn)
         return
 
-    # timed steps: no events inside (an event between kernels leaves the GPU idle for a few
-    # microseconds), bracketed by device synchronisation
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i % n_copies)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # per-phase breakdown from a second pass of the same steps, HIP events between the phases
-    # on the stream the kernels run on
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i % n_copies, evs[i])
-    torch.cuda.synchronize()
-    q_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    d_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    f_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    ms_step = wall * 1e3 / args.steps
+    K_ = args.steps
+    ms_step = back_to_back(step, K_)
+    ms_dec = back_to_back(decode_all_layers, K_)
+    ms_q = back_to_back(quantize, K_)
+    dec_calls = per_call(decode_all_layers, K_)
+    q_calls = per_call(quantize, K_)
+    f_calls = per_call(flush, K_) if w.n_ring > 0 else [0.0]
+
+    def pct(xs, p):
+        xs = sorted(xs)
+        return xs[min(len(xs) - 1, max(0, int(round(p / 100 * (len(xs) - 1)))))]
 
     ctx = Tp + w.n_ring
     kv_tokens = B * L * ctx
@@ -204,28 +247,25 @@ def main():
     # input instead and written to the ring once), queries in, outputs out
     dec_bytes = L * (n_sl_layer * (Tp * rec + w.n_ring * 4 * d + (2 * d * in_bytes if w.n_ring else 0))
                      + B * hq * d * (in_bytes + 4))
-    q_med, d_med = statistics.median(q_ms), statistics.median(d_ms)
-    q_gbps = q_bytes / (q_med * 1e-3) / 1e9
-    d_gbps = dec_bytes / (d_med * 1e-3) / 1e9
-    dominant = "quantize" if q_med >= d_med else "decode"
-    # decode kernel set: a prep launch only at head_dim 256 (at 128 the main kernel prepares
-    # the queries itself)
+    q_gbps = q_bytes / (ms_q * 1e-3) / 1e9
+    d_gbps = dec_bytes / (ms_dec * 1e-3) / 1e9
     q_kernels = "k_quant_kv"
+    # decode kernel set: a prep launch only at head_dim 256 (at 128 the main kernel prepares
+    # the queries itself); the merge launch only when a slice has several splits
     d_kernels = ("k_decode_prep+" if d == 256 else "") + "k_decode_main+k_decode_merge"
-    roof = {
-        "kernel": q_kernels if dominant == "quantize" else d_kernels,
-        "bound": "hbm",
-        "achieved": round(q_gbps if dominant == "quantize" else d_gbps, 1),
-        "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s",
-        "frac": round((q_gbps if dominant == "quantize" else d_gbps) / HBM_PEAK_GBPS, 4),
-        "traffic": measured_traffic(w.name, q_kernels if dominant == "quantize" else d_kernels),
-        "algorithmic_bytes_per_launch": q_bytes if dominant == "quantize" else dec_bytes // L,
-    }
+    roof_q = {"kernel": q_kernels, "bound": "hbm", "achieved": round(q_gbps, 1), "peak": HBM_PEAK_GBPS,
+              "unit": "GB/s", "frac": round(q_gbps / HBM_PEAK_GBPS, 4),
+              "traffic": measured_traffic(w.name, q_kernels), "algorithmic_bytes_per_launch": q_bytes,
+              "launch_ms_mean": round(ms_q, 4)}
+    roof_d = {"kernel": d_kernels, "bound": "hbm", "achieved": round(d_gbps, 1), "peak": HBM_PEAK_GBPS,
+              "unit": "GB/s", "frac": round(d_gbps / HBM_PEAK_GBPS, 4),
+              "traffic": measured_traffic(w.name, d_kernels), "algorithmic_bytes_per_launch": dec_bytes // L,
+              "launch_ms_mean": round(ms_dec / L, 5)}
+    dominant = roof_q if ms_q >= ms_dec else roof_d
 
     res = {
         "metric": METRIC,
-        "value": round(kv_tokens / (ms_step * 1e-3), 1),
+        "value": round(kv_tokens / (ms_dec * 1e-3), 1),
         "unit": "KV-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -239,28 +279,27 @@ def main():
         "config": {"workload": w.name, "layers": L, "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": d,
                    "packed_tokens": Tp, "ring_tokens": w.n_ring, "key_bits": 3, "qjl_bits": 1,
                    "value_bits": w.value_bits, "group": 32, "parallelism": "none (1 GPU)",
-                   "copies_cycled": n_copies, "paged": args.paged or None},
-        "breakdown_ms_median": {"quantize": round(q_med, 4), "append_and_decode_all_layers": round(d_med, 4),
-                                "flush": round(statistics.median(f_ms), 4)},
-        "quantize_tokens_per_s": round(B * L * Tp / (q_med * 1e-3), 1),
-        "quantize_algorithmic_bytes": q_bytes,
-        "decode_algorithmic_bytes_per_layer": dec_bytes // L,
+                   "input_copies": n_in, "store_copies": n_dec, "paged": args.paged or None},
+        "value_is": "decode KV-tokens/s: batch * layers * (packed + ring) per second of all layers' decode calls",
+        "decode_ms_per_step": {"mean": round(ms_dec, 4), "p10": round(pct(dec_calls, 10), 4),
+                               "p50": round(pct(dec_calls, 50), 4), "p90": round(pct(dec_calls, 90), 4)},
+        "quantize_ms": {"mean": round(ms_q, 4), "p10": round(pct(q_calls, 10), 4),
+                        "p50": round(pct(q_calls, 50), 4), "p90": round(pct(q_calls, 90), 4)},
+        "flush_ms_median": round(statistics.median(f_calls), 4),
+        "step_kv_tokens_per_s": round(kv_tokens / (ms_step * 1e-3), 1),
+        "quantize_tokens_per_s": round(B * L * Tp / (ms_q * 1e-3), 1),
         "quantize_GBps": round(q_gbps, 1),
-        "decode_kv_tokens_per_s": round(kv_tokens / (d_med * 1e-3), 1),
         "decode_GBps": round(d_gbps, 1),
-        "decode_frac_of_hbm_peak": round(d_gbps / HBM_PEAK_GBPS, 4),
-        "roofline": roof,
-        "roofline_decode": {"kernel": d_kernels, "bound": "hbm", "achieved": round(d_gbps, 1),
-                            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(d_gbps / HBM_PEAK_GBPS, 4),
-                            "traffic": measured_traffic(w.name, d_kernels),
-                            "algorithmic_bytes_per_launch": dec_bytes // L},
+        "roofline": dominant,
+        "roofline_quantize": roof_q,
+        "roofline_decode": roof_d,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
     print(json.dumps(res), flush=True)
 
 
-def ragged(args, w, cfg, tables, copies, n_copies, scale, rec, in_bytes):
+def ragged(args, w, cfg, tables, copies, n_copies, scale, rec, in_bytes, kn=None, vn=None):
     """Decode-only timing over a ragged batch (per-sequence lengths on the device), against the
     uniform decode of the same stores at the maxima, HIP events around K back-to-back calls."""
     import numpy as np
@@ -320,10 +359,30 @@ def ragged(args, w, cfg, tables, copies, n_copies, scale, rec, in_bytes):
     }), flush=True)
 
 
+def host_cpu():
+    """(threads to use, logical CPUs seen, CPU model): the pool is sized to the CPUs this
+    process may run on, at most 16 (a one-GPU share of the host)."""
+    n_aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return max(1, min(16, n_aff)), os.cpu_count() or 1, model
+
+
 def cpu_baseline(w, sample_tokens: int):
-    """The oracle (plain C, fp64, one thread) timed on a bounded sample of the same step:
-    quantize `sample_tokens` tokens of every kv head of one layer and one batch element,
-    then decode all q heads of that batch element over those tokens."""
+    """The oracle (plain C, fp64, unchanged) timed on a bounded sample of the same step, with
+    host threads over independent slices (the oracle's C calls release the interpreter lock):
+    quantize `sample_tokens` tokens of every kv head of one layer and one batch element (in
+    chunks of rows), then decode all q heads of that batch element over those tokens (one
+    kv head's query group per task).  value = decode KV-tokens/s of the sample."""
+    import concurrent.futures
+
     import numpy as np
 
     import oracle as O
@@ -333,26 +392,48 @@ def cpu_baseline(w, sample_tokens: int):
     T = min(sample_tokens, w.n_packed)
     ws = W.custom(w.cid, batch=1)
     (k, v), _ = W.host_kv(ws, 0, T)
-    k = k.reshape(ws.hkv, T, d).astype(np.float64)
-    v = v.reshape(ws.hkv, T, d).astype(np.float64)
+    k = k.reshape(ws.hkv * T, d).astype(np.float64)
+    v = v.reshape(ws.hkv * T, d).astype(np.float64)
     q, _ = W.host_queries(ws, 0)
+    q = q.astype(np.float64)
     c32, b32 = O.stored_codebook(d, 3)
     sigma, S = O.tables(d, W.TABLE_SEED)
-    t0 = time.perf_counter()
-    kq = O.quantize_keys(k.reshape(-1, d), c32, b32, sigma, S)
-    vq = O.quantize_values(v.reshape(-1, d), w.value_bits)
-    kw = O.pack_keys(kq["idx"], kq["z"]).reshape(ws.hkv, T, -1)
-    kn = np.stack([kq["norm"], kq["rnorm"]], 1).astype(np.float32).reshape(ws.hkv, T, 2)
-    vw = O.pack_values(vq["code"], w.value_bits).reshape(ws.hkv, T, -1)
-    vs = vq["scale"].reshape(ws.hkv, T, -1)
-    t1 = time.perf_counter()
-    O.decode(d=d, kb=3, vb=w.value_bits, c32=c32, sigma=sigma, S_bits=S, B=1, Hq=ws.hq, Hkv=ws.hkv, kw=kw, kn=kn,
-             vw=vw, vs=vs, cap=T, n_packed=T, rk=None, rv=None, buf=0, n_ring=0, q=q.astype(np.float64),
-             scale=1 / math.sqrt(d))
-    t2 = time.perf_counter()
-    return {"value": round(T / (t2 - t0), 1), "unit": "KV-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"1 layer, batch 1, {ws.hkv} kv heads x {T} tokens quantized, then decode of {ws.hq} q heads "
-                      f"over them (quantize {t1 - t0:.2f} s, decode {t2 - t1:.2f} s, fp64 C, one thread)"}
+    O.lib()
+    threads, ncpu, model = host_cpu()
+    chunk = 1024
+    spans = [(r, min(r + chunk, k.shape[0])) for r in range(0, k.shape[0], chunk)]
+
+    def quant(span):
+        a, b = span
+        kq = O.quantize_keys(k[a:b], c32, b32, sigma, S)
+        vq = O.quantize_values(v[a:b], w.value_bits)
+        return (O.pack_keys(kq["idx"], kq["z"]), np.stack([kq["norm"], kq["rnorm"]], 1).astype(np.float32),
+                O.pack_values(vq["code"], w.value_bits), vq["scale"])
+
+    G = ws.hq // ws.hkv
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        parts = list(ex.map(quant, spans))
+        t1 = time.perf_counter()
+        kw = np.concatenate([p_[0] for p_ in parts]).reshape(ws.hkv, T, -1)
+        kn = np.concatenate([p_[1] for p_ in parts]).reshape(ws.hkv, T, 2)
+        vw = np.concatenate([p_[2] for p_ in parts]).reshape(ws.hkv, T, -1)
+        vs = np.concatenate([p_[3] for p_ in parts]).reshape(ws.hkv, T, -1)
+
+        def dec(h):
+            return O.decode(d=d, kb=3, vb=w.value_bits, c32=c32, sigma=sigma, S_bits=S, B=1, Hq=G, Hkv=1,
+                            kw=kw[h:h + 1], kn=kn[h:h + 1], vw=vw[h:h + 1], vs=vs[h:h + 1], cap=T, n_packed=T,
+                            rk=None, rv=None, buf=0, n_ring=0, q=q[:, h * G:(h + 1) * G], scale=1 / math.sqrt(d))
+
+        t2 = time.perf_counter()
+        list(ex.map(dec, range(ws.hkv)))
+        t3 = time.perf_counter()
+    return {"value": round(T / (t3 - t2), 1), "unit": "KV-tokens/s", "cores": threads, "kind": "oracle",
+            "quantize_tokens_per_s": round(T / (t1 - t0), 1),
+            "host": {"logical_cpus": ncpu, "threads_used": threads, "cpu_model": model},
+            "sample": f"1 layer, batch 1: {ws.hkv} kv heads x {T} tokens quantized ({t1 - t0:.2f} s), then decode "
+                      f"of {ws.hq} q heads over them ({t3 - t2:.2f} s); fp64 C oracle on {threads} threads over "
+                      f"slices (row chunks of {chunk} for the quantize, one kv head's query group per decode task)"}
 
 
 if __name__ == "__main__":

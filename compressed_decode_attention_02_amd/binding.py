@@ -41,7 +41,8 @@ class tq_tables(ctypes.Structure):
 class tq_packed(ctypes.Structure):
     _fields_ = [("key_words", ctypes.c_void_p), ("key_norms", ctypes.c_void_p), ("val_words", ctypes.c_void_p),
                 ("val_scales", ctypes.c_void_p), ("capacity", ctypes.c_int64), ("block_table", ctypes.c_void_p),
-                ("page_tokens", ctypes.c_int32), ("pages_per_slice", ctypes.c_int32), ("n_pages", ctypes.c_int64)]
+                ("page_tokens", ctypes.c_int32), ("pages_per_slice", ctypes.c_int32), ("n_pages", ctypes.c_int64),
+                ("error_flag", ctypes.c_void_p)]
 
 
 class tq_ring(ctypes.Structure):
@@ -113,7 +114,47 @@ def _stream(stream):
 
 def _dtype_code(t) -> int:
     import torch
-    return {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16, torch.float16: TQ_F16}[t.dtype]
+    code = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16, torch.float16: TQ_F16}.get(t.dtype)
+    if code is None:
+        raise ValueError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)")
+    return code
+
+
+def _need(name: str, t, numel: int, dtype=None):
+    """A device tensor argument: contiguous, of dtype `dtype` (if given) and holding at least
+    `numel` elements.  Raises ValueError before anything reaches the library, which would
+    otherwise read or write past the end of a buffer that is too small.  (Where the tensors
+    live is checked by _on_one_gpu once every argument has passed these checks.)"""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, at least {numel} are needed")
+
+
+def _on_one_gpu(*named):
+    """Every given tensor is a GPU tensor, all on the same device."""
+    named = [(n, t) for n, t in named if t is not None]
+    for n, t in named:
+        if t.device.type != "cuda":
+            raise ValueError(f"{n} must be a GPU tensor, got device {t.device}")
+    if len({t.device for _, t in named}) > 1:
+        raise ValueError("tensors on different devices: " + ", ".join(f"{n}={t.device}" for n, t in named))
+
+
+def _kv_pair(k, v, numel: int, kname="k", vname="v"):
+    """k and v of one call: one dtype (the library reads both with it), contiguous, each
+    holding at least numel elements."""
+    if k is None or v is None:
+        raise ValueError(f"{kname} and {vname} are required")
+    if k.dtype != v.dtype:
+        raise ValueError(f"{kname} and {vname} must share a dtype, got {k.dtype} and {v.dtype}")
+    _dtype_code(k)
+    _need(kname, k, numel)
+    _need(vname, v, numel)
 
 
 def make_config(head_dim=128, key_bits=3, value_bits=2, group_size=32, buffer_size=128) -> tq_config:
@@ -181,7 +222,7 @@ class PackedStore:
         """tq_packed view starting at slice `slice_offset` (e.g. one layer of a larger store)."""
         return tq_packed(self.key_words[slice_offset:].data_ptr(), self.key_norms[slice_offset:].data_ptr(),
                          self.val_words[slice_offset:].data_ptr(), self.val_scales[slice_offset:].data_ptr(),
-                         self.capacity, None, 0, 0, 0)
+                         self.capacity, None, 0, 0, 0, None)
 
 
 class PagedStore:
@@ -205,12 +246,22 @@ class PagedStore:
             table = perm.reshape(n_slices, pages_per_slice)
         self.table_np = np.asarray(table, np.int32).reshape(n_slices, pages_per_slice)
         self.block_table = torch.from_numpy(self.table_np.copy()).to(device)
+        # set to 1 by a kernel that meets a table entry outside the pool (never cleared by the library)
+        self.error_flag = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def table_error(self) -> bool:
+        """True when a call since the last clear_table_error() met a table entry outside the
+        pool (synchronises with the device)."""
+        return bool(self.error_flag.item())
+
+    def clear_table_error(self):
+        self.error_flag.zero_()
 
     def struct(self, slice_offset: int = 0) -> tq_packed:
         """tq_packed view of slices slice_offset.. (their block-table rows; the pool is shared)."""
         return tq_packed(self.key_words.data_ptr(), self.key_norms.data_ptr(), self.val_words.data_ptr(),
                          self.val_scales.data_ptr(), self.capacity, self.block_table[slice_offset:].data_ptr(),
-                         self.page_tokens, self.pages_per_slice, self.n_pages)
+                         self.page_tokens, self.pages_per_slice, self.n_pages, self.error_flag.data_ptr())
 
     def gather(self):
         """The store as contiguous [n_slices][capacity][...] arrays (host copies through the table)."""
@@ -238,12 +289,16 @@ class Ring:
 
 def tq_quantize_kv(cfg, tables: Tables, k, v, n_slices: int, n_tokens: int, dst: tq_packed, dst_offset: int,
                    stream=None):
+    _kv_pair(k, v, max(n_slices, 0) * max(n_tokens, 0) * cfg.head_dim)
+    _on_one_gpu(("k", k), ("v", v))
     st = _lib().tq_quantize_kv(ctypes.byref(cfg), ctypes.byref(tables.view), _ptr(k), _ptr(v), _dtype_code(k),
                                n_slices, n_tokens, ctypes.byref(dst), dst_offset, _stream(stream))
     _check("tq_quantize_kv", st)
 
 
 def tq_append_ring(cfg, ring: tq_ring, k_new, v_new, n_slices: int, n_ring: int, stream=None):
+    _kv_pair(k_new, v_new, max(n_slices, 0) * cfg.head_dim, "k_new", "v_new")
+    _on_one_gpu(("k_new", k_new), ("v_new", v_new))
     st = _lib().tq_append_ring(ctypes.byref(cfg), ctypes.byref(ring), _ptr(k_new), _ptr(v_new),
                                _dtype_code(k_new), n_slices, n_ring, _stream(stream))
     _check("tq_append_ring", st)
@@ -260,9 +315,20 @@ def tq_decode_workspace_bytes(cfg, batch: int, n_q_heads: int, n_kv_heads: int, 
     return _lib().tq_decode_workspace_bytes(ctypes.byref(cfg), batch, n_q_heads, n_kv_heads, max_context)
 
 
+def _decode_io(cfg, q, out, workspace, batch: int, n_q_heads: int):
+    import torch
+    n = max(batch, 0) * max(n_q_heads, 0) * cfg.head_dim
+    _dtype_code(q)
+    _need("q", q, n)
+    _need("out", out, n, torch.float32)
+    _need("workspace", workspace, 1)
+
+
 def tq_decode_attention(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv_heads: int,
                         packed: tq_packed | None, n_packed: int, ring: tq_ring | None, n_ring: int,
                         softmax_scale: float, out, workspace, stream=None):
+    _decode_io(cfg, q, out, workspace, batch, n_q_heads)
+    _on_one_gpu(("q", q), ("out", out), ("workspace", workspace))
     st = _lib().tq_decode_attention(
         ctypes.byref(cfg), ctypes.byref(tables.view), _ptr(q), _dtype_code(q), batch, n_q_heads, n_kv_heads,
         ctypes.byref(packed) if packed is not None else None, n_packed,
@@ -273,6 +339,11 @@ def tq_decode_attention(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv
 
 def tq_rotate(cfg, tables: Tables, x, n_rows: int, out, stream=None):
     """Test hook: out = Pi x for n_rows rows (out: fp32 device tensor [n_rows][d])."""
+    import torch
+    _dtype_code(x)
+    _need("x", x, max(n_rows, 0) * cfg.head_dim)
+    _need("out", out, max(n_rows, 0) * cfg.head_dim, torch.float32)
+    _on_one_gpu(("x", x), ("out", out))
     st = _lib().tq_rotate(ctypes.byref(cfg), ctypes.byref(tables.view), _ptr(x), _dtype_code(x), n_rows, _ptr(out),
                           _stream(stream))
     _check("tq_rotate", st)
@@ -281,6 +352,11 @@ def tq_rotate(cfg, tables: Tables, x, n_rows: int, out, stream=None):
 def tq_decode_scores(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv_heads: int, packed: tq_packed | None,
                      n_packed: int, ring: tq_ring | None, n_ring: int, scores, stream=None):
     """Test hook: raw pre-softmax scores [batch][n_q_heads][n_packed + n_ring] (fp32 device tensor)."""
+    import torch
+    _dtype_code(q)
+    _need("q", q, max(batch, 0) * max(n_q_heads, 0) * cfg.head_dim)
+    _need("scores", scores, max(batch, 0) * max(n_q_heads, 0) * max(n_packed + n_ring, 0), torch.float32)
+    _on_one_gpu(("q", q), ("scores", scores))
     st = _lib().tq_decode_scores(
         ctypes.byref(cfg), ctypes.byref(tables.view), _ptr(q), _dtype_code(q), batch, n_q_heads, n_kv_heads,
         ctypes.byref(packed) if packed is not None else None, n_packed,
@@ -294,8 +370,10 @@ def tq_decode_attention_ragged(cfg, tables: Tables, q, batch: int, n_q_heads: in
     """Decode with per-sequence lengths: seq_packed (int64) and seq_ring (int32) are device
     tensors of `batch` entries."""
     import torch
-    if seq_packed.dtype != torch.int64 or seq_ring.dtype != torch.int32:
-        raise ValueError("seq_packed must be int64 and seq_ring int32")
+    _decode_io(cfg, q, out, workspace, batch, n_q_heads)
+    _need("seq_packed", seq_packed, max(batch, 0), torch.int64)
+    _need("seq_ring", seq_ring, max(batch, 0), torch.int32)
+    _on_one_gpu(("q", q), ("out", out), ("workspace", workspace), ("seq_packed", seq_packed), ("seq_ring", seq_ring))
     st = _lib().tq_decode_attention_ragged(
         ctypes.byref(cfg), ctypes.byref(tables.view), _ptr(q), _dtype_code(q), batch, n_q_heads, n_kv_heads,
         ctypes.byref(packed) if packed is not None else None, _ptr(seq_packed), n_packed_max,
@@ -309,8 +387,9 @@ def tq_decode_step(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv_head
                    softmax_scale: float, out, workspace, stream=None):
     """Append k_new / v_new to the ring (flushing a full ring first) and decode, in one call.
     Returns the new (n_packed, n_ring)."""
-    if k_new.dtype != v_new.dtype:
-        raise ValueError("k_new and v_new must share a dtype")
+    _decode_io(cfg, q, out, workspace, batch, n_q_heads)
+    _kv_pair(k_new, v_new, max(batch, 0) * max(n_kv_heads, 0) * cfg.head_dim, "k_new", "v_new")
+    _on_one_gpu(("q", q), ("out", out), ("workspace", workspace), ("k_new", k_new), ("v_new", v_new))
     np_ = ctypes.c_int64(n_packed)
     nr_ = ctypes.c_int32(n_ring)
     st = _lib().tq_decode_step(

@@ -14,6 +14,7 @@ namespace {
 constexpr int64_t kSplitQuantum = 128;     // split sizes are multiples of four 32-token blocks
 constexpr int64_t kMinSplitTokens = 512;   // at least four blocks per wave
 constexpr int64_t kMaxSplits = 256;        // the merge keeps one weight per split in LDS
+constexpr int64_t kMaxContext = (int64_t(1) << 31) - 256;  // decode token indices are 32-bit
 // ring tokens attended to per split, at most (the main kernel's register budget)
 int64_t ring_per_split_max(int d) { return d == 128 ? 64 : 32; }
 
@@ -26,7 +27,8 @@ bool packed_ok(const tq_packed *p) {
         return false;
     if (!p->block_table) return true;
     // paged: whole 32-token blocks per page, the capacity the table covers, a non-empty pool
-    return (reinterpret_cast<uintptr_t>(p->block_table) & 3u) == 0 && p->page_tokens > 0 &&
+    return (reinterpret_cast<uintptr_t>(p->block_table) & 3u) == 0 &&
+           (reinterpret_cast<uintptr_t>(p->error_flag) & 3u) == 0 && p->page_tokens > 0 &&
            p->page_tokens % 32 == 0 && p->pages_per_slice > 0 && p->n_pages > 0 &&
            p->capacity == (int64_t)p->pages_per_slice * p->page_tokens;
 }
@@ -37,6 +39,7 @@ void set_pages(Args &a, const tq_packed *p) {
     a.pt = p->block_table ? p->page_tokens : 1;
     a.pps = p->block_table ? p->pages_per_slice : 0;
     a.n_pages = p->block_table ? p->n_pages : 0;
+    a.err = p->block_table ? p->error_flag : nullptr;
 }
 
 bool tables_ok(const tq_tables *t) {
@@ -213,6 +216,7 @@ tq_status decode_impl(const tq_config *cfg, const tq_tables *tables, const void 
     if (n_packed > 0 && (!packed_ok(packed) || n_packed > packed->capacity)) return TQ_ERR_INVALID_ARG;
     if (n_ring > 0 && (!ring || !ring->k || !ring->v || !aligned16(ring->k) || !aligned16(ring->v)))
         return TQ_ERR_INVALID_ARG;
+    if (n_packed + n_ring >= kMaxContext) return TQ_ERR_UNSUPPORTED;  // 32-bit token indices in the kernels
     const int64_t slices = (int64_t)batch * n_kv_heads;
     // splits of the packed tokens, at least one (an empty context still writes its zeros), and
     // enough for the ring tokens at ring_per_split_max per split; the ring is spread evenly
@@ -365,7 +369,7 @@ extern "C" tq_status tq_decode_scores(const tq_config *cfg, const tq_tables *tab
     if (!tables_ok(tables) || !q || !scores || !aligned16(q) || !aligned16(scores)) return TQ_ERR_INVALID_ARG;
     if (n_packed > 0 && (!packed_ok(packed) || n_packed > packed->capacity)) return TQ_ERR_INVALID_ARG;
     if (n_ring > 0 && (!ring || !ring->k || !aligned16(ring->k))) return TQ_ERR_INVALID_ARG;
-    if ((n_packed + n_ring + 255) / 256 > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
+    if (n_packed + n_ring >= kMaxContext) return TQ_ERR_UNSUPPORTED;
     tq::ScoreArgs a{};
     a.q = q;
     a.q_dtype = (int)q_dtype;
@@ -380,6 +384,7 @@ extern "C" tq_status tq_decode_scores(const tq_config *cfg, const tq_tables *tab
         a.pt = packed->block_table ? packed->page_tokens : 1;
         a.pps = packed->block_table ? packed->pages_per_slice : 0;
         a.n_pages = packed->block_table ? packed->n_pages : 0;
+        a.err = packed->block_table ? packed->error_flag : nullptr;
     }
     a.n_packed = n_packed;
     a.rk = n_ring > 0 ? ring->k : nullptr;

@@ -600,7 +600,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     // one page of a paged store, since pages hold a multiple of 32 tokens)
     // (the same for every lane: made visibly uniform, so the copy bases are scalar values)
     auto block_rec = [&](int t0) -> int64_t {
-        const int64_t r = record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, bk, t0);
+        const int64_t r = record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, a.err, bk, t0);
         return (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)r) |
                ((int64_t)__builtin_amdgcn_readfirstlane((int)(r >> 32)) << 32);
     };

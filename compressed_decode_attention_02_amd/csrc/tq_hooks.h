@@ -18,6 +18,7 @@ struct ScoreArgs {
     const int32_t *bt;
     int pt, pps;
     int64_t n_pages;
+    int32_t *err;
     int64_t n_packed;
     const uint16_t *rk;
     int buffer_size;

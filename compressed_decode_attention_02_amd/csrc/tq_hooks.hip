@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kHookThreads) void k_scores(ScoreArgs a) {
     float s;
     if (t < a.n_packed) {
         // s = |k| (sum_j q'_j c[idx_j] + gamma sqrt(pi/2)/d sum_j w_j (2 z_j - 1))
-        const int64_t rec = record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, sl, t);
+        const int64_t rec = record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, a.err, sl, t);
         const uint32_t *kw = a.kw + rec * (D / 8);
         float mse = 0.f, sgn = 0.f;
         for (int wi = 0; wi < D / 8; ++wi) {

@@ -4,7 +4,7 @@
 #include <cstddef>
 #include <cstdint>
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include "tq.h"
 
@@ -41,6 +41,7 @@ struct QuantArgs {
     const int32_t *bt;
     int pt, pps;
     int64_t n_pages;
+    int32_t *err;  // set to 1 when a table entry lies outside the pool (may be null)
 };
 
 struct DecodeArgs {
@@ -57,6 +58,7 @@ struct DecodeArgs {
     const int32_t *bt;  // paged store, as in QuantArgs
     int pt, pps;
     int64_t n_pages;
+    int32_t *err;
     int64_t n_packed;
     uint16_t *rk;  // ring (written only by a fused step's append)
     uint16_t *rv;
@@ -84,12 +86,17 @@ struct DecodeArgs {
     float *partial_ml;   // [batch*hkv][n_split][G][2]: (m, l) of each split
 };
 
-// record index of token t of slice s (paged or contiguous store; page entries clamped to the pool)
-__host__ __device__ inline int64_t record_index(const int32_t *bt, int pt, int pps, int64_t n_pages, int64_t cap,
-                                                int64_t s, int64_t t) {
+// record index of token t of slice s (paged or contiguous store).  A table entry outside
+// [0, n_pages) is clamped to the pool, so no access leaves it, and reported through *err
+// (set to 1; every writer stores the same value) when err is not null.
+__device__ inline int64_t record_index(const int32_t *bt, int pt, int pps, int64_t n_pages, int64_t cap,
+                                       int32_t *err, int64_t s, int64_t t) {
     if (!bt) return s * cap + t;
     int64_t p = bt[s * pps + t / pt];
-    p = p < 0 ? 0 : (p >= n_pages ? n_pages - 1 : p);
+    if (p < 0 || p >= n_pages) {
+        if (err) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        p = p < 0 ? 0 : n_pages - 1;
+    }
     return p * pt + t % pt;
 }
 

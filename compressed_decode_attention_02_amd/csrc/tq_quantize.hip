@@ -319,7 +319,7 @@ void k_quant_kv(QuantArgs a) {
         if (row < a.n_rows) {
             int64_t sl, t;
             split_row(row, a.n_tokens, inv_tok, sl, t);
-            rec = record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, sl, a.dst_offset + t);
+            rec = record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, a.err, sl, a.dst_offset + t);
         }
 
         // ---- the tile's values: this lane's NV coordinates g NV .. g NV + NV - 1 of its token

@@ -20,6 +20,14 @@
  *     tq_packed.val_scales, which need 8 bytes (TQ_ERR_INVALID_ARG otherwise).
  *   - Supported now: head_dim in {128, 256}, key_bits = 3, value_bits in {2, 4},
  *     group_size = 32, 1 <= buffer_size <= 1024.  Other values give TQ_ERR_UNSUPPORTED.
+ *   - Decode calls address tokens with 32-bit indices: a context (packed + ring tokens) of
+ *     2^31 - 256 tokens or more gives TQ_ERR_UNSUPPORTED.
+ *   - Reproducibility: quantisation is deterministic.  A decode call repeats bit for bit
+ *     when its workgroups have 4 waves; for long contexts at head_dim 128 with up to four
+ *     query heads per kv head it uses one 12-wave workgroup per compute unit whose waves
+ *     take token blocks in arrival order, so the fp32 summation order, and with it the last
+ *     bits of the output, may differ between identical calls (well inside the accuracy of
+ *     the method; the tests bound the spread at 1e-5 relative).
  *   - Non-finite inputs give unspecified output (no device-side scan).
  */
 #ifndef TQ_H
@@ -117,11 +125,17 @@ typedef struct {
      * aligned).  page_tokens must be a multiple of 32 and capacity == pages_per_slice *
      * page_tokens.  Table entries outside [0, n_pages) are clamped on the device, so no entry
      * addresses outside the pool; pages shared by two slices receive both writes (the
-     * caller's table decides which tokens land where). */
+     * caller's table decides which tokens land where).
+     * error_flag (paged stores only; may be NULL): a device int32 (4-byte aligned) that a
+     * kernel sets to 1 when it meets a table entry outside [0, n_pages).  The library never
+     * clears it: the caller zeroes it, and reads it after the calls it covers have finished
+     * (a clamped entry reads or writes another page of the pool, so results of those calls
+     * are then unspecified). */
     const int32_t *block_table;
     int32_t page_tokens;
     int32_t pages_per_slice;
     int64_t n_pages;
+    int32_t *error_flag;
 } tq_packed;
 
 /* Exact recent tokens: fp16 [n_slices][buffer_size][d] keys and values (guide 5.1). */
@@ -130,6 +144,10 @@ typedef struct {
     uint16_t *v;
 } tq_ring;
 
+/* Bytes of one packed record (one token of one kv head) in device memory: the compressed
+ * size that replaces 4 * head_dim bytes of a bf16/fp16 K+V cache (the guide's section 5.2
+ * reports the bytes its free_kv_cache releases; this is the per-token figure behind such a
+ * report).  0 for an unsupported configuration. */
 size_t tq_packed_bytes_per_token(const tq_config *cfg);
 
 /* ------------------------------------------------------------------ device entry points */
@@ -156,9 +174,10 @@ tq_status tq_flush(const tq_config *cfg, const tq_tables *tables, const tq_ring 
                    int32_t n_ring, const tq_packed *dst, int64_t n_packed, void *stream);
 
 /* Workspace (device bytes) needed by tq_decode_attention for up to max_context tokens
- * (packed + ring): per-split partial results of the packed tokens, and at head_dim 256 the
- * prepared queries; scratch only (no initialisation needed).  Calls that share a workspace must be ordered (same stream), as
- * they use it in turn. */
+ * (packed + ring): per-split partial results (the split-K decode of long contexts across
+ * compute units), and at head_dim 256 the prepared queries; scratch only (no initialisation
+ * needed).  Calls that share a workspace must be ordered (same stream), as they use it in
+ * turn.  0 for invalid arguments. */
 size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch, int32_t n_q_heads,
                                  int32_t n_kv_heads, int64_t max_context);
 

@@ -12,7 +12,7 @@ import compressed_decode_attention_02_amd as tq
 pytestmark = pytest.mark.gpu
 
 from gpu_common import (Env, assert_decode_close, check_quantize, dev_to_stored, log, oracle_decode,  # noqa: E402
-                        packed_to_np, quantize_gpu, run_decode, to_dev, torch_mod)
+                        packed_to_np, quantize_gpu, rel_err_per_head, run_decode, to_dev, torch_mod)
 
 
 @pytest.fixture(scope="module")
@@ -434,6 +434,72 @@ def test_paged_store_matches_contiguous(torch, case):
     ref = oracle_decode(env, dev_to_stored(qd).astype(np.float64), w.hq, w.hkv, cont, w.n_packed + w.n_ring,
                         rings[1], 1, b_list=[0, 1])
     assert_decode_close(outs[1].cpu().numpy().astype(np.float64), ref, "paged step")
+    assert not paged.table_error()
+
+
+def test_paged_store_reports_bad_table_entries(torch):
+    """A block-table entry outside the pool is clamped on the device (no access leaves the pool)
+    and reported through the store's error flag, by the quantiser and by the decode; a valid
+    table leaves the flag clear."""
+    w = W.custom(3, batch=1, n_packed=256, n_ring=0)
+    env = Env(w.d, w.value_bits)
+    n_sl, pt, pps = w.hkv, 64, 4
+    (k, v), _ = W.host_kv(w, 0, w.n_packed)
+    kd = to_dev(np.ascontiguousarray(k.reshape(n_sl, -1, w.d)), w.in_dtype)
+    vd = to_dev(np.ascontiguousarray(v.reshape(n_sl, -1, w.d)), w.in_dtype)
+    q, _ = W.host_queries(w, 0)
+    qd = to_dev(q, w.in_dtype)
+    ws = tq.new_workspace(env.cfg, w.batch, w.hq, w.hkv, pt * pps)
+    out = torch.zeros((w.batch, w.hq, w.d), dtype=torch.float32, device="cuda")
+    good = tq.PagedStore(env.cfg, n_sl, pt, pps, n_sl * pps, seed=1)
+    quantize_gpu(env, kd, vd, n_sl, w.n_packed, store=good)
+    tq.tq_decode_attention(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, good.struct(), w.n_packed, None, 0,
+                           1 / math.sqrt(w.d), out, ws)
+    torch.cuda.synchronize()
+    assert not good.table_error()
+    table = good.table_np.copy()
+    table[3, 2] = n_sl * pps + 5          # past the pool: clamped to its last page
+    table[5, 0] = -1                      # negative: clamped to page 0
+    bad = tq.PagedStore(env.cfg, n_sl, pt, pps, n_sl * pps, table=table)
+    quantize_gpu(env, kd, vd, n_sl, w.n_packed, store=bad)
+    assert bad.table_error()
+    bad.clear_table_error()
+    assert not bad.table_error()
+    tq.tq_decode_attention(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, bad.struct(), w.n_packed, None, 0,
+                           1 / math.sqrt(w.d), out, ws)
+    torch.cuda.synchronize()
+    assert bad.table_error()
+
+
+def test_decode_12_wave_groups_within_tolerance(torch):
+    """Long contexts at d = 128 run one 12-wave workgroup per compute unit whose waves take
+    token blocks in arrival order, so the summation order varies: repeated calls and the fused
+    step agree with append + decode within 1e-5 relative (not bit for bit; measured 2e-6), and the result is
+    within the decode bounds of the oracle."""
+    w = W.custom(2, n_packed=32000, n_ring=20)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    slices = w.batch * w.hkv
+    assert slices * w.n_packed // (cus * 12 * 32) >= 2, "the case must select 12-wave workgroups"
+    env, q, qd, stores, rings, outs, (n_packed, n_ring) = _step_case(w, 20, "12-wave")
+    spread = rel_err_per_head(outs[1].astype(np.float64), outs[0].astype(np.float64)).max()
+    log(f"12-wave: fused step vs append + decode max rel diff {spread:.3e}")
+    assert spread <= 1e-5
+    ws = tq.new_workspace(env.cfg, w.batch, w.hq, w.hkv, n_packed + n_ring)
+    first = None
+    for rep in range(4):
+        o = torch.zeros((w.batch, w.hq, w.d), dtype=torch.float32, device="cuda")
+        tq.tq_decode_attention(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, stores[0].struct(), n_packed,
+                               rings[0].struct(), n_ring, 1 / math.sqrt(w.d), o, ws)
+        torch.cuda.synchronize()
+        o = o.cpu().numpy().astype(np.float64)
+        if first is None:
+            first = o
+        diff = rel_err_per_head(o, first).max()
+        log(f"12-wave: repeat {rep} max rel diff {diff:.3e}")
+        assert diff <= 1e-5
+    ref = oracle_decode(env, dev_to_stored(qd).astype(np.float64), w.hq, w.hkv, stores[1], n_packed, rings[1],
+                        n_ring, b_list=[0])
+    assert_decode_close(outs[1].astype(np.float64), ref, "12-wave step")
 
 
 def test_decode_empty_context_gives_zeros(torch):

@@ -152,6 +152,16 @@ def test_decode_errors():
     assert dec(n_packed=4097) == B.TQ_ERR_INVALID_ARG     # beyond capacity
     assert dec(n_ring=129) == B.TQ_ERR_INVALID_ARG
     assert dec(q=FAKE + 2) == B.TQ_ERR_INVALID_ARG
+    # decode token indices are 32-bit: a context of 2^31 - 256 tokens or more is refused
+    big = 1 << 31
+    P2 = _fake_packed(cap=big)
+    ws_big = L.tq_decode_workspace_bytes(ctypes.byref(cfg), 2, 8, 2, big)
+    dec_big = lambda n_packed, n_ring: L.tq_decode_attention(
+        ctypes.byref(cfg), ctypes.byref(T), FAKE, B.TQ_BF16, 2, 8, 2, ctypes.byref(P2), n_packed, ctypes.byref(R),
+        n_ring, ctypes.c_float(0.1), FAKE, FAKE, ws_big, None)
+    assert dec_big(big - 256, 0) == B.TQ_ERR_UNSUPPORTED
+    assert dec_big(big - 300, 44) == B.TQ_ERR_UNSUPPORTED
+    assert dec_big(big, 0) == B.TQ_ERR_UNSUPPORTED
     # a shorter context needs no more workspace than the maximum it was sized for
     for ctx in (0, 1, 255, 256, 1000, 4095):
         assert L.tq_decode_workspace_bytes(ctypes.byref(cfg), 2, 8, 2, ctx) <= need
@@ -210,8 +220,8 @@ def test_paged_store_errors():
     L = tq.lib()
     T = _fake_tables()
 
-    def q(page_tokens=64, pps=4, n_pages=40, cap=256, table=FAKE):
-        P = B.tq_packed(FAKE, FAKE, FAKE, FAKE, cap, table, page_tokens, pps, n_pages)
+    def q(page_tokens=64, pps=4, n_pages=40, cap=256, table=FAKE, flag=None):
+        P = B.tq_packed(FAKE, FAKE, FAKE, FAKE, cap, table, page_tokens, pps, n_pages, flag)
         return L.tq_quantize_kv(ctypes.byref(cfg), ctypes.byref(T), FAKE, FAKE, B.TQ_BF16, 8, 100,
                                 ctypes.byref(P), 300, None)   # offset 300 > capacity in every case
     assert q() == B.TQ_ERR_INVALID_ARG                       # (the offset check: a valid paged store)
@@ -219,6 +229,8 @@ def test_paged_store_errors():
     assert q(cap=512) == B.TQ_ERR_INVALID_ARG                 # capacity != pages * page tokens
     assert q(n_pages=0) == B.TQ_ERR_INVALID_ARG
     assert q(table=FAKE + 2) == B.TQ_ERR_INVALID_ARG          # int32 table: 4-byte aligned
+    assert q(flag=FAKE) == B.TQ_ERR_INVALID_ARG               # (an aligned error flag: the offset check)
+    assert q(flag=FAKE + 2) == B.TQ_ERR_INVALID_ARG           # int32 error flag: 4-byte aligned
 
 
 
@@ -249,3 +261,43 @@ def test_test_hook_errors():
     assert scores(out=FAKE + 4) == B.TQ_ERR_INVALID_ARG
     assert scores(q=None) == B.TQ_ERR_INVALID_ARG
     assert scores(hq=40000, hkv=1) == B.TQ_ERR_UNSUPPORTED  # batch * heads above the grid's y limit
+
+
+def test_binding_rejects_bad_tensors_before_the_library():
+    """The binding checks dtype agreement, contiguity, size and device of every tensor before
+    the call: a k/v dtype mismatch would make the kernel read v with k's element size."""
+    import torch
+    cfg = tq.make_config()
+    n = 2 * 16 * 128
+    k32 = torch.zeros(n, dtype=torch.float32)
+    kb = torch.zeros(n, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="share a dtype"):
+        tq.tq_quantize_kv(cfg, None, k32, kb, 2, 16, None, 0)
+    with pytest.raises(ValueError, match="share a dtype"):
+        tq.tq_quantize_kv(cfg, None, kb, k32, 2, 16, None, 0)
+    with pytest.raises(ValueError, match="contiguous"):
+        tq.tq_quantize_kv(cfg, None, kb.view(4, -1)[:, ::2], kb.view(4, -1)[:, ::2], 1, 4, None, 0)
+    with pytest.raises(ValueError, match="at least"):
+        tq.tq_quantize_kv(cfg, None, kb, kb, 2, 17, None, 0)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tq.tq_quantize_kv(cfg, None, kb, kb, 2, 16, None, 0)
+    with pytest.raises(ValueError, match="unsupported dtype"):
+        ki = torch.zeros(n, dtype=torch.int16)
+        tq.tq_quantize_kv(cfg, None, ki, ki, 2, 16, None, 0)
+    # the ring append: one token per slice
+    with pytest.raises(ValueError, match="share a dtype"):
+        tq.tq_append_ring(cfg, None, k32[:256], kb[:256], 2, 0)
+    with pytest.raises(ValueError, match="at least"):
+        tq.tq_append_ring(cfg, None, kb[:255], kb[:255], 2, 0)
+    # decode: q, out (fp32) and workspace; the fused step's new token pair
+    q = torch.zeros(4 * 128, dtype=torch.bfloat16)
+    out = torch.zeros(4 * 128, dtype=torch.float32)
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="out must be"):
+        tq.tq_decode_attention(cfg, None, q, 1, 4, 1, None, 0, None, 0, 0.1, out.half(), ws)
+    with pytest.raises(ValueError, match="at least"):
+        tq.tq_decode_attention(cfg, None, q[:500], 1, 4, 1, None, 0, None, 0, 0.1, out, ws)
+    with pytest.raises(ValueError, match="share a dtype"):
+        tq.tq_decode_step(cfg, None, q, 1, 4, 1, None, 0, None, 0, k32[:128], kb[:128], 0.1, out, ws)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tq.tq_decode_step(cfg, None, q, 1, 4, 1, None, 0, None, 0, kb[:128], kb[:128], 0.1, out, ws)
