@@ -12,13 +12,15 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtq.so")
 
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_RING_FULL, TQ_ERR_WORKSPACE, TQ_ERR_HIP = 0, -1, -2, -3, -4, -5
+TQ_ERR_SCRATCH_LIMIT = -6
+TQ_NOALLOC_SCRATCH_BYTES = 8 << 20
 TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 
 EXPORTS = [
     "tq_build_codebook", "tq_build_rotation", "tq_tables_bytes", "tq_build_tables", "tq_tables_view",
     "tq_packed_bytes_per_token", "tq_quantize_kv", "tq_append_ring", "tq_flush",
     "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_attention_ragged", "tq_decode_step",
-    "tq_status_string", "tq_rotate", "tq_decode_scores",
+    "tq_status_string", "tq_rotate", "tq_decode_scores", "tq_decode_attention_noalloc",
 ]
 
 
@@ -80,6 +82,8 @@ def _lib():
                                                       P, P, SZ, P]),
         "tq_decode_step": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, K, ctypes.POINTER(I64), R,
                                           ctypes.POINTER(I32), P, P, ctypes.c_int, F, P, P, SZ, P]),
+        "tq_decode_attention_noalloc": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, K, I64, R, I32, F, P,
+                                                       P]),
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tq_rotate": (ctypes.c_int, [C, T, P, ctypes.c_int, I64, P, P]),
         "tq_decode_scores": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, K, I64, R, I32, P, P]),
@@ -335,6 +339,25 @@ def tq_decode_attention(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv
         ctypes.byref(ring) if ring is not None else None, n_ring, ctypes.c_float(softmax_scale), _ptr(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("tq_decode_attention", st)
+
+
+def tq_decode_attention_noalloc(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv_heads: int,
+                                packed: tq_packed | None, n_packed: int, ring: tq_ring | None, n_ring: int,
+                                softmax_scale: float, out, stream=None):
+    """tq_decode_attention with the library's static scratch instead of a workspace (no
+    allocation; calls that may overlap on one GPU race on the scratch)."""
+    import torch
+    n = max(batch, 0) * max(n_q_heads, 0) * cfg.head_dim
+    _dtype_code(q)
+    _need("q", q, n)
+    _need("out", out, n, torch.float32)
+    _on_one_gpu(("q", q), ("out", out))
+    st = _lib().tq_decode_attention_noalloc(
+        ctypes.byref(cfg), ctypes.byref(tables.view), _ptr(q), _dtype_code(q), batch, n_q_heads, n_kv_heads,
+        ctypes.byref(packed) if packed is not None else None, n_packed,
+        ctypes.byref(ring) if ring is not None else None, n_ring, ctypes.c_float(softmax_scale), _ptr(out),
+        _stream(stream))
+    _check("tq_decode_attention_noalloc", st)
 
 
 def tq_rotate(cfg, tables: Tables, x, n_rows: int, out, stream=None):

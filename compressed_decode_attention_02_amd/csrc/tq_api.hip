@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "tq.h"
 #include "tq_internal.h"
@@ -338,6 +339,53 @@ extern "C" tq_status tq_decode_step(const tq_config *cfg, const tq_tables *table
     *n_packed = np;
     *n_ring = nr + 1;
     return TQ_OK;
+}
+
+// ------------------------------------------------------------------ decode without allocation
+// The scratch of tq_decode_attention_noalloc: a file-scope device array (one copy per GPU, held
+// until the process ends).  Host code never passes the array's name to a kernel (in host code it
+// is only a stand-in for the symbol): the device address comes from hipGetSymbolAddress, taken
+// once per device on the entry point's first call there, with that device current.
+static __device__ __align__(256) unsigned char scratch[TQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];  // per device: device address of `scratch`
+
+tq_status scratch_address(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TQ_ERR_HIP;
+    if (dev < 0 || dev >= 64) return TQ_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TQ_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return TQ_OK;
+}
+}  // namespace
+
+extern "C" tq_status tq_decode_attention_noalloc(const tq_config *cfg, const tq_tables *tables, const void *q,
+                                                 tq_dtype q_dtype, int32_t batch, int32_t n_q_heads,
+                                                 int32_t n_kv_heads, const tq_packed *packed, int64_t n_packed,
+                                                 const tq_ring *ring, int32_t n_ring, float softmax_scale,
+                                                 float *out, void *stream) {
+    // every argument checked, and the scratch the call needs against the array's size, before
+    // anything else (the check reads no scratch; a placeholder stands for its address).  The
+    // decode's scratch needs no clearing: every byte it reads was written earlier in the call.
+    void *const placeholder = reinterpret_cast<void *>(uintptr_t(256));
+    tq_status st = decode_impl(cfg, tables, q, q_dtype, batch, n_q_heads, n_kv_heads, packed, n_packed, ring,
+                               n_ring, softmax_scale, out, placeholder, TQ_NOALLOC_SCRATCH_BYTES, stream, nullptr,
+                               nullptr, TQ_F32, true);
+    if (st == TQ_ERR_WORKSPACE) return TQ_ERR_SCRATCH_LIMIT;
+    if (st != TQ_OK) return st;
+    void *ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != TQ_OK) return st;
+    return decode_impl(cfg, tables, q, q_dtype, batch, n_q_heads, n_kv_heads, packed, n_packed, ring, n_ring,
+                       softmax_scale, out, ws, TQ_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr, TQ_F32);
 }
 
 // ------------------------------------------------------------------ test hooks

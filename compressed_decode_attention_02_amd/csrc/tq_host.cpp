@@ -187,6 +187,7 @@ extern "C" const char *tq_status_string(tq_status s) {
         case TQ_ERR_RING_FULL: return "ring buffer full";
         case TQ_ERR_WORKSPACE: return "decode workspace too small";
         case TQ_ERR_HIP: return "HIP runtime error";
+        case TQ_ERR_SCRATCH_LIMIT: return "call needs more scratch than the library's static decode buffer holds";
     }
     return "unknown status";
 }

@@ -11,7 +11,10 @@
  *
  * Conventions for every entry point:
  *   - Pointers named host_* are host memory; every other buffer pointer is device memory
- *     owned by the caller.  The library never allocates device memory and keeps no state.
+ *     owned by the caller.  The library never allocates device memory.  Its only state is a
+ *     per-device cache of the compute-unit count and of the address of the static scratch
+ *     array of tq_decode_attention_noalloc (a fixed-size device array per GPU, held until the
+ *     process ends).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Device work is enqueued
  *     asynchronously on it; the call returns once the work is enqueued.
  *   - All argument checks run synchronously on the host before anything is enqueued; on
@@ -46,7 +49,9 @@ typedef enum {
     TQ_ERR_UNSUPPORTED = -2,  /* head_dim / bit width / group size not implemented          */
     TQ_ERR_RING_FULL = -3,    /* append to a ring that already holds buffer_size tokens     */
     TQ_ERR_WORKSPACE = -4,    /* decode workspace smaller than tq_decode_workspace_bytes()  */
-    TQ_ERR_HIP = -5           /* a HIP launch or runtime call failed                        */
+    TQ_ERR_HIP = -5,          /* a HIP launch or runtime call failed                        */
+    TQ_ERR_SCRATCH_LIMIT = -6 /* tq_decode_attention_noalloc: the call needs more scratch     */
+                              /* than TQ_NOALLOC_SCRATCH_BYTES                              */
 } tq_status;
 
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
@@ -221,6 +226,22 @@ tq_status tq_decode_step(const tq_config *cfg, const tq_tables *tables, const vo
                          int64_t *n_packed, const tq_ring *ring, int32_t *n_ring, const void *k_new,
                          const void *v_new, tq_dtype kv_dtype, float softmax_scale, float *out, void *workspace,
                          size_t workspace_bytes, void *stream);
+
+/* Decode without a workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): tq_decode_attention
+ * with the workspace taken from a static device array of TQ_NOALLOC_SCRATCH_BYTES (8 MiB) per
+ * GPU instead of the caller's buffer.  The call allocates nothing (no hipMalloc, no library
+ * allocation); its first call on a device looks the array's address up once.  A call whose
+ * scratch (tq_decode_workspace_bytes for its shape) exceeds the array returns
+ * TQ_ERR_SCRATCH_LIMIT before anything is launched.  Every call on one GPU uses that GPU's one
+ * array: calls that may overlap on a GPU (different streams, or several host threads) race on
+ * it and must be ordered by the caller.  The scratch needs no clearing (each call writes every
+ * byte it reads).  Arguments and results as tq_decode_attention. */
+#define TQ_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+tq_status tq_decode_attention_noalloc(const tq_config *cfg, const tq_tables *tables, const void *q,
+                                      tq_dtype q_dtype, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                      const tq_packed *packed, int64_t n_packed, const tq_ring *ring, int32_t n_ring,
+                                      float softmax_scale, float *out, void *stream);
 
 const char *tq_status_string(tq_status s);
 

@@ -301,3 +301,28 @@ def test_binding_rejects_bad_tensors_before_the_library():
         tq.tq_decode_step(cfg, None, q, 1, 4, 1, None, 0, None, 0, k32[:128], kb[:128], 0.1, out, ws)
     with pytest.raises(ValueError, match="GPU tensor"):
         tq.tq_decode_step(cfg, None, q, 1, 4, 1, None, 0, None, 0, kb[:128], kb[:128], 0.1, out, ws)
+
+
+def test_noalloc_decode_errors():
+    """The no-allocation decode checks its arguments like tq_decode_attention and refuses a call
+    whose scratch exceeds the static array (TQ_ERR_SCRATCH_LIMIT), all before any device call."""
+    cfg = tq.make_config()
+    L = tq.lib()
+    T, R = _fake_tables(), B.tq_ring(FAKE, FAKE)
+
+    def dec(bsz=2, hq=8, hkv=2, n_packed=4096, cap=4096, n_ring=5, q=FAKE):
+        P = _fake_packed(cap=cap)
+        return L.tq_decode_attention_noalloc(ctypes.byref(cfg), ctypes.byref(T), q, B.TQ_BF16, bsz, hq, hkv,
+                                             ctypes.byref(P), n_packed, ctypes.byref(R), n_ring,
+                                             ctypes.c_float(0.1), FAKE, None)
+    assert dec(hq=6, hkv=4) == B.TQ_ERR_INVALID_ARG
+    assert dec(n_packed=4097) == B.TQ_ERR_INVALID_ARG
+    assert dec(q=FAKE + 2) == B.TQ_ERR_INVALID_ARG
+    # a call that fits, and one that does not: 32000 slices of one query head each need
+    # 32000 partial rows of 128 fp32 (16 MB)
+    need = lambda bsz, hq, hkv, ctx: L.tq_decode_workspace_bytes(ctypes.byref(cfg), bsz, hq, hkv, ctx)
+    assert need(4, 32, 8, 32768) <= B.TQ_NOALLOC_SCRATCH_BYTES
+    assert need(1000, 32, 32, 100) > B.TQ_NOALLOC_SCRATCH_BYTES
+    assert dec(bsz=1000, hq=32, hkv=32, n_packed=100, cap=100, n_ring=0) == B.TQ_ERR_SCRATCH_LIMIT
+    assert B.TQ_ERR_SCRATCH_LIMIT == -6
+    assert b"scratch" in L.tq_status_string(B.TQ_ERR_SCRATCH_LIMIT)
