@@ -557,6 +557,25 @@ __device__ void ring_attend(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, f
     }
 }
 
+// ------------------------------------------------------------------ value operands
+// A value code of VB bits at bit position pos of a halfword (nothing else set) is the fp16
+// denormal code * 2^(pos - 24), exact while pos + VB <= 10 (the mantissa field).  The matrix
+// cores keep such products, but sums over many blocks of the smallest ones (pos 0 and 2) were
+// measured to lose precision (3e-5 and 8e-6 of the sum, against 2-3e-6 at pos 4 to 8), so every
+// code is brought to pos >= 4: the code of value tile t sits at bit sh = VB t mod 16 of its
+// halfword and is shifted right by kValShift<VB>(sh) (left when negative) to pos(t); the tile's
+// sums are scaled by kValScale<VB>(t) = 2^(24 - pos(t)) at the end.
+template <int VB>
+__device__ __forceinline__ constexpr int kValShift(int sh) {
+    if constexpr (VB == 2) return sh < 4 ? -4 : (sh <= 8 ? 0 : 6);
+    else return sh == 0 ? -4 : (sh == 4 ? 0 : (sh == 8 ? 2 : 6));
+}
+template <int VB>
+__device__ __forceinline__ constexpr float kValScale(int t) {
+    const int sh = (VB * t) % 16;
+    return (float)(1u << (24 - (sh - kValShift<VB>(sh))));
+}
+
 // ------------------------------------------------------------------ packed split (one wave)
 template <int D, int VB, int G, int NW>
 __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, int bk, int b, int kvh, int n_packed,
@@ -887,8 +906,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
 
     // constants kept in registers so that and-or forms take them as operands
     uint32_t kSel = 0x07070707u, kSgn = 0x80008000u, kOne = 0x3C003C00u;
-    uint32_t kCode = (((1u << VB) - 1u) << (10 - VB)) * 0x00010001u;
-    asm volatile("" : "+v"(kSel), "+v"(kSgn), "+v"(kOne), "+v"(kCode));
+    asm volatile("" : "+v"(kSel), "+v"(kSgn), "+v"(kOne));
 
     auto process = [&](const unsigned char *buf, int t0) {
         // ---- scores: query rows x token columns, centroid and sign parts on MFMA
@@ -1096,16 +1114,18 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
                 }
             }
         }
-        // A = 1 + code / 2^VB (exact fp16: the code in the top VB mantissa bits of each half)
+        // A = code * 2^(pos - 24): each half keeps only the VB code bits, at pos(t), an exact
+        // fp16 denormal (see kValShift); the power of two of each tile is removed from the sums
+        // at the end
 #pragma unroll
         for (int t = 0; t < S::NT; ++t) {
             const int k = (VB * t) / 16, sh = (VB * t) % 16;
+            const int shr = kValShift<VB>(sh);
+            const uint32_t mask = (((1u << VB) - 1u) * 0x00010001u) << (sh - shr);
             u32x4_t avu;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t zz = sh >= 10 - VB ? (z[k][r] >> (sh - (10 - VB))) : (z[k][r] << ((10 - VB) - sh));
-                avu[r] = (zz & kCode) | kOne;
-            }
+            for (int r = 0; r < 4; ++r)
+                avu[r] = (shr > 0 ? (z[k][r] >> shr) : (shr < 0 ? (z[k][r] << -shr) : z[k][r])) & mask;
             const half8_t av = __builtin_bit_cast(half8_t, avu);
 #pragma unroll
             for (int p = 0; p < S::NPASS; ++p) {
@@ -1158,9 +1178,9 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int c = (4 * q + i) * S::NT + t;
-                // acc = sum B (1 + code / 2^VB): o = 2^VB acc - (2^VB + HALF - 1/2) sum B
+                // acc = sum B code 2^(pos - 24): o = acc 2^(24 - pos) - (HALF - 1/2) sum B
                 if (c / 32 == grp)
-                    sm.x.wo[wave][gg][c] = (float)(1 << VB) * acc_v[p][t][i] - (float)((1 << VB) + S::HALF - 0.5f) * sumb[p];
+                    sm.x.wo[wave][gg][c] = kValScale<VB>(t) * acc_v[p][t][i] - (float)(S::HALF - 0.5f) * sumb[p];
             }
     }
 }
