@@ -39,6 +39,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -252,6 +253,7 @@ struct alignas(16) DecodeSmem {
     u32x4_t bfrag[S::BLDS ? 2 * S::NKS : 1][FZ + 1];  // [centroid, sign k-steps][row slot]
     float pb[NW][G][kBlock + 4];
     float corr[NW][G];
+    float i8c[G][4];    // int8 score path: per head alpha, beta / 4, -beta W (see packed_wave)
     float mref[NW][G];  // running reference max per wave and head (packed splits)
     float wm[NW][G], wl[NW][G];
     float rm[G], rl[G];  // the split's ring tokens: maximum and sum of p per head
@@ -557,25 +559,6 @@ __device__ void ring_attend(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, f
     }
 }
 
-// ------------------------------------------------------------------ value operands
-// A value code of VB bits at bit position pos of a halfword (nothing else set) is the fp16
-// denormal code * 2^(pos - 24), exact while pos + VB <= 10 (the mantissa field).  The matrix
-// cores keep such products, but sums over many blocks of the smallest ones (pos 0 and 2) were
-// measured to lose precision (3e-5 and 8e-6 of the sum, against 2-3e-6 at pos 4 to 8), so every
-// code is brought to pos >= 4: the code of value tile t sits at bit sh = VB t mod 16 of its
-// halfword and is shifted right by kValShift<VB>(sh) (left when negative) to pos(t); the tile's
-// sums are scaled by kValScale<VB>(t) = 2^(24 - pos(t)) at the end.
-template <int VB>
-__device__ __forceinline__ constexpr int kValShift(int sh) {
-    if constexpr (VB == 2) return sh < 4 ? -4 : (sh <= 8 ? 0 : 6);
-    else return sh == 0 ? -4 : (sh == 4 ? 0 : (sh == 8 ? 2 : 6));
-}
-template <int VB>
-__device__ __forceinline__ constexpr float kValScale(int t) {
-    const int sh = (VB * t) % 16;
-    return (float)(1u << (24 - (sh - kValShift<VB>(sh))));
-}
-
 // ------------------------------------------------------------------ packed split (one wave)
 template <int D, int VB, int G, int NW>
 __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, int bk, int b, int kvh, int n_packed,
@@ -809,7 +792,122 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
         rs = part == 2 ? 1 : (part == 3 ? 2 : 0);
     }
     u32x4_t bc[S::BLDS ? 1 : S::NKS], bs[S::BLDS ? 1 : S::NKS];
-    {
+    // ---- int8 score path (head_dim 128, four query heads per kv head).  The stored centroids
+    // are binary16 values, so c * 2^Sc is an integer for a power of two 2^Sc that keeps every
+    // |c * 2^Sc| < 2^14 (checked when the tables are built); each such integer is two signed
+    // bytes (hi * 256 + lo), looked up by index with byte permutes.  q' and w = S q' of each head
+    // are taken to 24-bit fixed point (x * 2^s rounded, |x * 2^s| < 2^22 for the head's largest
+    // coordinate) and split into three signed byte digits (x = 2^16 d0 + 2^8 d1 + d2): A rows
+    // 4 g + k hold digit k of head g (row 4 g + 3 is zero), so the products on
+    // v_mfma_i32_16x16x64_i8 are exact integer sums, and lane group q of the result holds head q.
+    // (Measured against the oracle at every workload's full size: the same decode errors as the
+    // fp16 hi + lo query operands this replaces, and as a fourth digit.)
+    // Coordinates: lane group q covers key words 4q .. 4q + 3; k-step ks uses words 4q + 2ks and
+    // 4q + 2ks + 1; dword r of an operand holds the even (r even) or odd coordinates of word
+    // 4q + 2ks + r / 2, byte b being coordinate 8 w + 2 b + r % 2.
+    constexpr bool I8 = D == 128 && G == 4;
+    i32x4_t qa[2], wa[2];
+    float i8_alpha = 0.f, i8_beta4 = 0.f, i8_mbw = 0.f;
+    uint32_t ch0 = 0, ch1 = 0, cl0 = 0, cl1 = 0;  // int8 path: hi / lo bytes of c * 2^Sc by index
+    u32x4_t *const afrag = reinterpret_cast<u32x4_t *>(&sm.bfrag[0][0]);  // [q', w][ks][lane]
+    static_assert(!I8 || sizeof(sm.bfrag) >= 256 * sizeof(u32x4_t), "int8 fragments in the fragment area");
+    int i8_sc = 0;
+    if constexpr (I8) {
+        float cmax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cmax = fmaxf(cmax, fabsf(a.centroids[i]));
+        int ec;
+        (void)frexpf(cmax, &ec);  // cmax < 2^ec
+        i8_sc = 14 - ec;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int ci = (int)ldexpf(a.centroids[i], i8_sc);
+            const int lo = ((ci + 128) & 255) - 128, hi = (ci - lo) >> 8;
+            const int sh = 8 * (i & 3);
+            if (i < 4) {
+                cl0 |= (uint32_t)(lo & 255) << sh;
+                ch0 |= (uint32_t)(hi & 255) << sh;
+            } else {
+                cl1 |= (uint32_t)(lo & 255) << sh;
+                ch1 |= (uint32_t)(hi & 255) << sh;
+            }
+        }
+    }
+    if constexpr (I8) {
+        const float cs = a.scale * kLog2e * (1.0f / sqrtf((float)D)), ss = cs * kQjl;
+        // phase A: wave g takes head g to fixed point (in place: q' as int32, w into the first
+        // partial-sum slot) and stores the head's constants
+        if (wave < G) {
+            constexpr int PARTS = PrepShape<D, NW>::PARTS;
+            const int g = wave;
+            float xq[2], xw[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int j = lane + 64 * e;
+                xq[e] = qw[g * D + j];
+                float sw = 0.f;
+#pragma unroll
+                for (int pt = 0; pt < PARTS; ++pt) sw += qw[(G + pt * G + g) * D + j];
+                xw[e] = sw;
+            }
+            float mq = fmaxf(fabsf(xq[0]), fabsf(xq[1])), mw = fmaxf(fabsf(xw[0]), fabsf(xw[1]));
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                mq = fmaxf(mq, __shfl_xor(mq, o));
+                mw = fmaxf(mw, __shfl_xor(mw, o));
+            }
+            int eq, ew;
+            (void)frexpf(mq, &eq);
+            (void)frexpf(mw, &ew);
+            const int sq = 22 - eq, sw = 22 - ew;
+            double wsum = 0.0;
+            int *qi = reinterpret_cast<int *>(qw);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int j = lane + 64 * e;
+                const int iq = (int)rintf(ldexpf(xq[e], sq)), iw = (int)rintf(ldexpf(xw[e], sw));
+                qi[g * D + j] = iq;
+                qi[(G + g) * D + j] = iw;
+                wsum += (double)iw;
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
+            if (lane == 0) {
+                // logit = |k| (alpha S + gamma (beta / 4 Z - beta W)), S and Z the integer sums
+                const float beta = ldexpf(ss, -sw);
+                sm.i8c[g][0] = ldexpf(cs, -(sq + i8_sc));
+                sm.i8c[g][1] = 0.25f * beta;
+                sm.i8c[g][2] = -beta * (float)wsum;
+            }
+        }
+        if constexpr (MERGED) {
+            if (nr > 0) ring_p3<D, G, NW>(rpr, sm.rm, sm.rl, nr);
+        }
+        __syncthreads();
+        // phase B: the fragment bytes, one 16-byte operand per thread (threads 0 .. 255)
+        if (threadIdx.x < 256) {
+            const int tid = threadIdx.x;
+            const int which = tid >> 7, ks = (tid >> 6) & 1, ln = tid & 63, r16 = ln & 15, qq = ln >> 4;
+            const int g = r16 >> 2, k = r16 & 3;
+            const int *src = reinterpret_cast<const int *>(qw) + (which ? G + g : g) * D;
+            u32x4_t f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint32_t wd = 0;
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int v = src[8 * (4 * qq + 2 * ks + (r >> 1)) + 2 * bb + (r & 1)];
+                    const int d2 = ((v + 128) & 255) - 128, v1 = (v - d2) >> 8;
+                    const int d1 = ((v1 + 128) & 255) - 128, d0 = (v1 - d1) >> 8;
+                    const int dk = k == 0 ? d0 : (k == 1 ? d1 : (k == 2 ? d2 : 0));
+                    wd |= (uint32_t)(dk & 255) << (8 * bb);
+                }
+                f[r] = wd;
+            }
+            afrag[(2 * which + ks) * 64 + ln] = f;
+        }
+        __syncthreads();
+    } else {
         const float cs = a.scale * kLog2e * (1.0f / sqrtf((float)D)), ss = cs * kQjl;
         // q' of head rg, and the partial sums of w = S q' (summed here)
         constexpr int PARTS = PrepShape<D, NW>::PARTS;
@@ -882,6 +980,16 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
             }
         }
     }
+    if constexpr (I8) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            qa[ks] = __builtin_bit_cast(i32x4_t, afrag[ks * 64 + lane]);
+            wa[ks] = __builtin_bit_cast(i32x4_t, afrag[(2 + ks) * 64 + lane]);
+        }
+        i8_alpha = sm.i8c[q][0];
+        i8_beta4 = sm.i8c[q][1];
+        i8_mbw = sm.i8c[q][2];
+    }
     // (the second staging buffers are free)
     if (b1 < nb) issue(t_begin + kBlock * b1, 1);
     const int cslot = rc ? q * SM::NSL + ri : SM::FZ, sslot = rs ? q * SM::NSL + ri : SM::FZ;
@@ -906,7 +1014,8 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
 
     // constants kept in registers so that and-or forms take them as operands
     uint32_t kSel = 0x07070707u, kSgn = 0x80008000u, kOne = 0x3C003C00u;
-    asm volatile("" : "+v"(kSel), "+v"(kSgn), "+v"(kOne));
+    uint32_t kCode = (((1u << VB) - 1u) << (10 - VB)) * 0x00010001u;
+    asm volatile("" : "+v"(kSel), "+v"(kSgn), "+v"(kOne), "+v"(kCode));
 
     auto process = [&](const unsigned char *buf, int t0) {
         // ---- scores: query rows x token columns, centroid and sign parts on MFMA
@@ -919,6 +1028,71 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
                 wds[tt][4 * i] = u[0]; wds[tt][4 * i + 1] = u[1]; wds[tt][4 * i + 2] = u[2]; wds[tt][4 * i + 3] = u[3];
             }
         }
+        if constexpr (I8) {
+            // ---- scores on int8 matrix cores: S (centroid part, c hi and lo bytes against the
+            //      digits of q') and Z (8 x the sign bits against the digits of w) per tile
+            const uint32_t m7 = 0x07070707u, m8 = 0x08080808u;
+            float lgv[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                i32x4_t ah = {0, 0, 0, 0}, al = {0, 0, 0, 0}, az = {0, 0, 0, 0};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const uint32_t w0 = wds[tt][2 * ks], w1 = wds[tt][2 * ks + 1];
+                    const uint32_t s0 = w0 >> 4, s1 = w1 >> 4;
+                    const uint32_t e0 = w0 & m7, o0 = s0 & m7, e1 = w1 & m7, o1 = s1 & m7;
+                    const i32x4_t bh = {(int)__builtin_amdgcn_perm(ch1, ch0, e0), (int)__builtin_amdgcn_perm(ch1, ch0, o0),
+                                        (int)__builtin_amdgcn_perm(ch1, ch0, e1), (int)__builtin_amdgcn_perm(ch1, ch0, o1)};
+                    const i32x4_t bl = {(int)__builtin_amdgcn_perm(cl1, cl0, e0), (int)__builtin_amdgcn_perm(cl1, cl0, o0),
+                                        (int)__builtin_amdgcn_perm(cl1, cl0, e1), (int)__builtin_amdgcn_perm(cl1, cl0, o1)};
+                    const i32x4_t bz = {(int)(w0 & m8), (int)(s0 & m8), (int)(w1 & m8), (int)(s1 & m8)};
+                    ah = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[ks], bh, ah, 0, 0, 0);
+                    al = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[ks], bl, al, 0, 0, 0);
+                    az = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[ks], bz, az, 0, 0, 0);
+                }
+                // lane (n16, q): head q, token 16 tt + n16; registers 0, 1, 2 = digits 0, 1, 2
+                const int c0 = (ah[0] << 8) + al[0], c1 = (ah[1] << 8) + al[1], c2 = (ah[2] << 8) + al[2];
+                const float sf = fmaf((float)c0, 65536.f, fmaf((float)c1, 256.f, (float)c2));
+                const float zf = fmaf((float)az[0], 65536.f, fmaf((float)az[1], 256.f, (float)az[2]));
+                const float2 kn = *reinterpret_cast<const float2 *>(buf + S::OFF_KN + (16 * tt + n16) * 8);
+                float lv = kn.x * fmaf(kn.y, fmaf(i8_beta4, zf, i8_mbw), i8_alpha * sf);
+                if (t0 + 16 * tt + n16 >= t_end) lv = -INFINITY;
+                lgv[tt] = lv;
+            }
+            // ---- online softmax of head q with a reference max that only moves when a logit
+            //      exceeds it (rare after the first block); p <= 1 always
+            float m_ref = sm.mref[wave][q];
+            if (__ballot(lgv[0] > m_ref || lgv[1] > m_ref)) {
+                float mb = fmaxf(lgv[0], lgv[1]);
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o));
+                const float m_new = fmaxf(m_ref, mb);
+                const float corr = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                m_ref = m_new;
+                if (n16 == 0) {
+                    sm.corr[wave][q] = corr;
+                    sm.mref[wave][q] = m_new;
+                }
+                wave_sync();
+#pragma unroll
+                for (int p = 0; p < S::NPASS; ++p) {
+                    const int n = n16 + 16 * p;
+                    const float c = (n < S::NCOL) ? sm.corr[wave][n / S::NG] : 0.f;
+                    sumb[p] *= c;
+                    lsum[p] *= c;
+#pragma unroll
+                    for (int t = 0; t < S::NT; ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            float e = acc_v[p][t][i];
+                            asm volatile("v_mul_f32 %0, %0, %1" : "+v"(e) : "v"(c));
+                            acc_v[p][t][i] = e;
+                        }
+                }
+            }
+            sm.pb[wave][q][n16] = __builtin_amdgcn_exp2f(lgv[0] - m_ref);
+            sm.pb[wave][q][16 + n16] = __builtin_amdgcn_exp2f(lgv[1] - m_ref);
+        } else {
         constexpr int NACC = G == 8 ? 2 : 1;  // [centroid, sign] for G = 8, one stacked otherwise
         f32x4_t acc[NACC][2];
 #pragma unroll
@@ -1056,6 +1230,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
         for (int i = 0; i < NLR; ++i) {
             sm.pb[wave][hbase + i][trow] = __builtin_amdgcn_exp2f(lg[i] - m_ref[i]);
         }
+        }
         wave_sync();
 
         // ---- values: B = p * scale in columns (head, group), hi + lo; A = codes of row n16
@@ -1114,18 +1289,19 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
                 }
             }
         }
-        // A = code * 2^(pos - 24): each half keeps only the VB code bits, at pos(t), an exact
-        // fp16 denormal (see kValShift); the power of two of each tile is removed from the sums
-        // at the end
+        // A = 1 + code / 2^VB (exact fp16: the code in the top VB mantissa bits of each half; the
+        // codes kept in place as fp16 denormals would need no shift, but sums of the smallest
+        // products were measured to lose precision on the matrix cores: decode error 2.8e-5
+        // against 5.6e-6 this way)
 #pragma unroll
         for (int t = 0; t < S::NT; ++t) {
             const int k = (VB * t) / 16, sh = (VB * t) % 16;
-            const int shr = kValShift<VB>(sh);
-            const uint32_t mask = (((1u << VB) - 1u) * 0x00010001u) << (sh - shr);
             u32x4_t avu;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                avu[r] = (shr > 0 ? (z[k][r] >> shr) : (shr < 0 ? (z[k][r] << -shr) : z[k][r])) & mask;
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t zz = sh >= 10 - VB ? (z[k][r] >> (sh - (10 - VB))) : (z[k][r] << ((10 - VB) - sh));
+                avu[r] = (zz & kCode) | kOne;
+            }
             const half8_t av = __builtin_bit_cast(half8_t, avu);
 #pragma unroll
             for (int p = 0; p < S::NPASS; ++p) {
@@ -1178,9 +1354,9 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int c = (4 * q + i) * S::NT + t;
-                // acc = sum B code 2^(pos - 24): o = acc 2^(24 - pos) - (HALF - 1/2) sum B
+                // acc = sum B (1 + code / 2^VB): o = 2^VB acc - (2^VB + HALF - 1/2) sum B
                 if (c / 32 == grp)
-                    sm.x.wo[wave][gg][c] = kValScale<VB>(t) * acc_v[p][t][i] - (float)(S::HALF - 0.5f) * sumb[p];
+                    sm.x.wo[wave][gg][c] = (float)(1 << VB) * acc_v[p][t][i] - (float)((1 << VB) + S::HALF - 0.5f) * sumb[p];
             }
     }
 }

@@ -150,6 +150,9 @@ extern "C" tq_status tq_build_tables(const tq_config *cfg, uint64_t seed, void *
     // stored table: centroids rounded to binary16, boundaries their exact midpoints
     for (int i = 0; i < L; ++i) cf[i] = (float)(_Float16)c[i];
     for (int i = 0; i + 1 < L; ++i) bf[i] = (float)(0.5 * ((double)cf[i] + (double)cf[i + 1]));
+    // the decode's integer score path (head_dim 128) takes c * 2^Sc (Sc: the power of two that
+    // keeps every |c * 2^Sc| below 2^14) as exact integers
+    if (d == 128 && !tq::centroids_are_scaled_integers(cf, L)) return TQ_ERR_UNSUPPORTED;
     std::vector<int8_t> sg(d);
     uint16_t *S = reinterpret_cast<uint16_t *>(p + tq::kTableSOffset);
     st = tq_build_rotation(d, seed, sg.data(), S);
@@ -159,6 +162,20 @@ extern "C" tq_status tq_build_tables(const tq_config *cfg, uint64_t seed, void *
         if (sg[j] < 0) sb[j / 32] |= 1u << (j % 32);
     return TQ_OK;
 }
+
+namespace tq {
+bool centroids_are_scaled_integers(const float *c, int n) {
+    float cmax = 0.f;
+    for (int i = 0; i < n; ++i) cmax = std::fmax(cmax, std::fabs(c[i]));
+    int ec = 0;
+    (void)std::frexp(cmax, &ec);
+    for (int i = 0; i < n; ++i) {
+        const double v = std::ldexp((double)c[i], 14 - ec);
+        if (v != std::nearbyint(v) || std::fabs(v) >= 16384.0) return false;
+    }
+    return true;
+}
+}  // namespace tq
 
 extern "C" tq_status tq_tables_view(const tq_config *cfg, const void *blob, tq_tables *out) {
     if (!cfg || !blob || !out) return TQ_ERR_INVALID_ARG;

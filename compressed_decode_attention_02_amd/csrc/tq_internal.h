@@ -18,6 +18,10 @@ constexpr size_t kTableSOffset = 256;
 
 tq_status check_config(const tq_config &c);
 
+// true when every c[i] * 2^(14 - e) is an integer below 2^14 in magnitude, 2^e the power of two
+// just above max |c[i]| (the decode's integer score path relies on it)
+bool centroids_are_scaled_integers(const float *c, int n);
+
 // compute units of the current device (cached per device; 256 if the query fails)
 int device_cus();
 
