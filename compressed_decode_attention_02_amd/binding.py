@@ -424,6 +424,37 @@ def tq_decode_step(cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv_head
     return np_.value, nr_.value
 
 
+class PreparedDecodeStep:
+    """One tq_decode_step call shape with its arguments checked and marshalled once, for loops
+    that repeat it (a model's layers at every decode step): calling it with the fill counts runs
+    tq_decode_step on the stream that was current when it was prepared and returns the new
+    counts.  The tensors and views passed in must stay alive and in place."""
+
+    def __init__(self, cfg, tables: Tables, q, batch: int, n_q_heads: int, n_kv_heads: int,
+                 packed: tq_packed | None, ring: tq_ring, k_new, v_new, softmax_scale: float, out, workspace,
+                 stream=None):
+        _decode_io(cfg, q, out, workspace, batch, n_q_heads)
+        _kv_pair(k_new, v_new, max(batch, 0) * max(n_kv_heads, 0) * cfg.head_dim, "k_new", "v_new")
+        _on_one_gpu(("q", q), ("out", out), ("workspace", workspace), ("k_new", k_new), ("v_new", v_new))
+        self._keep = (cfg, tables, q, packed, ring, k_new, v_new, out, workspace)
+        self._np = ctypes.c_int64(0)
+        self._nr = ctypes.c_int32(0)
+        self._fn = _lib().tq_decode_step
+        self._args = (ctypes.byref(cfg), ctypes.byref(tables.view), _ptr(q), _dtype_code(q), batch, n_q_heads,
+                      n_kv_heads, ctypes.byref(packed) if packed is not None else None, ctypes.byref(self._np),
+                      ctypes.byref(ring), ctypes.byref(self._nr), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                      ctypes.c_float(softmax_scale), _ptr(out), _ptr(workspace),
+                      workspace.numel() * workspace.element_size(), _stream(stream))
+
+    def __call__(self, n_packed: int, n_ring: int):
+        self._np.value = n_packed
+        self._nr.value = n_ring
+        st = self._fn(*self._args)
+        if st != TQ_OK:
+            raise TqError("tq_decode_step", st)
+        return self._np.value, self._nr.value
+
+
 def new_workspace(cfg, batch: int, n_q_heads: int, n_kv_heads: int, max_context: int, device="cuda"):
     """Decode workspace (scratch) of the size tq_decode_workspace_bytes reports."""
     import torch

@@ -298,6 +298,30 @@ def test_decode_step_matches_append_then_decode(torch):
         assert_decode_close(outs[1].astype(np.float64), ref, f"step {label}")
 
 
+def test_prepared_decode_step_matches_direct_call(torch):
+    """PreparedDecodeStep (arguments checked and marshalled once) runs the same tq_decode_step:
+    the same output bit for bit and the same counts, called again with the same fill counts."""
+    w = W.custom(3, batch=2, n_packed=700, n_ring=30)
+    env, q, qd, stores, rings, outs, (n_packed, n_ring) = _step_case(w, 30, "prepared")
+    n_sl = w.batch * w.hkv
+    (k, v), _ = W.host_kv(w, 0, w.n_packed + 31)
+    kn = to_dev(np.ascontiguousarray(k.reshape(n_sl, -1, w.d)[:, w.n_packed + 30]), w.in_dtype)
+    vn = to_dev(np.ascontiguousarray(v.reshape(n_sl, -1, w.d)[:, w.n_packed + 30]), w.in_dtype)
+    ws = tq.new_workspace(env.cfg, w.batch, w.hq, w.hkv, w.n_packed + w.buffer_size + 1)
+    scale = 1.0 / math.sqrt(w.d)
+    a = torch.zeros((w.batch, w.hq, w.d), dtype=torch.float32, device="cuda")
+    b = torch.zeros_like(a)
+    got_a = tq.tq_decode_step(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, stores[1].struct(), w.n_packed,
+                              rings[1].struct(), 30, kn, vn, scale, a, ws)
+    call = tq.PreparedDecodeStep(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, stores[1].struct(), rings[1].struct(),
+                                 kn, vn, scale, b, ws)
+    got_b = call(w.n_packed, 30)
+    torch.cuda.synchronize()
+    assert got_a == got_b == (w.n_packed, 31)
+    np.testing.assert_array_equal(b.cpu().numpy(), a.cpu().numpy())
+    np.testing.assert_array_equal(a.cpu().numpy(), outs[1])
+
+
 def test_decode_step_flushes_a_full_ring(torch):
     """A full ring is flushed into the packed store first: the same records, ring and
     output as tq_flush + tq_append_ring + tq_decode_attention."""

@@ -326,3 +326,20 @@ def test_noalloc_decode_errors():
     assert dec(bsz=1000, hq=32, hkv=32, n_packed=100, cap=100, n_ring=0) == B.TQ_ERR_SCRATCH_LIMIT
     assert B.TQ_ERR_SCRATCH_LIMIT == -6
     assert b"scratch" in L.tq_status_string(B.TQ_ERR_SCRATCH_LIMIT)
+
+
+def test_prepared_decode_step_checks_its_arguments():
+    """PreparedDecodeStep checks its tensors as tq_decode_step does, before marshalling."""
+    import torch
+    cfg = tq.make_config()
+    q = torch.zeros(4 * 128, dtype=torch.bfloat16)
+    out = torch.zeros(4 * 128, dtype=torch.float32)
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    k32 = torch.zeros(128, dtype=torch.float32)
+    kb = torch.zeros(128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="share a dtype"):
+        tq.PreparedDecodeStep(cfg, None, q, 1, 4, 1, None, None, k32, kb, 0.1, out, ws)
+    with pytest.raises(ValueError, match="out must be"):
+        tq.PreparedDecodeStep(cfg, None, q, 1, 4, 1, None, None, kb, kb, 0.1, out.half(), ws)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tq.PreparedDecodeStep(cfg, None, q, 1, 4, 1, None, None, kb, kb, 0.1, out, ws)
