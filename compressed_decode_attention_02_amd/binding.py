@@ -210,6 +210,11 @@ def tq_packed_bytes_per_token(cfg: tq_config) -> int:
     return _lib().tq_packed_bytes_per_token(ctypes.byref(cfg))
 
 
+def key_record_words(cfg: tq_config) -> int:
+    """32-bit words of one key record: (key_bits + 1) head_dim / 32 (layout in tq.h)."""
+    return (cfg.key_bits + 1) * cfg.head_dim // 32
+
+
 class PackedStore:
     """Device arrays of the packed cache, [n_slices][capacity][...] each (layout in tq.h)."""
 
@@ -217,7 +222,7 @@ class PackedStore:
         import torch
         d, vb = cfg.head_dim, cfg.value_bits
         self.cfg, self.n_slices, self.capacity = cfg, n_slices, capacity
-        self.key_words = torch.zeros((n_slices, capacity, d // 8), dtype=torch.int32, device=device)
+        self.key_words = torch.zeros((n_slices, capacity, key_record_words(cfg)), dtype=torch.int32, device=device)
         self.key_norms = torch.zeros((n_slices, capacity, 2), dtype=torch.float32, device=device)
         self.val_words = torch.zeros((n_slices, capacity, vb * d // 32), dtype=torch.int32, device=device)
         self.val_scales = torch.zeros((n_slices, capacity, d // 32), dtype=torch.int16, device=device)
@@ -241,7 +246,7 @@ class PagedStore:
         self.cfg, self.n_slices, self.page_tokens = cfg, n_slices, page_tokens
         self.pages_per_slice, self.n_pages = pages_per_slice, n_pages
         self.capacity = pages_per_slice * page_tokens
-        self.key_words = torch.zeros((n_pages, page_tokens, d // 8), dtype=torch.int32, device=device)
+        self.key_words = torch.zeros((n_pages, page_tokens, key_record_words(cfg)), dtype=torch.int32, device=device)
         self.key_norms = torch.zeros((n_pages, page_tokens, 2), dtype=torch.float32, device=device)
         self.val_words = torch.zeros((n_pages, page_tokens, vb * d // 32), dtype=torch.int32, device=device)
         self.val_scales = torch.zeros((n_pages, page_tokens, d // 32), dtype=torch.int16, device=device)

@@ -81,17 +81,19 @@ void split_shape(int d, int vb, int64_t G, int64_t slices, int64_t n_packed, int
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// decode workspace: at d = 256 the prepared queries (q', w) [slices][2][G][d]; the packed
+// decode workspace: at d = 256 and on the k_decode_any path the prepared queries (q', w)
+// [slices][2][G][d]; the packed
 // splits' partials o [slices][n_split][G][d] and (m, l) pairs [slices][n_split][G][2]
 // (slices * G = batch * hq)
 struct DecodeLayout {
     size_t prep, partial, partial_ml, total;
 };
 
-DecodeLayout decode_layout(int d, int64_t batch, int64_t hq, int64_t n_split) {
+DecodeLayout decode_layout(int d, int kb, int64_t batch, int64_t hq, int64_t n_split) {
     DecodeLayout L;
     L.prep = 0;
-    L.partial = d == 256 ? align256(sizeof(float) * (size_t)(batch * hq) * 2 * d) : 0;
+    const bool prep = d == 256 || tq::decode_uses_any(d, kb);
+    L.partial = prep ? align256(sizeof(float) * (size_t)(batch * hq) * 2 * d) : 0;
     L.partial_ml = L.partial + align256(sizeof(float) * (size_t)(batch * hq) * n_split * d);
     L.total = std::max<size_t>(256, L.partial_ml + align256(sizeof(float) * (size_t)(batch * hq) * n_split * 2));
     return L;
@@ -130,7 +132,7 @@ extern "C" tq_status tq_quantize_kv(const tq_config *cfg, const tq_tables *table
     a.cap = dst->capacity;
     a.dst_offset = dst_offset;
     set_pages(a, dst);
-    return hip_status(tq::launch_quantize(cfg->head_dim, cfg->value_bits, in_dtype, a, (hipStream_t)stream));
+    return hip_status(tq::launch_quantize(cfg->head_dim, cfg->key_bits, cfg->value_bits, in_dtype, a, (hipStream_t)stream));
 }
 
 extern "C" tq_status tq_append_ring(const tq_config *cfg, const tq_ring *ring, const void *k_new, const void *v_new,
@@ -177,7 +179,7 @@ extern "C" tq_status tq_flush(const tq_config *cfg, const tq_tables *tables, con
     a.cap = dst->capacity;
     a.dst_offset = n_packed;
     set_pages(a, dst);
-    return hip_status(tq::launch_quantize(cfg->head_dim, cfg->value_bits, TQ_F16, a, (hipStream_t)stream));
+    return hip_status(tq::launch_quantize(cfg->head_dim, cfg->key_bits, cfg->value_bits, TQ_F16, a, (hipStream_t)stream));
 }
 
 extern "C" size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch, int32_t n_q_heads,
@@ -190,7 +192,7 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch,
         std::max(decode_splits(cfg->head_dim, cfg->value_bits, n_q_heads / n_kv_heads, (int64_t)batch * n_kv_heads,
                                max_context, 4),
                  ((int64_t)cfg->buffer_size + ring_per_split_max(cfg->head_dim) - 1) / ring_per_split_max(cfg->head_dim));
-    return decode_layout(cfg->head_dim, batch, n_q_heads, n_split).total;
+    return decode_layout(cfg->head_dim, cfg->key_bits, batch, n_q_heads, n_split).total;
 }
 
 namespace {
@@ -234,7 +236,7 @@ tq_status decode_impl(const tq_config *cfg, const tq_tables *tables, const void 
         }
     }
     const int64_t ring_per_split = (n_ring + n_split - 1) / n_split;
-    const DecodeLayout L = decode_layout(cfg->head_dim, batch, n_q_heads, n_split);
+    const DecodeLayout L = decode_layout(cfg->head_dim, cfg->key_bits, batch, n_q_heads, n_split);
     if (workspace_bytes < L.total) return TQ_ERR_WORKSPACE;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     if (check_only) return TQ_OK;
@@ -277,7 +279,7 @@ tq_status decode_impl(const tq_config *cfg, const tq_tables *tables, const void 
     a.new_slot = k_new ? n_ring - 1 : -1;
     a.partial = reinterpret_cast<float *>(ws + L.partial);
     a.partial_ml = reinterpret_cast<float *>(ws + L.partial_ml);
-    return hip_status(tq::launch_decode(cfg->head_dim, cfg->value_bits, G, a, (hipStream_t)stream));
+    return hip_status(tq::launch_decode(cfg->head_dim, cfg->key_bits, cfg->value_bits, G, a, (hipStream_t)stream));
 }
 }  // namespace
 
@@ -438,6 +440,7 @@ extern "C" tq_status tq_decode_scores(const tq_config *cfg, const tq_tables *tab
     a.rk = n_ring > 0 ? ring->k : nullptr;
     a.buffer_size = cfg->buffer_size;
     a.n_ring = n_ring;
+    a.kb = cfg->key_bits;
     a.centroids = tables->centroids;
     a.sign_bits = tables->sign_bits;
     a.S = tables->qjl_S;

@@ -261,10 +261,16 @@ struct alignas(16) DecodeSmem {
 };
 
 // ---- global -> LDS copies issued by hand, waited for with explicit counts.  M0 holds the
-//      LDS destination of the wave's 64 x 16 (or 64 x 4) bytes, the global address is a
-//      uniform base plus a 32-bit per-lane byte offset; the instruction's immediate offset
-//      IMM is added to both the global and the LDS address.  Every LDS read of a buffer is
-//      complete (lgkmcnt(0)) before the buffer is refilled.
+//      LDS destination of the wave's 64 x 16 (or 64 x 4) bytes: an input operand of the asm
+//      bound to that register, so the compiler writes M0 itself and knows it is read.  The
+//      global address is a uniform base plus a 32-bit per-lane byte offset; the instruction's
+//      immediate offset IMM is added to both the global and the LDS address.  The compiler
+//      does not count these loads, so every read of a staged buffer follows an explicit
+//      vmcnt wait, and every LDS read of a buffer is complete (lgkmcnt(0)) before the buffer
+//      is refilled.  Nor does its hazard recognizer look into the asm: the s_nop 4 in front
+//      of each copy gives the wait states the ISA requires between a VALU write of an SGPR
+//      (the v_readfirstlane of the base) and a VMEM read of it (5), which also covers an SALU
+//      write of M0 before an LDS-DMA load (1).
 // (the base is uniform by construction; readfirstlane makes that visible to the compiler
 // wherever it would otherwise keep the pointer in vector registers, and folds away elsewhere)
 __device__ __forceinline__ const void *uniform_ptr(const void *p) {
@@ -276,18 +282,18 @@ __device__ __forceinline__ const void *uniform_ptr(const void *p) {
 template <int IMM = 0>
 __device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t lds) {
     static_assert(IMM >= 0 && IMM < 4096, "global instruction offset range");
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 offset:%2"
                  :
-                 : "v"(off), "s"(uniform_ptr(base)), "s"(lds), "n"(IMM)
-                 : "memory", "m0");
+                 : "v"(off), "s"(uniform_ptr(base)), "n"(IMM), "{m0}"(lds)
+                 : "memory");
 }
 template <int IMM = 0>
 __device__ __forceinline__ void dma4(const void *base, uint32_t off, uint32_t lds) {
     static_assert(IMM >= 0 && IMM < 4096, "global instruction offset range");
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1 offset:%3"
+    asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1 offset:%2"
                  :
-                 : "v"(off), "s"(uniform_ptr(base)), "s"(lds), "n"(IMM)
-                 : "memory", "m0");
+                 : "v"(off), "s"(uniform_ptr(base)), "n"(IMM), "{m0}"(lds)
+                 : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -1680,7 +1686,40 @@ static hipError_t launch_main_dv(int G, const DecodeArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_decode(int d, int vb, int G, const DecodeArgs &a, hipStream_t st) {
+// the other key widths and head_dim 64: k_decode_prep for the queries, k_decode_any
+// (tq_decode_any.hip) for the splits, the same merge; a fused step's new token is appended to
+// the ring first
+template <int D>
+static hipError_t launch_any_d(int kb, int vb, int G, const DecodeArgs &a, hipStream_t st) {
+    if (a.k_new && a.new_slot >= 0) {
+        const hipError_t e = launch_ring_append(D, (tq_dtype)a.kv_dtype, a.k_new, a.v_new, a.rk, a.rv,
+                                                a.batch * a.hkv, a.buffer_size, a.new_slot, st);
+        if (e != hipSuccess) return e;
+    }
+    const dim3 pgrid((unsigned)(a.batch * a.hkv * PrepBand<D>::NB));
+    switch (G) {
+        case 1: hipLaunchKernelGGL((k_decode_prep<D, 1>), pgrid, dim3(kThreads), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((k_decode_prep<D, 2>), pgrid, dim3(kThreads), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((k_decode_prep<D, 4>), pgrid, dim3(kThreads), 0, st, a); break;
+        default: hipLaunchKernelGGL((k_decode_prep<D, 8>), pgrid, dim3(kThreads), 0, st, a); break;
+    }
+    launch_decode_any_main(D, kb, vb, G, a, st);
+    if (a.n_split > 1) {
+        const dim3 mgrid((unsigned)(a.batch * a.hkv * G));
+        switch (G) {
+            case 1: hipLaunchKernelGGL((k_decode_merge<D, 1>), mgrid, dim3(kThreads), 0, st, a); break;
+            case 2: hipLaunchKernelGGL((k_decode_merge<D, 2>), mgrid, dim3(kThreads), 0, st, a); break;
+            case 4: hipLaunchKernelGGL((k_decode_merge<D, 4>), mgrid, dim3(kThreads), 0, st, a); break;
+            default: hipLaunchKernelGGL((k_decode_merge<D, 8>), mgrid, dim3(kThreads), 0, st, a); break;
+        }
+    }
+    return hipGetLastError();
+}
+
+bool decode_uses_any(int d, int kb) { return kb != 3 || d == 64; }
+
+hipError_t launch_decode(int d, int kb, int vb, int G, const DecodeArgs &a, hipStream_t st) {
+    if (decode_uses_any(d, kb)) return d == 64 ? launch_any_d<64>(kb, vb, G, a, st) : launch_any_d<128>(kb, vb, G, a, st);
     if (d == 128 && vb == 2) return launch_main_dv<128, 2>(G, a, st);
     if (d == 128 && vb == 4) return launch_main_dv<128, 4>(G, a, st);
     if (d == 256 && vb == 2) return launch_main_dv<256, 2>(G, a, st);
@@ -1693,7 +1732,11 @@ hipError_t launch_ring_append(int d, tq_dtype dt, const void *kn, const void *vn
     const unsigned grid = (unsigned)((total + 255) / 256);
 #define TQ_RING(TAG, DD) hipLaunchKernelGGL((k_ring_append<TAG, DD>), dim3(grid), dim3(256), 0, st, kn, vn, rk, rv, \
                                             n_slices, buffer_size, slot)
-    if (d == 128) {
+    if (d == 64) {
+        if (dt == TQ_F32) TQ_RING(f32_tag, 64);
+        else if (dt == TQ_BF16) TQ_RING(bf16_tag, 64);
+        else TQ_RING(f16_tag, 64);
+    } else if (d == 128) {
         if (dt == TQ_F32) TQ_RING(f32_tag, 128);
         else if (dt == TQ_BF16) TQ_RING(bf16_tag, 128);
         else TQ_RING(f16_tag, 128);

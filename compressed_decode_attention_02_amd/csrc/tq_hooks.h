@@ -23,6 +23,7 @@ struct ScoreArgs {
     const uint16_t *rk;
     int buffer_size;
     int n_ring;
+    int kb;  // codebook bits of the key records
     const float *centroids;
     const uint32_t *sign_bits;
     const uint16_t *S;

@@ -45,7 +45,7 @@ __device__ void hadamard_row(float (&v)[D / 64], int lane) {
 #pragma unroll
         for (int e = 0; e < E; ++e) v[e] = u[e];
     }
-    const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.0625f;
+    const float inv_sqrt_d = D == 64 ? 0.125f : (D == 128 ? 0.08838834764831845f : 0.0625f);
 #pragma unroll
     for (int e = 0; e < E; ++e) v[e] *= inv_sqrt_d;
 }
@@ -100,18 +100,24 @@ __global__ __launch_bounds__(kHookThreads) void k_scores(ScoreArgs a) {
     float s;
     if (t < a.n_packed) {
         // s = |k| (sum_j q'_j c[idx_j] + gamma sqrt(pi/2)/d sum_j w_j (2 z_j - 1))
+        // key record: (kb + 1) d / 32 words; kb = 3: nibbles (index, sign bit on top), else a
+        // code plane of kb-bit fields and a sign plane
         const int64_t rec = record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, a.err, sl, t);
-        const uint32_t *kw = a.kw + rec * (D / 8);
+        const int kb = a.kb, per = 32 / kb;
+        const uint32_t *kw = a.kw + rec * ((kb + 1) * D / 32);
         float mse = 0.f, sgn = 0.f;
-        for (int wi = 0; wi < D / 8; ++wi) {
-            const uint32_t word = kw[wi];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int j = 8 * wi + k;
-                const uint32_t nib = (word >> (4 * k)) & 15u;
-                mse = fmaf(qr[j], a.centroids[nib & 7u], mse);
-                sgn += (nib & 8u) ? ws[j] : -ws[j];
+        for (int j = 0; j < D; ++j) {
+            uint32_t idx, z;
+            if (kb == 3) {
+                const uint32_t nib = (kw[j / 8] >> (4 * (j % 8))) & 15u;
+                idx = nib & 7u;
+                z = nib >> 3;
+            } else {
+                idx = (kw[j / per] >> (kb * (j % per))) & ((1u << kb) - 1u);
+                z = (kw[kb * D / 32 + j / 32] >> (j % 32)) & 1u;
             }
+            mse = fmaf(qr[j], a.centroids[idx], mse);
+            sgn += z ? ws[j] : -ws[j];
         }
         const float kqjl = 1.2533141373155003f / (float)D;  // sqrt(pi / 2) / d
         s = a.kn[rec * 2] * fmaf(a.kn[rec * 2 + 1] * kqjl, sgn, mse);
@@ -131,7 +137,8 @@ hipError_t launch_rotate(int d, const uint32_t *sign_bits, const void *x, int dt
                          hipStream_t st) {
     if (n_rows == 0) return hipSuccess;
     const dim3 grid((unsigned)((n_rows + kHookThreads / 64 - 1) / (kHookThreads / 64)));
-    if (d == 128) hipLaunchKernelGGL((k_rotate<128>), grid, dim3(kHookThreads), 0, st, sign_bits, x, dtype, n_rows, out);
+    if (d == 64) hipLaunchKernelGGL((k_rotate<64>), grid, dim3(kHookThreads), 0, st, sign_bits, x, dtype, n_rows, out);
+    else if (d == 128) hipLaunchKernelGGL((k_rotate<128>), grid, dim3(kHookThreads), 0, st, sign_bits, x, dtype, n_rows, out);
     else hipLaunchKernelGGL((k_rotate<256>), grid, dim3(kHookThreads), 0, st, sign_bits, x, dtype, n_rows, out);
     return hipGetLastError();
 }
@@ -140,7 +147,8 @@ hipError_t launch_scores(int d, const ScoreArgs &a, hipStream_t st) {
     const int64_t T = a.n_packed + a.n_ring;
     if (T == 0) return hipSuccess;
     const dim3 grid((unsigned)((T + kHookThreads - 1) / kHookThreads), (unsigned)(a.batch * a.hq));
-    if (d == 128) hipLaunchKernelGGL((k_scores<128>), grid, dim3(kHookThreads), 0, st, a);
+    if (d == 64) hipLaunchKernelGGL((k_scores<64>), grid, dim3(kHookThreads), 0, st, a);
+    else if (d == 128) hipLaunchKernelGGL((k_scores<128>), grid, dim3(kHookThreads), 0, st, a);
     else hipLaunchKernelGGL((k_scores<256>), grid, dim3(kHookThreads), 0, st, a);
     return hipGetLastError();
 }

@@ -152,7 +152,7 @@ extern "C" tq_status tq_build_tables(const tq_config *cfg, uint64_t seed, void *
     for (int i = 0; i + 1 < L; ++i) bf[i] = (float)(0.5 * ((double)cf[i] + (double)cf[i + 1]));
     // the decode's integer score path (head_dim 128) takes c * 2^Sc (Sc: the power of two that
     // keeps every |c * 2^Sc| below 2^14) as exact integers
-    if (d == 128 && !tq::centroids_are_scaled_integers(cf, L)) return TQ_ERR_UNSUPPORTED;
+    if (d == 128 && cfg->key_bits == 3 && !tq::centroids_are_scaled_integers(cf, L)) return TQ_ERR_UNSUPPORTED;
     std::vector<int8_t> sg(d);
     uint16_t *S = reinterpret_cast<uint16_t *>(p + tq::kTableSOffset);
     st = tq_build_rotation(d, seed, sg.data(), S);
@@ -226,8 +226,9 @@ int device_cus() {
 tq_status check_config(const tq_config &c) {
     if (c.head_dim <= 0 || c.key_bits <= 0 || c.value_bits <= 0 || c.group_size <= 0 || c.buffer_size <= 0)
         return TQ_ERR_INVALID_ARG;
-    if (c.head_dim != 128 && c.head_dim != 256) return TQ_ERR_UNSUPPORTED;
-    if (c.key_bits != 3) return TQ_ERR_UNSUPPORTED;
+    if (c.head_dim != 64 && c.head_dim != 128 && c.head_dim != 256) return TQ_ERR_UNSUPPORTED;
+    if (c.key_bits < 1 || c.key_bits > 4) return TQ_ERR_UNSUPPORTED;
+    if (c.head_dim == 256 && c.key_bits != 3) return TQ_ERR_UNSUPPORTED;
     if (c.value_bits != 2 && c.value_bits != 4) return TQ_ERR_UNSUPPORTED;
     if (c.group_size != 32) return TQ_ERR_UNSUPPORTED;
     if (c.buffer_size > 1024) return TQ_ERR_UNSUPPORTED;

@@ -75,7 +75,7 @@ struct DecodeArgs {
     int64_t per_split;  // packed tokens per split
     float scale;
     float *out;
-    float *prep;         // d = 256: [batch*hkv][2][G][D], q' then w of the slice's query heads
+    float *prep;         // d = 256 and k_decode_any: [batch*hkv][2][G][D], q' then w of the slice's query heads
     // ragged batches: per-sequence lengths [batch] on the device (n_packed / n_ring are then
     // their maxima, each length clamped to [0, maximum]); null: every sequence n_packed / n_ring
     const int64_t *seq_packed;
@@ -104,8 +104,12 @@ __device__ inline int64_t record_index(const int32_t *bt, int pt, int pps, int64
     return p * pt + t % pt;
 }
 
-hipError_t launch_quantize(int d, int vb, tq_dtype dt, const QuantArgs &a, hipStream_t st);
-hipError_t launch_decode(int d, int vb, int G, const DecodeArgs &a, hipStream_t st);
+hipError_t launch_quantize(int d, int kb, int vb, tq_dtype dt, const QuantArgs &a, hipStream_t st);
+hipError_t launch_decode(int d, int kb, int vb, int G, const DecodeArgs &a, hipStream_t st);
+// decode through k_decode_any (the key widths other than 3 bits, and head_dim 64), whose
+// workspace holds the prepared queries
+bool decode_uses_any(int d, int kb);
+void launch_decode_any_main(int d, int kb, int vb, int G, const DecodeArgs &a, hipStream_t st);
 hipError_t launch_ring_append(int d, tq_dtype dt, const void *kn, const void *vn, uint16_t *rk, uint16_t *rv,
                               int n_slices, int buffer_size, int slot, hipStream_t st);
 

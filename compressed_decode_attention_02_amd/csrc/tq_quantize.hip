@@ -43,7 +43,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // tile shape: RR tokens per wave, 32 (v_mfma_f32_32x32x16, d = 128 only) or 16
 // (v_mfma_f32_16x16x32)
-template <int D, int RR>
+template <int D, int RR, int KB = 3>
 struct KeyShape {
     static constexpr int R = RR;                  // tokens per wave (MFMA M = N)
     static constexpr int KG = 64 / R;             // lanes per token
@@ -53,10 +53,12 @@ struct KeyShape {
     static constexpr int RPT = R * R / 64;        // accumulator registers per tile and lane
     static constexpr int NV = D / KG;             // coordinates per lane (64, or 32 at d = 128, R = 16)
     static constexpr int NQ = NV / 8;             // projection k-steps
-    static constexpr int KW = D / 8;              // key words per record
-    static constexpr int NP = NV / 8;             // u32 registers of nibble half-word pairs
+    static constexpr int KW = (KB + 1) * D / 32;  // key words per record
+    static constexpr int NP = NV / 8;             // u32 registers of nibble half-word pairs (KB = 3)
     static constexpr int NVG = NV / 32;           // value groups per lane
-    static_assert(R == 16 || (R == 32 && D == 128), "tile shapes");
+    static constexpr int NCW = KB * D / 32;       // code-plane words (KB = 1, 2, 4)
+    static_assert(R == 16 || (R == 32 && D <= 128), "tile shapes");
+    static_assert(KB == 3 || R == 32, "two-plane key records are assembled from 32-token tiles");
 };
 
 template <int R>
@@ -180,7 +182,7 @@ constexpr int kKeyGroupWaves = 12;
 // once the waves have a tile each on average, else 4, so that short inputs spread over more
 // CUs (d = 256: its LDS copy of S allows one workgroup per CU, so always 12)
 static int quant_waves_per_group(int d, int64_t tiles, int64_t cus) {
-    if (d != 128) return 12;
+    if (d == 256) return 12;
     return tiles >= cus * 12 ? 12 : 4;
 }
 template <int D>
@@ -206,11 +208,14 @@ __device__ __forceinline__ void split_row(int64_t r, int64_t n_tok, double inv, 
     t = rem;
 }
 
-template <typename Tag, int D, int VB, int RR>
+template <typename Tag, int D, int VB, int RR, int KB>
 __global__ __launch_bounds__(64 * kKeyGroupWaves<D>)
 __attribute__((amdgpu_waves_per_eu(kKeyWavesPerSimd<D>, kKeyWavesPerSimd<D>)))
 void k_quant_kv(QuantArgs a) {
-    using S = KeyShape<D, RR>;
+    using S = KeyShape<D, RR, KB>;
+    constexpr int L = 1 << KB;         // codebook size
+    constexpr int NPOS = L / 2;        // cells on each side of 0 (the codebook is antisymmetric)
+    constexpr uint32_t kTag = L - 1;   // tag bits of the tagged centroids
     constexpr int R = S::R;
     constexpr bool kF32 = std::is_same_v<Tag, f32_tag>;
     constexpr bool kF16 = std::is_same_v<Tag, f16_tag>;
@@ -227,7 +232,7 @@ void k_quant_kv(QuantArgs a) {
     {
         // 16-byte chunks of S: every load of the thread issued before the LDS stores (the
         // block has at least 256 threads at d = 128 and 768 at d = 256)
-        constexpr int NCH = D * D / 8, KMAX = D == 128 ? NCH / 256 : (NCH + 767) / 768;
+        constexpr int NCH = D * D / 8, KMAX = D <= 128 ? NCH / 256 : (NCH + 767) / 768;
         uint4 x[KMAX];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
@@ -258,9 +263,7 @@ void k_quant_kv(QuantArgs a) {
     // raw inputs of one row: k-step s holds coordinates K s + 8 g + 0..7 (rows past the end
     // are clamped to the last row, so every lane reads real data)
     uint32_t raw[S::NS][RAWW];
-    auto load_raw = [&](int64_t row) {
-        int64_t sl, t;
-        split_row(row < a.n_rows ? row : a.n_rows - 1, a.n_tokens, inv_tok, sl, t);
+    auto load_raw = [&](int64_t sl, int64_t t) {
         const int64_t in_off = sl * a.in_slice_stride + t * D + 8 * g;
 #pragma unroll
         for (int s = 0; s < S::NS; ++s) {
@@ -297,15 +300,19 @@ void k_quant_kv(QuantArgs a) {
                 hf[v][w] = pair;
             }
     }
-    // the positive decision boundaries b_4 < b_5 < b_6 (the codebook is symmetric)
-    const float B4 = a.boundaries[4], B5 = a.boundaries[5], B6 = a.boundaries[6];
-    // scaled positive centroids 2^8 c[4+k], tagged with their index 4 + k in the three low
+    // the positive decision boundaries b_{L/2} < ... < b_{L-2} (the codebook is antisymmetric
+    // with b_{L/2-1} = 0)
+    float BP[NPOS > 1 ? NPOS - 1 : 1];
+#pragma unroll
+    for (int k = 0; k + 1 < NPOS; ++k) BP[k] = a.boundaries[NPOS + k];
+    // scaled positive centroids 2^8 c[L/2+k], tagged with their index L/2 + k in the KB low
     // mantissa bits (the stored centroids are binary16 values, so those bits are zero)
-    float M0 = __uint_as_float((__float_as_uint(256.f * a.centroids[4]) & ~7u) | 4u);
-    float M1 = __uint_as_float((__float_as_uint(256.f * a.centroids[5]) & ~7u) | 5u);
-    float M2 = __uint_as_float((__float_as_uint(256.f * a.centroids[6]) & ~7u) | 6u);
-    float M3 = __uint_as_float((__float_as_uint(256.f * a.centroids[7]) & ~7u) | 7u);
-    asm volatile("" : "+v"(M0), "+v"(M1), "+v"(M2), "+v"(M3));
+    float M[NPOS];
+#pragma unroll
+    for (int k = 0; k < NPOS; ++k) {
+        M[k] = __uint_as_float((__float_as_uint(256.f * a.centroids[NPOS + k]) & ~kTag) | (uint32_t)(NPOS + k));
+        asm volatile("" : "+v"(M[k]));
+    }
 
     for (;;) {
         int64_t tile = 0;
@@ -314,13 +321,12 @@ void k_quant_kv(QuantArgs a) {
                ((int64_t)__builtin_amdgcn_readfirstlane((int)(tile >> 32)) << 32);
         if (tile >= n_tiles) break;
         const int64_t row = tile * R + n;
-        load_raw(row);
-        int64_t rec = -1;  // destination record, -1 past the last row
-        if (row < a.n_rows) {
-            int64_t sl, t;
-            split_row(row, a.n_tokens, inv_tok, sl, t);
-            rec = record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, a.err, sl, a.dst_offset + t);
-        }
+        int64_t sl, t;
+        split_row(row < a.n_rows ? row : a.n_rows - 1, a.n_tokens, inv_tok, sl, t);
+        load_raw(sl, t);
+        // destination record, -1 past the last row
+        const int64_t rec =
+            row < a.n_rows ? record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, a.err, sl, a.dst_offset + t) : -1;
 
         // ---- the tile's values: this lane's NV coordinates g NV .. g NV + NV - 1 of its token
         //      (NVG groups of 32), loaded with the keys and quantised first (their registers are
@@ -329,8 +335,6 @@ void k_quant_kv(QuantArgs a) {
         constexpr int VCH = NVG * (kF32 ? 8 : 4);  // 16-byte chunks of the lane's values
         uint4 vr[VCH];
         {
-            int64_t sl, t;
-            split_row(row < a.n_rows ? row : a.n_rows - 1, a.n_tokens, inv_tok, sl, t);
             const uint4 *vp = reinterpret_cast<const uint4 *>(static_cast<const unsigned char *>(a.v) +
                                                               ((sl * a.in_slice_stride + t * D + S::NV * g) * (kF32 ? 4 : 2)));
 #pragma unroll
@@ -467,8 +471,19 @@ void k_quant_kv(QuantArgs a) {
         const float knorm = sqrtf(ss);
         const float rsd = sqrtf((float)D * ss);
         const float inv256 = ss > 0.f ? 256.f / rsd : 0.f;
-        const float T4 = B4 * rsd, T5 = B5 * rsd, T6 = B6 * rsd;
-        uint32_t P[S::NP];  // nibble half-words: slot f at bit 4 (f & 7) of P[f >> 3]
+        float T[NPOS > 1 ? NPOS - 1 : 1];
+#pragma unroll
+        for (int k = 0; k + 1 < NPOS; ++k) T[k] = BP[k] * rsd;
+        uint32_t P[S::NP];  // KB = 3: nibble half-words: slot f at bit 4 (f & 7) of P[f >> 3]
+        // KB = 1, 2, 4: the lane's fields of the code plane and of the sign plane, at the
+        // positions of lane group 0 (lane group g is shifted into place at the end)
+        uint32_t CW[KB == 3 ? 1 : S::NCW], SW[KB == 3 ? 1 : D / 32];
+        if constexpr (KB != 3) {
+#pragma unroll
+            for (int i = 0; i < S::NCW; ++i) CW[i] = 0;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) SW[i] = 0;
+        }
         float ggp[4] = {0.f, 0.f, 0.f, 0.f};
         // negated scaled residual -r' as fp16 hi + lo; projection k-step q = slots 8q .. 8q+7
         u32x4_t rhi[S::NQ], rlo[S::NQ];
@@ -489,21 +504,32 @@ void k_quant_kv(QuantArgs a) {
             for (int o = 0; o < 4; ++o) {
                 const float yv = y[(f4 + o) / S::RPT][(f4 + o) % S::RPT];
                 const float ay = fabsf(yv);
-                // signed tagged centroid: sign = (y <= 0), low bits = 4 + #{boundaries passed}
-                float mt = ay > T4 ? M1 : M0;
-                mt = ay > T5 ? M2 : mt;
-                mt = ay > T6 ? M3 : mt;
+                // signed tagged centroid: sign = (y <= 0), low bits = L/2 + #{boundaries passed}
+                float mt = M[0];
+#pragma unroll
+                for (int k = 0; k + 1 < NPOS; ++k) mt = ay > T[k] ? M[k + 1] : mt;
                 sb[o] = __float_as_uint(yv > 0.f ? mt : -mt);
                 // -r' = c[idx] - u'
-                nr[o] = fmaf(-yv, inv256, __uint_as_float(sb[o] & ~7u));
+                nr[o] = fmaf(-yv, inv256, __uint_as_float(sb[o] & ~kTag));
                 ggp[o] = fmaf(nr[o], nr[o], ggp[o]);
             }
-            // slots (0, 2) and (1, 3) of the four at nibble offsets 0 and 4 (plus 16 for the
-            // upper four of a word); materialised here so that the centroids die now
-            uint32_t q4 = pair_idx(sb[0], sb[2]) | (pair_idx(sb[1], sb[3]) << 4);
-            asm volatile("" : "+v"(q4));
-            if (f4 & 4) P[f4 >> 3] |= q4 << 16;
-            else P[f4 >> 3] = q4;
+            if constexpr (KB == 3) {
+                // slots (0, 2) and (1, 3) of the four at nibble offsets 0 and 4 (plus 16 for the
+                // upper four of a word); materialised here so that the centroids die now
+                uint32_t q4 = pair_idx(sb[0], sb[2]) | (pair_idx(sb[1], sb[3]) << 4);
+                asm volatile("" : "+v"(q4));
+                if (f4 & 4) P[f4 >> 3] |= q4 << 16;
+                else P[f4 >> 3] = q4;
+            } else {
+                // index = tag on the positive side, tag ^ (L - 1) = L/2 - 1 - k otherwise, into
+                // the code plane at coordinate slot_coord(f, 0)
+#pragma unroll
+                for (int o = 0; o < 4; ++o) {
+                    const int c = slot_coord<D, R>(f4 + o, 0);
+                    const uint32_t ix = (sb[o] ^ (uint32_t)((int32_t)sb[o] >> 31)) & kTag;
+                    CW[c / (32 / KB)] |= ix << (KB * (c % (32 / KB)));
+                }
+            }
 #pragma unroll
             for (int o = 0; o < 4; o += 2) {
                 const int f2 = f4 + o;
@@ -526,25 +552,47 @@ void k_quant_kv(QuantArgs a) {
 
         // ---- QJL on the matrix cores: D[j][token] = -sum_c S[j][c] r'[c]; lane (n, g)
         //      receives the projections j = slot_coord(f, g) of its own coordinates
+        //      The S fragments of output tile jt2 + 1 are read from LDS while the sign bits of
+        //      tile jt2 are extracted, so the products wait on one LDS read latency at most.
         uint32_t se = 0, so = 0;  // sign bytes of the first half of the current word
-#pragma unroll
-        for (int jt2 = 0; jt2 < S::NJ; ++jt2) {
-            __builtin_amdgcn_sched_barrier(0);
-            acc_t<R> acc = acc_t<R>{};
+        u32x4_t sf[S::NQ];
+        auto load_sfrag = [&](int jt2) {
             const uint16_t *srow = sS + (R * jt2 + n) * kSRow<D>;
 #pragma unroll
             for (int q = 0; q < S::NQ; ++q) {
                 const uint2 s0 = *reinterpret_cast<const uint2 *>(srow + slot_coord<D, R>(8 * q, g));
                 const uint2 s1 = *reinterpret_cast<const uint2 *>(srow + slot_coord<D, R>(8 * q + 4, g));
-                const u32x4_t A = {s0.x, s0.y, s1.x, s1.y};
-                acc = mfma_f16<R>(A, rhi[q], acc);
-                acc = mfma_f16<R>(A, rlo[q], acc);
+                sf[q] = u32x4_t{s0.x, s0.y, s1.x, s1.y};
             }
+        };
+        __builtin_amdgcn_sched_barrier(0);
+        load_sfrag(0);
+#pragma unroll
+        for (int jt2 = 0; jt2 < S::NJ; ++jt2) {
+            __builtin_amdgcn_sched_barrier(0);
+            acc_t<R> acc = acc_t<R>{};
+#pragma unroll
+            for (int q = 0; q < S::NQ; ++q) {
+                acc = mfma_f16<R>(sf[q], rhi[q], acc);
+                acc = mfma_f16<R>(sf[q], rlo[q], acc);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (jt2 + 1 < S::NJ) load_sfrag(jt2 + 1);
             // the accumulator holds -(S r')_j: its sign bit is set exactly when the projection
             // is positive (or a zero came out as -0); it goes to bit 4 (f & 7) + 3 of
             // P[f >> 3].  Byte permutes replicate the sign bits of slots (f, f + 2) into bytes
             // (0, 1) of a word for f & 7 < 4, else bytes (2, 3), and of slots (f + 1, f + 3)
             // likewise into a second word shifted by 4 at the end.
+            if constexpr (KB != 3) {
+                // sign bit of slot f (set when the projection is positive) to bit
+                // slot_coord(f, 0) mod 32 of sign word slot_coord(f, 0) / 32
+#pragma unroll
+                for (int r = 0; r < S::RPT; ++r) {
+                    const int c = slot_coord<D, R>(jt2 * S::RPT + r, 0);
+                    SW[c / 32] |= (__float_as_uint(acc[r]) >> 31) << (c % 32);
+                }
+                continue;
+            }
 #pragma unroll
             for (int r4 = 0; r4 < S::RPT; r4 += 4) {
                 const int f = jt2 * S::RPT + r4;
@@ -561,6 +609,34 @@ void k_quant_kv(QuantArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
 
+        if constexpr (KB != 3) {
+            // ---- two-plane record: lane group 1 holds the coordinates 4 further of every
+            //      field it shares a word with; shift into place, OR the two lanes' words
+            //      (lanes n and n + 32) and store from lane group 0
+            static_assert(R == 32 && S::KG == 2 && S::KW % 2 == 0, "two lane groups per token");
+#pragma unroll
+            for (int i = 0; i < S::NCW; ++i) {
+                const uint32_t x = CW[i] << (4 * KB * g);
+                CW[i] = x | (uint32_t)__shfl_xor((int)x, 32);
+            }
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) {
+                const uint32_t x = SW[i] << (4 * g);
+                SW[i] = x | (uint32_t)__shfl_xor((int)x, 32);
+            }
+            if (rec >= 0 && g == 0) {
+                uint32_t outw[S::KW];
+#pragma unroll
+                for (int i = 0; i < S::NCW; ++i) outw[i] = CW[i];
+#pragma unroll
+                for (int i = 0; i < D / 32; ++i) outw[S::NCW + i] = SW[i];
+                uint2 *d2 = reinterpret_cast<uint2 *>(a.kw + rec * S::KW);
+#pragma unroll
+                for (int i = 0; i < S::KW / 2; ++i) d2[i] = make_uint2(outw[2 * i], outw[2 * i + 1]);
+                *reinterpret_cast<float2 *>(a.kn + rec * 2) = make_float2(knorm, sqrtf(gg) * (1.0f / 256.f));
+            }
+            continue;
+        }
         // ---- assemble key words: half-words of word w live in lanes g (even) and g ^ 1
         uint32_t outw[S::NP];
 #pragma unroll
@@ -585,10 +661,12 @@ void k_quant_kv(QuantArgs a) {
             uint32_t *dst = a.kw + rec * S::KW;
             const int odd = g & 1;
             if constexpr (R == 32) {
-                // slots of P[p] cover words 2p, 2p+1; even lanes store words 0..7, odd 8..15
-                uint4 *d4 = reinterpret_cast<uint4 *>(dst + 8 * odd);
-                d4[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-                d4[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
+                // slots of P[p] cover words 2p, 2p+1; even lanes store words 0..NP-1, odd
+                // NP..2NP-1
+                uint4 *d4 = reinterpret_cast<uint4 *>(dst + S::NP * odd);
+#pragma unroll
+                for (int i = 0; i < S::NP / 4; ++i)
+                    d4[i] = make_uint4(outw[4 * i], outw[4 * i + 1], outw[4 * i + 2], outw[4 * i + 3]);
             } else {
 #pragma unroll
                 for (int p = 0; p < S::NP / 2; ++p) {
@@ -606,44 +684,69 @@ void k_quant_kv(QuantArgs a) {
 
 // ------------------------------------------------------------------------------ values
 // ------------------------------------------------------------------------------ launch
-template <typename Tag, int D, int VB, int RR>
+template <typename Tag, int D, int VB, int RR, int KB>
 static void launch_kv_r(const QuantArgs &a, int64_t cus, hipStream_t st) {
     const int64_t tiles = (a.n_rows + RR - 1) / RR;
     const int nw = quant_waves_per_group(D, tiles, cus);
     const int64_t per_cu = kKeyGroupWaves<D> / nw;  // workgroups of nw waves resident per CU
     int64_t grid = (tiles + nw - 1) / nw;
     if (grid > cus * per_cu) grid = cus * per_cu;
-    hipLaunchKernelGGL((k_quant_kv<Tag, D, VB, RR>), dim3((unsigned)grid), dim3(64 * nw), 0, st, a);
+    hipLaunchKernelGGL((k_quant_kv<Tag, D, VB, RR, KB>), dim3((unsigned)grid), dim3(64 * nw), 0, st, a);
 }
 
-// d = 128: 32-token tiles, or 16-token tiles (half the arithmetic per wave, twice the waves)
-// while the 32-token ones would not give every CU one: a short input such as a ring flush is
-// bound by the latency of one tile
-template <typename Tag, int D, int VB>
+// d = 128, 3-bit keys: 32-token tiles, or 16-token tiles (half the arithmetic per wave, twice
+// the waves) while the 32-token ones would not give every CU one: a short input such as a
+// ring flush is bound by the latency of one tile.  d = 64 and the two-plane key widths: 32-token
+// tiles (a lane then holds whole value groups and its token's other lane group is lane + 32).
+// d = 256: 16-token tiles.
+template <typename Tag, int D, int VB, int KB>
 static void launch_kv_t(const QuantArgs &a, hipStream_t st) {
     const int64_t cus = (int64_t)device_cus();
-    if (D == 128 && (a.n_rows + 31) / 32 >= cus) launch_kv_r<Tag, D, VB, D == 128 ? 32 : 16>(a, cus, st);
-    else launch_kv_r<Tag, D, VB, 16>(a, cus, st);
+    if constexpr (D == 256) {
+        launch_kv_r<Tag, D, VB, 16, KB>(a, cus, st);
+    } else if constexpr (D == 128 && KB == 3) {
+        if ((a.n_rows + 31) / 32 >= cus) launch_kv_r<Tag, D, VB, 32, KB>(a, cus, st);
+        else launch_kv_r<Tag, D, VB, 16, KB>(a, cus, st);
+    } else {
+        launch_kv_r<Tag, D, VB, 32, KB>(a, cus, st);
+    }
+}
+
+template <typename Tag, int D, int VB>
+static void launch_kv_kb(int kb, const QuantArgs &a, hipStream_t st) {
+    if constexpr (D == 256) {
+        launch_kv_t<Tag, D, VB, 3>(a, st);
+    } else {
+        switch (kb) {
+            case 1: launch_kv_t<Tag, D, VB, 1>(a, st); break;
+            case 2: launch_kv_t<Tag, D, VB, 2>(a, st); break;
+            case 4: launch_kv_t<Tag, D, VB, 4>(a, st); break;
+            default: launch_kv_t<Tag, D, VB, 3>(a, st); break;
+        }
+    }
 }
 
 template <typename Tag>
-static hipError_t launch_quantize_d(int d, int vb, const QuantArgs &a, hipStream_t st) {
-    if (d == 128) {
-        if (vb == 2) launch_kv_t<Tag, 128, 2>(a, st);
-        else launch_kv_t<Tag, 128, 4>(a, st);
+static hipError_t launch_quantize_d(int d, int kb, int vb, const QuantArgs &a, hipStream_t st) {
+    if (d == 64) {
+        if (vb == 2) launch_kv_kb<Tag, 64, 2>(kb, a, st);
+        else launch_kv_kb<Tag, 64, 4>(kb, a, st);
+    } else if (d == 128) {
+        if (vb == 2) launch_kv_kb<Tag, 128, 2>(kb, a, st);
+        else launch_kv_kb<Tag, 128, 4>(kb, a, st);
     } else {
-        if (vb == 2) launch_kv_t<Tag, 256, 2>(a, st);
-        else launch_kv_t<Tag, 256, 4>(a, st);
+        if (vb == 2) launch_kv_kb<Tag, 256, 2>(kb, a, st);
+        else launch_kv_kb<Tag, 256, 4>(kb, a, st);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(int d, int vb, tq_dtype dt, const QuantArgs &a, hipStream_t st) {
+hipError_t launch_quantize(int d, int kb, int vb, tq_dtype dt, const QuantArgs &a, hipStream_t st) {
     if (a.n_rows == 0) return hipSuccess;
     switch (dt) {
-        case TQ_F32: return launch_quantize_d<f32_tag>(d, vb, a, st);
-        case TQ_BF16: return launch_quantize_d<bf16_tag>(d, vb, a, st);
-        default: return launch_quantize_d<f16_tag>(d, vb, a, st);
+        case TQ_F32: return launch_quantize_d<f32_tag>(d, kb, vb, a, st);
+        case TQ_BF16: return launch_quantize_d<bf16_tag>(d, kb, vb, a, st);
+        default: return launch_quantize_d<f16_tag>(d, kb, vb, a, st);
     }
 }
 

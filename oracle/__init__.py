@@ -73,9 +73,11 @@ def lib():
     L.orc_quantize_values.restype = None
     L.orc_quantize_values.argtypes = [_int, _int, _int, _dp, _i64, _u8, _u16, _dp]
     L.orc_pack_keys.restype = None
-    L.orc_pack_keys.argtypes = [_int, _u8, _u8, _i64, _u32]
+    L.orc_pack_keys.argtypes = [_int, _int, _u8, _u8, _i64, _u32]
     L.orc_unpack_keys.restype = None
-    L.orc_unpack_keys.argtypes = [_int, _u32, _i64, _u8, _u8]
+    L.orc_unpack_keys.argtypes = [_int, _int, _u32, _i64, _u8, _u8]
+    L.orc_key_words.restype = _int
+    L.orc_key_words.argtypes = [_int, _int]
     L.orc_pack_values.restype = None
     L.orc_pack_values.argtypes = [_int, _int, _u8, _i64, _u32]
     L.orc_unpack_values.restype = None
@@ -210,20 +212,25 @@ def quantize_values(v: np.ndarray, vb: int, group: int = 32):
     return {"code": code, "scale": sc, "margin": m}
 
 
-def pack_keys(idx, z) -> np.ndarray:
+def key_words(d: int, kb: int = 3) -> int:
+    """Words of one key record: (kb + 1) d / 32 (kb codebook bits and one sign bit per coordinate)."""
+    return lib().orc_key_words(d, kb)
+
+
+def pack_keys(idx, z, kb: int = 3) -> np.ndarray:
     idx = _c(idx, np.uint8)
     rows, d = idx.shape
-    out = np.zeros((rows, d // 8), np.uint32)
-    lib().orc_pack_keys(d, idx, _c(z, np.uint8), rows, out)
+    out = np.zeros((rows, key_words(d, kb)), np.uint32)
+    lib().orc_pack_keys(d, kb, idx, _c(z, np.uint8), rows, out)
     return out
 
 
-def unpack_keys(words, d: int):
-    words = _c(words, np.uint32).reshape(-1, d // 8)
+def unpack_keys(words, d: int, kb: int = 3):
+    words = _c(words, np.uint32).reshape(-1, key_words(d, kb))
     rows = words.shape[0]
     idx = np.zeros((rows, d), np.uint8)
     z = np.zeros((rows, d), np.uint8)
-    lib().orc_unpack_keys(d, words, rows, idx, z)
+    lib().orc_unpack_keys(d, kb, words, rows, idx, z)
     return idx, z
 
 

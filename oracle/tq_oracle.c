@@ -372,37 +372,59 @@ void orc_quantize_values(int d, int vb, int group, const double *v, int64_t n_ro
 }
 
 /* ------------------------------------------------------------------------------ */
-/* Packed record layout (one token-head):                                          */
-/*   key word w (0 <= w < d/8) covers coordinates 8w..8w+7 as eight 4-bit nibbles: */
-/*   nibble k (bits 4k..4k+3) holds the 3-bit codebook index of coordinate 8w+k in */
-/*   its low three bits and that coordinate's QJL sign bit in its top bit;         */
-/*   value codes least-significant first: code j sits at bit vb*(j mod (32/vb)) of */
-/*   word floor(j*vb/32)  (four 2-bit codes per byte, as the pages state).         */
+/* Packed record layout (one token-head).  A key record has (kb + 1) d / 32 words.  */
+/*   kb = 3: word w (0 <= w < d/8) covers coordinates 8w..8w+7 as eight 4-bit       */
+/*   nibbles: nibble k (bits 4k..4k+3) holds the codebook index of coordinate 8w+k  */
+/*   in its low three bits and that coordinate's QJL sign bit in its top bit.        */
+/*   kb = 1, 2, 4: two planes.  The code plane (words 0 .. kb d/32 - 1) holds the    */
+/*   index of coordinate j at bit kb*(j mod (32/kb)) of word floor(j kb / 32); the   */
+/*   sign plane (the d/32 words after it) holds the sign bit of coordinate j at bit  */
+/*   j mod 32 of its word floor(j / 32).                                             */
+/*   Value codes least-significant first: code j sits at bit vb*(j mod (32/vb)) of   */
+/*   word floor(j*vb/32)  (four 2-bit codes per byte, as the pages state).           */
 /* ------------------------------------------------------------------------------ */
-void orc_pack_keys(int d, const uint8_t *idx, const uint8_t *z, int64_t n_rows, uint32_t *words)
+int orc_key_words(int d, int kb) { return (kb + 1) * d / 32; }
+
+void orc_pack_keys(int d, int kb, const uint8_t *idx, const uint8_t *z, int64_t n_rows, uint32_t *words)
 {
-    int nw = d / 8;
-    for (int64_t row = 0; row < n_rows; ++row)
-        for (int w = 0; w < nw; ++w) {
-            uint32_t x = 0;
-            for (int k = 0; k < 8; ++k) {
-                int j = 8 * w + k;
-                uint32_t nib = ((uint32_t)idx[row * d + j] & 7u) | (((uint32_t)z[row * d + j] & 1u) << 3);
-                x |= nib << (4 * k);
+    int nw = orc_key_words(d, kb);
+    for (int64_t row = 0; row < n_rows; ++row) {
+        const uint8_t *ir = idx + row * d, *zr = z + row * d;
+        uint32_t *wr = words + row * nw;
+        for (int w = 0; w < nw; ++w) wr[w] = 0;
+        for (int j = 0; j < d; ++j) {
+            uint32_t code = (uint32_t)ir[j] & ((1u << kb) - 1u), sign = (uint32_t)zr[j] & 1u;
+            if (kb == 3) {
+                wr[j / 8] |= (code | (sign << 3)) << (4 * (j % 8));
+            } else {
+                int per = 32 / kb;
+                wr[j / per] |= code << (kb * (j % per));
+                wr[kb * d / 32 + j / 32] |= sign << (j % 32);
             }
-            words[row * nw + w] = x;
         }
+    }
 }
 
-void orc_unpack_keys(int d, const uint32_t *words, int64_t n_rows, uint8_t *idx, uint8_t *z)
+void orc_unpack_keys(int d, int kb, const uint32_t *words, int64_t n_rows, uint8_t *idx, uint8_t *z)
 {
-    int nw = d / 8;
-    for (int64_t row = 0; row < n_rows; ++row)
+    int nw = orc_key_words(d, kb);
+    for (int64_t row = 0; row < n_rows; ++row) {
+        const uint32_t *wr = words + row * nw;
         for (int j = 0; j < d; ++j) {
-            uint32_t nib = (words[row * nw + j / 8] >> (4 * (j % 8))) & 15u;
-            idx[row * d + j] = (uint8_t)(nib & 7u);
-            z[row * d + j] = (uint8_t)(nib >> 3);
+            uint32_t code, sign;
+            if (kb == 3) {
+                uint32_t nib = (wr[j / 8] >> (4 * (j % 8))) & 15u;
+                code = nib & 7u;
+                sign = nib >> 3;
+            } else {
+                int per = 32 / kb;
+                code = (wr[j / per] >> (kb * (j % per))) & ((1u << kb) - 1u);
+                sign = (wr[kb * d / 32 + j / 32] >> (j % 32)) & 1u;
+            }
+            idx[row * d + j] = (uint8_t)code;
+            z[row * d + j] = (uint8_t)sign;
         }
+    }
 }
 
 void orc_pack_values(int d, int vb, const uint8_t *code, int64_t n_rows, uint32_t *words)
@@ -436,7 +458,8 @@ void orc_unpack_values(int d, int vb, const uint32_t *words, int64_t n_rows, uin
 /*                                                                                 */
 /* Arrays (slice = b * Hkv + kv head; cap = capacity of the packed store,          */
 /* buf = ring capacity):                                                           */
-/*   kw [slices][cap][d/8] u32, kn [slices][cap][2] f32 (norm, residual norm),     */
+/*   kw [slices][cap][(kb+1) d/32] u32, kn [slices][cap][2] f32 (norm, residual   */
+/*   norm),                                                                         */
 /*   vw [slices][cap][vb d/32] u32, vs [slices][cap][d/32] fp16,                   */
 /*   rk, rv [slices][buf][d] fp16, q [B][Hq][d] (double), out [B][Hq][d] (double). */
 /* ------------------------------------------------------------------------------ */
@@ -447,11 +470,10 @@ void orc_decode(int d, int kb, int vb, int group, const double *c32, const int8_
                 const uint16_t *rk, const uint16_t *rv, int buf, int n_ring,
                 const double *q, double scale, double *out, double *scores_out)
 {
-    (void)kb;
     int G = Hq / Hkv;
     int half = 1 << (vb - 1);
     int ng = d / group;
-    int nkw = d / 8, nvw = d * vb / 32;
+    int nkw = orc_key_words(d, kb), nvw = d * vb / 32;
     int64_t T = n_packed + n_ring;
     const double kqjl = sqrt(3.14159265358979323846 / 2.0) / d;
     double *S = (double *)malloc(sizeof(double) * d * d);
@@ -473,7 +495,7 @@ void orc_decode(int d, int kb, int vb, int group, const double *c32, const int8_
             }
             for (int64_t t = 0; t < n_packed; ++t) {
                 int64_t rec = sl * cap + t;
-                orc_unpack_keys(d, kw + rec * nkw, 1, idx, z);
+                orc_unpack_keys(d, kb, kw + rec * nkw, 1, idx, z);
                 double mse = 0.0, sgn = 0.0;
                 for (int j = 0; j < d; ++j) {
                     mse += qr[j] * c32[idx[j]];

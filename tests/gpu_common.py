@@ -66,11 +66,12 @@ def dev_to_stored(t):
 class Env:
     """Library tables on the device plus the oracle's own tables, for one config."""
 
-    def __init__(self, d: int, vb: int, buffer_size: int = 128, seed: int = W.TABLE_SEED):
-        self.cfg = tq.make_config(d, 3, vb, 32, buffer_size)
+    def __init__(self, d: int, vb: int, buffer_size: int = 128, seed: int = W.TABLE_SEED, kb: int = 3):
+        self.cfg = tq.make_config(d, kb, vb, 32, buffer_size)
         self.tables = tq.Tables(self.cfg, seed)
-        self.d, self.vb = d, vb
-        self.c32, self.b32 = O.stored_codebook(d, 3)
+        self.d, self.vb, self.kb = d, vb, kb
+        self.kw = O.key_words(d, kb)  # words of one key record
+        self.c32, self.b32 = O.stored_codebook(d, kb)
         self.sigma, self.S = O.tables(d, seed)
 
 
@@ -86,15 +87,16 @@ def check_quantize(env: Env, k_rows: np.ndarray, v_rows: np.ndarray, kw, kn, vw,
     oracle.  Returns a dict of window counts.  Raises AssertionError on a violation."""
     d, vb = env.d, env.vb
     rows = k_rows.shape[0]
-    ref = O.quantize_keys(k_rows, env.c32, env.b32, env.sigma, env.S)
-    g_idx, g_z = O.unpack_keys(kw, d)
+    ref = O.quantize_keys(k_rows, env.c32, env.b32, env.sigma, env.S, kb=env.kb)
+    g_idx, g_z = O.unpack_keys(kw, d, env.kb)
     idx_diff = g_idx != ref["idx"]
     bad_idx = idx_diff & (ref["u_margin"] >= WINDOW)
     assert not bad_idx.any(), f"{label}: key code mismatch outside the window at {np.argwhere(bad_idx)[:5]}"
     n_idx_win = int(idx_diff.sum())
     rows_redo = np.where(idx_diff.any(axis=1))[0]
     if rows_redo.size:
-        red = O.quantize_keys(k_rows[rows_redo], env.c32, env.b32, env.sigma, env.S, force_idx=g_idx[rows_redo])
+        red = O.quantize_keys(k_rows[rows_redo], env.c32, env.b32, env.sigma, env.S, kb=env.kb,
+                              force_idx=g_idx[rows_redo])
         for key in ("z", "rnorm", "p_margin"):
             ref[key][rows_redo] = red[key]
     z_diff = g_z != ref["z"]
@@ -183,7 +185,7 @@ def oracle_decode(env: Env, q_stored, hq, hkv, store, n_packed, ring, n_ring, sl
         else:
             rk = rv = None
             buf = 0
-        o = O.decode(d=d, kb=3, vb=env.vb, c32=env.c32, sigma=env.sigma, S_bits=env.S, B=1, Hq=hq, Hkv=hkv,
+        o = O.decode(d=d, kb=env.kb, vb=env.vb, c32=env.c32, sigma=env.sigma, S_bits=env.S, B=1, Hq=hq, Hkv=hkv,
                      kw=kw, kn=kn, vw=vw, vs=vs, cap=cap, n_packed=n_packed, rk=rk, rv=rv, buf=buf,
                      n_ring=n_ring, q=q_stored[b:b + 1], scale=1.0 / math.sqrt(d))
         outs.append(o[0])

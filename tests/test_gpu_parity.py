@@ -32,7 +32,7 @@ def _quantize_case(env, w: W.Workload, n_tokens, cap_extra=0, offset=0, label=""
     P = packed_to_np(store)
     sl = slice(offset, offset + n_tokens)
     st = check_quantize(env, k.reshape(-1, w.d).astype(np.float64), v.reshape(-1, w.d).astype(np.float64),
-                        P["kw"][:, sl].reshape(-1, w.d // 8), P["kn"][:, sl].reshape(-1, 2),
+                        P["kw"][:, sl].reshape(-1, env.kw), P["kn"][:, sl].reshape(-1, 2),
                         P["vw"][:, sl].reshape(-1, w.value_bits * w.d // 32),
                         P["vs"][:, sl].reshape(-1, w.d // 32), label=label)
     # records outside [offset, offset + n_tokens) are untouched (zero)
@@ -170,7 +170,7 @@ def test_flush_writes_records_after_the_history(torch):
 # ------------------------------------------------------------------------- decode
 
 def _decode_case(w: W.Workload, label, b_list=None, seed_layer=0):
-    env = Env(w.d, w.value_bits, buffer_size=w.buffer_size)
+    env = Env(w.d, w.value_bits, buffer_size=w.buffer_size, kb=w.key_bits)
     n_sl = w.batch * w.hkv
     (k, v), _ = W.host_kv(w, seed_layer, w.n_packed + w.n_ring)
     k = k.reshape(n_sl, -1, w.d)
@@ -239,7 +239,7 @@ def test_decode_slices_not_a_multiple_of_eight(torch):
 def _step_case(w: W.Workload, fill: int, label: str):
     """Two identical stores and rings, `fill` ring tokens; returns the fused step's and the
     two-call path's outputs, rings and stores."""
-    env = Env(w.d, w.value_bits, buffer_size=w.buffer_size)
+    env = Env(w.d, w.value_bits, buffer_size=w.buffer_size, kb=w.key_bits)
     n_sl = w.batch * w.hkv
     (k, v), _ = W.host_kv(w, 0, w.n_packed + fill + 1)
     k = k.reshape(n_sl, -1, w.d)
@@ -346,7 +346,7 @@ def test_decode_ragged_batch(torch):
     for w, lens in ((W.custom(3, batch=6, n_packed=3000, n_ring=64),
                      [(0, 0), (1, 5), (700, 64), (3000, 17), (1500, 0), (0, 33)]),
                     (W.custom(4, batch=3, n_packed=900, n_ring=128), [(900, 128), (37, 2), (450, 90)])):
-        env = Env(w.d, w.value_bits, buffer_size=w.buffer_size)
+        env = Env(w.d, w.value_bits, buffer_size=w.buffer_size, kb=w.key_bits)
         n_sl = w.batch * w.hkv
         (k, v), _ = W.host_kv(w, 0, w.n_packed + w.n_ring)
         k = k.reshape(n_sl, -1, w.d)
@@ -384,7 +384,7 @@ def test_decode_ragged_batch(torch):
         np.testing.assert_array_equal(out.cpu().numpy(), g2.astype(np.float32))
 
 
-@pytest.mark.parametrize("case", ["d128_v4", "d256_v4"])
+@pytest.mark.parametrize("case", ["d128_v4", "d256_v4", "d64_kb2"])
 def test_paged_store_matches_contiguous(torch, case):
     """A paged store (pages in a seeded random order, spare pages in the pool) holds exactly the
     contiguous store's records, and every decode entry point reads it to the same results bit
@@ -393,10 +393,13 @@ def test_paged_store_matches_contiguous(torch, case):
     if case == "d128_v4":
         w = W.custom(3, batch=2, n_packed=600, n_ring=64, buffer_size=64)
         pt, pps = 64, 12                   # capacity 768 >= 600 + 64 + 1
-    else:
+    elif case == "d256_v4":
         w = W.custom(4, batch=2, n_packed=500, n_ring=32, buffer_size=32)
         pt, pps = 32, 18                   # capacity 576 >= 500 + 32 + 1
-    env = Env(w.d, w.value_bits, buffer_size=w.buffer_size)
+    else:
+        w = W.custom(2, d=64, key_bits=2, batch=2, hq=8, hkv=2, n_packed=600, n_ring=64, buffer_size=64)
+        pt, pps = 64, 12                   # capacity 768 >= 600 + 64 + 1
+    env = Env(w.d, w.value_bits, buffer_size=w.buffer_size, kb=w.key_bits)
     n_sl = w.batch * w.hkv
     (k, v), _ = W.host_kv(w, 0, w.n_packed + w.n_ring + 1)
     k = k.reshape(n_sl, -1, w.d)
@@ -629,7 +632,9 @@ def test_decode_scores_hook(torch):
     ring: packed tokens (the estimator) and ring tokens (exact products), both head sizes,
     GQA, a paged store.  Per (batch, head): max |s - s*| / max |s*| <= 1e-5."""
     cases = ((W.custom(2, batch=2, n_packed=700, n_ring=40), "d128 b2"),
-             (W.custom(4, batch=1, hq=8, hkv=2, n_packed=300, n_ring=20), "d256 G=4"))
+             (W.custom(4, batch=1, hq=8, hkv=2, n_packed=300, n_ring=20), "d256 G=4"),
+             (W.custom(2, d=64, key_bits=1, batch=1, hq=8, hkv=2, n_packed=300, n_ring=20), "d64 kb1"),
+             (W.custom(2, d=128, key_bits=4, batch=1, hq=8, hkv=2, n_packed=300, n_ring=20), "d128 kb4"))
     for w, label in cases:
         env, store, ring, q, ws, g, _ = _decode_case(w, label)
         qd = to_dev(q, w.in_dtype)
@@ -644,7 +649,7 @@ def test_decode_scores_hook(torch):
         ref_all = []
         for b in range(w.batch):
             sl = slice(b * w.hkv, (b + 1) * w.hkv)
-            _, ref = O.decode(d=w.d, kb=3, vb=w.value_bits, c32=env.c32, sigma=env.sigma, S_bits=env.S, B=1, Hq=w.hq,
+            _, ref = O.decode(d=w.d, kb=w.key_bits, vb=w.value_bits, c32=env.c32, sigma=env.sigma, S_bits=env.S, B=1, Hq=w.hq,
                               Hkv=w.hkv, kw=P["kw"][sl], kn=P["kn"][sl], vw=P["vw"][sl], vs=P["vs"][sl],
                               cap=store.capacity, n_packed=w.n_packed,
                               rk=ring.k[sl].cpu().numpy().view(np.uint16), rv=ring.v[sl].cpu().numpy().view(np.uint16),
@@ -674,3 +679,97 @@ def test_append_flush_decode_sequence(torch):
     g2, q_stored, _ = run_decode(env, q, "bf16", w.batch, w.hq, w.hkv, store, n_packed, None, 0)
     ref = oracle_decode(env, q_stored, w.hq, w.hkv, store, n_packed, None, 0, b_list=list(range(w.batch)))
     assert_decode_close(g2, ref, "after flush")
+
+
+# ------------------------------------------------------------------------- key widths 1, 2, 4 and head_dim 64
+# (two-plane key records; decode through k_decode_any)
+
+WIDTHS = [(64, 1), (64, 2), (64, 3), (64, 4), (128, 1), (128, 2), (128, 4)]
+
+
+@pytest.mark.parametrize("d,kb", WIDTHS)
+def test_quantize_key_widths(torch, d, kb):
+    """Codes, signs, norms, value codes and scales of every key width against the oracle, for
+    bf16 (values 2-bit) and fp32 (values 4-bit) inputs: 3 slices x 211 tokens, so 32-token
+    tiles with a ragged last one, at a store offset."""
+    for vb, dt in ((2, "bf16"), (4, "f32")):
+        w = W.custom(2, d=d, key_bits=kb, batch=1, hkv=3, value_bits=vb, in_dtype=dt)
+        env = Env(d, vb, kb=kb)
+        _quantize_case(env, w, 211, cap_extra=3, offset=5, label=f"d{d} kb{kb} v{vb} {dt}")
+
+
+@pytest.mark.parametrize("d,kb", WIDTHS)
+def test_decode_key_widths(torch, d, kb):
+    """Decode over packed records of every key width plus the ring, against the oracle on the
+    same bytes: GQA groups 4 (several splits and the merge), 1 and 8, ring only, packed only."""
+    _decode_case(W.custom(2, d=d, key_bits=kb, batch=2, hq=8, hkv=2, n_packed=1100, n_ring=9), f"d{d} kb{kb} G=4")
+    if kb in (1, 4):
+        _decode_case(W.custom(2, d=d, key_bits=kb, batch=1, hq=4, hkv=4, n_packed=333, n_ring=70,
+                              value_bits=4), f"d{d} kb{kb} G=1 v4")
+        _decode_case(W.custom(2, d=d, key_bits=kb, batch=1, hq=16, hkv=2, n_packed=200, n_ring=3),
+                     f"d{d} kb{kb} G=8")
+        _decode_case(W.custom(2, d=d, key_bits=kb, n_packed=0, n_ring=77), f"d{d} kb{kb} ring only")
+        _decode_case(W.custom(2, d=d, key_bits=kb, n_packed=65, n_ring=0), f"d{d} kb{kb} packed only")
+
+
+@pytest.mark.parametrize("d,kb", [(64, 2), (128, 4)])
+def test_decode_step_key_widths(torch, d, kb):
+    """The fused step (append, and a full ring's flush, then decode) equals the separate calls
+    bit for bit and the oracle, on the k_decode_any path."""
+    for w, fill, label in ((W.custom(2, d=d, key_bits=kb, batch=2, hq=8, hkv=2, n_packed=600, n_ring=20), 20,
+                            f"d{d} kb{kb}"),
+                           (W.custom(2, d=d, key_bits=kb, batch=1, hq=8, hkv=2, n_packed=300, n_ring=32,
+                                     buffer_size=32), 32, f"d{d} kb{kb} flush")):
+        env, q, qd, stores, rings, outs, (n_packed, n_ring) = _step_case(w, fill, label)
+        np.testing.assert_array_equal(outs[1], outs[0], err_msg=label)
+        ref = oracle_decode(env, dev_to_stored(qd).astype(np.float64), w.hq, w.hkv, stores[1], n_packed, rings[1],
+                            n_ring, b_list=list(range(w.batch)))
+        assert_decode_close(outs[1].astype(np.float64), ref, f"step {label}")
+
+
+def test_decode_ragged_key_widths(torch):
+    """Per-sequence lengths on the k_decode_any path, each against the oracle."""
+    w = W.custom(2, d=64, key_bits=4, batch=4, hq=8, hkv=2, n_packed=1500, n_ring=40)
+    lens = [(0, 0), (1500, 40), (37, 3), (900, 0)]
+    env = Env(w.d, w.value_bits, buffer_size=w.buffer_size, kb=w.key_bits)
+    n_sl = w.batch * w.hkv
+    (k, v), _ = W.host_kv(w, 0, w.n_packed + w.n_ring)
+    k = k.reshape(n_sl, -1, w.d)
+    v = v.reshape(n_sl, -1, w.d)
+    store = quantize_gpu(env, to_dev(np.ascontiguousarray(k[:, :w.n_packed]), w.in_dtype),
+                         to_dev(np.ascontiguousarray(v[:, :w.n_packed]), w.in_dtype), n_sl, w.n_packed)
+    ring = tq.Ring(env.cfg, n_sl)
+    for t_ in range(w.n_ring):
+        tq.tq_append_ring(env.cfg, ring.struct(), to_dev(np.ascontiguousarray(k[:, w.n_packed + t_]), w.in_dtype),
+                          to_dev(np.ascontiguousarray(v[:, w.n_packed + t_]), w.in_dtype), n_sl, t_)
+    q, _ = W.host_queries(w, 0)
+    qd = to_dev(q, w.in_dtype)
+    sp = torch.tensor([a for a, _ in lens], dtype=torch.int64, device="cuda")
+    sr = torch.tensor([r for _, r in lens], dtype=torch.int32, device="cuda")
+    out = torch.zeros((w.batch, w.hq, w.d), dtype=torch.float32, device="cuda")
+    ws = tq.new_workspace(env.cfg, w.batch, w.hq, w.hkv, w.n_packed + w.n_ring)
+    tq.tq_decode_attention_ragged(env.cfg, env.tables, qd, w.batch, w.hq, w.hkv, store.struct(), sp, w.n_packed,
+                                  ring.struct(), sr, w.n_ring, 1.0 / math.sqrt(w.d), out, ws)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy().astype(np.float64)
+    q_stored = dev_to_stored(qd).astype(np.float64)
+    for b, (n_p, n_r) in enumerate(lens):
+        if n_p + n_r == 0:
+            assert not g[b].any()
+            continue
+        ref = oracle_decode(env, q_stored[b:b + 1], w.hq, w.hkv, store, n_p, ring, n_r, slice_offset=b * w.hkv,
+                            b_list=[0])
+        assert_decode_close(g[b:b + 1], ref, f"ragged d64 kb4 b{b} ({n_p} + {n_r})")
+
+
+def test_rotate_hook_d64(torch):
+    env = Env(64, 2, kb=2)
+    x = np.random.default_rng(12).standard_normal((19, 64)).astype(np.float32)
+    xd = to_dev(x, "f32")
+    out = torch.zeros((19, 64), dtype=torch.float32, device="cuda")
+    tq.tq_rotate(env.cfg, env.tables, xd, 19, out)
+    torch.cuda.synchronize()
+    ref = O.rotate(env.sigma, x.astype(np.float64))
+    g = out.cpu().numpy().astype(np.float64)
+    err = np.abs(g - ref).max(axis=1) / np.abs(ref).max(axis=1)
+    assert err.max() <= 1e-6, err.max()

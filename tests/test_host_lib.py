@@ -38,7 +38,7 @@ def test_codebook_matches_oracle(d, kb):
     np.testing.assert_array_equal(b.astype(np.float32), bo.astype(np.float32))
 
 
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("seed", [0, W.TABLE_SEED, 2**63 + 12345])
 def test_rotation_tables_match_oracle_bit_exact(d, seed):
     s, S = tq.tq_build_rotation(d, seed)
@@ -47,14 +47,16 @@ def test_rotation_tables_match_oracle_bit_exact(d, seed):
     np.testing.assert_array_equal(S, So)
 
 
-@pytest.mark.parametrize("d,vb", [(128, 2), (128, 4), (256, 4), (256, 2)])
-def test_table_blob_layout(d, vb):
-    cfg = tq.make_config(d, 3, vb)
+@pytest.mark.parametrize("d,vb,kb", [(128, 2, 3), (128, 4, 3), (256, 4, 3), (256, 2, 3), (64, 2, 1), (64, 4, 2),
+                                     (64, 2, 3), (64, 2, 4), (128, 2, 2), (128, 4, 4)])
+def test_table_blob_layout(d, vb, kb):
+    cfg = tq.make_config(d, kb, vb)
     blob = tq.tq_build_tables(cfg, W.TABLE_SEED)
     assert blob.size == tq.tq_tables_bytes(cfg) == 256 + 2 * d * d
-    c32, b32 = O.stored_codebook(d, 3)
-    np.testing.assert_array_equal(blob[0:32].view(np.float32), c32.astype(np.float32))
-    np.testing.assert_array_equal(blob[64:92].view(np.float32), b32.astype(np.float32))
+    c32, b32 = O.stored_codebook(d, kb)
+    L = 1 << kb
+    np.testing.assert_array_equal(blob[0:4 * L].view(np.float32), c32.astype(np.float32))
+    np.testing.assert_array_equal(blob[64:64 + 4 * (L - 1)].view(np.float32), b32.astype(np.float32))
     sigma, S = O.tables(d, W.TABLE_SEED)
     bits = blob[128:128 + d // 8].view(np.uint32)
     got = np.array([(bits[j // 32] >> (j % 32)) & 1 for j in range(d)])
@@ -66,6 +68,11 @@ def test_packed_bytes_per_token():
     assert tq.tq_packed_bytes_per_token(tq.make_config(128, 3, 2)) == W.packed_record_bytes(128, 2) == 112
     assert tq.tq_packed_bytes_per_token(tq.make_config(128, 3, 4)) == 144
     assert tq.tq_packed_bytes_per_token(tq.make_config(256, 3, 4)) == 280
+    # (kb + 1) d / 8 key bytes + 8 norm bytes + vb d / 8 value bytes + 2 d / 32 scale bytes
+    for d, kb, vb in [(64, 1, 2), (64, 2, 4), (64, 4, 2), (128, 2, 2), (128, 4, 4)]:
+        want = (kb + 1) * d // 8 + 8 + vb * d // 8 + 2 * d // 32
+        assert tq.tq_packed_bytes_per_token(tq.make_config(d, kb, vb)) == want
+        assert B.key_record_words(tq.make_config(d, kb, vb)) * 4 == (kb + 1) * d // 8
 
 
 # ------------------------------------------------------------------ error paths (host only)
@@ -82,9 +89,11 @@ def _fake_packed(cap=1000):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(head_dim=64), B.TQ_ERR_UNSUPPORTED),
+    (dict(head_dim=32), B.TQ_ERR_UNSUPPORTED),
     (dict(head_dim=576), B.TQ_ERR_UNSUPPORTED),
-    (dict(key_bits=4), B.TQ_ERR_UNSUPPORTED),
+    (dict(key_bits=5), B.TQ_ERR_UNSUPPORTED),
+    (dict(head_dim=256, key_bits=2), B.TQ_ERR_UNSUPPORTED),
+    (dict(head_dim=256, key_bits=4), B.TQ_ERR_UNSUPPORTED),
     (dict(value_bits=3), B.TQ_ERR_UNSUPPORTED),
     (dict(group_size=64), B.TQ_ERR_UNSUPPORTED),
     (dict(head_dim=0), B.TQ_ERR_INVALID_ARG),

@@ -224,15 +224,15 @@ def _rotate_numpy(sigma, k):
     return (np.asarray(k, np.float64) * sigma.astype(np.float64)) @ H.T / math.sqrt(d)
 
 
-@pytest.mark.parametrize("d", [128, 256])
-def test_key_margins_against_numpy(d):
+@pytest.mark.parametrize("d,kb", [(128, 3), (256, 3), (64, 1), (64, 2), (64, 3), (64, 4), (128, 2), (128, 4)])
+def test_key_margins_against_numpy(d, kb):
     """u_margin (distance of the unit rotated key to the nearest stored boundary) and p_margin
     (|S r|) decide which GPU/oracle differences the parity window forgives; both recomputed
     with scipy's Hadamard matrix and numpy's fp16 decode of S."""
-    c32, b32 = O.stored_codebook(d, 3)
+    c32, b32 = O.stored_codebook(d, kb)
     sigma, S = O.tables(d, W.TABLE_SEED)
     k = _keys(d, 48, seed=21)
-    r = O.quantize_keys(k, c32, b32, sigma, S)
+    r = O.quantize_keys(k, c32, b32, sigma, S, kb=kb)
     u = _rotate_numpy(sigma, k) / np.linalg.norm(k, axis=1)[:, None]
     um = np.abs(u[:, :, None] - b32[None, None, :]).min(-1)
     np.testing.assert_allclose(r["u_margin"], um, rtol=0, atol=1e-15)
@@ -346,19 +346,20 @@ def test_qjl_estimate_is_unbiased_over_projection_draws():
     assert abs(mse_only.mean() - truth) > 8 * sd / math.sqrt(M)
 
 
-def test_decode_scores_equal_estimator():
-    """orc_decode's raw scores use the same estimator (cross-check through the decoder)."""
-    d = 128
-    c32, b32 = O.stored_codebook(d, 3)
+@pytest.mark.parametrize("d,kb", [(128, 3), (64, 1), (64, 2), (64, 4), (128, 4)])
+def test_decode_scores_equal_estimator(d, kb):
+    """orc_decode's raw scores use the same estimator (cross-check through the decoder, which
+    reads the packed record of the key width)."""
+    c32, b32 = O.stored_codebook(d, kb)
     sigma, S = O.tables(d, W.TABLE_SEED)
     r = np.random.default_rng(4)
     k = r.standard_normal((5, d))
     q = r.standard_normal((1, 1, d))
-    qr = O.quantize_keys(k, c32, b32, sigma, S)
+    qr = O.quantize_keys(k, c32, b32, sigma, S, kb=kb)
     v = O.quantize_values(r.standard_normal((5, d)), 2)
-    kw = O.pack_keys(qr["idx"], qr["z"])
+    kw = O.pack_keys(qr["idx"], qr["z"], kb)
     kn = np.stack([qr["norm"], qr["rnorm"]], 1).astype(np.float32)
-    _, sc = O.decode(d=d, kb=3, vb=2, c32=c32, sigma=sigma, S_bits=S, B=1, Hq=1, Hkv=1,
+    _, sc = O.decode(d=d, kb=kb, vb=2, c32=c32, sigma=sigma, S_bits=S, B=1, Hq=1, Hkv=1,
                      kw=kw, kn=kn, vw=O.pack_values(v["code"], 2), vs=v["scale"], cap=5,
                      n_packed=5, rk=None, rv=None, buf=0, n_ring=0, q=q, scale=1.0,
                      want_scores=True)
@@ -440,13 +441,36 @@ def test_pack_single_bit_patterns():
     assert w[0, 1] == 0xF << 4
 
 
+def test_pack_key_planes_hand_computed_words():
+    """Key widths 1, 2 and 4: a code plane of kb-bit fields (least significant first) and a
+    sign plane of one bit per coordinate after it; the expected words are worked by hand."""
+    d = 64
+    j = np.arange(d)
+    # kb = 2: codes 0,1,2,3,0,... -> every byte 0b11100100; signs where j % 3 == 0
+    w = O.pack_keys((j % 4)[None].astype(np.uint8), (j % 3 == 0)[None].astype(np.uint8), 2)[0]
+    assert w.shape == (6,)
+    assert list(w[:4]) == [0xE4E4E4E4] * 4
+    assert w[4] == 0x49249249 and w[5] == 0x92492492   # bits 0,3,..,30 and 1,4,..,31
+    # kb = 4: codes j % 16 -> nibbles 0..7 then 8..15; signs for j < 5
+    w = O.pack_keys((j % 16)[None].astype(np.uint8), (j < 5)[None].astype(np.uint8), 4)[0]
+    assert w.shape == (10,)
+    assert list(w[:8]) == [0x76543210, 0xFEDCBA98] * 4
+    assert w[8] == 0x1F and w[9] == 0
+    # kb = 1: codes j % 2 -> odd bits; signs for j >= 60
+    w = O.pack_keys((j % 2)[None].astype(np.uint8), (j >= 60)[None].astype(np.uint8), 1)[0]
+    assert list(w) == [0xAAAAAAAA, 0xAAAAAAAA, 0, 0xF0000000]
+    # a record is (kb + 1) d / 32 words at every width
+    for kb in (1, 2, 3, 4):
+        assert O.key_words(128, kb) == (kb + 1) * 4 and O.key_words(64, kb) == (kb + 1) * 2
+
+
+@pytest.mark.parametrize("d,kb", [(256, 3), (64, 1), (64, 2), (64, 4), (128, 2), (128, 4)])
 @pytest.mark.parametrize("vb", [2, 4])
-def test_pack_round_trip(vb):
-    d = 256
+def test_pack_round_trip(vb, d, kb):
     r = np.random.default_rng(2)
-    idx = r.integers(0, 8, (50, d), dtype=np.uint8)
+    idx = r.integers(0, 1 << kb, (50, d), dtype=np.uint8)
     z = r.integers(0, 2, (50, d), dtype=np.uint8)
-    i2, z2 = O.unpack_keys(O.pack_keys(idx, z), d)
+    i2, z2 = O.unpack_keys(O.pack_keys(idx, z, kb), d, kb)
     np.testing.assert_array_equal(i2, idx); np.testing.assert_array_equal(z2, z)
     c = r.integers(0, 1 << vb, (50, d), dtype=np.uint8)
     np.testing.assert_array_equal(O.unpack_values(O.pack_values(c, vb), d, vb), c)
