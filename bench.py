@@ -27,6 +27,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -49,6 +50,11 @@ def parse():
     p.add_argument("--config", type=int, default=5,
                    help="workload id (1..5); 5 = 32 layers x batch 4 x 32K context (the default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--key-bits", type=int, default=0,
+                   help="codebook bits per key coordinate (1..4) instead of the workload's 3; the workload "
+                        "name gets a _kb<N> suffix")
+    p.add_argument("--head-dim", type=int, default=0,
+                   help="head_dim (64 or 128) instead of the workload's; the workload name gets a _d<N> suffix")
     p.add_argument("--paged", type=int, default=0, metavar="PAGE_TOKENS",
                    help="keep the packed cache in pages of this many tokens (a multiple of 32), in a "
                         "seeded random page order per slice")
@@ -114,13 +120,17 @@ def main():
     import compressed_decode_attention_02_amd as tq
 
     w = W.WORKLOADS[args.config]
+    if args.head_dim and args.head_dim != w.d:
+        w = dataclasses.replace(w, d=args.head_dim, name=f"{w.name}_d{args.head_dim}")
+    if args.key_bits and args.key_bits != w.key_bits:
+        w = dataclasses.replace(w, key_bits=args.key_bits, name=f"{w.name}_kb{args.key_bits}")
     dev = torch.device("cuda:0")
     d, L, B, hq, hkv = w.d, w.layers, w.batch, w.hq, w.hkv
     n_sl_layer = B * hkv
     n_sl = L * n_sl_layer
     Tp = w.n_packed
     ring_fill = max(w.n_ring - 1, 0)  # the step's append brings the ring to n_ring tokens
-    cfg = tq.make_config(d, 3, w.value_bits, 32, w.buffer_size)
+    cfg = tq.make_config(d, w.key_bits, w.value_bits, 32, w.buffer_size)
     tables = tq.Tables(cfg, W.TABLE_SEED, device=dev)
     rec = tq.tq_packed_bytes_per_token(cfg)
     in_bytes = 2 if w.in_dtype == "bf16" else 4
@@ -258,8 +268,12 @@ def main():
     d_gbps = dec_bytes / (ms_dec * 1e-3) / 1e9
     q_kernels = "k_quant_kv"
     # decode kernel set: a prep launch only at head_dim 256 (at 128 the main kernel prepares
-    # the queries itself); the merge launch only when a slice has several splits
-    d_kernels = ("k_decode_prep+" if d == 256 else "") + "k_decode_main+k_decode_merge"
+    # the queries itself); the merge launch only when a slice has several splits; the other key
+    # widths and head_dim 64: prep, the fp32 decode kernel, merge
+    if w.key_bits != 3 or d == 64:
+        d_kernels = "k_decode_prep+k_decode_any+k_decode_merge"
+    else:
+        d_kernels = ("k_decode_prep+" if d == 256 else "") + "k_decode_main+k_decode_merge"
     roof_q = {"kernel": q_kernels, "bound": "hbm", "achieved": round(q_gbps, 1), "peak": HBM_PEAK_GBPS,
               "unit": "GB/s", "frac": round(q_gbps / HBM_PEAK_GBPS, 4),
               "traffic": measured_traffic(w.name, q_kernels), "algorithmic_bytes_per_launch": q_bytes,
@@ -284,7 +298,7 @@ def main():
         "dtype": w.in_dtype,
         "data": "synthetic (seeded device draws of the workload's laws)",
         "config": {"workload": w.name, "layers": L, "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": d,
-                   "packed_tokens": Tp, "ring_tokens": w.n_ring, "key_bits": 3, "qjl_bits": 1,
+                   "packed_tokens": Tp, "ring_tokens": w.n_ring, "key_bits": w.key_bits, "qjl_bits": 1,
                    "value_bits": w.value_bits, "group": 32, "parallelism": "none (1 GPU)",
                    "input_copies": n_in, "store_copies": n_dec, "paged": args.paged or None},
         "value_is": "decode KV-tokens/s: batch * layers * (packed + ring) per second of all layers' decode calls",
@@ -403,7 +417,7 @@ def cpu_baseline(w, sample_tokens: int):
     v = v.reshape(ws.hkv * T, d).astype(np.float64)
     q, _ = W.host_queries(ws, 0)
     q = q.astype(np.float64)
-    c32, b32 = O.stored_codebook(d, 3)
+    c32, b32 = O.stored_codebook(d, w.key_bits)
     sigma, S = O.tables(d, W.TABLE_SEED)
     O.lib()
     threads, ncpu, model = host_cpu()
@@ -412,9 +426,9 @@ def cpu_baseline(w, sample_tokens: int):
 
     def quant(span):
         a, b = span
-        kq = O.quantize_keys(k[a:b], c32, b32, sigma, S)
+        kq = O.quantize_keys(k[a:b], c32, b32, sigma, S, kb=w.key_bits)
         vq = O.quantize_values(v[a:b], w.value_bits)
-        return (O.pack_keys(kq["idx"], kq["z"]), np.stack([kq["norm"], kq["rnorm"]], 1).astype(np.float32),
+        return (O.pack_keys(kq["idx"], kq["z"], w.key_bits), np.stack([kq["norm"], kq["rnorm"]], 1).astype(np.float32),
                 O.pack_values(vq["code"], w.value_bits), vq["scale"])
 
     G = ws.hq // ws.hkv
@@ -428,7 +442,7 @@ def cpu_baseline(w, sample_tokens: int):
         vs = np.concatenate([p_[3] for p_ in parts]).reshape(ws.hkv, T, -1)
 
         def dec(h):
-            return O.decode(d=d, kb=3, vb=w.value_bits, c32=c32, sigma=sigma, S_bits=S, B=1, Hq=G, Hkv=1,
+            return O.decode(d=d, kb=w.key_bits, vb=w.value_bits, c32=c32, sigma=sigma, S_bits=S, B=1, Hq=G, Hkv=1,
                             kw=kw[h:h + 1], kn=kn[h:h + 1], vw=vw[h:h + 1], vs=vs[h:h + 1], cap=T, n_packed=T,
                             rk=None, rv=None, buf=0, n_ring=0, q=q[:, h * G:(h + 1) * G], scale=1 / math.sqrt(d))
 

@@ -21,8 +21,11 @@
  *     any error nothing is launched and a negative tq_status is returned.
  *   - Device pointers must be 16-byte aligned, except tq_packed.key_norms and
  *     tq_packed.val_scales, which need 8 bytes (TQ_ERR_INVALID_ARG otherwise).
- *   - Supported now: head_dim in {128, 256}, key_bits = 3, value_bits in {2, 4},
- *     group_size = 32, 1 <= buffer_size <= 1024.  Other values give TQ_ERR_UNSUPPORTED.
+ *   - Supported: head_dim in {64, 128, 256}; key_bits in {1, 2, 3, 4} (head_dim 256: 3 only);
+ *     value_bits in {2, 4}; group_size = 32; 1 <= buffer_size <= 1024.  Other values give
+ *     TQ_ERR_UNSUPPORTED.  The guide (section 二) ships codebooks for dimensions 64 and 128
+ *     at 1 to 4 bits; 3-bit keys at head_dim 128 and 256 decode on the matrix cores, the
+ *     other configurations through a plain fp32 decode kernel.
  *   - Decode calls address tokens with 32-bit indices: a context (packed + ring tokens) of
  *     2^31 - 256 tokens or more gives TQ_ERR_UNSUPPORTED.
  *   - Reproducibility: quantisation is deterministic.  A decode call repeats bit for bit
@@ -61,8 +64,8 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
  * key_bits counts the codebook bits only; every key coordinate also stores one QJL sign
  * bit (so key_bits = 3 costs 4 bits per coordinate). */
 typedef struct {
-    int32_t head_dim;     /* d: 128 or 256                                  */
-    int32_t key_bits;     /* codebook bits per key coordinate: 3            */
+    int32_t head_dim;     /* d: 64, 128 or 256                              */
+    int32_t key_bits;     /* codebook bits per key coordinate: 1 to 4       */
     int32_t value_bits;   /* 2 or 4                                         */
     int32_t group_size;   /* values per quantisation group: 32              */
     int32_t buffer_size;  /* ring capacity in tokens (the pages use 128)    */
@@ -109,14 +112,20 @@ tq_status tq_tables_view(const tq_config *cfg, const void *device_blob, tq_table
 
 /* One packed record per (slice, token), slice = flattened (layer, batch, kv head);
  * every array is [n_slices][capacity][...] with the record of token t at t:
- *   key_words  [d/8] u32 : word w covers coordinates 8w..8w+7 as nibbles: bits 4k..4k+2
- *                          hold the 3-bit codebook index of coordinate 8w+k, bit 4k+3 its
- *                          QJL sign bit (1 when the projected residual is >= 0);
+ *   key_words  [(kb+1)*d/32] u32, kb = key_bits:
+ *                          kb = 3: word w covers coordinates 8w..8w+7 as nibbles: bits
+ *                          4k..4k+2 hold the codebook index of coordinate 8w+k, bit 4k+3
+ *                          its QJL sign bit (1 when the projected residual is >= 0);
+ *                          kb = 1, 2, 4: a code plane, words 0..kb*d/32-1, index of
+ *                          coordinate j at bit kb*(j mod 32/kb) of word j*kb/32, then a
+ *                          sign plane, sign bit of coordinate j at bit j mod 32 of word
+ *                          kb*d/32 + j/32;
  *   key_norms  [2]   f32 : |k| and the residual norm |u - c[idx]| of the unit key u;
  *   val_words  [vb*d/32] u32 : vb-bit codes, code j at bit vb*(j mod 32/vb) of word
  *                          j*vb/32 (least significant first: four 2-bit codes per byte);
  *   val_scales [d/32] fp16 : per-group scale s; value = (code - 2^(vb-1) + 1/2) * s.
- * Bytes per record: 112 (d 128, vb 2), 144 (d 128, vb 4), 280 (d 256, vb 4). */
+ * Bytes per record: (kb+1)*d/8 + 8 + vb*d/8 + d/16, e.g. 112 (d 128, kb 3, vb 2), 144
+ * (d 128, kb 3, vb 4), 280 (d 256, kb 3, vb 4), 44 (d 64, kb 1, vb 2). */
 typedef struct {
     uint32_t *key_words;
     float *key_norms;
@@ -180,7 +189,8 @@ tq_status tq_flush(const tq_config *cfg, const tq_tables *tables, const tq_ring 
 
 /* Workspace (device bytes) needed by tq_decode_attention for up to max_context tokens
  * (packed + ring): per-split partial results (the split-K decode of long contexts across
- * compute units), and at head_dim 256 the prepared queries; scratch only (no initialisation
+ * compute units), and at head_dim 256 and for the configurations decoded in fp32 (key_bits
+ * other than 3, head_dim 64) the prepared queries; scratch only (no initialisation
  * needed).  Calls that share a workspace must be ordered (same stream), as they use it in
  * turn.  0 for invalid arguments. */
 size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch, int32_t n_q_heads,
