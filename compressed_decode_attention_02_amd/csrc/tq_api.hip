@@ -57,23 +57,24 @@ int decode_waves(int d, int64_t G, int64_t slices, int64_t n_packed) {
 
 // decode workgroups resident per CU (LDS and registers; see the decode kernel's budget): the
 // split count fills one such wave of workgroups on the current device
-int64_t decode_target_wgs(int d, int vb, int64_t G, int waves) {
+int64_t decode_target_wgs(int d, int vb, int64_t G, int waves, bool any) {
     const int64_t cus = tq::device_cus();
+    if (any) return cus * 4;  // k_decode_any: 4-wave workgroups of at most 41 KB LDS, 4 per CU
     if (waves == 12) return cus;
     return cus * ((d == 128 && G <= 4) ? (vb == 2 ? 4 : 3) : 2);
 }
 
 // (4-wave workgroups give the most splits: the workspace is sized with them)
-int64_t decode_splits(int d, int vb, int64_t G, int64_t slices, int64_t n_packed, int waves) {
+int64_t decode_splits(int d, int vb, int64_t G, int64_t slices, int64_t n_packed, int waves, bool any) {
     const int64_t by_tokens = std::max<int64_t>(1, (n_packed + kMinSplitTokens - 1) / kMinSplitTokens);
-    const int64_t want = std::max<int64_t>(1, (decode_target_wgs(d, vb, G, waves) + slices - 1) / slices);
+    const int64_t want = std::max<int64_t>(1, (decode_target_wgs(d, vb, G, waves, any) + slices - 1) / slices);
     return std::min({by_tokens, want, kMaxSplits});
 }
 
 // tokens per split: a whole number of 128-token passes; then as few splits as cover n_packed
-void split_shape(int d, int vb, int64_t G, int64_t slices, int64_t n_packed, int waves, int64_t &n_split,
+void split_shape(int d, int vb, int64_t G, int64_t slices, int64_t n_packed, int waves, bool any, int64_t &n_split,
                  int64_t &per_split) {
-    const int64_t s0 = decode_splits(d, vb, G, slices, n_packed, waves);
+    const int64_t s0 = decode_splits(d, vb, G, slices, n_packed, waves, any);
     per_split = (n_packed + s0 - 1) / s0;
     per_split = (per_split + kSplitQuantum - 1) / kSplitQuantum * kSplitQuantum;
     n_split = (n_packed + per_split - 1) / per_split;
@@ -190,7 +191,7 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_config *cfg, int32_t batch,
     if (n_q_heads % n_kv_heads != 0) return 0;
     const int64_t n_split =
         std::max(decode_splits(cfg->head_dim, cfg->value_bits, n_q_heads / n_kv_heads, (int64_t)batch * n_kv_heads,
-                               max_context, 4),
+                               max_context, 4, tq::decode_uses_any(cfg->head_dim, cfg->key_bits)),
                  ((int64_t)cfg->buffer_size + ring_per_split_max(cfg->head_dim) - 1) / ring_per_split_max(cfg->head_dim));
     return decode_layout(cfg->head_dim, cfg->key_bits, batch, n_q_heads, n_split).total;
 }
@@ -224,8 +225,11 @@ tq_status decode_impl(const tq_config *cfg, const tq_tables *tables, const void 
     // splits of the packed tokens, at least one (an empty context still writes its zeros), and
     // enough for the ring tokens at ring_per_split_max per split; the ring is spread evenly
     int64_t n_split = 1, per_split = 0;
-    const int waves = n_packed > 0 ? decode_waves(cfg->head_dim, G, slices, n_packed) : 4;
-    if (n_packed > 0) split_shape(cfg->head_dim, cfg->value_bits, G, slices, n_packed, waves, n_split, per_split);
+    // (k_decode_any has 4-wave workgroups: its splits are planned for those)
+    const bool any = tq::decode_uses_any(cfg->head_dim, cfg->key_bits);
+    const int waves = n_packed > 0 && !any ? decode_waves(cfg->head_dim, G, slices, n_packed) : 4;
+    if (n_packed > 0)
+        split_shape(cfg->head_dim, cfg->value_bits, G, slices, n_packed, waves, any, n_split, per_split);
     const int64_t ring_splits = (n_ring + ring_per_split_max(cfg->head_dim) - 1) / ring_per_split_max(cfg->head_dim);
     if (ring_splits > n_split) {
         // more splits for the ring than for the packed tokens: spread the packed tokens too

@@ -13,7 +13,7 @@
 // chunks to the waves in turn (packed chunks, then the ring chunk).  Per chunk:
 //   * scores, one lane per token: the lane reads its token's key record and norms and sums
 //     G heads over the d coordinates in fp32 (the codebook value from an LDS table, q' and w
-//     scaled into the log2 domain from LDS, broadcast);
+//     as scalar operands; sum_j w_j (2 z_j - 1) taken as 2 sum_{z_j = 1} w_j - sum_j w_j);
 //   * online softmax per head across the wave's chunks (chunk maximum by lane shuffles);
 //   * values, one lane per coordinate (d / 64 each): p of every token of the chunk and its
 //     value record come from LDS (the lane of the token wrote them), fp32 accumulation.
@@ -47,10 +47,9 @@ struct AnyShape {
 template <int D, int KB, int VB, int G>
 struct AnySmem {
     using S = AnyShape<D, KB, VB, G>;
-    float qs[G][D];  // scale log2(e) / sqrt(d) * q'
-    float ws[G][D];  // scale log2(e) / sqrt(d) * sqrt(pi/2) / d * w
     float qr[G][D];  // scale log2(e) * q (the ring's exact scores)
     float ctab[16];  // stored centroids
+    float wsum[G];   // sum_j w[g][j]
     float pb[kAnyWaves][kChunk][G];  // p of the chunk's tokens
     union {
         struct {
@@ -104,18 +103,22 @@ __global__ __launch_bounds__(kAnyThreads) void k_decode_any(DecodeArgs a) {
     const int t_end = max(t_begin, min(n_packed, t_begin + per_split));
     const int r0 = split * ring_per_split, nr = max(0, min(n_ring - r0, ring_per_split));
 
-    // prepared queries of the slice, scaled into the log2 domain
+    // prepared queries of the slice (q' [G][D], then w [G][D]): the same values in every lane,
+    // read through the scalar unit (constant address space: the kernel never writes them);
+    // the log2-domain scales are applied to the sums
     const float cs = a.scale * kAnyLog2e * rsqrtf((float)D);
     const float ss = cs * (1.2533141373155003f / (float)D);  // sqrt(pi/2) / d
-    const float *prep = a.prep + (int64_t)bk * 2 * G * D;
+    typedef const __attribute__((address_space(4))) float cfloat;
+    cfloat *prep = (cfloat *)(a.prep + (int64_t)bk * 2 * G * D);
     const float lscale = a.scale * kAnyLog2e;
     const int64_t qoff = ((int64_t)b * a.hq + kvh * G) * D;
-    for (int i = tid; i < G * D; i += kAnyThreads) {
-        (&sm.qs[0][0])[i] = cs * prep[i];
-        (&sm.ws[0][0])[i] = ss * prep[G * D + i];
-        (&sm.qr[0][0])[i] = lscale * load_q_elem(a, qoff + i);
-    }
+    for (int i = tid; i < G * D; i += kAnyThreads) (&sm.qr[0][0])[i] = lscale * load_q_elem(a, qoff + i);
     if (tid < (1 << KB)) sm.ctab[tid] = a.centroids[tid];
+    if (tid < G) {
+        float sw = 0.f;
+        for (int j = 0; j < D; ++j) sw += prep[G * D + tid * D + j];
+        sm.wsum[tid] = sw;
+    }
     __syncthreads();
 
     float M[G], Lw[G], o[G][S::EPL];
@@ -160,12 +163,13 @@ __global__ __launch_bounds__(kAnyThreads) void k_decode_any(DecodeArgs a) {
                 const float c = sm.ctab[idx];
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    mse[h] = fmaf(sm.qs[h][j], c, mse[h]);
-                    sgn[h] += flip_sign(sm.ws[h][j], z ^ 1u);
+                    mse[h] = fmaf(prep[h * D + j], c, mse[h]);
+                    sgn[h] = fmaf((float)z, prep[G * D + h * D + j], sgn[h]);  // sum of w over the set sign bits
                 }
             }
 #pragma unroll
-            for (int h = 0; h < G; ++h) s[h] = kn.x * fmaf(kn.y, sgn[h], mse[h]);
+            for (int h = 0; h < G; ++h)
+                s[h] = kn.x * fmaf(ss * kn.y, fmaf(2.f, sgn[h], -sm.wsum[h]), cs * mse[h]);
             // the token's value record and scales for the value phase
             const uint32_t *vp = a.vw + rec * S::VW;
 #pragma unroll
