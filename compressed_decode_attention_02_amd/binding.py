@@ -21,6 +21,7 @@ EXPORTS = [
     "tq_packed_bytes_per_token", "tq_quantize_kv", "tq_append_ring", "tq_flush",
     "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_attention_ragged", "tq_decode_step",
     "tq_status_string", "tq_rotate", "tq_decode_scores", "tq_decode_attention_noalloc",
+    "tq_prefill_workspace_bytes", "tq_prefill_attention",
 ]
 
 
@@ -84,6 +85,9 @@ def _lib():
                                           ctypes.POINTER(I32), P, P, ctypes.c_int, F, P, P, SZ, P]),
         "tq_decode_attention_noalloc": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, K, I64, R, I32, F, P,
                                                        P]),
+        "tq_prefill_workspace_bytes": (SZ, [C, I32, I32, I32, I32, I64]),
+        "tq_prefill_attention": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, I32, K, I64, I64, I32, F, P,
+                                                P, SZ, P]),
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tq_rotate": (ctypes.c_int, [C, T, P, ctypes.c_int, I64, P, P]),
         "tq_decode_scores": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, K, I64, R, I32, P, P]),
@@ -458,6 +462,39 @@ class PreparedDecodeStep:
         if st != TQ_OK:
             raise TqError("tq_decode_step", st)
         return self._np.value, self._nr.value
+
+
+def tq_prefill_workspace_bytes(cfg, batch: int, q_tokens: int, n_q_heads: int, n_kv_heads: int,
+                               n_packed: int) -> int:
+    return _lib().tq_prefill_workspace_bytes(ctypes.byref(cfg), batch, q_tokens, n_q_heads, n_kv_heads, n_packed)
+
+
+def tq_prefill_attention(cfg, tables: Tables, q, batch: int, q_tokens: int, n_q_heads: int, n_kv_heads: int,
+                         packed: tq_packed, n_packed: int, q_pos0: int, causal: bool, softmax_scale: float, out,
+                         workspace, stream=None):
+    """Prefill attention over the packed cache: q and out [batch][q_tokens][n_q_heads][d]."""
+    import torch
+    n = max(batch, 0) * max(q_tokens, 0) * max(n_q_heads, 0) * cfg.head_dim
+    _dtype_code(q)
+    _need("q", q, n)
+    _need("out", out, n, torch.float32)
+    _need("workspace", workspace, 1)
+    _on_one_gpu(("q", q), ("out", out), ("workspace", workspace))
+    st = _lib().tq_prefill_attention(
+        ctypes.byref(cfg), ctypes.byref(tables.view), _ptr(q), _dtype_code(q), batch, q_tokens, n_q_heads,
+        n_kv_heads, ctypes.byref(packed), n_packed, q_pos0, 1 if causal else 0, ctypes.c_float(softmax_scale),
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("tq_prefill_attention", st)
+
+
+def new_prefill_workspace(cfg, batch: int, q_tokens: int, n_q_heads: int, n_kv_heads: int, n_packed: int,
+                          device="cuda"):
+    """Prefill workspace (scratch) of the size tq_prefill_workspace_bytes reports."""
+    import torch
+    n = tq_prefill_workspace_bytes(cfg, batch, q_tokens, n_q_heads, n_kv_heads, n_packed)
+    if n == 0:
+        raise TqError("tq_prefill_workspace_bytes", TQ_ERR_INVALID_ARG)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def new_workspace(cfg, batch: int, n_q_heads: int, n_kv_heads: int, max_context: int, device="cuda"):

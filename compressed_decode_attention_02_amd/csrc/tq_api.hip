@@ -204,7 +204,8 @@ tq_status decode_impl(const tq_config *cfg, const tq_tables *tables, const void 
                       const tq_ring *ring, int32_t n_ring, float softmax_scale, float *out, void *workspace,
                       size_t workspace_bytes, void *stream, const void *k_new, const void *v_new, tq_dtype kv_dtype,
                       bool check_only = false, const int64_t *seq_packed = nullptr,
-                      const int32_t *seq_ring = nullptr) {
+                      const int32_t *seq_ring = nullptr, int32_t q_tokens = 0, int64_t q_pos0 = 0,
+                      int32_t causal = 0, int64_t q_slice0 = 0) {
     if (!cfg) return TQ_ERR_INVALID_ARG;
     tq_status st = tq::check_config(*cfg);
     if (st != TQ_OK) return st;
@@ -281,6 +282,10 @@ tq_status decode_impl(const tq_config *cfg, const tq_tables *tables, const void 
     a.v_new = v_new;
     a.kv_dtype = (int)kv_dtype;
     a.new_slot = k_new ? n_ring - 1 : -1;
+    a.q_tokens = q_tokens;
+    a.q_pos0 = q_pos0;
+    a.causal = causal;
+    a.q_slice0 = q_slice0;
     a.partial = reinterpret_cast<float *>(ws + L.partial);
     a.partial_ml = reinterpret_cast<float *>(ws + L.partial_ml);
     return hip_status(tq::launch_decode(cfg->head_dim, cfg->key_bits, cfg->value_bits, G, a, (hipStream_t)stream));
@@ -307,6 +312,65 @@ extern "C" tq_status tq_decode_attention_ragged(const tq_config *cfg, const tq_t
     return decode_impl(cfg, tables, q, q_dtype, batch, n_q_heads, n_kv_heads, packed, n_packed_max, ring, n_ring_max,
                        softmax_scale, out, workspace, workspace_bytes, stream, nullptr, nullptr, TQ_F32, false,
                        seq_packed, seq_ring);
+}
+
+// ------------------------------------------------------------------ prefill (full_tq)
+namespace {
+// query tokens per decode launch of a prefill call: batch * kv heads of a launch stays within
+// the grid's 65535 rows
+int64_t prefill_launch_tokens(int32_t n_kv_heads) { return std::max<int64_t>(1, 65535 / n_kv_heads); }
+}  // namespace
+
+extern "C" size_t tq_prefill_workspace_bytes(const tq_config *cfg, int32_t batch, int32_t q_tokens,
+                                             int32_t n_q_heads, int32_t n_kv_heads, int64_t n_packed) {
+    if (!cfg || batch <= 0 || q_tokens <= 0 || n_kv_heads <= 0) return 0;
+    const int64_t vb = std::min<int64_t>((int64_t)batch * q_tokens, prefill_launch_tokens(n_kv_heads));
+    return tq_decode_workspace_bytes(cfg, (int32_t)vb, n_q_heads, n_kv_heads, n_packed);
+}
+
+extern "C" tq_status tq_prefill_attention(const tq_config *cfg, const tq_tables *tables, const void *q,
+                                          tq_dtype q_dtype, int32_t batch, int32_t q_tokens, int32_t n_q_heads,
+                                          int32_t n_kv_heads, const tq_packed *packed, int64_t n_packed,
+                                          int64_t q_pos0, int32_t causal, float softmax_scale, float *out,
+                                          void *workspace, size_t workspace_bytes, void *stream) {
+    if (!cfg) return TQ_ERR_INVALID_ARG;
+    tq_status st = tq::check_config(*cfg);
+    if (st != TQ_OK) return st;
+    if (batch <= 0 || q_tokens <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_packed < 0 || q_pos0 < 0 ||
+        (causal != 0 && causal != 1) || !packed)
+        return TQ_ERR_INVALID_ARG;
+    if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_ERR_INVALID_ARG;
+    const int64_t per = prefill_launch_tokens(n_kv_heads);
+    const int64_t esz = q_dtype == TQ_F32 ? 4 : 2;
+    const int64_t row = (int64_t)n_q_heads * cfg->head_dim;  // elements of one query token
+    // the launches: whole sequences per launch while a sequence's tokens fit one launch,
+    // else chunks of one sequence's tokens; every launch is checked before the first one
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool check = pass == 0;
+        if (q_tokens <= per) {
+            const int64_t seqs = std::max<int64_t>(1, per / q_tokens);
+            for (int64_t s0 = 0; s0 < batch; s0 += seqs) {
+                const int64_t ns = std::min<int64_t>(seqs, batch - s0);
+                st = decode_impl(cfg, tables, static_cast<const char *>(q) + s0 * q_tokens * row * esz, q_dtype,
+                                 (int32_t)(ns * q_tokens), n_q_heads, n_kv_heads, packed, n_packed, nullptr, 0,
+                                 softmax_scale, out + s0 * q_tokens * row, workspace, workspace_bytes, stream, nullptr,
+                                 nullptr, TQ_F32, check, nullptr, nullptr, q_tokens, q_pos0, causal, s0 * n_kv_heads);
+                if (st != TQ_OK) return st;
+            }
+        } else {
+            for (int64_t s = 0; s < batch; ++s)
+                for (int64_t i0 = 0; i0 < q_tokens; i0 += per) {
+                    const int64_t c = std::min<int64_t>(per, q_tokens - i0);
+                    const int64_t off = (s * q_tokens + i0) * row;
+                    st = decode_impl(cfg, tables, static_cast<const char *>(q) + off * esz, q_dtype, (int32_t)c,
+                                     n_q_heads, n_kv_heads, packed, n_packed, nullptr, 0, softmax_scale, out + off,
+                                     workspace, workspace_bytes, stream, nullptr, nullptr, TQ_F32, check, nullptr,
+                                     nullptr, (int32_t)c, q_pos0 + i0, causal, s * n_kv_heads);
+                    if (st != TQ_OK) return st;
+                }
+        }
+    }
+    return TQ_OK;
 }
 
 extern "C" tq_status tq_decode_step(const tq_config *cfg, const tq_tables *tables, const void *q, tq_dtype q_dtype,

@@ -567,8 +567,9 @@ __device__ void ring_attend(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, f
 
 // ------------------------------------------------------------------ packed split (one wave)
 template <int D, int VB, int G, int NW>
-__device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, int bk, int b, int kvh, int n_packed,
-                            int t_begin, int t_end, int r0, int nr, float (&orr)[RingShape<D, G, NW>::NE]) {
+__device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, int bk, int sbk, int b, int kvh,
+                            int n_packed, int t_begin, int t_end, int r0, int nr,
+                            float (&orr)[RingShape<D, G, NW>::NE]) {
     using S = DecodeShape<D, VB, G>;
     constexpr float kQjl = 1.2533141373155003f / D;  // sqrt(pi/2) / d
     const int lane = threadIdx.x & 63;
@@ -608,7 +609,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     // one page of a paged store, since pages hold a multiple of 32 tokens)
     // (the same for every lane: made visibly uniform, so the copy bases are scalar values)
     auto block_rec = [&](int t0) -> int64_t {
-        const int64_t r = record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, a.err, bk, t0);
+        const int64_t r = record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, a.err, sbk, t0);
         return (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)r) |
                ((int64_t)__builtin_amdgcn_readfirstlane((int)(r >> 32)) << 32);
     };
@@ -1492,20 +1493,30 @@ void k_decode_main(DecodeArgs a) {
 
     {
         using R = RingShape<D, G, NW>;
-        // this sequence's lengths: the call's, or (ragged batches) its own, clamped to them
+        // this sequence's lengths: the call's, or (ragged batches) its own, clamped to them;
+        // prefill: batch element b is query token b % q_tokens of sequence b / q_tokens, whose
+        // packed records it reads (store slice sbk), causally up to its own position
         int n_packed = (int)a.n_packed, n_ring = a.n_ring;
+        int sbk = bk;
         if (a.seq_packed) n_packed = (int)min(max(a.seq_packed[b], (int64_t)0), a.n_packed);
         if (a.seq_ring) n_ring = min(max(a.seq_ring[b], 0), a.n_ring);
-        // ragged batches: this sequence's own lengths divided evenly over the splits (whole
-        // 32-token blocks; at most the call's split sizes, since the lengths are clamped)
+        if (a.q_tokens) {
+            const int seq = b / a.q_tokens, qi = b - seq * a.q_tokens;
+            sbk = (int)(a.q_slice0 + seq * a.hkv + kvh);
+            if (a.causal) n_packed = (int)max((int64_t)0, min((int64_t)n_packed, a.q_pos0 + qi + 1));
+        }
+        // ragged batches (and causal prefill): this sequence's own lengths divided evenly over
+        // the splits (whole 32-token blocks; at most the call's split sizes, since the lengths
+        // are clamped)
         int per_split = (int)a.per_split, ring_per_split = a.ring_per_split;
-        if (a.seq_packed) per_split = ((n_packed + a.n_split - 1) / a.n_split + kBlock - 1) / kBlock * kBlock;
+        if (a.seq_packed || (a.q_tokens && a.causal))
+            per_split = ((n_packed + a.n_split - 1) / a.n_split + kBlock - 1) / kBlock * kBlock;
         if (a.seq_ring) ring_per_split = (n_ring + a.n_split - 1) / a.n_split;
         const int t_begin = split * per_split;
         const int t_end = max(t_begin, min(n_packed, t_begin + per_split));
         const int r0 = split * ring_per_split, nr = max(0, min(n_ring - r0, ring_per_split));
         float orr[R::NE];
-        packed_wave<D, VB, G, NW>(a, sm, bk, b, kvh, n_packed, t_begin, t_end, r0, nr, orr);
+        packed_wave<D, VB, G, NW>(a, sm, bk, sbk, b, kvh, n_packed, t_begin, t_end, r0, nr, orr);
         __syncthreads();
         // combine the waves and the split's ring tokens
 #pragma unroll

@@ -94,10 +94,16 @@ __global__ __launch_bounds__(kAnyThreads) void k_decode_any(DecodeArgs a) {
 
     // this sequence's lengths and the split's token ranges (as in the matrix-core decode)
     int n_packed = (int)a.n_packed, n_ring = a.n_ring;
+    int sbk = bk;  // store slice (prefill: the sequence's, shared by its query tokens)
     if (a.seq_packed) n_packed = (int)min(max(a.seq_packed[b], (int64_t)0), a.n_packed);
     if (a.seq_ring) n_ring = min(max(a.seq_ring[b], 0), a.n_ring);
+    if (a.q_tokens) {
+        const int seq = b / a.q_tokens, qi = b - seq * a.q_tokens;
+        sbk = (int)(a.q_slice0 + seq * a.hkv + kvh);
+        if (a.causal) n_packed = (int)max((int64_t)0, min((int64_t)n_packed, a.q_pos0 + qi + 1));
+    }
     int per_split = (int)a.per_split, ring_per_split = a.ring_per_split;
-    if (a.seq_packed) per_split = ((n_packed + a.n_split - 1) / a.n_split + 31) / 32 * 32;
+    if (a.seq_packed || (a.q_tokens && a.causal)) per_split = ((n_packed + a.n_split - 1) / a.n_split + 31) / 32 * 32;
     if (a.seq_ring) ring_per_split = (n_ring + a.n_split - 1) / a.n_split;
     const int t_begin = split * per_split;
     const int t_end = max(t_begin, min(n_packed, t_begin + per_split));
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(kAnyThreads) void k_decode_any(DecodeArgs a) {
         for (int h = 0; h < G; ++h) s[h] = 0.f;
         if (!ring) {
             // ---- scores of a packed token (one per lane)
-            const int64_t rec = record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, a.err, bk, tt);
+            const int64_t rec = record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, a.err, sbk, tt);
             uint32_t kw[S::KW];
             const uint2 *kp = reinterpret_cast<const uint2 *>(a.kw + rec * S::KW);
 #pragma unroll

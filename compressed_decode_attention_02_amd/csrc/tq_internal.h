@@ -86,6 +86,13 @@ struct DecodeArgs {
     const void *v_new;
     int kv_dtype;
     int new_slot;
+    // prefill (tq_prefill_attention): q_tokens > 0 makes batch element b query token
+    // b % q_tokens of sequence b / q_tokens, which reads that sequence's packed records; with
+    // causal set, query token i attends to packed tokens [0, q_pos0 + i] only
+    int q_tokens;
+    int64_t q_pos0;
+    int causal;
+    int64_t q_slice0;  // prefill: store slice of the launch's first sequence
     float *partial;      // [batch*hkv][n_split][G][D]: o of each split
     float *partial_ml;   // [batch*hkv][n_split][G][2]: (m, l) of each split
 };

@@ -237,6 +237,28 @@ tq_status tq_decode_step(const tq_config *cfg, const tq_tables *tables, const vo
                          const void *v_new, tq_dtype kv_dtype, float softmax_scale, float *out, void *workspace,
                          size_t workspace_bytes, void *stream);
 
+/* Prefill attention over the packed cache (guide section 三, the full_tq mode: attention taken
+ * entirely from the compressed cache, prefill included).  For sequence b (packed slices
+ * b * n_kv_heads + kv head, as in tq_decode_attention) and query token i of q_tokens, query
+ * head h attends, with the same estimator and value reconstruction as the decode, to packed
+ * tokens [0, min(n_packed, q_pos0 + i + 1)) when causal == 1 (the query token at position
+ * q_pos0 + i of a prompt whose tokens are already in the store), else to [0, n_packed).
+ *   q   : [batch][q_tokens][n_q_heads][head_dim] in q_dtype (device);
+ *   out : [batch][q_tokens][n_q_heads][head_dim] fp32 (device); a token with no packed token
+ *         to attend to gets zeros.
+ * Runs the decode kernels with one batch element per query token reading its sequence's
+ * records (launches of at most 65535 / n_kv_heads query tokens each, all checked before the
+ * first); no ring.  workspace: tq_prefill_workspace_bytes(cfg, batch, q_tokens, n_q_heads,
+ * n_kv_heads, n_packed) bytes.  Errors as tq_decode_attention; q_pos0 < 0 or causal not 0/1:
+ * TQ_ERR_INVALID_ARG. */
+size_t tq_prefill_workspace_bytes(const tq_config *cfg, int32_t batch, int32_t q_tokens, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int64_t n_packed);
+tq_status tq_prefill_attention(const tq_config *cfg, const tq_tables *tables, const void *q, tq_dtype q_dtype,
+                               int32_t batch, int32_t q_tokens, int32_t n_q_heads, int32_t n_kv_heads,
+                               const tq_packed *packed, int64_t n_packed, int64_t q_pos0, int32_t causal,
+                               float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 /* Decode without a workspace, for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation): tq_decode_attention
  * with the workspace taken from a static device array of TQ_NOALLOC_SCRATCH_BYTES (8 MiB) per

@@ -281,3 +281,23 @@ def decode(*, d, kb, vb, c32, sigma, S_bits, B, Hq, Hkv, kw, kn, vw, vs, cap, n_
         buf, n_ring, _c(q, np.float64).ravel(), float(scale), out.ravel(),
         scores.ctypes.data_as(ctypes.c_void_p) if want_scores else None)
     return (out, scores) if want_scores else out
+
+
+def prefill(*, d, kb, vb, c32, sigma, S_bits, B, T, Hq, Hkv, kw, kn, vw, vs, cap, n_packed, q, pos0, causal,
+            scale, group=32):
+    """Prefill attention over the packed cache (guide section 三, full_tq): query token i of
+    sequence b, q [B][T][Hq][d], is a decode query over that sequence's packed tokens
+    [0, min(n_packed, pos0 + i + 1)) when causal, else [0, n_packed); a token with nothing to
+    attend to gives zeros.  Store arrays as in decode ([B*Hkv][cap][...])."""
+    out = np.zeros((B, T, Hq, d), np.float64)
+    for b in range(B):
+        sl = slice(b * Hkv, (b + 1) * Hkv)
+        for i in range(T):
+            n = min(n_packed, pos0 + i + 1) if causal else n_packed
+            if n <= 0:
+                continue
+            out[b, i] = decode(d=d, kb=kb, vb=vb, c32=c32, sigma=sigma, S_bits=S_bits, B=1, Hq=Hq, Hkv=Hkv,
+                               kw=kw[sl], kn=kn[sl], vw=vw[sl], vs=vs[sl], cap=cap, n_packed=n, rk=None, rv=None,
+                               buf=0, n_ring=0, q=q[b, i][None], scale=scale, group=group)[0]
+    return out
+

@@ -1,0 +1,92 @@
+"""Prefill attention over the packed cache (tq_prefill_attention) against the oracle's prefill
+on the same packed bytes: causal and full windows, both decode kernels (3-bit keys at
+head_dim 128 and 256, and the fp32 path for other key widths), paged stores."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import tq_workloads as W
+import compressed_decode_attention_02_amd as tq
+
+pytestmark = pytest.mark.gpu
+
+from gpu_common import Env, assert_decode_close, dev_to_stored, log, packed_to_np, quantize_gpu, to_dev  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need a GPU"
+    return t
+
+
+def _prefill_case(torch, w: W.Workload, T: int, pos0: int, causal: bool, label: str, paged=None):
+    env = Env(w.d, w.value_bits, buffer_size=w.buffer_size, kb=w.key_bits)
+    n_sl = w.batch * w.hkv
+    (k, v), _ = W.host_kv(w, 0, w.n_packed)
+    k = k.reshape(n_sl, -1, w.d)
+    v = v.reshape(n_sl, -1, w.d)
+    if paged:
+        pt, pps = paged
+        store = tq.PagedStore(env.cfg, n_sl, pt, pps, n_sl * pps + 3, seed=11)
+        quantize_gpu(env, to_dev(k, w.in_dtype), to_dev(v, w.in_dtype), n_sl, w.n_packed, store=store)
+    else:
+        store = quantize_gpu(env, to_dev(k, w.in_dtype), to_dev(v, w.in_dtype), n_sl, w.n_packed)
+    r = np.random.default_rng(31)
+    q = r.standard_normal((w.batch, T, w.hq, w.d)).astype(np.float32)
+    qd = to_dev(q.reshape(-1, w.d), w.in_dtype)
+    out = torch.zeros((w.batch, T, w.hq, w.d), dtype=torch.float32, device="cuda")
+    ws = tq.new_prefill_workspace(env.cfg, w.batch, T, w.hq, w.hkv, w.n_packed)
+    scale = 1.0 / math.sqrt(w.d)
+    tq.tq_prefill_attention(env.cfg, env.tables, qd, w.batch, T, w.hq, w.hkv, store.struct(), w.n_packed, pos0,
+                            causal, scale, out, ws)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy().astype(np.float64)
+    if paged:
+        P = {k_: v_ for k_, v_ in store.gather().items()}
+        P = dict(kw=P["key_words"].view(np.uint32), kn=P["key_norms"], vw=P["val_words"].view(np.uint32),
+                 vs=P["val_scales"].view(np.uint16))
+        cap = store.capacity
+    else:
+        P = packed_to_np(store)
+        cap = store.capacity
+    qs = dev_to_stored(qd).astype(np.float64).reshape(w.batch, T, w.hq, w.d)
+    ref = O.prefill(d=w.d, kb=w.key_bits, vb=w.value_bits, c32=env.c32, sigma=env.sigma, S_bits=env.S, B=w.batch,
+                    T=T, Hq=w.hq, Hkv=w.hkv, kw=P["kw"], kn=P["kn"], vw=P["vw"], vs=P["vs"], cap=cap,
+                    n_packed=w.n_packed, q=qs, pos0=pos0, causal=causal, scale=scale)
+    empty = np.abs(ref).max(axis=-1) == 0
+    assert not g[empty].any(), f"{label}: query tokens with no packed token must give zeros"
+    live = ~empty.all(axis=-1)
+    assert_decode_close(g[live], ref[live], label)
+    return g, store, env, qd, ws
+
+
+def test_prefill_d128_causal_and_full(torch):
+    w = W.custom(2, batch=2, hq=8, hkv=2, n_packed=700)
+    _prefill_case(torch, w, 37, 700 - 37, True, "d128 causal, the prompt's last 37 tokens")
+    _prefill_case(torch, w, 37, 700 - 37, False, "d128 full window")
+    # query tokens before the history's end and before its start (positions 0..): the first
+    # token attends to one packed token
+    _prefill_case(torch, W.custom(2, batch=1, hq=4, hkv=1, n_packed=300), 40, 0, True, "d128 causal from 0")
+
+
+def test_prefill_d256_and_gqa(torch):
+    _prefill_case(torch, W.custom(4, batch=1, hq=4, hkv=2, n_packed=300), 20, 280, True, "d256 G=2 causal")
+    _prefill_case(torch, W.custom(2, batch=1, hq=16, hkv=2, n_packed=400), 9, 391, True, "d128 G=8 causal")
+
+
+def test_prefill_key_widths(torch):
+    _prefill_case(torch, W.custom(2, d=64, key_bits=2, batch=2, hq=8, hkv=2, n_packed=500), 33, 467, True,
+                  "d64 kb2 causal")
+    _prefill_case(torch, W.custom(2, d=128, key_bits=4, batch=1, hq=8, hkv=2, n_packed=260), 12, 0, False,
+                  "d128 kb4 full")
+
+
+def test_prefill_paged_store_matches_contiguous(torch):
+    w = W.custom(2, batch=2, hq=8, hkv=2, n_packed=640)
+    g1, _, _, _, _ = _prefill_case(torch, w, 17, 623, True, "d128 contiguous")
+    g2, paged, _, _, _ = _prefill_case(torch, w, 17, 623, True, "d128 paged", paged=(64, 10))
+    np.testing.assert_array_equal(g1, g2)
+    assert not paged.table_error()

@@ -352,3 +352,34 @@ def test_prepared_decode_step_checks_its_arguments():
         tq.PreparedDecodeStep(cfg, None, q, 1, 4, 1, None, None, kb, kb, 0.1, out.half(), ws)
     with pytest.raises(ValueError, match="GPU tensor"):
         tq.PreparedDecodeStep(cfg, None, q, 1, 4, 1, None, None, kb, kb, 0.1, out, ws)
+
+
+def test_prefill_argument_errors():
+    """Prefill: every argument checked on the host before a launch (fake device pointers)."""
+    cfg = tq.make_config()
+    L = tq.lib()
+    T, P = _fake_tables(), _fake_packed(cap=1000)
+
+    def pf(batch=2, q_tokens=16, hq=8, hkv=2, n_packed=500, pos0=0, causal=1, q=FAKE, out=FAKE, ws_bytes=1 << 30,
+           packed=P, dtype=B.TQ_BF16):
+        return L.tq_prefill_attention(ctypes.byref(cfg), ctypes.byref(T), q, dtype, batch, q_tokens, hq, hkv,
+                                      ctypes.byref(packed) if packed is not None else None, n_packed, pos0, causal,
+                                      ctypes.c_float(0.1), out, FAKE, ws_bytes, None)
+    assert pf(batch=0) == B.TQ_ERR_INVALID_ARG
+    assert pf(q_tokens=0) == B.TQ_ERR_INVALID_ARG
+    assert pf(pos0=-1) == B.TQ_ERR_INVALID_ARG
+    assert pf(causal=2) == B.TQ_ERR_INVALID_ARG
+    assert pf(packed=None) == B.TQ_ERR_INVALID_ARG
+    assert pf(n_packed=1001) == B.TQ_ERR_INVALID_ARG          # beyond the store's capacity
+    assert pf(q=FAKE + 4) == B.TQ_ERR_INVALID_ARG             # 16-byte alignment
+    assert pf(dtype=9) == B.TQ_ERR_INVALID_ARG
+    assert pf(hq=24, hkv=2) == B.TQ_ERR_UNSUPPORTED          # G = 12
+    assert pf(ws_bytes=16) == B.TQ_ERR_WORKSPACE
+    need = L.tq_prefill_workspace_bytes(ctypes.byref(cfg), 2, 16, 8, 2, 500)
+    assert need > 0 and L.tq_prefill_workspace_bytes(ctypes.byref(cfg), 0, 16, 8, 2, 500) == 0
+    # long prompts run in several launches of at most 65535 / kv heads query tokens: the
+    # workspace is sized for one launch, and every launch is checked before the first
+    big = L.tq_prefill_workspace_bytes(ctypes.byref(cfg), 1, 40000, 8, 2, 500)
+    assert big == L.tq_prefill_workspace_bytes(ctypes.byref(cfg), 1, 32767, 8, 2, 500)
+    assert pf(batch=1, q_tokens=40000, ws_bytes=16) == B.TQ_ERR_WORKSPACE
+    assert pf(batch=1, q_tokens=40000, n_packed=1001) == B.TQ_ERR_INVALID_ARG

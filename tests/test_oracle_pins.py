@@ -535,3 +535,47 @@ def test_kv_bytes_formula_matches_pages():
     assert round(b2048 / 1e9, 2) == g["seq2048_GB"]
     assert round(b8192 / 1e9, 1) == g["seq8192_GB"]
     assert W.packed_record_bytes(128, 2) == 112 and W.packed_record_bytes(256, 4) == 280
+
+
+def test_prefill_is_causal_estimator_attention():
+    """The prefill oracle against numpy written from the estimator: scores
+    n (q'.c[idx] + gamma sqrt(pi/2)/d w.(2z - 1)) with q' = Pi q (scipy's Hadamard matrix) and
+    w = S q', a causal mask from position pos0, softmax of scale * s, bin-centre values."""
+    d, kb, vb, Hq, Hkv, T, n_packed, pos0 = 64, 2, 2, 4, 2, 5, 9, 3
+    c32, b32 = O.stored_codebook(d, kb)
+    sigma, S = O.tables(d, W.TABLE_SEED)
+    r = np.random.default_rng(23)
+    k = r.standard_normal((Hkv * n_packed, d))
+    v = r.standard_normal((Hkv * n_packed, d))
+    q = r.standard_normal((1, T, Hq, d))
+    kq = O.quantize_keys(k, c32, b32, sigma, S, kb=kb)
+    vq = O.quantize_values(v, vb)
+    kw = O.pack_keys(kq["idx"], kq["z"], kb).reshape(Hkv, n_packed, -1)
+    kn = np.stack([kq["norm"], kq["rnorm"]], 1).astype(np.float32).reshape(Hkv, n_packed, 2)
+    vw = O.pack_values(vq["code"], vb).reshape(Hkv, n_packed, -1)
+    vs = vq["scale"].reshape(Hkv, n_packed, -1)
+    scale = 1 / math.sqrt(d)
+    common = dict(d=d, kb=kb, vb=vb, c32=c32, sigma=sigma, S_bits=S, B=1, T=T, Hq=Hq, Hkv=Hkv, kw=kw, kn=kn,
+                  vw=vw, vs=vs, cap=n_packed, n_packed=n_packed, q=q, scale=scale)
+    got = O.prefill(pos0=pos0, causal=True, **common)
+    full = O.prefill(pos0=pos0, causal=False, **common)
+    Sd = S.view(np.float16).astype(np.float64)
+    idx = kq["idx"].reshape(Hkv, n_packed, d)
+    z = kq["z"].reshape(Hkv, n_packed, d).astype(np.float64)
+    nrm = kn[..., 0].astype(np.float64)
+    gam = kn[..., 1].astype(np.float64)
+    vhat = O.dequant_values(vq["code"], vq["scale"], vb).reshape(Hkv, n_packed, d)
+    G = Hq // Hkv
+    for i in range(T):
+        for h in range(Hq):
+            g = h // G
+            qp = _rotate_numpy(sigma, q[0, i, h][None])[0]
+            w = Sd @ qp
+            s = nrm[g] * ((c32[idx[g]] @ qp) + gam[g] * math.sqrt(math.pi / 2) / d * ((2 * z[g] - 1) @ w))
+            for out, n in ((got, min(n_packed, pos0 + i + 1)), (full, n_packed)):
+                e = np.exp(scale * (s[:n] - s[:n].max()))
+                np.testing.assert_allclose(out[0, i, h], e @ vhat[g, :n] / e.sum(), rtol=1e-10, atol=1e-12)
+    # a query token past the history attends to all of it; before it (pos0 < 0 is not allowed
+    # by the library) the causal window would be empty: zeros
+    assert not O.prefill(pos0=-1, causal=True, **{**common, "T": 1, "q": q[:, :1]}).any()
+
