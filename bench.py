@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--ragged", action="store_true",
                    help="time only the decode, over a ragged batch: sequence b attends to its own seeded "
                         "lengths (packed uniform in [1, packed tokens], ring uniform in [0, ring tokens])")
+    p.add_argument("--prefill", type=int, default=0, metavar="QUERY_TOKENS",
+                   help="time only prefill attention over the packed cache (layer 0): the last QUERY_TOKENS "
+                        "tokens of every sequence's history as causal queries")
     p.add_argument("--cpu-sample-tokens", type=int, default=32768)
     p.add_argument("--probe-copy-mib", type=int, default=0,
                    help="only time a plain device-to-device copy of this many MiB (achievable HBM "
@@ -244,6 +247,9 @@ def main():
     if args.ragged:
         ragged(args, w, cfg, tables, copies, n_dec, scale, rec, in_bytes, kn, vn)
         return
+    if args.prefill:
+        prefill(args, w, cfg, tables, copies, n_dec, scale, rec, in_bytes)
+        return
 
     K_ = args.steps
     ms_step = back_to_back(step, K_)
@@ -377,6 +383,55 @@ def ragged(args, w, cfg, tables, copies, n_copies, scale, rec, in_bytes, kn=None
                             "unit": "GB/s", "frac": round(bytes_r / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                             "traffic": None, "algorithmic_bytes_per_launch": bytes_r // L},
         "uniform_at_maxima_ms": round(ms_u, 4),
+    }), flush=True)
+
+
+def prefill(args, w, cfg, tables, copies, n_copies, scale, rec, in_bytes):
+    """Prefill attention over the packed cache of layer 0: the last T tokens of every
+    sequence's history as causal query tokens (query token i at position n_packed - T + i),
+    HIP events around K back-to-back calls."""
+    import torch
+    import compressed_decode_attention_02_amd as tq
+    d, B, hq, hkv, Tp = w.d, w.batch, w.hq, w.hkv, w.n_packed
+    T = min(args.prefill, Tp)
+    pos0 = Tp - T
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.cid * 1000 + 17)
+    dt = torch.bfloat16 if w.in_dtype == "bf16" else torch.float32
+    q = torch.randn((B, T, hq, d), generator=gen, device="cuda", dtype=torch.float32).to(dt)
+    out = torch.empty((B, T, hq, d), dtype=torch.float32, device="cuda")
+    ws = tq.new_prefill_workspace(cfg, B, T, hq, hkv, Tp)
+
+    def call(c):
+        tq.tq_prefill_attention(cfg, tables, q, B, T, hq, hkv, copies[c]["store"].struct(0), Tp, pos0, True, scale,
+                                out, ws)
+    for i in range(args.warmup):
+        call(i % n_copies)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        call(i % n_copies)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # algorithmic: every sequence's records once, queries in, outputs out; streamed: each query
+    # token reads its own prefix (the decode kernels take one query token per batch element)
+    alg = B * hkv * Tp * rec + B * T * hq * d * (in_bytes + 4)
+    streamed = hkv * rec * B * sum(pos0 + i + 1 for i in range(T)) + B * T * hq * d * (in_bytes + 4)
+    print(json.dumps({
+        "metric": "prefill attention over the packed cache: query tokens/s + HBM GB/s",
+        "value": round(B * T / (ms * 1e-3), 1), "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.in_dtype, "data": "synthetic (seeded device draws of the workload's laws)",
+        "config": {"workload": w.name + "_prefill%d" % T, "layers": 1, "batch": B, "q_heads": hq, "kv_heads": hkv,
+                   "head_dim": d, "packed_tokens": Tp, "query_tokens": T, "causal": True, "first_position": pos0,
+                   "key_bits": w.key_bits, "value_bits": w.value_bits},
+        "streamed_GBps": round(streamed / (ms * 1e-3) / 1e9, 1),
+        "roofline": {"kernel": "decode kernels, one query token per batch element", "bound": "hbm",
+                     "achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": alg, "streamed_bytes_per_call": streamed},
     }), flush=True)
 
 
