@@ -85,7 +85,8 @@ __device__ __forceinline__ float load_q(const DecodeArgs &a, int64_t off) {
 template <int D, int NW>
 struct PrepShape {
     static constexpr int NT = 64 * NW;
-    static constexpr int PARTS = NT / D >= 4 ? 4 : (NT / D >= 2 ? 2 : 1);
+    // (12-wave groups form w = S q' whole, one (row, head) per thread, from an LDS copy of S)
+    static constexpr int PARTS = NW == 12 ? 1 : (NT / D >= 4 ? 4 : (NT / D >= 2 ? 2 : 1));
     static constexpr int SEG = D / PARTS;  // columns of S per thread
     template <int G>
     static constexpr int floats() { return (1 + PARTS) * G * D; }
@@ -202,6 +203,71 @@ __device__ void prep_query(PrepRegs<D, G, NW> &pr, float *qw) {
     __syncthreads();
 }
 
+// 12-wave groups (d = 128): the preparation from LDS copies of S and of the slice's queries,
+// made by the waves' first copies ahead of their packed blocks (so that it does not wait for
+// those).  S is stored piece-major: 16-byte piece k of row i (columns 8k .. 8k + 7) at slot
+// k D + i; the queries in their input dtype, [G][D].
+// element j of head g of the copied queries, as fp32
+__device__ __forceinline__ float lds_q(const unsigned char *pq, int dtype, int idx) {
+    if (dtype == TQ_F32) return reinterpret_cast<const float *>(pq)[idx];
+    const uint32_t h = reinterpret_cast<const uint16_t *>(pq)[idx];
+    return dtype == TQ_BF16 ? __uint_as_float(h << 16) : f16_lo(h);
+}
+
+// q'_g = H (sigma o q_g) by wave g < G, as prep_transform
+template <int D, int G, int NW>
+__device__ __forceinline__ void prep_transform12(const DecodeArgs &a, const uint32_t (&sg)[4], const unsigned char *pq,
+                                                 float *qw) {
+    static_assert(D == 128, "two coordinates per lane");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (wave >= G) return;
+    const int g = wave;
+    // sigma (its words loaded at the start); coordinate lane + 64 e is bit `lane` of the 64-bit
+    // pair of words 2 e, 2 e + 1
+    const uint64_t sw0 = sg[0] | ((uint64_t)sg[1] << 32), sw1 = sg[2] | ((uint64_t)sg[3] << 32);
+    float v[2];
+    v[0] = flip_sign(lds_q(pq, a.q_dtype, g * D + lane), (uint32_t)(sw0 >> lane) & 1u);
+    v[1] = flip_sign(lds_q(pq, a.q_dtype, g * D + lane + 64), (uint32_t)(sw1 >> lane) & 1u);
+#pragma unroll
+    for (int len = 1; len < 64; len <<= 1)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float o = __shfl_xor(v[e], len);
+            v[e] = (lane & len) ? (o - v[e]) : (v[e] + o);
+        }
+    const float u0 = v[0] + v[1], u1 = v[0] - v[1];
+    qw[g * D + lane] = u0;
+    qw[g * D + lane + 64] = u1;
+}
+
+// w_g = S q'_g: thread (row i, head g) of the first G D threads, from the piece-major copy of S
+// (a wave reads one piece of 64 consecutive rows: one contiguous kilobyte) and q'_g (the same
+// address in every lane); written as the single partial sum
+template <int D, int G, int NW>
+__device__ __forceinline__ void prep_product12(const unsigned char *ps, float *qw) {
+    const int tid = threadIdx.x;
+    if (tid >= G * D) return;
+    const int i = tid % D, g = tid / D;
+    const float *qg = qw + g * D;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};  // four chains (the sum is latency-bound)
+#pragma unroll
+    for (int k = 0; k < D / 8; ++k) {
+        const uint4 pk = *reinterpret_cast<const uint4 *>(ps + (k * D + i) * 16);
+        const float4 q0 = *reinterpret_cast<const float4 *>(qg + 8 * k);
+        const float4 q1 = *reinterpret_cast<const float4 *>(qg + 8 * k + 4);
+        float &c = acc[k & 3];
+        c = fmaf(f16_lo(pk.x), q0.x, c);
+        c = fmaf(f16_hi(pk.x), q0.y, c);
+        c = fmaf(f16_lo(pk.y), q0.z, c);
+        c = fmaf(f16_hi(pk.y), q0.w, c);
+        c = fmaf(f16_lo(pk.z), q1.x, c);
+        c = fmaf(f16_hi(pk.z), q1.y, c);
+        c = fmaf(f16_lo(pk.w), q1.z, c);
+        c = fmaf(f16_hi(pk.w), q1.w, c);
+    }
+    qw[(G + g) * D + i] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 template <int D, int VB, int G>
 struct DecodeShape {
     static constexpr int KW = D / 8;          // key words per token
@@ -258,6 +324,15 @@ struct alignas(16) DecodeSmem {
     float wm[NW][G], wl[NW][G];
     float rm[G], rl[G];  // the split's ring tokens: maximum and sum of p per head
     int next_blk;       // the split's next block not yet handed to a wave
+    // 12-wave groups: the split's ring rows, copied into LDS by the wave that attends to them
+    // (4-token chunks: keys 1 KB each padded by 16 bytes, values 1 KB each), its unrotated
+    // queries (then its p values) and its result o
+    static constexpr bool RW = NW == 12;
+    static constexpr int RCH = 16;  // 64 ring tokens per split at most
+    alignas(16) unsigned char rk[RW ? RCH * 1040 : 16];
+    alignas(16) unsigned char rv[RW ? RCH * 1024 : 16];
+    alignas(16) float rq[RW ? G : 1][RW ? D : 1];
+    alignas(16) float ro[RW ? G : 1][RW ? D : 1];
 };
 
 // ---- global -> LDS copies issued by hand, waited for with explicit counts.  M0 holds the
@@ -565,6 +640,115 @@ __device__ void ring_attend(const DecodeArgs &a, const RingRegs<D, G, NW> &rr, f
     }
 }
 
+// The split's ring tokens in 12-wave groups, attended by one wave from the LDS copies of their
+// rows (made by that wave's first copies): logits with lane = token, the softmax of each head
+// across the lanes, o with lane = coordinate pair; (m, l) into rm / rl and o into ro.  A fused
+// step's new token (ring slot new_slot) is taken from the input rounded to fp16, as the append
+// rounds it, and written into the ring and into the LDS rows first.  rq holds the unrotated
+// queries on entry and the p values afterwards.
+template <int D, int VB, int G, int NW>
+__device__ void ring_wave12(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, int bk, int r0, int n) {
+    static_assert(D == 128 && NW == 12, "12-wave groups at head_dim 128");
+    const int lane = threadIdx.x & 63;
+    wait_vm<0>();  // the wave's own copies of the rows
+    const int ns = a.new_slot - r0;
+    if (a.new_slot >= 0 && ns >= 0 && ns < n) {
+        const int64_t e0 = (int64_t)bk * D + 2 * lane;
+        float k0, k1, v0, v1;
+        if (a.kv_dtype == TQ_F32) {
+            k0 = load1(a.k_new, e0, f32_tag{}); k1 = load1(a.k_new, e0 + 1, f32_tag{});
+            v0 = load1(a.v_new, e0, f32_tag{}); v1 = load1(a.v_new, e0 + 1, f32_tag{});
+        } else if (a.kv_dtype == TQ_BF16) {
+            k0 = load1(a.k_new, e0, bf16_tag{}); k1 = load1(a.k_new, e0 + 1, bf16_tag{});
+            v0 = load1(a.v_new, e0, bf16_tag{}); v1 = load1(a.v_new, e0 + 1, bf16_tag{});
+        } else {
+            k0 = load1(a.k_new, e0, f16_tag{}); k1 = load1(a.k_new, e0 + 1, f16_tag{});
+            v0 = load1(a.v_new, e0, f16_tag{}); v1 = load1(a.v_new, e0 + 1, f16_tag{});
+        }
+        const uint32_t kw = f32_to_f16_bits(k0) | ((uint32_t)f32_to_f16_bits(k1) << 16);
+        const uint32_t vw = f32_to_f16_bits(v0) | ((uint32_t)f32_to_f16_bits(v1) << 16);
+        *reinterpret_cast<uint32_t *>(sm.rk + (ns >> 2) * 1040 + (ns & 3) * 256 + 4 * lane) = kw;
+        *reinterpret_cast<uint32_t *>(sm.rv + (ns >> 2) * 1024 + (ns & 3) * 256 + 4 * lane) = vw;
+        const int64_t slot = ((int64_t)bk * a.buffer_size + a.new_slot) * D;
+        reinterpret_cast<uint32_t *>(a.rk + slot)[lane] = kw;
+        reinterpret_cast<uint32_t *>(a.rv + slot)[lane] = vw;
+    }
+    wave_sync();
+    // logits (log2 units) of token `lane` for every head
+    const int tk = min(lane, n - 1);
+    const unsigned char *kr = sm.rk + (tk >> 2) * 1040 + (tk & 3) * 256;
+    float s[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) s[g] = 0.f;
+#pragma unroll 4
+    for (int k = 0; k < D / 8; ++k) {
+        const uint4 kv = *reinterpret_cast<const uint4 *>(kr + 16 * k);
+        const float e[8] = {f16_lo(kv.x), f16_hi(kv.x), f16_lo(kv.y), f16_hi(kv.y),
+                            f16_lo(kv.z), f16_hi(kv.z), f16_lo(kv.w), f16_hi(kv.w)};
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float4 q0 = *reinterpret_cast<const float4 *>(&sm.rq[g][8 * k]);
+            const float4 q1 = *reinterpret_cast<const float4 *>(&sm.rq[g][8 * k + 4]);
+            s[g] = fmaf(e[0], q0.x, s[g]);
+            s[g] = fmaf(e[1], q0.y, s[g]);
+            s[g] = fmaf(e[2], q0.z, s[g]);
+            s[g] = fmaf(e[3], q0.w, s[g]);
+            s[g] = fmaf(e[4], q1.x, s[g]);
+            s[g] = fmaf(e[5], q1.y, s[g]);
+            s[g] = fmaf(e[6], q1.z, s[g]);
+            s[g] = fmaf(e[7], q1.w, s[g]);
+        }
+    }
+    const float lscale = a.scale * kLog2e;
+    float m[G], l[G], pv[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float x = lane < n ? s[g] * lscale : -INFINITY;
+        float mx = x;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        pv[g] = lane < n ? exp2f(x - mx) : 0.f;
+        float sum = pv[g];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+        m[g] = mx;
+        l[g] = sum;
+    }
+    wave_sync();  // every lane has read the queries
+#pragma unroll
+    for (int g = 0; g < G; ++g) sm.rq[g][lane] = pv[g];
+    wave_sync();
+    // o of coordinates 2 lane, 2 lane + 1: sum over the tokens of p v (p = 0 past n)
+    float o0[G], o1[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) o0[g] = o1[g] = 0.f;
+    for (int t4 = 0; t4 < n; t4 += 4) {
+        float4 pp[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) pp[g] = *reinterpret_cast<const float4 *>(&sm.rq[g][t4]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int tt = t4 + u;
+            const uint32_t vv = *reinterpret_cast<const uint32_t *>(sm.rv + (tt >> 2) * 1024 + (tt & 3) * 256 + 4 * lane);
+            const float va = f16_lo(vv), vb = f16_hi(vv);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float pg = u == 0 ? pp[g].x : (u == 1 ? pp[g].y : (u == 2 ? pp[g].z : pp[g].w));
+                o0[g] = fmaf(pg, va, o0[g]);
+                o1[g] = fmaf(pg, vb, o1[g]);
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) *reinterpret_cast<float2 *>(&sm.ro[g][2 * lane]) = make_float2(o0[g], o1[g]);
+    if (lane == 0)
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            sm.rm[g] = m[g];
+            sm.rl[g] = l[g];
+        }
+}
+
 // ------------------------------------------------------------------ packed split (one wave)
 template <int D, int VB, int G, int NW>
 __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, int bk, int sbk, int b, int kvh,
@@ -577,22 +761,23 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     // then scalar values
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n16 = lane & 15, q = lane >> 4;
-
-    // centroid byte tables: v_perm with selector byte idx picks byte idx of (t*1 : t*0), so
-    // tl/th hold the low/high bytes of the eight fp16 centroids
-    uint32_t tl0 = 0, tl1 = 0, th0 = 0, th1 = 0;
+    // 12-wave groups: the codebook and sigma, loaded first and waited for here (loads issued
+    // after the block copies of every workgroup come back late, and the LDS waits of the
+    // preparation would wait for them too when they are scalar loads: lgkmcnt counts both)
+    float cent[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    uint32_t sgw[4] = {0u, 0u, 0u, 0u};
+    if constexpr (NW == 12) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t h = f32_to_f16_bits(a.centroids[i]);
-        const int sh = 8 * (i & 3);
-        if (i < 4) {
-            tl0 |= (h & 0xffu) << sh;
-            th0 |= (h >> 8) << sh;
-        } else {
-            tl1 |= (h & 0xffu) << sh;
-            th1 |= (h >> 8) << sh;
-        }
+        for (int i = 0; i < 8; ++i) cent[i] = a.centroids[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sgw[i] = a.sign_bits[i];
+        asm volatile("" : "+v"(cent[0]), "+v"(cent[1]), "+v"(cent[2]), "+v"(cent[3]), "+v"(cent[4]), "+v"(cent[5]),
+                     "+v"(cent[6]), "+v"(cent[7]), "+v"(sgw[0]), "+v"(sgw[1]), "+v"(sgw[2]), "+v"(sgw[3]));
     }
+    auto centroid = [&](int i) -> float {
+        if constexpr (NW == 12) return cent[i];
+        else return a.centroids[i];
+    };
 
     // score products.  The query is the A operand (16 rows of query parts), the key block
     // the B operand (16 token columns per tile), so a tile's result holds every part of
@@ -648,9 +833,10 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
         vw_rc(lane, i, r, col);
         o_vw[i] = r * (S::VW * 4) + col;
     }
-    auto issue = [&](int t0, int bi) {
+    auto issue = [&](int t0, int bi, bool first = false) {
         const uint32_t base = lds_wave + (uint32_t)(bi * NW * S::BUF_B);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // (a wave's first copies overwrite no buffer it has read)
+        if (!first) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const int64_t rb = block_rec(t0);
         const uint32_t *kw_b = a.kw + rb * S::KW;
         const float *kn_b = a.kn + rb * 2;
@@ -717,14 +903,74 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     // the second block's after it.  The compiler's own waits for the preparation's loads
     // then also cover the older copies.
     const int nb = (t_end - t_begin + kBlock - 1) / kBlock;
-    int b0 = wave, b1 = wave + NW;
-    if (threadIdx.x == 0) sm.next_blk = 2 * NW;  // read after the barriers below
-    if (b0 < nb) issue(t_begin + kBlock * b0, 0);
+    // 12-wave groups: wave NW - 1 attends to the split's ring tokens and takes no first blocks
+    constexpr bool RW = NW == 12;
+    const bool ringw = RW && nr > 0;
+    const int nws = ringw ? NW - 1 : NW;
+    int b0 = wave, b1 = wave + nws;
+    if (wave >= nws) b0 = b1 = nb;
+    if (threadIdx.x == 0) sm.next_blk = 2 * nws;  // read after the barriers below
+    // 12-wave groups: S (piece-major) and the slice's queries into the second staging buffers,
+    // copied ahead of the first blocks (the preparation then waits for these alone); the ring
+    // wave copies its tokens' rows instead
+    unsigned char *const prepb = &sm.stage[1][0][0];
+    constexpr int PS_B = D * D * 2;
+    constexpr int PQ_B = G * D * 4 > 1024 ? G * D * 4 : 1024;
+    if constexpr (RW) {
+        static_assert(D == 128 && PS_B + PQ_B + 2 * G * D * 4 <= NW * S::BUF_B, "12-wave preparation in LDS");
+        if (wave < nws) {
+            const int qbytes = a.q_dtype == TQ_F32 ? 4 : 2;
+            const int qsz = G * D * qbytes;
+            const int nch = PS_B / 1024 + (qsz + 1023) / 1024;
+            const unsigned char *qsrc =
+                static_cast<const unsigned char *>(a.q) + ((int64_t)b * a.hq + kvh * G) * D * qbytes;
+            const uint32_t pl = (uint32_t)(uintptr_t)prepb;
+            for (int c = wave; c < nch; c += nws) {
+                if (c < PS_B / 1024) {
+                    const int s = 64 * c + lane, k = s / D, i = s % D;
+                    dma16(a.S, (uint32_t)((i * D + 8 * k) * 2), pl + 1024 * c);
+                } else {
+                    const int cq = c - PS_B / 1024;
+                    dma16(qsrc, (uint32_t)min(1024 * cq + 16 * lane, qsz - 16), pl + PS_B + 1024 * cq);
+                }
+            }
+        } else {
+            const int64_t r0e = ((int64_t)bk * a.buffer_size + r0) * D;
+            const uint32_t lk = (uint32_t)(uintptr_t)&sm.rk[0], lv = (uint32_t)(uintptr_t)&sm.rv[0];
+            for (int c = 0; 4 * c < nr; ++c) {
+                const uint32_t off = (uint32_t)(min(4 * c + (lane >> 4), nr - 1) * D * 2 + (lane & 15) * 16);
+                dma16(a.rk + r0e, off, lk + 1040 * c);
+                dma16(a.rv + r0e, off, lv + 1024 * c);
+            }
+        }
+        // S and the queries come back before the block copies of every workgroup crowd the
+        // memory system, and the preparation then runs while those are in flight
+        if (wave < nws) wait_vm<0>();
+    }
+    if (b0 < nb) issue(t_begin + kBlock * b0, 0, true);
+    // centroid byte tables (built after the first copies are out): v_perm with selector byte idx picks byte idx of (t*1 : t*0), so
+    // tl/th hold the low/high bytes of the eight fp16 centroids
+    uint32_t tl0 = 0, tl1 = 0, th0 = 0, th1 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t h = f32_to_f16_bits(centroid(i));
+        const int sh = 8 * (i & 3);
+        if (i < 4) {
+            tl0 |= (h & 0xffu) << sh;
+            th0 |= (h >> 8) << sh;
+        } else {
+            tl1 |= (h & 0xffu) << sh;
+            th1 |= (h >> 8) << sh;
+        }
+    }
+
     // all loads of the start at once: the ring tokens' words, then the query preparation's
     // inputs (at d = 256 the prepared queries from the workspace)
     RingRegs<D, G, NW> rr;
-    if (nr > 0) ring_load<D, G, NW>(a, rr, bk, r0, nr);
-    float *qw = reinterpret_cast<float *>(&sm.stage[1][0][0]);
+    if constexpr (!RW) {
+        if (nr > 0) ring_load<D, G, NW>(a, rr, bk, r0, nr);
+    }
+    float *qw = reinterpret_cast<float *>(RW ? prepb + PS_B + PQ_B : &sm.stage[1][0][0]);
     static_assert(PrepShape<D, NW>::template floats<G>() * 4 <= NW * S::BUF_B, "query preparation in LDS");
     constexpr int NQ4 = 2 * G * D / 4;                        // float4 of the prepared queries (d = 256)
     constexpr int NPW = (NQ4 + 64 * NW - 1) / (64 * NW);      // per thread
@@ -738,7 +984,7 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
 #pragma unroll
         for (int i = 0; i < NPW; ++i)
             if (threadIdx.x + i * 64 * NW < NQ4) pw4[i] = src[threadIdx.x + i * 64 * NW];
-    } else {
+    } else if constexpr (!RW) {
         prep_load<D, G, NW>(a, prg, b, kvh);
     }
     // The split's ring tokens use the second staging buffers as scratch too.  Where the ring
@@ -748,12 +994,23 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     constexpr int QWB = PrepShape<D, NW>::template floats<G>() * 4;
     constexpr int RSB = NW * S::BUF_B - QWB;
     constexpr int GBM = RS::gb(NW * S::BUF_B);
-    constexpr bool MERGED = (RS::fixed() + RS::NTG * GBM * D) * 4 <= RSB;
+    constexpr bool MERGED = !RW && (RS::fixed() + RS::NTG * GBM * D) * 4 <= RSB;
     float *rqr = qw + QWB / 4, *rpr = rqr + G * D, *ros = rpr + G * kRingPerSplit<D>;
-    if constexpr (!MERGED) {
+    if constexpr (!MERGED && !RW) {
         if (nr > 0) ring_attend<D, G, NW, NW * S::BUF_B>(a, rr, qw, sm.rm, sm.rl, bk, b, kvh, r0, nr, orr);
     }
-    if constexpr (D == 256) {
+    if constexpr (RW) {
+        __syncthreads();  // every wave's copies of S and of the queries
+        prep_transform12<D, G, NW>(a, sgw, prepb + PS_B, qw);
+        if (ringw && wave == NW - 1) {
+            // the ring wave's unrotated queries (fp32)
+#pragma unroll
+            for (int e = 0; e < G * D / 64; ++e) {
+                const int idx = lane + 64 * e;
+                sm.rq[idx / D][idx % D] = lds_q(prepb + PS_B, a.q_dtype, idx);
+            }
+        }
+    } else if constexpr (D == 256) {
 #pragma unroll
         for (int i = 0; i < NPW; ++i)
             if (threadIdx.x + i * 64 * NW < NQ4) reinterpret_cast<float4 *>(qw)[threadIdx.x + i * 64 * NW] = pw4[i];
@@ -764,7 +1021,8 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
         if (nr > 0) ring_p1<D, G, NW>(a, rr, rqr, bk, b, kvh, r0, nr);
     }
     __syncthreads();
-    if constexpr (D != 256) prep_product<D, G, NW>(prg, qw);
+    if constexpr (RW) prep_product12<D, G, NW>(prepb, qw);
+    else if constexpr (D != 256) prep_product<D, G, NW>(prg, qw);
     if constexpr (MERGED) {
         if (nr > 0) ring_p2<D, G, NW>(a, rr, rqr, rpr, nr);
     }
@@ -816,19 +1074,19 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     i32x4_t qa[2], wa[2];
     float i8_alpha = 0.f, i8_beta4 = 0.f, i8_mbw = 0.f;
     uint32_t ch0 = 0, ch1 = 0, cl0 = 0, cl1 = 0;  // int8 path: hi / lo bytes of c * 2^Sc by index
-    u32x4_t *const afrag = reinterpret_cast<u32x4_t *>(&sm.bfrag[0][0]);  // [q', w][ks][lane]
-    static_assert(!I8 || sizeof(sm.bfrag) >= 256 * sizeof(u32x4_t), "int8 fragments in the fragment area");
+    u32x4_t *const afrag = reinterpret_cast<u32x4_t *>(&sm.bfrag[0][0]);  // the digit bytes
+    static_assert(!I8 || sizeof(sm.bfrag) >= 2 * G * 3 * 128, "int8 digits in the fragment area");
     int i8_sc = 0;
     if constexpr (I8) {
         float cmax = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) cmax = fmaxf(cmax, fabsf(a.centroids[i]));
+        for (int i = 0; i < 8; ++i) cmax = fmaxf(cmax, fabsf(centroid(i)));
         int ec;
         (void)frexpf(cmax, &ec);  // cmax < 2^ec
         i8_sc = 14 - ec;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int ci = (int)ldexpf(a.centroids[i], i8_sc);
+            const int ci = (int)ldexpf(centroid(i), i8_sc);
             const int lo = ((ci + 128) & 255) - 128, hi = (ci - lo) >> 8;
             const int sh = 8 * (i & 3);
             if (i < 4) {
@@ -842,8 +1100,12 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
     }
     if constexpr (I8) {
         const float cs = a.scale * kLog2e * (1.0f / sqrtf((float)D)), ss = cs * kQjl;
-        // phase A: wave g takes head g to fixed point (in place: q' as int32, w into the first
-        // partial-sum slot) and stores the head's constants
+        // wave g takes head g to fixed point and writes the digit bytes straight into the
+        // operand layout: region (which = q' or w, head g, digit k) holds 128 bytes, coordinate
+        // c at byte 8 (c / 8) + 4 (c % 2) + (c % 8) / 2, so that the operand of lane (row
+        // 4 g + k, lane group qq) at k-step ks is the 16 bytes at 32 qq + 16 ks; and stores the
+        // head's constants
+        unsigned char *const dig = reinterpret_cast<unsigned char *>(afrag);  // [which][g][k][128]
         if (wave < G) {
             constexpr int PARTS = PrepShape<D, NW>::PARTS;
             const int g = wave;
@@ -867,15 +1129,23 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
             (void)frexpf(mq, &eq);
             (void)frexpf(mw, &ew);
             const int sq = 22 - eq, sw = 22 - ew;
-            double wsum = 0.0;
-            int *qi = reinterpret_cast<int *>(qw);
+            int wsum = 0;  // |sum| < 128 * 2^22: exact in 32 bits
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const int j = lane + 64 * e;
+                const int c = lane + 64 * e;
+                const int pos = 8 * (c >> 3) + 4 * (c & 1) + ((c & 7) >> 1);
                 const int iq = (int)rintf(ldexpf(xq[e], sq)), iw = (int)rintf(ldexpf(xw[e], sw));
-                qi[g * D + j] = iq;
-                qi[(G + g) * D + j] = iw;
-                wsum += (double)iw;
+                wsum += iw;
+#pragma unroll
+                for (int wh = 0; wh < 2; ++wh) {
+                    const int v = wh ? iw : iq;
+                    const int d2 = ((v + 128) & 255) - 128, v1 = (v - d2) >> 8;
+                    const int d1 = ((v1 + 128) & 255) - 128, d0 = (v1 - d1) >> 8;
+                    unsigned char *r = dig + ((wh * G + g) * 3) * 128 + pos;
+                    r[0] = (unsigned char)d0;
+                    r[128] = (unsigned char)d1;
+                    r[256] = (unsigned char)d2;
+                }
             }
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
@@ -889,29 +1159,6 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
         }
         if constexpr (MERGED) {
             if (nr > 0) ring_p3<D, G, NW>(rpr, sm.rm, sm.rl, nr);
-        }
-        __syncthreads();
-        // phase B: the fragment bytes, one 16-byte operand per thread (threads 0 .. 255)
-        if (threadIdx.x < 256) {
-            const int tid = threadIdx.x;
-            const int which = tid >> 7, ks = (tid >> 6) & 1, ln = tid & 63, r16 = ln & 15, qq = ln >> 4;
-            const int g = r16 >> 2, k = r16 & 3;
-            const int *src = reinterpret_cast<const int *>(qw) + (which ? G + g : g) * D;
-            u32x4_t f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uint32_t wd = 0;
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb) {
-                    const int v = src[8 * (4 * qq + 2 * ks + (r >> 1)) + 2 * bb + (r & 1)];
-                    const int d2 = ((v + 128) & 255) - 128, v1 = (v - d2) >> 8;
-                    const int d1 = ((v1 + 128) & 255) - 128, d0 = (v1 - d1) >> 8;
-                    const int dk = k == 0 ? d0 : (k == 1 ? d1 : (k == 2 ? d2 : 0));
-                    wd |= (uint32_t)(dk & 255) << (8 * bb);
-                }
-                f[r] = wd;
-            }
-            afrag[(2 * which + ks) * 64 + ln] = f;
         }
         __syncthreads();
     } else {
@@ -988,16 +1235,33 @@ __device__ void packed_wave(const DecodeArgs &a, DecodeSmem<D, VB, G, NW> &sm, i
         }
     }
     if constexpr (I8) {
+        // row n16 = 4 g + k: digit k of head g (row 4 g + 3 is zero)
+        const int fg = n16 >> 2, fk = n16 & 3;
+        const unsigned char *dig = reinterpret_cast<const unsigned char *>(afrag);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            qa[ks] = __builtin_bit_cast(i32x4_t, afrag[ks * 64 + lane]);
-            wa[ks] = __builtin_bit_cast(i32x4_t, afrag[(2 + ks) * 64 + lane]);
+            const int off = 32 * q + 16 * ks;
+            qa[ks] = fk < 3 ? *reinterpret_cast<const i32x4_t *>(dig + (fg * 3 + fk) * 128 + off) : (i32x4_t){0, 0, 0, 0};
+            wa[ks] = fk < 3 ? *reinterpret_cast<const i32x4_t *>(dig + ((G + fg) * 3 + fk) * 128 + off)
+                            : (i32x4_t){0, 0, 0, 0};
         }
         i8_alpha = sm.i8c[q][0];
         i8_beta4 = sm.i8c[q][1];
         i8_mbw = sm.i8c[q][2];
     }
     // (the second staging buffers are free)
+    if constexpr (RW) {
+        if (ringw && wave == NW - 1) {
+            ring_wave12<D, VB, G, NW>(a, sm, bk, r0, nr);
+            // then two blocks from the counter
+            int nx = 0;
+            if (lane == 0) nx = atomicAdd(&sm.next_blk, 2);
+            nx = __builtin_amdgcn_readfirstlane(nx);
+            b0 = nx;
+            b1 = nx + 1;
+            if (b0 < nb) issue(t_begin + kBlock * b0, 0);
+        }
+    }
     if (b1 < nb) issue(t_begin + kBlock * b1, 1);
     const int cslot = rc ? q * SM::NSL + ri : SM::FZ, sslot = rs ? q * SM::NSL + ri : SM::FZ;
     // The lane's logits after the score products: token row trow of the block, heads
@@ -1483,6 +1747,12 @@ __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd<D, VB, G, NW>, kDecodeWav
 void k_decode_main(DecodeArgs a) {
     static_assert(sizeof(DecodeSmem<D, VB, G, NW>) <= 160 * 1024, "LDS of one workgroup");
     __shared__ DecodeSmem<D, VB, G, NW> sm;
+    // the arguments the start of every workgroup reads, loaded in one batch (arguments read
+    // only under branches would otherwise be loaded and waited for one after another before
+    // the first copies go out)
+    asm volatile("" ::"s"(a.n_packed), "s"(a.per_split), "s"(a.seq_packed), "s"(a.seq_ring), "s"(a.n_ring),
+                 "s"(a.ring_per_split), "s"(a.q_tokens), "s"(a.causal), "s"(a.hkv), "s"(a.n_split), "s"(a.kw),
+                 "s"(a.kn), "s"(a.vw), "s"(a.vs), "s"(a.bt), "s"(a.cap));
     const int tid = threadIdx.x;
     const int split = blockIdx.x;  // split: a range of packed tokens and of ring tokens
     const int bk = blockIdx.y;     // b * hkv + kv head == slice
@@ -1540,7 +1810,8 @@ void k_decode_main(DecodeArgs a) {
                 if (mr != -INFINITY) {
                     const float f = exp2f(mr - M);
                     L = fmaf(sm.rl[g], f, L);
-                    O = fmaf(orr[k], f, O);
+                    if constexpr (NW == 12) O = fmaf(sm.ro[g][j], f, O);
+                    else O = fmaf(orr[k], f, O);
                 }
             }
             if (a.n_split == 1) {
