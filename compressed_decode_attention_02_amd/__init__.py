@@ -11,4 +11,6 @@ from .binding import (  # noqa: F401
     tq_decode_attention_ragged, tq_decode_scores, tq_decode_step, tq_decode_workspace_bytes, tq_flush, tq_packed,
     tq_packed_bytes_per_token, tq_quantize_kv, tq_ring, tq_rotate, tq_tables, tq_tables_bytes,
     tq_prefill_attention, tq_prefill_workspace_bytes, new_prefill_workspace, key_record_words,
+    KiviStore, tq_kivi_store, tq_kivi_bytes_per_token, tq_kivi_quantize, tq_kivi_decode_workspace_bytes,
+    tq_kivi_decode_attention, new_kivi_workspace,
 )

@@ -22,6 +22,7 @@ EXPORTS = [
     "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_attention_ragged", "tq_decode_step",
     "tq_status_string", "tq_rotate", "tq_decode_scores", "tq_decode_attention_noalloc",
     "tq_prefill_workspace_bytes", "tq_prefill_attention",
+    "tq_kivi_bytes_per_token", "tq_kivi_quantize", "tq_kivi_decode_workspace_bytes", "tq_kivi_decode_attention",
 ]
 
 
@@ -46,6 +47,11 @@ class tq_packed(ctypes.Structure):
                 ("val_scales", ctypes.c_void_p), ("capacity", ctypes.c_int64), ("block_table", ctypes.c_void_p),
                 ("page_tokens", ctypes.c_int32), ("pages_per_slice", ctypes.c_int32), ("n_pages", ctypes.c_int64),
                 ("error_flag", ctypes.c_void_p)]
+
+
+class tq_kivi_store(ctypes.Structure):
+    _fields_ = [("key_codes", ctypes.c_void_p), ("key_scale", ctypes.c_void_p), ("key_zero", ctypes.c_void_p),
+                ("val_codes", ctypes.c_void_p), ("val_params", ctypes.c_void_p), ("capacity", ctypes.c_int64)]
 
 
 class tq_ring(ctypes.Structure):
@@ -89,6 +95,11 @@ def _lib():
         "tq_prefill_attention": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, I32, K, I64, I64, I32, F, P,
                                                 P, SZ, P]),
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "tq_kivi_bytes_per_token": (SZ, [I32]),
+        "tq_kivi_quantize": (ctypes.c_int, [I32, P, P, ctypes.c_int, I32, I64, ctypes.POINTER(tq_kivi_store), I64, P]),
+        "tq_kivi_decode_workspace_bytes": (SZ, [I32, I32, I32, I32, I64]),
+        "tq_kivi_decode_attention": (ctypes.c_int, [I32, P, ctypes.c_int, I32, I32, I32,
+                                                    ctypes.POINTER(tq_kivi_store), I64, F, P, P, SZ, P]),
         "tq_rotate": (ctypes.c_int, [C, T, P, ctypes.c_int, I64, P, P]),
         "tq_decode_scores": (ctypes.c_int, [C, T, P, ctypes.c_int, I32, I32, I32, K, I64, R, I32, P, P]),
     }
@@ -504,3 +515,66 @@ def new_workspace(cfg, batch: int, n_q_heads: int, n_kv_heads: int, max_context:
     if n == 0:
         raise TqError("tq_decode_workspace_bytes", TQ_ERR_INVALID_ARG)
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ KIVI 2-bit variant (layout in tq.h)
+
+def tq_kivi_bytes_per_token(head_dim: int) -> int:
+    return int(_lib().tq_kivi_bytes_per_token(head_dim))
+
+
+class KiviStore:
+    """Device arrays of a KIVI store, [n_slices][capacity][...] each (capacity a multiple of 32)."""
+
+    def __init__(self, head_dim: int, n_slices: int, capacity: int, device="cuda"):
+        import torch
+        if capacity % 32:
+            raise ValueError("capacity must be a multiple of 32")
+        d = head_dim
+        self.head_dim, self.n_slices, self.capacity = d, n_slices, capacity
+        self.key_codes = torch.zeros((n_slices, capacity, d // 16), dtype=torch.int32, device=device)
+        self.key_scale = torch.zeros((n_slices, capacity // 32, d), dtype=torch.int16, device=device)
+        self.key_zero = torch.zeros((n_slices, capacity // 32, d), dtype=torch.int16, device=device)
+        self.val_codes = torch.zeros((n_slices, capacity, d // 16), dtype=torch.int32, device=device)
+        self.val_params = torch.zeros((n_slices, capacity, 2), dtype=torch.int16, device=device)
+
+    def struct(self, slice_offset: int = 0) -> tq_kivi_store:
+        return tq_kivi_store(self.key_codes[slice_offset:].data_ptr(), self.key_scale[slice_offset:].data_ptr(),
+                             self.key_zero[slice_offset:].data_ptr(), self.val_codes[slice_offset:].data_ptr(),
+                             self.val_params[slice_offset:].data_ptr(), self.capacity)
+
+
+def tq_kivi_quantize(head_dim: int, k, v, n_slices: int, n_tokens: int, dst: tq_kivi_store, dst_token0: int,
+                     stream=None):
+    _kv_pair(k, v, max(n_slices, 0) * max(n_tokens, 0) * head_dim)
+    _on_one_gpu(("k", k), ("v", v))
+    st = _lib().tq_kivi_quantize(head_dim, _ptr(k), _ptr(v), _dtype_code(k), n_slices, n_tokens, ctypes.byref(dst),
+                                 dst_token0, _stream(stream))
+    _check("tq_kivi_quantize", st)
+
+
+def tq_kivi_decode_workspace_bytes(head_dim: int, batch: int, n_q_heads: int, n_kv_heads: int,
+                                   max_context: int) -> int:
+    return int(_lib().tq_kivi_decode_workspace_bytes(head_dim, batch, n_q_heads, n_kv_heads, max_context))
+
+
+def new_kivi_workspace(head_dim: int, batch: int, n_q_heads: int, n_kv_heads: int, max_context: int, device="cuda"):
+    import torch
+    n = tq_kivi_decode_workspace_bytes(head_dim, batch, n_q_heads, n_kv_heads, max_context)
+    if n == 0:
+        raise TqError("tq_kivi_decode_workspace_bytes", TQ_ERR_INVALID_ARG)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def tq_kivi_decode_attention(head_dim: int, q, batch: int, n_q_heads: int, n_kv_heads: int, src: tq_kivi_store,
+                             n_packed: int, softmax_scale: float, out, workspace, stream=None):
+    import torch
+    _need("q", q, batch * n_q_heads * head_dim)
+    _dtype_code(q)
+    _need("out", out, batch * n_q_heads * head_dim, torch.float32)
+    _need("workspace", workspace, 0)
+    _on_one_gpu(("q", q), ("out", out), ("workspace", workspace))
+    st = _lib().tq_kivi_decode_attention(head_dim, _ptr(q), _dtype_code(q), batch, n_q_heads, n_kv_heads,
+                                         ctypes.byref(src), n_packed, softmax_scale, _ptr(out), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("tq_kivi_decode_attention", st)

@@ -515,3 +515,100 @@ extern "C" tq_status tq_decode_scores(const tq_config *cfg, const tq_tables *tab
     a.scores = scores;
     return hip_status(tq::launch_scores(cfg->head_dim, a, (hipStream_t)stream));
 }
+
+// ------------------------------------------------------------------ KIVI 2-bit variant
+namespace {
+
+bool kivi_dim_ok(int32_t d) { return d == 64 || d == 128 || d == 256; }
+
+bool kivi_store_ok(const tq_kivi_store *s) {
+    return s && s->key_codes && s->key_scale && s->key_zero && s->val_codes && s->val_params && s->capacity >= 0 &&
+           s->capacity % 32 == 0 && aligned16(s->key_codes) && aligned16(s->key_scale) && aligned16(s->key_zero) &&
+           aligned16(s->val_codes) && aligned16(s->val_params);
+}
+
+// splits of a KIVI decode: four 4-wave workgroups per CU, 64-token chunks per wave, whole
+// chunks per split
+void kivi_split_shape(int64_t slices, int64_t n_packed, int64_t &n_split, int64_t &per_split) {
+    const int64_t want = std::max<int64_t>(1, ((int64_t)tq::device_cus() * 4 + slices - 1) / slices);
+    const int64_t by_tokens = std::max<int64_t>(1, (n_packed + 255) / 256);  // a chunk for each wave
+    n_split = std::min({want, by_tokens, kMaxSplits});
+    per_split = (n_packed + n_split - 1) / n_split;
+    per_split = std::max<int64_t>(64, (per_split + 63) / 64 * 64);
+    n_split = std::max<int64_t>(1, (n_packed + per_split - 1) / per_split);
+}
+
+size_t kivi_ws_bytes(int64_t slices, int64_t G, int64_t d, int64_t n_split) {
+    const size_t po = align256(sizeof(float) * (size_t)(slices * n_split * G * d));
+    return std::max<size_t>(256, po + align256(sizeof(float) * (size_t)(slices * n_split * G * 2)));
+}
+
+}  // namespace
+
+extern "C" size_t tq_kivi_bytes_per_token(int32_t head_dim) {
+    if (!kivi_dim_ok(head_dim)) return 0;
+    return (size_t)head_dim / 4 + (size_t)head_dim / 8 + (size_t)head_dim / 4 + 4;
+}
+
+extern "C" tq_status tq_kivi_quantize(int32_t head_dim, const void *k, const void *v, tq_dtype in_dtype,
+                                      int32_t n_slices, int64_t n_tokens, const tq_kivi_store *dst, int64_t dst_token0,
+                                      void *stream) {
+    if (!kivi_dim_ok(head_dim)) return TQ_ERR_UNSUPPORTED;
+    if (in_dtype != TQ_F32 && in_dtype != TQ_BF16 && in_dtype != TQ_F16) return TQ_ERR_INVALID_ARG;
+    if (n_slices <= 0 || n_tokens < 0 || n_tokens % 32 != 0 || dst_token0 < 0 || dst_token0 % 32 != 0)
+        return TQ_ERR_INVALID_ARG;
+    if (!kivi_store_ok(dst) || dst_token0 + n_tokens > dst->capacity) return TQ_ERR_INVALID_ARG;
+    if (n_tokens == 0) return TQ_OK;
+    if (!k || !v || !aligned16(k) || !aligned16(v)) return TQ_ERR_INVALID_ARG;
+    if ((int64_t)n_slices * (n_tokens / 32) > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
+    return hip_status(tq::launch_kivi_quantize(head_dim, in_dtype, k, v, n_slices, n_tokens, *dst, dst_token0,
+                                               (hipStream_t)stream));
+}
+
+extern "C" size_t tq_kivi_decode_workspace_bytes(int32_t head_dim, int32_t batch, int32_t n_q_heads,
+                                                 int32_t n_kv_heads, int64_t max_context) {
+    if (!kivi_dim_ok(head_dim) || batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0 ||
+        max_context < 0)
+        return 0;
+    const int64_t slices = (int64_t)batch * n_kv_heads, G = n_q_heads / n_kv_heads;
+    int64_t n_split, per_split;
+    kivi_split_shape(slices, max_context, n_split, per_split);
+    return kivi_ws_bytes(slices, G, head_dim, n_split);
+}
+
+extern "C" tq_status tq_kivi_decode_attention(int32_t head_dim, const void *q, tq_dtype q_dtype, int32_t batch,
+                                              int32_t n_q_heads, int32_t n_kv_heads, const tq_kivi_store *src,
+                                              int64_t n_packed, float softmax_scale, float *out, void *workspace,
+                                              size_t workspace_bytes, void *stream) {
+    if (!kivi_dim_ok(head_dim)) return TQ_ERR_UNSUPPORTED;
+    if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0 || n_packed < 0)
+        return TQ_ERR_INVALID_ARG;
+    if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_ERR_INVALID_ARG;
+    const int G = n_q_heads / n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return TQ_ERR_UNSUPPORTED;
+    if ((int64_t)batch * n_kv_heads > 65535) return TQ_ERR_UNSUPPORTED;
+    if (!q || !out || !aligned16(q) || !aligned16(out) || !workspace || !aligned16(workspace))
+        return TQ_ERR_INVALID_ARG;
+    if (!kivi_store_ok(src) || n_packed > src->capacity) return TQ_ERR_INVALID_ARG;
+    if (n_packed >= kMaxContext) return TQ_ERR_UNSUPPORTED;
+    const int64_t slices = (int64_t)batch * n_kv_heads;
+    int64_t n_split, per_split;
+    kivi_split_shape(slices, n_packed, n_split, per_split);
+    const size_t need = kivi_ws_bytes(slices, G, head_dim, n_split);
+    if (workspace_bytes < need) return TQ_ERR_WORKSPACE;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    tq::DecodeArgs a{};
+    a.q = q;
+    a.q_dtype = (int)q_dtype;
+    a.batch = batch;
+    a.hq = n_q_heads;
+    a.hkv = n_kv_heads;
+    a.n_packed = n_packed;
+    a.n_split = (int)n_split;
+    a.per_split = per_split;
+    a.scale = softmax_scale;
+    a.out = out;
+    a.partial = reinterpret_cast<float *>(ws);
+    a.partial_ml = reinterpret_cast<float *>(ws + align256(sizeof(float) * (size_t)(slices * n_split * G * head_dim)));
+    return hip_status(tq::launch_kivi_decode(head_dim, G, a, *src, (hipStream_t)stream));
+}

@@ -2008,6 +2008,24 @@ hipError_t launch_decode(int d, int kb, int vb, int G, const DecodeArgs &a, hipS
     return launch_main_dv<256, 4>(G, a, st);
 }
 
+template <int D>
+hipError_t launch_merge_d(int G, const DecodeArgs &a, hipStream_t st) {
+    const dim3 mgrid((unsigned)(a.batch * a.hkv * G));
+    switch (G) {
+        case 1: hipLaunchKernelGGL((k_decode_merge<D, 1>), mgrid, dim3(kThreads), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((k_decode_merge<D, 2>), mgrid, dim3(kThreads), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((k_decode_merge<D, 4>), mgrid, dim3(kThreads), 0, st, a); break;
+        default: hipLaunchKernelGGL((k_decode_merge<D, 8>), mgrid, dim3(kThreads), 0, st, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(int d, int G, const DecodeArgs &a, hipStream_t st) {
+    if (d == 64) return launch_merge_d<64>(G, a, st);
+    if (d == 128) return launch_merge_d<128>(G, a, st);
+    return launch_merge_d<256>(G, a, st);
+}
+
 hipError_t launch_ring_append(int d, tq_dtype dt, const void *kn, const void *vn, uint16_t *rk, uint16_t *rv,
                               int n_slices, int buffer_size, int slot, hipStream_t st) {
     const int64_t total = (int64_t)n_slices * d / 8;

@@ -117,6 +117,12 @@ hipError_t launch_decode(int d, int kb, int vb, int G, const DecodeArgs &a, hipS
 // workspace holds the prepared queries
 bool decode_uses_any(int d, int kb);
 void launch_decode_any_main(int d, int kb, int vb, int G, const DecodeArgs &a, hipStream_t st);
+// the split merge alone (a.n_split > 1), for decode kernels that write the same partials
+hipError_t launch_decode_merge(int d, int G, const DecodeArgs &a, hipStream_t st);
+// KIVI 2-bit variant (tq_kivi.hip)
+hipError_t launch_kivi_quantize(int d, tq_dtype dt, const void *k, const void *v, int64_t n_slices, int64_t n_tokens,
+                                const tq_kivi_store &dst, int64_t dst_token0, hipStream_t st);
+hipError_t launch_kivi_decode(int d, int G, const DecodeArgs &a, const tq_kivi_store &src, hipStream_t st);
 hipError_t launch_ring_append(int d, tq_dtype dt, const void *kn, const void *vn, uint16_t *rk, uint16_t *rv,
                               int n_slices, int buffer_size, int slot, hipStream_t st);
 

@@ -275,6 +275,56 @@ tq_status tq_decode_attention_noalloc(const tq_config *cfg, const tq_tables *tab
                                       const tq_packed *packed, int64_t n_packed, const tq_ring *ring, int32_t n_ring,
                                       float softmax_scale, float *out, void *stream);
 
+/* ------------------------------------------------------------------ KIVI 2-bit variant
+ * The forum page's asymmetric quantiser (zingnex.cn "TurboQuant-vLLM：大模型推理的KV缓存量化
+ * 实战方案", section "KIVI非对称量化"): keys per channel, values per token, each set with a scale
+ * and a zero point, 2 bits; a second workload beside the TurboQuant records, with no rotation,
+ * codebook or QJL bit.  A key channel's scale and zero cover 32 consecutive tokens, a value
+ * token's pair its head_dim entries.  scale = binary16(fp32(fp32(max - min) / 3)), zero =
+ * binary16(min) of the set; code = clamp(round-to-nearest-even(fp32(x - zero) / scale), 0, 3)
+ * (IEEE binary32 division; 0 where the scale is 0); x^ = code scale + zero.  Inputs are taken
+ * to lie within the binary16 range.  head_dim in {64, 128, 256}.
+ *
+ * Store (device arrays per slice, [n_slices][capacity][...], capacity a multiple of 32):
+ *   key_codes  uint32 [capacity][head_dim / 16]: 2-bit codes, channel c at bits 2 (c % 16)
+ *              of word c / 16;
+ *   key_scale, key_zero  binary16 [capacity / 32][head_dim]: per 32-token group and channel;
+ *   val_codes  uint32 [capacity][head_dim / 16] as key_codes;
+ *   val_params binary16 [capacity][2]: (scale, zero) per token.
+ * Arrays 16-byte aligned (TQ_ERR_INVALID_ARG otherwise); owned by the caller. */
+typedef struct tq_kivi_store {
+    uint32_t *key_codes;
+    uint16_t *key_scale;
+    uint16_t *key_zero;
+    uint32_t *val_codes;
+    uint16_t *val_params;
+    int64_t capacity;
+} tq_kivi_store;
+
+/* Store bytes per token: head_dim / 4 (key codes) + head_dim / 8 (key scale and zero, a
+ * 32-token group's share) + head_dim / 4 (value codes) + 4 (value scale and zero); 84 at
+ * head_dim 128.  0 for an unsupported head_dim. */
+size_t tq_kivi_bytes_per_token(int32_t head_dim);
+
+/* Quantise k and v [n_slices][n_tokens][head_dim] (in_dtype) into records dst_token0 ..
+ * dst_token0 + n_tokens - 1 of every slice.  n_tokens and dst_token0 multiples of 32 (whole
+ * key groups; TQ_ERR_INVALID_ARG otherwise), dst_token0 + n_tokens <= capacity. */
+tq_status tq_kivi_quantize(int32_t head_dim, const void *k, const void *v, tq_dtype in_dtype, int32_t n_slices,
+                           int64_t n_tokens, const tq_kivi_store *dst, int64_t dst_token0, void *stream);
+
+/* Decode attention over the first n_packed records of every slice of a KIVI store: out[b][h]
+ * = softmax(softmax_scale q[b][h] . k^) v^ over the dequantised keys and values of kv head
+ * h / (n_q_heads / n_kv_heads); q [batch][n_q_heads][head_dim] (q_dtype), out fp32, slices
+ * b * n_kv_heads + kv head.  n_q_heads / n_kv_heads in {1, 2, 4, 8}; n_packed <= capacity; a
+ * zero context writes zeros.  The workspace (tq_kivi_decode_workspace_bytes for the largest
+ * context the caller will pass) holds the splits' partial results; it needs no clearing. */
+size_t tq_kivi_decode_workspace_bytes(int32_t head_dim, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                      int64_t max_context);
+tq_status tq_kivi_decode_attention(int32_t head_dim, const void *q, tq_dtype q_dtype, int32_t batch,
+                                   int32_t n_q_heads, int32_t n_kv_heads, const tq_kivi_store *src,
+                                   int64_t n_packed, float softmax_scale, float *out, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
 const char *tq_status_string(tq_status s);
 
 /* ------------------------------------------------------------------ test hooks

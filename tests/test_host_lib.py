@@ -383,3 +383,46 @@ def test_prefill_argument_errors():
     assert big == L.tq_prefill_workspace_bytes(ctypes.byref(cfg), 1, 32767, 8, 2, 500)
     assert pf(batch=1, q_tokens=40000, ws_bytes=16) == B.TQ_ERR_WORKSPACE
     assert pf(batch=1, q_tokens=40000, n_packed=1001) == B.TQ_ERR_INVALID_ARG
+
+
+def test_kivi_bytes_per_token():
+    # key codes d/4 + key scale and zero d/8 (a 32-token group's share) + value codes d/4 + 4
+    for d, want in ((64, 16 + 8 + 16 + 4), (128, 32 + 16 + 32 + 4), (256, 64 + 32 + 64 + 4)):
+        assert tq.tq_kivi_bytes_per_token(d) == want
+    for d in (0, 32, 96, 512):
+        assert tq.tq_kivi_bytes_per_token(d) == 0
+
+
+def test_kivi_argument_errors():
+    """Every case fails before a launch (the store and data pointers are never dereferenced)."""
+    L = B.lib()
+    S = B.tq_kivi_store(FAKE, FAKE, FAKE, FAKE, FAKE, 256)
+    q = lambda d=128, k=FAKE, dt=B.TQ_BF16, ns=2, nt=64, st=S, t0=0: L.tq_kivi_quantize(
+        d, k, FAKE, dt, ns, nt, ctypes.byref(st) if st is not None else None, t0, None)
+    assert q(d=96) == B.TQ_ERR_UNSUPPORTED
+    assert q(nt=40) == B.TQ_ERR_INVALID_ARG      # not whole 32-token groups
+    assert q(t0=16) == B.TQ_ERR_INVALID_ARG
+    assert q(nt=256, t0=32) == B.TQ_ERR_INVALID_ARG  # past the capacity
+    assert q(ns=0) == B.TQ_ERR_INVALID_ARG
+    assert q(dt=9) == B.TQ_ERR_INVALID_ARG
+    assert q(k=FAKE + 4) == B.TQ_ERR_INVALID_ARG
+    assert q(k=None) == B.TQ_ERR_INVALID_ARG
+    assert q(st=None) == B.TQ_ERR_INVALID_ARG
+    assert q(st=B.tq_kivi_store(FAKE, FAKE, FAKE, FAKE, FAKE, 100)) == B.TQ_ERR_INVALID_ARG  # capacity % 32
+    assert q(st=B.tq_kivi_store(FAKE, FAKE + 2, FAKE, FAKE, FAKE, 256)) == B.TQ_ERR_INVALID_ARG
+    assert q(nt=0) == B.TQ_OK  # nothing to do: returns before any launch
+    need = tq.tq_kivi_decode_workspace_bytes(128, 2, 8, 2, 256)
+    assert need > 0
+    assert tq.tq_kivi_decode_workspace_bytes(128, 2, 6, 4, 256) == 0
+
+    def dec(d=128, bsz=2, hq=8, hkv=2, n=256, ws=need, qp=FAKE, st=S):
+        return L.tq_kivi_decode_attention(d, qp, B.TQ_BF16, bsz, hq, hkv, ctypes.byref(st), n, 0.1, FAKE, FAKE, ws,
+                                          None)
+    assert dec(d=32) == B.TQ_ERR_UNSUPPORTED
+    assert dec(hq=6, hkv=4) == B.TQ_ERR_INVALID_ARG
+    assert dec(hq=24, hkv=2) == B.TQ_ERR_UNSUPPORTED  # 12 query heads per kv head
+    assert dec(n=257) == B.TQ_ERR_INVALID_ARG          # past the capacity
+    assert dec(n=-1) == B.TQ_ERR_INVALID_ARG
+    assert dec(qp=FAKE + 8) == B.TQ_ERR_INVALID_ARG
+    assert dec(ws=need - 1) == B.TQ_ERR_WORKSPACE
+    assert dec(bsz=40000, hkv=2, hq=2) == B.TQ_ERR_UNSUPPORTED  # more than 65535 slices
