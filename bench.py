@@ -64,6 +64,9 @@ def parse():
     p.add_argument("--prefill", type=int, default=0, metavar="QUERY_TOKENS",
                    help="time only prefill attention over the packed cache (layer 0): the last QUERY_TOKENS "
                         "tokens of every sequence's history as causal queries")
+    p.add_argument("--kivi", action="store_true",
+                   help="time the KIVI 2-bit variant instead (quantize every layer's history into a KIVI "
+                        "store, decode attention of every layer over it): its own JSON line")
     p.add_argument("--cpu-sample-tokens", type=int, default=32768)
     p.add_argument("--probe-copy-mib", type=int, default=0,
                    help="only time a plain device-to-device copy of this many MiB (achievable HBM "
@@ -128,6 +131,9 @@ def main():
     if args.key_bits and args.key_bits != w.key_bits:
         w = dataclasses.replace(w, key_bits=args.key_bits, name=f"{w.name}_kb{args.key_bits}")
     dev = torch.device("cuda:0")
+    if args.kivi:
+        kivi(args, w, dev)
+        return
     d, L, B, hq, hkv = w.d, w.layers, w.batch, w.hq, w.hkv
     n_sl_layer = B * hkv
     n_sl = L * n_sl_layer
@@ -432,6 +438,79 @@ def prefill(args, w, cfg, tables, copies, n_copies, scale, rec, in_bytes):
                      "achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": alg, "streamed_bytes_per_call": streamed},
+    }), flush=True)
+
+
+def kivi(args, w, dev):
+    """The KIVI 2-bit variant on the workload's shapes: one quantize call over every layer's
+    history (whole 32-token groups), then every layer's decode attention over its store; HBM-cold
+    copies as in the main leg; HIP events around K back-to-back repetitions of each leg."""
+    import torch
+    import tq_workloads as W
+    import compressed_decode_attention_02_amd as tq
+    d, L, B, hq, hkv = w.d, w.layers, w.batch, w.hq, w.hkv
+    Tp = w.n_packed // 32 * 32
+    n_sl_layer = B * hkv
+    n_sl = L * n_sl_layer
+    rec = tq.tq_kivi_bytes_per_token(d)
+    in_bytes = 2 if w.in_dtype == "bf16" else 4
+    mall2 = 2 * 256 * 10**6
+    n_cp = max(1, math.ceil(mall2 / (n_sl * Tp * rec)))
+    ks, vs = [], []
+    for layer in range(L):
+        k, v = W.device_kv(w, layer, w.n_packed, dev)
+        ks.append(k.reshape(n_sl_layer, w.n_packed, d)[:, :Tp].contiguous())
+        vs.append(v.reshape(n_sl_layer, w.n_packed, d)[:, :Tp].contiguous())
+    K = torch.cat(ks).contiguous() if L > 1 else ks[0]
+    V = torch.cat(vs).contiguous() if L > 1 else vs[0]
+    del ks, vs
+    stores = [tq.KiviStore(d, n_sl, Tp, device=dev) for _ in range(n_cp)]
+    qs = [W.device_queries(w, layer, dev) for layer in range(L)]
+    out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+    ws = tq.new_kivi_workspace(d, B, hq, hkv, Tp, device=dev)
+    scale = 1.0 / math.sqrt(d)
+
+    def quant(i):
+        tq.tq_kivi_quantize(d, K, V, n_sl, Tp, stores[i % n_cp].struct(), 0)
+
+    def dec(i):
+        st = stores[i % n_cp]
+        for layer in range(L):
+            tq.tq_kivi_decode_attention(d, qs[layer], B, hq, hkv, st.struct(layer * n_sl_layer), Tp, scale, out, ws)
+
+    for i in range(max(args.warmup, n_cp)):
+        quant(i)
+        dec(i)
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+    ms_q, ms_d = timed(quant), timed(dec)
+    q_bytes = n_sl * Tp * (2 * d * in_bytes + rec)
+    d_bytes = n_sl * Tp * rec + L * B * hq * d * (in_bytes + 4)
+    dg = d_bytes / (ms_d * 1e-3) / 1e9
+    qg = q_bytes / (ms_q * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "KIVI 2-bit decode attention KV-tokens/s + HBM GB/s; quantize tokens/s",
+        "value": round(B * L * Tp / (ms_d * 1e-3), 1), "unit": "KV-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_d + ms_q, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.in_dtype, "data": "synthetic (seeded device draws of the workload's laws)",
+        "config": {"workload": w.name + "_kivi2", "layers": L, "batch": B, "q_heads": hq, "kv_heads": hkv,
+                   "head_dim": d, "packed_tokens": Tp, "bits": 2, "key_group": 32, "store_copies": n_cp},
+        "decode_ms_per_step": round(ms_d, 4), "quantize_ms": round(ms_q, 4),
+        "quantize_tokens_per_s": round(B * L * Tp / (ms_q * 1e-3), 1), "record_bytes": rec,
+        "roofline_decode": {"kernel": "k_kivi_decode+k_decode_merge", "bound": "hbm", "achieved": round(dg, 1),
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dg / HBM_PEAK_GBPS, 4),
+                            "traffic": None, "algorithmic_bytes_per_launch": d_bytes // L},
+        "roofline_quantize": {"kernel": "k_kivi_quant", "bound": "hbm", "achieved": round(qg, 1),
+                              "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(qg / HBM_PEAK_GBPS, 4),
+                              "traffic": None, "algorithmic_bytes_per_launch": q_bytes},
     }), flush=True)
 
 

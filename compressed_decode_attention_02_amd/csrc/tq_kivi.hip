@@ -38,6 +38,10 @@ __device__ __forceinline__ void kwave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+template <typename Tag> struct TagBytes { typedef float type; };
+template <> struct TagBytes<bf16_tag> { typedef uint16_t type; };
+template <> struct TagBytes<f16_tag> { typedef uint16_t type; };
+
 template <typename Tag>
 __device__ __forceinline__ float in_elem(const void *p, int64_t off) {
     return load1(p, off, Tag{});
@@ -65,22 +69,29 @@ __global__ __launch_bounds__(kKThreads) void k_kivi_quant(const void *k, const v
     constexpr int VPT = kKThreads / kGroup;  // threads per value token (8)
     constexpr int VE = D / VPT;             // value entries per thread
     static_assert(VE == 8 || VE == 16 || VE == 32, "value entries per thread");
+    constexpr int IB = sizeof(typename TagBytes<Tag>::type);  // input bytes per element
     __shared__ float red[2][kKThreads];
     __shared__ __align__(16) uint8_t kc[kGroup][D];
+    __shared__ __align__(16) uint4 kt[kGroup * D * IB / 16];  // the group's keys (16-byte loads)
     const int tid = threadIdx.x;
     const int64_t sl = blockIdx.x / n_groups, grp = blockIdx.x % n_groups;
     const int64_t t0 = grp * kGroup;                        // first token of the group (input)
     const int64_t r0 = dst_token0 + t0;                     // its record index in the slice
     const int64_t in0 = (sl * n_tokens + t0) * D;           // element offset of the group's first token
 
-    // ---- keys: channel c = tid % D, tokens h TPT .. h TPT + TPT - 1 (h = tid / D)
+    // ---- keys: the group's tile into LDS with 16-byte loads, then channel c = tid % D,
+    //      tokens h TPT .. h TPT + TPT - 1 (h = tid / D)
     {
+        const uint4 *ksrc = reinterpret_cast<const uint4 *>(static_cast<const unsigned char *>(k) + in0 * IB);
+#pragma unroll
+        for (int i = tid; i < kGroup * D * IB / 16; i += kKThreads) kt[i] = ksrc[i];
+        __syncthreads();
         const int c = tid % D, h = tid / D;
         float x[TPT];
         float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
-            x[i] = in_elem<Tag>(k, in0 + (int64_t)(h * TPT + i) * D + c);
+            x[i] = in_elem<Tag>(kt, (int64_t)(h * TPT + i) * D + c);
             mn = fminf(mn, x[i]);
             mx = fmaxf(mx, x[i]);
         }
