@@ -548,7 +548,9 @@ void k_quant_kv(QuantArgs a) {
 #pragma unroll
         for (int o = R; o < 64; o <<= 1) gg += __shfl_xor(gg, o);
 
-        // ---- the next tile's raw keys are loaded during the projection and the stores
+        // (a tile's inputs are loaded at the top of its iteration, not during the previous
+        // tile: the kernel is bound by instruction issue, and a copy of the next tile's values
+        // into LDS one tile ahead was measured slower)
 
         // ---- QJL on the matrix cores: D[j][token] = -sum_c S[j][c] r'[c]; lane (n, g)
         //      receives the projections j = slot_coord(f, g) of its own coordinates
