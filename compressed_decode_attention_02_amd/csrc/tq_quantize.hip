@@ -305,12 +305,14 @@ void k_quant_kv(QuantArgs a) {
     float BP[NPOS > 1 ? NPOS - 1 : 1];
 #pragma unroll
     for (int k = 0; k + 1 < NPOS; ++k) BP[k] = a.boundaries[NPOS + k];
-    // scaled positive centroids 2^8 c[L/2+k], tagged with their index L/2 + k in the KB low
-    // mantissa bits (the stored centroids are binary16 values, so those bits are zero)
+    // tagged positive centroids: the binary16 value 2^8 c[L/2+k] in the upper half-word (exact:
+    // the stored centroids are binary16 values well inside its range) and the index L/2 + k in
+    // the low bits; negating the word as fp32 negates the binary16 value
     float M[NPOS];
 #pragma unroll
     for (int k = 0; k < NPOS; ++k) {
-        M[k] = __uint_as_float((__float_as_uint(256.f * a.centroids[NPOS + k]) & ~kTag) | (uint32_t)(NPOS + k));
+        const _Float16 c16 = (_Float16)(256.f * a.centroids[NPOS + k]);
+        M[k] = __uint_as_float(((uint32_t)__builtin_bit_cast(uint16_t, c16) << 16) | (uint32_t)(NPOS + k));
         asm volatile("" : "+v"(M[k]));
     }
 
@@ -509,8 +511,9 @@ void k_quant_kv(QuantArgs a) {
 #pragma unroll
                 for (int k = 0; k + 1 < NPOS; ++k) mt = ay > T[k] ? M[k + 1] : mt;
                 sb[o] = __float_as_uint(yv > 0.f ? mt : -mt);
-                // -r' = c[idx] - u'
-                nr[o] = fmaf(-yv, inv256, __uint_as_float(sb[o] & ~kTag));
+                // -r' = c[idx] - u', one fused product-add with the binary16 centroid as addend
+                asm("v_fma_mix_f32 %0, -%1, %2, %3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+                    : "=v"(nr[o]) : "v"(yv), "v"(inv256), "v"(sb[o]));
                 ggp[o] = fmaf(nr[o], nr[o], ggp[o]);
             }
             if constexpr (KB == 3) {
