@@ -184,13 +184,20 @@ struct KivDecodeSmem {
     float a[4][2][G][D];          // per wave: scaled query per (group of the chunk, head, channel)
     float bq[4][2][G];            // per wave: group constants
     uint32_t vcw[4][kChunk][D / 16];  // per wave: the chunk's value code words
-    float pv[4][G][kChunk][2];    // per wave: (p scale, p zero) per head and token
+    float pv[4][G][kChunk];       // per wave: p scale per head and token
     float wm[4][G], wl[4][G];
     float wo[4][G][D];
 };
 
+// waves per SIMD the decode is compiled for: four (<= 128 VGPRs) where a lane's heads and
+// channels allow it, so that the chunks' loads of more waves overlap
 template <int D, int G>
-__global__ __launch_bounds__(kKThreads) void k_kivi_decode(DecodeArgs a, tq_kivi_store src) {
+constexpr int kKivDecWaves = D * G <= 512 ? 4 : 2;
+
+template <int D, int G>
+__global__ __launch_bounds__(kKThreads)
+__attribute__((amdgpu_waves_per_eu(kKivDecWaves<D, G>, kKivDecWaves<D, G>)))
+void k_kivi_decode(DecodeArgs a, tq_kivi_store src) {
     constexpr int W = D / 16;
     constexpr int CPL = D / 64;  // value channels per lane
     __shared__ KivDecodeSmem<D, G> sm;
@@ -290,6 +297,7 @@ __global__ __launch_bounds__(kKThreads) void k_kivi_decode(DecodeArgs a, tq_kivi
             }
         }
         // ---- online softmax per head (reference max raised when a logit exceeds it)
+        float zsum[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const float x = live ? s[g] : -INFINITY;
@@ -306,24 +314,23 @@ __global__ __launch_bounds__(kKThreads) void k_kivi_decode(DecodeArgs a, tq_kivi
             l[g] = l[g] * corr + ps;
 #pragma unroll
             for (int e = 0; e < CPL; ++e) oacc[g][e] *= corr;
-            sm.pv[wave][g][lane][0] = p * vs;
-            sm.pv[wave][g][lane][1] = p * vz;
+            sm.pv[wave][g][lane] = p * vs;
+            // the zero points' share, sum over the chunk of p zero: the same for every channel
+            float pz = p * vz;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) pz += __shfl_xor(pz, off);
+            zsum[g] = pz;
         }
         kwave_sync();
         // ---- values: lane = channels lane + 64 e; sum over the chunk's tokens
-        float zsum[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) zsum[g] = 0.f;
         for (int tt = 0; tt < kChunk; ++tt) {
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
                 const int c = lane + 64 * e;
                 const float code = (float)((sm.vcw[wave][tt][c >> 4] >> (2 * (c & 15))) & 3u);
 #pragma unroll
-                for (int g = 0; g < G; ++g) oacc[g][e] = fmaf(sm.pv[wave][g][tt][0], code, oacc[g][e]);
+                for (int g = 0; g < G; ++g) oacc[g][e] = fmaf(sm.pv[wave][g][tt], code, oacc[g][e]);
             }
-#pragma unroll
-            for (int g = 0; g < G; ++g) zsum[g] += sm.pv[wave][g][tt][1];
         }
 #pragma unroll
         for (int g = 0; g < G; ++g)
