@@ -180,10 +180,12 @@ __global__ __launch_bounds__(kKThreads) void k_kivi_quant(const void *k, const v
 constexpr int kChunk = 64;  // tokens per wave iteration (one per lane; two key groups)
 
 template <int D, int G>
-struct KivDecodeSmem {
+struct alignas(16) KivDecodeSmem {
     float a[4][2][G][D];          // per wave: scaled query per (group of the chunk, head, channel)
     float bq[4][2][G];            // per wave: group constants
-    uint32_t vcw[4][kChunk][D / 16];  // per wave: the chunk's value code words
+    // per wave: the chunk's value code words, word-major (rows padded by 4 words: the four
+    // rows one read reaches fall in different banks)
+    uint32_t vcw[4][D / 16][kChunk + 4];
     float pv[4][G][kChunk];       // per wave: p scale per head and token
     float wm[4][G], wl[4][G];
     float wo[4][G][D];
@@ -269,8 +271,13 @@ void k_kivi_decode(DecodeArgs a, tq_kivi_store src) {
             kw[w] = u.x; kw[w + 1] = u.y; kw[w + 2] = u.z; kw[w + 3] = u.w;
         }
 #pragma unroll
-        for (int w = 0; w < W; w += 4)
-            *reinterpret_cast<uint4 *>(&sm.vcw[wave][lane][w]) = *reinterpret_cast<const uint4 *>(src.val_codes + rec * W + w);
+        for (int w = 0; w < W; w += 4) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(src.val_codes + rec * W + w);
+            sm.vcw[wave][w][lane] = u.x;
+            sm.vcw[wave][w + 1][lane] = u.y;
+            sm.vcw[wave][w + 2][lane] = u.z;
+            sm.vcw[wave][w + 3][lane] = u.w;
+        }
         const uint32_t vp = *reinterpret_cast<const uint32_t *>(src.val_params + rec * 2);
         const float vs = f16_lo(vp), vz = f16_hi(vp);
         kwave_sync();  // a, b and the value code words visible to the wave
@@ -323,13 +330,28 @@ void k_kivi_decode(DecodeArgs a, tq_kivi_store src) {
         }
         kwave_sync();
         // ---- values: lane = channels lane + 64 e; sum over the chunk's tokens
-        for (int tt = 0; tt < kChunk; ++tt) {
+        // (four tokens per pass: their code words of the lane's channels and their p scale of
+        // every head as 16-byte reads)
+        for (int t4 = 0; t4 < kChunk; t4 += 4) {
+            float4 pw[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) pw[g] = *reinterpret_cast<const float4 *>(&sm.pv[wave][g][t4]);
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
                 const int c = lane + 64 * e;
-                const float code = (float)((sm.vcw[wave][tt][c >> 4] >> (2 * (c & 15))) & 3u);
+                const uint4 cw = *reinterpret_cast<const uint4 *>(&sm.vcw[wave][c >> 4][t4]);
+                const uint32_t sh = 2 * (c & 15);
+                const float c0 = (float)((cw.x >> sh) & 3u), c1 = (float)((cw.y >> sh) & 3u);
+                const float c2 = (float)((cw.z >> sh) & 3u), c3 = (float)((cw.w >> sh) & 3u);
 #pragma unroll
-                for (int g = 0; g < G; ++g) oacc[g][e] = fmaf(sm.pv[wave][g][tt], code, oacc[g][e]);
+                for (int g = 0; g < G; ++g) {
+                    float o = oacc[g][e];
+                    o = fmaf(pw[g].x, c0, o);
+                    o = fmaf(pw[g].y, c1, o);
+                    o = fmaf(pw[g].z, c2, o);
+                    o = fmaf(pw[g].w, c3, o);
+                    oacc[g][e] = o;
+                }
             }
         }
 #pragma unroll
