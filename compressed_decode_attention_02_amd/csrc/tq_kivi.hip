@@ -192,9 +192,10 @@ struct alignas(16) KivDecodeSmem {
 };
 
 // waves per SIMD the decode is compiled for: four (<= 128 VGPRs) where a lane's heads and
-// channels allow it, so that the chunks' loads of more waves overlap
+// channels allow it, so that the chunks' loads of more waves overlap; fewer as they grow (d = 256
+// with eight heads: one, as its LDS allows one workgroup per CU)
 template <int D, int G>
-constexpr int kKivDecWaves = D * G <= 512 ? 4 : 2;
+constexpr int kKivDecWaves = D * G <= 256 || (D * G <= 512 && D <= 128) ? 4 : (D * G <= 512 ? 3 : (D * G < 2048 ? 2 : 1));
 
 template <int D, int G>
 __global__ __launch_bounds__(kKThreads)
