@@ -45,16 +45,19 @@ struct AnyShape {
 };
 
 template <int D, int KB, int VB, int G>
-struct AnySmem {
+struct alignas(16) AnySmem {
     using S = AnyShape<D, KB, VB, G>;
     float qr[G][D];  // scale log2(e) * q (the ring's exact scores)
     float ctab[16];  // stored centroids
     float wsum[G];   // sum_j w[g][j]
-    float pb[kAnyWaves][kChunk][G];  // p of the chunk's tokens
-    union {
+    float pb[kAnyWaves][kChunk][G];  // p of the chunk's tokens (ring chunks)
+    union alignas(16) {
         struct {
-            uint32_t vrec[kAnyWaves][kChunk][S::VW];  // the chunk's value records
-            float vsc[kAnyWaves][kChunk][S::NG];      // and their scales
+            // the chunk's value records, word-major (rows padded by 4 words: the rows one
+            // 16-byte read reaches fall in different banks), and p times the token's group
+            // scale per head and group
+            uint32_t vrec[kAnyWaves][S::VW][kChunk + 4];
+            float psc[kAnyWaves][G][S::NG][kChunk];
         } c;
         float wo[kAnyWaves][G][D];  // wave combine
     };
@@ -84,7 +87,9 @@ __device__ __forceinline__ float load_q_elem(const DecodeArgs &a, int64_t off) {
 }
 
 template <int D, int KB, int VB, int G>
-__global__ __launch_bounds__(kAnyThreads) void k_decode_any(DecodeArgs a) {
+__global__ __launch_bounds__(kAnyThreads)
+__attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2, G <= 4 ? 4 : 2)))
+void k_decode_any(DecodeArgs a) {
     using S = AnyShape<D, KB, VB, G>;
     __shared__ AnySmem<D, KB, VB, G> sm;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -147,6 +152,7 @@ __global__ __launch_bounds__(kAnyThreads) void k_decode_any(DecodeArgs a) {
         float s[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) s[h] = 0.f;
+        float vsc[S::NG] = {};  // packed chunks: the lane's token's value group scales
         if (!ring) {
             // ---- scores of a packed token (one per lane)
             const int64_t rec = record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, a.err, sbk, tt);
@@ -176,12 +182,12 @@ __global__ __launch_bounds__(kAnyThreads) void k_decode_any(DecodeArgs a) {
 #pragma unroll
             for (int h = 0; h < G; ++h)
                 s[h] = kn.x * fmaf(ss * kn.y, fmaf(2.f, sgn[h], -sm.wsum[h]), cs * mse[h]);
-            // the token's value record and scales for the value phase
+            // the token's value record for the value phase; its group scales for the p products
             const uint32_t *vp = a.vw + rec * S::VW;
 #pragma unroll
-            for (int i = 0; i < S::VW; ++i) sm.c.vrec[wave][lane][i] = vp[i];
+            for (int i = 0; i < S::VW; ++i) sm.c.vrec[wave][i][lane] = vp[i];
 #pragma unroll
-            for (int i = 0; i < S::NG; ++i) sm.c.vsc[wave][lane][i] = f16_lo(a.vs[rec * S::NG + i]);
+            for (int i = 0; i < S::NG; ++i) vsc[i] = f16_lo(a.vs[rec * S::NG + i]);
         } else {
             // ---- scores of a ring token: q . k over its exact fp16 key
             const uint16_t *kr = a.rk + ((int64_t)bk * a.buffer_size + tt) * D;
@@ -212,29 +218,62 @@ __global__ __launch_bounds__(kAnyThreads) void k_decode_any(DecodeArgs a) {
             Lw[h] = fmaf(Lw[h], alpha, ps);
 #pragma unroll
             for (int e = 0; e < S::EPL; ++e) o[h][e] *= alpha;
-            sm.pb[wave][lane][h] = p;
+            if (ring) {
+                sm.pb[wave][lane][h] = p;
+            } else {
+                // v = (code - HALF + 1/2) s: sum_t p_t s_t code_t over the chunk below, and the
+                // offset -(HALF - 1/2) sum_t p_t s_t of each group, the same for its coordinates
+#pragma unroll
+                for (int i = 0; i < S::NG; ++i) {
+                    const float q = p * vsc[i];
+                    sm.c.psc[wave][h][i][lane] = q;
+                    float r = q;
+#pragma unroll
+                    for (int off = 32; off > 0; off >>= 1) r += __shfl_xor(r, off);
+#pragma unroll
+                    for (int e = 0; e < S::EPL; ++e)
+                        if ((lane + 64 * e) / 32 == i) o[h][e] = fmaf(-((float)S::HALF - 0.5f), r, o[h][e]);
+                }
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         // ---- values: lane holds coordinates lane + 64 e
-        for (int t = 0; t < cn; ++t) {
-            float p[G];
+        if (!ring) {
+            // four tokens per pass (tokens past cn have p = 0): their code words of the lane's
+            // coordinates and their p s of every head as 16-byte reads
+            for (int t4 = 0; t4 < cn; t4 += 4) {
 #pragma unroll
-            for (int h = 0; h < G; ++h) p[h] = sm.pb[wave][t][h];
+                for (int e = 0; e < S::EPL; ++e) {
+                    const int j = lane + 64 * e;
+                    const uint4 wd = *reinterpret_cast<const uint4 *>(&sm.c.vrec[wave][j / (32 / VB)][t4]);
+                    const uint32_t sh = VB * (j % (32 / VB)), msk = (1u << VB) - 1u;
+                    const float c0f = (float)((wd.x >> sh) & msk), c1f = (float)((wd.y >> sh) & msk);
+                    const float c2f = (float)((wd.z >> sh) & msk), c3f = (float)((wd.w >> sh) & msk);
 #pragma unroll
-            for (int e = 0; e < S::EPL; ++e) {
-                const int j = lane + 64 * e;
-                float v;
-                if (!ring) {
-                    const uint32_t wd = sm.c.vrec[wave][t][j / (32 / VB)];
-                    const uint32_t code = (wd >> (VB * (j % (32 / VB)))) & ((1u << VB) - 1u);
-                    v = ((float)code - (float)S::HALF + 0.5f) * sm.c.vsc[wave][t][j / 32];
-                } else {
-                    v = f16_lo(a.rv[((int64_t)bk * a.buffer_size + c0 + t) * D + j]);
+                    for (int h = 0; h < G; ++h) {
+                        const float4 q = *reinterpret_cast<const float4 *>(&sm.c.psc[wave][h][j / 32][t4]);
+                        float x = o[h][e];
+                        x = fmaf(q.x, c0f, x);
+                        x = fmaf(q.y, c1f, x);
+                        x = fmaf(q.z, c2f, x);
+                        x = fmaf(q.w, c3f, x);
+                        o[h][e] = x;
+                    }
                 }
+            }
+        } else {
+            for (int t = 0; t < cn; ++t) {
+                float p[G];
 #pragma unroll
-                for (int h = 0; h < G; ++h) o[h][e] = fmaf(p[h], v, o[h][e]);
+                for (int h = 0; h < G; ++h) p[h] = sm.pb[wave][t][h];
+#pragma unroll
+                for (int e = 0; e < S::EPL; ++e) {
+                    const float v = f16_lo(a.rv[((int64_t)bk * a.buffer_size + c0 + t) * D + lane + 64 * e]);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) o[h][e] = fmaf(p[h], v, o[h][e]);
+                }
             }
         }
         // the chunk's LDS rows are rewritten by the wave's next chunk only after every lane
