@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
-SOURCES = ["tq_host.cpp", "tq_quantize.hip", "tq_decode.hip", "tq_decode_any.hip", "tq_hooks.hip", "tq_kivi.hip", "tq_api.hip"]
+SOURCES = ["tq_host.cpp", "tq_quantize.hip", "tq_decode.hip", "tq_decode_any.hip", "tq_hooks.hip", "tq_kivi.hip", "tq_prefill.hip", "tq_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -316,16 +316,79 @@ extern "C" tq_status tq_decode_attention_ragged(const tq_config *cfg, const tq_t
 
 // ------------------------------------------------------------------ prefill (full_tq)
 namespace {
-// query tokens per decode launch of a prefill call: batch * kv heads of a launch stays within
-// the grid's 65535 rows
+// query tokens per launch of a prefill call: batch * kv heads of a decode launch stays within
+// the grid's 65535 rows, and it bounds the workspace of either path
 int64_t prefill_launch_tokens(int32_t n_kv_heads) { return std::max<int64_t>(1, 65535 / n_kv_heads); }
+
+// the tiled kernel's workspace: q' and w of every query row of a launch of `tokens` tokens
+size_t prefill_prep_bytes(int d, int64_t tokens, int64_t n_q_heads) {
+    return align256(sizeof(float) * (size_t)(tokens * n_q_heads) * 2 * d);
+}
+
+// a launch of T query tokens per sequence goes to the tiled kernel when its rows (T G per kv
+// head) fill at least half a tile; shorter ones (a few query tokens over a long history) to the
+// decode kernels, whose splits spread one row's tokens over many workgroups
+bool prefill_tiled(int d, int64_t T, int64_t G) { return T * G * 2 >= tq::prefill_tile_rows(d); }
+
+// prefill by query tiles: n_seq sequences of T query tokens at positions q_pos0 .., store
+// slices slice0 ..; every argument checked before anything is launched
+tq_status prefill_tiled_impl(const tq_config *cfg, const tq_tables *tables, const void *q, tq_dtype q_dtype,
+                             int64_t n_seq, int32_t T, int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *packed,
+                             int64_t n_packed, int64_t q_pos0, int32_t causal, float softmax_scale, float *out,
+                             void *workspace, size_t workspace_bytes, void *stream, bool check_only, int64_t slice0) {
+    const int G = n_q_heads / n_kv_heads;
+    if (n_q_heads % n_kv_heads != 0 || (G != 1 && G != 2 && G != 4 && G != 8)) return TQ_ERR_UNSUPPORTED;
+    if (!tables_ok(tables) || !q || !out || !aligned16(q) || !aligned16(out) || !workspace || !aligned16(workspace))
+        return TQ_ERR_INVALID_ARG;
+    if (n_packed > 0 && (!packed_ok(packed) || n_packed > packed->capacity)) return TQ_ERR_INVALID_ARG;
+    if (n_packed >= kMaxContext) return TQ_ERR_UNSUPPORTED;  // 32-bit token indices in the kernels
+    if (workspace_bytes < prefill_prep_bytes(cfg->head_dim, n_seq * T, n_q_heads)) return TQ_ERR_WORKSPACE;
+    if (check_only) return TQ_OK;
+    const hipStream_t st = (hipStream_t)stream;
+    tq::PrefillPrepArgs pp{};
+    pp.q = q;
+    pp.q_dtype = (int)q_dtype;
+    pp.sign_bits = tables->sign_bits;
+    pp.S = tables->qjl_S;
+    pp.n_rows = n_seq * T * n_q_heads;
+    pp.hq = n_q_heads;
+    pp.hkv = n_kv_heads;
+    pp.prep = static_cast<float *>(workspace);
+    hipError_t e = tq::launch_prefill_prep(cfg->head_dim, pp, st);
+    if (e != hipSuccess) return TQ_ERR_HIP;
+    tq::PrefillArgs a{};
+    a.prep = pp.prep;
+    a.centroids = tables->centroids;
+    if (n_packed > 0) {
+        a.kw = packed->key_words;
+        a.kn = packed->key_norms;
+        a.vw = packed->val_words;
+        a.vs = packed->val_scales;
+        a.cap = packed->capacity;
+        set_pages(a, packed);
+    }
+    a.n_packed = n_packed;
+    a.q_pos0 = q_pos0;
+    a.causal = causal;
+    a.T = T;
+    a.hq = n_q_heads;
+    a.hkv = n_kv_heads;
+    a.slice0 = slice0;
+    const int tr = tq::prefill_tile_rows(cfg->head_dim);
+    a.tiles = (int)(((int64_t)T * G + tr - 1) / tr);
+    a.scale = softmax_scale;
+    a.out = out;
+    return hip_status(tq::launch_prefill(cfg->head_dim, cfg->key_bits, cfg->value_bits, n_seq, a, st));
+}
 }  // namespace
 
 extern "C" size_t tq_prefill_workspace_bytes(const tq_config *cfg, int32_t batch, int32_t q_tokens,
                                              int32_t n_q_heads, int32_t n_kv_heads, int64_t n_packed) {
-    if (!cfg || batch <= 0 || q_tokens <= 0 || n_kv_heads <= 0) return 0;
+    if (!cfg || tq::check_config(*cfg) != TQ_OK || batch <= 0 || q_tokens <= 0 || n_q_heads <= 0 || n_kv_heads <= 0)
+        return 0;
     const int64_t vb = std::min<int64_t>((int64_t)batch * q_tokens, prefill_launch_tokens(n_kv_heads));
-    return tq_decode_workspace_bytes(cfg, (int32_t)vb, n_q_heads, n_kv_heads, n_packed);
+    return std::max(tq_decode_workspace_bytes(cfg, (int32_t)vb, n_q_heads, n_kv_heads, n_packed),
+                    prefill_prep_bytes(cfg->head_dim, vb, n_q_heads));
 }
 
 extern "C" tq_status tq_prefill_attention(const tq_config *cfg, const tq_tables *tables, const void *q,
@@ -351,10 +414,16 @@ extern "C" tq_status tq_prefill_attention(const tq_config *cfg, const tq_tables 
             const int64_t seqs = std::max<int64_t>(1, per / q_tokens);
             for (int64_t s0 = 0; s0 < batch; s0 += seqs) {
                 const int64_t ns = std::min<int64_t>(seqs, batch - s0);
-                st = decode_impl(cfg, tables, static_cast<const char *>(q) + s0 * q_tokens * row * esz, q_dtype,
-                                 (int32_t)(ns * q_tokens), n_q_heads, n_kv_heads, packed, n_packed, nullptr, 0,
-                                 softmax_scale, out + s0 * q_tokens * row, workspace, workspace_bytes, stream, nullptr,
-                                 nullptr, TQ_F32, check, nullptr, nullptr, q_tokens, q_pos0, causal, s0 * n_kv_heads);
+                const void *qs = static_cast<const char *>(q) + s0 * q_tokens * row * esz;
+                if (prefill_tiled(cfg->head_dim, q_tokens, n_q_heads / n_kv_heads))
+                    st = prefill_tiled_impl(cfg, tables, qs, q_dtype, ns, q_tokens, n_q_heads, n_kv_heads, packed,
+                                            n_packed, q_pos0, causal, softmax_scale, out + s0 * q_tokens * row,
+                                            workspace, workspace_bytes, stream, check, s0 * n_kv_heads);
+                else
+                    st = decode_impl(cfg, tables, qs, q_dtype, (int32_t)(ns * q_tokens), n_q_heads, n_kv_heads, packed,
+                                     n_packed, nullptr, 0, softmax_scale, out + s0 * q_tokens * row, workspace,
+                                     workspace_bytes, stream, nullptr, nullptr, TQ_F32, check, nullptr, nullptr,
+                                     q_tokens, q_pos0, causal, s0 * n_kv_heads);
                 if (st != TQ_OK) return st;
             }
         } else {
@@ -362,10 +431,16 @@ extern "C" tq_status tq_prefill_attention(const tq_config *cfg, const tq_tables 
                 for (int64_t i0 = 0; i0 < q_tokens; i0 += per) {
                     const int64_t c = std::min<int64_t>(per, q_tokens - i0);
                     const int64_t off = (s * q_tokens + i0) * row;
-                    st = decode_impl(cfg, tables, static_cast<const char *>(q) + off * esz, q_dtype, (int32_t)c,
-                                     n_q_heads, n_kv_heads, packed, n_packed, nullptr, 0, softmax_scale, out + off,
-                                     workspace, workspace_bytes, stream, nullptr, nullptr, TQ_F32, check, nullptr,
-                                     nullptr, (int32_t)c, q_pos0 + i0, causal, s * n_kv_heads);
+                    const void *qs = static_cast<const char *>(q) + off * esz;
+                    if (prefill_tiled(cfg->head_dim, c, n_q_heads / n_kv_heads))
+                        st = prefill_tiled_impl(cfg, tables, qs, q_dtype, 1, (int32_t)c, n_q_heads, n_kv_heads, packed,
+                                                n_packed, q_pos0 + i0, causal, softmax_scale, out + off, workspace,
+                                                workspace_bytes, stream, check, s * n_kv_heads);
+                    else
+                        st = decode_impl(cfg, tables, qs, q_dtype, (int32_t)c, n_q_heads, n_kv_heads, packed, n_packed,
+                                         nullptr, 0, softmax_scale, out + off, workspace, workspace_bytes, stream,
+                                         nullptr, nullptr, TQ_F32, check, nullptr, nullptr, (int32_t)c, q_pos0 + i0,
+                                         causal, s * n_kv_heads);
                     if (st != TQ_OK) return st;
                 }
         }

@@ -111,12 +111,52 @@ __device__ inline int64_t record_index(const int32_t *bt, int pt, int pps, int64
     return p * pt + t % pt;
 }
 
+// prefill attention by query tiles (tq_prefill.hip): the launch's query rows are (sequence,
+// query token, head) with the G heads of a kv head consecutive; q' and w of every row come from
+// k_decode_prep run over the launch's query tokens as a batch of n_seq * T
+struct PrefillArgs {
+    const float *prep;  // [n_seq * T][hkv][2][G][D]: q' then w of each row
+    const float *centroids;
+    const uint32_t *kw;
+    const float *kn;
+    const uint32_t *vw;
+    const uint16_t *vs;
+    int64_t cap;
+    const int32_t *bt;  // paged store, as in QuantArgs
+    int pt, pps;
+    int64_t n_pages;
+    int32_t *err;
+    int64_t n_packed;
+    int64_t q_pos0;     // position of the launch's first query token
+    int causal;
+    int T;              // query tokens per sequence in this launch
+    int hq, hkv;
+    int64_t slice0;     // store slice of the launch's first sequence (times hkv)
+    int tiles;          // query tiles per (sequence, kv head)
+    float scale;
+    float *out;         // [n_seq][T][hq][D] fp32
+};
+
 hipError_t launch_quantize(int d, int kb, int vb, tq_dtype dt, const QuantArgs &a, hipStream_t st);
 hipError_t launch_decode(int d, int kb, int vb, int G, const DecodeArgs &a, hipStream_t st);
 // decode through k_decode_any (the key widths other than 3 bits, and head_dim 64), whose
 // workspace holds the prepared queries
 bool decode_uses_any(int d, int kb);
 void launch_decode_any_main(int d, int kb, int vb, int G, const DecodeArgs &a, hipStream_t st);
+// q' and w of every query row of a prefill launch (tq_prefill.hip)
+struct PrefillPrepArgs {
+    const void *q;      // [n_rows][D] in q_dtype: rows (token, head)
+    int q_dtype;
+    const uint32_t *sign_bits;
+    const uint16_t *S;
+    int64_t n_rows;     // tokens * hq
+    int hq, hkv;
+    float *prep;        // [tokens][hkv][2][G][D]
+};
+hipError_t launch_prefill_prep(int d, const PrefillPrepArgs &a, hipStream_t st);
+// query rows per prefill tile, and the tiled prefill itself (prep already in a.prep)
+int prefill_tile_rows(int d);
+hipError_t launch_prefill(int d, int kb, int vb, int64_t n_seq, const PrefillArgs &a, hipStream_t st);
 // the split merge alone (a.n_split > 1), for decode kernels that write the same partials
 hipError_t launch_decode_merge(int d, int G, const DecodeArgs &a, hipStream_t st);
 // KIVI 2-bit variant (tq_kivi.hip)

@@ -1,0 +1,606 @@
+// tq_prefill.hip -- prefill attention over the packed cache by query tiles: the full_tq mode
+// of the hotelren.com guide "企业官网建设流程全解析" (section 三: attention for every prompt
+// token taken from the compressed records), with the estimate of its section 二,
+//   s_t = |k_t| ( <q', c[idx_t]> + gamma_t sqrt(pi/2)/d <w, 2 z_t - 1> ),  q' = Pi q,  w = S q',
+// softmax over the packed tokens a query may see (causal: those up to its own position) and
+// values dequantised to their bin centres (code - 2^(vb-1) + 1/2) * group scale.
+//
+// One workgroup of NW waves per (query tile, sequence, kv head): NW = 8 at head_dim 64 and
+// 128, 4 at 256 (its query operands take twice the registers).  A tile is 16 NW query rows
+// (token, head) of one kv head, the G heads of a token in consecutive rows; wave w takes rows
+// 16 w .. 16 w + 15.  The workgroup walks the packed tokens the tile can see in blocks of 32,
+// with two LDS buffers of matrix-core operands and one barrier per block: while a wave
+// computes on block n it then expands block n + 1 (loaded into registers one block ahead)
+// into the other buffer, so one wave's expansion (VALU) overlaps another's products:
+//   * the key centroids and the signs as +-1 in fp16, [token][coordinate];
+//   * the values as fp16 hi + lo pairs (v = hi + lo exactly: v has at most 16 significant
+//     bits), [coordinate][token], written transposed from each token's value word;
+//   * each wave forms its 16 x 32 scores transposed (tokens as rows: A = the key operand from
+//     LDS, B = the query rows held in registers as fp16 hi + lo of q' * scale * log2 e / sqrt d
+//     and of -w * scale * log2 e * sqrt(pi/2) / d), v_mfma_f32_16x16x32_f16; a lane then holds
+//     one query row and eight tokens, logit = |k| (c + gamma s) in log2 units;
+//   * online softmax per row (running maximum raised only when a block exceeds it; the 4 lanes
+//     of a row share it through two lane exchanges), p = 2^(logit - m) with hi + lo parts;
+//   * o^T += V^T P^T on the matrix cores (A = the value pairs from LDS, B = the lane's own p:
+//     the token order of the value columns is chosen so that the score lanes already hold
+//     the operand), three products per pair (hi hi, hi lo, lo hi).
+// Rows are divided by their l at the end; a row with no token gets zeros.
+#include <hip/hip_runtime.h>
+
+#include "tq.h"
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kPfBlk = 32;  // packed tokens per block
+constexpr float kPfLog2e = 1.4426950408889634f;
+
+// waves per workgroup (16 query rows each)
+template <int D>
+constexpr int kPfWaves = D == 256 ? 4 : 8;
+
+template <int D, int KB, int VB>
+struct PfShape {
+    static constexpr int NW = kPfWaves<D>;
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int ROWS = 16 * NW;          // query rows per tile
+    static constexpr int KW = (KB + 1) * D / 32;  // key record words
+    static constexpr int NCW = KB * D / 32;       // code-plane words (KB != 3)
+    static constexpr int VW = VB * D / 32;        // value record words
+    static constexpr int NG = D / 32;             // value groups (fp16 scales)
+    static constexpr int NKS = D / 32;            // k-steps of the score products
+    static constexpr int NDT = D / 16;            // 16-coordinate tiles of the output
+    static constexpr int KRS = D + 8;             // key operand row stride (halfwords)
+    static constexpr int VRS = kPfBlk + 8;        // value operand row stride (halfwords)
+    static constexpr int ITEMS = kPfBlk * D / 8;  // (token, 8-coordinate chunk) items of a block
+    static constexpr int NI = (ITEMS + THREADS - 1) / THREADS;
+    static constexpr int HALF = 1 << (VB - 1);
+};
+
+// one block's matrix-core operands
+template <int D, int KB, int VB>
+struct alignas(16) PfBuf {
+    using S = PfShape<D, KB, VB>;
+    // key operands: 8-coordinate chunk c of token t at [t][8 c ..]; centroids in the slot order
+    // (0 2 4 6 1 3 5 7) of the chunk's coordinates, signs (as 1 - 2 z) in the order (0 4 1 5 2 6 3 7)
+    uint16_t kc[kPfBlk * S::KRS];
+    uint16_t ks[kPfBlk * S::KRS];
+    // value operands [coordinate][slot]: slot 8 b + j holds token 4 b + j (j < 4) or
+    // 16 + 4 b + j - 4 (j >= 4), the tokens the score lanes of group b hold
+    uint16_t vh[D * S::VRS];
+    uint16_t vl[D * S::VRS];
+    float nrm[2 * kPfBlk];  // |k| then gamma, per token
+};
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+// x0 s0 and x1 s1 (x fp32, s fp16) as fp16 pairs: hi = fp16(x s), lo = fp16(x s - hi), each one
+// rounding of an exact value (mixed fma)
+__device__ __forceinline__ uint2 mix_split(float x0, _Float16 s0, float x1, _Float16 s1) {
+    uint32_t hi, lo;
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=&v"(hi) : "v"(x0), "v"(s0));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "+v"(hi) : "v"(x1), "v"(s1));
+    asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,1,1]" : "=&v"(lo) : "v"(x0), "v"(s0), "v"(hi));
+    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,1,1]" : "+v"(lo) : "v"(x1), "v"(s1), "v"(hi));
+    return make_uint2(hi, lo);
+}
+
+// x = hi + lo, hi = fp16(x), lo = fp16(x - hi), for the pairs (x0, x1): (hi pair, lo pair)
+__device__ __forceinline__ uint2 split_pair(float x0, float x1) {
+    const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+    return make_uint2(pack_h2(h0, h1), pack_h2((_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)));
+}
+
+// the 8 codebook indices of chunk c8 of a key record as bytes (coordinates 0 2 4 6 in sel_e,
+// 1 3 5 7 in sel_o) and its sign bits at bit 4 j + 3 of zw (the nibble layout's places)
+template <int D, int KB>
+__device__ __forceinline__ void key_chunk(uint32_t w0, uint32_t w1, int c8, uint32_t &sel_e, uint32_t &sel_o,
+                                          uint32_t &zw) {
+    if constexpr (KB == 3) {
+        sel_e = w0 & 0x07070707u;
+        sel_o = (w0 >> 4) & 0x07070707u;
+        zw = w0;
+    } else {
+        const uint32_t f = w0 >> ((8 * c8 * KB) % 32);  // 8 KB bits, coordinate j at KB j
+        const uint32_t s8 = w1 >> ((8 * c8) % 32);      // 8 bits, coordinate j at j
+        sel_e = sel_o = zw = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t idx = (f >> (KB * j)) & ((1u << KB) - 1u);
+            if (j & 1) sel_o |= idx << (8 * (j >> 1));
+            else sel_e |= idx << (8 * (j >> 1));
+            zw |= ((s8 >> j) & 1u) << (4 * j + 3);
+        }
+    }
+}
+
+// slot of token t in the value operand rows (see PfBuf)
+__device__ __forceinline__ int value_slot(int t) { return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3); }
+
+template <int D, int KB, int VB>
+__global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a) {
+    using S = PfShape<D, KB, VB>;
+    __shared__ PfBuf<D, KB, VB> sm[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lb = lane >> 4;
+
+    // workgroup -> (slice, tile): consecutive tiles of a slice on one XCD (workgroups are dealt
+    // to the 8 XCDs in turn), so that they share its L2; the longest tiles of a slice first
+    const int64_t nwg = gridDim.x, id = blockIdx.x;
+    const int64_t per = nwg / 8, rem = nwg % 8, xcd = id % 8, kk = id / 8;
+    const int64_t lid = xcd < rem ? xcd * (per + 1) + kk : rem * (per + 1) + (xcd - rem) * per + kk;
+    const int sl = (int)(lid / a.tiles);
+    const int tile = a.tiles - 1 - (int)(lid - (int64_t)sl * a.tiles);
+    const int seq = sl / a.hkv, kvh = sl - seq * a.hkv;
+    const int G = a.hq / a.hkv;
+    const int rows = a.T * G;
+    const int64_t sbk = a.slice0 + sl;  // store slice
+
+    // the tile's packed range: what its last row may see
+    const int r_last = min(rows, (tile + 1) * S::ROWS) - 1;
+    auto row_limit = [&](int r) -> int {
+        if (r >= rows) return 0;
+        const int64_t lim = a.causal ? min(a.n_packed, a.q_pos0 + r / G + 1) : a.n_packed;
+        return (int)max((int64_t)0, lim);
+    };
+    const int kv_end = row_limit(r_last);
+
+    // this lane's row
+    const int r = tile * S::ROWS + 16 * wave + lr;
+    const bool row_ok = r < rows;
+    const int rc = row_ok ? r : rows - 1;
+    const int qi = rc / G, qg = rc - qi * G;
+    const int lim = row_limit(r);
+    const int wave_lim = __builtin_amdgcn_readfirstlane(lim);  // lane 0: the wave's first row
+    float *const orow = a.out + (((int64_t)seq * a.T + qi) * a.hq + kvh * G + qg) * D;
+
+    f32x4_t o[S::NDT];
+#pragma unroll
+    for (int i = 0; i < S::NDT; ++i) o[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    if (kv_end == 0) {
+        if (row_ok)
+#pragma unroll
+            for (int dt = 0; dt < S::NDT; ++dt)
+                *reinterpret_cast<f32x4_t *>(orow + 16 * dt + 4 * lb) = o[dt];
+        return;
+    }
+
+    // query operands of the row: k-step ks covers coordinates 32 ks + 8 lb .. + 7 in the slot
+    // orders of the key operands, as fp16 hi + lo
+    u32x4_t qch[S::NKS], qcl[S::NKS], qsh[S::NKS], qsl[S::NKS];
+    {
+        const float cs = a.scale * kPfLog2e * rsqrtf((float)D);
+        const float ss = -cs * (1.2533141373155003f / (float)D);  // -sqrt(pi/2) / d
+        const float *pq = a.prep + (((int64_t)seq * a.T + qi) * a.hkv + kvh) * 2 * G * D + (int64_t)qg * D;
+        const float *pw = pq + (int64_t)G * D;
+#pragma unroll
+        for (int ks = 0; ks < S::NKS; ++ks) {
+            const int c0 = 32 * ks + 8 * lb;
+            const float4 x0 = *reinterpret_cast<const float4 *>(pq + c0);
+            const float4 x1 = *reinterpret_cast<const float4 *>(pq + c0 + 4);
+            const float4 y0 = *reinterpret_cast<const float4 *>(pw + c0);
+            const float4 y1 = *reinterpret_cast<const float4 *>(pw + c0 + 4);
+            const float xc[8] = {x0.x, x0.z, x1.x, x1.z, x0.y, x0.w, x1.y, x1.w};  // 0 2 4 6 1 3 5 7
+            const float xs[8] = {y0.x, y1.x, y0.y, y1.y, y0.z, y1.z, y0.w, y1.w};  // 0 4 1 5 2 6 3 7
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint2 c2 = split_pair(cs * xc[2 * p], cs * xc[2 * p + 1]);
+                const uint2 s2 = split_pair(ss * xs[2 * p], ss * xs[2 * p + 1]);
+                qch[ks][p] = c2.x;
+                qcl[ks][p] = c2.y;
+                qsh[ks][p] = s2.x;
+                qsl[ks][p] = s2.y;
+            }
+        }
+    }
+
+    // codebook as fp16 byte tables (entry e: byte e % 4 of word e / 4)
+    uint32_t tl[4] = {0u, 0u, 0u, 0u}, th[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < (1 << KB); ++e) {
+        const uint32_t h = f32_to_f16_bits(a.centroids[e]);
+        tl[e / 4] |= (h & 0xffu) << (8 * (e % 4));
+        th[e / 4] |= (h >> 8) << (8 * (e % 4));
+    }
+
+    // ---- one block's records into registers.  Key items: (token it / (D / 8), chunk
+    // it % (D / 8)); value items: (token it % 32, chunk it / 32).  Tokens past kv_end read the
+    // last one (their logits are masked).
+    auto rec_of = [&](int tok) -> int64_t {
+        return record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, a.err, sbk, min(tok, kv_end - 1));
+    };
+    uint32_t kr0[S::NI], kr1[S::NI], vr[S::NI], vsr[S::NI];
+    float2 knr = make_float2(0.f, 0.f);
+    auto load_block = [&](int t0) {
+        const int tmax = kv_end - 1 - t0;  // last valid token of the block, relative
+        if (!a.bt) {
+            // contiguous store: the block's records from one base (scalar), 32-bit offsets
+            const int64_t r0 = sbk * a.cap + t0;
+            const uint32_t *kwb = a.kw + r0 * S::KW;
+            const uint32_t *vwb = a.vw + r0 * S::VW;
+            const uint16_t *vsb = a.vs + r0 * S::NG;
+#pragma unroll
+            for (int k = 0; k < S::NI; ++k) {
+                const int it = tid + S::THREADS * k;
+                kr0[k] = kr1[k] = vr[k] = vsr[k] = 0u;
+                if (S::ITEMS % S::THREADS == 0 || it < S::ITEMS) {
+                    const int tk = min(it / (D / 8), tmax), c8 = it % (D / 8);
+                    if constexpr (KB == 3) {
+                        kr0[k] = kwb[tk * S::KW + c8];
+                    } else {
+                        kr0[k] = kwb[tk * S::KW + (8 * c8 * KB) / 32];
+                        kr1[k] = kwb[tk * S::KW + S::NCW + c8 / 4];
+                    }
+                    const int tv = min(it % kPfBlk, tmax), cv = it / kPfBlk;
+                    vr[k] = vwb[tv * S::VW + (8 * cv * VB) / 32];
+                    vsr[k] = vsb[tv * S::NG + cv / 4];
+                }
+            }
+            if (tid < kPfBlk) knr = *reinterpret_cast<const float2 *>(a.kn + (r0 + min(tid, tmax)) * 2);
+            return;
+        }
+#pragma unroll
+        for (int k = 0; k < S::NI; ++k) {
+            const int it = tid + S::THREADS * k;
+            kr0[k] = kr1[k] = vr[k] = vsr[k] = 0u;
+            if (S::ITEMS % S::THREADS == 0 || it < S::ITEMS) {
+                {
+                    const int t = it / (D / 8), c8 = it - t * (D / 8);
+                    const uint32_t *kp = a.kw + rec_of(t0 + t) * S::KW;
+                    if constexpr (KB == 3) {
+                        kr0[k] = kp[c8];
+                    } else {
+                        kr0[k] = kp[(8 * c8 * KB) / 32];
+                        kr1[k] = kp[S::NCW + c8 / 4];
+                    }
+                }
+                {
+                    const int t = it % kPfBlk, c8 = it / kPfBlk;
+                    const int64_t rec = rec_of(t0 + t);
+                    vr[k] = a.vw[rec * S::VW + (8 * c8 * VB) / 32];
+                    vsr[k] = a.vs[rec * S::NG + c8 / 4];
+                }
+            }
+        }
+        if (tid < kPfBlk) knr = *reinterpret_cast<const float2 *>(a.kn + rec_of(t0 + tid) * 2);
+    };
+
+    // ---- expand the registers' block into buffer B
+    auto stage = [&](PfBuf<D, KB, VB> &B) {
+#pragma unroll
+        for (int k = 0; k < S::NI; ++k) {
+            const int it = tid + S::THREADS * k;
+            if (S::ITEMS % S::THREADS == 0 || it < S::ITEMS) {
+                {
+                    const int t = it / (D / 8), c8 = it - t * (D / 8);
+                    uint32_t sel_e, sel_o, zw;
+                    key_chunk<D, KB>(kr0[k], kr1[k], c8, sel_e, sel_o, zw);
+                    uint32_t le, he, lo, ho;
+                    if constexpr (KB <= 3) {
+                        le = __builtin_amdgcn_perm(tl[1], tl[0], sel_e);
+                        he = __builtin_amdgcn_perm(th[1], th[0], sel_e);
+                        lo = __builtin_amdgcn_perm(tl[1], tl[0], sel_o);
+                        ho = __builtin_amdgcn_perm(th[1], th[0], sel_o);
+                    } else {
+                        // 16 entries: the low three index bits pick within a half of the
+                        // table, bit 3 (as a byte mask) picks the half
+                        const uint32_t e3 = sel_e & 0x07070707u, o3 = sel_o & 0x07070707u;
+                        const uint32_t me = ((sel_e >> 3) & 0x01010101u) * 0xffu;
+                        const uint32_t mo = ((sel_o >> 3) & 0x01010101u) * 0xffu;
+                        le = (__builtin_amdgcn_perm(tl[3], tl[2], e3) & me) | (__builtin_amdgcn_perm(tl[1], tl[0], e3) & ~me);
+                        he = (__builtin_amdgcn_perm(th[3], th[2], e3) & me) | (__builtin_amdgcn_perm(th[1], th[0], e3) & ~me);
+                        lo = (__builtin_amdgcn_perm(tl[3], tl[2], o3) & mo) | (__builtin_amdgcn_perm(tl[1], tl[0], o3) & ~mo);
+                        ho = (__builtin_amdgcn_perm(th[3], th[2], o3) & mo) | (__builtin_amdgcn_perm(th[1], th[0], o3) & ~mo);
+                    }
+                    const u32x4_t kc = {__builtin_amdgcn_perm(he, le, 0x05010400u), __builtin_amdgcn_perm(he, le, 0x07030602u),
+                                        __builtin_amdgcn_perm(ho, lo, 0x05010400u), __builtin_amdgcn_perm(ho, lo, 0x07030602u)};
+                    u32x4_t kz;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) kz[q] = ((zw << (12 - 4 * q)) & 0x80008000u) | 0x3c003c00u;
+                    *reinterpret_cast<u32x4_t *>(&B.kc[t * S::KRS + 8 * c8]) = kc;
+                    *reinterpret_cast<u32x4_t *>(&B.ks[t * S::KRS + 8 * c8]) = kz;
+                }
+                {
+                    // values of coordinates 8 c8 .. 8 c8 + 7 of token t: (code - HALF + 1/2) s
+                    const int t = it % kPfBlk, c8 = it / kPfBlk;
+                    const uint32_t w = vr[k] >> ((8 * c8 * VB) % 32);
+                    const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)vsr[k]);
+                    const int slot = value_slot(t);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float u0 = (float)((w >> (VB * 2 * q)) & ((1u << VB) - 1u)) + (0.5f - (float)S::HALF);
+                        const float u1 = (float)((w >> (VB * (2 * q + 1))) & ((1u << VB) - 1u)) + (0.5f - (float)S::HALF);
+                        const uint2 hl = mix_split(u0, sc, u1, sc);
+                        const int row = (8 * c8 + 2 * q) * S::VRS + slot;
+                        B.vh[row] = (uint16_t)hl.x;
+                        B.vh[row + S::VRS] = (uint16_t)(hl.x >> 16);
+                        B.vl[row] = (uint16_t)hl.y;
+                        B.vl[row + S::VRS] = (uint16_t)(hl.y >> 16);
+                    }
+                }
+            }
+        }
+        if (tid < kPfBlk) {
+            B.nrm[tid] = knr.x;
+            B.nrm[kPfBlk + tid] = knr.y;
+        }
+    };
+
+    float m_run = -INFINITY, l_run = 0.f;
+    const int nb = (kv_end + kPfBlk - 1) / kPfBlk;
+    load_block(0);
+    stage(sm[0]);
+    if (nb > 1) load_block(kPfBlk);
+    __syncthreads();
+    for (int n = 0; n < nb; ++n) {
+        const int t0 = n * kPfBlk;
+        const PfBuf<D, KB, VB> &B = sm[n & 1];
+        // ---- scores, transposed: C[token][row], lane (row lr, tokens 4 lb + i | 16 + 4 lb + i).
+        //      Issue order: four independent accumulators between dependent products.
+        f32x4_t sc[2], sz[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) sc[tt] = sz[tt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < S::NKS; ++ks) {
+            half8_t kc[2], kz[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int off = (16 * tt + lr) * S::KRS + 32 * ks + 8 * lb;
+                kc[tt] = *reinterpret_cast<const half8_t *>(&B.kc[off]);
+                kz[tt] = *reinterpret_cast<const half8_t *>(&B.ks[off]);
+            }
+            const half8_t qh = __builtin_bit_cast(half8_t, qch[ks]), ql = __builtin_bit_cast(half8_t, qcl[ks]);
+            const half8_t wh = __builtin_bit_cast(half8_t, qsh[ks]), wl = __builtin_bit_cast(half8_t, qsl[ks]);
+            sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[0], qh, sc[0], 0, 0, 0);
+            sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[1], qh, sc[1], 0, 0, 0);
+            sz[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kz[0], wh, sz[0], 0, 0, 0);
+            sz[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kz[1], wh, sz[1], 0, 0, 0);
+            sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[0], ql, sc[0], 0, 0, 0);
+            sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[1], ql, sc[1], 0, 0, 0);
+            sz[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kz[0], wl, sz[0], 0, 0, 0);
+            sz[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kz[1], wl, sz[1], 0, 0, 0);
+        }
+        float lg[8];
+        {
+            const f32x4_t n1a = *reinterpret_cast<const f32x4_t *>(&B.nrm[4 * lb]);
+            const f32x4_t n1b = *reinterpret_cast<const f32x4_t *>(&B.nrm[16 + 4 * lb]);
+            const f32x4_t n2a = *reinterpret_cast<const f32x4_t *>(&B.nrm[kPfBlk + 4 * lb]);
+            const f32x4_t n2b = *reinterpret_cast<const f32x4_t *>(&B.nrm[kPfBlk + 16 + 4 * lb]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lg[i] = n1a[i] * fmaf(n2a[i], sz[0][i], sc[0][i]);
+                lg[4 + i] = n1b[i] * fmaf(n2b[i], sz[1][i], sc[1][i]);
+            }
+        }
+        if (t0 + kPfBlk > wave_lim) {
+            // tokens at or past the row's limit (its causal end, or the packed end) drop out
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int t = t0 + (j < 4 ? 4 * lb + j : 16 + 4 * lb + j - 4);
+                if (t >= lim) lg[j] = -INFINITY;
+            }
+        }
+        // ---- online softmax of the row (its 4 lanes: lb = 0 .. 3)
+        float mx = lg[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, lg[j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool raise = mx > m_run;
+        if (__ballot(raise)) {
+            const float mn = raise ? mx : m_run;
+            const float alpha = raise ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mn)) : 1.f;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < S::NDT; ++dt) o[dt] *= alpha;
+            m_run = mn;
+        }
+        const float mu = m_run == -INFINITY ? 0.f : m_run;
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(lg[j] - mu);
+            l_run += p[j];
+        }
+        u32x4_t ph, pl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint2 x = mix_split(p[2 * q], (_Float16)1.0f, p[2 * q + 1], (_Float16)1.0f);
+            ph[q] = x.x;
+            pl[q] = x.y;
+        }
+        // ---- o^T[coordinate][row] += V^T P^T, four output tiles at a time (independent
+        //      accumulators between dependent products)
+        const half8_t bph = __builtin_bit_cast(half8_t, ph), bpl = __builtin_bit_cast(half8_t, pl);
+#pragma unroll
+        for (int d4 = 0; d4 < S::NDT; d4 += 4) {
+            half8_t vh[4], vl[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int off = (16 * (d4 + u) + lr) * S::VRS + 8 * lb;
+                vh[u] = *reinterpret_cast<const half8_t *>(&B.vh[off]);
+                vl[u] = *reinterpret_cast<const half8_t *>(&B.vl[off]);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) o[d4 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[u], bph, o[d4 + u], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) o[d4 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[u], bpl, o[d4 + u], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) o[d4 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl[u], bph, o[d4 + u], 0, 0, 0);
+        }
+        // ---- the next block into the other buffer (no wave reads it before the barrier), and
+        //      the one after into registers
+        if (n + 1 < nb) {
+            stage(sm[(n + 1) & 1]);
+            if (n + 2 < nb) load_block(t0 + 2 * kPfBlk);
+        }
+        __syncthreads();
+    }
+    // ---- l of the row over its 4 lanes; lane holds coordinates 16 dt + 4 lb + i
+    float l = l_run;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (row_ok)
+#pragma unroll
+        for (int dt = 0; dt < S::NDT; ++dt)
+            *reinterpret_cast<f32x4_t *>(orow + 16 * dt + 4 * lb) = o[dt] * inv;
+}
+
+// ---- query preparation for the tiles: for each query row (token, head) of the launch,
+// q' = H (sigma o q) (unnormalised Walsh-Hadamard transform by lane exchanges, as the decode's
+// preparation) and w = S q' on the matrix cores (S is fp16; q' 2^-e, e per row so that its
+// largest entry lies in [2^13, 2^14), enters as fp16 hi + lo, so each product is exact up to
+// the split's 2^-22 and the fp32 sums; the sums are scaled back by 2^e).  Workgroups of 4 waves take 64
+// consecutive rows, 16 per wave; rows are [token][head] of q, and the results go to the
+// layout the tiles read: [token][kv head][q' of the G heads, then their w][D].
+constexpr int kPrepRows = 64;
+
+template <int D>
+__global__ __launch_bounds__(256) void k_prefill_prep(PrefillPrepArgs a) {
+    constexpr int E = D / 64;       // coordinates per lane of one row (lane + 64 e)
+    constexpr int NKS = D / 32, NOT = D / 16;
+    constexpr int QRS = D + 4;      // LDS row stride (floats)
+    __shared__ __align__(16) float qs[kPrepRows * QRS];
+    __shared__ int qe[kPrepRows];  // per row: q' enters the products as q' 2^-qe (|q' 2^-qe| < 2^14)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lb = lane >> 4;
+    const int64_t r0 = (int64_t)blockIdx.x * kPrepRows;
+    const int G = a.hq / a.hkv;
+    // q' of the wave's 16 rows (one row at a time across the wave's lanes)
+    for (int i = 0; i < 16; ++i) {
+        const int rl = 16 * wave + i;
+        const int64_t r = min(r0 + rl, a.n_rows - 1);
+        float v[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = lane + 64 * e;
+            float x;
+            if (a.q_dtype == TQ_F32) x = load1(a.q, r * D + j, f32_tag{});
+            else if (a.q_dtype == TQ_BF16) x = load1(a.q, r * D + j, bf16_tag{});
+            else x = load1(a.q, r * D + j, f16_tag{});
+            v[e] = flip_sign(x, (a.sign_bits[j >> 5] >> (j & 31)) & 1u);
+        }
+#pragma unroll
+        for (int len = 1; len < 64; len <<= 1)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float o = __shfl_xor(v[e], len);
+                v[e] = (lane & len) ? (o - v[e]) : (v[e] + o);
+            }
+#pragma unroll
+        for (int m = 1; m < E; m <<= 1) {
+            float u[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) u[e] = (e & m) ? (v[e ^ m] - v[e]) : (v[e] + v[e ^ m]);
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = u[e];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) qs[rl * QRS + lane + 64 * e] = v[e];
+        // a power of two that brings the row's largest |q'| into [2^13, 2^14), so that the fp16
+        // split neither overflows nor loses bits to subnormals
+        float mx = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) mx = fmaxf(mx, fabsf(v[e]));
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        if (lane == 0) {
+            int ex = 0;
+            if (mx > 0.f) (void)frexpf(mx, &ex);  // mx < 2^ex
+            qe[rl] = ex - 14;
+        }
+    }
+    __syncthreads();
+    // w^T = S q'^T for the wave's rows: A = rows of S (fp16, 16 output coordinates x 32), B = q'
+    // of the 16 rows as hi + lo; C lane: row lr, coordinates 16 ot + 4 lb + i
+    const int rl = 16 * wave + lr;
+    const int64_t r = r0 + rl;
+    const int ex = qe[rl];
+    half8_t bh[NKS], bl[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        const float4 x0 = *reinterpret_cast<const float4 *>(&qs[rl * QRS + 32 * ks + 8 * lb]);
+        const float4 x1 = *reinterpret_cast<const float4 *>(&qs[rl * QRS + 32 * ks + 8 * lb + 4]);
+        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float y = ldexpf(x[j], -ex);
+            bh[ks][j] = (_Float16)y;
+            bl[ks][j] = (_Float16)(y - (float)bh[ks][j]);
+        }
+    }
+    const int64_t tok = r / a.hq;
+    const int h = (int)(r - tok * a.hq), kvh = h / G, g = h - kvh * G;
+    float *const dst = a.prep + ((tok * a.hkv + kvh) * 2 * G + g) * D;
+    const bool ok = r < a.n_rows;
+#pragma unroll
+    for (int ot = 0; ot < NOT; ++ot) {
+        f32x4_t acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const half8_t sa = *reinterpret_cast<const half8_t *>(a.S + (int64_t)(16 * ot + lr) * D + 32 * ks + 8 * lb);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, bh[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, bl[ks], acc, 0, 0, 0);
+        }
+        if (ok) {
+            f32x4_t wv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[i] = ldexpf(acc[i], ex);
+            *reinterpret_cast<f32x4_t *>(dst + (int64_t)G * D + 16 * ot + 4 * lb) = wv;
+        }
+    }
+    // q' itself: lane lr's row, coordinates 16 ot + 4 lb .. (the same lanes as w)
+    if (ok)
+#pragma unroll
+        for (int ot = 0; ot < NOT; ++ot)
+            *reinterpret_cast<float4 *>(dst + 16 * ot + 4 * lb) =
+                *reinterpret_cast<const float4 *>(&qs[rl * QRS + 16 * ot + 4 * lb]);
+}
+
+template <int D, int KB>
+hipError_t launch_kb(int vb, dim3 grid, const PrefillArgs &a, hipStream_t st) {
+    const dim3 block(64 * kPfWaves<D>);
+    if (vb == 2) hipLaunchKernelGGL((k_prefill_tile<D, KB, 2>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_prefill_tile<D, KB, 4>), grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(int kb, int vb, dim3 grid, const PrefillArgs &a, hipStream_t st) {
+    switch (kb) {
+        case 1: return launch_kb<D, 1>(vb, grid, a, st);
+        case 2: return launch_kb<D, 2>(vb, grid, a, st);
+        case 3: return launch_kb<D, 3>(vb, grid, a, st);
+        default: return launch_kb<D, 4>(vb, grid, a, st);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_prep(int d, const PrefillPrepArgs &a, hipStream_t st) {
+    const dim3 grid((unsigned)((a.n_rows + kPrepRows - 1) / kPrepRows));
+    if (d == 64) hipLaunchKernelGGL((k_prefill_prep<64>), grid, dim3(256), 0, st, a);
+    else if (d == 128) hipLaunchKernelGGL((k_prefill_prep<128>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_prefill_prep<256>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+int prefill_tile_rows(int d) { return 16 * (d == 256 ? kPfWaves<256> : kPfWaves<128>); }
+
+hipError_t launch_prefill(int d, int kb, int vb, int64_t n_seq, const PrefillArgs &a, hipStream_t st) {
+    const dim3 grid((unsigned)(n_seq * a.hkv * a.tiles));
+    if (d == 64) return launch_d<64>(kb, vb, grid, a, st);
+    if (d == 128) return launch_d<128>(kb, vb, grid, a, st);
+    return launch_kb<256, 3>(vb, grid, a, st);
+}
+
+}  // namespace tq

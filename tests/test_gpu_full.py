@@ -7,6 +7,7 @@ import math
 import numpy as np
 import pytest
 
+import oracle as O
 import tq_workloads as W
 import compressed_decode_attention_02_amd as tq
 
@@ -85,11 +86,42 @@ def _decode_sampled(torch, env, w, store, ring, n_layer, layer, b_list, label):
     assert_decode_close(g[b_list], ref, f"{label} layer {layer} b {b_list}")
 
 
+def _prefill_sampled(torch, env, w, store, T, picks, label):
+    """Prefill attention over layer 0's packed history as the benchmark times it (the last T
+    tokens of every sequence as causal query tokens, one call); the sampled (sequence, query
+    token) pairs are decoded by the oracle over their causal prefix."""
+    dev = store.key_words.device
+    pos0 = w.n_packed - T
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.cid * 1000 + 29)
+    dt = torch.bfloat16 if w.in_dtype == "bf16" else torch.float32
+    q = torch.randn((w.batch, T, w.hq, w.d), generator=gen, device=dev, dtype=torch.float32).to(dt)
+    out = torch.zeros((w.batch, T, w.hq, w.d), dtype=torch.float32, device=dev)
+    ws = tq.new_prefill_workspace(env.cfg, w.batch, T, w.hq, w.hkv, w.n_packed)
+    scale = 1.0 / math.sqrt(w.d)
+    tq.tq_prefill_attention(env.cfg, env.tables, q, w.batch, T, w.hq, w.hkv, store.struct(0), w.n_packed, pos0, True,
+                            scale, out, ws)
+    torch.cuda.synchronize()
+    for b, i in picks:
+        sl = slice(b * w.hkv, (b + 1) * w.hkv)
+        P = dict(kw=store.key_words[sl].cpu().numpy().view(np.uint32), kn=store.key_norms[sl].cpu().numpy(),
+                 vw=store.val_words[sl].cpu().numpy().view(np.uint32),
+                 vs=store.val_scales[sl].cpu().numpy().view(np.uint16))
+        qs = dev_to_stored(q[b, i]).astype(np.float64)[None, None]
+        ref = O.prefill(d=w.d, kb=w.key_bits, vb=w.value_bits, c32=env.c32, sigma=env.sigma, S_bits=env.S, B=1, T=1,
+                        Hq=w.hq, Hkv=w.hkv, kw=P["kw"], kn=P["kn"], vw=P["vw"], vs=P["vs"], cap=store.capacity,
+                        n_packed=w.n_packed, q=qs, pos0=pos0 + i, causal=True, scale=scale)
+        g = out[b, i].cpu().numpy().astype(np.float64)[None, None]
+        assert_decode_close(g, ref, f"{label} prefill T={T} sequence {b} query token {i}")
+
+
 def test_full_llama_b1_32k(torch):
     w = W.WORKLOADS[2]
     env, K, V, store, ring, n_layer, n_sl = _build(torch, w)
     _check_sampled_records(torch, env, w, K, V, store, n_sl, w.name)
     _decode_sampled(torch, env, w, store, ring, n_layer, 0, [0], w.name)
+    del K, V
+    _prefill_sampled(torch, env, w, store, 512, [(0, 0), (0, 511)], w.name)
 
 
 def test_full_batched_8k_v4(torch):
@@ -97,6 +129,8 @@ def test_full_batched_8k_v4(torch):
     env, K, V, store, ring, n_layer, n_sl = _build(torch, w)
     _check_sampled_records(torch, env, w, K, V, store, n_sl, w.name)
     _decode_sampled(torch, env, w, store, ring, n_layer, 0, [0, 17, 31], w.name)
+    del K, V
+    _prefill_sampled(torch, env, w, store, 512, [(0, 0), (13, 300), (31, 511)], w.name)
 
 
 def test_full_d256_16k(torch):
@@ -104,6 +138,8 @@ def test_full_d256_16k(torch):
     env, K, V, store, ring, n_layer, n_sl = _build(torch, w)
     _check_sampled_records(torch, env, w, K, V, store, n_sl, w.name)
     _decode_sampled(torch, env, w, store, ring, n_layer, 0, [0, 7], w.name)
+    del K, V
+    _prefill_sampled(torch, env, w, store, 512, [(0, 0), (7, 511)], w.name)
 
 
 def test_full_32_layers_b4_32k(torch):

@@ -1,6 +1,8 @@
 """Prefill attention over the packed cache (tq_prefill_attention) against the oracle's prefill
-on the same packed bytes: causal and full windows, both decode kernels (3-bit keys at
-head_dim 128 and 256, and the fp32 path for other key widths), paged stores."""
+on the same packed bytes: causal and full windows, the tiled kernel (query tiles of 128 rows,
+64 at head_dim 256: every key width, head_dim 64, 128 and 256, G = 1 to 8, ragged last
+tiles, query tokens before and past the history's end) and the decode kernels for launches of
+few query rows, paged stores."""
 import math
 
 import numpy as np
@@ -90,3 +92,33 @@ def test_prefill_paged_store_matches_contiguous(torch):
     g2, paged, _, _, _ = _prefill_case(torch, w, 17, 623, True, "d128 paged", paged=(64, 10))
     np.testing.assert_array_equal(g1, g2)
     assert not paged.table_error()
+
+
+def test_prefill_tiled_tiles_and_tails(torch):
+    # 7 tiles of 128 rows per kv head, the last one ragged; causal from position 0 with more
+    # query tokens than packed ones (tokens 150 .. 199 see all 150)
+    _prefill_case(torch, W.custom(2, batch=2, hq=8, hkv=2, n_packed=150), 200, 0, True, "d128 G=4 from 0, T > n_packed")
+    _prefill_case(torch, W.custom(2, batch=1, hq=2, hkv=2, n_packed=333), 150, 200, True, "d128 G=1 ragged")
+    _prefill_case(torch, W.custom(3, batch=2, hq=16, hkv=2, n_packed=333), 11, 322, False, "d128 G=8 vb4 full")
+    _prefill_case(torch, W.custom(3, batch=1, hq=8, hkv=4, n_packed=97), 64, 40, True, "d128 G=2 vb4 causal")
+    _prefill_case(torch, W.custom(4, batch=1, hq=8, hkv=4, n_packed=170), 50, 120, True, "d256 G=2 vb4 causal")
+
+
+def test_prefill_tiled_key_widths(torch):
+    for kb in (1, 2, 4):
+        _prefill_case(torch, W.custom(2, d=64, key_bits=kb, batch=1, hq=8, hkv=2, n_packed=230), 40, 190, True,
+                      f"d64 kb{kb} vb2")
+    _prefill_case(torch, W.custom(3, d=64, key_bits=3, batch=1, hq=4, hkv=1, n_packed=75), 24, 51, True, "d64 kb3 vb4")
+    _prefill_case(torch, W.custom(3, d=128, key_bits=1, batch=1, hq=8, hkv=2, n_packed=230), 40, 190, True,
+                  "d128 kb1 vb4")
+    _prefill_case(torch, W.custom(2, d=128, key_bits=2, batch=1, hq=4, hkv=2, n_packed=130), 70, 0, False,
+                  "d128 kb2 full")
+    _prefill_case(torch, W.custom(3, d=128, key_bits=4, batch=2, hq=8, hkv=2, n_packed=100), 33, 67, True,
+                  "d128 kb4 vb4")
+
+
+def test_prefill_decode_path_for_few_query_rows(torch):
+    # fewer rows per kv head than half a tile (T G < 64 at head_dim 128): the decode kernels
+    _prefill_case(torch, W.custom(2, batch=2, hq=8, hkv=2, n_packed=700), 5, 695, True, "d128 T=5 (decode kernels)")
+    _prefill_case(torch, W.custom(2, d=64, key_bits=1, batch=1, hq=4, hkv=1, n_packed=300), 3, 10, True,
+                  "d64 kb1 T=3 (decode kernels)")
