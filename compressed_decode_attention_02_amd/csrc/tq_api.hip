@@ -320,15 +320,39 @@ namespace {
 // the grid's 65535 rows, and it bounds the workspace of either path
 int64_t prefill_launch_tokens(int32_t n_kv_heads) { return std::max<int64_t>(1, 65535 / n_kv_heads); }
 
-// the tiled kernel's workspace: q' and w of every query row of a launch of `tokens` tokens
-size_t prefill_prep_bytes(int d, int64_t tokens, int64_t n_q_heads) {
-    return align256(sizeof(float) * (size_t)(tokens * n_q_heads) * 2 * d);
-}
-
 // a launch of T query tokens per sequence goes to the tiled kernel when its rows (T G per kv
 // head) fill at least half a tile; shorter ones (a few query tokens over a long history) to the
 // decode kernels, whose splits spread one row's tokens over many workgroups
 bool prefill_tiled(int d, int64_t T, int64_t G) { return T * G * 2 >= tq::prefill_tile_rows(d); }
+
+// query tokens per launch of the tiled path (bounds its workspace)
+int64_t prefill_tiled_launch_tokens(int32_t n_kv_heads) { return std::max<int64_t>(1, 65536 / n_kv_heads); }
+
+// the tiled path's plan for n_seq sequences of T query tokens: tiles per (sequence, kv head)
+// and the split of each tile's packed range (so that the workgroups cover the CUs; splits of
+// whole 32-token blocks, at least 8 blocks each, at most 16 splits)
+struct PrefillPlan {
+    int tiles, n_split, per_split;
+    size_t prep, partial, partial_ml, total;  // workspace layout (bytes)
+};
+PrefillPlan prefill_plan(int d, int64_t n_seq, int64_t T, int64_t hq, int64_t hkv, int64_t n_packed) {
+    PrefillPlan p{};
+    const int64_t G = hq / hkv, tr = tq::prefill_tile_rows(d);
+    p.tiles = (int)((T * G + tr - 1) / tr);
+    const int64_t wg = n_seq * hkv * p.tiles, cus = tq::device_cus();
+    const int64_t blocks = (n_packed + 31) / 32;
+    int64_t ns = wg < cus ? (cus + wg - 1) / wg : 1;
+    ns = std::max<int64_t>(1, std::min<int64_t>({ns, 16, blocks / 8}));
+    p.n_split = (int)ns;
+    p.per_split = (int)(((blocks + ns - 1) / ns) * 32);
+    const int64_t rows = n_seq * T * hq;
+    p.prep = 0;
+    p.partial = align256(sizeof(float) * (size_t)rows * 2 * d);
+    const size_t part = ns > 1 ? align256(sizeof(float) * (size_t)(rows * ns) * d) : 0;
+    p.partial_ml = p.partial + part;
+    p.total = p.partial_ml + (ns > 1 ? align256(sizeof(float) * (size_t)(rows * ns) * 2) : 0);
+    return p;
+}
 
 // prefill by query tiles: n_seq sequences of T query tokens at positions q_pos0 .., store
 // slices slice0 ..; every argument checked before anything is launched
@@ -342,7 +366,8 @@ tq_status prefill_tiled_impl(const tq_config *cfg, const tq_tables *tables, cons
         return TQ_ERR_INVALID_ARG;
     if (n_packed > 0 && (!packed_ok(packed) || n_packed > packed->capacity)) return TQ_ERR_INVALID_ARG;
     if (n_packed >= kMaxContext) return TQ_ERR_UNSUPPORTED;  // 32-bit token indices in the kernels
-    if (workspace_bytes < prefill_prep_bytes(cfg->head_dim, n_seq * T, n_q_heads)) return TQ_ERR_WORKSPACE;
+    const PrefillPlan plan = prefill_plan(cfg->head_dim, n_seq, T, n_q_heads, n_kv_heads, n_packed);
+    if (workspace_bytes < plan.total) return TQ_ERR_WORKSPACE;
     if (check_only) return TQ_OK;
     const hipStream_t st = (hipStream_t)stream;
     tq::PrefillPrepArgs pp{};
@@ -353,7 +378,8 @@ tq_status prefill_tiled_impl(const tq_config *cfg, const tq_tables *tables, cons
     pp.n_rows = n_seq * T * n_q_heads;
     pp.hq = n_q_heads;
     pp.hkv = n_kv_heads;
-    pp.prep = static_cast<float *>(workspace);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    pp.prep = reinterpret_cast<float *>(ws + plan.prep);
     hipError_t e = tq::launch_prefill_prep(cfg->head_dim, pp, st);
     if (e != hipSuccess) return TQ_ERR_HIP;
     tq::PrefillArgs a{};
@@ -374,21 +400,48 @@ tq_status prefill_tiled_impl(const tq_config *cfg, const tq_tables *tables, cons
     a.hq = n_q_heads;
     a.hkv = n_kv_heads;
     a.slice0 = slice0;
-    const int tr = tq::prefill_tile_rows(cfg->head_dim);
-    a.tiles = (int)(((int64_t)T * G + tr - 1) / tr);
+    a.tiles = plan.tiles;
     a.scale = softmax_scale;
     a.out = out;
-    return hip_status(tq::launch_prefill(cfg->head_dim, cfg->key_bits, cfg->value_bits, n_seq, a, st));
+    a.n_split = plan.n_split;
+    a.per_split = plan.per_split;
+    a.partial = reinterpret_cast<float *>(ws + plan.partial);
+    a.partial_ml = reinterpret_cast<float *>(ws + plan.partial_ml);
+    e = tq::launch_prefill(cfg->head_dim, cfg->key_bits, cfg->value_bits, n_seq, a, st);
+    if (e != hipSuccess || plan.n_split == 1) return hip_status(e);
+    // the splits' partials of every row combined by the decode's merge (query token = batch
+    // element of the decode's layout)
+    tq::DecodeArgs m{};
+    m.batch = (int)(n_seq * T);
+    m.hq = n_q_heads;
+    m.hkv = n_kv_heads;
+    m.n_split = plan.n_split;
+    m.out = out;
+    m.partial = a.partial;
+    m.partial_ml = a.partial_ml;
+    return hip_status(tq::launch_decode_merge(cfg->head_dim, G, m, st));
 }
 }  // namespace
 
 extern "C" size_t tq_prefill_workspace_bytes(const tq_config *cfg, int32_t batch, int32_t q_tokens,
                                              int32_t n_q_heads, int32_t n_kv_heads, int64_t n_packed) {
-    if (!cfg || tq::check_config(*cfg) != TQ_OK || batch <= 0 || q_tokens <= 0 || n_q_heads <= 0 || n_kv_heads <= 0)
+    if (!cfg || tq::check_config(*cfg) != TQ_OK || batch <= 0 || q_tokens <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 ||
+        n_q_heads % n_kv_heads != 0 || n_packed < 0)
         return 0;
+    if (prefill_tiled(cfg->head_dim, q_tokens, n_q_heads / n_kv_heads)) {
+        // the launches' plans: whole sequences per launch, or chunks of one sequence
+        const int64_t per = prefill_tiled_launch_tokens(n_kv_heads);
+        const int64_t ns = q_tokens <= per ? std::min<int64_t>(batch, per / q_tokens) : 1;
+        const int64_t T = std::min<int64_t>(q_tokens, per);
+        size_t need = prefill_plan(cfg->head_dim, ns, T, n_q_heads, n_kv_heads, n_packed).total;
+        if (q_tokens > per && q_tokens % per)  // the last chunk of a sequence
+            need = std::max(need, prefill_plan(cfg->head_dim, 1, q_tokens % per, n_q_heads, n_kv_heads, n_packed).total);
+        if (q_tokens <= per && batch % ns)     // the last launch's sequences
+            need = std::max(need, prefill_plan(cfg->head_dim, batch % ns, q_tokens, n_q_heads, n_kv_heads, n_packed).total);
+        return need;
+    }
     const int64_t vb = std::min<int64_t>((int64_t)batch * q_tokens, prefill_launch_tokens(n_kv_heads));
-    return std::max(tq_decode_workspace_bytes(cfg, (int32_t)vb, n_q_heads, n_kv_heads, n_packed),
-                    prefill_prep_bytes(cfg->head_dim, vb, n_q_heads));
+    return tq_decode_workspace_bytes(cfg, (int32_t)vb, n_q_heads, n_kv_heads, n_packed);
 }
 
 extern "C" tq_status tq_prefill_attention(const tq_config *cfg, const tq_tables *tables, const void *q,
@@ -403,7 +456,9 @@ extern "C" tq_status tq_prefill_attention(const tq_config *cfg, const tq_tables 
         (causal != 0 && causal != 1) || !packed)
         return TQ_ERR_INVALID_ARG;
     if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_ERR_INVALID_ARG;
-    const int64_t per = prefill_launch_tokens(n_kv_heads);
+    if (n_q_heads % n_kv_heads != 0) return TQ_ERR_INVALID_ARG;
+    const bool tiled = prefill_tiled(cfg->head_dim, q_tokens, n_q_heads / n_kv_heads);
+    const int64_t per = tiled ? prefill_tiled_launch_tokens(n_kv_heads) : prefill_launch_tokens(n_kv_heads);
     const int64_t esz = q_dtype == TQ_F32 ? 4 : 2;
     const int64_t row = (int64_t)n_q_heads * cfg->head_dim;  // elements of one query token
     // the launches: whole sequences per launch while a sequence's tokens fit one launch,
@@ -415,7 +470,7 @@ extern "C" tq_status tq_prefill_attention(const tq_config *cfg, const tq_tables 
             for (int64_t s0 = 0; s0 < batch; s0 += seqs) {
                 const int64_t ns = std::min<int64_t>(seqs, batch - s0);
                 const void *qs = static_cast<const char *>(q) + s0 * q_tokens * row * esz;
-                if (prefill_tiled(cfg->head_dim, q_tokens, n_q_heads / n_kv_heads))
+                if (tiled)
                     st = prefill_tiled_impl(cfg, tables, qs, q_dtype, ns, q_tokens, n_q_heads, n_kv_heads, packed,
                                             n_packed, q_pos0, causal, softmax_scale, out + s0 * q_tokens * row,
                                             workspace, workspace_bytes, stream, check, s0 * n_kv_heads);
@@ -432,7 +487,7 @@ extern "C" tq_status tq_prefill_attention(const tq_config *cfg, const tq_tables 
                     const int64_t c = std::min<int64_t>(per, q_tokens - i0);
                     const int64_t off = (s * q_tokens + i0) * row;
                     const void *qs = static_cast<const char *>(q) + off * esz;
-                    if (prefill_tiled(cfg->head_dim, c, n_q_heads / n_kv_heads))
+                    if (tiled)
                         st = prefill_tiled_impl(cfg, tables, qs, q_dtype, 1, (int32_t)c, n_q_heads, n_kv_heads, packed,
                                                 n_packed, q_pos0 + i0, causal, softmax_scale, out + off, workspace,
                                                 workspace_bytes, stream, check, s * n_kv_heads);

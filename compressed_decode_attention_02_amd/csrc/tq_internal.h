@@ -134,7 +134,14 @@ struct PrefillArgs {
     int64_t slice0;     // store slice of the launch's first sequence (times hkv)
     int tiles;          // query tiles per (sequence, kv head)
     float scale;
-    float *out;         // [n_seq][T][hq][D] fp32
+    float *out;         // [n_seq][T][hq][D] fp32 (n_split == 1)
+    // split of each tile's packed tokens over n_split workgroups (per_split tokens each, a
+    // multiple of 32): each writes its unnormalised o and (m, l) per row in the decode's split
+    // layout, [n_seq * T * hkv][n_split][G][D] and [..][n_split][G][2], for k_decode_merge
+    int n_split;
+    int per_split;
+    float *partial;
+    float *partial_ml;
 };
 
 hipError_t launch_quantize(int d, int kb, int vb, tq_dtype dt, const QuantArgs &a, hipStream_t st);

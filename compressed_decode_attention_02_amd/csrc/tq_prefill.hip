@@ -24,7 +24,9 @@
 //   * o^T += V^T P^T on the matrix cores (A = the value pairs from LDS, B = the lane's own p:
 //     the token order of the value columns is chosen so that the score lanes already hold
 //     the operand), three products per pair (hi hi, hi lo, lo hi).
-// Rows are divided by their l at the end; a row with no token gets zeros.
+// Rows are divided by their l at the end; a row with no token gets zeros.  When the tiles alone
+// would not fill the GPU, each tile's packed range is split over several workgroups, which write
+// their unnormalised o and (m, l) per row for the decode's split merge.
 #include <hip/hip_runtime.h>
 
 #include "tq.h"
@@ -137,8 +139,9 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
     const int64_t nwg = gridDim.x, id = blockIdx.x;
     const int64_t per = nwg / 8, rem = nwg % 8, xcd = id % 8, kk = id / 8;
     const int64_t lid = xcd < rem ? xcd * (per + 1) + kk : rem * (per + 1) + (xcd - rem) * per + kk;
-    const int sl = (int)(lid / a.tiles);
-    const int tile = a.tiles - 1 - (int)(lid - (int64_t)sl * a.tiles);
+    const int64_t ss = lid / a.tiles;  // (slice, split)
+    const int tile = a.tiles - 1 - (int)(lid - ss * a.tiles);
+    const int sl = (int)(ss / a.n_split), split = (int)(ss - (int64_t)sl * a.n_split);
     const int seq = sl / a.hkv, kvh = sl - seq * a.hkv;
     const int G = a.hq / a.hkv;
     const int rows = a.T * G;
@@ -151,7 +154,10 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
         const int64_t lim = a.causal ? min(a.n_packed, a.q_pos0 + r / G + 1) : a.n_packed;
         return (int)max((int64_t)0, lim);
     };
-    const int kv_end = row_limit(r_last);
+    const int kv_all = row_limit(r_last);
+    // this workgroup's part of it: [t_lo, kv_end)
+    const int t_lo = split * a.per_split;
+    const int kv_end = a.n_split > 1 ? min(kv_all, t_lo + a.per_split) : kv_all;
 
     // this lane's row
     const int r = tile * S::ROWS + 16 * wave + lr;
@@ -165,11 +171,21 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
     f32x4_t o[S::NDT];
 #pragma unroll
     for (int i = 0; i < S::NDT; ++i) o[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    if (kv_end == 0) {
-        if (row_ok)
+    // split partials of this lane's row: o, then (m, l)
+    const int64_t prow = (((int64_t)seq * a.T + qi) * a.hkv + kvh) * a.n_split + split;
+    float *const po = a.partial + (prow * G + qg) * D;
+    float *const pml = a.partial_ml + (prow * G + qg) * 2;
+    if (kv_end <= t_lo) {
+        if (row_ok) {
+            if (a.n_split == 1) {
 #pragma unroll
-            for (int dt = 0; dt < S::NDT; ++dt)
-                *reinterpret_cast<f32x4_t *>(orow + 16 * dt + 4 * lb) = o[dt];
+                for (int dt = 0; dt < S::NDT; ++dt) *reinterpret_cast<f32x4_t *>(orow + 16 * dt + 4 * lb) = o[dt];
+            } else {
+#pragma unroll
+                for (int dt = 0; dt < S::NDT; ++dt) *reinterpret_cast<f32x4_t *>(po + 16 * dt + 4 * lb) = o[dt];
+                if (lb == 0) *reinterpret_cast<float2 *>(pml) = make_float2(-INFINITY, 0.f);
+            }
+        }
         return;
     }
 
@@ -335,13 +351,13 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
     };
 
     float m_run = -INFINITY, l_run = 0.f;
-    const int nb = (kv_end + kPfBlk - 1) / kPfBlk;
-    load_block(0);
+    const int nb = (kv_end - t_lo + kPfBlk - 1) / kPfBlk;
+    load_block(t_lo);
     stage(sm[0]);
-    if (nb > 1) load_block(kPfBlk);
+    if (nb > 1) load_block(t_lo + kPfBlk);
     __syncthreads();
     for (int n = 0; n < nb; ++n) {
-        const int t0 = n * kPfBlk;
+        const int t0 = t_lo + n * kPfBlk;
         const PfBuf<D, KB, VB> &B = sm[n & 1];
         // ---- scores, transposed: C[token][row], lane (row lr, tokens 4 lb + i | 16 + 4 lb + i).
         //      Issue order: four independent accumulators between dependent products.
@@ -448,11 +464,16 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
     float l = l_run;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (row_ok)
+    if (!row_ok) return;
+    if (a.n_split == 1) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-        for (int dt = 0; dt < S::NDT; ++dt)
-            *reinterpret_cast<f32x4_t *>(orow + 16 * dt + 4 * lb) = o[dt] * inv;
+        for (int dt = 0; dt < S::NDT; ++dt) *reinterpret_cast<f32x4_t *>(orow + 16 * dt + 4 * lb) = o[dt] * inv;
+    } else {
+#pragma unroll
+        for (int dt = 0; dt < S::NDT; ++dt) *reinterpret_cast<f32x4_t *>(po + 16 * dt + 4 * lb) = o[dt];
+        if (lb == 0) *reinterpret_cast<float2 *>(pml) = make_float2(m_run, l);
+    }
 }
 
 // ---- query preparation for the tiles: for each query row (token, head) of the launch,
@@ -597,7 +618,7 @@ hipError_t launch_prefill_prep(int d, const PrefillPrepArgs &a, hipStream_t st) 
 int prefill_tile_rows(int d) { return 16 * (d == 256 ? kPfWaves<256> : kPfWaves<128>); }
 
 hipError_t launch_prefill(int d, int kb, int vb, int64_t n_seq, const PrefillArgs &a, hipStream_t st) {
-    const dim3 grid((unsigned)(n_seq * a.hkv * a.tiles));
+    const dim3 grid((unsigned)(n_seq * a.hkv * a.n_split * a.tiles));
     if (d == 64) return launch_d<64>(kb, vb, grid, a, st);
     if (d == 128) return launch_d<128>(kb, vb, grid, a, st);
     return launch_kb<256, 3>(vb, grid, a, st);

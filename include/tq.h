@@ -246,11 +246,15 @@ tq_status tq_decode_step(const tq_config *cfg, const tq_tables *tables, const vo
  *   q   : [batch][q_tokens][n_q_heads][head_dim] in q_dtype (device);
  *   out : [batch][q_tokens][n_q_heads][head_dim] fp32 (device); a token with no packed token
  *         to attend to gets zeros.
- * Runs the decode kernels with one batch element per query token reading its sequence's
- * records (launches of at most 65535 / n_kv_heads query tokens each, all checked before the
- * first); no ring.  workspace: tq_prefill_workspace_bytes(cfg, batch, q_tokens, n_q_heads,
- * n_kv_heads, n_packed) bytes.  Errors as tq_decode_attention; q_pos0 < 0 or causal not 0/1:
- * TQ_ERR_INVALID_ARG. */
+ * Calls whose query rows per kv head (q_tokens * G, G = n_q_heads / n_kv_heads) fill at least
+ * half a query tile (64 rows; 32 at head_dim 256) run the tiled kernel: a query preparation
+ * launch, one launch over (query tile, sequence, kv head, split of the packed range) and, when
+ * the packed range is split, the decode's merge; launches of at most 65536 / n_kv_heads query
+ * tokens.  Fewer rows run the decode kernels with one batch element per query token reading its
+ * sequence's records (launches of at most 65535 / n_kv_heads query tokens).  Every launch is
+ * checked before the first; no ring.  workspace: tq_prefill_workspace_bytes(cfg, batch,
+ * q_tokens, n_q_heads, n_kv_heads, n_packed) bytes (scratch; never needs clearing).  Errors as
+ * tq_decode_attention; q_pos0 < 0 or causal not 0/1: TQ_ERR_INVALID_ARG. */
 size_t tq_prefill_workspace_bytes(const tq_config *cfg, int32_t batch, int32_t q_tokens, int32_t n_q_heads,
                                   int32_t n_kv_heads, int64_t n_packed);
 tq_status tq_prefill_attention(const tq_config *cfg, const tq_tables *tables, const void *q, tq_dtype q_dtype,

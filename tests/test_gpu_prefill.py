@@ -104,6 +104,17 @@ def test_prefill_tiled_tiles_and_tails(torch):
     _prefill_case(torch, W.custom(4, batch=1, hq=8, hkv=4, n_packed=170), 50, 120, True, "d256 G=2 vb4 causal")
 
 
+def test_prefill_tiled_split_ranges(torch):
+    # few tiles over a long history: each tile's packed range is split over up to 16
+    # workgroups whose partials the decode's merge combines (splits that see none of a row's
+    # tokens included: causal rows near the start)
+    _prefill_case(torch, W.custom(2, batch=1, hq=8, hkv=2, n_packed=5000), 64, 4936, True, "d128 split, causal at the end")
+    _prefill_case(torch, W.custom(2, batch=1, hq=8, hkv=2, n_packed=5000), 40, 100, True, "d128 split, causal near 0")
+    _prefill_case(torch, W.custom(4, batch=1, hq=4, hkv=2, n_packed=2100), 40, 0, False, "d256 split, full window")
+    _prefill_case(torch, W.custom(2, d=64, key_bits=2, batch=2, hq=4, hkv=1, n_packed=3000), 50, 2950, True,
+                  "d64 kb2 split")
+
+
 def test_prefill_tiled_key_widths(torch):
     for kb in (1, 2, 4):
         _prefill_case(torch, W.custom(2, d=64, key_bits=kb, batch=1, hq=8, hkv=2, n_packed=230), 40, 190, True,

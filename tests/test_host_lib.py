@@ -377,10 +377,12 @@ def test_prefill_argument_errors():
     assert pf(ws_bytes=16) == B.TQ_ERR_WORKSPACE
     need = L.tq_prefill_workspace_bytes(ctypes.byref(cfg), 2, 16, 8, 2, 500)
     assert need > 0 and L.tq_prefill_workspace_bytes(ctypes.byref(cfg), 0, 16, 8, 2, 500) == 0
-    # long prompts run in several launches of at most 65535 / kv heads query tokens: the
-    # workspace is sized for one launch, and every launch is checked before the first
+    # long prompts run in several launches of at most 65536 / kv heads query tokens (the tiled
+    # kernel; 65535 / kv heads on the decode kernels): the workspace is sized for one launch,
+    # and every launch is checked before the first
     big = L.tq_prefill_workspace_bytes(ctypes.byref(cfg), 1, 40000, 8, 2, 500)
-    assert big == L.tq_prefill_workspace_bytes(ctypes.byref(cfg), 1, 32767, 8, 2, 500)
+    assert big == L.tq_prefill_workspace_bytes(ctypes.byref(cfg), 1, 32768, 8, 2, 500)
+    assert big > L.tq_prefill_workspace_bytes(ctypes.byref(cfg), 1, 32767, 8, 2, 500)
     assert pf(batch=1, q_tokens=40000, ws_bytes=16) == B.TQ_ERR_WORKSPACE
     assert pf(batch=1, q_tokens=40000, n_packed=1001) == B.TQ_ERR_INVALID_ARG
 
