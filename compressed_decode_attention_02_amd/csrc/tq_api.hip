@@ -330,7 +330,7 @@ int64_t prefill_tiled_launch_tokens(int32_t n_kv_heads) { return std::max<int64_
 
 // the tiled path's plan for n_seq sequences of T query tokens: tiles per (sequence, kv head)
 // and the split of each tile's packed range (so that the workgroups cover the CUs; splits of
-// whole 32-token blocks, at least 8 blocks each, at most 16 splits)
+// whole blocks, at least 256 tokens each, at most 16 splits)
 struct PrefillPlan {
     int tiles, n_split, per_split;
     size_t prep, partial, partial_ml, total;  // workspace layout (bytes)
@@ -340,11 +340,11 @@ PrefillPlan prefill_plan(int d, int64_t n_seq, int64_t T, int64_t hq, int64_t hk
     const int64_t G = hq / hkv, tr = tq::prefill_tile_rows(d);
     p.tiles = (int)((T * G + tr - 1) / tr);
     const int64_t wg = n_seq * hkv * p.tiles, cus = tq::device_cus();
-    const int64_t blocks = (n_packed + 31) / 32;
+    const int64_t bt = tq::prefill_block_tokens(d), blocks = (n_packed + bt - 1) / bt;
     int64_t ns = wg < cus ? (cus + wg - 1) / wg : 1;
-    ns = std::max<int64_t>(1, std::min<int64_t>({ns, 16, blocks / 8}));
+    ns = std::max<int64_t>(1, std::min<int64_t>({ns, 16, blocks * bt / 256}));
     p.n_split = (int)ns;
-    p.per_split = (int)(((blocks + ns - 1) / ns) * 32);
+    p.per_split = (int)(((blocks + ns - 1) / ns) * bt);
     const int64_t rows = n_seq * T * hq;
     p.prep = 0;
     p.partial = align256(sizeof(float) * (size_t)rows * 2 * d);

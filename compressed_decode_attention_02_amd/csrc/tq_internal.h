@@ -136,7 +136,7 @@ struct PrefillArgs {
     float scale;
     float *out;         // [n_seq][T][hq][D] fp32 (n_split == 1)
     // split of each tile's packed tokens over n_split workgroups (per_split tokens each, a
-    // multiple of 32): each writes its unnormalised o and (m, l) per row in the decode's split
+    // multiple of the block size): each writes its unnormalised o and (m, l) per row in the decode's split
     // layout, [n_seq * T * hkv][n_split][G][D] and [..][n_split][G][2], for k_decode_merge
     int n_split;
     int per_split;
@@ -163,6 +163,7 @@ struct PrefillPrepArgs {
 hipError_t launch_prefill_prep(int d, const PrefillPrepArgs &a, hipStream_t st);
 // query rows per prefill tile, and the tiled prefill itself (prep already in a.prep)
 int prefill_tile_rows(int d);
+int prefill_block_tokens(int d);
 hipError_t launch_prefill(int d, int kb, int vb, int64_t n_seq, const PrefillArgs &a, hipStream_t st);
 // the split merge alone (a.n_split > 1), for decode kernels that write the same partials
 hipError_t launch_decode_merge(int d, int G, const DecodeArgs &a, hipStream_t st);

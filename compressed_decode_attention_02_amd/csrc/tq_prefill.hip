@@ -8,7 +8,8 @@
 // One workgroup of NW waves per (query tile, sequence, kv head): NW = 8 at head_dim 64 and
 // 128, 4 at 256 (its query operands take twice the registers).  A tile is 16 NW query rows
 // (token, head) of one kv head, the G heads of a token in consecutive rows; wave w takes rows
-// 16 w .. 16 w + 15.  The workgroup walks the packed tokens the tile can see in blocks of 32,
+// 16 w .. 16 w + 15.  The workgroup walks the packed tokens the tile can see in blocks of 64
+// tokens (32 at head_dim 256),
 // with two LDS buffers of matrix-core operands and one barrier per block: while a wave
 // computes on block n it then expands block n + 1 (loaded into registers one block ahead)
 // into the other buffer, so one wave's expansion (VALU) overlaps another's products:
@@ -39,7 +40,6 @@ namespace {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kPfBlk = 32;  // packed tokens per block
 constexpr float kPfLog2e = 1.4426950408889634f;
 
 // waves per workgroup (16 query rows each)
@@ -48,6 +48,9 @@ constexpr int kPfWaves = D == 256 ? 4 : 8;
 
 template <int D, int KB, int VB>
 struct PfShape {
+    static constexpr int BLK = D == 256 ? 32 : 64;  // packed tokens per block
+    static constexpr int NTT = BLK / 16;            // 16-token tiles of a block (score products)
+    static constexpr int NPS = BLK / 32;            // 32-token steps of a block (value products)
     static constexpr int NW = kPfWaves<D>;
     static constexpr int THREADS = 64 * NW;
     static constexpr int ROWS = 16 * NW;          // query rows per tile
@@ -58,8 +61,8 @@ struct PfShape {
     static constexpr int NKS = D / 32;            // k-steps of the score products
     static constexpr int NDT = D / 16;            // 16-coordinate tiles of the output
     static constexpr int KRS = D + 8;             // key operand row stride (halfwords)
-    static constexpr int VRS = kPfBlk + 8;        // value operand row stride (halfwords)
-    static constexpr int ITEMS = kPfBlk * D / 8;  // (token, 8-coordinate chunk) items of a block
+    static constexpr int VRS = BLK + 8;           // value operand row stride (halfwords)
+    static constexpr int ITEMS = BLK * D / 8;     // (token, 8-coordinate chunk) items of a block
     static constexpr int NI = (ITEMS + THREADS - 1) / THREADS;
     static constexpr int HALF = 1 << (VB - 1);
 };
@@ -70,13 +73,13 @@ struct alignas(16) PfBuf {
     using S = PfShape<D, KB, VB>;
     // key operands: 8-coordinate chunk c of token t at [t][8 c ..]; centroids in the slot order
     // (0 2 4 6 1 3 5 7) of the chunk's coordinates, signs (as 1 - 2 z) in the order (0 4 1 5 2 6 3 7)
-    uint16_t kc[kPfBlk * S::KRS];
-    uint16_t ks[kPfBlk * S::KRS];
-    // value operands [coordinate][slot]: slot 8 b + j holds token 4 b + j (j < 4) or
-    // 16 + 4 b + j - 4 (j >= 4), the tokens the score lanes of group b hold
+    uint16_t kc[S::BLK * S::KRS];
+    uint16_t ks[S::BLK * S::KRS];
+    // value operands [coordinate][slot]: in each 32-token step, slot 8 b + j holds token 4 b + j
+    // (j < 4) or 16 + 4 b + j - 4 (j >= 4) of the step, the tokens the score lanes of group b hold
     uint16_t vh[D * S::VRS];
     uint16_t vl[D * S::VRS];
-    float nrm[2 * kPfBlk];  // |k| then gamma, per token
+    float nrm[2 * S::BLK];  // |k| then gamma, per token
 };
 
 __device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
@@ -124,7 +127,9 @@ __device__ __forceinline__ void key_chunk(uint32_t w0, uint32_t w1, int c8, uint
 }
 
 // slot of token t in the value operand rows (see PfBuf)
-__device__ __forceinline__ int value_slot(int t) { return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3); }
+__device__ __forceinline__ int value_slot(int t) {
+    return 32 * (t >> 5) + 8 * ((t & 15) >> 2) + 4 * ((t >> 4) & 1) + (t & 3);
+}
 
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a) {
@@ -255,12 +260,12 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
                         kr0[k] = kwb[tk * S::KW + (8 * c8 * KB) / 32];
                         kr1[k] = kwb[tk * S::KW + S::NCW + c8 / 4];
                     }
-                    const int tv = min(it % kPfBlk, tmax), cv = it / kPfBlk;
+                    const int tv = min(it % S::BLK, tmax), cv = it / S::BLK;
                     vr[k] = vwb[tv * S::VW + (8 * cv * VB) / 32];
                     vsr[k] = vsb[tv * S::NG + cv / 4];
                 }
             }
-            if (tid < kPfBlk) knr = *reinterpret_cast<const float2 *>(a.kn + (r0 + min(tid, tmax)) * 2);
+            if (tid < S::BLK) knr = *reinterpret_cast<const float2 *>(a.kn + (r0 + min(tid, tmax)) * 2);
             return;
         }
 #pragma unroll
@@ -279,14 +284,14 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
                     }
                 }
                 {
-                    const int t = it % kPfBlk, c8 = it / kPfBlk;
+                    const int t = it % S::BLK, c8 = it / S::BLK;
                     const int64_t rec = rec_of(t0 + t);
                     vr[k] = a.vw[rec * S::VW + (8 * c8 * VB) / 32];
                     vsr[k] = a.vs[rec * S::NG + c8 / 4];
                 }
             }
         }
-        if (tid < kPfBlk) knr = *reinterpret_cast<const float2 *>(a.kn + rec_of(t0 + tid) * 2);
+        if (tid < S::BLK) knr = *reinterpret_cast<const float2 *>(a.kn + rec_of(t0 + tid) * 2);
     };
 
     // ---- expand the registers' block into buffer B
@@ -326,7 +331,7 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
                 }
                 {
                     // values of coordinates 8 c8 .. 8 c8 + 7 of token t: (code - HALF + 1/2) s
-                    const int t = it % kPfBlk, c8 = it / kPfBlk;
+                    const int t = it % S::BLK, c8 = it / S::BLK;
                     const uint32_t w = vr[k] >> ((8 * c8 * VB) % 32);
                     const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)vsr[k]);
                     const int slot = value_slot(t);
@@ -344,70 +349,68 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
                 }
             }
         }
-        if (tid < kPfBlk) {
+        if (tid < S::BLK) {
             B.nrm[tid] = knr.x;
-            B.nrm[kPfBlk + tid] = knr.y;
+            B.nrm[S::BLK + tid] = knr.y;
         }
     };
 
     float m_run = -INFINITY, l_run = 0.f;
-    const int nb = (kv_end - t_lo + kPfBlk - 1) / kPfBlk;
+    const int nb = (kv_end - t_lo + S::BLK - 1) / S::BLK;
     load_block(t_lo);
     stage(sm[0]);
-    if (nb > 1) load_block(t_lo + kPfBlk);
+    if (nb > 1) load_block(t_lo + S::BLK);
     __syncthreads();
     for (int n = 0; n < nb; ++n) {
-        const int t0 = t_lo + n * kPfBlk;
+        const int t0 = t_lo + n * S::BLK;
         const PfBuf<D, KB, VB> &B = sm[n & 1];
-        // ---- scores, transposed: C[token][row], lane (row lr, tokens 4 lb + i | 16 + 4 lb + i).
+        // ---- scores, transposed: C[token][row], lane (row lr, tokens 16 tt + 4 lb + i).
         //      Issue order: four independent accumulators between dependent products.
-        f32x4_t sc[2], sz[2];
+        f32x4_t sc[S::NTT], sz[S::NTT];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) sc[tt] = sz[tt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < S::NTT; ++tt) sc[tt] = sz[tt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < S::NKS; ++ks) {
-            half8_t kc[2], kz[2];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const int off = (16 * tt + lr) * S::KRS + 32 * ks + 8 * lb;
-                kc[tt] = *reinterpret_cast<const half8_t *>(&B.kc[off]);
-                kz[tt] = *reinterpret_cast<const half8_t *>(&B.ks[off]);
-            }
             const half8_t qh = __builtin_bit_cast(half8_t, qch[ks]), ql = __builtin_bit_cast(half8_t, qcl[ks]);
             const half8_t wh = __builtin_bit_cast(half8_t, qsh[ks]), wl = __builtin_bit_cast(half8_t, qsl[ks]);
-            sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[0], qh, sc[0], 0, 0, 0);
-            sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[1], qh, sc[1], 0, 0, 0);
-            sz[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kz[0], wh, sz[0], 0, 0, 0);
-            sz[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kz[1], wh, sz[1], 0, 0, 0);
-            sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[0], ql, sc[0], 0, 0, 0);
-            sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[1], ql, sc[1], 0, 0, 0);
-            sz[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kz[0], wl, sz[0], 0, 0, 0);
-            sz[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kz[1], wl, sz[1], 0, 0, 0);
-        }
-        float lg[8];
-        {
-            const f32x4_t n1a = *reinterpret_cast<const f32x4_t *>(&B.nrm[4 * lb]);
-            const f32x4_t n1b = *reinterpret_cast<const f32x4_t *>(&B.nrm[16 + 4 * lb]);
-            const f32x4_t n2a = *reinterpret_cast<const f32x4_t *>(&B.nrm[kPfBlk + 4 * lb]);
-            const f32x4_t n2b = *reinterpret_cast<const f32x4_t *>(&B.nrm[kPfBlk + 16 + 4 * lb]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                lg[i] = n1a[i] * fmaf(n2a[i], sz[0][i], sc[0][i]);
-                lg[4 + i] = n1b[i] * fmaf(n2b[i], sz[1][i], sc[1][i]);
+            for (int tp = 0; tp < S::NTT; tp += 2) {
+                half8_t kc[2], kz[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int off = (16 * (tp + u) + lr) * S::KRS + 32 * ks + 8 * lb;
+                    kc[u] = *reinterpret_cast<const half8_t *>(&B.kc[off]);
+                    kz[u] = *reinterpret_cast<const half8_t *>(&B.ks[off]);
+                }
+                sc[tp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[0], qh, sc[tp], 0, 0, 0);
+                sc[tp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[1], qh, sc[tp + 1], 0, 0, 0);
+                sz[tp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kz[0], wh, sz[tp], 0, 0, 0);
+                sz[tp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kz[1], wh, sz[tp + 1], 0, 0, 0);
+                sc[tp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[0], ql, sc[tp], 0, 0, 0);
+                sc[tp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[1], ql, sc[tp + 1], 0, 0, 0);
+                sz[tp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kz[0], wl, sz[tp], 0, 0, 0);
+                sz[tp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kz[1], wl, sz[tp + 1], 0, 0, 0);
             }
         }
-        if (t0 + kPfBlk > wave_lim) {
+        constexpr int NL = 4 * S::NTT;  // logits per lane
+        float lg[NL];
+#pragma unroll
+        for (int tt = 0; tt < S::NTT; ++tt) {
+            const f32x4_t n1 = *reinterpret_cast<const f32x4_t *>(&B.nrm[16 * tt + 4 * lb]);
+            const f32x4_t n2 = *reinterpret_cast<const f32x4_t *>(&B.nrm[S::BLK + 16 * tt + 4 * lb]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lg[4 * tt + i] = n1[i] * fmaf(n2[i], sz[tt][i], sc[tt][i]);
+        }
+        if (t0 + S::BLK > wave_lim) {
             // tokens at or past the row's limit (its causal end, or the packed end) drop out
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int t = t0 + (j < 4 ? 4 * lb + j : 16 + 4 * lb + j - 4);
-                if (t >= lim) lg[j] = -INFINITY;
-            }
+            for (int j = 0; j < NL; ++j)
+                if (t0 + 16 * (j / 4) + 4 * lb + (j % 4) >= lim) lg[j] = -INFINITY;
         }
         // ---- online softmax of the row (its 4 lanes: lb = 0 .. 3)
         float mx = lg[0];
 #pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, lg[j]);
+        for (int j = 1; j < NL; ++j) mx = fmaxf(mx, lg[j]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const bool raise = mx > m_run;
@@ -420,43 +423,49 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
             m_run = mn;
         }
         const float mu = m_run == -INFINITY ? 0.f : m_run;
-        float p[8];
+        float p[NL];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NL; ++j) {
             p[j] = __builtin_amdgcn_exp2f(lg[j] - mu);
             l_run += p[j];
         }
-        u32x4_t ph, pl;
+        // value step s takes the lane's tokens of tiles 2 s and 2 s + 1 as its 8 k-slots
+        u32x4_t ph[S::NPS], pl[S::NPS];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint2 x = mix_split(p[2 * q], (_Float16)1.0f, p[2 * q + 1], (_Float16)1.0f);
-            ph[q] = x.x;
-            pl[q] = x.y;
-        }
+        for (int st = 0; st < S::NPS; ++st)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint2 x = mix_split(p[8 * st + 2 * q], (_Float16)1.0f, p[8 * st + 2 * q + 1], (_Float16)1.0f);
+                ph[st][q] = x.x;
+                pl[st][q] = x.y;
+            }
         // ---- o^T[coordinate][row] += V^T P^T, four output tiles at a time (independent
         //      accumulators between dependent products)
-        const half8_t bph = __builtin_bit_cast(half8_t, ph), bpl = __builtin_bit_cast(half8_t, pl);
 #pragma unroll
-        for (int d4 = 0; d4 < S::NDT; d4 += 4) {
-            half8_t vh[4], vl[4];
+        for (int st = 0; st < S::NPS; ++st) {
+            const half8_t bph = __builtin_bit_cast(half8_t, ph[st]), bpl = __builtin_bit_cast(half8_t, pl[st]);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int off = (16 * (d4 + u) + lr) * S::VRS + 8 * lb;
-                vh[u] = *reinterpret_cast<const half8_t *>(&B.vh[off]);
-                vl[u] = *reinterpret_cast<const half8_t *>(&B.vl[off]);
+            for (int d4 = 0; d4 < S::NDT; d4 += 4) {
+                half8_t vh[4], vl[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int off = (16 * (d4 + u) + lr) * S::VRS + 32 * st + 8 * lb;
+                    vh[u] = *reinterpret_cast<const half8_t *>(&B.vh[off]);
+                    vl[u] = *reinterpret_cast<const half8_t *>(&B.vl[off]);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) o[d4 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[u], bph, o[d4 + u], 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) o[d4 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[u], bpl, o[d4 + u], 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) o[d4 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl[u], bph, o[d4 + u], 0, 0, 0);
             }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) o[d4 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[u], bph, o[d4 + u], 0, 0, 0);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) o[d4 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[u], bpl, o[d4 + u], 0, 0, 0);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) o[d4 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl[u], bph, o[d4 + u], 0, 0, 0);
         }
         // ---- the next block into the other buffer (no wave reads it before the barrier), and
         //      the one after into registers
         if (n + 1 < nb) {
             stage(sm[(n + 1) & 1]);
-            if (n + 2 < nb) load_block(t0 + 2 * kPfBlk);
+            if (n + 2 < nb) load_block(t0 + 2 * S::BLK);
         }
         __syncthreads();
     }
@@ -614,6 +623,8 @@ hipError_t launch_prefill_prep(int d, const PrefillPrepArgs &a, hipStream_t st) 
     else hipLaunchKernelGGL((k_prefill_prep<256>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
+
+int prefill_block_tokens(int d) { return d == 256 ? PfShape<256, 3, 2>::BLK : PfShape<128, 3, 2>::BLK; }
 
 int prefill_tile_rows(int d) { return 16 * (d == 256 ? kPfWaves<256> : kPfWaves<128>); }
 
