@@ -62,8 +62,10 @@ struct PfShape {
     static constexpr int NDT = D / 16;            // 16-coordinate tiles of the output
     static constexpr int KRS = D + 8;             // key operand row stride (halfwords)
     static constexpr int VRS = BLK + 8;           // value operand row stride (halfwords)
-    static constexpr int ITEMS = BLK * D / 8;     // (token, 8-coordinate chunk) items of a block
+    static constexpr int ITEMS = BLK * D / 8;     // key items of a block: (token, 8-coordinate chunk)
     static constexpr int NI = (ITEMS + THREADS - 1) / THREADS;
+    static constexpr int VITEMS = ITEMS / 2;      // value items: (token pair, 8-coordinate chunk)
+    static constexpr int VNI = (VITEMS + THREADS - 1) / THREADS;
     static constexpr int HALF = 1 << (VB - 1);
 };
 
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
     auto rec_of = [&](int tok) -> int64_t {
         return record_index(a.bt, a.pt, a.pps, a.n_pages, a.cap, a.err, sbk, min(tok, kv_end - 1));
     };
-    uint32_t kr0[S::NI], kr1[S::NI], vr[S::NI], vsr[S::NI];
+    uint32_t kr0[S::NI], kr1[S::NI], vr[S::VNI][2], vsr[S::VNI][2];
     float2 knr = make_float2(0.f, 0.f);
     auto load_block = [&](int t0) {
         const int tmax = kv_end - 1 - t0;  // last valid token of the block, relative
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
 #pragma unroll
             for (int k = 0; k < S::NI; ++k) {
                 const int it = tid + S::THREADS * k;
-                kr0[k] = kr1[k] = vr[k] = vsr[k] = 0u;
+                kr0[k] = kr1[k] = 0u;
                 if (S::ITEMS % S::THREADS == 0 || it < S::ITEMS) {
                     const int tk = min(it / (D / 8), tmax), c8 = it % (D / 8);
                     if constexpr (KB == 3) {
@@ -260,9 +262,19 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
                         kr0[k] = kwb[tk * S::KW + (8 * c8 * KB) / 32];
                         kr1[k] = kwb[tk * S::KW + S::NCW + c8 / 4];
                     }
-                    const int tv = min(it % S::BLK, tmax), cv = it / S::BLK;
-                    vr[k] = vwb[tv * S::VW + (8 * cv * VB) / 32];
-                    vsr[k] = vsb[tv * S::NG + cv / 4];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < S::VNI; ++k) {
+                const int it = tid + S::THREADS * k;
+                if (S::VITEMS % S::THREADS == 0 || it < S::VITEMS) {
+                    const int pr = it % (S::BLK / 2), cv = it / (S::BLK / 2);
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int tv = min(2 * pr + e, tmax);
+                        vr[k][e] = vwb[tv * S::VW + (8 * cv * VB) / 32];
+                        vsr[k][e] = vsb[tv * S::NG + cv / 4];
+                    }
                 }
             }
             if (tid < S::BLK) knr = *reinterpret_cast<const float2 *>(a.kn + (r0 + min(tid, tmax)) * 2);
@@ -271,23 +283,28 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
 #pragma unroll
         for (int k = 0; k < S::NI; ++k) {
             const int it = tid + S::THREADS * k;
-            kr0[k] = kr1[k] = vr[k] = vsr[k] = 0u;
+            kr0[k] = kr1[k] = 0u;
             if (S::ITEMS % S::THREADS == 0 || it < S::ITEMS) {
-                {
-                    const int t = it / (D / 8), c8 = it - t * (D / 8);
-                    const uint32_t *kp = a.kw + rec_of(t0 + t) * S::KW;
-                    if constexpr (KB == 3) {
-                        kr0[k] = kp[c8];
-                    } else {
-                        kr0[k] = kp[(8 * c8 * KB) / 32];
-                        kr1[k] = kp[S::NCW + c8 / 4];
-                    }
+                const int t = it / (D / 8), c8 = it - t * (D / 8);
+                const uint32_t *kp = a.kw + rec_of(t0 + t) * S::KW;
+                if constexpr (KB == 3) {
+                    kr0[k] = kp[c8];
+                } else {
+                    kr0[k] = kp[(8 * c8 * KB) / 32];
+                    kr1[k] = kp[S::NCW + c8 / 4];
                 }
-                {
-                    const int t = it % S::BLK, c8 = it / S::BLK;
-                    const int64_t rec = rec_of(t0 + t);
-                    vr[k] = a.vw[rec * S::VW + (8 * c8 * VB) / 32];
-                    vsr[k] = a.vs[rec * S::NG + c8 / 4];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < S::VNI; ++k) {
+            const int it = tid + S::THREADS * k;
+            if (S::VITEMS % S::THREADS == 0 || it < S::VITEMS) {
+                const int pr = it % (S::BLK / 2), cv = it / (S::BLK / 2);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int64_t rec = rec_of(t0 + 2 * pr + e);
+                    vr[k][e] = a.vw[rec * S::VW + (8 * cv * VB) / 32];
+                    vsr[k][e] = a.vs[rec * S::NG + cv / 4];
                 }
             }
         }
@@ -329,23 +346,28 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
                     *reinterpret_cast<u32x4_t *>(&B.kc[t * S::KRS + 8 * c8]) = kc;
                     *reinterpret_cast<u32x4_t *>(&B.ks[t * S::KRS + 8 * c8]) = kz;
                 }
-                {
-                    // values of coordinates 8 c8 .. 8 c8 + 7 of token t: (code - HALF + 1/2) s
-                    const int t = it % S::BLK, c8 = it / S::BLK;
-                    const uint32_t w = vr[k] >> ((8 * c8 * VB) % 32);
-                    const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)vsr[k]);
-                    const int slot = value_slot(t);
+            }
+        }
+        // values of coordinates 8 c8 .. 8 c8 + 7 of tokens 2 p and 2 p + 1, (code - HALF + 1/2) s,
+        // whose slots are adjacent: one 32-bit write per coordinate and part
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float u0 = (float)((w >> (VB * 2 * q)) & ((1u << VB) - 1u)) + (0.5f - (float)S::HALF);
-                        const float u1 = (float)((w >> (VB * (2 * q + 1))) & ((1u << VB) - 1u)) + (0.5f - (float)S::HALF);
-                        const uint2 hl = mix_split(u0, sc, u1, sc);
-                        const int row = (8 * c8 + 2 * q) * S::VRS + slot;
-                        B.vh[row] = (uint16_t)hl.x;
-                        B.vh[row + S::VRS] = (uint16_t)(hl.x >> 16);
-                        B.vl[row] = (uint16_t)hl.y;
-                        B.vl[row + S::VRS] = (uint16_t)(hl.y >> 16);
-                    }
+        for (int k = 0; k < S::VNI; ++k) {
+            const int it = tid + S::THREADS * k;
+            if (S::VITEMS % S::THREADS == 0 || it < S::VITEMS) {
+                const int pr = it % (S::BLK / 2), c8 = it / (S::BLK / 2);
+                const uint32_t w0 = vr[k][0] >> ((8 * c8 * VB) % 32), w1 = vr[k][1] >> ((8 * c8 * VB) % 32);
+                const _Float16 s0 = __builtin_bit_cast(_Float16, (uint16_t)vsr[k][0]);
+                const _Float16 s1 = __builtin_bit_cast(_Float16, (uint16_t)vsr[k][1]);
+                const int dw = value_slot(2 * pr) / 2;
+                uint32_t *const vh = reinterpret_cast<uint32_t *>(B.vh), *const vl = reinterpret_cast<uint32_t *>(B.vl);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float u0 = (float)((w0 >> (VB * j)) & ((1u << VB) - 1u)) + (0.5f - (float)S::HALF);
+                    const float u1 = (float)((w1 >> (VB * j)) & ((1u << VB) - 1u)) + (0.5f - (float)S::HALF);
+                    const uint2 hl = mix_split(u0, s0, u1, s1);
+                    const int row = (8 * c8 + j) * (S::VRS / 2) + dw;
+                    vh[row] = hl.x;
+                    vl[row] = hl.y;
                 }
             }
         }
@@ -505,48 +527,68 @@ __global__ __launch_bounds__(256) void k_prefill_prep(PrefillPrepArgs a) {
     const int lr = lane & 15, lb = lane >> 4;
     const int64_t r0 = (int64_t)blockIdx.x * kPrepRows;
     const int G = a.hq / a.hkv;
-    // q' of the wave's 16 rows (one row at a time across the wave's lanes)
-    for (int i = 0; i < 16; ++i) {
-        const int rl = 16 * wave + i;
-        const int64_t r = min(r0 + rl, a.n_rows - 1);
-        float v[E];
+    // q' of the wave's 16 rows, four at a time across the wave's lanes (four independent
+    // chains of lane exchanges)
+    constexpr int RB = 4;
+    for (int i0 = 0; i0 < 16; i0 += RB) {
+        float v[RB][E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int j = lane + 64 * e;
-            float x;
-            if (a.q_dtype == TQ_F32) x = load1(a.q, r * D + j, f32_tag{});
-            else if (a.q_dtype == TQ_BF16) x = load1(a.q, r * D + j, bf16_tag{});
-            else x = load1(a.q, r * D + j, f16_tag{});
-            v[e] = flip_sign(x, (a.sign_bits[j >> 5] >> (j & 31)) & 1u);
+        for (int i = 0; i < RB; ++i) {
+            const int64_t r = min(r0 + 16 * wave + i0 + i, a.n_rows - 1);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int j = lane + 64 * e;
+                float x;
+                if (a.q_dtype == TQ_F32) x = load1(a.q, r * D + j, f32_tag{});
+                else if (a.q_dtype == TQ_BF16) x = load1(a.q, r * D + j, bf16_tag{});
+                else x = load1(a.q, r * D + j, f16_tag{});
+                v[i][e] = flip_sign(x, (a.sign_bits[j >> 5] >> (j & 31)) & 1u);
+            }
         }
 #pragma unroll
         for (int len = 1; len < 64; len <<= 1)
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float o = __shfl_xor(v[e], len);
-                v[e] = (lane & len) ? (o - v[e]) : (v[e] + o);
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float o = __shfl_xor(v[i][e], len);
+                    v[i][e] = (lane & len) ? (o - v[i][e]) : (v[i][e] + o);
+                }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+#pragma unroll
+            for (int m = 1; m < E; m <<= 1) {
+                float u[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) u[e] = (e & m) ? (v[i][e ^ m] - v[i][e]) : (v[i][e] + v[i][e ^ m]);
+#pragma unroll
+                for (int e = 0; e < E; ++e) v[i][e] = u[e];
             }
+        }
+        // a power of two per row that brings its largest |q'| into [2^13, 2^14), so that the
+        // fp16 split neither overflows nor loses bits to subnormals
+        float mx[RB];
 #pragma unroll
-        for (int m = 1; m < E; m <<= 1) {
-            float u[E];
+        for (int i = 0; i < RB; ++i) {
+            const int rl = 16 * wave + i0 + i;
+            mx[i] = 0.f;
 #pragma unroll
-            for (int e = 0; e < E; ++e) u[e] = (e & m) ? (v[e ^ m] - v[e]) : (v[e] + v[e ^ m]);
-#pragma unroll
-            for (int e = 0; e < E; ++e) v[e] = u[e];
+            for (int e = 0; e < E; ++e) {
+                qs[rl * QRS + lane + 64 * e] = v[i][e];
+                mx[i] = fmaxf(mx[i], fabsf(v[i][e]));
+            }
         }
 #pragma unroll
-        for (int e = 0; e < E; ++e) qs[rl * QRS + lane + 64 * e] = v[e];
-        // a power of two that brings the row's largest |q'| into [2^13, 2^14), so that the fp16
-        // split neither overflows nor loses bits to subnormals
-        float mx = 0.f;
+        for (int o = 32; o > 0; o >>= 1)
 #pragma unroll
-        for (int e = 0; e < E; ++e) mx = fmaxf(mx, fabsf(v[e]));
+            for (int i = 0; i < RB; ++i) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], o));
+        if (lane < RB) {
+            float m = mx[0];
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        if (lane == 0) {
+            for (int i = 1; i < RB; ++i) m = lane == i ? mx[i] : m;
             int ex = 0;
-            if (mx > 0.f) (void)frexpf(mx, &ex);  // mx < 2^ex
-            qe[rl] = ex - 14;
+            if (m > 0.f) (void)frexpf(m, &ex);  // m < 2^ex
+            qe[16 * wave + i0 + lane] = ex - 14;
         }
     }
     __syncthreads();
