@@ -11,8 +11,8 @@
 // 16 w .. 16 w + 15.  The workgroup walks the packed tokens the tile can see in blocks of 64
 // tokens (32 at head_dim 256),
 // with two LDS buffers of matrix-core operands and one barrier per block: while a wave
-// computes on block n it then expands block n + 1 (loaded into registers one block ahead)
-// into the other buffer, so one wave's expansion (VALU) overlaps another's products:
+// computes on block n it expands block n + 1 (loaded into registers one block ahead) into the
+// other buffer, issued between its products so that the expansion (VALU) overlaps them:
 //   * the key centroids and the signs as +-1 in fp16, [token][coordinate];
 //   * the values as fp16 hi + lo pairs (v = hi + lo exactly: v has at most 16 significant
 //     bits), [coordinate][token], written transposed from each token's value word;
@@ -414,6 +414,11 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
                 sz[tp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kz[1], wl, sz[tp + 1], 0, 0, 0);
             }
         }
+        // ---- the next block into the other buffer (no wave reads it before the barrier; a stage
+        //      past the end writes a buffer no wave reads again), issued while this block's
+        //      products run: after the score products at head_dim 64 and 128, before the value
+        //      products at 256 (measured)
+        if constexpr (D != 256) stage(sm[(n + 1) & 1]);
         constexpr int NL = 4 * S::NTT;  // logits per lane
         float lg[NL];
 #pragma unroll
@@ -461,6 +466,7 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
                 ph[st][q] = x.x;
                 pl[st][q] = x.y;
             }
+        if constexpr (D == 256) stage(sm[(n + 1) & 1]);
         // ---- o^T[coordinate][row] += V^T P^T, four output tiles at a time (independent
         //      accumulators between dependent products)
 #pragma unroll
@@ -483,12 +489,8 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
                 for (int u = 0; u < 4; ++u) o[d4 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl[u], bph, o[d4 + u], 0, 0, 0);
             }
         }
-        // ---- the next block into the other buffer (no wave reads it before the barrier), and
-        //      the one after into registers
-        if (n + 1 < nb) {
-            stage(sm[(n + 1) & 1]);
-            if (n + 2 < nb) load_block(t0 + 2 * S::BLK);
-        }
+        // ---- the block after next into registers
+        if (n + 2 < nb) load_block(t0 + 2 * S::BLK);
         __syncthreads();
     }
     // ---- l of the row over its 4 lanes; lane holds coordinates 16 dt + 4 lb + i
