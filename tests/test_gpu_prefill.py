@@ -24,7 +24,8 @@ def torch():
     return t
 
 
-def _prefill_case(torch, w: W.Workload, T: int, pos0: int, causal: bool, label: str, paged=None):
+def _prefill_case(torch, w: W.Workload, T: int, pos0: int, causal: bool, label: str, paged=None, q_dtype=None,
+                  q_scale=1.0):
     env = Env(w.d, w.value_bits, buffer_size=w.buffer_size, kb=w.key_bits)
     n_sl = w.batch * w.hkv
     (k, v), _ = W.host_kv(w, 0, w.n_packed)
@@ -37,8 +38,8 @@ def _prefill_case(torch, w: W.Workload, T: int, pos0: int, causal: bool, label: 
     else:
         store = quantize_gpu(env, to_dev(k, w.in_dtype), to_dev(v, w.in_dtype), n_sl, w.n_packed)
     r = np.random.default_rng(31)
-    q = r.standard_normal((w.batch, T, w.hq, w.d)).astype(np.float32)
-    qd = to_dev(q.reshape(-1, w.d), w.in_dtype)
+    q = (q_scale * r.standard_normal((w.batch, T, w.hq, w.d))).astype(np.float32)
+    qd = to_dev(q.reshape(-1, w.d), q_dtype or w.in_dtype)
     out = torch.zeros((w.batch, T, w.hq, w.d), dtype=torch.float32, device="cuda")
     ws = tq.new_prefill_workspace(env.cfg, w.batch, T, w.hq, w.hkv, w.n_packed)
     scale = 1.0 / math.sqrt(w.d)
@@ -133,3 +134,16 @@ def test_prefill_decode_path_for_few_query_rows(torch):
     _prefill_case(torch, W.custom(2, batch=2, hq=8, hkv=2, n_packed=700), 5, 695, True, "d128 T=5 (decode kernels)")
     _prefill_case(torch, W.custom(2, d=64, key_bits=1, batch=1, hq=4, hkv=1, n_packed=300), 3, 10, True,
                   "d64 kb1 T=3 (decode kernels)")
+
+
+def test_prefill_query_dtypes_and_magnitudes(torch):
+    # fp32 and fp16 queries through the tiled path's preparation, and queries of very large and
+    # very small magnitude (the preparation scales each row by a power of two before its fp16
+    # split: no overflow, no subnormals)
+    w = W.custom(2, batch=1, hq=8, hkv=2, n_packed=300)
+    _prefill_case(torch, w, 40, 260, True, "d128 fp32 queries", q_dtype="f32")
+    _prefill_case(torch, w, 40, 260, True, "d128 fp16 queries", q_dtype="f16")
+    _prefill_case(torch, w, 40, 260, True, "d128 fp32 queries x 1e4", q_dtype="f32", q_scale=1e4)
+    _prefill_case(torch, w, 40, 260, True, "d128 fp32 queries x 1e-4", q_dtype="f32", q_scale=1e-4)
+    _prefill_case(torch, W.custom(4, batch=1, hq=4, hkv=2, n_packed=200), 30, 170, True, "d256 fp16 queries x 300",
+                  q_dtype="f16", q_scale=300.0)
