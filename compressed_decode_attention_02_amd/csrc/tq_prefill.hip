@@ -5,21 +5,21 @@
 // softmax over the packed tokens a query may see (causal: those up to its own position) and
 // values dequantised to their bin centres (code - 2^(vb-1) + 1/2) * group scale.
 //
-// One workgroup of NW waves per (query tile, sequence, kv head): NW = 8 at head_dim 64 and
-// 128, 4 at 256 (its query operands take twice the registers).  A tile is 16 NW query rows
-// (token, head) of one kv head, the G heads of a token in consecutive rows; wave w takes rows
-// 16 w .. 16 w + 15.  The workgroup walks the packed tokens the tile can see in blocks of 64
-// tokens (32 at head_dim 256),
-// with two LDS buffers of matrix-core operands and one barrier per block: while a wave
-// computes on block n it expands block n + 1 (loaded into registers one block ahead) into the
-// other buffer, issued between its products so that the expansion (VALU) overlaps them:
+// One workgroup of NW waves per (query tile, sequence, kv head, split of the packed range):
+// NW = 8 at head_dim 64 and 128, 4 at 256 (its query operands take twice the registers).  A
+// tile is 16 NW query rows (token, head) of one kv head, the G heads of a token in consecutive
+// rows; wave w takes rows 16 w .. 16 w + 15.  The workgroup walks the packed tokens the tile can
+// see in blocks of 64 tokens (32 at head_dim 256), with two LDS buffers of matrix-core operands
+// and one barrier per block; while a wave computes on block n it expands block n + 1 (loaded
+// into registers one block ahead) into the other buffer, issued between its products so that
+// the expansion (VALU) overlaps them:
 //   * the key centroids and the signs as +-1 in fp16, [token][coordinate];
 //   * the values as fp16 hi + lo pairs (v = hi + lo exactly: v has at most 16 significant
-//     bits), [coordinate][token], written transposed from each token's value word;
-//   * each wave forms its 16 x 32 scores transposed (tokens as rows: A = the key operand from
-//     LDS, B = the query rows held in registers as fp16 hi + lo of q' * scale * log2 e / sqrt d
-//     and of -w * scale * log2 e * sqrt(pi/2) / d), v_mfma_f32_16x16x32_f16; a lane then holds
-//     one query row and eight tokens, logit = |k| (c + gamma s) in log2 units;
+//     bits), [coordinate][token], two tokens per lane from their value words;
+//   * each wave forms its scores transposed (tokens as rows: A = the key operand from LDS, B =
+//     the query rows held in registers as fp16 hi + lo of q' * scale * log2 e / sqrt d and of
+//     -w * scale * log2 e * sqrt(pi/2) / d), v_mfma_f32_16x16x32_f16; a lane then holds one
+//     query row and four tokens of each 16-token tile, logit = |k| (c + gamma s) in log2 units;
 //   * online softmax per row (running maximum raised only when a block exceeds it; the 4 lanes
 //     of a row share it through two lane exchanges), p = 2^(logit - m) with hi + lo parts;
 //   * o^T += V^T P^T on the matrix cores (A = the value pairs from LDS, B = the lane's own p:
@@ -146,9 +146,9 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
     const int64_t nwg = gridDim.x, id = blockIdx.x;
     const int64_t per = nwg / 8, rem = nwg % 8, xcd = id % 8, kk = id / 8;
     const int64_t lid = xcd < rem ? xcd * (per + 1) + kk : rem * (per + 1) + (xcd - rem) * per + kk;
-    const int64_t ss = lid / a.tiles;  // (slice, split)
-    const int tile = a.tiles - 1 - (int)(lid - ss * a.tiles);
-    const int sl = (int)(ss / a.n_split), split = (int)(ss - (int64_t)sl * a.n_split);
+    const int64_t sps = lid / a.tiles;  // (slice, split)
+    const int tile = a.tiles - 1 - (int)(lid - sps * a.tiles);
+    const int sl = (int)(sps / a.n_split), split = (int)(sps - (int64_t)sl * a.n_split);
     const int seq = sl / a.hkv, kvh = sl - seq * a.hkv;
     const int G = a.hq / a.hkv;
     const int rows = a.T * G;
