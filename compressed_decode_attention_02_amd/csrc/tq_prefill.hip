@@ -418,7 +418,10 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
         //      past the end writes a buffer no wave reads again), issued while this block's
         //      products run: after the score products at head_dim 64 and 128, before the value
         //      products at 256 (measured)
-        if constexpr (D != 256) stage(sm[(n + 1) & 1]);
+        if constexpr (D != 256) {
+            stage(sm[(n + 1) & 1]);
+            if (n + 2 < nb) load_block(t0 + 2 * S::BLK);  // the block after next into registers
+        }
         constexpr int NL = 4 * S::NTT;  // logits per lane
         float lg[NL];
 #pragma unroll
@@ -462,11 +465,19 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
         for (int st = 0; st < S::NPS; ++st)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint2 x = mix_split(p[8 * st + 2 * q], (_Float16)1.0f, p[8 * st + 2 * q + 1], (_Float16)1.0f);
-                ph[st][q] = x.x;
-                pl[st][q] = x.y;
+                // hi = fp16 pair (round to nearest), lo = fp16(p - hi) by mixed fma
+                const float x0 = p[8 * st + 2 * q], x1 = p[8 * st + 2 * q + 1];
+                uint32_t hi, lo;
+                asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(hi) : "v"(x0), "v"(x1));
+                asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=&v"(lo) : "v"(x0), "v"(hi));
+                asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(lo) : "v"(x1), "v"(hi));
+                ph[st][q] = hi;
+                pl[st][q] = lo;
             }
-        if constexpr (D == 256) stage(sm[(n + 1) & 1]);
+        if constexpr (D == 256) {
+            stage(sm[(n + 1) & 1]);
+            if (n + 2 < nb) load_block(t0 + 2 * S::BLK);
+        }
         // ---- o^T[coordinate][row] += V^T P^T, four output tiles at a time (independent
         //      accumulators between dependent products)
 #pragma unroll
@@ -489,8 +500,6 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
                 for (int u = 0; u < 4; ++u) o[d4 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl[u], bph, o[d4 + u], 0, 0, 0);
             }
         }
-        // ---- the block after next into registers
-        if (n + 2 < nb) load_block(t0 + 2 * S::BLK);
         __syncthreads();
     }
     // ---- l of the row over its 4 lanes; lane holds coordinates 16 dt + 4 lb + i
