@@ -325,7 +325,7 @@ int64_t prefill_launch_tokens(int32_t n_kv_heads) { return std::max<int64_t>(1, 
 // decode kernels, whose splits spread one row's tokens over many workgroups
 bool prefill_tiled(int d, int64_t T, int64_t G) { return T * G * 2 >= tq::prefill_tile_rows(d); }
 
-// query tokens per launch of the tiled path (bounds its workspace)
+// query tokens per launch of the tiled path (bounds its split partials)
 int64_t prefill_tiled_launch_tokens(int32_t n_kv_heads) { return std::max<int64_t>(1, 65536 / n_kv_heads); }
 
 // the tiled path's plan for n_seq sequences of T query tokens: tiles per (sequence, kv head)
@@ -333,7 +333,7 @@ int64_t prefill_tiled_launch_tokens(int32_t n_kv_heads) { return std::max<int64_
 // whole blocks, at least 256 tokens each, at most 16 splits)
 struct PrefillPlan {
     int tiles, n_split, per_split;
-    size_t prep, partial, partial_ml, total;  // workspace layout (bytes)
+    size_t partial, partial_ml, total;  // workspace layout (bytes): split partials only
 };
 PrefillPlan prefill_plan(int d, int64_t n_seq, int64_t T, int64_t hq, int64_t hkv, int64_t n_packed) {
     PrefillPlan p{};
@@ -346,11 +346,10 @@ PrefillPlan prefill_plan(int d, int64_t n_seq, int64_t T, int64_t hq, int64_t hk
     p.n_split = (int)ns;
     p.per_split = (int)(((blocks + ns - 1) / ns) * bt);
     const int64_t rows = n_seq * T * hq;
-    p.prep = 0;
-    p.partial = align256(sizeof(float) * (size_t)rows * 2 * d);
+    p.partial = 0;
     const size_t part = ns > 1 ? align256(sizeof(float) * (size_t)(rows * ns) * d) : 0;
     p.partial_ml = p.partial + part;
-    p.total = p.partial_ml + (ns > 1 ? align256(sizeof(float) * (size_t)(rows * ns) * 2) : 0);
+    p.total = std::max<size_t>(256, p.partial_ml + (ns > 1 ? align256(sizeof(float) * (size_t)(rows * ns) * 2) : 0));
     return p;
 }
 
@@ -370,20 +369,12 @@ tq_status prefill_tiled_impl(const tq_config *cfg, const tq_tables *tables, cons
     if (workspace_bytes < plan.total) return TQ_ERR_WORKSPACE;
     if (check_only) return TQ_OK;
     const hipStream_t st = (hipStream_t)stream;
-    tq::PrefillPrepArgs pp{};
-    pp.q = q;
-    pp.q_dtype = (int)q_dtype;
-    pp.sign_bits = tables->sign_bits;
-    pp.S = tables->qjl_S;
-    pp.n_rows = n_seq * T * n_q_heads;
-    pp.hq = n_q_heads;
-    pp.hkv = n_kv_heads;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
-    pp.prep = reinterpret_cast<float *>(ws + plan.prep);
-    hipError_t e = tq::launch_prefill_prep(cfg->head_dim, pp, st);
-    if (e != hipSuccess) return TQ_ERR_HIP;
     tq::PrefillArgs a{};
-    a.prep = pp.prep;
+    a.q = q;
+    a.q_dtype = (int)q_dtype;
+    a.sign_bits = tables->sign_bits;
+    a.S = tables->qjl_S;
     a.centroids = tables->centroids;
     if (n_packed > 0) {
         a.kw = packed->key_words;
@@ -407,7 +398,7 @@ tq_status prefill_tiled_impl(const tq_config *cfg, const tq_tables *tables, cons
     a.per_split = plan.per_split;
     a.partial = reinterpret_cast<float *>(ws + plan.partial);
     a.partial_ml = reinterpret_cast<float *>(ws + plan.partial_ml);
-    e = tq::launch_prefill(cfg->head_dim, cfg->key_bits, cfg->value_bits, n_seq, a, st);
+    hipError_t e = tq::launch_prefill(cfg->head_dim, cfg->key_bits, cfg->value_bits, n_seq, a, st);
     if (e != hipSuccess || plan.n_split == 1) return hip_status(e);
     // the splits' partials of every row combined by the decode's merge (query token = batch
     // element of the decode's layout)

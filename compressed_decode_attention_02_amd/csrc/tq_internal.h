@@ -112,10 +112,13 @@ __device__ inline int64_t record_index(const int32_t *bt, int pt, int pps, int64
 }
 
 // prefill attention by query tiles (tq_prefill.hip): the launch's query rows are (sequence,
-// query token, head) with the G heads of a kv head consecutive; q' and w of every row come from
-// k_decode_prep run over the launch's query tokens as a batch of n_seq * T
+// query token, head) with the G heads of a kv head consecutive; each workgroup prepares its
+// rows' q' and w itself
 struct PrefillArgs {
-    const float *prep;  // [n_seq * T][hkv][2][G][D]: q' then w of each row
+    const void *q;      // [n_seq][T][hq][D] in q_dtype
+    int q_dtype;
+    const uint32_t *sign_bits;
+    const uint16_t *S;
     const float *centroids;
     const uint32_t *kw;
     const float *kn;
@@ -150,18 +153,7 @@ hipError_t launch_decode(int d, int kb, int vb, int G, const DecodeArgs &a, hipS
 // workspace holds the prepared queries
 bool decode_uses_any(int d, int kb);
 void launch_decode_any_main(int d, int kb, int vb, int G, const DecodeArgs &a, hipStream_t st);
-// q' and w of every query row of a prefill launch (tq_prefill.hip)
-struct PrefillPrepArgs {
-    const void *q;      // [n_rows][D] in q_dtype: rows (token, head)
-    int q_dtype;
-    const uint32_t *sign_bits;
-    const uint16_t *S;
-    int64_t n_rows;     // tokens * hq
-    int hq, hkv;
-    float *prep;        // [tokens][hkv][2][G][D]
-};
-hipError_t launch_prefill_prep(int d, const PrefillPrepArgs &a, hipStream_t st);
-// query rows per prefill tile, and the tiled prefill itself (prep already in a.prep)
+// query rows per prefill tile, and the tiled prefill itself
 int prefill_tile_rows(int d);
 int prefill_block_tokens(int d);
 hipError_t launch_prefill(int d, int kb, int vb, int64_t n_seq, const PrefillArgs &a, hipStream_t st);

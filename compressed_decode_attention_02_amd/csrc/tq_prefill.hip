@@ -196,14 +196,120 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
         return;
     }
 
+    // ---- query preparation of the tile's rows, in LDS (the operand buffers serve as scratch
+    //      before the first block; each wave works on its own 16 rows): q' = H (sigma o q),
+    //      unnormalised, by lane exchanges with four rows in flight; w = S q' on the matrix
+    //      cores (S fp16 exact; q' 2^-e as fp16 hi + lo, e per row so that its largest entry
+    //      lies in [2^13, 2^14): no overflow, no subnormals; the sums scaled back by 2^e)
+    constexpr int QRS = D + 4;  // scratch row stride (floats)
+    float *const qsc = reinterpret_cast<float *>(&sm[0]);         // q' [ROWS][QRS]
+    float *const wsc = qsc + S::ROWS * QRS;                      // w  [ROWS][QRS]
+    int *const qex = reinterpret_cast<int *>(wsc + S::ROWS * QRS);  // e [ROWS]
+    static_assert((2 * S::ROWS * QRS + S::ROWS) * 4 <= sizeof(sm), "preparation scratch");
+    {
+        constexpr int E = D / 64, RB = 4;
+        for (int i0 = 0; i0 < 16; i0 += RB) {
+            float v[RB][E];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const int rr = min(tile * S::ROWS + 16 * wave + i0 + i, rows - 1);
+                const int ti = rr / G, gi = rr - ti * G;
+                const int64_t qrow = (((int64_t)seq * a.T + ti) * a.hq + kvh * G + gi) * D;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int j = lane + 64 * e;
+                    float x;
+                    if (a.q_dtype == TQ_F32) x = load1(a.q, qrow + j, f32_tag{});
+                    else if (a.q_dtype == TQ_BF16) x = load1(a.q, qrow + j, bf16_tag{});
+                    else x = load1(a.q, qrow + j, f16_tag{});
+                    v[i][e] = flip_sign(x, (a.sign_bits[j >> 5] >> (j & 31)) & 1u);
+                }
+            }
+#pragma unroll
+            for (int len = 1; len < 64; len <<= 1)
+#pragma unroll
+                for (int i = 0; i < RB; ++i)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float o2 = __shfl_xor(v[i][e], len);
+                        v[i][e] = (lane & len) ? (o2 - v[i][e]) : (v[i][e] + o2);
+                    }
+            float mx[RB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+#pragma unroll
+                for (int m = 1; m < E; m <<= 1) {
+                    float u[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) u[e] = (e & m) ? (v[i][e ^ m] - v[i][e]) : (v[i][e] + v[i][e ^ m]);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) v[i][e] = u[e];
+                }
+                const int rl = 16 * wave + i0 + i;
+                mx[i] = 0.f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    qsc[rl * QRS + lane + 64 * e] = v[i][e];
+                    mx[i] = fmaxf(mx[i], fabsf(v[i][e]));
+                }
+            }
+#pragma unroll
+            for (int o2 = 32; o2 > 0; o2 >>= 1)
+#pragma unroll
+                for (int i = 0; i < RB; ++i) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], o2));
+            if (lane < RB) {
+                float m = mx[0];
+#pragma unroll
+                for (int i = 1; i < RB; ++i) m = lane == i ? mx[i] : m;
+                int ex = 0;
+                if (m > 0.f) (void)frexpf(m, &ex);  // m < 2^ex
+                qex[16 * wave + i0 + lane] = ex - 14;
+            }
+        }
+    }
+    __syncthreads();
+    {
+        // w^T = S q'^T for the wave's rows: A = 16 rows of S x 32, B = q' 2^-e of the 16 rows
+        // as hi + lo; C lane: row lr, coordinates 16 ot + 4 lb + i
+        const int rl = 16 * wave + lr, ex = qex[rl];
+        half8_t bh[S::NKS], bl[S::NKS];
+#pragma unroll
+        for (int ks = 0; ks < S::NKS; ++ks) {
+            const float4 x0 = *reinterpret_cast<const float4 *>(&qsc[rl * QRS + 32 * ks + 8 * lb]);
+            const float4 x1 = *reinterpret_cast<const float4 *>(&qsc[rl * QRS + 32 * ks + 8 * lb + 4]);
+            const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float y = ldexpf(x[j], -ex);
+                bh[ks][j] = (_Float16)y;
+                bl[ks][j] = (_Float16)(y - (float)bh[ks][j]);
+            }
+        }
+#pragma unroll
+        for (int ot = 0; ot < S::NDT; ++ot) {
+            f32x4_t acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < S::NKS; ++ks) {
+                const half8_t sa = *reinterpret_cast<const half8_t *>(a.S + (int64_t)(16 * ot + lr) * D + 32 * ks + 8 * lb);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, bh[ks], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, bl[ks], acc, 0, 0, 0);
+            }
+            f32x4_t wv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[i] = ldexpf(acc[i], ex);
+            *reinterpret_cast<f32x4_t *>(&wsc[rl * QRS + 16 * ot + 4 * lb]) = wv;
+        }
+    }
+    __syncthreads();
+
     // query operands of the row: k-step ks covers coordinates 32 ks + 8 lb .. + 7 in the slot
     // orders of the key operands, as fp16 hi + lo
     u32x4_t qch[S::NKS], qcl[S::NKS], qsh[S::NKS], qsl[S::NKS];
     {
         const float cs = a.scale * kPfLog2e * rsqrtf((float)D);
         const float ss = -cs * (1.2533141373155003f / (float)D);  // -sqrt(pi/2) / d
-        const float *pq = a.prep + (((int64_t)seq * a.T + qi) * a.hkv + kvh) * 2 * G * D + (int64_t)qg * D;
-        const float *pw = pq + (int64_t)G * D;
+        const float *pq = qsc + (16 * wave + lr) * QRS;
+        const float *pw = wsc + (16 * wave + lr) * QRS;
 #pragma unroll
         for (int ks = 0; ks < S::NKS; ++ks) {
             const int c0 = 32 * ks + 8 * lb;
@@ -224,6 +330,7 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
             }
         }
     }
+    __syncthreads();  // the scratch is the first block's buffer
 
     // codebook as fp16 byte tables (entry e: byte e % 4 of word e / 4)
     uint32_t tl[4] = {0u, 0u, 0u, 0u}, th[4] = {0u, 0u, 0u, 0u};
@@ -518,137 +625,6 @@ __global__ __launch_bounds__(64 * kPfWaves<D>) void k_prefill_tile(PrefillArgs a
     }
 }
 
-// ---- query preparation for the tiles: for each query row (token, head) of the launch,
-// q' = H (sigma o q) (unnormalised Walsh-Hadamard transform by lane exchanges, as the decode's
-// preparation) and w = S q' on the matrix cores (S is fp16; q' 2^-e, e per row so that its
-// largest entry lies in [2^13, 2^14), enters as fp16 hi + lo, so each product is exact up to
-// the split's 2^-22 and the fp32 sums; the sums are scaled back by 2^e).  Workgroups of 4 waves take 64
-// consecutive rows, 16 per wave; rows are [token][head] of q, and the results go to the
-// layout the tiles read: [token][kv head][q' of the G heads, then their w][D].
-constexpr int kPrepRows = 64;
-
-template <int D>
-__global__ __launch_bounds__(256) void k_prefill_prep(PrefillPrepArgs a) {
-    constexpr int E = D / 64;       // coordinates per lane of one row (lane + 64 e)
-    constexpr int NKS = D / 32, NOT = D / 16;
-    constexpr int QRS = D + 4;      // LDS row stride (floats)
-    __shared__ __align__(16) float qs[kPrepRows * QRS];
-    __shared__ int qe[kPrepRows];  // per row: q' enters the products as q' 2^-qe (|q' 2^-qe| < 2^14)
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lr = lane & 15, lb = lane >> 4;
-    const int64_t r0 = (int64_t)blockIdx.x * kPrepRows;
-    const int G = a.hq / a.hkv;
-    // q' of the wave's 16 rows, four at a time across the wave's lanes (four independent
-    // chains of lane exchanges)
-    constexpr int RB = 4;
-    for (int i0 = 0; i0 < 16; i0 += RB) {
-        float v[RB][E];
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            const int64_t r = min(r0 + 16 * wave + i0 + i, a.n_rows - 1);
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int j = lane + 64 * e;
-                float x;
-                if (a.q_dtype == TQ_F32) x = load1(a.q, r * D + j, f32_tag{});
-                else if (a.q_dtype == TQ_BF16) x = load1(a.q, r * D + j, bf16_tag{});
-                else x = load1(a.q, r * D + j, f16_tag{});
-                v[i][e] = flip_sign(x, (a.sign_bits[j >> 5] >> (j & 31)) & 1u);
-            }
-        }
-#pragma unroll
-        for (int len = 1; len < 64; len <<= 1)
-#pragma unroll
-            for (int i = 0; i < RB; ++i)
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float o = __shfl_xor(v[i][e], len);
-                    v[i][e] = (lane & len) ? (o - v[i][e]) : (v[i][e] + o);
-                }
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-#pragma unroll
-            for (int m = 1; m < E; m <<= 1) {
-                float u[E];
-#pragma unroll
-                for (int e = 0; e < E; ++e) u[e] = (e & m) ? (v[i][e ^ m] - v[i][e]) : (v[i][e] + v[i][e ^ m]);
-#pragma unroll
-                for (int e = 0; e < E; ++e) v[i][e] = u[e];
-            }
-        }
-        // a power of two per row that brings its largest |q'| into [2^13, 2^14), so that the
-        // fp16 split neither overflows nor loses bits to subnormals
-        float mx[RB];
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            const int rl = 16 * wave + i0 + i;
-            mx[i] = 0.f;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                qs[rl * QRS + lane + 64 * e] = v[i][e];
-                mx[i] = fmaxf(mx[i], fabsf(v[i][e]));
-            }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1)
-#pragma unroll
-            for (int i = 0; i < RB; ++i) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], o));
-        if (lane < RB) {
-            float m = mx[0];
-#pragma unroll
-            for (int i = 1; i < RB; ++i) m = lane == i ? mx[i] : m;
-            int ex = 0;
-            if (m > 0.f) (void)frexpf(m, &ex);  // m < 2^ex
-            qe[16 * wave + i0 + lane] = ex - 14;
-        }
-    }
-    __syncthreads();
-    // w^T = S q'^T for the wave's rows: A = rows of S (fp16, 16 output coordinates x 32), B = q'
-    // of the 16 rows as hi + lo; C lane: row lr, coordinates 16 ot + 4 lb + i
-    const int rl = 16 * wave + lr;
-    const int64_t r = r0 + rl;
-    const int ex = qe[rl];
-    half8_t bh[NKS], bl[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        const float4 x0 = *reinterpret_cast<const float4 *>(&qs[rl * QRS + 32 * ks + 8 * lb]);
-        const float4 x1 = *reinterpret_cast<const float4 *>(&qs[rl * QRS + 32 * ks + 8 * lb + 4]);
-        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float y = ldexpf(x[j], -ex);
-            bh[ks][j] = (_Float16)y;
-            bl[ks][j] = (_Float16)(y - (float)bh[ks][j]);
-        }
-    }
-    const int64_t tok = r / a.hq;
-    const int h = (int)(r - tok * a.hq), kvh = h / G, g = h - kvh * G;
-    float *const dst = a.prep + ((tok * a.hkv + kvh) * 2 * G + g) * D;
-    const bool ok = r < a.n_rows;
-#pragma unroll
-    for (int ot = 0; ot < NOT; ++ot) {
-        f32x4_t acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const half8_t sa = *reinterpret_cast<const half8_t *>(a.S + (int64_t)(16 * ot + lr) * D + 32 * ks + 8 * lb);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, bh[ks], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, bl[ks], acc, 0, 0, 0);
-        }
-        if (ok) {
-            f32x4_t wv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wv[i] = ldexpf(acc[i], ex);
-            *reinterpret_cast<f32x4_t *>(dst + (int64_t)G * D + 16 * ot + 4 * lb) = wv;
-        }
-    }
-    // q' itself: lane lr's row, coordinates 16 ot + 4 lb .. (the same lanes as w)
-    if (ok)
-#pragma unroll
-        for (int ot = 0; ot < NOT; ++ot)
-            *reinterpret_cast<float4 *>(dst + 16 * ot + 4 * lb) =
-                *reinterpret_cast<const float4 *>(&qs[rl * QRS + 16 * ot + 4 * lb]);
-}
-
 template <int D, int KB>
 hipError_t launch_kb(int vb, dim3 grid, const PrefillArgs &a, hipStream_t st) {
     const dim3 block(64 * kPfWaves<D>);
@@ -668,14 +644,6 @@ hipError_t launch_d(int kb, int vb, dim3 grid, const PrefillArgs &a, hipStream_t
 }
 
 }  // namespace
-
-hipError_t launch_prefill_prep(int d, const PrefillPrepArgs &a, hipStream_t st) {
-    const dim3 grid((unsigned)((a.n_rows + kPrepRows - 1) / kPrepRows));
-    if (d == 64) hipLaunchKernelGGL((k_prefill_prep<64>), grid, dim3(256), 0, st, a);
-    else if (d == 128) hipLaunchKernelGGL((k_prefill_prep<128>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_prefill_prep<256>), grid, dim3(256), 0, st, a);
-    return hipGetLastError();
-}
 
 int prefill_block_tokens(int d) { return d == 256 ? PfShape<256, 3, 2>::BLK : PfShape<128, 3, 2>::BLK; }
 

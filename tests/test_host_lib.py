@@ -382,7 +382,6 @@ def test_prefill_argument_errors():
     # and every launch is checked before the first
     big = L.tq_prefill_workspace_bytes(ctypes.byref(cfg), 1, 40000, 8, 2, 500)
     assert big == L.tq_prefill_workspace_bytes(ctypes.byref(cfg), 1, 32768, 8, 2, 500)
-    assert big > L.tq_prefill_workspace_bytes(ctypes.byref(cfg), 1, 32767, 8, 2, 500)
     assert pf(batch=1, q_tokens=40000, ws_bytes=16) == B.TQ_ERR_WORKSPACE
     assert pf(batch=1, q_tokens=40000, n_packed=1001) == B.TQ_ERR_INVALID_ARG
 
@@ -390,9 +389,9 @@ def test_prefill_argument_errors():
 def test_prefill_workspace_plan():
     """The prefill's host plan (no device: 256 compute units assumed).  Few query rows per kv head
     (T G below half a 128-row tile) take the decode kernels' workspace; more take the tiled
-    kernel's: q' and w per query row (2 d fp32), and, when the tiles alone do not cover the
+    kernel's, which prepares its queries itself: only when the tiles alone do not cover the
     compute units, (o, m, l) partials per row and split of the packed range (splits of whole
-    64-token blocks, at least 256 tokens each, at most 16)."""
+    64-token blocks, at least 256 tokens each, at most 16); else the 256-byte minimum."""
     cfg = tq.make_config()  # head_dim 128
     L = tq.lib()
     ws = lambda bsz, T, hq, hkv, n: L.tq_prefill_workspace_bytes(ctypes.byref(cfg), bsz, T, hq, hkv, n)
@@ -401,13 +400,13 @@ def test_prefill_workspace_plan():
     assert ws(1, 15, 8, 2, 5000) == L.tq_decode_workspace_bytes(ctypes.byref(cfg), 15, 8, 2, 5000)
     # T G = 256: 2 tiles per kv head, 4 workgroups < 256 CUs, 79 blocks of 64 -> 16 splits
     rows = 64 * 8
-    assert ws(1, 64, 8, 2, 5000) == al(rows * 2 * 128 * 4) + al(rows * 16 * 128 * 4) + al(rows * 16 * 2 * 4)
+    assert ws(1, 64, 8, 2, 5000) == al(rows * 16 * 128 * 4) + al(rows * 16 * 2 * 4)
     # a short history limits the splits: 600 tokens -> 2 splits of 320
-    assert ws(1, 64, 8, 2, 600) == al(rows * 2 * 128 * 4) + al(rows * 2 * 128 * 4) + al(rows * 2 * 2 * 4)
-    # enough tiles to cover the CUs (32 sequences x 8 kv heads x 16 tiles): no split, prep only
-    rows = 16 * 512 * 32
-    assert ws(32, 512, 32, 8, 8128) == al(rows * 2 * 128 * 4)
-    assert ws(1, 64, 8, 2, 100) == al(64 * 8 * 2 * 128 * 4)  # under 256 tokens: one split
+    assert ws(1, 64, 8, 2, 600) == al(rows * 2 * 128 * 4) + al(rows * 2 * 2 * 4)
+    # enough tiles to cover the CUs (32 sequences x 8 kv heads x 16 tiles), or under 256
+    # tokens of history: no split
+    assert ws(32, 512, 32, 8, 8128) == 256
+    assert ws(1, 64, 8, 2, 100) == 256
 
 
 def test_kivi_bytes_per_token():
