@@ -247,8 +247,8 @@ tq_status tq_decode_step(const tq_config *cfg, const tq_tables *tables, const vo
  *   out : [batch][q_tokens][n_q_heads][head_dim] fp32 (device); a token with no packed token
  *         to attend to gets zeros.
  * Calls whose query rows per kv head (q_tokens * G, G = n_q_heads / n_kv_heads) fill at least
- * half a query tile (64 rows; 32 at head_dim 256) run the tiled kernel: a query preparation
- * launch, one launch over (query tile, sequence, kv head, split of the packed range) and, when
+ * half a query tile (64 rows; 32 at head_dim 256) run the tiled kernel: one launch over (query
+ * tile of 128 rows (64 at head_dim 256), sequence, kv head, split of the packed range) and, when
  * the packed range is split, the decode's merge; launches of at most 65536 / n_kv_heads query
  * tokens.  Fewer rows run the decode kernels with one batch element per query token reading its
  * sequence's records (launches of at most 65535 / n_kv_heads query tokens).  Every launch is
